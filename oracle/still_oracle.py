@@ -1,0 +1,432 @@
+"""CPU oracle for the STILL intra-layer hybrid attention operator.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.
+The product path (the HIP library and its Python binding) never touches it,
+and this module imports nothing from the product.
+
+Everything is plain float64 numpy, one obvious step at a time.  Sources are
+the paper "STILL: Selecting Tokens for Intra-Layer Hybrid Attention to
+Linearize LLMs" (Meng et al., 2026), as printed on its web pages:
+
+* full text (paperpeel): Sec. 3.1 "Selecting Tokens by Self-Saliency Score",
+  Sec. 3.2 "Norm-Preserved Feature Map", Sec. 3.3 ("Recurrent Form",
+  "Chunk-Wise Parallel Form", "Complexity Analysis"), Appendix A.2 (the
+  linear-attention state recurrence), A.3 (Lemma 1 and its Remark),
+  A.4 (budget certification), A.7.5 (window spans one chunk);
+* list view (thelatestinai): captions of Fig. 1 and Fig. 2.
+
+The display equations of those pages were lost in extraction, so several
+steps are readings of the prose.  Each reading is named where it is used:
+
+R-SCORE   Self-Saliency of token t = the epsilon-smoothed divergence between
+          token t's own local attention row ``a`` (over its window, itself
+          included) and the leave-one-out row ``a~`` (the same logits with the
+          self term removed, renormalised; a~_t = 0):
+              Score_t = sum_j a_j * ln((a_j + eps) / (a~_j + eps)).
+          (A.3 Lemma 1: rises with the diagonal probability as eps -> 0;
+          Remark: at finite eps it re-ranks by the whole leave-one-out change.)
+R-GQA     Under grouped-query attention the routing score of a KV head is the
+          mean of its query heads' scores, summed in ascending head order
+          (Sec. 3.3: routing is per head; the caches are per KV head).
+R-SELECT  For every complete chunk, keep the top-lambda tokens by score;
+          ties go to the lower position; -0 == +0; NaN ranks lowest.
+R-DELAY   Chunk c is decided when its last token arrives; token j's route is
+          used by every query t with j <= t - W (the token has left the
+          window).  Needs W >= C whenever lambda > 0 (A.7.5: the window
+          spans one chunk; Sec. 3.3 Recurrent Form: routing happens when a
+          token leaves the window, per chunk).
+R-NPMAP   phi(x) = [softmax(z); softmax(-z)] with u = P x and
+          z = ||x|| u / ||u||  (z = 0 when u = 0): direction from the learned
+          projection, pretrained norm re-injected before the softmax
+          (Sec. 2 Hedgehog form; Sec. 3.2; abstract).
+R-AGG     One shared normaliser: SA tokens weigh exp(tau q.k), LA tokens weigh
+          phi_q(q).phi_k(k); out = sum w v / sum w  (Fig. 2 "hybrid
+          aggregation"; Fig. 1: the context is kept without loss).
+R-SCALE   tau = 1/sqrt(d) unless given.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+# route flag values (same meaning as the cache's win_route bytes)
+PENDING, ROUTE_SA, ROUTE_LA = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class Params:
+    window: int          # W
+    chunk: int           # C
+    topk: int            # lambda, per chunk
+    eps: float = 1e-6    # Self-Saliency smoothing (A.3: "infinitesimally small")
+    scale: float = 0.0   # tau; 0 -> 1/sqrt(d)
+
+    def tau(self, d: int) -> float:
+        return self.scale if self.scale > 0 else 1.0 / math.sqrt(d)
+
+    def topk_eff(self) -> int:
+        return min(self.topk, self.chunk)
+
+
+def validate(p: Params, n_q_heads: int, n_kv_heads: int, feat_dim: int) -> None:
+    """Shape rules that follow from R-DELAY and the GQA layout."""
+    if n_kv_heads <= 0 or n_q_heads % n_kv_heads:
+        raise ValueError("query heads must be a multiple of KV heads")
+    if p.window < 0 or p.chunk <= 0 or p.topk < 0:
+        raise ValueError("window >= 0, chunk > 0, topk >= 0")
+    if p.window == 0 and p.topk > 0:
+        raise ValueError("no window means no scores, so topk must be 0")
+    if p.topk > 0 and p.window < p.chunk:
+        raise ValueError("delayed selection needs window >= chunk")
+    if feat_dim % 2:
+        raise ValueError("NP-Map feature dimension must be even")
+
+
+def topk_for_budget(m: int, window: int, chunk: int, n_max: int) -> int:
+    """Certified per-chunk quota (A.4): lambda = floor((m - W) / ceil(N_max / C)),
+    so that T_max * lambda <= m - W for every length up to N_max."""
+    t_max = -(-n_max // chunk)
+    return max(0, (m - window) // t_max)
+
+
+# --------------------------------------------------------------------------
+# NP-Map (Sec. 3.2; reading R-NPMAP)
+# --------------------------------------------------------------------------
+def np_map(x: np.ndarray, P: np.ndarray) -> np.ndarray:
+    """phi(x) for x [..., d] and projection P [d'/2, d]  ->  [..., d']."""
+    x = np.asarray(x, np.float64)
+    u = x @ np.asarray(P, np.float64).T                       # direction source
+    nu = np.linalg.norm(u, axis=-1, keepdims=True)
+    nx = np.linalg.norm(x, axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        z = np.where(nu > 0, nx * u / np.where(nu > 0, nu, 1.0), 0.0)
+    return np.concatenate([_softmax(z), _softmax(-z)], axis=-1)
+
+
+def _softmax(z: np.ndarray) -> np.ndarray:
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Self-Saliency (Sec. 3.1, A.3; reading R-SCORE)
+# --------------------------------------------------------------------------
+def self_saliency(logits: np.ndarray, diag: np.ndarray, eps: float) -> np.ndarray:
+    """Score of each row of ``logits`` [R, K] whose own (diagonal) entry sits
+    in column ``diag[r]``.  Masked-out keys carry -inf and contribute 0.
+
+    a  = softmax over the row (the token's local attention row),
+    a~ = softmax over the row with the diagonal removed (a~_diag = 0),
+    Score = sum_j a_j * ln((a_j + eps) / (a~_j + eps)).
+    """
+    s = np.asarray(logits, np.float64)
+    R = s.shape[0]
+    rows = np.arange(R)
+    a = _masked_softmax(s)
+    s_loo = s.copy()
+    s_loo[rows, diag] = -np.inf
+    a_loo = _masked_softmax(s_loo)
+    term = a * (np.log(a + eps) - np.log(a_loo + eps))
+    return term.sum(axis=1)
+
+
+def _masked_softmax(s: np.ndarray) -> np.ndarray:
+    """Row softmax where -inf entries get weight 0; an all -inf row gives 0."""
+    finite = np.isfinite(s)
+    mx = np.where(finite, s, -np.inf).max(axis=1, keepdims=True)
+    mx = np.where(np.isfinite(mx), mx, 0.0)
+    e = np.where(finite, np.exp(np.where(finite, s, 0.0) - mx), 0.0)
+    tot = e.sum(axis=1, keepdims=True)
+    return np.where(tot > 0, e / np.where(tot > 0, tot, 1.0), 0.0)
+
+
+def window_scores(q: np.ndarray, k: np.ndarray, p: Params, n_kv_heads: int,
+                  per_head: bool = False, block: int = 256) -> np.ndarray:
+    """sigma[b, g, t]: Self-Saliency of every token, averaged over the query
+    heads of KV head g (R-GQA).  The window of query t is
+    J_t = [max(0, t-W+1), t].  With per_head=True returns [B, Hq, N] instead.
+
+    Queries are taken in blocks only to bound memory; each row is still the
+    plain definition over its own window."""
+    B, N, Hq, d = q.shape
+    W = p.window
+    if W <= 0:
+        raise ValueError("scores need a window")
+    G = Hq // n_kv_heads
+    tau = p.tau(d)
+    out = np.zeros((B, Hq, N))
+    for b in range(B):
+        for t0 in range(0, N, block):
+            t1 = min(N, t0 + block)
+            j0 = max(0, t0 - W + 1)
+            keys = np.arange(j0, t1)
+            ts = np.arange(t0, t1)
+            # window mask: j in [t-W+1, t]
+            mask = (keys[None, :] <= ts[:, None]) & (keys[None, :] > ts[:, None] - W)
+            diag = ts - j0
+            for h in range(Hq):
+                g = h // G
+                lg = tau * (q[b, t0:t1, h, :] @ k[b, j0:t1, g, :].T)
+                lg = np.where(mask, lg, -np.inf)
+                out[b, h, t0:t1] = self_saliency(lg, diag, p.eps)
+    if per_head:
+        return out
+    sig = np.zeros((B, n_kv_heads, N))
+    for g in range(n_kv_heads):
+        acc = np.zeros((B, N))
+        for h in range(g * G, (g + 1) * G):      # ascending head order
+            acc = acc + out[:, h, :]
+        sig[:, g, :] = acc / G
+    return sig
+
+
+# --------------------------------------------------------------------------
+# Per-chunk selection (Sec. 3.3 Chunk-Wise Parallel Form; R-SELECT)
+# --------------------------------------------------------------------------
+def rank_order(scores: np.ndarray, positions: np.ndarray) -> np.ndarray:
+    """Indices that sort tokens best-first: higher score, then lower position.
+    -0 is +0 (numpy compares them equal); NaN ranks below everything."""
+    key = np.where(np.isnan(scores), -np.inf, scores)
+    return np.lexsort((positions, -key))
+
+
+def select_chunks(sigma: np.ndarray, p: Params, n_tokens: int | None = None):
+    """Top-lambda per complete chunk.  sigma [B, Hkv, N].
+
+    Returns (sel_idx [B, Hkv, n_full, lambda_eff] ascending positions,
+             route [B, Hkv, N] in {PENDING, ROUTE_SA, ROUTE_LA}).
+    Tokens of the last, incomplete chunk stay PENDING (R-DELAY)."""
+    B, Hkv, N = sigma.shape
+    C, lam = p.chunk, p.topk_eff()
+    n_full = N // C
+    sel = np.zeros((B, Hkv, n_full, lam), np.int64)
+    route = np.full((B, Hkv, N), PENDING, np.uint8)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(n_full):
+                pos = np.arange(c * C, (c + 1) * C)
+                order = rank_order(sigma[b, g, pos], pos)
+                chosen = np.sort(pos[order[:lam]])
+                sel[b, g, c] = chosen
+                route[b, g, pos] = ROUTE_LA
+                route[b, g, chosen] = ROUTE_SA
+    return sel, route
+
+
+def route_from_selection(sel_idx: np.ndarray, N: int, C: int) -> np.ndarray:
+    """Route flags implied by a given selection (used for the near-tie
+    protocol, where the oracle is re-run with another selection)."""
+    B, Hkv, n_full, _ = sel_idx.shape
+    route = np.full((B, Hkv, N), PENDING, np.uint8)
+    route[:, :, : n_full * C] = ROUTE_LA
+    for b in range(B):
+        for g in range(Hkv):
+            route[b, g, sel_idx[b, g].reshape(-1)] = ROUTE_SA
+    return route
+
+
+# --------------------------------------------------------------------------
+# Chunk-parallel forward, direct per-query form (Sec. 3.3; R-DELAY, R-AGG)
+# --------------------------------------------------------------------------
+def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None):
+    """Hybrid attention output from the explicit per-query index sets.
+
+    q [B,N,Hq,d], k/v [B,N,Hkv,d], wq/wk [Hkv, d'/2, d]  (float64 views).
+    rows: optional list of (b, t) to evaluate (default: every query).
+    sel_override: optional sel_idx [B,Hkv,N//C,lambda] to route with instead
+    of the oracle's own selection (near-tie protocol).
+
+    Returns dict(out [B,N,Hq,d] (NaN where not evaluated), scores, sel_idx, route).
+
+    For query t of head h (KV head g):
+      J_t  = [max(0, t-W+1), t]                       window (softmax)
+      R_t  = {j <= t-W}                               routed region
+      SA_t = J_t  U  {j in R_t : route_j = SA}        exp(tau q.k) weights
+      LA_t = R_t \\ SA_t                              phi_q(q).phi_k(k) weights
+      out  = sum_{SA_t u LA_t} w_j v_j / sum w_j
+    """
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    validate(p, Hq, Hkv, 2 * wq.shape[1])
+    G = Hq // Hkv
+    W, tau = p.window, p.tau(d)
+
+    if W > 0:
+        sigma = window_scores(q, k, p, Hkv)
+    else:
+        sigma = np.zeros((B, Hkv, N))
+    if p.topk_eff() > 0:
+        sel_idx, route = select_chunks(sigma, p)
+        if sel_override is not None:
+            sel_idx = np.asarray(sel_override, np.int64)
+            route = route_from_selection(sel_idx, N, p.chunk)
+    else:
+        sel_idx = np.zeros((B, Hkv, N // p.chunk, 0), np.int64)
+        route = np.full((B, Hkv, N), ROUTE_LA, np.uint8)
+
+    phik = np.stack([np_map(k[:, :, g, :], wk[g]) for g in range(Hkv)], axis=2)  # [B,N,Hkv,d']
+
+    out = np.full(q.shape, np.nan)
+    if rows is None:
+        rows = [(b, t) for b in range(B) for t in range(N)]
+    for b, t in rows:
+        r_end = t - W + 1                       # R_t = [0, r_end)
+        for g in range(Hkv):
+            win = np.arange(max(0, t - W + 1), t + 1) if W > 0 else np.arange(0)
+            routed = np.arange(0, max(0, r_end))
+            if routed.size:
+                rr = route[b, g, routed]
+                if np.any(rr == PENDING):
+                    raise AssertionError("a routed token has no decision")
+                sa_routed = routed[rr == ROUTE_SA]
+                la_routed = routed[rr == ROUTE_LA]
+            else:
+                sa_routed = la_routed = routed
+            sa = np.concatenate([sa_routed, win])
+            for h in range(g * G, (g + 1) * G):
+                qv = q[b, t, h]
+                s = tau * (k[b, sa, g, :] @ qv)
+                w_la = phik[b, la_routed, g, :] @ np_map(qv, wq[g]) if la_routed.size else np.zeros(0)
+                # shared normaliser; subtracting M = max(0, max s) changes nothing
+                M = max(0.0, s.max()) if s.size else 0.0
+                w_sa = np.exp(s - M)
+                w_la = w_la * math.exp(-M)
+                num = w_sa @ v[b, sa, g, :] + (w_la @ v[b, la_routed, g, :] if la_routed.size else 0.0)
+                den = w_sa.sum() + w_la.sum()
+                out[b, t, h] = num / den
+    return dict(out=out, scores=sigma, sel_idx=sel_idx, route=route)
+
+
+# --------------------------------------------------------------------------
+# Recurrent (decode) form (Sec. 3.3 Recurrent Form; A.2 state recurrence)
+# --------------------------------------------------------------------------
+def new_cache(B, Hkv, d, feat_dim, p: Params, cap: int) -> dict:
+    """Empty decode cache, laid out like the library's cache tensors."""
+    W, C = p.window, p.chunk
+    return dict(
+        win_k=np.zeros((B, Hkv, max(W, 1), d)), win_v=np.zeros((B, Hkv, max(W, 1), d)),
+        win_route=np.zeros((B, Hkv, max(W, 1)), np.uint8),
+        pend_score=np.zeros((B, Hkv, C)),
+        sel_k=np.zeros((B, Hkv, cap, d)), sel_v=np.zeros((B, Hkv, cap, d)),
+        sel_count=np.zeros((B, Hkv), np.int64),
+        lin_S=np.zeros((B, Hkv, feat_dim, d)), lin_z=np.zeros((B, Hkv, feat_dim)),
+        pos=0,
+    )
+
+
+def decode_step(cache: dict, q_t, k_t, v_t, wq, wk, p: Params, sel_override=None):
+    """One recurrent step at position t = cache['pos'] for every sequence.
+
+    q_t [B,Hq,d], k_t/v_t [B,Hkv,d].  Mutates the cache; returns out [B,Hq,d].
+
+    Steps per (b, g):
+      1. token j = t-W leaves the window: SA -> appended to the selected
+         list (kept forever); LA -> S += phi_k(k_j) v_j^T, z += phi_k(k_j).
+         With W = 0 the incoming token itself is that token.
+      2. k_t, v_t enter the window ring at slot t mod W.
+      3. Self-Saliency of t from its window row, mean over the group's
+         heads -> pending score slot t mod C.
+      4. Output over window + selected list (softmax weights) and the
+         linear state (phi weights), one shared normaliser.
+      5. If t closes its chunk, pick the chunk's top-lambda: those tokens
+         are marked SA, the others LA.
+    """
+    q_t, k_t, v_t = (np.asarray(a, np.float64) for a in (q_t, k_t, v_t))
+    B, Hq, d = q_t.shape
+    Hkv = k_t.shape[1]
+    G = Hq // Hkv
+    W, C, lam = p.window, p.chunk, p.topk_eff()
+    tau = p.tau(d)
+    t = cache["pos"]
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        for g in range(Hkv):
+            # 1. eviction
+            if W == 0:
+                ev = (k_t[b, g], v_t[b, g], ROUTE_LA)
+            elif t - W >= 0:
+                slot = (t - W) % W
+                r = ROUTE_LA if lam == 0 else cache["win_route"][b, g, slot]
+                if r == PENDING:
+                    raise AssertionError("token left the window before its chunk was decided")
+                ev = (cache["win_k"][b, g, slot].copy(), cache["win_v"][b, g, slot].copy(), r)
+            else:
+                ev = None
+            if ev is not None:
+                kj, vj, r = ev
+                if r == ROUTE_SA:
+                    n = cache["sel_count"][b, g]
+                    if n >= cache["sel_k"].shape[2]:
+                        raise OverflowError("selected cache is full")
+                    cache["sel_k"][b, g, n] = kj
+                    cache["sel_v"][b, g, n] = vj
+                    cache["sel_count"][b, g] = n + 1
+                else:
+                    f = np_map(kj, wk[g])
+                    cache["lin_S"][b, g] += np.outer(f, vj)
+                    cache["lin_z"][b, g] += f
+            # 2. window write
+            if W > 0:
+                cache["win_k"][b, g, t % W] = k_t[b, g]
+                cache["win_v"][b, g, t % W] = v_t[b, g]
+                cache["win_route"][b, g, t % W] = PENDING
+                win_pos = np.arange(max(0, t - W + 1), t + 1)
+                slots = win_pos % W
+                wk_ = cache["win_k"][b, g, slots]
+                wv_ = cache["win_v"][b, g, slots]
+            n = cache["sel_count"][b, g]
+            sk, sv = cache["sel_k"][b, g, :n], cache["sel_v"][b, g, :n]
+            score_sum = 0.0
+            for h in range(g * G, (g + 1) * G):
+                qv = q_t[b, h]
+                if W > 0:
+                    lw = tau * (wk_ @ qv)
+                    score_sum += self_saliency(lw[None, :], np.array([len(lw) - 1]), p.eps)[0]
+                    s = np.concatenate([tau * (sk @ qv), lw])
+                    vv = np.concatenate([sv, wv_])
+                else:
+                    s = tau * (sk @ qv)
+                    vv = sv
+                fq = np_map(qv, wq[g])
+                M = max(0.0, s.max()) if s.size else 0.0
+                w_sa = np.exp(s - M)
+                num = w_sa @ vv + math.exp(-M) * (fq @ cache["lin_S"][b, g])
+                den = w_sa.sum() + math.exp(-M) * (fq @ cache["lin_z"][b, g])
+                out[b, h] = num / den
+            # 3. pending score
+            if W > 0:
+                cache["pend_score"][b, g, t % C] = score_sum / G
+            # 5. chunk end
+            if W > 0 and t % C == C - 1:
+                pos = np.arange(t - C + 1, t + 1)
+                if lam > 0:
+                    order = rank_order(cache["pend_score"][b, g, pos % C], pos)
+                    chosen = set(pos[order[:lam]].tolist())
+                else:
+                    chosen = set()
+                if sel_override is not None:
+                    chosen = set(np.asarray(sel_override[b, g, t // C]).tolist())
+                for j in pos:
+                    cache["win_route"][b, g, j % W] = ROUTE_SA if j in chosen else ROUTE_LA
+    cache["pos"] = t + 1
+    return out
+
+
+def fwd_recurrent(q, k, v, wq, wk, p: Params, cap: int | None = None, sel_override=None):
+    """Run the recurrent form token by token from an empty cache.
+    Returns (out [B,N,Hq,d], cache after N tokens)."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    validate(p, Hq, Hkv, 2 * wq.shape[1])
+    if cap is None:
+        cap = p.topk_eff() * (-(-N // p.chunk)) + 1
+    cache = new_cache(B, Hkv, d, 2 * wq.shape[1], p, cap)
+    out = np.zeros(q.shape)
+    for t in range(N):
+        out[:, t] = decode_step(cache, q[:, t], k[:, t], v[:, t], wq, wk, p, sel_override)
+    return out, cache
