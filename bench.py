@@ -1,0 +1,285 @@
+"""Benchmark of the STILL hybrid-attention layer on one MI355X.
+
+One step = one whole forward of the operator (window scores, per-chunk
+selection, sparse softmax + NP-Map linear attention, aggregation) over the
+Llama-3-8B-shaped 16K-token prefill (batch 1, 32 query / 8 KV heads,
+head_dim 128, window = chunk = 64, top-32 per chunk, bf16 storage with fp32
+accumulation), inputs resident in HBM.  The decode step (batch 64 at
+position 16384) is timed the same way and reported in the "decode" object.
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
+the launch stream by the library's *_timed entry points; the roofline uses
+the dominant kernel's algorithmic work per launch over its average duration.
+The CPU baseline is the float64 oracle on a bounded sample of the same
+workload, timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "hybrid-attn layer tokens/s (Llama-3-8B shape, 16K prefill; decode) + % roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (counted once per mathematical operation; exp/log excluded)
+# ---------------------------------------------------------------------------
+def prefill_flops(cfg: dict, sel_idx: np.ndarray) -> dict:
+    B, N, Hq, Hkv = cfg["batch"], cfg["seqlen"], cfg["n_q_heads"], cfg["n_kv_heads"]
+    d = cfg["head_dim"]
+    fd = d
+    W, C = cfg["window"], cfg["chunk"]
+    G = Hq // Hkv
+    t = np.arange(N)
+    win_pairs = float(np.minimum(t + 1, W).sum()) * Hq * B
+    r_end = np.maximum(0, t - W + 1)
+    sel_pairs = 0.0
+    for b in range(B):
+        for g in range(Hkv):
+            pos = np.sort(sel_idx[b, g].reshape(-1))
+            sel_pairs += float(np.searchsorted(pos, r_end, side="left").sum()) * G
+    per_qh_la = 2 * fd * d + 2 * C * fd + 2 * C * d + 2 * fd
+    return dict(
+        win=4.0 * d * win_pairs,                     # QK^T + PV over window pairs
+        sel=4.0 * d * sel_pairs,                     # QK^T + PV over visible selected pairs
+        la_read=float(per_qh_la) * N * Hq * B,       # phi_q.P + intra-chunk LA block
+        np_q=float(fd * d) * N * Hq * B,             # NP-Map projection of queries
+        np_k=float(fd * d) * N * Hkv * B,            # NP-Map projection of keys
+        la_state=float(2 * fd * d + 2 * fd) * N * Hkv * B,   # per-chunk phi_k^T V, z
+        score_qk=2.0 * d * win_pairs,                # window logits for the scores
+    )
+
+
+KERNEL_FLOPS = {
+    # kernel launch name -> which algorithmic terms that kernel computes
+    "main_general": ("win", "sel", "la_read"),
+    "hybrid_main": ("win", "sel", "la_read", "np_q"),
+}
+
+
+def decode_bytes(cfg: dict, sel_count: np.ndarray) -> dict:
+    """HBM bytes of one decode step that the method must move."""
+    d, W, Hq, Hkv, B = cfg["head_dim"], cfg["window"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["batch"]
+    e = 2  # bf16
+    sel = float(sel_count.sum()) * 2 * d * e             # selected K and V rows
+    ring = float(B * Hkv) * W * 2 * d * e
+    state = float(B * Hkv) * (d * d + d) * 4 * 2          # S, z read + (LA eviction) write
+    qo = float(B * Hq) * d * e * 2 + float(B * Hkv) * 2 * d * e
+    return dict(sel=sel, ring=ring, state=state, qo=qo, total=sel + ring + state + qo)
+
+
+# ---------------------------------------------------------------------------
+def bench_prefill(still, torch, name, steps, warmup):
+    cfg = workloads.CONFIGS[name]
+    seed = workloads.seed_of(name)
+    t0 = time.time()
+    raw = workloads.make_prefill(cfg, seed)
+    dev = {k: torch.from_numpy(raw[k]).to(torch.bfloat16).cuda() for k in ("q", "k", "v")}
+    for k in ("wphi_q", "wphi_k"):
+        dev[k] = torch.from_numpy(raw[k]).cuda()
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    kw = dict(window=W, chunk=C, topk=lam)
+    out = torch.empty_like(dev["q"])
+    sh = still.make_shape(batch=cfg["batch"], seqlen=cfg["seqlen"], n_q_heads=cfg["n_q_heads"],
+                          n_kv_heads=cfg["n_kv_heads"], head_dim=cfg["head_dim"], **kw)
+    ws = torch.empty(still.fwd_workspace_size(sh), dtype=torch.uint8, device="cuda")
+    args = (dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"])
+    first = still.fwd(*args, **kw, return_sel=True, workspace=ws)
+    sel_idx = first["sel_idx"].cpu().numpy()
+    for _ in range(warmup):
+        still.fwd(*args, **kw, out=out, workspace=ws)
+    timers = [still.LaunchTimer() for _ in range(steps)]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        still.fwd(*args, **kw, out=out, workspace=ws, timer=timers[i])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per = {}
+    for tm in timers:
+        for kname, dur in tm.durations_ms():
+            per.setdefault(kname, []).append(dur)
+    kern = {k: float(np.mean(v)) for k, v in per.items()}
+    log(f"[bench] {name}: {ms:.3f} ms/step; kernels (ms): " +
+        ", ".join(f"{k}={v:.3f}" for k, v in kern.items()))
+    flops = prefill_flops(cfg, sel_idx)
+    dom = max(kern, key=kern.get)
+    terms = KERNEL_FLOPS.get(dom)
+    roof = None
+    if terms:
+        alg = sum(flops[t] for t in terms)
+        achieved = alg / (kern[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "kernel": dom, "avg_ms": round(kern[dom], 4),
+                "algorithmic_flop_per_launch": alg}
+    total_alg = sum(v for k, v in flops.items() if k != "score_qk")
+    return dict(cfg=cfg, raw=raw, ms=ms, kern=kern, roof=roof, flops=flops,
+                total_alg=total_alg, tokens=cfg["batch"] * cfg["seqlen"])
+
+
+def bench_decode(still, torch, steps, warmup):
+    name = "decode_b64_16k"
+    cfg = workloads.CONFIGS[name]
+    seed = workloads.seed_of(name)
+    B, Hq, Hkv, d = cfg["batch"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    t0 = time.time()
+    full = workloads.make_decode_cache(cfg, seed)
+    cache = still.DecodeCache(batch=B, n_kv_heads=Hkv, head_dim=d, window=cfg["window"],
+                              chunk=cfg["chunk"], topk=cfg["topk"], sel_cap=cfg["sel_cap"],
+                              pos=cfg["pos"])
+    for key, arr in full.items():
+        t = getattr(cache, key)
+        t.copy_(torch.from_numpy(arr).to(t.dtype))
+    del full
+    n_tok = warmup + steps
+    toks = workloads.make_decode_tokens(cfg, seed, n_tok)
+    q = torch.from_numpy(toks["q"]).to(torch.bfloat16).cuda()
+    k = torch.from_numpy(toks["k"]).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(toks["v"]).to(torch.bfloat16).cuda()
+    wq = torch.from_numpy(toks["wphi_q"]).cuda()
+    wk = torch.from_numpy(toks["wphi_k"]).cuda()
+    log(f"[bench] {name}: cache ready in {time.time() - t0:.1f}s")
+    sh = still.make_shape(batch=B, seqlen=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                          window=cfg["window"], chunk=cfg["chunk"], topk=cfg["topk"])
+    ws = torch.empty(still.decode_workspace_size(sh, cfg["sel_cap"]), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, 1, Hq, d), dtype=torch.bfloat16, device="cuda")
+    qs = [q[i][:, None].contiguous() for i in range(n_tok)]
+    ks = [k[i][:, None].contiguous() for i in range(n_tok)]
+    vs = [v[i][:, None].contiguous() for i in range(n_tok)]
+    for i in range(warmup):
+        still.decode_step(qs[i], ks[i], vs[i], wq, wk, cache, out=out, workspace=ws)
+    sel_before = cache.sel_count.cpu().numpy().copy()
+    timers = [still.LaunchTimer() for _ in range(steps)]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        j = warmup + i
+        still.decode_step(qs[j], ks[j], vs[j], wq, wk, cache, out=out, workspace=ws, timer=timers[i])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    sel_after = cache.sel_count.cpu().numpy()
+    per = {}
+    for tm in timers:
+        for kname, dur in tm.durations_ms():
+            per.setdefault(kname, []).append(dur)
+    kern = {k: float(np.mean(v)) for k, v in per.items()}
+    log(f"[bench] {name}: {ms:.3f} ms/step; kernels (ms): " +
+        ", ".join(f"{k}={v:.3f}" for k, v in kern.items()))
+    mid = (sel_before.astype(np.float64) + sel_after) / 2
+    by = decode_bytes(cfg, mid)
+    dom = max(kern, key=kern.get)
+    dom_bytes = by["sel"] + float(B * Hq) * d * 2 if dom.startswith("decode_sel") else by["total"]
+    achieved = dom_bytes / (kern[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+            "avg_ms": round(kern[dom], 4), "algorithmic_bytes_per_launch": dom_bytes}
+    step_gbs = by["total"] / (ms * 1e-3) / 1e9
+    return {"metric": "decode tokens/s (batch 64 at position 16384)", "value": round(B / (ms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+            "config": {"workload": "decode_b64_16k: batch 64, one token per sequence at position "
+                       "16384, 32 q / 8 KV heads, d 128, window 64, chunk 64, top-32, "
+                       "8160 selected rows per (sequence, KV head), fp32 128x128 state",
+                       "batch": B, "pos": cfg["pos"]},
+            "step_algorithmic_bytes": by["total"], "step_GBps": round(step_gbs, 1),
+            "kernels_ms": {k: round(v, 4) for k, v in kern.items()}, "roofline": roof}
+
+
+def cpu_baseline(raw, cfg, n_rows=12):
+    """The oracle as it stands, on a bounded sample: group scores and
+    selection over the whole sequence, then n_rows output rows evaluated one
+    by one; tokens/s extrapolates the per-row cost to every row."""
+    import oracle as O
+    import torch
+    from threadpoolctl import threadpool_info
+
+    ref = {}
+    for key in ("q", "k", "v"):
+        ref[key] = torch.from_numpy(raw[key]).to(torch.bfloat16).double().numpy()
+    wq, wk = raw["wphi_q"].astype(np.float64), raw["wphi_k"].astype(np.float64)
+    p = O.Params(window=cfg["window"], chunk=cfg["chunk"], topk=cfg["topk"])
+    B, N = cfg["batch"], cfg["seqlen"]
+    t0 = time.perf_counter()
+    sigma = O.window_scores(ref["q"], ref["k"], p, cfg["n_kv_heads"])
+    O.select_chunks(sigma, p)
+    t1 = time.perf_counter()
+    rows = [(0, int(t)) for t in np.linspace(0, N - 1, n_rows).round()]
+    O.fwd_direct(ref["q"], ref["k"], ref["v"], wq, wk, p, rows=rows, scores=sigma)
+    t2 = time.perf_counter()
+    per_row = (t2 - t1) / len(rows)
+    est = (t1 - t0) + per_row * B * N
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(B * N / est, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"float64 numpy oracle: scores+selection over all {B * N} tokens "
+                       f"({t1 - t0:.1f}s) plus {len(rows)} output rows evaluated one by one "
+                       f"({t2 - t1:.1f}s), per-row cost extrapolated to all {B * N} rows; "
+                       f"BLAS threads {threads}, elementwise numpy single-threaded")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_16k", choices=["prefill_4k", "prefill_16k", "train_8x2k"])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the STILL operator here runs on a single MI355X "
+              f"(no sharding or collectives are built); --gpus {args.gpus} is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from hybrid_sparse_softmax_amd import still
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    still.lib()
+    pre = bench_prefill(still, torch, args.workload, args.steps, args.warmup)
+    cfg = pre["cfg"]
+    dec = None if args.no_decode else bench_decode(still, torch, args.steps, args.warmup)
+    cpu = None if args.no_cpu else cpu_baseline(pre["raw"], cfg)
+    tok_s = pre["tokens"] / (pre["ms"] * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: batch {cfg['batch']}, seq {cfg['seqlen']}, "
+                               f"{cfg['n_q_heads']} q / {cfg['n_kv_heads']} KV heads, d {cfg['head_dim']}, "
+                               f"window {cfg['window']}, chunk {cfg['chunk']}, top-{cfg['topk']} per chunk",
+                   "batch": cfg["batch"], "seq_len": cfg["seqlen"]},
+        "roofline": pre["roof"],
+        "cpu_baseline": cpu,
+        "whole_step_TFLOPs": round(pre["total_alg"] / (pre["ms"] * 1e-3) / 1e12, 2),
+        "kernels_ms": {k: round(v, 4) for k, v in pre["kern"].items()},
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

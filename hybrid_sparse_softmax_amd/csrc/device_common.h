@@ -1,0 +1,59 @@
+// Device helpers shared by the STILL kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace still {
+
+constexpr int kWave = 64;
+
+// route flag bytes (same values as the cache's win_route)
+constexpr uint8_t kPending = 0, kRouteSA = 1, kRouteLA = 2;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+    return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
+// Sort key of a routing score: -0 counts as +0 and NaN ranks below every
+// number, so that float comparison of keys gives the selection order.
+__device__ __forceinline__ float route_key(float s) {
+    if (s != s) return -__builtin_inff();
+    return s == 0.0f ? 0.0f : s;
+}
+
+// One Self-Saliency term.  For the diagonal (own) key:
+//   a_t ln((a_t + eps)/eps) = a_t log1p(a_t / eps).
+// For another key j of the row, with e_j the unnormalised weight, sa the row
+// sum and so the row sum without the diagonal (a~_j = e_j / so):
+//   a_j ln((a_j + eps)/(a~_j + eps)) = -a_j log1p((a~_j - a_j)/(a_j + eps)),
+//   a~_j - a_j = e_j e_t / (so sa)  (no cancellation).
+__device__ __forceinline__ float saliency_term(float e, bool is_diag, float et, float sa, float so,
+                                               float eps) {
+    if (e == 0.0f) return 0.0f;
+    float a = e / sa;
+    if (is_diag) return a * log1pf(a / eps);
+    float diff = (e * et) / (so * sa);
+    return -a * log1pf(diff / (a + eps));
+}
+
+}  // namespace still

@@ -1,0 +1,70 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace still {
+
+// Validated problem dimensions.
+struct Dims {
+    int B, N, Hq, Hkv, G, d, fd;  // fd = NP-Map feature size d'
+    int W, C, lam;                // lam = min(topk, C)
+    int T;                        // ceil(N / C)
+    int n_full;                   // N / C complete chunks
+    float eps, tau;
+    bool bf16;
+};
+
+// Cache pointers as the kernels see them.
+struct CacheView {
+    void *win_k, *win_v;
+    uint8_t* win_route;
+    float* pend;
+    void *sel_k, *sel_v;
+    int32_t* sel_count;
+    int32_t cap;
+    float *lin_S, *lin_z;
+    int64_t pos;
+};
+
+// ---- general kernels (any supported shape, f32 or bf16 storage) ----------
+// phi[tok, h, :] = NP-Map of x[tok, h, :] with projection P[h / heads_per_proj]
+hipError_t launch_phi(const Dims& D, const void* x, int H, int heads_per_proj, const float* P,
+                      float* phi, hipStream_t s);
+// per-query-head Self-Saliency hs[b, h, t]
+hipError_t launch_head_scores(const Dims& D, const void* q, const void* k, float* hs, hipStream_t s);
+// group mean, per-chunk top-k, route flags, selected positions
+hipError_t launch_select(const Dims& D, const float* hs, float* scores, int32_t* sel_idx,
+                         uint8_t* route, hipStream_t s);
+// per-chunk linear-attention sums (S then z, fd*(d+1) floats per chunk), then
+// in-place inclusive prefix over chunks; optional fp32 copy of chunk `cap_chunk`
+hipError_t launch_la_chunks(const Dims& D, const float* phik, const void* v, const uint8_t* route,
+                            float* lin, hipStream_t s);
+hipError_t launch_la_scan(const Dims& D, float* lin, int cap_chunk, float* cap_S, float* cap_z,
+                          hipStream_t s);
+// hybrid output, one wave per (b, t, h)
+hipError_t launch_main_general(const Dims& D, const void* q, const void* k, const void* v,
+                               const float* phiq, const float* phik, const uint8_t* route,
+                               const int32_t* sel_idx, const float* lin, void* out, hipStream_t s);
+// prefill -> decode cache hand-off (after the scan wrote chunk cap_chunk into lin_S / lin_z)
+hipError_t launch_handoff(const Dims& D, const void* k, const void* v, const float* wphi_k,
+                          const float* scores, const int32_t* sel_idx, const uint8_t* route,
+                          int cap_chunk, const CacheView& c, hipStream_t s);
+
+// ---- decode step ------------------------------------------------------------
+struct DecodeWork {
+    float* la;      // [B, Hq, d + 1]   linear numerator, denominator
+    float* win;     // [B, Hq, d + 2]   window partial (m, l, acc)
+    float* part;    // [B, Hq, splits, d + 2] selected-list partials
+    int splits;
+    int rows_per_split;
+};
+hipError_t launch_decode_prep(const Dims& D, const void* q, const void* k, const void* v,
+                              const float* wphi_q, const float* wphi_k, const CacheView& c,
+                              const DecodeWork& w, hipStream_t s);
+hipError_t launch_decode_sel(const Dims& D, const void* q, const CacheView& c, const DecodeWork& w,
+                             hipStream_t s);
+hipError_t launch_decode_combine(const Dims& D, const DecodeWork& w, void* out, hipStream_t s);
+
+}  // namespace still

@@ -1,0 +1,368 @@
+// C-ABI layer of libstill: host-side validation, workspace carving and the
+// launch sequence of each entry point.  Declarations and contracts are in
+// include/still.h.
+#include "still.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "launch.h"
+
+namespace still {
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int check_shape(const still_shape* sh, bool decode) {
+    if (!sh) return STILL_ERR_INVALID_ARG;
+    if (sh->batch < 0 || sh->seqlen < 0) return STILL_ERR_INVALID_ARG;
+    if (sh->n_q_heads < 1 || sh->n_kv_heads < 1) return STILL_ERR_INVALID_ARG;
+    if (sh->n_q_heads % sh->n_kv_heads) return STILL_ERR_INVALID_ARG;
+    if (sh->window < 0 || sh->chunk < 1 || sh->topk < 0) return STILL_ERR_INVALID_ARG;
+    if (sh->window == 0 && sh->topk > 0) return STILL_ERR_INVALID_ARG;
+    if (sh->topk > 0 && sh->window < sh->chunk) return STILL_ERR_INVALID_ARG;
+    if (!(sh->eps > 0.f) || !std::isfinite(sh->eps)) return STILL_ERR_INVALID_ARG;
+    if (!(sh->softmax_scale >= 0.f) || !std::isfinite(sh->softmax_scale)) return STILL_ERR_INVALID_ARG;
+    if (sh->dtype != STILL_F32 && sh->dtype != STILL_BF16) return STILL_ERR_INVALID_ARG;
+    if (sh->head_dim < 1 || sh->feat_dim < 2 || (sh->feat_dim & 1)) return STILL_ERR_INVALID_ARG;
+    if (sh->flags & ~STILL_FLAG_GENERAL_KERNELS) return STILL_ERR_INVALID_ARG;
+    // built variants
+    if (sh->head_dim != 64 && sh->head_dim != 128) return STILL_ERR_UNSUPPORTED;
+    if (sh->feat_dim != sh->head_dim) return STILL_ERR_UNSUPPORTED;
+    if (sh->n_q_heads / sh->n_kv_heads > 8) return STILL_ERR_UNSUPPORTED;
+    if (sh->window > 1024 || sh->chunk > 1024) return STILL_ERR_UNSUPPORTED;
+    (void)decode;
+    return STILL_OK;
+}
+
+static Dims make_dims(const still_shape* sh, int seqlen) {
+    Dims D;
+    D.B = sh->batch;
+    D.N = seqlen;
+    D.Hq = sh->n_q_heads;
+    D.Hkv = sh->n_kv_heads;
+    D.G = D.Hq / D.Hkv;
+    D.d = sh->head_dim;
+    D.fd = sh->feat_dim;
+    D.W = sh->window;
+    D.C = sh->chunk;
+    D.lam = sh->topk < sh->chunk ? sh->topk : sh->chunk;
+    D.T = (seqlen + D.C - 1) / D.C;
+    D.n_full = seqlen / D.C;
+    D.eps = sh->eps;
+    D.tau = sh->softmax_scale > 0.f ? sh->softmax_scale : 1.0f / std::sqrt((float)D.d);
+    D.bf16 = sh->dtype == STILL_BF16;
+    return D;
+}
+
+static size_t elem_size(const Dims& D) { return D.bf16 ? 2 : 4; }
+
+// Bump allocator over the caller's workspace; 256-byte aligned pieces.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+    template <typename X> X* take(size_t count) {
+        off = (off + 255) & ~size_t(255);
+        X* p = base ? reinterpret_cast<X*>(base + off) : nullptr;
+        off += count * sizeof(X);
+        return p;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+struct FwdBuffers {
+    float *phiq, *phik, *hs, *scores, *lin;
+    int32_t* sel;
+    uint8_t* route;
+};
+
+static FwdBuffers carve_fwd(const Dims& D, Carver& cv) {
+    FwdBuffers f;
+    const size_t BN = (size_t)D.B * D.N;
+    f.phiq = cv.take<float>(BN * D.Hq * D.fd);
+    f.phik = cv.take<float>(BN * D.Hkv * D.fd);
+    f.hs = cv.take<float>((size_t)D.B * D.Hq * D.N);
+    f.scores = cv.take<float>((size_t)D.B * D.Hkv * D.N);
+    f.sel = cv.take<int32_t>((size_t)D.B * D.Hkv * D.n_full * D.lam);
+    f.route = cv.take<uint8_t>((size_t)D.B * D.Hkv * D.N);
+    f.lin = cv.take<float>((size_t)D.B * D.Hkv * D.T * D.fd * (D.d + 1));
+    return f;
+}
+
+static size_t fwd_bytes(const Dims& D) {
+    Carver cv(nullptr);
+    carve_fwd(D, cv);
+    return cv.off + 256;
+}
+
+static int check_cache(const Dims& D, const still_cache* c, int64_t pos, int64_t need_sel) {
+    if (!c) return STILL_ERR_INVALID_ARG;
+    if (c->pos != pos && pos >= 0) return STILL_ERR_INVALID_ARG;
+    if (c->pos < 0) return STILL_ERR_INVALID_ARG;
+    if (!c->lin_S || !c->lin_z) return STILL_ERR_INVALID_ARG;
+    if (D.W > 0 && (!c->win_k || !c->win_v || !c->win_route || !c->pend_score))
+        return STILL_ERR_INVALID_ARG;
+    if (D.W > 0 && (!aligned16(c->win_k) || !aligned16(c->win_v))) return STILL_ERR_INVALID_ARG;
+    if (D.lam > 0) {
+        if (!c->sel_k || !c->sel_v || !c->sel_count || c->sel_cap < 0) return STILL_ERR_INVALID_ARG;
+        if (!aligned16(c->sel_k) || !aligned16(c->sel_v)) return STILL_ERR_INVALID_ARG;
+        if (need_sel > c->sel_cap) return STILL_ERR_CAPACITY;
+    }
+    return STILL_OK;
+}
+
+static CacheView view_of(const still_cache* c) {
+    CacheView v;
+    v.win_k = c->win_k;
+    v.win_v = c->win_v;
+    v.win_route = c->win_route;
+    v.pend = c->pend_score;
+    v.sel_k = c->sel_k;
+    v.sel_v = c->sel_v;
+    v.sel_count = c->sel_count;
+    v.cap = c->sel_cap;
+    v.lin_S = c->lin_S;
+    v.lin_z = c->lin_z;
+    v.pos = c->pos;
+    return v;
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return a <= 0 ? 0 : (a + b - 1) / b; }
+
+#define STILL_TRY(expr)                                \
+    do {                                               \
+        if ((expr) != hipSuccess) return STILL_ERR_HIP; \
+    } while (0)
+
+// Optional per-launch events (the *_timed entry points).
+struct Timeline {
+    hipEvent_t* ev = nullptr;
+    int max_ev = 0;
+    int n = 0;
+    const char** names = nullptr;
+    hipError_t mark(hipStream_t s, const char* name) {
+        if (ev) {
+            if (names) names[n] = name;
+            hipError_t e = hipEventRecord(ev[n], s);
+            ++n;
+            return e;
+        }
+        ++n;
+        return hipSuccess;
+    }
+    hipError_t end(hipStream_t s) { return ev ? hipEventRecord(ev[n], s) : hipSuccess; }
+};
+#define STILL_LAUNCH(tl, s, name, expr)       \
+    do {                                      \
+        STILL_TRY((tl).mark((s), (name)));    \
+        STILL_TRY(expr);                      \
+    } while (0)
+
+static int fwd_launches(const Dims& D, bool with_cache) {
+    return 6 + (D.W > 0 ? 1 : 0) + (with_cache ? 1 : 0);
+}
+
+static int fwd(const still_shape* sh, const void* q, const void* k, const void* v,
+               const float* wq, const float* wk, void* out, float* scores_opt,
+               int32_t* sel_idx_opt, still_cache* cache, void* ws, size_t ws_bytes,
+               hipStream_t s, Timeline& tl) {
+    int st = check_shape(sh, false);
+    if (st) return st;
+    const Dims D = make_dims(sh, sh->seqlen);
+    if (D.B == 0 || D.N == 0) return STILL_OK;  // nothing to compute; pointers unused
+    if (!q || !k || !v || !wq || !wk || !out) return STILL_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(wq) ||
+        !aligned16(wk))
+        return STILL_ERR_INVALID_ARG;
+    if (cache) {
+        const int64_t need = D.lam * ceil_div((int64_t)D.N - D.W, D.C);
+        st = check_cache(D, cache, D.N, need);
+        if (st) return st;
+    }
+    const size_t need_ws = fwd_bytes(D);
+    if (!ws || ws_bytes < need_ws) return STILL_ERR_WORKSPACE;
+    if (tl.ev && tl.max_ev < fwd_launches(D, cache != nullptr) + 1) return STILL_ERR_INVALID_ARG;
+
+    void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    Carver cv(wsa);
+    FwdBuffers f = carve_fwd(D, cv);
+    float* scores = scores_opt ? scores_opt : f.scores;
+    int32_t* sel = sel_idx_opt ? sel_idx_opt : f.sel;
+
+    STILL_LAUNCH(tl, s, "phi_q", launch_phi(D, q, D.Hq, D.G, wq, f.phiq, s));
+    STILL_LAUNCH(tl, s, "phi_k", launch_phi(D, k, D.Hkv, 1, wk, f.phik, s));
+    if (D.W > 0) STILL_LAUNCH(tl, s, "head_scores", launch_head_scores(D, q, k, f.hs, s));
+    STILL_LAUNCH(tl, s, "select", launch_select(D, f.hs, scores, sel, f.route, s));
+    STILL_LAUNCH(tl, s, "la_chunk", launch_la_chunks(D, f.phik, v, f.route, f.lin, s));
+    // the hand-off's linear state covers tokens j <= N-1-W: chunks below
+    // floor((N-W)/C) in full, captured by the scan
+    const int cap_chunk = cache ? (D.N > D.W ? D.N - D.W : 0) / D.C - 1 : -1;
+    STILL_LAUNCH(tl, s, "la_scan", launch_la_scan(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
+                                                  cache ? cache->lin_z : nullptr, s));
+    STILL_LAUNCH(tl, s, "main_general",
+                 launch_main_general(D, q, k, v, f.phiq, f.phik, f.route, sel, f.lin, out, s));
+    if (cache)
+        STILL_LAUNCH(tl, s, "handoff",
+                     launch_handoff(D, k, v, wk, scores, sel, f.route, cap_chunk, view_of(cache), s));
+    STILL_TRY(tl.end(s));
+    return STILL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------
+static constexpr int kRowsPerSplit = 256;
+
+static DecodeWork carve_decode(const Dims& D, int cap, Carver& cv) {
+    DecodeWork w;
+    w.rows_per_split = kRowsPerSplit;
+    w.splits = D.lam > 0 ? (int)ceil_div(cap, kRowsPerSplit) : 0;
+    w.la = cv.take<float>((size_t)D.B * D.Hq * (D.d + 1));
+    w.win = cv.take<float>((size_t)D.B * D.Hq * (D.d + 2));
+    w.part = cv.take<float>((size_t)D.B * D.Hq * (w.splits > 0 ? w.splits : 1) * (D.d + 2));
+    return w;
+}
+
+static size_t decode_bytes(const Dims& D, int cap) {
+    Carver cv(nullptr);
+    carve_decode(D, cap, cv);
+    return cv.off + 256;
+}
+
+static int decode(const still_shape* sh, const void* q, const void* k, const void* v,
+                  const float* wq, const float* wk, still_cache* cache, void* out, void* ws,
+                  size_t ws_bytes, hipStream_t s, Timeline& tl) {
+    int st = check_shape(sh, true);
+    if (st) return st;
+    const Dims D = make_dims(sh, 1);
+    if (!cache) return STILL_ERR_INVALID_ARG;
+    if (D.B == 0) {  // nothing to compute; the batch's position still advances
+        if (cache->pos < 0) return STILL_ERR_INVALID_ARG;
+        cache->pos += 1;
+        return STILL_OK;
+    }
+    if (!q || !k || !v || !wq || !wk || !out) return STILL_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return STILL_ERR_INVALID_ARG;
+    const int64_t t = cache->pos;
+    const int64_t need = D.lam * ceil_div(t + 1 - D.W, D.C);
+    st = check_cache(D, cache, -1, need);
+    if (st) return st;
+    if (D.lam > 0 && cache->sel_cap < 1) return STILL_ERR_CAPACITY;
+    const size_t need_ws = decode_bytes(D, cache->sel_cap);
+    if (!ws || ws_bytes < need_ws) return STILL_ERR_WORKSPACE;
+    if (tl.ev && tl.max_ev < 4) return STILL_ERR_INVALID_ARG;
+    void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    Carver cv(wsa);
+    DecodeWork w = carve_decode(D, cache->sel_cap, cv);
+    const CacheView cvw = view_of(cache);
+    STILL_LAUNCH(tl, s, "decode_prep", launch_decode_prep(D, q, k, v, wq, wk, cvw, w, s));
+    STILL_LAUNCH(tl, s, "decode_sel", launch_decode_sel(D, q, cvw, w, s));
+    STILL_LAUNCH(tl, s, "decode_combine", launch_decode_combine(D, w, out, s));
+    STILL_TRY(tl.end(s));
+    cache->pos = t + 1;
+    return STILL_OK;
+}
+
+}  // namespace still
+
+// ---------------------------------------------------------------------------
+// exported C symbols
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int32_t still_abi_version(void) { return STILL_ABI_VERSION; }
+
+const char* still_status_str(int status) {
+    switch (status) {
+        case STILL_OK: return "ok";
+        case STILL_ERR_INVALID_ARG: return "invalid argument";
+        case STILL_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case STILL_ERR_WORKSPACE: return "workspace too small";
+        case STILL_ERR_CAPACITY: return "selected-token cache capacity exceeded";
+        case STILL_ERR_HIP: return "HIP launch failure";
+        default: return "unknown status";
+    }
+}
+
+int32_t still_topk_for_budget(int32_t m, int32_t window, int32_t chunk, int64_t n_max) {
+    if (chunk < 1 || n_max < 1 || m < window || window < 0) return -1;
+    const int64_t t_max = (n_max + chunk - 1) / chunk;
+    return (int32_t)((int64_t)(m - window) / t_max);
+}
+
+int still_fwd_workspace_size(const still_shape* shape, size_t* bytes) {
+    if (!bytes) return STILL_ERR_INVALID_ARG;
+    const int st = still::check_shape(shape, false);
+    if (st) return st;
+    *bytes = still::fwd_bytes(still::make_dims(shape, shape->seqlen));
+    return STILL_OK;
+}
+
+int still_hybrid_attn_fwd(const still_shape* shape, const void* q, const void* k, const void* v,
+                          const float* wphi_q, const float* wphi_k, void* out, float* scores_opt,
+                          int32_t* sel_idx_opt, still_cache* cache_opt, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    still::Timeline tl;
+    return still::fwd(shape, q, k, v, wphi_q, wphi_k, out, scores_opt, sel_idx_opt, cache_opt,
+                      workspace, workspace_bytes, stream, tl);
+}
+
+int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const void* k,
+                                const void* v, const float* wphi_q, const float* wphi_k,
+                                void* out, float* scores_opt, int32_t* sel_idx_opt,
+                                still_cache* cache_opt, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream, hipEvent_t* events, int32_t max_events,
+                                int32_t* n_launches, const char** kernel_names_opt) {
+    if (!events || !n_launches || max_events < 1) return STILL_ERR_INVALID_ARG;
+    still::Timeline tl;
+    tl.ev = events;
+    tl.max_ev = max_events;
+    tl.names = kernel_names_opt;
+    const int st = still::fwd(shape, q, k, v, wphi_q, wphi_k, out, scores_opt, sel_idx_opt,
+                              cache_opt, workspace, workspace_bytes, stream, tl);
+    *n_launches = tl.n;
+    return st;
+}
+
+int still_decode_workspace_size(const still_shape* shape, int32_t sel_cap, size_t* bytes) {
+    if (!bytes || sel_cap < 0) return STILL_ERR_INVALID_ARG;
+    const int st = still::check_shape(shape, true);
+    if (st) return st;
+    *bytes = still::decode_bytes(still::make_dims(shape, 1), sel_cap);
+    return STILL_OK;
+}
+
+int still_hybrid_attn_decode_step(const still_shape* shape, const void* q, const void* k,
+                                  const void* v, const float* wphi_q, const float* wphi_k,
+                                  still_cache* cache, void* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    still::Timeline tl;
+    return still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, workspace, workspace_bytes,
+                         stream, tl);
+}
+
+int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q, const void* k,
+                                        const void* v, const float* wphi_q,
+                                        const float* wphi_k, still_cache* cache, void* out,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream, hipEvent_t* events,
+                                        int32_t max_events, int32_t* n_launches,
+                                        const char** kernel_names_opt) {
+    if (!events || !n_launches || max_events < 1) return STILL_ERR_INVALID_ARG;
+    still::Timeline tl;
+    tl.ev = events;
+    tl.max_ev = max_events;
+    tl.names = kernel_names_opt;
+    const int st = still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, workspace,
+                                 workspace_bytes, stream, tl);
+    *n_launches = tl.n;
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,274 @@
+"""Python binding of libstill: argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+include/still.h; PyTorch supplies device memory and the current stream.  The
+names follow the C entry points.  There is no fallback: if the library is
+not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libstill.so")
+
+STILL_OK, STILL_ERR_INVALID_ARG, STILL_ERR_UNSUPPORTED = 0, -1, -2
+STILL_ERR_WORKSPACE, STILL_ERR_CAPACITY, STILL_ERR_HIP = -3, -4, -5
+STILL_F32, STILL_BF16 = 0, 1
+STILL_FLAG_GENERAL_KERNELS = 1
+
+STILL_MAX_LAUNCHES = 16
+
+EXPORTED = (
+    "still_abi_version", "still_status_str", "still_topk_for_budget",
+    "still_fwd_workspace_size", "still_hybrid_attn_fwd",
+    "still_decode_workspace_size", "still_hybrid_attn_decode_step",
+    "still_hybrid_attn_fwd_timed", "still_hybrid_attn_decode_step_timed",
+)
+
+
+class StillError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+class Shape(ct.Structure):
+    _fields_ = [("batch", ct.c_int32), ("seqlen", ct.c_int32), ("n_q_heads", ct.c_int32),
+                ("n_kv_heads", ct.c_int32), ("head_dim", ct.c_int32), ("feat_dim", ct.c_int32),
+                ("window", ct.c_int32), ("chunk", ct.c_int32), ("topk", ct.c_int32),
+                ("eps", ct.c_float), ("softmax_scale", ct.c_float), ("dtype", ct.c_int32),
+                ("flags", ct.c_uint32)]
+
+
+class CacheStruct(ct.Structure):
+    _fields_ = [("win_k", ct.c_void_p), ("win_v", ct.c_void_p), ("win_route", ct.c_void_p),
+                ("pend_score", ct.c_void_p), ("sel_k", ct.c_void_p), ("sel_v", ct.c_void_p),
+                ("sel_count", ct.c_void_p), ("sel_cap", ct.c_int32), ("lin_S", ct.c_void_p),
+                ("lin_z", ct.c_void_p), ("pos", ct.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ct.CDLL:
+    """Load libstill.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m hybrid_sparse_softmax_amd.build`")
+        L = ct.CDLL(LIB_PATH)
+        vp, sz = ct.c_void_p, ct.c_size_t
+        L.still_abi_version.restype = ct.c_int32
+        L.still_abi_version.argtypes = []
+        L.still_status_str.restype = ct.c_char_p
+        L.still_status_str.argtypes = [ct.c_int]
+        L.still_topk_for_budget.restype = ct.c_int32
+        L.still_topk_for_budget.argtypes = [ct.c_int32, ct.c_int32, ct.c_int32, ct.c_int64]
+        L.still_fwd_workspace_size.restype = ct.c_int
+        L.still_fwd_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
+        L.still_hybrid_attn_fwd.restype = ct.c_int
+        L.still_hybrid_attn_fwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp,
+                                            ct.POINTER(CacheStruct), vp, sz, vp]
+        L.still_decode_workspace_size.restype = ct.c_int
+        L.still_decode_workspace_size.argtypes = [ct.POINTER(Shape), ct.c_int32, ct.POINTER(sz)]
+        L.still_hybrid_attn_decode_step.restype = ct.c_int
+        L.still_hybrid_attn_decode_step.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
+                                                    ct.POINTER(CacheStruct), vp, vp, sz, vp]
+        ev = [ct.POINTER(ct.c_void_p), ct.c_int32, ct.POINTER(ct.c_int32), ct.POINTER(ct.c_char_p)]
+        L.still_hybrid_attn_fwd_timed.restype = ct.c_int
+        L.still_hybrid_attn_fwd_timed.argtypes = L.still_hybrid_attn_fwd.argtypes + ev
+        L.still_hybrid_attn_decode_step_timed.restype = ct.c_int
+        L.still_hybrid_attn_decode_step_timed.argtypes = L.still_hybrid_attn_decode_step.argtypes + ev
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().still_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().still_abi_version())
+
+
+def topk_for_budget(m: int, window: int, chunk: int, n_max: int) -> int:
+    return int(lib().still_topk_for_budget(m, window, chunk, n_max))
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return STILL_BF16
+    if dt == torch.float32:
+        return STILL_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def make_shape(*, batch, seqlen, n_q_heads, n_kv_heads, head_dim, window, chunk, topk,
+               eps=1e-6, softmax_scale=0.0, dtype=torch.bfloat16, feat_dim=None,
+               general=False) -> Shape:
+    return Shape(batch, seqlen, n_q_heads, n_kv_heads, head_dim,
+                 head_dim if feat_dim is None else feat_dim, window, chunk, topk, eps,
+                 softmax_scale, _dtype_code(dtype), STILL_FLAG_GENERAL_KERNELS if general else 0)
+
+
+def _ptr(t):
+    return None if t is None else ct.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != STILL_OK:
+        raise StillError(status, where)
+
+
+def fwd_workspace_size(shape: Shape) -> int:
+    n = ct.c_size_t(0)
+    _check(lib().still_fwd_workspace_size(ct.byref(shape), ct.byref(n)), "still_fwd_workspace_size")
+    return n.value
+
+
+def decode_workspace_size(shape: Shape, sel_cap: int) -> int:
+    n = ct.c_size_t(0)
+    _check(lib().still_decode_workspace_size(ct.byref(shape), sel_cap, ct.byref(n)),
+           "still_decode_workspace_size")
+    return n.value
+
+
+def _expect(t, name, dtype, shape):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: want contiguous {dtype} {tuple(shape)} on the GPU, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+class LaunchTimer:
+    """HIP events handed to the *_timed entry points: event i is recorded on
+    the launch stream before kernel launch i, the last one after the final
+    launch.  Events come from torch (each recorded once so it exists)."""
+
+    def __init__(self, n_events: int = STILL_MAX_LAUNCHES + 1):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+        for e in self.events:
+            e.record()
+        torch.cuda.synchronize()
+        self.handles = (ct.c_void_p * n_events)(*[e.cuda_event for e in self.events])
+        self.names = (ct.c_char_p * n_events)()
+        self.n = ct.c_int32(0)
+
+    def args(self):
+        return [self.handles, len(self.events), ct.byref(self.n), self.names]
+
+    def durations_ms(self) -> list:
+        """[(kernel name, milliseconds)] of the last timed call (synchronises)."""
+        self.events[self.n.value].synchronize()
+        return [(self.names[i].decode(), self.events[i].elapsed_time(self.events[i + 1]))
+                for i in range(self.n.value)]
+
+
+class DecodeCache:
+    """Caller-owned decode cache tensors (layouts of still_cache)."""
+
+    def __init__(self, *, batch, n_kv_heads, head_dim, window, chunk, topk, sel_cap,
+                 dtype=torch.bfloat16, feat_dim=None, device="cuda", pos=0):
+        fd = head_dim if feat_dim is None else feat_dim
+        B, H, d, W, C = batch, n_kv_heads, head_dim, window, chunk
+        self.window, self.chunk, self.topk = W, C, topk
+        self.win_k = torch.zeros((B, H, max(W, 1), d), dtype=dtype, device=device)
+        self.win_v = torch.zeros_like(self.win_k)
+        self.win_route = torch.zeros((B, H, max(W, 1)), dtype=torch.uint8, device=device)
+        self.pend_score = torch.zeros((B, H, C), dtype=torch.float32, device=device)
+        self.sel_k = torch.zeros((B, H, max(sel_cap, 1), d), dtype=dtype, device=device)
+        self.sel_v = torch.zeros_like(self.sel_k)
+        self.sel_count = torch.zeros((B, H), dtype=torch.int32, device=device)
+        self.sel_cap = sel_cap
+        self.lin_S = torch.zeros((B, H, fd, d), dtype=torch.float32, device=device)
+        self.lin_z = torch.zeros((B, H, fd), dtype=torch.float32, device=device)
+        self.pos = pos
+        self._struct = None
+
+    def struct(self) -> CacheStruct:
+        self._struct = CacheStruct(self.win_k.data_ptr(), self.win_v.data_ptr(),
+                                   self.win_route.data_ptr(), self.pend_score.data_ptr(),
+                                   self.sel_k.data_ptr(), self.sel_v.data_ptr(),
+                                   self.sel_count.data_ptr(), self.sel_cap,
+                                   self.lin_S.data_ptr(), self.lin_z.data_ptr(), self.pos)
+        return self._struct
+
+    def tensors(self) -> dict:
+        return {k: getattr(self, k) for k in ("win_k", "win_v", "win_route", "pend_score", "sel_k",
+                                              "sel_v", "sel_count", "lin_S", "lin_z")}
+
+
+def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale=0.0,
+        return_scores=False, return_sel=False, cache: DecodeCache | None = None,
+        out=None, workspace=None, general=False, timer: LaunchTimer | None = None) -> dict:
+    """still_hybrid_attn_fwd.  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or f32),
+    wphi_* [Hkv, d'/2, d] f32.  Returns dict(out, scores?, sel_idx?)."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
+                    chunk=chunk, topk=topk, eps=eps, softmax_scale=softmax_scale, dtype=q.dtype,
+                    feat_dim=2 * wphi_q.shape[1], general=general)
+    _expect(q, "q", q.dtype, (B, N, Hq, d))
+    _expect(k, "k", q.dtype, (B, N, Hkv, d))
+    _expect(v, "v", q.dtype, (B, N, Hkv, d))
+    _expect(wphi_q, "wphi_q", torch.float32, (Hkv, wphi_q.shape[1], d))
+    _expect(wphi_k, "wphi_k", torch.float32, (Hkv, wphi_q.shape[1], d))
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lam = min(topk, chunk)
+    scores = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev) if return_scores else None
+    sel = torch.empty((B, Hkv, N // chunk, lam), dtype=torch.int32, device=dev) if return_sel else None
+    nbytes = fwd_workspace_size(sh)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    cs = ct.byref(cache.struct()) if cache is not None else None
+    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(out),
+            _ptr(scores), _ptr(sel), cs, _ptr(workspace), workspace.numel(), _stream()]
+    if timer is None:
+        _check(lib().still_hybrid_attn_fwd(*args), "still_hybrid_attn_fwd")
+    else:
+        _check(lib().still_hybrid_attn_fwd_timed(*args, *timer.args()), "still_hybrid_attn_fwd_timed")
+    res = {"out": out}
+    if scores is not None:
+        res["scores"] = scores
+    if sel is not None:
+        res["sel_idx"] = sel
+    return res
+
+
+def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softmax_scale=0.0,
+                out=None, workspace=None, general=False, timer: LaunchTimer | None = None):
+    """still_hybrid_attn_decode_step at position cache.pos; q [B,1,Hq,d],
+    k/v [B,1,Hkv,d].  Advances cache.pos.  Returns out [B,1,Hq,d]."""
+    B, one, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sh = make_shape(batch=B, seqlen=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                    window=cache.window, chunk=cache.chunk, topk=cache.topk, eps=eps,
+                    softmax_scale=softmax_scale, dtype=q.dtype, feat_dim=2 * wphi_q.shape[1],
+                    general=general)
+    _expect(q, "q", q.dtype, (B, 1, Hq, d))
+    _expect(k, "k", q.dtype, (B, 1, Hkv, d))
+    _expect(v, "v", q.dtype, (B, 1, Hkv, d))
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = decode_workspace_size(sh, cache.sel_cap)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    cs = cache.struct()
+    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), ct.byref(cs),
+            _ptr(out), _ptr(workspace), workspace.numel(), _stream()]
+    if timer is None:
+        _check(lib().still_hybrid_attn_decode_step(*args), "still_hybrid_attn_decode_step")
+    else:
+        _check(lib().still_hybrid_attn_decode_step_timed(*args, *timer.args()),
+               "still_hybrid_attn_decode_step_timed")
+    cache.pos = int(cs.pos)
+    return out

@@ -1,0 +1,216 @@
+/*
+ * still.h -- C ABI of the STILL intra-layer hybrid attention operator on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operator comes from "STILL: Selecting Tokens for Intra-Layer Hybrid
+ * Attention to Linearize LLMs" (Meng et al., 2026).  Section references are
+ * to the paper's full-text web page; figure captions are from its list view.
+ *
+ * For every attention layer it
+ *   1. runs sliding-window softmax attention and scores every token's
+ *      Self-Saliency inside its window (Sec. 3.1, Fig. 2);
+ *   2. keeps the top-`topk` tokens of every complete chunk of `chunk` tokens,
+ *      decided once per chunk (delayed selection, Sec. 3.3), separately per
+ *      KV head (Sec. 3.3: routing is per head);
+ *   3. runs softmax attention over the selected tokens and linear attention
+ *      with the Norm-Preserved Feature Map (NP-Map, Sec. 3.2) over every other
+ *      token that has left the window (Sec. 3.3, Appendix A.2);
+ *   4. merges both branches with one shared normaliser (Fig. 2, "hybrid
+ *      aggregation").
+ *
+ * Where the pages leave a step open this library follows these readings:
+ *   - Score_t = sum_j a_j ln((a_j+eps)/(a~_j+eps)) over token t's own window
+ *     row a (itself included) and its leave-one-out row a~ (a~_t = 0)
+ *     (Appendix A.3, Lemma 1 and Remark);
+ *   - a KV head routes by the mean score of its query heads;
+ *   - top-k ties go to the lower position;
+ *   - token j is routed for query t once j <= t - window; chunk decisions are
+ *     therefore complete in time only when window >= chunk (Appendix A.7.5:
+ *     the window spans one chunk);
+ *   - phi(x) = [softmax(z); softmax(-z)], z = ||x|| P x / ||P x||;
+ *   - out = (sum_SA e^{tau q.k} v + sum_LA phi_q.phi_k v) /
+ *           (sum_SA e^{tau q.k}   + sum_LA phi_q.phi_k).
+ *
+ * Conventions for every call
+ *   - Tensors are dense row-major, innermost dimension last, on the current
+ *     HIP device, 16-byte aligned.  q / out: [B, N, Hq, d]; k / v:
+ *     [B, N, Hkv, d]; query head h reads KV head h / (Hq / Hkv).
+ *   - `dtype` is the element type of q, k, v, out and the cached K/V:
+ *     STILL_BF16 (bf16 storage, fp32 arithmetic, results rounded to nearest
+ *     even) or STILL_F32.  NP-Map projections, scores and linear states are
+ *     always fp32.
+ *   - The caller owns and allocates every buffer (inputs, outputs, workspace,
+ *     cache).  The library never allocates, frees or synchronises: work is
+ *     enqueued on `stream` and results are valid once the stream reaches
+ *     that point.  No state survives a call except a per-process cache of
+ *     device properties, so calls on distinct buffers are thread-safe.
+ *   - Every entry point validates all arguments on the host before
+ *     launching anything, returns a still_status, and never aborts.
+ */
+#ifndef STILL_H
+#define STILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STILL_ABI_VERSION 1
+
+typedef enum {
+    STILL_OK = 0,
+    STILL_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad shape or parameter   */
+    STILL_ERR_UNSUPPORTED = -2,  /* valid for the method, not built here (e.g. d=96)  */
+    STILL_ERR_WORKSPACE = -3,    /* workspace_bytes smaller than the size call asks   */
+    STILL_ERR_CAPACITY = -4,     /* the selected-token cache could overflow           */
+    STILL_ERR_HIP = -5           /* a kernel launch failed (hipGetLastError)          */
+} still_status;
+
+typedef enum { STILL_F32 = 0, STILL_BF16 = 1 } still_dtype;
+
+/* Force the general kernels even where the gfx950 MFMA kernels apply
+ * (cross-checking; both compute the same operator). */
+#define STILL_FLAG_GENERAL_KERNELS 1u
+
+/* Problem statement (Sec. 3.3 and Appendix A.4: window W, chunk C, per-chunk
+ * quota lambda; Sec. 3.2: NP-Map feature size d').
+ *   batch B >= 0, seqlen N >= 0 (1 for a decode step),
+ *   n_q_heads Hq >= 1, n_kv_heads Hkv >= 1 with Hq % Hkv == 0,
+ *   head_dim d in {64, 128}, feat_dim d' == d,
+ *   window W >= 0, chunk C in [1, 1024], topk lambda >= 0 (clamped to C),
+ *   W == 0 requires lambda == 0; lambda > 0 requires W >= C,
+ *   eps > 0 (Self-Saliency smoothing, Appendix A.3),
+ *   softmax_scale tau > 0, or 0 for 1/sqrt(d). */
+typedef struct {
+    int32_t batch, seqlen, n_q_heads, n_kv_heads, head_dim, feat_dim;
+    int32_t window, chunk, topk;
+    float eps, softmax_scale;
+    int32_t dtype;   /* still_dtype */
+    uint32_t flags;  /* STILL_FLAG_* */
+} still_shape;
+
+/* Decode cache of Sec. 3.3 "Recurrent Form": the sliding window, the
+ * permanently retained selected tokens, and the linear-attention state of
+ * every other token that has left the window.  All device memory, all owned
+ * by the caller; layouts per (sequence b, KV head g):
+ *   win_k, win_v   [B, Hkv, W, d]  dtype; position p lives in slot p % W
+ *   win_route      [B, Hkv, W]     u8: 0 pending, 1 selected (SA), 2 linear (LA)
+ *   pend_score     [B, Hkv, C]     fp32 group-mean scores of the open chunk,
+ *                                  position p in slot p % C
+ *   sel_k, sel_v   [B, Hkv, cap, d] dtype, selected tokens in the order they
+ *                                  left the window (ascending position)
+ *   sel_count      [B, Hkv]        int32 rows of sel_k/sel_v in use
+ *   lin_S          [B, Hkv, d', d] fp32, sum of phi_k(k_j) v_j^T (Appendix A.2)
+ *   lin_z          [B, Hkv, d']    fp32, sum of phi_k(k_j)
+ *   pos            next position t (host value, shared by the batch; the
+ *                  decode step advances it by one on success).
+ * Pointers of parts that a shape does not use (window parts when W == 0,
+ * selected parts when lambda == 0) may be NULL. */
+typedef struct {
+    void* win_k;
+    void* win_v;
+    uint8_t* win_route;
+    float* pend_score;
+    void* sel_k;
+    void* sel_v;
+    int32_t* sel_count;
+    int32_t sel_cap;
+    float* lin_S;
+    float* lin_z;
+    int64_t pos;
+} still_cache;
+
+/* Version of this header's ABI (STILL_ABI_VERSION). */
+int32_t still_abi_version(void);
+
+/* Static text for a still_status value. */
+const char* still_status_str(int status);
+
+/* Certified per-chunk quota of Appendix A.4:
+ * lambda = floor((m - W) / ceil(n_max / C)), so that every length up to n_max
+ * keeps at most m tokens (window included) in the softmax cache.  Returns -1
+ * for m < W, C < 1 or n_max < 1. */
+int32_t still_topk_for_budget(int32_t m, int32_t window, int32_t chunk, int64_t n_max);
+
+/* Bytes of device workspace still_hybrid_attn_fwd needs for `shape`.
+ * Returns STILL_OK and writes *bytes, or an error status for an invalid
+ * shape. */
+int still_fwd_workspace_size(const still_shape* shape, size_t* bytes);
+
+/* Chunk-parallel forward (Sec. 3.3, "Chunk-Wise Parallel Form"): the whole
+ * sequence at once, causal, with the same routing as the recurrent form.
+ *   q, k, v         inputs (layouts above), read only
+ *   wphi_q, wphi_k  [Hkv, d'/2, d] fp32 NP-Map projections of queries and
+ *                   keys (Sec. 3.2), one pair per KV head
+ *   out             [B, N, Hq, d] dtype, written
+ *   scores_opt      [B, Hkv, N] fp32 group-mean Self-Saliency, or NULL
+ *   sel_idx_opt     [B, Hkv, N / C, min(topk, C)] int32 selected positions of
+ *                   every complete chunk, ascending, or NULL
+ *   cache_opt       if not NULL, filled as the recurrent form would leave it
+ *                   after these N tokens (prefill -> decode hand-off):
+ *                   cache_opt->pos must equal N on entry; needs
+ *                   sel_cap >= min(topk,C) * ceil(max(0, N - W) / C)
+ *                   (else STILL_ERR_CAPACITY)
+ *   workspace       >= still_fwd_workspace_size bytes of device memory
+ * N == 0 or B == 0 is a no-op returning STILL_OK once the shape is valid (no
+ * pointer is inspected). */
+int still_hybrid_attn_fwd(const still_shape* shape, const void* q, const void* k, const void* v,
+                          const float* wphi_q, const float* wphi_k, void* out, float* scores_opt,
+                          int32_t* sel_idx_opt, still_cache* cache_opt, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace one decode step needs for `shape` (seqlen is
+ * ignored) and a selected cache of `sel_cap` rows. */
+int still_decode_workspace_size(const still_shape* shape, int32_t sel_cap, size_t* bytes);
+
+/* One recurrent step (Sec. 3.3, "Recurrent Form") at position t = cache->pos
+ * for all B sequences:
+ *   1. the token at t - W leaves the window: if its chunk selected it, it is
+ *      appended to sel_k/sel_v for good; otherwise it is folded into
+ *      lin_S / lin_z (W == 0: the new token itself goes to the linear state);
+ *   2. k_t, v_t enter the window;
+ *   3. the Self-Saliency of t (mean over the group's query heads) is stored
+ *      in pend_score;
+ *   4. out = hybrid attention of q_t over window + selected tokens + linear
+ *      state;
+ *   5. when t closes a chunk, its top-k tokens are marked selected, the rest
+ *      linear.
+ *   q [B, 1, Hq, d], k / v [B, 1, Hkv, d], out [B, 1, Hq, d].
+ * Returns STILL_ERR_CAPACITY (nothing launched) when
+ * min(topk,C) * ceil((t + 1 - W) / C) > sel_cap.  On STILL_OK cache->pos is
+ * incremented. */
+int still_hybrid_attn_decode_step(const still_shape* shape, const void* q, const void* k,
+                                  const void* v, const float* wphi_q, const float* wphi_k,
+                                  still_cache* cache, void* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Instrumented forms of the two entry points, for measurement (they compute
+ * exactly what the plain calls compute).  Before the i-th kernel launch the
+ * call records events[i] on `stream`, and events[n] after the last launch,
+ * so hipEventElapsedTime(events[i], events[i+1]) is launch i's duration on
+ * that stream.  kernel_names_opt[i] (if not NULL) receives a static name of
+ * launch i.  *n_launches receives n.  Needs max_events >= n + 1, else
+ * STILL_ERR_INVALID_ARG before anything is launched; events are created and
+ * destroyed by the caller. */
+#define STILL_MAX_LAUNCHES 16
+int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const void* k,
+                                const void* v, const float* wphi_q, const float* wphi_k,
+                                void* out, float* scores_opt, int32_t* sel_idx_opt,
+                                still_cache* cache_opt, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream, hipEvent_t* events, int32_t max_events,
+                                int32_t* n_launches, const char** kernel_names_opt);
+int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q, const void* k,
+                                        const void* v, const float* wphi_q,
+                                        const float* wphi_k, still_cache* cache, void* out,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream, hipEvent_t* events,
+                                        int32_t max_events, int32_t* n_launches,
+                                        const char** kernel_names_opt);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STILL_H */

@@ -231,13 +231,15 @@ def route_from_selection(sel_idx: np.ndarray, N: int, C: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Chunk-parallel forward, direct per-query form (Sec. 3.3; R-DELAY, R-AGG)
 # --------------------------------------------------------------------------
-def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None):
+def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=None):
     """Hybrid attention output from the explicit per-query index sets.
 
     q [B,N,Hq,d], k/v [B,N,Hkv,d], wq/wk [Hkv, d'/2, d]  (float64 views).
     rows: optional list of (b, t) to evaluate (default: every query).
     sel_override: optional sel_idx [B,Hkv,N//C,lambda] to route with instead
     of the oracle's own selection (near-tie protocol).
+    scores: optional group scores [B,Hkv,N] already computed by window_scores
+    (saves recomputing them when only a few rows are evaluated).
 
     Returns dict(out [B,N,Hq,d] (NaN where not evaluated), scores, sel_idx, route).
 
@@ -255,7 +257,9 @@ def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None):
     G = Hq // Hkv
     W, tau = p.window, p.tau(d)
 
-    if W > 0:
+    if scores is not None:
+        sigma = np.asarray(scores, np.float64)
+    elif W > 0:
         sigma = window_scores(q, k, p, Hkv)
     else:
         sigma = np.zeros((B, Hkv, N))

@@ -1,0 +1,154 @@
+"""Host-side tests of the C ABI: the library loads, exports every entry point
+include/still.h declares, sizes workspaces, and rejects every bad argument
+with the documented status before launching anything (no GPU needed: all
+of these calls return before the first HIP call)."""
+import ctypes as ct
+import json
+import os
+import re
+
+import pytest
+
+from hybrid_sparse_softmax_amd import still as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ct.c_void_p(0x1000)          # 16-byte aligned, never dereferenced
+MISALIGNED = ct.c_void_p(0x1004)
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "still.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(still_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    L = S.lib()
+    names = header_functions()
+    assert set(names) == set(S.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert S.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert S.status_str(code) and S.status_str(code) != "unknown status"
+    assert S.status_str(7) == "unknown status"
+
+
+def test_topk_for_budget_matches_stated_budgets():
+    with open(os.path.join(ROOT, "tests", "golden", "budgets.json")) as f:
+        for c in json.load(f)["cases"]:
+            assert S.topk_for_budget(c["m"], c["window"], c["chunk"], c["n_max"]) == c["topk"]
+    assert S.topk_for_budget(10, 64, 64, 100) == -1
+    assert S.topk_for_budget(128, 64, 0, 100) == -1
+
+
+def shape(**kw):
+    base = dict(batch=1, seqlen=256, n_q_heads=4, n_kv_heads=2, head_dim=128, window=64,
+                chunk=64, topk=16)
+    base.update(kw)
+    return S.make_shape(**base)
+
+
+def fwd_status(sh, ws_bytes=1 << 40, cache=None, ptr=FAKE, ws=FAKE):
+    return S.lib().still_hybrid_attn_fwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, ptr, None, None,
+                                         ct.byref(cache) if cache is not None else None, ws,
+                                         ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=6, n_kv_heads=4), S.STILL_ERR_INVALID_ARG),      # G not integer
+    (dict(window=0, topk=4), S.STILL_ERR_INVALID_ARG),                # no window, topk > 0
+    (dict(window=32, chunk=64, topk=4), S.STILL_ERR_INVALID_ARG),     # W < C with selection
+    (dict(chunk=0), S.STILL_ERR_INVALID_ARG),
+    (dict(topk=-1), S.STILL_ERR_INVALID_ARG),
+    (dict(seqlen=-5), S.STILL_ERR_INVALID_ARG),
+    (dict(eps=0.0), S.STILL_ERR_INVALID_ARG),
+    (dict(softmax_scale=-1.0), S.STILL_ERR_INVALID_ARG),
+    (dict(head_dim=96), S.STILL_ERR_UNSUPPORTED),
+    (dict(head_dim=128, feat_dim=64), S.STILL_ERR_UNSUPPORTED),
+    (dict(n_q_heads=32, n_kv_heads=2), S.STILL_ERR_UNSUPPORTED),     # G = 16
+])
+def test_bad_shapes_rejected(kw, status):
+    sh = shape(**kw)
+    assert fwd_status(sh) == status
+    n = ct.c_size_t(0)
+    assert S.lib().still_fwd_workspace_size(ct.byref(sh), ct.byref(n)) == status
+    assert S.lib().still_decode_workspace_size(ct.byref(sh), 64, ct.byref(n)) == status
+
+
+def test_bad_dtype_and_flags():
+    sh = shape()
+    sh.dtype = 7
+    assert fwd_status(sh) == S.STILL_ERR_INVALID_ARG
+    sh = shape()
+    sh.flags = 0x80
+    assert fwd_status(sh) == S.STILL_ERR_INVALID_ARG
+    assert S.lib().still_fwd_workspace_size(None, ct.byref(ct.c_size_t())) == S.STILL_ERR_INVALID_ARG
+    assert S.lib().still_fwd_workspace_size(ct.byref(shape()), None) == S.STILL_ERR_INVALID_ARG
+
+
+def test_null_and_misaligned_pointers():
+    sh = shape()
+    assert fwd_status(sh, ptr=None) == S.STILL_ERR_INVALID_ARG
+    assert fwd_status(sh, ptr=MISALIGNED) == S.STILL_ERR_INVALID_ARG
+
+
+def test_workspace_size_and_too_small_workspace():
+    sh = shape()
+    need = S.fwd_workspace_size(sh)
+    assert need > 0
+    assert fwd_status(sh, ws_bytes=need - 1) == S.STILL_ERR_WORKSPACE
+    assert fwd_status(sh, ws=None) == S.STILL_ERR_WORKSPACE
+    # bigger problems need more
+    assert S.fwd_workspace_size(shape(seqlen=4096)) > need
+    assert S.decode_workspace_size(shape(), 8192) > S.decode_workspace_size(shape(), 64)
+
+
+def test_empty_problems_are_noops():
+    for kw in (dict(seqlen=0), dict(batch=0)):
+        sh = shape(**kw)
+        assert fwd_status(sh, ws_bytes=0, ws=None, ptr=None) == S.STILL_OK
+
+
+def fake_cache(cap, pos, W=64, topk=16):
+    c = S.CacheStruct(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, cap, 0x1000, 0x1000, pos)
+    return c
+
+
+def test_handoff_capacity_and_position_checks():
+    sh = shape(seqlen=1024)                      # 16 selected per chunk
+    need = 16 * ((1024 - 64 + 63) // 64)         # tokens that left the window
+    assert fwd_status(sh, cache=fake_cache(need - 1, 1024)) == S.STILL_ERR_CAPACITY
+    assert fwd_status(sh, cache=fake_cache(need, 1000)) == S.STILL_ERR_INVALID_ARG   # pos != N
+    c = fake_cache(need, 1024)
+    c.lin_S = None
+    assert fwd_status(sh, cache=c) == S.STILL_ERR_INVALID_ARG
+    # with enough capacity only the (fake) workspace size stops the call
+    assert fwd_status(sh, cache=fake_cache(need, 1024), ws_bytes=16) == S.STILL_ERR_WORKSPACE
+
+
+def decode_status(sh, cache, ws_bytes=1 << 40, ptr=FAKE):
+    return S.lib().still_hybrid_attn_decode_step(ct.byref(sh), ptr, ptr, ptr, ptr, ptr,
+                                                 ct.byref(cache), ptr, FAKE, ws_bytes, None)
+
+
+def test_decode_capacity_guard():
+    sh = shape(seqlen=1, topk=32)
+    # step at t needs topk * ceil((t + 1 - W) / C) rows
+    t = 16384
+    need = 32 * ((t + 1 - 64 + 63) // 64)
+    assert decode_status(sh, fake_cache(need - 1, t)) == S.STILL_ERR_CAPACITY
+    assert decode_status(sh, fake_cache(need, t), ws_bytes=16) == S.STILL_ERR_WORKSPACE
+    c = fake_cache(need, -1)
+    assert decode_status(sh, c) == S.STILL_ERR_INVALID_ARG
+    assert decode_status(sh, fake_cache(need, t), ptr=None) == S.STILL_ERR_INVALID_ARG
+
+
+def test_decode_empty_batch_advances_position():
+    sh = shape(seqlen=1, batch=0)
+    c = fake_cache(64, 100)
+    assert decode_status(sh, c, ws_bytes=0, ptr=None) == S.STILL_OK
+    assert c.pos == 101

@@ -1,0 +1,160 @@
+"""GPU parity of the prefill -> decode hand-off and of the decode step against
+the oracle's recurrent form (Sec. 3.3 "Recurrent Form"): the cache the
+forward leaves behind must equal the oracle's cache after the same tokens,
+and each decode step must match the oracle's step, including the chunk-end
+routing decisions."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from parity import (BF16_TOL, F32_TOL, TIE_TOL, check_selection, make_case, prepare, rel_l2,
+                    say, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+DEC_CASES = {
+    # name: (cfg over N0 + K tokens, N0 prefill tokens, seed)
+    "bf16_G4": (make_case("a", 2, 190 + 80, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 190, 31),
+    "f32_W48_C16": (make_case("b", 1, 70 + 40, 4, 1, 64, 48, 16, 4, dtype="f32"), 70, 32),
+    "bf16_pure_linear": (make_case("c", 1, 20 + 30, 4, 2, 64, 0, 8, 0), 20, 33),
+    "bf16_swa_la": (make_case("d", 1, 100 + 40, 4, 4, 128, 32, 64, 0), 100, 34),
+    "bf16_from_empty": (make_case("e", 1, 140, 4, 1, 128, 64, 64, 16), 0, 35),
+    "bf16_G8_boundary": (make_case("f", 1, 128 + 70, 8, 1, 128, 64, 64, 8), 128, 36),
+}
+
+
+def compare_cache(gc, oc, cfg, n_tok, tol):
+    """gc: DecodeCache on the GPU; oc: oracle cache dict.  Exact for copies,
+    route flags and counts; tolerance for fp32 sums."""
+    W, C = cfg["window"], cfg["chunk"]
+    if W > 0:
+        n_ring = min(n_tok, W)
+        slots = [j % W for j in range(n_tok - n_ring, n_tok)]
+        gk = gc.win_k.double().cpu().numpy()
+        gv = gc.win_v.double().cpu().numpy()
+        np.testing.assert_array_equal(gk[:, :, slots], oc["win_k"][:, :, slots])
+        np.testing.assert_array_equal(gv[:, :, slots], oc["win_v"][:, :, slots])
+        np.testing.assert_array_equal(gc.win_route.cpu().numpy()[:, :, slots],
+                                      oc["win_route"][:, :, slots])
+        open_ = [j % C for j in range((n_tok // C) * C, n_tok)]
+        if open_:
+            gp = gc.pend_score.cpu().numpy()[:, :, open_]
+            op = oc["pend_score"][:, :, open_]
+            assert np.max(np.abs(gp - op) / np.maximum(1, np.abs(op))) <= 1e-4
+    if cfg["topk"] > 0:
+        cnt = gc.sel_count.cpu().numpy()
+        np.testing.assert_array_equal(cnt, oc["sel_count"])
+        gsk = gc.sel_k.double().cpu().numpy()
+        gsv = gc.sel_v.double().cpu().numpy()
+        for b in range(cnt.shape[0]):
+            for g in range(cnt.shape[1]):
+                n = cnt[b, g]
+                np.testing.assert_array_equal(gsk[b, g, :n], oc["sel_k"][b, g, :n])
+                np.testing.assert_array_equal(gsv[b, g, :n], oc["sel_v"][b, g, :n])
+    es = rel_l2(gc.lin_S.double().cpu().numpy(), oc["lin_S"]) if np.any(oc["lin_S"]) else \
+        float(np.abs(gc.lin_S.cpu().numpy()).max())
+    ez = rel_l2(gc.lin_z.double().cpu().numpy(), oc["lin_z"]) if np.any(oc["lin_z"]) else \
+        float(np.abs(gc.lin_z.cpu().numpy()).max())
+    assert es <= tol and ez <= tol, (es, ez)
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
+@pytest.mark.parametrize("name", list(DEC_CASES))
+def test_prefill_handoff_then_decode(gpu_lib, name, general):
+    cfg, N0, seed = DEC_CASES[name]
+    say(f"[decode] case={name} general={general} shape={workloads.shape_of(cfg)} N0={N0} seed={seed}")
+    raw = workloads.make_prefill(cfg, seed)
+    dt = torch_dtype(cfg["dtype"])
+    dev, ref = prepare(raw, dt)
+    B, N = cfg["batch"], cfg["seqlen"]
+    Hq, Hkv, d = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    p = O.Params(window=W, chunk=C, topk=lam)
+    cap = p.topk_eff() * (-(-N // C)) + 1
+    tol = F32_TOL if cfg["dtype"] == "f32" else BF16_TOL
+    state_tol = 1e-5
+
+    gc = gpu_lib.DecodeCache(batch=B, n_kv_heads=Hkv, head_dim=d, window=W, chunk=C, topk=lam,
+                             sel_cap=cap, dtype=dt, pos=N0)
+    override = None
+    if N0 > 0:
+        res = gpu_lib.fwd(dev["q"][:, :N0].contiguous(), dev["k"][:, :N0].contiguous(),
+                          dev["v"][:, :N0].contiguous(), dev["wphi_q"], dev["wphi_k"], window=W,
+                          chunk=C, topk=lam, return_sel=True, cache=gc, general=general)
+        torch.cuda.synchronize()
+        if p.topk_eff() > 0 and N0 >= C:
+            sig = O.window_scores(ref["q"][:, :N0], ref["k"][:, :N0], p, Hkv)
+            osel, _ = O.select_chunks(sig, p)
+            gsel = res["sel_idx"].cpu().numpy().astype(np.int64)
+            if check_selection(gsel, sig, osel, C)[0]:
+                override = gsel
+    _, oc = O.fwd_recurrent(ref["q"][:, :N0], ref["k"][:, :N0], ref["v"][:, :N0], ref["wphi_q"],
+                            ref["wphi_k"], p, cap=cap, sel_override=override)
+    compare_cache(gc, oc, cfg, N0, state_tol)
+    say("  hand-off cache matches")
+
+    ws = None
+    worst = 0.0
+    for t in range(N0, N):
+        q_t = dev["q"][:, t:t + 1].contiguous()
+        k_t = dev["k"][:, t:t + 1].contiguous()
+        v_t = dev["v"][:, t:t + 1].contiguous()
+        g_out = gpu_lib.decode_step(q_t, k_t, v_t, dev["wphi_q"], dev["wphi_k"], gc,
+                                    general=general)
+        o_out = O.decode_step(oc, ref["q"][:, t], ref["k"][:, t], ref["v"][:, t], ref["wphi_q"],
+                              ref["wphi_k"], p)
+        torch.cuda.synchronize()
+        assert gc.pos == oc["pos"] == t + 1
+        err = rel_l2(g_out[:, 0].double().cpu().numpy(), o_out)
+        worst = max(worst, err)
+        assert err <= tol, f"step t={t}: rel-L2 {err:.3e}"
+        if W > 0 and t % C == C - 1 and lam > 0:
+            # chunk-end decision: same flags, or a near-tie that the oracle adopts
+            gf = gc.win_route.cpu().numpy()
+            slots = [j % W for j in range(t - C + 1, t + 1)]
+            if not np.array_equal(gf[:, :, slots], oc["win_route"][:, :, slots]):
+                pend = oc["pend_score"]
+                for b in range(B):
+                    for g in range(Hkv):
+                        pos = np.arange(t - C + 1, t + 1)
+                        gs = pos[gf[b, g, slots] == O.ROUTE_SA][None, None, None, :]
+                        os_ = pos[oc["win_route"][b, g, slots] == O.ROUTE_SA][None, None, None, :]
+                        sig = np.zeros((1, 1, t + 1))
+                        sig[0, 0, pos] = pend[b, g, pos % C]
+                        check_selection(gs, sig, os_, C, TIE_TOL)
+                oc["win_route"][:, :, slots] = gf[:, :, slots]
+    say(f"  {N - N0} steps, worst step rel-L2 {worst:.3e}")
+    compare_cache(gc, oc, cfg, N, state_tol)
+
+
+def test_cache_checkpoint_restore_is_bit_exact(gpu_lib):
+    """The decode state is the caller's tensors: copying them out, running on,
+    restoring and re-running gives bit-identical outputs."""
+    cfg, N0, seed = DEC_CASES["bf16_G4"]
+    raw = workloads.make_prefill(cfg, seed)
+    dev, _ = prepare(raw, torch.bfloat16)
+    gc = gpu_lib.DecodeCache(batch=2, n_kv_heads=2, head_dim=128, window=64, chunk=64, topk=16,
+                             sel_cap=128, pos=N0)
+    gpu_lib.fwd(dev["q"][:, :N0].contiguous(), dev["k"][:, :N0].contiguous(),
+                dev["v"][:, :N0].contiguous(), dev["wphi_q"], dev["wphi_k"], window=64, chunk=64,
+                topk=16, cache=gc)
+    snap = {k: v.clone() for k, v in gc.tensors().items()}
+
+    def run():
+        outs = []
+        for t in range(N0, N0 + 70):
+            outs.append(gpu_lib.decode_step(dev["q"][:, t:t + 1].contiguous(),
+                                            dev["k"][:, t:t + 1].contiguous(),
+                                            dev["v"][:, t:t + 1].contiguous(), dev["wphi_q"],
+                                            dev["wphi_k"], gc).clone())
+        return torch.cat(outs, 1)
+
+    a = run()
+    for k, v in snap.items():
+        getattr(gc, k).copy_(v)
+    gc.pos = N0
+    b = run()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -1,0 +1,98 @@
+"""GPU parity of the chunk-parallel forward against the float64 oracle, whole
+tensors, element by element, at sizes the oracle finishes in seconds (several
+tiles and a ragged tail), plus the method's degenerate cases.
+
+Bars: selected positions bit-exact (or the near-tie protocol), output rel-L2
+<= 1e-2 for bf16 storage and <= 1e-5 for fp32, group scores within 1e-4
+relative.  Every case runs through the C ABI, both with the kernels the
+library picks for the shape and with the general kernels forced."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from parity import (BF16_TOL, F32_TOL, check_selection, make_case, prepare, rel_l2, say,
+                    torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "toy_fp32": (workloads.CONFIGS["toy_fp32"], workloads.seed_of("toy_fp32")),
+    "bf16_ragged_G4": (make_case("r", 2, 600, 8, 2, 128, 64, 64, 16, outlier_frac=0.01, heavy_scale=6.0), 11),
+    "bf16_tiles_G4": (make_case("t", 1, 1024, 8, 2, 128, 64, 64, 32, outlier_frac=0.01, heavy_scale=6.0), 12),
+    "bf16_d64_W96_C32": (make_case("a", 1, 333, 4, 1, 64, 96, 32, 8), 13),
+    "f32_G8_d64": (make_case("b", 1, 200, 8, 1, 64, 32, 16, 5, dtype="f32"), 14),
+    "bf16_all_selected": (make_case("c", 1, 300, 4, 2, 128, 64, 64, 64), 15),
+    "bf16_window_covers": (make_case("d", 1, 200, 4, 2, 128, 256, 64, 0), 16),
+    "bf16_pure_linear": (make_case("e", 1, 200, 4, 2, 128, 0, 64, 0), 17),
+    "bf16_short_no_chunk": (make_case("f", 2, 50, 4, 2, 128, 64, 64, 16), 18),
+    "bf16_G1": (make_case("g", 1, 400, 2, 2, 128, 64, 64, 16), 19),
+    "bf16_G8": (make_case("h", 1, 320, 8, 1, 128, 64, 64, 8), 20),
+    "f32_lam_gt_C": (make_case("i", 1, 256, 4, 1, 64, 32, 32, 40, dtype="f32"), 21),
+    "bf16_swa_la_W_lt_C": (make_case("j", 1, 300, 4, 1, 128, 40, 64, 0), 22),
+}
+
+
+def run_case(gpu_lib, cfg, seed, general):
+    raw = workloads.make_prefill(cfg, seed)
+    dt = torch_dtype(cfg["dtype"])
+    dev, ref = prepare(raw, dt)
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    res = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W,
+                      chunk=C, topk=lam, return_scores=True, return_sel=True, general=general)
+    torch.cuda.synchronize()
+    p = O.Params(window=W, chunk=C, topk=lam)
+    Hkv = cfg["n_kv_heads"]
+    sigma = O.window_scores(ref["q"], ref["k"], p, Hkv) if W > 0 else np.zeros(
+        (cfg["batch"], Hkv, cfg["seqlen"]))
+    gsel = res["sel_idx"].cpu().numpy().astype(np.int64)
+    override = None
+    if p.topk_eff() > 0:
+        osel, _ = O.select_chunks(sigma, p)
+        n_bad, worst = check_selection(gsel, sigma, osel, C)
+        if n_bad:
+            say(f"  near-tie chunks: {n_bad} (worst margin {worst:.3g}); oracle re-run with GPU picks")
+            override = gsel
+    o = O.fwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"], p,
+                     sel_override=override, scores=sigma)
+    return res, o, sigma
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_fwd_matches_oracle(gpu_lib, name, general):
+    cfg, seed = CASES[name]
+    say(f"[fwd] case={name} general={general} shape={workloads.shape_of(cfg)} seed={seed}")
+    res, o, sigma = run_case(gpu_lib, cfg, seed, general)
+    out = res["out"].double().cpu().numpy()
+    assert np.isfinite(out).all()
+    err = rel_l2(out, o["out"])
+    tol = F32_TOL if cfg["dtype"] == "f32" else BF16_TOL
+    if cfg["window"] > 0:
+        gs = res["scores"].cpu().numpy()
+        serr = float(np.max(np.abs(gs - sigma) / np.maximum(1.0, np.abs(sigma))))
+    else:
+        serr = 0.0
+    say(f"  out rel-L2 {err:.3e} (tol {tol:g}), score max rel err {serr:.3e}")
+    assert err <= tol
+    assert serr <= 1e-4
+
+
+def test_fwd_is_deterministic(gpu_lib):
+    cfg, seed = CASES["bf16_ragged_G4"]
+    raw = workloads.make_prefill(cfg, seed)
+    dev, _ = prepare(raw, torch.bfloat16)
+    runs = [gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=64,
+                        chunk=64, topk=16, return_scores=True, return_sel=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    for key in ("out", "scores", "sel_idx"):
+        assert torch.equal(runs[0][key], runs[1][key]), key
+
+
+def test_empty_sequence_is_noop(gpu_lib):
+    q = torch.zeros((1, 0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((2, 64, 128), dtype=torch.float32, device="cuda")
+    res = gpu_lib.fwd(q, k, k, w, w, window=64, chunk=64, topk=16)
+    assert res["out"].shape == (1, 0, 4, 128)

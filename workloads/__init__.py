@@ -124,3 +124,32 @@ def make_decode_tokens(cfg: dict, seed: int, n_steps: int) -> dict:
     wq = (rng.standard_normal((Hkv, d // 2, d)) * sd).astype(np.float32)
     wk = (rng.standard_normal((Hkv, d // 2, d)) * sd).astype(np.float32)
     return dict(q=q, k=k, v=v, wphi_q=wq, wphi_k=wk)
+
+
+def make_decode_cache(cfg: dict, seed: int, batches=None) -> dict:
+    """Whole-cache arrays in the library's cache layout for the sequences in
+    ``batches`` (default: all), built from the per-stream draws of
+    make_decode_stream.  bf16 callers round sel/win K and V themselves."""
+    B = cfg["batch"] if batches is None else len(batches)
+    bs = list(range(cfg["batch"])) if batches is None else list(batches)
+    Hkv, d, W, C, cap = cfg["n_kv_heads"], cfg["head_dim"], cfg["window"], cfg["chunk"], cfg["sel_cap"]
+    out = dict(
+        win_k=np.zeros((B, Hkv, W, d), np.float32), win_v=np.zeros((B, Hkv, W, d), np.float32),
+        win_route=np.zeros((B, Hkv, W), np.uint8), pend_score=np.zeros((B, Hkv, C), np.float32),
+        sel_k=np.zeros((B, Hkv, cap, d), np.float32), sel_v=np.zeros((B, Hkv, cap, d), np.float32),
+        sel_count=np.zeros((B, Hkv), np.int32), lin_S=np.zeros((B, Hkv, d, d), np.float32),
+        lin_z=np.zeros((B, Hkv, d), np.float32),
+    )
+    for i, b in enumerate(bs):
+        for g in range(Hkv):
+            s = make_decode_stream(cfg, seed, b, g)
+            n = s["sel_count"]
+            out["win_k"][i, g] = s["win_k"]
+            out["win_v"][i, g] = s["win_v"]
+            out["win_route"][i, g] = s["win_route"]
+            out["sel_k"][i, g, :n] = s["sel_k"]
+            out["sel_v"][i, g, :n] = s["sel_v"]
+            out["sel_count"][i, g] = n
+            out["lin_S"][i, g] = s["lin_S"]
+            out["lin_z"][i, g] = s["lin_z"]
+    return out
