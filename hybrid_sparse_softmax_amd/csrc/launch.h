@@ -52,6 +52,23 @@ hipError_t launch_handoff(const Dims& D, const void* k, const void* v, const flo
                           const float* scores, const int32_t* sel_idx, const uint8_t* route,
                           int cap_chunk, const CacheView& c, hipStream_t s);
 
+// ---- gfx950 MFMA forward (bf16, d = d' = 128, window = chunk = 64, topk > 0) ----
+bool mfma_fwd_supported(const Dims& D);
+// scores, top-k, route flags, compact selected K/V [B, Hkv, n_full * lam, d]
+hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const void* v,
+                             float* scores, int32_t* sel_idx, uint8_t* route, void* ksel,
+                             void* vsel, hipStream_t s);
+// phi_k rows [B, Hkv, N, d'] (bf16, features in kperm order) and per-chunk
+// linear sums [B, Hkv, n_full, d + 1, d'] (S^T rows then z, kperm order)
+hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const float* wphi_k,
+                           const uint8_t* route, void* phik, float* lin, hipStream_t s);
+hipError_t launch_la_scan_t(const Dims& D, float* lin, int cap_chunk, float* cap_S, float* cap_z,
+                            hipStream_t s);
+hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
+                              const float* wphi_q, const void* phik, const uint8_t* route,
+                              const void* ksel, const void* vsel, const float* lin, void* out,
+                              hipStream_t s);
+
 // ---- decode step ------------------------------------------------------------
 struct DecodeWork {
     float* la;      // [B, Hq, d + 1]   linear numerator, denominator

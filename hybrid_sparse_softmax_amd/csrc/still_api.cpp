@@ -95,9 +95,35 @@ static FwdBuffers carve_fwd(const Dims& D, Carver& cv) {
     return f;
 }
 
-static size_t fwd_bytes(const Dims& D) {
+struct MfmaBuffers {
+    float *scores, *lin;
+    int32_t* sel;
+    uint8_t* route;
+    void *ksel, *vsel, *phik;
+};
+
+static MfmaBuffers carve_mfma(const Dims& D, Carver& cv) {
+    MfmaBuffers f;
+    const size_t BG = (size_t)D.B * D.Hkv;
+    const size_t nsel = BG * D.n_full * D.lam;
+    f.scores = cv.take<float>(BG * D.N);
+    f.sel = cv.take<int32_t>(nsel);
+    f.route = cv.take<uint8_t>(BG * D.N);
+    f.ksel = cv.take<uint16_t>(nsel * D.d);
+    f.vsel = cv.take<uint16_t>(nsel * D.d);
+    f.phik = cv.take<uint16_t>(BG * D.N * D.fd);
+    f.lin = cv.take<float>(BG * D.n_full * (size_t)(D.d + 1) * D.fd);
+    return f;
+}
+
+static bool use_mfma(const Dims& D, const still_shape* sh) {
+    return !(sh->flags & STILL_FLAG_GENERAL_KERNELS) && mfma_fwd_supported(D);
+}
+
+static size_t fwd_bytes(const Dims& D, const still_shape* sh) {
     Carver cv(nullptr);
-    carve_fwd(D, cv);
+    if (use_mfma(D, sh)) carve_mfma(D, cv);
+    else carve_fwd(D, cv);
     return cv.off + 256;
 }
 
@@ -164,7 +190,8 @@ struct Timeline {
         STILL_TRY(expr);                      \
     } while (0)
 
-static int fwd_launches(const Dims& D, bool with_cache) {
+static int fwd_launches(const Dims& D, const still_shape* sh, bool with_cache) {
+    if (use_mfma(D, sh)) return 4 + (with_cache ? 1 : 0);
     return 6 + (D.W > 0 ? 1 : 0) + (with_cache ? 1 : 0);
 }
 
@@ -185,12 +212,33 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
         st = check_cache(D, cache, D.N, need);
         if (st) return st;
     }
-    const size_t need_ws = fwd_bytes(D);
+    const size_t need_ws = fwd_bytes(D, sh);
     if (!ws || ws_bytes < need_ws) return STILL_ERR_WORKSPACE;
-    if (tl.ev && tl.max_ev < fwd_launches(D, cache != nullptr) + 1) return STILL_ERR_INVALID_ARG;
+    if (tl.ev && tl.max_ev < fwd_launches(D, sh, cache != nullptr) + 1) return STILL_ERR_INVALID_ARG;
 
     void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     Carver cv(wsa);
+    // the hand-off's linear state covers tokens j <= N-1-W: chunks below
+    // floor((N-W)/C) in full, captured by the scan
+    const int cap_chunk = cache ? (D.N > D.W ? D.N - D.W : 0) / D.C - 1 : -1;
+    if (use_mfma(D, sh)) {
+        MfmaBuffers f = carve_mfma(D, cv);
+        float* scores = scores_opt ? scores_opt : f.scores;
+        int32_t* sel = sel_idx_opt ? sel_idx_opt : f.sel;
+        STILL_LAUNCH(tl, s, "win_select",
+                     launch_win_select(D, q, k, v, scores, sel, f.route, f.ksel, f.vsel, s));
+        STILL_LAUNCH(tl, s, "la_state", launch_la_state(D, k, v, wk, f.route, f.phik, f.lin, s));
+        STILL_LAUNCH(tl, s, "la_scan",
+                     launch_la_scan_t(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
+                                      cache ? cache->lin_z : nullptr, s));
+        STILL_LAUNCH(tl, s, "hybrid_main",
+                     launch_hybrid_main(D, q, k, v, wq, f.phik, f.route, f.ksel, f.vsel, f.lin, out, s));
+        if (cache)
+            STILL_LAUNCH(tl, s, "handoff",
+                         launch_handoff(D, k, v, wk, scores, sel, f.route, cap_chunk, view_of(cache), s));
+        STILL_TRY(tl.end(s));
+        return STILL_OK;
+    }
     FwdBuffers f = carve_fwd(D, cv);
     float* scores = scores_opt ? scores_opt : f.scores;
     int32_t* sel = sel_idx_opt ? sel_idx_opt : f.sel;
@@ -200,9 +248,6 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
     if (D.W > 0) STILL_LAUNCH(tl, s, "head_scores", launch_head_scores(D, q, k, f.hs, s));
     STILL_LAUNCH(tl, s, "select", launch_select(D, f.hs, scores, sel, f.route, s));
     STILL_LAUNCH(tl, s, "la_chunk", launch_la_chunks(D, f.phik, v, f.route, f.lin, s));
-    // the hand-off's linear state covers tokens j <= N-1-W: chunks below
-    // floor((N-W)/C) in full, captured by the scan
-    const int cap_chunk = cache ? (D.N > D.W ? D.N - D.W : 0) / D.C - 1 : -1;
     STILL_LAUNCH(tl, s, "la_scan", launch_la_scan(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
                                                   cache ? cache->lin_z : nullptr, s));
     STILL_LAUNCH(tl, s, "main_general",
@@ -300,7 +345,7 @@ int still_fwd_workspace_size(const still_shape* shape, size_t* bytes) {
     if (!bytes) return STILL_ERR_INVALID_ARG;
     const int st = still::check_shape(shape, false);
     if (st) return st;
-    *bytes = still::fwd_bytes(still::make_dims(shape, shape->seqlen));
+    *bytes = still::fwd_bytes(still::make_dims(shape, shape->seqlen), shape);
     return STILL_OK;
 }
 
