@@ -44,6 +44,12 @@ R-AGG     One shared normaliser: SA tokens weigh exp(tau q.k), LA tokens weigh
           phi_q(q).phi_k(k); out = sum w v / sum w  (Fig. 2 "hybrid
           aggregation"; Fig. 1: the context is kept without loss).
 R-SCALE   tau = 1/sqrt(d) unless given.
+
+Parity unpinned: the pages fix neither the exact Self-Saliency formula
+(R-SCORE), nor the exact NP-Map (R-NPMAP), nor the exact weighting of the two
+branches (R-AGG).  The functions implementing them are pinned to closed
+forms, invariants and the method's endpoints (causal softmax, causal linear
+attention, Lemma 1), but the readings themselves are the contract.
 """
 from __future__ import annotations
 
