@@ -45,16 +45,17 @@ constexpr float kLazy = 8.0f;   // rescale only when the running max grows by mo
 enum { kModePrev = 0, kModeDiag = 1, kModeSparse = 2 };
 
 // Q operand of one wave: tokens t0 .. t0+63 of head h; qf[qt][s] holds
-// token t0 + 32 qt + l%32, dims 16 s + 8 (l/32) .. +7 (zero beyond N).
+// token t0 + 32 qt + l%32, dims 16 s + 8 (l/32) .. +7.  Tokens beyond N
+// repeat token N-1 (their outputs are never written).
 __device__ __forceinline__ void load_q(const bf16* __restrict__ q, const Dims& D, int b, int t0,
                                        int h, bf16x8 (&qf)[2][8]) {
     const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        const int t = t0 + 32 * qt + col;
+        const int t = min(t0 + 32 * qt + col, D.N - 1);
         const bf16* row = q + (((size_t)b * D.N + t) * D.Hq + h) * kD + 8 * hf;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) qf[qt][s] = t < D.N ? ld_bf8(row + 16 * s) : zero_bf8();
+        for (int s = 0; s < 8; ++s) qf[qt][s] = ld_bf8(row + 16 * s);
     }
 }
 
@@ -407,15 +408,78 @@ __global__ __launch_bounds__(256) void la_scan_t_kernel(float* __restrict__ lin,
 // ---------------------------------------------------------------------------
 // hybrid output
 // ---------------------------------------------------------------------------
-// Block = NW query heads of KV head g (one wave each) x the 64 tokens of
-// chunk c.  Blocks are issued longest first (largest c); consecutive blocks
-// take different KV heads, so each XCD's L2 keeps few compact lists.
+// What each of the NT threads of a block carries for one 64-row tile between
+// its global loads and its LDS stores: 16-byte pieces of K rows, and 4-row x
+// 8-column blocks of V (transposed on the way into LDS).  Rows at or beyond
+// the tile's valid count nv (>= 1) repeat row nv-1: every address stays in
+// bounds without a branch, and those keys are masked out of every sum.
+template <int NT>
+struct TileRegs {
+    static constexpr int KR = kC * 16 / NT;
+    static constexpr int VR = 16 * 16 / NT;
+    bf16x8 kr[KR];
+    bf16x8 vr[VR][4];
+};
+
+template <int NT>
+__device__ __forceinline__ void tile_fetch(TileRegs<NT>& R, const bf16* __restrict__ ksrc,
+                                           const bf16* __restrict__ vsrc, size_t ld, int nv,
+                                           int tid) {
+#pragma unroll
+    for (int r = 0; r < TileRegs<NT>::KR; ++r) {
+        const int x = tid + NT * r, row = min(x >> 4, nv - 1), piece = x & 15;
+        R.kr[r] = ld_bf8(ksrc + (size_t)row * ld + 8 * piece);
+    }
+#pragma unroll
+    for (int r = 0; r < TileRegs<NT>::VR; ++r) {
+        const int x = tid + NT * r, kq = x >> 4, oct = x & 15;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int row = min(4 * kq + rr, nv - 1);
+            R.vr[r][rr] = ld_bf8(vsrc + (size_t)row * ld + 8 * oct);
+        }
+    }
+}
+
+// K rows into ks[row * kKS + col]; V transposed into vt[col * kVS + kperm(row)]
+template <int NT>
+__device__ __forceinline__ void tile_store(const TileRegs<NT>& R, bf16* __restrict__ ks,
+                                           bf16* __restrict__ vt, int tid) {
+#pragma unroll
+    for (int r = 0; r < TileRegs<NT>::KR; ++r) {
+        const int x = tid + NT * r, row = x >> 4, piece = x & 15;
+        st_bf8(ks + row * kKS + 8 * piece, R.kr[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < TileRegs<NT>::VR; ++r) {
+        const int x = tid + NT * r, kq = x >> 4, oct = x & 15;
+        const int pos = kperm(4 * kq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bf16x4 t4;
+            t4[0] = R.vr[r][0][e];
+            t4[1] = R.vr[r][1][e];
+            t4[2] = R.vr[r][2][e];
+            t4[3] = R.vr[r][3][e];
+            *reinterpret_cast<bf16x4*>(vt + (8 * oct + e) * kVS + pos) = t4;
+        }
+    }
+}
+
+// Block = NW query heads of KV head g (one wave each, 64 queries per wave) x
+// the 64 tokens of chunk c.  Key tiles, in order: chunk c-1, chunk c, then the
+// compact selected rows of chunks <= c-2, 64 at a time; each tile is staged in
+// one of two LDS buffers while the previous one is computed.  Blocks are
+// issued longest first (largest c); consecutive blocks take different KV
+// heads, so each XCD's L2 keeps few compact lists.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ wq, const bf16* __restrict__ phik, const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const float* __restrict__ lin,
     bf16* __restrict__ out, Dims D) {
+    constexpr int NT = NW * 64;
+    constexpr int kBuf = kC * kKS + kD * kVS;  // elements of one K + V^T buffer
     const int HG = D.G / NW;
     const int per_c = D.B * D.Hkv * HG;
     const int c = D.T - 1 - (int)(blockIdx.x / per_c);
@@ -428,31 +492,48 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
     const int t0 = c * kC;
     const size_t bg = (size_t)b * D.Hkv + g;
     const float cl2 = D.tau * kLog2e;
-    constexpr int NT = NW * 64;
 
-    __shared__ __align__(16) bf16 ks_lds[kC * kKS];
-    __shared__ __align__(16) bf16 vt_lds[kD * kVS];
+    __shared__ __align__(16) bf16 smem[2 * kBuf];
 
+    // tiles: 0 = chunk c-1 (c >= 1), 1 = chunk c, 2.. = compact selected rows
+    const int nrows = c >= 2 ? (c - 1) * D.lam : 0;
+    const int ntile = 2 + (nrows + kC - 1) / kC;
+    const int first = c >= 1 ? 0 : 1;
+    const bf16* kb = ksel + bg * (size_t)D.n_full * D.lam * kD;
+    const bf16* vb = vsel + bg * (size_t)D.n_full * D.lam * kD;
+    const size_t ldkv = (size_t)D.Hkv * kD;
+    auto fetch = [&](int i, TileRegs<NT>& R) {
+        if (i < 2) {
+            const int tc = c - 1 + i;
+            const size_t off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
+            tile_fetch<NT>(R, k + off, v + off, ldkv, min(kC, D.N - tc * kC), tid);
+        } else {
+            const int r0 = (i - 2) * kC;
+            tile_fetch<NT>(R, kb + (size_t)r0 * kD, vb + (size_t)r0 * kD, kD, min(kC, nrows - r0), tid);
+        }
+    };
+
+    TileRegs<NT> R;
+    fetch(first, R);
     bf16x8 qf[2][8];
     load_q(q, D, b, t0, h, qf);
+    tile_store<NT>(R, smem, smem + kC * kKS, tid);
+    if (first + 1 < ntile) fetch(first + 1, R);
+    __syncthreads();
 
     // running state per query (lane column): reference point m2 (log2 units,
-    // starts at 0, the linear terms' reference), partial normaliser ls of this
-    // half's rows; O rows = queries, columns = dims
+    // starts at 0, the linear terms' reference), partial normaliser ls of
+    // this half's rows; O^T tiles: rows = dims, column = query
     f32x16 o[2][4];
+    float m2[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f};
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[qt][dt] = zero16();
-    float m2[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f};
+    uint64_t selmask = 0;
 
-    f32x16 wla[2][2];  // linear weights of chunk c-1: rows = keys, column = query
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        wla[kt][0] = zero16();
-        wla[kt][1] = zero16();
-    }
     if (c >= 1) {
+        selmask = __ballot(route[bg * D.N + (t0 - kC) + lane] == kRouteSA);
         f32x16 phi[2][2][2];
         np_map_mfma<2>(qf, wq + (size_t)g * (kD / 2) * kD, phi);
         const float* st = lin + (bg * D.n_full + (c >= 2 ? c - 2 : 0)) * (size_t)((kD + 1) * kD);
@@ -482,23 +563,53 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
                     phb[qt][sgn][f2][0] = pack_acc(phi[qt][sgn][f2], 0);
                     phb[qt][sgn][f2][1] = pack_acc(phi[qt][sgn][f2], 1);
                 }
-        // phi_k(k_j) . phi_q(q_t) for the keys j of chunk c-1
+        {
+            // routed linear tokens of chunk c-1 (offset <= the query's, not
+            // selected): weight phi_k(k_j) . phi_q(q_t) at reference point 0
+            f32x16 wl[2][2];  // rows = keys, column = query
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            const bf16* pk = phik + (bg * D.N + (t0 - kC) + 32 * kt + col) * kD + 8 * hf;
+            for (int kt = 0; kt < 2; ++kt) {
+                wl[kt][0] = zero16();
+                wl[kt][1] = zero16();
+                const bf16* pk = phik + (bg * D.N + (t0 - kC) + 32 * kt + col) * kD + 8 * hf;
 #pragma unroll
-            for (int sgn = 0; sgn < 2; ++sgn)
+                for (int sgn = 0; sgn < 2; ++sgn)
 #pragma unroll
-                for (int f2 = 0; f2 < 2; ++f2)
+                    for (int f2 = 0; f2 < 2; ++f2)
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        const bf16x8 a = ld_bf8(pk + 64 * sgn + 32 * f2 + 16 * s2);
-                        wla[kt][0] = mfma32(a, phb[0][sgn][f2][s2], wla[kt][0]);
-                        wla[kt][1] = mfma32(a, phb[1][sgn][f2][s2], wla[kt][1]);
+                        for (int s2 = 0; s2 < 2; ++s2) {
+                            const bf16x8 a = ld_bf8(pk + 64 * sgn + 32 * f2 + 16 * s2);
+                            wl[kt][0] = mfma32(a, phb[0][sgn][f2][s2], wl[kt][0]);
+                            wl[kt][1] = mfma32(a, phb[1][sgn][f2][s2], wl[kt][1]);
+                        }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) {
+                        const int rk = 32 * kt + acc_row(vv, hf), oq = 32 * qt + col;
+                        const bool la = rk <= oq && !((selmask >> rk) & 1ull);
+                        const float p = la ? wl[kt][qt][vv] : 0.f;
+                        wl[kt][qt][vv] = p;
+                        ls[qt] += p;
                     }
+            const bf16* vt = smem + kC * kKS;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kt = ks >> 1, s2 = ks & 1;
+                const bf16x8 pa0 = pack_acc(wl[kt][0], s2), pa1 = pack_acc(wl[kt][1], s2);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x8 av = ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf);
+                    o[0][dt] = mfma32(av, pa0, o[0][dt]);
+                    o[1][dt] = mfma32(av, pa1, o[1][dt]);
+                }
+            }
         }
         if (c >= 2) {
-            // numerator of the linear prefix: O = phi_q S
+            // numerator of the linear prefix: O^T += S^T phi_q
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -512,16 +623,19 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
                                       hi, lo);
 #pragma unroll
                             for (int qt = 0; qt < 2; ++qt) {
-                                o[qt][dt] = mfma32(phb[qt][sgn][f2][s2], hi, o[qt][dt]);
-                                o[qt][dt] = mfma32(phb[qt][sgn][f2][s2], lo, o[qt][dt]);
+                                o[qt][dt] = mfma32(hi, phb[qt][sgn][f2][s2], o[qt][dt]);
+                                o[qt][dt] = mfma32(lo, phb[qt][sgn][f2][s2], o[qt][dt]);
                             }
                         }
         }
     }
 
-    // one 64-key tile staged in LDS (K rows, V transposed)
-    auto run_tile = [&](auto mode_tag, int nvalid, uint64_t selmask) {
-        constexpr int MODE = decltype(mode_tag)::value;
+    // Softmax terms of one staged tile.  With MASKED, key row rk counts for
+    // query oq when bit rk of (rk > oq ? hi_m : lo_m) is set.
+    auto run_tile = [&](auto masked_tag, const bf16* ks, const bf16* vt, uint64_t hi_m,
+                        uint64_t lo_m) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const bool use_mask = (hi_m & lo_m) != ~0ull;
         f32x16 sc[2][2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -532,7 +646,7 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 a = ld_bf8(ks_lds + (32 * kt + col) * kKS + 16 * s + 8 * hf);
+                const bf16x8 a = ld_bf8(ks + (32 * kt + col) * kKS + 16 * s + 8 * hf);
                 sc[kt][0] = mfma32(a, qf[0][s], sc[kt][0]);
                 sc[kt][1] = mfma32(a, qf[1][s], sc[kt][1]);
             }
@@ -544,52 +658,44 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
             for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    const int rk = 32 * kt + acc_row(vv, hf), oq = 32 * qt + col;
-                    bool sa;
-                    if constexpr (MODE == kModePrev) sa = rk > oq || ((selmask >> rk) & 1ull);
-                    else if constexpr (MODE == kModeDiag) sa = rk <= oq;
-                    else sa = rk < nvalid;
-                    const float x = sa ? sc[kt][qt][vv] * cl2 : kNegInf;
-                    sc[kt][qt][vv] = x;
+                    float x = sc[kt][qt][vv];
+                    if constexpr (MASKED) {
+                        if (use_mask) {
+                            const int rk = 32 * kt + acc_row(vv, hf), oq = 32 * qt + col;
+                            const uint64_t m = rk > oq ? hi_m : lo_m;
+                            if (!((m >> rk) & 1ull)) x = kNegInf;
+                            sc[kt][qt][vv] = x;
+                        }
+                    }
                     tmax[qt] = fmaxf(tmax[qt], x);
                 }
-        tmax[0] = fmaxf(tmax[0], xor32(tmax[0]));
-        tmax[1] = fmaxf(tmax[1], xor32(tmax[1]));
-        const bool need = tmax[0] > m2[0] + kLazy || tmax[1] > m2[1] + kLazy;
-        if (__any(need)) {
+        float tm2[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) tm2[qt] = fmaxf(tmax[qt], xor32(tmax[qt])) * cl2;
+        if (__any(tm2[0] > m2[0] + kLazy || tm2[1] > m2[1] + kLazy)) {
             float al[2];
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
-                const float mn = fmaxf(m2[qt], tmax[qt]);
-                al[qt] = exp2f(m2[qt] - mn);
+                const float mn = fmaxf(m2[qt], tm2[qt]);
+                al[qt] = __builtin_amdgcn_exp2f(m2[qt] - mn);
                 m2[qt] = mn;
                 ls[qt] *= al[qt];
             }
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-                for (int vv = 0; vv < 16; ++vv) {
-                    const float a = __shfl(al[qt], acc_row(vv, hf), kWave);
+                for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) o[qt][dt][vv] *= a;
-                }
+                    for (int vv = 0; vv < 16; ++vv) o[qt][dt][vv] *= al[qt];
         }
-        float fla[2] = {0.f, 0.f};
-        if constexpr (MODE == kModePrev) {
-            fla[0] = exp2f(-m2[0]);
-            fla[1] = exp2f(-m2[1]);
-        }
+        const float nm0 = -m2[0], nm1 = -m2[1];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    const float x = sc[kt][qt][vv];
-                    float p = exp2f(x - m2[qt]);
-                    if constexpr (MODE == kModePrev) {
-                        if (x == kNegInf) p = wla[kt][qt][vv] * fla[qt];  // routed to linear attention
-                    }
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][qt][vv], cl2, qt ? nm1 : nm0));
                     sc[kt][qt][vv] = p;
                     ls[qt] += p;
                 }
@@ -599,61 +705,55 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
             const bf16x8 pa0 = pack_acc(sc[kt][0], s2), pa1 = pack_acc(sc[kt][1], s2);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const bf16x8 bv = ld_bf8(vt_lds + (32 * dt + col) * kVS + 16 * ks + 8 * hf);
-                o[0][dt] = mfma32(pa0, bv, o[0][dt]);
-                o[1][dt] = mfma32(pa1, bv, o[1][dt]);
+                const bf16x8 av = ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf);
+                o[0][dt] = mfma32(av, pa0, o[0][dt]);
+                o[1][dt] = mfma32(av, pa1, o[1][dt]);
             }
         }
     };
 
-    const size_t ldkv = (size_t)D.Hkv * kD;
-    if (c >= 1) {
-        const uint8_t rf = route[bg * D.N + (t0 - kC) + lane];
-        const uint64_t selmask = __ballot(rf == kRouteSA);
-        const size_t off = (((size_t)b * D.N + (t0 - kC)) * D.Hkv + g) * kD;
-        load_k_tile(k + off, ldkv, kC, ks_lds, tid, NT);
-        load_vt_tile(v + off, ldkv, kC, vt_lds, tid, NT);
-        __syncthreads();
-        run_tile(std::integral_constant<int, kModePrev>{}, kC, selmask);
-        __syncthreads();
-    }
-    {
-        const int nvalid = min(kC, D.N - t0);
-        const size_t off = (((size_t)b * D.N + t0) * D.Hkv + g) * kD;
-        load_k_tile(k + off, ldkv, nvalid, ks_lds, tid, NT);
-        load_vt_tile(v + off, ldkv, nvalid, vt_lds, tid, NT);
-        __syncthreads();
-        run_tile(std::integral_constant<int, kModeDiag>{}, nvalid, 0ull);
-    }
-    if (c >= 2) {
-        const int nrows = (c - 1) * D.lam;
-        const bf16* kb = ksel + bg * (size_t)D.n_full * D.lam * kD;
-        const bf16* vb = vsel + bg * (size_t)D.n_full * D.lam * kD;
-        for (int r0 = 0; r0 < nrows; r0 += kC) {
-            const int nv = min(kC, nrows - r0);
-            __syncthreads();
-            load_k_tile(kb + (size_t)r0 * kD, kD, nv, ks_lds, tid, NT);
-            load_vt_tile(vb + (size_t)r0 * kD, kD, nv, vt_lds, tid, NT);
-            __syncthreads();
-            run_tile(std::integral_constant<int, kModeSparse>{}, nv, 0ull);
+    for (int i = first; i < ntile; ++i) {
+        const int cur = (i - first) & 1;
+        const bf16* ks = smem + cur * kBuf;
+        const bf16* vt = ks + kC * kKS;
+        uint64_t hm, lm;
+        if (i == 0) { hm = ~0ull; lm = selmask; }
+        else if (i == 1) { hm = 0ull; lm = ~0ull; }
+        else { const int nv = min(kC, nrows - (i - 2) * kC); hm = lm = nv == kC ? ~0ull : (1ull << nv) - 1ull; }
+        run_tile(std::true_type{}, ks, vt, hm, lm);
+        if (i + 1 < ntile) {
+            bf16* nb = smem + (cur ^ 1) * kBuf;
+            tile_store<NT>(R, nb, nb + kC * kKS, tid);
+            if (i + 2 < ntile) fetch(i + 2, R);
         }
+        __syncthreads();
     }
 
+    // epilogue: normalise, stage each wave's 64 x 128 tile in LDS, write rows
     float il[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) il[qt] = 1.f / (ls[qt] + xor32(ls[qt]));
+    bf16* ot = smem + wave * (kC * kKS);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int vv = 0; vv < 16; ++vv) {
-            const float a = __shfl(il[qt], acc_row(vv, hf), kWave);
-            const int t = t0 + 32 * qt + acc_row(vv, hf);
-            if (t < D.N) {
-                bf16* orow = out + (((size_t)b * D.N + t) * D.Hq + h) * kD + col;
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) orow[32 * dt] = (bf16)(o[qt][dt][vv] * a);
+            for (int v4 = 0; v4 < 4; ++v4) {
+                // dims 32 dt + acc_row(4 v4 .. 4 v4 + 3) are consecutive
+                bf16x4 t4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t4[j] = (bf16)(o[qt][dt][4 * v4 + j] * il[qt]);
+                *reinterpret_cast<bf16x4*>(ot + (32 * qt + col) * kKS + 32 * dt + acc_row(4 * v4, hf)) = t4;
             }
-        }
+    __syncthreads();
+    const int nq = min(kC, D.N - t0);
+    for (int x = lane; x < kC * 16; x += kWave) {
+        const int row = x >> 4, piece = x & 15;
+        if (row < nq)
+            st_bf8(out + (((size_t)b * D.N + t0 + row) * D.Hq + h) * kD + 8 * piece,
+                   ld_bf8(ot + row * kKS + 8 * piece));
+    }
 }
 
 }  // namespace
