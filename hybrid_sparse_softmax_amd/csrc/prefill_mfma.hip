@@ -201,48 +201,49 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
         for (int qt = 0; qt < 2; ++qt) {
             bf16x8 qf[8];
             {
-                const int t = t0 + 32 * qt + col;
+                const int t = min(t0 + 32 * qt + col, D.N - 1);
                 const bf16* row = q + (((size_t)b * D.N + t) * D.Hq + h) * kD + 8 * hf;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) qf[s] = t < D.N ? ld_bf8(row + 16 * s) : zero_bf8();
+                for (int s = 0; s < 8; ++s) qf[s] = ld_bf8(row + 16 * s);
             }
-            // logits against keys t0-64 .. t0+63: key index kk = 32 kt + row
-            f32x16 sc[4];
+            // logits against keys t0-64 .. t0+63 (key index kk = 32 kt + row);
+            // the window of query offset qo is kk in [qo+1, qo+64], inside key
+            // subtiles kt = qt .. qt+2
+            f32x16 sc[3];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) sc[kt] = zero16();
+            for (int j = 0; j < 3; ++j) sc[j] = zero16();
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const int key = t0 - kC + 32 * kt + col;
-                    const bf16x8 a = (key >= 0 && key < D.N)
-                                         ? ld_bf8(k + (((size_t)b * D.N + key) * D.Hkv + g) * kD + 16 * s + 8 * hf)
-                                         : zero_bf8();
-                    sc[kt] = mfma32(a, qf[s], sc[kt]);
+                for (int j = 0; j < 3; ++j) {
+                    const int key = max(0, t0 - kC + 32 * (qt + j) + col);
+                    const bf16x8 a = ld_bf8(k + (((size_t)b * D.N + min(key, D.N - 1)) * D.Hkv + g) * kD +
+                                            16 * s + 8 * hf);
+                    sc[j] = mfma32(a, qf[s], sc[j]);
                 }
             }
             const int qo = 32 * qt + col;  // query offset in the chunk; its own key is kk = qo + 64
             float mx = kNegInf;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int j = 0; j < 3; ++j)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    const int kk = 32 * kt + acc_row(vv, hf);
+                    const int kk = 32 * (qt + j) + acc_row(vv, hf);
                     const bool ok = kk >= qo + 1 && kk <= qo + kC && t0 - kC + kk >= 0;
-                    const float x = ok ? D.tau * sc[kt][vv] : kNegInf;
-                    sc[kt][vv] = x;
+                    const float x = ok ? D.tau * sc[j][vv] : kNegInf;
+                    sc[j][vv] = x;
                     mx = fmaxf(mx, x);
                 }
             mx = fmaxf(mx, xor32(mx));
             float sa = 0.f, so = 0.f, et = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int j = 0; j < 3; ++j)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    const int kk = 32 * kt + acc_row(vv, hf);
-                    const float x = sc[kt][vv];
+                    const int kk = 32 * (qt + j) + acc_row(vv, hf);
+                    const float x = sc[j][vv];
                     const float e = x == kNegInf ? 0.f : expf(x - mx);
-                    sc[kt][vv] = e;
+                    sc[j][vv] = e;
                     sa += e;
                     if (kk == qo + kC) et += e;
                     else so += e;
@@ -250,13 +251,28 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
             sa += xor32(sa);
             so += xor32(so);
             et += xor32(et);
+            // Score = sum_j a_j ln((a_j + eps) / (a~_j + eps)) with a_j = e_j / sa
+            // and the leave-one-out a~_j = e_j / so (j != t), a~_t = 0:
+            //   own key:    a_t log1p(a_t / eps)
+            //   other keys: -a_j log1p(r e_j / (e_j + eps sa)),  r = e_t / so
+            const float isa = 1.f / sa;
+            const float r = so > 0.f ? et / so : 0.f;
+            const float esa = D.eps * sa;
             float term = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int j = 0; j < 3; ++j)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    const int kk = 32 * kt + acc_row(vv, hf);
-                    term += saliency_term(sc[kt][vv], kk == qo + kC, et, sa, so, D.eps);
+                    const int kk = 32 * (qt + j) + acc_row(vv, hf);
+                    const float e = sc[j][vv];
+                    float tj;
+                    if (kk == qo + kC) {
+                        const float at = e * isa;
+                        tj = at * log1pf(at / D.eps);
+                    } else {
+                        tj = -(e * isa) * log1pf(__fdividef(r * e, e + esa));
+                    }
+                    term += e > 0.f ? tj : 0.f;
                 }
             term += xor32(term);
             if (hf == 0) hsc[hh][qo] = term;
@@ -384,23 +400,34 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
 }
 
 // Inclusive prefix over complete chunks, in place; chunk cap_chunk is also
-// copied into the decode cache's lin_S [f][dim] / lin_z [f].
+// copied into the decode cache's lin_S [f][dim] / lin_z [f].  Each thread
+// owns one entry and keeps 16 chunks' loads in flight.
 __global__ __launch_bounds__(256) void la_scan_t_kernel(float* __restrict__ lin, int cap_chunk,
                                                         float* __restrict__ cap_S,
                                                         float* __restrict__ cap_z, Dims D) {
     constexpr int E1 = (kD + 1) * kD;
+    constexpr int kDepth = 16;
     const int e = blockIdx.x * 256 + threadIdx.x, g = blockIdx.y, b = blockIdx.z;
     if (e >= E1) return;
     const size_t bg = (size_t)b * D.Hkv + g;
     float* base = lin + bg * D.n_full * (size_t)E1 + e;
     float run = 0.f;
-    for (int c = 0; c < D.n_full; ++c) {
-        run += base[(size_t)c * E1];
-        base[(size_t)c * E1] = run;
-        if (c == cap_chunk && cap_S) {
-            const int row = e / kD, f = kperm(e % kD);
-            if (row < kD) cap_S[(bg * kD + f) * kD + row] = run;
-            else cap_z[bg * kD + f] = run;
+    for (int c0 = 0; c0 < D.n_full; c0 += kDepth) {
+        const int n = min(kDepth, D.n_full - c0);
+        float x[kDepth];
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) x[i] = i < n ? base[(size_t)(c0 + i) * E1] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) {
+            if (i < n) {
+                run += x[i];
+                base[(size_t)(c0 + i) * E1] = run;
+                if (c0 + i == cap_chunk && cap_S) {
+                    const int row = e / kD, f = kperm(e % kD);
+                    if (row < kD) cap_S[(bg * kD + f) * kD + row] = run;
+                    else cap_z[bg * kD + f] = run;
+                }
+            }
         }
     }
 }
@@ -630,11 +657,9 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
         }
     }
 
-    // Softmax terms of one staged tile.  With MASKED, key row rk counts for
-    // query oq when bit rk of (rk > oq ? hi_m : lo_m) is set.
-    auto run_tile = [&](auto masked_tag, const bf16* ks, const bf16* vt, uint64_t hi_m,
-                        uint64_t lo_m) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
+    // Softmax terms of one staged tile: key row rk counts for query oq when
+    // bit rk of (rk > oq ? hi_m : lo_m) is set.
+    auto run_tile = [&](const bf16* ks, const bf16* vt, uint64_t hi_m, uint64_t lo_m) {
         const bool use_mask = (hi_m & lo_m) != ~0ull;
         f32x16 sc[2][2];
 #pragma unroll
@@ -651,6 +676,20 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
                 sc[kt][1] = mfma32(a, qf[1][s], sc[kt][1]);
             }
         }
+        if (use_mask) {
+            // edge tiles only: masked key rows drop out of the softmax
+            __asm__ volatile("");
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) {
+                        const int rk = 32 * kt + acc_row(vv, hf), oq = 32 * qt + col;
+                        const uint64_t m = rk > oq ? hi_m : lo_m;
+                        if (!((m >> rk) & 1ull)) sc[kt][qt][vv] = kNegInf;
+                    }
+        }
         float tmax[2] = {kNegInf, kNegInf};
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -658,21 +697,14 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
             for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    float x = sc[kt][qt][vv];
-                    if constexpr (MASKED) {
-                        if (use_mask) {
-                            const int rk = 32 * kt + acc_row(vv, hf), oq = 32 * qt + col;
-                            const uint64_t m = rk > oq ? hi_m : lo_m;
-                            if (!((m >> rk) & 1ull)) x = kNegInf;
-                            sc[kt][qt][vv] = x;
-                        }
-                    }
-                    tmax[qt] = fmaxf(tmax[qt], x);
+                    tmax[qt] = fmaxf(tmax[qt], sc[kt][qt][vv]);
                 }
         float tm2[2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) tm2[qt] = fmaxf(tmax[qt], xor32(tmax[qt])) * cl2;
         if (__any(tm2[0] > m2[0] + kLazy || tm2[1] > m2[1] + kLazy)) {
+            // a rare path: keep the compiler from speculating it into every tile
+            __asm__ volatile("");
             float al[2];
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
@@ -712,6 +744,9 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
         }
     };
 
+    // settle every outstanding load (Q, the first prefetch) here, once: the
+    // loop then only ever waits for its own prefetch, at the LDS store
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     for (int i = first; i < ntile; ++i) {
         const int cur = (i - first) & 1;
         const bf16* ks = smem + cur * kBuf;
@@ -720,7 +755,7 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
         if (i == 0) { hm = ~0ull; lm = selmask; }
         else if (i == 1) { hm = 0ull; lm = ~0ull; }
         else { const int nv = min(kC, nrows - (i - 2) * kC); hm = lm = nv == kC ? ~0ull : (1ull << nv) - 1ull; }
-        run_tile(std::true_type{}, ks, vt, hm, lm);
+        run_tile(ks, vt, hm, lm);
         if (i + 1 < ntile) {
             bf16* nb = smem + (cur ^ 1) * kBuf;
             tile_store<NT>(R, nb, nb + kC * kKS, tid);
