@@ -84,4 +84,12 @@ hipError_t launch_decode_sel(const Dims& D, const void* q, const CacheView& c, c
                              hipStream_t s);
 hipError_t launch_decode_combine(const Dims& D, const DecodeWork& w, void* out, hipStream_t s);
 
+// ---- fast decode step (bf16, d = d' = 128, window 1..64, G in {1,2,4,8}) --------
+bool fast_decode_supported(const Dims& D);
+int fast_decode_splits(int cap);                     // stream splits of 1024 selected rows
+size_t fast_decode_floats(const Dims& D, int nsplit);  // workspace, in floats
+hipError_t launch_fast_decode(const Dims& D, const void* q, const void* k, const void* v,
+                              const float* wq, const float* wk, const CacheView& c, float* ws,
+                              int nsplit, void* out, int phase, hipStream_t s);  // phase 0, then 1
+
 }  // namespace still

@@ -274,7 +274,12 @@ static DecodeWork carve_decode(const Dims& D, int cap, Carver& cv) {
     return w;
 }
 
-static size_t decode_bytes(const Dims& D, int cap) {
+static bool use_fast_decode(const Dims& D, const still_shape* sh) {
+    return !(sh->flags & STILL_FLAG_GENERAL_KERNELS) && fast_decode_supported(D);
+}
+
+static size_t decode_bytes(const Dims& D, const still_shape* sh, int cap) {
+    if (use_fast_decode(D, sh)) return fast_decode_floats(D, fast_decode_splits(cap)) * sizeof(float) + 256;
     Carver cv(nullptr);
     carve_decode(D, cap, cv);
     return cv.off + 256;
@@ -299,10 +304,20 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
     st = check_cache(D, cache, -1, need);
     if (st) return st;
     if (D.lam > 0 && cache->sel_cap < 1) return STILL_ERR_CAPACITY;
-    const size_t need_ws = decode_bytes(D, cache->sel_cap);
+    const size_t need_ws = decode_bytes(D, sh, cache->sel_cap);
     if (!ws || ws_bytes < need_ws) return STILL_ERR_WORKSPACE;
     if (tl.ev && tl.max_ev < 4) return STILL_ERR_INVALID_ARG;
     void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    if (use_fast_decode(D, sh)) {
+        const CacheView cvw = view_of(cache);
+        const int nsplit = fast_decode_splits(cache->sel_cap);
+        float* fw = static_cast<float*>(wsa);
+        STILL_LAUNCH(tl, s, "dec_stream", launch_fast_decode(D, q, k, v, wq, wk, cvw, fw, nsplit, out, 0, s));
+        STILL_LAUNCH(tl, s, "dec_combine", launch_fast_decode(D, q, k, v, wq, wk, cvw, fw, nsplit, out, 1, s));
+        STILL_TRY(tl.end(s));
+        cache->pos = t + 1;
+        return STILL_OK;
+    }
     Carver cv(wsa);
     DecodeWork w = carve_decode(D, cache->sel_cap, cv);
     const CacheView cvw = view_of(cache);
@@ -379,7 +394,7 @@ int still_decode_workspace_size(const still_shape* shape, int32_t sel_cap, size_
     if (!bytes || sel_cap < 0) return STILL_ERR_INVALID_ARG;
     const int st = still::check_shape(shape, true);
     if (st) return st;
-    *bytes = still::decode_bytes(still::make_dims(shape, 1), sel_cap);
+    *bytes = still::decode_bytes(still::make_dims(shape, 1), shape, sel_cap);
     return STILL_OK;
 }
 
