@@ -29,6 +29,40 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 METRIC = "hybrid-attn layer tokens/s (Llama-3-8B shape, 16K prefill; decode) + % roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# sources that define each measured kernel: a stored counter reading is used
+# only while their hash is unchanged
+KERNEL_SOURCES = {
+    "hybrid_main": ["hybrid_sparse_softmax_amd/csrc/prefill_mfma.hip",
+                    "hybrid_sparse_softmax_amd/csrc/mfma_common.h"],
+    "dec_stream": ["hybrid_sparse_softmax_amd/csrc/decode_fast.hip"],
+}
+
+
+def sources_sha(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each divided by what the same counter
+    reads per byte of a plain copy), or None when there is no reading for
+    this workload or the kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("workload") != workload or rec.get("sources_sha256") != sources_sha(kernel):
+        return None
+    fetch = rec["fetch_kib"] * 1024.0 / rec["copy_fetch_per_byte"]
+    write = rec["write_kib"] * 1024.0 / rec["copy_write_per_byte"]
+    return round(fetch + write)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
@@ -130,7 +164,7 @@ def bench_prefill(still, torch, name, steps, warmup):
         achieved = alg / (kern[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "kernel": dom, "avg_ms": round(kern[dom], 4),
+                "traffic": measured_traffic(dom, name), "kernel": dom, "avg_ms": round(kern[dom], 4),
                 "algorithmic_flop_per_launch": alg}
     total_alg = sum(v for k, v in flops.items() if k != "score_qk")
     return dict(cfg=cfg, raw=raw, ms=ms, kern=kern, roof=roof, flops=flops,
@@ -190,10 +224,12 @@ def bench_decode(still, torch, steps, warmup):
     mid = (sel_before.astype(np.float64) + sel_after) / 2
     by = decode_bytes(cfg, mid)
     dom = max(kern, key=kern.get)
+    # the general path's split-KV kernel moves only the selected rows; the
+    # fast path's stream kernel does every step's memory work but the merge
     dom_bytes = by["sel"] + float(B * Hq) * d * 2 if dom.startswith("decode_sel") else by["total"]
     achieved = dom_bytes / (kern[dom] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom, name), "kernel": dom,
             "avg_ms": round(kern[dom], 4), "algorithmic_bytes_per_launch": dom_bytes}
     step_gbs = by["total"] / (ms * 1e-3) / 1e9
     return {"metric": "decode tokens/s (batch 64 at position 16384)", "value": round(B / (ms * 1e-3), 1),
@@ -246,6 +282,10 @@ def main():
     ap.add_argument("--workload", default="prefill_16k", choices=["prefill_4k", "prefill_16k", "train_8x2k"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode step and print its JSON object")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 256 MiB device copy three times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the STILL operator here runs on a single MI355X "
@@ -258,6 +298,19 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     still.lib()
+    if args.calibrate_copy:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}),
+              flush=True)
+        return
+    if args.decode_only:
+        print(json.dumps(bench_decode(still, torch, args.steps, args.warmup)), flush=True)
+        return
     pre = bench_prefill(still, torch, args.workload, args.steps, args.warmup)
     cfg = pre["cfg"]
     dec = None if args.no_decode else bench_decode(still, torch, args.steps, args.warmup)
