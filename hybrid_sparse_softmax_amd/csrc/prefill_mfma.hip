@@ -435,35 +435,47 @@ __global__ __launch_bounds__(256) void la_scan_t_kernel(float* __restrict__ lin,
 // ---------------------------------------------------------------------------
 // hybrid output
 // ---------------------------------------------------------------------------
-// What each of the NT threads of a block carries for one 64-row tile between
-// its global loads and its LDS stores: 16-byte pieces of K rows, and 4-row x
-// 8-column blocks of V (transposed on the way into LDS).  Rows at or beyond
-// the tile's valid count nv (>= 1) repeat row nv-1: every address stays in
-// bounds without a branch, and those keys are masked out of every sum.
+// What the NT threads of a block carry for one 64-row tile between its global
+// loads and its LDS stores: 1024 16-byte pieces of K rows and 256 blocks of
+// 4 V rows x 8 columns (transposed on the way into LDS).  With 512 threads
+// the first 256 take K and the rest V.  Rows at or beyond the tile's valid
+// count nv (>= 1) repeat row nv-1: every address stays in bounds without a
+// branch, and those keys are masked out of every sum.
 template <int NT>
 struct TileRegs {
-    static constexpr int KR = kC * 16 / NT;
-    static constexpr int VR = 16 * 16 / NT;
-    bf16x8 kr[KR];
-    bf16x8 vr[VR][4];
+    static constexpr bool kSplit = NT == 512;
+    static constexpr int KR = kSplit ? 4 : 1024 / NT;  // K pieces per thread
+    static constexpr int VU = kSplit ? 1 : 256 / NT;   // V blocks per thread
+    static constexpr int N = kSplit ? 4 : KR + 4 * VU;
+    bf16x8 r[N];
 };
 
 template <int NT>
 __device__ __forceinline__ void tile_fetch(TileRegs<NT>& R, const bf16* __restrict__ ksrc,
                                            const bf16* __restrict__ vsrc, size_t ld, int nv,
                                            int tid) {
+    using TR = TileRegs<NT>;
+    const bool do_k = !TR::kSplit || tid < 256;
+    const bool do_v = !TR::kSplit || tid >= 256;
+    const int kt0 = TR::kSplit ? tid : tid, vt0 = TR::kSplit ? tid - 256 : tid;
+    constexpr int kstride = TR::kSplit ? 256 : NT, vstride = TR::kSplit ? 256 : NT;
+    if (do_k) {
 #pragma unroll
-    for (int r = 0; r < TileRegs<NT>::KR; ++r) {
-        const int x = tid + NT * r, row = min(x >> 4, nv - 1), piece = x & 15;
-        R.kr[r] = ld_bf8(ksrc + (size_t)row * ld + 8 * piece);
+        for (int i = 0; i < TR::KR; ++i) {
+            const int x = kt0 + kstride * i, row = min(x >> 4, nv - 1), piece = x & 15;
+            R.r[i] = ld_bf8(ksrc + (size_t)row * ld + 8 * piece);
+        }
     }
+    if (do_v) {
+        constexpr int base = TR::kSplit ? 0 : TR::KR;
 #pragma unroll
-    for (int r = 0; r < TileRegs<NT>::VR; ++r) {
-        const int x = tid + NT * r, kq = x >> 4, oct = x & 15;
+        for (int j = 0; j < TR::VU; ++j) {
+            const int u = vt0 + vstride * j, kq = u >> 4, oct = u & 15;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = min(4 * kq + rr, nv - 1);
-            R.vr[r][rr] = ld_bf8(vsrc + (size_t)row * ld + 8 * oct);
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = min(4 * kq + rr, nv - 1);
+                R.r[base + 4 * j + rr] = ld_bf8(vsrc + (size_t)row * ld + 8 * oct);
+            }
         }
     }
 }
@@ -472,42 +484,54 @@ __device__ __forceinline__ void tile_fetch(TileRegs<NT>& R, const bf16* __restri
 template <int NT>
 __device__ __forceinline__ void tile_store(const TileRegs<NT>& R, bf16* __restrict__ ks,
                                            bf16* __restrict__ vt, int tid) {
+    using TR = TileRegs<NT>;
+    const bool do_k = !TR::kSplit || tid < 256;
+    const bool do_v = !TR::kSplit || tid >= 256;
+    const int kt0 = tid, vt0 = TR::kSplit ? tid - 256 : tid;
+    constexpr int kstride = TR::kSplit ? 256 : NT, vstride = TR::kSplit ? 256 : NT;
+    if (do_k) {
 #pragma unroll
-    for (int r = 0; r < TileRegs<NT>::KR; ++r) {
-        const int x = tid + NT * r, row = x >> 4, piece = x & 15;
-        st_bf8(ks + row * kKS + 8 * piece, R.kr[r]);
+        for (int i = 0; i < TR::KR; ++i) {
+            const int x = kt0 + kstride * i, row = x >> 4, piece = x & 15;
+            st_bf8(ks + row * kKS + 8 * piece, R.r[i]);
+        }
     }
+    if (do_v) {
+        constexpr int base = TR::kSplit ? 0 : TR::KR;
 #pragma unroll
-    for (int r = 0; r < TileRegs<NT>::VR; ++r) {
-        const int x = tid + NT * r, kq = x >> 4, oct = x & 15;
-        const int pos = kperm(4 * kq);
+        for (int j = 0; j < TR::VU; ++j) {
+            const int u = vt0 + vstride * j, kq = u >> 4, oct = u & 15;
+            const int pos = kperm(4 * kq);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 t4;
-            t4[0] = R.vr[r][0][e];
-            t4[1] = R.vr[r][1][e];
-            t4[2] = R.vr[r][2][e];
-            t4[3] = R.vr[r][3][e];
-            *reinterpret_cast<bf16x4*>(vt + (8 * oct + e) * kVS + pos) = t4;
+            for (int e = 0; e < 8; ++e) {
+                bf16x4 t4;
+                t4[0] = R.r[base + 4 * j + 0][e];
+                t4[1] = R.r[base + 4 * j + 1][e];
+                t4[2] = R.r[base + 4 * j + 2][e];
+                t4[3] = R.r[base + 4 * j + 3][e];
+                *reinterpret_cast<bf16x4*>(vt + (8 * oct + e) * kVS + pos) = t4;
+            }
         }
     }
 }
 
-// Block = NW query heads of KV head g (one wave each, 64 queries per wave) x
-// the 64 tokens of chunk c.  Key tiles, in order: chunk c-1, chunk c, then the
-// compact selected rows of chunks <= c-2, 64 at a time; each tile is staged in
-// one of two LDS buffers while the previous one is computed.  Blocks are
-// issued longest first (largest c); consecutive blocks take different KV
-// heads, so each XCD's L2 keeps few compact lists.
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
+// Block = HB query heads of KV head g x the 64 tokens of chunk c; two waves
+// per head, each owning 32 queries, so two waves share every SIMD and one's
+// softmax arithmetic overlaps the other's matrix products.  Key tiles, in
+// order: chunk c-1, chunk c, then the compact selected rows of chunks <= c-2,
+// 64 at a time; each tile is staged in one of two LDS buffers while the
+// previous one is computed.  Blocks are issued longest first (largest c);
+// consecutive blocks take different KV heads, so each XCD's L2 keeps few
+// compact lists.
+template <int HB>
+__global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ wq, const bf16* __restrict__ phik, const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const float* __restrict__ lin,
     bf16* __restrict__ out, Dims D) {
-    constexpr int NT = NW * 64;
+    constexpr int NT = HB * 128;
     constexpr int kBuf = kC * kKS + kD * kVS;  // elements of one K + V^T buffer
-    const int HG = D.G / NW;
+    const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
     const int c = D.T - 1 - (int)(blockIdx.x / per_c);
     int r = (int)(blockIdx.x % per_c);
@@ -515,8 +539,10 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
     r /= HG;
     const int g = r % D.Hkv, b = r / D.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
-    const int h = g * D.G + hg * NW + wave;
+    const int qh = wave & 1;                       // which 32 queries of the chunk
+    const int h = g * D.G + hg * HB + (wave >> 1);
     const int t0 = c * kC;
+    const int oq = 32 * qh + col;                  // this lane's query offset in the chunk
     const size_t bg = (size_t)b * D.Hkv + g;
     const float cl2 = D.tau * kLog2e;
 
@@ -542,97 +568,87 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
 
     TileRegs<NT> R;
     fetch(first, R);
-    bf16x8 qf[2][8];
-    load_q(q, D, b, t0, h, qf);
+    // Q operand: qf[s] holds query t0 + oq (tokens past N repeat N-1, never
+    // written), dims 16 s + 8 hf .. +7
+    bf16x8 qf[1][8];
+    {
+        const int t = min(t0 + oq, D.N - 1);
+        const bf16* row = q + (((size_t)b * D.N + t) * D.Hq + h) * kD + 8 * hf;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[0][s] = ld_bf8(row + 16 * s);
+    }
     tile_store<NT>(R, smem, smem + kC * kKS, tid);
     if (first + 1 < ntile) fetch(first + 1, R);
     __syncthreads();
 
-    // running state per query (lane column): reference point m2 (log2 units,
+    // running state of the lane's query: reference point m2 (log2 units,
     // starts at 0, the linear terms' reference), partial normaliser ls of
-    // this half's rows; O^T tiles: rows = dims, column = query
-    f32x16 o[2][4];
-    float m2[2] = {0.f, 0.f}, ls[2] = {0.f, 0.f};
+    // this half's rows; O^T tiles o[dt]: rows = dims 32 dt + .., column = query
+    f32x16 o[4];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[qt][dt] = zero16();
+    for (int dt = 0; dt < 4; ++dt) o[dt] = zero16();
+    float m2 = 0.f, ls = 0.f;
     uint64_t selmask = 0;
 
     if (c >= 1) {
         selmask = __ballot(route[bg * D.N + (t0 - kC) + lane] == kRouteSA);
-        f32x16 phi[2][2][2];
-        np_map_mfma<2>(qf, wq + (size_t)g * (kD / 2) * kD, phi);
+        f32x16 phi[1][2][2];
+        np_map_mfma<1>(qf, wq + (size_t)g * (kD / 2) * kD, phi);
         const float* st = lin + (bg * D.n_full + (c >= 2 ? c - 2 : 0)) * (size_t)((kD + 1) * kD);
         if (c >= 2) {
             // normaliser of the linear prefix (chunks <= c-2): phi_q . z
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                float acc = 0.f;
-#pragma unroll
-                for (int sgn = 0; sgn < 2; ++sgn)
-#pragma unroll
-                    for (int f2 = 0; f2 < 2; ++f2)
-#pragma unroll
-                        for (int vv = 0; vv < 16; ++vv)
-                            acc = fmaf(st[kD * kD + kperm(64 * sgn + 32 * f2 + acc_row(vv, hf))],
-                                       phi[qt][sgn][f2][vv], acc);
-                ls[qt] = acc;
-            }
-        }
-        bf16x8 phb[2][2][2][2];  // [qt][sgn][ft][s2]
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+            float acc = 0.f;
 #pragma unroll
             for (int sgn = 0; sgn < 2; ++sgn)
 #pragma unroll
-                for (int f2 = 0; f2 < 2; ++f2) {
-                    phb[qt][sgn][f2][0] = pack_acc(phi[qt][sgn][f2], 0);
-                    phb[qt][sgn][f2][1] = pack_acc(phi[qt][sgn][f2], 1);
-                }
+                for (int f2 = 0; f2 < 2; ++f2)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv)
+                        acc = fmaf(st[kD * kD + kperm(64 * sgn + 32 * f2 + acc_row(vv, hf))],
+                                   phi[0][sgn][f2][vv], acc);
+            ls = acc;
+        }
+        bf16x8 phb[2][2][2];  // [sgn][ft][s2]
+#pragma unroll
+        for (int sgn = 0; sgn < 2; ++sgn)
+#pragma unroll
+            for (int f2 = 0; f2 < 2; ++f2) {
+                phb[sgn][f2][0] = pack_acc(phi[0][sgn][f2], 0);
+                phb[sgn][f2][1] = pack_acc(phi[0][sgn][f2], 1);
+            }
         {
             // routed linear tokens of chunk c-1 (offset <= the query's, not
             // selected): weight phi_k(k_j) . phi_q(q_t) at reference point 0
-            f32x16 wl[2][2];  // rows = keys, column = query
+            f32x16 wl[2];  // rows = keys, column = query
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                wl[kt][0] = zero16();
-                wl[kt][1] = zero16();
+                wl[kt] = zero16();
                 const bf16* pk = phik + (bg * D.N + (t0 - kC) + 32 * kt + col) * kD + 8 * hf;
 #pragma unroll
                 for (int sgn = 0; sgn < 2; ++sgn)
 #pragma unroll
                     for (int f2 = 0; f2 < 2; ++f2)
 #pragma unroll
-                        for (int s2 = 0; s2 < 2; ++s2) {
-                            const bf16x8 a = ld_bf8(pk + 64 * sgn + 32 * f2 + 16 * s2);
-                            wl[kt][0] = mfma32(a, phb[0][sgn][f2][s2], wl[kt][0]);
-                            wl[kt][1] = mfma32(a, phb[1][sgn][f2][s2], wl[kt][1]);
-                        }
+                        for (int s2 = 0; s2 < 2; ++s2)
+                            wl[kt] = mfma32(ld_bf8(pk + 64 * sgn + 32 * f2 + 16 * s2), phb[sgn][f2][s2], wl[kt]);
             }
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-                    for (int vv = 0; vv < 16; ++vv) {
-                        const int rk = 32 * kt + acc_row(vv, hf), oq = 32 * qt + col;
-                        const bool la = rk <= oq && !((selmask >> rk) & 1ull);
-                        const float p = la ? wl[kt][qt][vv] : 0.f;
-                        wl[kt][qt][vv] = p;
-                        ls[qt] += p;
-                    }
+                for (int vv = 0; vv < 16; ++vv) {
+                    const int rk = 32 * kt + acc_row(vv, hf);
+                    const bool la = rk <= oq && !((selmask >> rk) & 1ull);
+                    const float p = la ? wl[kt][vv] : 0.f;
+                    wl[kt][vv] = p;
+                    ls += p;
+                }
             const bf16* vt = smem + kC * kKS;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int kt = ks >> 1, s2 = ks & 1;
-                const bf16x8 pa0 = pack_acc(wl[kt][0], s2), pa1 = pack_acc(wl[kt][1], s2);
+                const bf16x8 pa = pack_acc(wl[ks >> 1], ks & 1);
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const bf16x8 av = ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf);
-                    o[0][dt] = mfma32(av, pa0, o[0][dt]);
-                    o[1][dt] = mfma32(av, pa1, o[1][dt]);
-                }
+                for (int dt = 0; dt < 4; ++dt)
+                    o[dt] = mfma32(ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf), pa, o[dt]);
             }
         }
         if (c >= 2) {
@@ -648,99 +664,69 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
                             bf16x8 hi, lo;
                             ld_split8(st + (size_t)(32 * dt + col) * kD + 64 * sgn + 32 * f2 + 16 * s2 + 8 * hf,
                                       hi, lo);
-#pragma unroll
-                            for (int qt = 0; qt < 2; ++qt) {
-                                o[qt][dt] = mfma32(hi, phb[qt][sgn][f2][s2], o[qt][dt]);
-                                o[qt][dt] = mfma32(lo, phb[qt][sgn][f2][s2], o[qt][dt]);
-                            }
+                            o[dt] = mfma32(hi, phb[sgn][f2][s2], o[dt]);
+                            o[dt] = mfma32(lo, phb[sgn][f2][s2], o[dt]);
                         }
         }
     }
 
-    // Softmax terms of one staged tile: key row rk counts for query oq when
-    // bit rk of (rk > oq ? hi_m : lo_m) is set.
+    // Softmax terms of one staged tile: key row rk counts for the lane's
+    // query when bit rk of (rk > oq ? hi_m : lo_m) is set.
     auto run_tile = [&](const bf16* ks, const bf16* vt, uint64_t hi_m, uint64_t lo_m) {
-        const bool use_mask = (hi_m & lo_m) != ~0ull;
-        f32x16 sc[2][2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            sc[kt][0] = zero16();
-            sc[kt][1] = zero16();
-        }
+        f32x16 sc[2];
+        sc[0] = zero16();
+        sc[1] = zero16();
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 a = ld_bf8(ks + (32 * kt + col) * kKS + 16 * s + 8 * hf);
-                sc[kt][0] = mfma32(a, qf[0][s], sc[kt][0]);
-                sc[kt][1] = mfma32(a, qf[1][s], sc[kt][1]);
-            }
+            for (int kt = 0; kt < 2; ++kt)
+                sc[kt] = mfma32(ld_bf8(ks + (32 * kt + col) * kKS + 16 * s + 8 * hf), qf[0][s], sc[kt]);
         }
-        if (use_mask) {
+        if ((hi_m & lo_m) != ~0ull) {
             // edge tiles only: masked key rows drop out of the softmax
             __asm__ volatile("");
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-                    for (int vv = 0; vv < 16; ++vv) {
-                        const int rk = 32 * kt + acc_row(vv, hf), oq = 32 * qt + col;
-                        const uint64_t m = rk > oq ? hi_m : lo_m;
-                        if (!((m >> rk) & 1ull)) sc[kt][qt][vv] = kNegInf;
-                    }
+                for (int vv = 0; vv < 16; ++vv) {
+                    const int rk = 32 * kt + acc_row(vv, hf);
+                    const uint64_t m = rk > oq ? hi_m : lo_m;
+                    if (!((m >> rk) & 1ull)) sc[kt][vv] = kNegInf;
+                }
         }
-        float tmax[2] = {kNegInf, kNegInf};
+        float tmax = kNegInf;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-                for (int vv = 0; vv < 16; ++vv) {
-                    tmax[qt] = fmaxf(tmax[qt], sc[kt][qt][vv]);
-                }
-        float tm2[2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) tm2[qt] = fmaxf(tmax[qt], xor32(tmax[qt])) * cl2;
-        if (__any(tm2[0] > m2[0] + kLazy || tm2[1] > m2[1] + kLazy)) {
+            for (int vv = 0; vv < 16; ++vv) tmax = fmaxf(tmax, sc[kt][vv]);
+        const float tm2 = fmaxf(tmax, xor32(tmax)) * cl2;
+        if (__any(tm2 > m2 + kLazy)) {
             // a rare path: keep the compiler from speculating it into every tile
             __asm__ volatile("");
-            float al[2];
+            const float mn = fmaxf(m2, tm2);
+            const float al = __builtin_amdgcn_exp2f(m2 - mn);
+            m2 = mn;
+            ls *= al;
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                const float mn = fmaxf(m2[qt], tm2[qt]);
-                al[qt] = __builtin_amdgcn_exp2f(m2[qt] - mn);
-                m2[qt] = mn;
-                ls[qt] *= al[qt];
-            }
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int vv = 0; vv < 16; ++vv) o[qt][dt][vv] *= al[qt];
+                for (int vv = 0; vv < 16; ++vv) o[dt][vv] *= al;
         }
-        const float nm0 = -m2[0], nm1 = -m2[1];
+        const float nm = -m2;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-                for (int vv = 0; vv < 16; ++vv) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][qt][vv], cl2, qt ? nm1 : nm0));
-                    sc[kt][qt][vv] = p;
-                    ls[qt] += p;
-                }
+            for (int vv = 0; vv < 16; ++vv) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][vv], cl2, nm));
+                sc[kt][vv] = p;
+                ls += p;
+            }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int kt = ks >> 1, s2 = ks & 1;
-            const bf16x8 pa0 = pack_acc(sc[kt][0], s2), pa1 = pack_acc(sc[kt][1], s2);
+            const bf16x8 pa = pack_acc(sc[ks >> 1], ks & 1);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const bf16x8 av = ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf);
-                o[0][dt] = mfma32(av, pa0, o[0][dt]);
-                o[1][dt] = mfma32(av, pa1, o[1][dt]);
-            }
+            for (int dt = 0; dt < 4; ++dt)
+                o[dt] = mfma32(ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf), pa, o[dt]);
         }
     };
 
@@ -752,9 +738,16 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
         const bf16* ks = smem + cur * kBuf;
         const bf16* vt = ks + kC * kKS;
         uint64_t hm, lm;
-        if (i == 0) { hm = ~0ull; lm = selmask; }
-        else if (i == 1) { hm = 0ull; lm = ~0ull; }
-        else { const int nv = min(kC, nrows - (i - 2) * kC); hm = lm = nv == kC ? ~0ull : (1ull << nv) - 1ull; }
+        if (i == 0) {  // chunk c-1: window keys (offset above the query's) and routed selected keys
+            hm = ~0ull;
+            lm = selmask;
+        } else if (i == 1) {  // chunk c: causal
+            hm = 0ull;
+            lm = ~0ull;
+        } else {
+            const int nv = min(kC, nrows - (i - 2) * kC);
+            hm = lm = nv == kC ? ~0ull : (1ull << nv) - 1ull;
+        }
         run_tile(ks, vt, hm, lm);
         if (i + 1 < ntile) {
             bf16* nb = smem + (cur ^ 1) * kBuf;
@@ -764,29 +757,25 @@ __global__ __launch_bounds__(NW * 64) void hybrid_main_kernel(
         __syncthreads();
     }
 
-    // epilogue: normalise, stage each wave's 64 x 128 tile in LDS, write rows
-    float il[2];
+    // epilogue: normalise, stage each wave's 32 x 128 tile in LDS, write rows
+    const float il = 1.f / (ls + xor32(ls));
+    bf16* ot = smem + wave * (32 * kKS);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) il[qt] = 1.f / (ls[qt] + xor32(ls[qt]));
-    bf16* ot = smem + wave * (kC * kKS);
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+        for (int v4 = 0; v4 < 4; ++v4) {
+            // dims 32 dt + acc_row(4 v4 .. 4 v4 + 3) are consecutive
+            bf16x4 t4;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                // dims 32 dt + acc_row(4 v4 .. 4 v4 + 3) are consecutive
-                bf16x4 t4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) t4[j] = (bf16)(o[qt][dt][4 * v4 + j] * il[qt]);
-                *reinterpret_cast<bf16x4*>(ot + (32 * qt + col) * kKS + 32 * dt + acc_row(4 * v4, hf)) = t4;
-            }
+            for (int j = 0; j < 4; ++j) t4[j] = (bf16)(o[dt][4 * v4 + j] * il);
+            *reinterpret_cast<bf16x4*>(ot + col * kKS + 32 * dt + acc_row(4 * v4, hf)) = t4;
+        }
     __syncthreads();
-    const int nq = min(kC, D.N - t0);
-    for (int x = lane; x < kC * 16; x += kWave) {
+    const int nq = min(32, D.N - t0 - 32 * qh);
+    for (int x = lane; x < 32 * 16; x += kWave) {
         const int row = x >> 4, piece = x & 15;
         if (row < nq)
-            st_bf8(out + (((size_t)b * D.N + t0 + row) * D.Hq + h) * kD + 8 * piece,
+            st_bf8(out + (((size_t)b * D.N + t0 + 32 * qh + row) * D.Hq + h) * kD + 8 * piece,
                    ld_bf8(ot + row * kKS + 8 * piece));
     }
 }
@@ -838,17 +827,17 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                               const float* wphi_q, const void* phik, const uint8_t* route,
                               const void* ksel, const void* vsel, const float* lin, void* out,
                               hipStream_t s) {
-    const int NW = D.G >= 4 ? 4 : D.G;
-    const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / NW);
-#define STILL_MAIN(W)                                                                            \
-    hipLaunchKernelGGL(hybrid_main_kernel<W>, dim3(nblk), dim3(64 * W), 0, s,                   \
+    const int HB = D.G >= 4 ? 4 : D.G;  // query heads per block, two waves each
+    const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
+#define STILL_MAIN(H)                                                                            \
+    hipLaunchKernelGGL(hybrid_main_kernel<H>, dim3(nblk), dim3(128 * H), 0, s,                  \
                        reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),      \
                        reinterpret_cast<const bf16*>(v), wphi_q,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
                        lin, reinterpret_cast<bf16*>(out), D)
-    if (NW == 4) STILL_MAIN(4);
-    else if (NW == 2) STILL_MAIN(2);
+    if (HB == 4) STILL_MAIN(4);
+    else if (HB == 2) STILL_MAIN(2);
     else STILL_MAIN(1);
 #undef STILL_MAIN
     return hipGetLastError();
