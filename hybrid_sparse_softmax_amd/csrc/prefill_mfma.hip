@@ -32,6 +32,8 @@ namespace still {
 namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kC = 64;          // chunk = window
@@ -75,7 +77,9 @@ __device__ __forceinline__ void load_k_tile(const bf16* __restrict__ src, size_t
 __device__ __forceinline__ void load_vt_tile(const bf16* __restrict__ src, size_t ld, int nvalid,
                                              bf16* __restrict__ dst, int tid, int nthr) {
     for (int x = tid; x < 16 * 16; x += nthr) {
-        const int kq = x >> 4, oct = x & 15;  // rows 4kq..4kq+3, columns 8oct..8oct+7
+        // rows 4kq..4kq+3, columns 8oct..8oct+7; consecutive threads fill one
+        // LDS row (no bank conflicts on the transposed stores)
+        const int kq = x & 15, oct = x >> 4;
         bf16x8 r[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -470,7 +474,9 @@ __device__ __forceinline__ void tile_fetch(TileRegs<NT>& R, const bf16* __restri
         constexpr int base = TR::kSplit ? 0 : TR::KR;
 #pragma unroll
         for (int j = 0; j < TR::VU; ++j) {
-            const int u = vt0 + vstride * j, kq = u >> 4, oct = u & 15;
+            // consecutive lanes take consecutive row quads of one column block,
+            // so their transposed LDS stores fill one LDS row without bank conflicts
+            const int u = vt0 + vstride * j, kq = u & 15, oct = u >> 4;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int row = min(4 * kq + rr, nv - 1);
@@ -500,16 +506,23 @@ __device__ __forceinline__ void tile_store(const TileRegs<NT>& R, bf16* __restri
         constexpr int base = TR::kSplit ? 0 : TR::KR;
 #pragma unroll
         for (int j = 0; j < TR::VU; ++j) {
-            const int u = vt0 + vstride * j, kq = u >> 4, oct = u & 15;
+            const int u = vt0 + vstride * j, kq = u & 15, oct = u >> 4;
             const int pos = kperm(4 * kq);
+            // 4 rows x 8 columns -> 8 columns x 4 rows: byte permutes pair the
+            // low (even column) or high (odd column) halves of two rows' dwords
+            const u32x4 a0 = __builtin_bit_cast(u32x4, R.r[base + 4 * j + 0]);
+            const u32x4 a1 = __builtin_bit_cast(u32x4, R.r[base + 4 * j + 1]);
+            const u32x4 a2 = __builtin_bit_cast(u32x4, R.r[base + 4 * j + 2]);
+            const u32x4 a3 = __builtin_bit_cast(u32x4, R.r[base + 4 * j + 3]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 t4;
-                t4[0] = R.r[base + 4 * j + 0][e];
-                t4[1] = R.r[base + 4 * j + 1][e];
-                t4[2] = R.r[base + 4 * j + 2][e];
-                t4[3] = R.r[base + 4 * j + 3][e];
-                *reinterpret_cast<bf16x4*>(vt + (8 * oct + e) * kVS + pos) = t4;
+            for (int d = 0; d < 4; ++d) {
+                u32x2 ev, od;
+                ev[0] = __builtin_amdgcn_perm(a1[d], a0[d], 0x05040100u);
+                ev[1] = __builtin_amdgcn_perm(a3[d], a2[d], 0x05040100u);
+                od[0] = __builtin_amdgcn_perm(a1[d], a0[d], 0x07060302u);
+                od[1] = __builtin_amdgcn_perm(a3[d], a2[d], 0x07060302u);
+                *reinterpret_cast<u32x2*>(vt + (8 * oct + 2 * d) * kVS + pos) = ev;
+                *reinterpret_cast<u32x2*>(vt + (8 * oct + 2 * d + 1) * kVS + pos) = od;
             }
         }
     }
