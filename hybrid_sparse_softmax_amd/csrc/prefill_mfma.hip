@@ -269,16 +269,14 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 for (int vv = 0; vv < 16; ++vv) {
                     const int kk = 32 * (qt + j) + acc_row(vv, hf);
                     const float e = sc[j][vv];
-                    float tj;
-                    if (kk == qo + kC) {
-                        const float at = e * isa;
-                        tj = at * log1pf(at / D.eps);
-                    } else {
-                        tj = -(e * isa) * log1pf(__fdividef(r * e, e + esa));
-                    }
-                    term += e > 0.f ? tj : 0.f;
+                    const float tj = -(e * isa) * log1p_fast(__fdividef(r * e, e + esa));
+                    term += (e > 0.f && kk != qo + kC) ? tj : 0.f;
                 }
             term += xor32(term);
+            {
+                const float at = et * isa;  // the query's own key, once
+                term += at * log1pf(at / D.eps);
+            }
             if (hf == 0) hsc[hh][qo] = term;
         }
     }
