@@ -12,6 +12,7 @@ struct Dims {
     int W, C, lam;                // lam = min(topk, C)
     int T;                        // ceil(N / C)
     int n_full;                   // N / C complete chunks
+    int ng;                       // chunks per run of the MFMA path's linear-state kernel
     float eps, tau;
     bool bf16;
 };
@@ -62,12 +63,13 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
 // linear sums [B, Hkv, n_full, d + 1, d'] (S^T rows then z, kperm order)
 hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const float* wphi_k,
                            const uint8_t* route, void* phik, float* lin, hipStream_t s);
-hipError_t launch_la_scan_t(const Dims& D, float* lin, int cap_chunk, float* cap_S, float* cap_z,
-                            hipStream_t s);
+// gpre [B, Hkv, ceil(n_full / ng), d + 1, d']: exclusive prefix over runs
+hipError_t launch_la_group_scan(const Dims& D, const float* lin, float* gpre, int cap_chunk,
+                                float* cap_S, float* cap_z, hipStream_t s);
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const float* wphi_q, const void* phik, const uint8_t* route,
-                              const void* ksel, const void* vsel, const float* lin, void* out,
-                              hipStream_t s);
+                              const void* ksel, const void* vsel, const float* lin,
+                              const float* gpre, void* out, hipStream_t s);
 
 // ---- decode step ------------------------------------------------------------
 struct DecodeWork {

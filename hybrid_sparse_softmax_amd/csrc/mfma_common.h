@@ -64,6 +64,21 @@ __device__ __forceinline__ void ld_split8(const float* p, bf16x8& hi, bf16x8& lo
     }
 }
 
+// the same for the sum of two fp32 arrays (a + b, then split)
+__device__ __forceinline__ void ld_split8_sum(const float* a, const float* b, bf16x8& hi, bf16x8& lo) {
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(a), a1 = *reinterpret_cast<const f32x4*>(a + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float x0 = a0[j] + b0[j], x1 = a1[j] + b1[j];
+        const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+        hi[j] = h0;
+        hi[4 + j] = h1;
+        lo[j] = (__bf16)(x0 - (float)h0);
+        lo[4 + j] = (__bf16)(x1 - (float)h1);
+    }
+}
+
 // elements 8*s2 .. 8*s2+7 of an accumulator as a bf16 operand
 __device__ __forceinline__ bf16x8 pack_acc(const f32x16& x, int s2) {
     bf16x8 r;

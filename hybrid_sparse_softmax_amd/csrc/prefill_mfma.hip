@@ -8,11 +8,11 @@
 //                       Appendix A.3), group mean, per-chunk top-k, route
 //                       flags, gather of the selected K/V rows into a
 //                       compact per-KV-head list
-//   la_state_kernel     NP-Map of the chunk's keys (Sec. 3.2, MFMA
-//                       projection), phi_k rows for the read-out, and the
-//                       chunk's linear-attention sums over its unselected
-//                       tokens (MFMA; Appendix A.2 state)
-//   la_scan_t_kernel    inclusive prefix of those sums over chunks
+//   la_state_kernel     NP-Map of the keys (Sec. 3.2, MFMA projection),
+//                       phi_k rows for the read-out, and running sums of
+//                       phi_k v^T over unselected tokens (MFMA; Appendix A.2
+//                       state) along runs of consecutive chunks
+//   la_group_scan_kernel  prefix over the runs' totals
 //   hybrid_main_kernel  per query chunk: linear prefix read-out, chunk c-1
 //                       (window, routed selected and routed linear tokens),
 //                       chunk c (causal window), then every selected token of
@@ -41,6 +41,7 @@ constexpr int kD = 128;         // head_dim = NP-Map feature dim
 constexpr int kKS = kD + 8;     // LDS row stride (elements) of a K tile
 constexpr int kVS = kC + 8;     // LDS row stride (elements) of a transposed V tile
 constexpr int kFS = kC + 4;     // LDS row stride (floats) of transposed phi_k
+constexpr int kSS = kD + 4;     // LDS row stride (floats) of a staged linear state
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;   // rescale only when the running max grows by more (log2 units)
 
@@ -326,111 +327,116 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// NP-Map of keys and per-chunk linear-attention sums (complete chunks only)
+// NP-Map of keys and linear-attention prefixes (complete chunks only)
 // ---------------------------------------------------------------------------
-// lin block of chunk c: rows 0..127 = S^T[dim][kperm(f)] = sum over the
-// chunk's LA tokens of v[dim] phi_k[f]; row 128 = z[kperm(f)] = sum phi_k[f].
+// One block walks a run of D.ng consecutive chunks of one (b, KV head),
+// keeping the running sums in its MFMA accumulators, and writes for each
+// chunk c the prefix within its run:
+//   lin[c] rows 0..127 = S^T[dim][kperm(f)] = sum over the LA tokens of the
+//   run's chunks <= c of v[dim] phi_k[f];  row 128 = z[kperm(f)] = sum phi_k[f].
+// la_group_scan_kernel then forms each run's exclusive prefix over the
+// earlier runs, so the full prefix of chunk c is lin[c] + gpre[c / ng].
 __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v,
                                                        const float* __restrict__ wk,
                                                        const uint8_t* __restrict__ route,
                                                        bf16* __restrict__ phik,
                                                        float* __restrict__ lin, Dims D) {
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int grp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
-    const int t0 = c * kC;
     const size_t bg = (size_t)b * D.Hkv + g;
+    const int c_lo = grp * D.ng, c_hi = min(D.n_full, c_lo + D.ng);
     __shared__ __align__(16) bf16 vt[kD * kVS];
     __shared__ __align__(16) float ft[kD * kFS];
 
-    if (wave < 2) {
-        const int tt = wave;
-        const int tok = t0 + 32 * tt + col;
-        bf16x8 xb[1][8];
-        const bf16* kr = k + (((size_t)b * D.N + tok) * D.Hkv + g) * kD + 8 * hf;
+    f32x16 acc[4];  // S^T rows 32 wave + .., feature tiles f4; running over the run
 #pragma unroll
-        for (int s = 0; s < 8; ++s) xb[0][s] = ld_bf8(kr + 16 * s);
-        f32x16 phi[1][2][2];
-        np_map_mfma<1>(xb, wk + (size_t)g * (kD / 2) * kD, phi);
-        // phi_k row of the token, features in kperm order, for the read-out
-        bf16* pr = phik + (bg * D.N + tok) * kD;
+    for (int f4 = 0; f4 < 4; ++f4) acc[f4] = zero16();
+    float zacc = 0.f;  // threads < 128: z of feature tid
+    for (int c = c_lo; c < c_hi; ++c) {
+        const int t0 = c * kC;
+        if (wave < 2) {
+            const int tt = wave;
+            const int tok = t0 + 32 * tt + col;
+            bf16x8 xb[1][8];
+            const bf16* kr = k + (((size_t)b * D.N + tok) * D.Hkv + g) * kD + 8 * hf;
 #pragma unroll
-        for (int sgn = 0; sgn < 2; ++sgn)
+            for (int s = 0; s < 8; ++s) xb[0][s] = ld_bf8(kr + 16 * s);
+            f32x16 phi[1][2][2];
+            np_map_mfma<1>(xb, wk + (size_t)g * (kD / 2) * kD, phi);
+            // phi_k row of the token, features in kperm order, for the read-out
+            bf16* pr = phik + (bg * D.N + tok) * kD;
 #pragma unroll
-            for (int f2 = 0; f2 < 2; ++f2)
+            for (int sgn = 0; sgn < 2; ++sgn)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    st_bf8(pr + 64 * sgn + 32 * f2 + 16 * s2 + 8 * hf, pack_acc(phi[0][sgn][f2], s2));
-        const bool la = route[bg * D.N + tok] == kRouteLA;
-        const int tp = kperm(32 * tt + col);
+                for (int f2 = 0; f2 < 2; ++f2)
 #pragma unroll
-        for (int sgn = 0; sgn < 2; ++sgn)
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        st_bf8(pr + 64 * sgn + 32 * f2 + 16 * s2 + 8 * hf, pack_acc(phi[0][sgn][f2], s2));
+            const bool la = route[bg * D.N + tok] == kRouteLA;
+            const int tp = kperm(32 * tt + col);
 #pragma unroll
-            for (int f2 = 0; f2 < 2; ++f2)
+            for (int sgn = 0; sgn < 2; ++sgn)
 #pragma unroll
-                for (int vv = 0; vv < 16; ++vv)
-                    ft[(64 * sgn + 32 * f2 + acc_row(vv, hf)) * kFS + tp] = la ? phi[0][sgn][f2][vv] : 0.f;
-    } else {
-        load_vt_tile(v + (((size_t)b * D.N + t0) * D.Hkv + g) * kD, (size_t)D.Hkv * kD, kC, vt,
-                     tid - 128, 128);
-    }
-    __syncthreads();
-    float* out = lin + (bg * D.n_full + c) * (size_t)((kD + 1) * kD);
-    {
+                for (int f2 = 0; f2 < 2; ++f2)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv)
+                        ft[(64 * sgn + 32 * f2 + acc_row(vv, hf)) * kFS + tp] = la ? phi[0][sgn][f2][vv] : 0.f;
+        } else {
+            load_vt_tile(v + (((size_t)b * D.N + t0) * D.Hkv + g) * kD, (size_t)D.Hkv * kD, kC, vt,
+                         tid - 128, 128);
+        }
+        __syncthreads();
+        float* out = lin + (bg * D.n_full + c) * (size_t)((kD + 1) * kD);
         const int dt = wave;  // dims 32 dt .. 32 dt + 31
 #pragma unroll
         for (int f4 = 0; f4 < 4; ++f4) {
-            f32x16 acc = zero16();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 a = ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf);
                 bf16x8 hi, lo;
                 ld_split8(ft + (32 * f4 + col) * kFS + 16 * ks + 8 * hf, hi, lo);
-                acc = mfma32(a, hi, acc);
-                acc = mfma32(a, lo, acc);
+                acc[f4] = mfma32(a, hi, acc[f4]);
+                acc[f4] = mfma32(a, lo, acc[f4]);
             }
             const int sp = kperm(32 * f4 + col);
 #pragma unroll
-            for (int vv = 0; vv < 16; ++vv) out[(size_t)(32 * dt + acc_row(vv, hf)) * kD + sp] = acc[vv];
+            for (int vv = 0; vv < 16; ++vv) out[(size_t)(32 * dt + acc_row(vv, hf)) * kD + sp] = acc[f4][vv];
         }
-    }
-    if (tid < kD) {
-        float z = 0.f;
-        for (int t = 0; t < kC; ++t) z += ft[tid * kFS + t];
-        out[(size_t)kD * kD + kperm(tid)] = z;
+        if (tid < kD) {
+            float z = 0.f;
+            for (int t = 0; t < kC; ++t) z += ft[tid * kFS + t];
+            zacc += z;
+            out[(size_t)kD * kD + kperm(tid)] = zacc;
+        }
+        __syncthreads();  // the next chunk overwrites vt and ft
     }
 }
 
-// Inclusive prefix over complete chunks, in place; chunk cap_chunk is also
-// copied into the decode cache's lin_S [f][dim] / lin_z [f].  Each thread
-// owns one entry and keeps 16 chunks' loads in flight.
-__global__ __launch_bounds__(256) void la_scan_t_kernel(float* __restrict__ lin, int cap_chunk,
-                                                        float* __restrict__ cap_S,
-                                                        float* __restrict__ cap_z, Dims D) {
+// gpre[run] = sum of the totals of the runs before it (exclusive), per entry;
+// the full prefix of chunk cap_chunk also goes into the decode cache's
+// lin_S [f][dim] / lin_z [f].
+__global__ __launch_bounds__(256) void la_group_scan_kernel(const float* __restrict__ lin,
+                                                            float* __restrict__ gpre, int ngroups,
+                                                            int cap_chunk, float* __restrict__ cap_S,
+                                                            float* __restrict__ cap_z, Dims D) {
     constexpr int E1 = (kD + 1) * kD;
-    constexpr int kDepth = 16;
     const int e = blockIdx.x * 256 + threadIdx.x, g = blockIdx.y, b = blockIdx.z;
     if (e >= E1) return;
     const size_t bg = (size_t)b * D.Hkv + g;
-    float* base = lin + bg * D.n_full * (size_t)E1 + e;
+    const float* base = lin + bg * D.n_full * (size_t)E1 + e;
+    float* gp = gpre + bg * (size_t)ngroups * E1 + e;
     float run = 0.f;
-    for (int c0 = 0; c0 < D.n_full; c0 += kDepth) {
-        const int n = min(kDepth, D.n_full - c0);
-        float x[kDepth];
-#pragma unroll
-        for (int i = 0; i < kDepth; ++i) x[i] = i < n ? base[(size_t)(c0 + i) * E1] : 0.f;
-#pragma unroll
-        for (int i = 0; i < kDepth; ++i) {
-            if (i < n) {
-                run += x[i];
-                base[(size_t)(c0 + i) * E1] = run;
-                if (c0 + i == cap_chunk && cap_S) {
-                    const int row = e / kD, f = kperm(e % kD);
-                    if (row < kD) cap_S[(bg * kD + f) * kD + row] = run;
-                    else cap_z[bg * kD + f] = run;
-                }
-            }
+    for (int grp = 0; grp < ngroups; ++grp) {
+        gp[(size_t)grp * E1] = run;
+        const int first = grp * D.ng, last = min(D.n_full, first + D.ng) - 1;
+        if (cap_S && cap_chunk >= first && cap_chunk <= last) {
+            const float val = run + base[(size_t)cap_chunk * E1];
+            const int row = e / kD, f = kperm(e % kD);
+            if (row < kD) cap_S[(bg * kD + f) * kD + row] = val;
+            else cap_z[bg * kD + f] = val;
         }
+        run += base[(size_t)last * E1];
     }
 }
 
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ wq, const bf16* __restrict__ phik, const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const float* __restrict__ lin,
-    bf16* __restrict__ out, Dims D) {
+    const float* __restrict__ gpre, bf16* __restrict__ out, Dims D) {
     constexpr int NT = HB * 128;
     constexpr int kBuf = kC * kKS + kD * kVS;  // elements of one K + V^T buffer
     const int HG = D.G / HB;
@@ -558,6 +564,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const float cl2 = D.tau * kLog2e;
 
     __shared__ __align__(16) bf16 smem[2 * kBuf];
+    __shared__ __align__(16) float sts[(kD + 1) * kSS];  // linear prefix S^T rows, then z
 
     // tiles: 0 = chunk c-1 (c >= 1), 1 = chunk c, 2.. = compact selected rows
     const int nrows = c >= 2 ? (c - 1) * D.lam : 0;
@@ -603,9 +610,21 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 
     if (c >= 1) {
         selmask = __ballot(route[bg * D.N + (t0 - kC) + lane] == kRouteSA);
+        if (c >= 2) {
+            // prefix of chunks <= c-2 (within-run part + earlier runs), staged
+            // in LDS once for all waves; rows padded to kSS floats
+            const int cp = c - 2;
+            const f32x4* st4 = reinterpret_cast<const f32x4*>(lin + (bg * D.n_full + cp) * (size_t)((kD + 1) * kD));
+            const f32x4* gs4 = reinterpret_cast<const f32x4*>(
+                gpre + (bg * ((D.n_full + D.ng - 1) / D.ng) + cp / D.ng) * (size_t)((kD + 1) * kD));
+            for (int x = tid; x < (kD + 1) * kD / 4; x += NT) {
+                const int row = (4 * x) / kD, c4 = (4 * x) % kD;
+                *reinterpret_cast<f32x4*>(&sts[row * kSS + c4]) = st4[x] + gs4[x];
+            }
+        }
+        __syncthreads();
         f32x16 phi[1][2][2];
         np_map_mfma<1>(qf, wq + (size_t)g * (kD / 2) * kD, phi);
-        const float* st = lin + (bg * D.n_full + (c >= 2 ? c - 2 : 0)) * (size_t)((kD + 1) * kD);
         if (c >= 2) {
             // normaliser of the linear prefix (chunks <= c-2): phi_q . z
             float acc = 0.f;
@@ -615,7 +634,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 for (int f2 = 0; f2 < 2; ++f2)
 #pragma unroll
                     for (int vv = 0; vv < 16; ++vv)
-                        acc = fmaf(st[kD * kD + kperm(64 * sgn + 32 * f2 + acc_row(vv, hf))],
+                        acc = fmaf(sts[kD * kSS + kperm(64 * sgn + 32 * f2 + acc_row(vv, hf))],
                                    phi[0][sgn][f2][vv], acc);
             ls = acc;
         }
@@ -673,8 +692,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
                         for (int s2 = 0; s2 < 2; ++s2) {
                             bf16x8 hi, lo;
-                            ld_split8(st + (size_t)(32 * dt + col) * kD + 64 * sgn + 32 * f2 + 16 * s2 + 8 * hf,
-                                      hi, lo);
+                            ld_split8(&sts[(32 * dt + col) * kSS + 64 * sgn + 32 * f2 + 16 * s2 + 8 * hf], hi, lo);
                             o[dt] = mfma32(hi, phb[sgn][f2][s2], o[dt]);
                             o[dt] = mfma32(lo, phb[sgn][f2][s2], o[dt]);
                         }
@@ -819,25 +837,27 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
 hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const float* wphi_k,
                            const uint8_t* route, void* phik, float* lin, hipStream_t s) {
     if (D.n_full == 0) return hipSuccess;
-    dim3 grid(D.n_full, D.Hkv, D.B);
+    dim3 grid((D.n_full + D.ng - 1) / D.ng, D.Hkv, D.B);
     hipLaunchKernelGGL(la_state_kernel, grid, dim3(256), 0, s, reinterpret_cast<const bf16*>(k),
                        reinterpret_cast<const bf16*>(v), wphi_k, route, reinterpret_cast<bf16*>(phik),
                        lin, D);
     return hipGetLastError();
 }
 
-hipError_t launch_la_scan_t(const Dims& D, float* lin, int cap_chunk, float* cap_S, float* cap_z,
-                            hipStream_t s) {
+hipError_t launch_la_group_scan(const Dims& D, const float* lin, float* gpre, int cap_chunk,
+                                float* cap_S, float* cap_z, hipStream_t s) {
     constexpr int E1 = (kD + 1) * kD;
+    const int ngroups = D.n_full == 0 ? 0 : (D.n_full + D.ng - 1) / D.ng;
     dim3 grid((E1 + 255) / 256, D.Hkv, D.B);
-    hipLaunchKernelGGL(la_scan_t_kernel, grid, dim3(256), 0, s, lin, cap_chunk, cap_S, cap_z, D);
+    hipLaunchKernelGGL(la_group_scan_kernel, grid, dim3(256), 0, s, lin, gpre, ngroups, cap_chunk,
+                       cap_S, cap_z, D);
     return hipGetLastError();
 }
 
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const float* wphi_q, const void* phik, const uint8_t* route,
-                              const void* ksel, const void* vsel, const float* lin, void* out,
-                              hipStream_t s) {
+                              const void* ksel, const void* vsel, const float* lin,
+                              const float* gpre, void* out, hipStream_t s) {
     const int HB = D.G >= 4 ? 4 : D.G;  // query heads per block, two waves each
     const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
 #define STILL_MAIN(H)                                                                            \
@@ -846,7 +866,7 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                        reinterpret_cast<const bf16*>(v), wphi_q,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       lin, reinterpret_cast<bf16*>(out), D)
+                       lin, gpre, reinterpret_cast<bf16*>(out), D)
     if (HB == 4) STILL_MAIN(4);
     else if (HB == 2) STILL_MAIN(2);
     else STILL_MAIN(1);

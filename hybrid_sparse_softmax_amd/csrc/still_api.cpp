@@ -52,6 +52,13 @@ static Dims make_dims(const still_shape* sh, int seqlen) {
     D.lam = sh->topk < sh->chunk ? sh->topk : sh->chunk;
     D.T = (seqlen + D.C - 1) / D.C;
     D.n_full = seqlen / D.C;
+    {
+        // runs of consecutive chunks for the MFMA path's linear-state kernel:
+        // about one block per compute unit, at most 16 chunks per run
+        const int64_t chunks = (int64_t)D.B * D.Hkv * D.n_full;
+        const int64_t ng = chunks / 256;
+        D.ng = ng < 1 ? 1 : (ng > 16 ? 16 : (int)ng);
+    }
     D.eps = sh->eps;
     D.tau = sh->softmax_scale > 0.f ? sh->softmax_scale : 1.0f / std::sqrt((float)D.d);
     D.bf16 = sh->dtype == STILL_BF16;
@@ -96,7 +103,7 @@ static FwdBuffers carve_fwd(const Dims& D, Carver& cv) {
 }
 
 struct MfmaBuffers {
-    float *scores, *lin;
+    float *scores, *lin, *gpre;
     int32_t* sel;
     uint8_t* route;
     void *ksel, *vsel, *phik;
@@ -113,6 +120,8 @@ static MfmaBuffers carve_mfma(const Dims& D, Carver& cv) {
     f.vsel = cv.take<uint16_t>(nsel * D.d);
     f.phik = cv.take<uint16_t>(BG * D.N * D.fd);
     f.lin = cv.take<float>(BG * D.n_full * (size_t)(D.d + 1) * D.fd);
+    const size_t ngroups = D.n_full == 0 ? 0 : (size_t)(D.n_full + D.ng - 1) / D.ng;
+    f.gpre = cv.take<float>(BG * ngroups * (size_t)(D.d + 1) * D.fd);
     return f;
 }
 
@@ -229,10 +238,11 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
                      launch_win_select(D, q, k, v, scores, sel, f.route, f.ksel, f.vsel, s));
         STILL_LAUNCH(tl, s, "la_state", launch_la_state(D, k, v, wk, f.route, f.phik, f.lin, s));
         STILL_LAUNCH(tl, s, "la_scan",
-                     launch_la_scan_t(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
-                                      cache ? cache->lin_z : nullptr, s));
+                     launch_la_group_scan(D, f.lin, f.gpre, cap_chunk, cache ? cache->lin_S : nullptr,
+                                          cache ? cache->lin_z : nullptr, s));
         STILL_LAUNCH(tl, s, "hybrid_main",
-                     launch_hybrid_main(D, q, k, v, wq, f.phik, f.route, f.ksel, f.vsel, f.lin, out, s));
+                     launch_hybrid_main(D, q, k, v, wq, f.phik, f.route, f.ksel, f.vsel, f.lin, f.gpre,
+                                        out, s));
         if (cache)
             STILL_LAUNCH(tl, s, "handoff",
                          launch_handoff(D, k, v, wk, scores, sel, f.route, cap_chunk, view_of(cache), s));
