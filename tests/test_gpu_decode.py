@@ -22,6 +22,9 @@ DEC_CASES = {
     "bf16_swa_la": (make_case("d", 1, 100 + 40, 4, 4, 128, 32, 64, 0), 100, 34),
     "bf16_from_empty": (make_case("e", 1, 140, 4, 1, 128, 64, 64, 16), 0, 35),
     "bf16_G8_boundary": (make_case("f", 1, 128 + 70, 8, 1, 128, 64, 64, 8), 128, 36),
+    # window wider than the chunk, two query heads per KV head (bf16 d=128 decode path)
+    "bf16_W48_C16_G2": (make_case("g", 2, 90 + 60, 4, 2, 128, 48, 16, 4, outlier_frac=0.03, heavy_scale=6.0), 90, 37),
+    "bf16_W64_C32_G1": (make_case("h", 1, 100 + 50, 2, 2, 128, 64, 32, 8), 100, 38),
 }
 
 

@@ -31,6 +31,8 @@ CASES = {
     "bf16_G8": (make_case("h", 1, 320, 8, 1, 128, 64, 64, 8), 20),
     "f32_lam_gt_C": (make_case("i", 1, 256, 4, 1, 64, 32, 32, 40, dtype="f32"), 21),
     "bf16_swa_la_W_lt_C": (make_case("j", 1, 300, 4, 1, 128, 40, 64, 0), 22),
+    # matrix-core path with two query heads per KV head, three sequences, a ragged tail
+    "bf16_G2_B3_ragged": (make_case("k", 3, 777, 4, 2, 128, 64, 64, 20, outlier_frac=0.02, heavy_scale=6.0), 23),
 }
 
 
