@@ -547,7 +547,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const float* __restrict__ lin,
     const float* __restrict__ gpre, bf16* __restrict__ out, Dims D) {
     constexpr int NT = HB * 128;
-    constexpr int kBuf = kC * kKS + kD * kVS;  // elements of one K + V^T buffer
+    constexpr int kKBuf = kC * kKS, kVBuf = kD * kVS;
     const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
     const int c = D.T - 1 - (int)(blockIdx.x / per_c);
@@ -556,14 +556,21 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     r /= HG;
     const int g = r % D.Hkv, b = r / D.Hkv;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
-    const int qh = wave & 1;                       // which 32 queries of the chunk
-    const int h = g * D.G + hg * HB + (wave >> 1);
+    // waves 0..HB-1 take the first 32 queries of their head, waves HB.. the
+    // last 32; with HB = 4 the two halves of a head share a SIMD
+    const int qh = wave / HB;
+    const int h = g * D.G + hg * HB + wave % HB;
     const int t0 = c * kC;
     const int oq = 32 * qh + col;                  // this lane's query offset in the chunk
     const size_t bg = (size_t)b * D.Hkv + g;
     const float cl2 = D.tau * kLog2e;
 
-    __shared__ __align__(16) bf16 smem[2 * kBuf];
+    // K of tile i in kbuf(i) (two buffers), V^T of tile i in vbuf(i) (three:
+    // the second half of the queries finishes tile i-1 while the first half
+    // works on tile i)
+    __shared__ __align__(16) bf16 smem[2 * kKBuf + 3 * kVBuf];
+    auto kbuf = [&](int i) { return smem + (i & 1) * kKBuf; };
+    auto vbuf = [&](int i) { return smem + 2 * kKBuf + (i % 3) * kVBuf; };
     __shared__ __align__(16) float sts[(kD + 1) * kSS];  // linear prefix S^T rows, then z
 
     // tiles: 0 = chunk c-1 (c >= 1), 1 = chunk c, 2.. = compact selected rows
@@ -595,7 +602,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[0][s] = ld_bf8(row + 16 * s);
     }
-    tile_store<NT>(R, smem, smem + kC * kKS, tid);
+    tile_store<NT>(R, kbuf(first), vbuf(first), tid);
     if (first + 1 < ntile) fetch(first + 1, R);
     __syncthreads();
 
@@ -672,7 +679,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     wl[kt][vv] = p;
                     ls += p;
                 }
-            const bf16* vt = smem + kC * kKS;
+            const bf16* vt = vbuf(first);  // tile 0 = chunk c-1
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 pa = pack_acc(wl[ks >> 1], ks & 1);
@@ -699,10 +706,9 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         }
     }
 
-    // Softmax terms of one staged tile: key row rk counts for the lane's
-    // query when bit rk of (rk > oq ? hi_m : lo_m) is set.
-    auto run_tile = [&](const bf16* ks, const bf16* vt, uint64_t hi_m, uint64_t lo_m) {
-        f32x16 sc[2];
+    // logits of tile i (K^T Q on the matrix cores)
+    auto qk = [&](int i, f32x16 (&sc)[2]) {
+        const bf16* ks = kbuf(i);
         sc[0] = zero16();
         sc[1] = zero16();
 #pragma unroll
@@ -710,6 +716,21 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
                 sc[kt] = mfma32(ld_bf8(ks + (32 * kt + col) * kKS + 16 * s + 8 * hf), qf[0][s], sc[kt]);
+        }
+    };
+    // softmax terms and value product of tile i: key row rk counts for the
+    // lane's query when bit rk of (rk > oq ? hi_m : lo_m) is set
+    auto finish = [&](int i, f32x16 (&sc)[2]) {
+        uint64_t hi_m, lo_m;
+        if (i == 0) {  // chunk c-1: window keys (offset above the query's) and routed selected keys
+            hi_m = ~0ull;
+            lo_m = selmask;
+        } else if (i == 1) {  // chunk c: causal
+            hi_m = 0ull;
+            lo_m = ~0ull;
+        } else {
+            const int nv = min(kC, nrows - (i - 2) * kC);
+            hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
         }
         if ((hi_m & lo_m) != ~0ull) {
             // edge tiles only: masked key rows drop out of the softmax
@@ -750,6 +771,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 sc[kt][vv] = p;
                 ls += p;
             }
+        const bf16* vt = vbuf(i);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 pa = pack_acc(sc[ks >> 1], ks & 1);
@@ -762,25 +784,23 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // settle every outstanding load (Q, the first prefetch) here, once: the
     // loop then only ever waits for its own prefetch, at the LDS store
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    for (int i = first; i < ntile; ++i) {
-        const int cur = (i - first) & 1;
-        const bf16* ks = smem + cur * kBuf;
-        const bf16* vt = ks + kC * kKS;
-        uint64_t hm, lm;
-        if (i == 0) {  // chunk c-1: window keys (offset above the query's) and routed selected keys
-            hm = ~0ull;
-            lm = selmask;
-        } else if (i == 1) {  // chunk c: causal
-            hm = 0ull;
-            lm = ~0ull;
-        } else {
-            const int nv = min(kC, nrows - (i - 2) * kC);
-            hm = lm = nv == kC ? ~0ull : (1ull << nv) - 1ull;
+    // The first query half runs [logits, softmax, values] of tile i; the
+    // second runs [softmax, values] of tile i-1 and then the logits of tile i,
+    // so on each SIMD one wave's exp arithmetic meets the other's products.
+    f32x16 sc[2];
+    for (int i = first; i <= ntile; ++i) {
+        // one copy of each step: phase 0 = (first half: logits) + softmax and
+        // values of tile i - qh; phase 1 = (second half: logits)
+#pragma unroll 1
+        for (int ph = 0; ph < 2; ++ph) {
+            if (ph == qh && i < ntile) qk(i, sc);
+            if (ph == 0) {
+                const int j = i - qh;
+                if (j >= first && j < ntile) finish(j, sc);
+            }
         }
-        run_tile(ks, vt, hm, lm);
         if (i + 1 < ntile) {
-            bf16* nb = smem + (cur ^ 1) * kBuf;
-            tile_store<NT>(R, nb, nb + kC * kKS, tid);
+            tile_store<NT>(R, kbuf(i + 1), vbuf(i + 1), tid);
             if (i + 2 < ntile) fetch(i + 2, R);
         }
         __syncthreads();
