@@ -443,92 +443,147 @@ __global__ __launch_bounds__(256) void la_group_scan_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 // hybrid output
 // ---------------------------------------------------------------------------
-// What the NT threads of a block carry for one 64-row tile between its global
-// loads and its LDS stores: 1024 16-byte pieces of K rows and 256 blocks of
-// 4 V rows x 8 columns (transposed on the way into LDS).  With 512 threads
-// the first 256 take K and the rest V.  Rows at or beyond the tile's valid
-// count nv (>= 1) repeat row nv-1: every address stays in bounds without a
-// branch, and those keys are masked out of every sum.
-template <int NT>
-struct TileRegs {
-    static constexpr bool kSplit = NT == 512;
-    static constexpr int KR = kSplit ? 4 : 1024 / NT;  // K pieces per thread
-    static constexpr int VU = kSplit ? 1 : 256 / NT;   // V blocks per thread
-    static constexpr int N = kSplit ? 4 : KR + 4 * VU;
-    bf16x8 r[N];
-};
+// Tile staging for the output kernel: global memory straight into LDS
+// (global_load_lds, 16 bytes per lane; lane l of one instruction lands at
+// byte 16 l of that instruction's 1 KB).  Rows at or beyond a tile's valid
+// count nv (>= 1) repeat row nv-1, so every address stays in bounds; those
+// keys are masked out of every sum.
+//   K tile: 64 rows of kKS elements (17 slots of 16 bytes, the last one
+//     padding); 17 instructions cover its 1088 slots, padding slots load a
+//     slot of the same row.  The logits read a K row per lane at a fixed slot:
+//     the 17-slot stride spreads 16 rows over all banks.
+//   V tile: 64 unpadded rows of 128 elements; slot x of row r is stored at
+//     x ^ vswz(r); 16 instructions.  The value product reads it transposed.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kKTile = kC * kKS;  // elements of a staged K tile
+constexpr int kVTile = kC * kD;   // elements of a staged V tile
+constexpr int kKPieces = kKTile / 512;  // 17 staging instructions
+constexpr int kVPieces = kVTile / 512;  // 16
 
-template <int NT>
-__device__ __forceinline__ void tile_fetch(TileRegs<NT>& R, const bf16* __restrict__ ksrc,
-                                           const bf16* __restrict__ vsrc, size_t ld, int nv,
-                                           int tid) {
-    using TR = TileRegs<NT>;
-    const bool do_k = !TR::kSplit || tid < 256;
-    const bool do_v = !TR::kSplit || tid >= 256;
-    const int kt0 = TR::kSplit ? tid : tid, vt0 = TR::kSplit ? tid - 256 : tid;
-    constexpr int kstride = TR::kSplit ? 256 : NT, vstride = TR::kSplit ? 256 : NT;
-    if (do_k) {
-#pragma unroll
-        for (int i = 0; i < TR::KR; ++i) {
-            const int x = kt0 + kstride * i, row = min(x >> 4, nv - 1), piece = x & 15;
-            R.r[i] = ld_bf8(ksrc + (size_t)row * ld + 8 * piece);
-        }
-    }
-    if (do_v) {
-        constexpr int base = TR::kSplit ? 0 : TR::KR;
-#pragma unroll
-        for (int j = 0; j < TR::VU; ++j) {
-            // consecutive lanes take consecutive row quads of one column block,
-            // so their transposed LDS stores fill one LDS row without bank conflicts
-            const int u = vt0 + vstride * j, kq = u & 15, oct = u >> 4;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = min(4 * kq + rr, nv - 1);
-                R.r[base + 4 * j + rr] = ld_bf8(vsrc + (size_t)row * ld + 8 * oct);
-            }
-        }
-    }
+__device__ __forceinline__ int vswz(int r) { return 4 * (r & 3) + 2 * ((r >> 2) & 1); }
+
+__device__ __forceinline__ void dma16(const bf16* g, bf16* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
 
-// K rows into ks[row * kKS + col]; V transposed into vt[col * kVS + kperm(row)]
-template <int NT>
-__device__ __forceinline__ void tile_store(const TileRegs<NT>& R, bf16* __restrict__ ks,
-                                           bf16* __restrict__ vt, int tid) {
-    using TR = TileRegs<NT>;
-    const bool do_k = !TR::kSplit || tid < 256;
-    const bool do_v = !TR::kSplit || tid >= 256;
-    const int kt0 = tid, vt0 = TR::kSplit ? tid - 256 : tid;
-    constexpr int kstride = TR::kSplit ? 256 : NT, vstride = TR::kSplit ? 256 : NT;
-    if (do_k) {
+// The same load written out, for the lock-step loop: the compiler does not
+// track it, so it places no wait for it before later LDS reads of other
+// buffers; its users wait for it (vmcnt) explicitly.  M0 holds the LDS
+// destination (wave-uniform); one wait state separates the M0 write from the
+// load that reads it.
+__device__ __forceinline__ void dma16_untracked(const bf16* g, unsigned lds_byte) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(g), "s"(m0)
+                     : "memory", "m0");
+}
+
+// staging instruction j (0..16) of a K tile
+__device__ __forceinline__ void stage_k_piece(int j, const bf16* __restrict__ src, size_t ld, int nv,
+                                              bf16* __restrict__ dst) {
+    const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
+    dma16(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 512 * j);
+}
+
+// staging instruction j (0..16) of a K tile, untracked load; dst = LDS
+// byte address of the tile
+__device__ __forceinline__ void stage_k_piece_u(int j, const bf16* __restrict__ src, size_t ld, int nv,
+                                                unsigned dst) {
+    const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
+    dma16_untracked(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 1024u * j);
+}
+
+// staging instruction j (0..15) of a V tile, untracked load
+__device__ __forceinline__ void stage_v_piece_u(int j, const bf16* __restrict__ src, size_t ld, int nv,
+                                                unsigned dst) {
+    const int l = threadIdx.x & 63, row = 4 * j + (l >> 4), slot = (l & 15) ^ vswz(row);
+    dma16_untracked(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 1024u * j);
+}
+
+// one staging wave's instructions w, w + NS, ... of a K or V tile
+template <int NS>
+__device__ __forceinline__ void stage_k_share_u(const bf16* __restrict__ src, size_t ld, int nv, unsigned dst,
+                                                int w) {
 #pragma unroll
-        for (int i = 0; i < TR::KR; ++i) {
-            const int x = kt0 + kstride * i, row = x >> 4, piece = x & 15;
-            st_bf8(ks + row * kKS + 8 * piece, R.r[i]);
-        }
+    for (int t = 0; t < (kKPieces + NS - 1) / NS; ++t)
+        if (w + NS * t < kKPieces) stage_k_piece_u(w + NS * t, src, ld, nv, dst);
+}
+
+template <int NS>
+__device__ __forceinline__ void stage_v_share_u(const bf16* __restrict__ src, size_t ld, int nv, unsigned dst,
+                                                int w) {
+#pragma unroll
+    for (int t = 0; t < (kVPieces + NS - 1) / NS; ++t)
+        if (w + NS * t < kVPieces) stage_v_piece_u(w + NS * t, src, ld, nv, dst);
+}
+
+// staging instruction j (0..15) of a V tile
+__device__ __forceinline__ void stage_v_piece(int j, const bf16* __restrict__ src, size_t ld, int nv,
+                                              bf16* __restrict__ dst) {
+    const int l = threadIdx.x & 63, row = 4 * j + (l >> 4), slot = (l & 15) ^ vswz(row);
+    dma16(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 512 * j);
+}
+
+// Transposed reads of a staged V tile: the value product's A operand for dims
+// 32 dt + l%32 and key storage positions 16 ks + 8 hf .. +7 (key kperm(pos)).
+// ds_read_b64_tr_b16 hands lane d of each 16-lane group element j of the
+// 8-byte read of lane 4j + d/4 of the group (element d%4); lane s of group
+// G = l/16 therefore reads row K0 + s/4, dims 32 dt + 16 (G&1) + 4 (s&3) ..+3,
+// and receives keys K0 .. K0+3 of dim 32 dt + l%32.  K0 = 16 ks + 4 hf for
+// operand elements 0-3 and K0 + 8 for elements 4-7, which are exactly the
+// keys kperm assigns to those elements.  voff[dt] holds the lane's part of
+// the element offset.
+__device__ __forceinline__ void vt_lane_offsets(int (&voff)[4]) {
+    const int l = threadIdx.x & 63, s = l & 15, grp = l >> 4, hf = grp >> 1, gc = grp & 1, m = s >> 2;
+    const int c = (4 * hf + m) * kD + 8 * ((2 * gc + ((s & 3) >> 1)) ^ (2 * hf)) + 4 * (s & 1);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) voff[dt] = c + 32 * (dt ^ m);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 vt_frag(const bf16* vtile, const int (&voff)[4], int dt, int ks) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const bf16* p = vtile + voff[dt] + 16 * ks * kD;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * kD));
+    const i16x8 r = __builtin_shufflevector(a, b2, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// Workgroup barrier that settles only this wave's LDS reads (lgkmcnt), not
+// its outstanding tile staging: staged rows are waited for explicitly
+// (vmcnt) at the barrier that publishes them.  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// Matrix phase of the lock-step output loop: the value product of the
+// previous tile (V in vread, operand pb) and the logits of the current one
+// (K in kread) on the matrix cores.
+__device__ __forceinline__ void matrix_phase(f32x16 (&o)[4], f32x16 (&sc)[2], const bf16x8 (&pb)[4],
+                                             const bf16x8 (&qf)[8], const int (&voff)[4],
+                                             const bf16* __restrict__ kread, const bf16* __restrict__ vread) {
+    const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
+    const bf16* kt = kread + col * kKS + 8 * hf;
+    bf16x8 fv[16], fk[16];
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+        fv[st] = vt_frag(vread, voff, st & 3, st >> 2);
+        fk[st] = ld_bf8(kt + 32 * (st & 1) * kKS + 16 * (st >> 1));
     }
-    if (do_v) {
-        constexpr int base = TR::kSplit ? 0 : TR::KR;
+    sc[0] = zero16();
+    sc[1] = zero16();
 #pragma unroll
-        for (int j = 0; j < TR::VU; ++j) {
-            const int u = vt0 + vstride * j, kq = u & 15, oct = u >> 4;
-            const int pos = kperm(4 * kq);
-            // 4 rows x 8 columns -> 8 columns x 4 rows: byte permutes pair the
-            // low (even column) or high (odd column) halves of two rows' dwords
-            const u32x4 a0 = __builtin_bit_cast(u32x4, R.r[base + 4 * j + 0]);
-            const u32x4 a1 = __builtin_bit_cast(u32x4, R.r[base + 4 * j + 1]);
-            const u32x4 a2 = __builtin_bit_cast(u32x4, R.r[base + 4 * j + 2]);
-            const u32x4 a3 = __builtin_bit_cast(u32x4, R.r[base + 4 * j + 3]);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                u32x2 ev, od;
-                ev[0] = __builtin_amdgcn_perm(a1[d], a0[d], 0x05040100u);
-                ev[1] = __builtin_amdgcn_perm(a3[d], a2[d], 0x05040100u);
-                od[0] = __builtin_amdgcn_perm(a1[d], a0[d], 0x07060302u);
-                od[1] = __builtin_amdgcn_perm(a3[d], a2[d], 0x07060302u);
-                *reinterpret_cast<u32x2*>(vt + (8 * oct + 2 * d) * kVS + pos) = ev;
-                *reinterpret_cast<u32x2*>(vt + (8 * oct + 2 * d + 1) * kVS + pos) = od;
-            }
-        }
+    for (int st = 0; st < 16; ++st) {
+        o[st & 3] = mfma32(fv[st], pb[st >> 2], o[st & 3]);
+        sc[st & 1] = mfma32(fk[st], qf[st >> 1], sc[st & 1]);
     }
 }
 
@@ -546,8 +601,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const float* __restrict__ wq, const bf16* __restrict__ phik, const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const float* __restrict__ lin,
     const float* __restrict__ gpre, bf16* __restrict__ out, Dims D) {
-    constexpr int NT = HB * 128;
-    constexpr int kKBuf = kC * kKS, kVBuf = kD * kVS;
+    constexpr int NW = HB * 2;  // waves
     const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
     const int c = D.T - 1 - (int)(blockIdx.x / per_c);
@@ -555,23 +609,27 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const int hg = r % HG;
     r /= HG;
     const int g = r % D.Hkv, b = r / D.Hkv;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // waves 0..HB-1 take the first 32 queries of their head, waves HB.. the
     // last 32; with HB = 4 the two halves of a head share a SIMD
-    const int qh = wave / HB;
+    const int qh = wave / HB;  // wave-uniform (scalar)
     const int h = g * D.G + hg * HB + wave % HB;
     const int t0 = c * kC;
     const int oq = 32 * qh + col;                  // this lane's query offset in the chunk
     const size_t bg = (size_t)b * D.Hkv + g;
     const float cl2 = D.tau * kLog2e;
 
-    // K of tile i in kbuf(i) (two buffers), V^T of tile i in vbuf(i) (three:
-    // the second half of the queries finishes tile i-1 while the first half
-    // works on tile i)
-    __shared__ __align__(16) bf16 smem[2 * kKBuf + 3 * kVBuf];
-    auto kbuf = [&](int i) { return smem + (i & 1) * kKBuf; };
-    auto vbuf = [&](int i) { return smem + 2 * kKBuf + (i % 3) * kVBuf; };
-    __shared__ __align__(16) float sts[(kD + 1) * kSS];  // linear prefix S^T rows, then z
+    // K of tile i in kbuf(i) (two buffers), V of tile i in vbuf(i): two
+    // buffers when the two query halves alternate in lock step (HB = 4), three
+    // when the second half only trails the first by part of a tile.  The
+    // linear prefix S^T rows (then z) follow; the epilogue reuses the front.
+    constexpr int kNV = HB == 4 ? 2 : 3;
+    constexpr int kStsFloats = (kD + 1) * kSS > HB * 32 * kKS ? (kD + 1) * kSS : HB * 32 * kKS;
+    __shared__ __align__(16) bf16 smem[2 * kKTile + kNV * kVTile];
+    __shared__ __align__(16) float sts[kStsFloats];
+    auto kbuf = [&](int i) { return smem + (i & 1) * kKTile; };
+    auto vbuf = [&](int i) { return smem + 2 * kKTile + (kNV == 2 ? (i & 1) : i % 3) * kVTile; };
 
     // tiles: 0 = chunk c-1 (c >= 1), 1 = chunk c, 2.. = compact selected rows
     const int nrows = c >= 2 ? (c - 1) * D.lam : 0;
@@ -580,19 +638,44 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* kb = ksel + bg * (size_t)D.n_full * D.lam * kD;
     const bf16* vb = vsel + bg * (size_t)D.n_full * D.lam * kD;
     const size_t ldkv = (size_t)D.Hkv * kD;
-    auto fetch = [&](int i, TileRegs<NT>& R) {
+    // rows of tile i: source offset (elements, K and V alike), row stride, valid count
+    auto tile_src = [&](int i, size_t& off, size_t& ld, int& nv, bool& compact) {
         if (i < 2) {
             const int tc = c - 1 + i;
-            const size_t off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
-            tile_fetch<NT>(R, k + off, v + off, ldkv, min(kC, D.N - tc * kC), tid);
+            off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
+            ld = ldkv;
+            nv = min(kC, D.N - tc * kC);
+            compact = false;
         } else {
             const int r0 = (i - 2) * kC;
-            tile_fetch<NT>(R, kb + (size_t)r0 * kD, vb + (size_t)r0 * kD, kD, min(kC, nrows - r0), tid);
+            off = (size_t)r0 * kD;
+            ld = kD;
+            nv = min(kC, nrows - r0);
+            compact = true;
         }
     };
+    // issue this wave's share of the staging instructions of K and/or V of
+    // tile i; they complete by the wave's next vmcnt(0)
+    auto stage = [&](int i, bool do_k, bool do_v) {
+        size_t off, ld;
+        int nv;
+        bool cp;
+        tile_src(i, off, ld, nv, cp);
+        if (do_k)
+            for (int j = wave; j < kKPieces; j += NW) stage_k_piece(j, (cp ? kb : k) + off, ld, nv, kbuf(i));
+        if (do_v)
+            for (int j = wave; j < kVPieces; j += NW) stage_v_piece(j, (cp ? vb : v) + off, ld, nv, vbuf(i));
+    };
+    int voff[4];
+    vt_lane_offsets(voff);
 
-    TileRegs<NT> R;
-    fetch(first, R);
+    stage(first, true, true);
+    if constexpr (HB == 4) {
+        // the V buffer tile `first` does not use holds zeros: the first value
+        // product reads it (with zero probabilities)
+        bf16* vz = vbuf(first + 1);
+        for (int x = tid; x < kVTile / 8; x += 64 * NW) st_bf8(vz + 8 * x, zero_bf8());
+    }
     // Q operand: qf[s] holds query t0 + oq (tokens past N repeat N-1, never
     // written), dims 16 s + 8 hf .. +7
     bf16x8 qf[1][8];
@@ -602,8 +685,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[0][s] = ld_bf8(row + 16 * s);
     }
-    tile_store<NT>(R, kbuf(first), vbuf(first), tid);
-    if (first + 1 < ntile) fetch(first + 1, R);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile
     __syncthreads();
 
     // running state of the lane's query: reference point m2 (log2 units,
@@ -624,7 +706,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             const f32x4* st4 = reinterpret_cast<const f32x4*>(lin + (bg * D.n_full + cp) * (size_t)((kD + 1) * kD));
             const f32x4* gs4 = reinterpret_cast<const f32x4*>(
                 gpre + (bg * ((D.n_full + D.ng - 1) / D.ng) + cp / D.ng) * (size_t)((kD + 1) * kD));
-            for (int x = tid; x < (kD + 1) * kD / 4; x += NT) {
+            for (int x = tid; x < (kD + 1) * kD / 4; x += 64 * NW) {
                 const int row = (4 * x) / kD, c4 = (4 * x) % kD;
                 *reinterpret_cast<f32x4*>(&sts[row * kSS + c4]) = st4[x] + gs4[x];
             }
@@ -684,8 +766,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 pa = pack_acc(wl[ks >> 1], ks & 1);
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-                    o[dt] = mfma32(ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf), pa, o[dt]);
+                for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vt_frag(vt, voff, dt, ks), pa, o[dt]);
             }
         }
         if (c >= 2) {
@@ -718,9 +799,9 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 sc[kt] = mfma32(ld_bf8(ks + (32 * kt + col) * kKS + 16 * s + 8 * hf), qf[0][s], sc[kt]);
         }
     };
-    // softmax terms and value product of tile i: key row rk counts for the
-    // lane's query when bit rk of (rk > oq ? hi_m : lo_m) is set
-    auto finish = [&](int i, f32x16 (&sc)[2]) {
+    // softmax terms of tile i, in place: key row rk counts for the lane's
+    // query when bit rk of (rk > oq ? hi_m : lo_m) is set
+    auto softmax = [&](int i, f32x16 (&sc)[2]) {
         uint64_t hi_m, lo_m;
         if (i == 0) {  // chunk c-1: window keys (offset above the query's) and routed selected keys
             hi_m = ~0ull;
@@ -733,23 +814,25 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
         }
         if ((hi_m & lo_m) != ~0ull) {
-            // edge tiles only: masked key rows drop out of the softmax
+            // edge tiles only: masked key rows drop out of the softmax.  The
+            // lane's combined mask, shifted down by 4 hf, holds the bit of
+            // element vv of accumulator kt at 32 kt + 8 (vv / 4) + vv % 4.
             __asm__ volatile("");
+            const uint64_t gt = oq >= 63 ? 0ull : ~0ull << (oq + 1);
+            const uint64_t mm = ((hi_m & gt) | (lo_m & ~gt)) >> (4 * hf);
+            const uint32_t mw[2] = {(uint32_t)mm, (uint32_t)(mm >> 32)};
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int vv = 0; vv < 16; ++vv) {
-                    const int rk = 32 * kt + acc_row(vv, hf);
-                    const uint64_t m = rk > oq ? hi_m : lo_m;
-                    if (!((m >> rk) & 1ull)) sc[kt][vv] = kNegInf;
-                }
+                for (int vv = 0; vv < 16; ++vv)
+                    if (!((mw[kt] >> (8 * (vv >> 2) + (vv & 3))) & 1u)) sc[kt][vv] = kNegInf;
         }
         float tmax = kNegInf;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) tmax = fmaxf(tmax, sc[kt][vv]);
-        const float tm2 = fmaxf(tmax, xor32(tmax)) * cl2;
+        const float tm2 = half_pair_max(tmax) * cl2;
         if (__any(tm2 > m2 + kLazy)) {
             // a rare path: keep the compiler from speculating it into every tile
             __asm__ volatile("");
@@ -771,44 +854,100 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 sc[kt][vv] = p;
                 ls += p;
             }
-        const bf16* vt = vbuf(i);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 pa = pack_acc(sc[ks >> 1], ks & 1);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                o[dt] = mfma32(ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf), pa, o[dt]);
-        }
     };
 
-    // settle every outstanding load (Q, the first prefetch) here, once: the
-    // loop then only ever waits for its own prefetch, at the LDS store
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    // The first query half runs [logits, softmax, values] of tile i; the
-    // second runs [softmax, values] of tile i-1 and then the logits of tile i,
-    // so on each SIMD one wave's exp arithmetic meets the other's products.
     f32x16 sc[2];
-    for (int i = first; i <= ntile; ++i) {
-        // one copy of each step: phase 0 = (first half: logits) + softmax and
-        // values of tile i - qh; phase 1 = (second half: logits)
-#pragma unroll 1
-        for (int ph = 0; ph < 2; ++ph) {
-            if (ph == qh && i < ntile) qk(i, sc);
-            if (ph == 0) {
-                const int j = i - qh;
-                if (j >= first && j < ntile) finish(j, sc);
+    if constexpr (HB == 4) {
+        // Lock-step ping-pong.  Each wave alternates a matrix phase M(s) (the
+        // value product of tile s-1 and the logits of tile s: 32 products, no
+        // exp) and a vector phase V(s) (softmax of tile s), one barrier after
+        // each.  The second query half starts one phase late, so on every
+        // SIMD one wave's products overlap the other's exp arithmetic.
+        // During step s (M(s) of the first half, then its V(s)) K of tile s
+        // and V of tile s-1 are read.  M(first) runs its value product on zero probabilities
+        // over the zero-filled other V buffer, and the logits of M(ntile) are
+        // never used.
+        bf16x8 pb[4];  // probabilities of the last softmaxed tile (value-product operand)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) pb[ks] = zero_bf8();
+        // The second half stages, in its vector phases (their exp work
+        // leaves issue slots free): K of tile s+2 and V of tile s+1 during
+        // step s+1, while that step reads K of s+1 and V of s; it settles
+        // them at the end of its own matrix phase of that step.
+        const unsigned lds0 = (unsigned)(size_t)(lds_void*)smem;
+        // source of the rows of tile i (K when is_k, else V)
+        auto rows_of = [&](int i, bool is_k, size_t& ld, int& nv) -> const bf16* {
+            size_t off;
+            bool cp;
+            tile_src(i, off, ld, nv, cp);
+            return (is_k ? (cp ? kb : k) : (cp ? vb : v)) + off;
+        };
+        if (qh == 1) {
+            if (first + 1 < ntile) {  // V of `first` is already in place
+                size_t ld;
+                int nv;
+                const bf16* src = rows_of(first + 1, true, ld, nv);
+                stage_k_share_u<HB>(src, ld, nv, lds0 + 2u * ((first + 1) & 1) * kKTile, wave - HB);
             }
+            lds_barrier();
         }
-        if (i + 1 < ntile) {
-            tile_store<NT>(R, kbuf(i + 1), vbuf(i + 1), tid);
-            if (i + 2 < ntile) fetch(i + 2, R);
+        for (int s = first;; ++s) {
+            matrix_phase(o, sc, pb, qf[0], voff, kbuf(s), vbuf(s > first ? s - 1 : s + 1));
+            if (qh == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged tiles landed
+            lds_barrier();
+            if (qh == 1 && s == ntile) break;
+            if (qh == 1) {
+                size_t ld;
+                int nv;
+                if (s + 2 < ntile) {
+                    const bf16* src = rows_of(s + 2, true, ld, nv);
+                    stage_k_share_u<HB>(src, ld, nv, lds0 + 2u * (s & 1) * kKTile, wave - HB);
+                }
+                if (s + 1 < ntile) {
+                    const bf16* src = rows_of(s + 1, false, ld, nv);
+                    stage_v_share_u<HB>(src, ld, nv, lds0 + 2u * (2 * kKTile + ((s + 1) & 1) * kVTile), wave - HB);
+                }
+            }
+            if (s < ntile) {
+                softmax(s, sc);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) pb[ks] = pack_acc(sc[ks >> 1], ks & 1);
+            }
+            lds_barrier();
+            if (s == ntile) break;
         }
-        __syncthreads();
+    } else {
+        // The first query half runs [logits, softmax, values] of tile i; the
+        // second runs [softmax, values] of tile i-1 and then the logits of
+        // tile i, so on each SIMD one wave's exp arithmetic meets the other's
+        // products.  Tile i+1 is staged during step i.
+        for (int i = first; i <= ntile; ++i) {
+            if (i + 1 < ntile) stage(i + 1, true, true);
+#pragma unroll 1
+            for (int ph = 0; ph < 2; ++ph) {
+                if (ph == qh && i < ntile) qk(i, sc);
+                if (ph == 0) {
+                    const int j = i - qh;
+                    if (j >= first && j < ntile) {
+                        softmax(j, sc);
+                        const bf16* vt = vbuf(j);
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks) {
+                            const bf16x8 pa = pack_acc(sc[ks >> 1], ks & 1);
+#pragma unroll
+                            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vt_frag(vt, voff, dt, ks), pa, o[dt]);
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i+1 landed
+            __syncthreads();
+        }
     }
 
     // epilogue: normalise, stage each wave's 32 x 128 tile in LDS, write rows
     const float il = 1.f / (ls + xor32(ls));
-    bf16* ot = smem + wave * (32 * kKS);
+    bf16* ot = reinterpret_cast<bf16*>(sts) + wave * (32 * kKS);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
