@@ -486,24 +486,44 @@ __device__ __forceinline__ void stage_k_piece(int j, const bf16* __restrict__ sr
     dma16(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 512 * j);
 }
 
+// The same, issued only when en != 0 (wave-uniform); the test and skip sit
+// inside the asm statement, so the surrounding code stays one basic block.
+__device__ __forceinline__ void dma16_untracked_if(const bf16* g, unsigned lds_byte, int en) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+    const int e = __builtin_amdgcn_readfirstlane(en);
+    __asm__ volatile("s_cmp_eq_u32 %2, 0\n\ts_cbranch_scc1 1f\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %0, off\n1:"
+                     :
+                     : "v"(g), "s"(m0), "s"(e)
+                     : "memory", "m0", "scc");
+}
+
 // staging instruction j (0..16) of a K tile, untracked load; dst = LDS
-// byte address of the tile
-__device__ __forceinline__ void stage_k_piece_u(int j, const bf16* __restrict__ src, size_t ld, int nv,
+// byte address of the tile; ld (elements) and row offsets fit 24 bits
+__device__ __forceinline__ void stage_k_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
                                                 unsigned dst) {
     const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
-    dma16_untracked(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 1024u * j);
+    dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
+}
+
+// staging instruction j of a K tile when j < 17 (no branch around it)
+__device__ __forceinline__ void stage_k_piece_if(int j, const bf16* __restrict__ src, int ld, int nv,
+                                                 unsigned dst) {
+    const int jj = min(j, kKPieces - 1);
+    const int p = 64 * jj + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
+    dma16_untracked_if(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * jj, j < kKPieces);
 }
 
 // staging instruction j (0..15) of a V tile, untracked load
-__device__ __forceinline__ void stage_v_piece_u(int j, const bf16* __restrict__ src, size_t ld, int nv,
+__device__ __forceinline__ void stage_v_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
                                                 unsigned dst) {
     const int l = threadIdx.x & 63, row = 4 * j + (l >> 4), slot = (l & 15) ^ vswz(row);
-    dma16_untracked(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 1024u * j);
+    dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
 }
 
 // one staging wave's instructions w, w + NS, ... of a K or V tile
 template <int NS>
-__device__ __forceinline__ void stage_k_share_u(const bf16* __restrict__ src, size_t ld, int nv, unsigned dst,
+__device__ __forceinline__ void stage_k_share_u(const bf16* __restrict__ src, int ld, int nv, unsigned dst,
                                                 int w) {
 #pragma unroll
     for (int t = 0; t < (kKPieces + NS - 1) / NS; ++t)
@@ -511,7 +531,7 @@ __device__ __forceinline__ void stage_k_share_u(const bf16* __restrict__ src, si
 }
 
 template <int NS>
-__device__ __forceinline__ void stage_v_share_u(const bf16* __restrict__ src, size_t ld, int nv, unsigned dst,
+__device__ __forceinline__ void stage_v_share_u(const bf16* __restrict__ src, int ld, int nv, unsigned dst,
                                                 int w) {
 #pragma unroll
     for (int t = 0; t < (kVPieces + NS - 1) / NS; ++t)
@@ -551,6 +571,19 @@ __device__ __forceinline__ bf16x8 vt_frag(const bf16* vtile, const int (&voff)[4
     const i16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * kD));
     const i16x8 r = __builtin_shufflevector(a, b2, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, r);
+}
+
+// Scheduling pattern for one pair of products (value, logits) of the
+// software-pipelined loop: product, R1 LDS reads, NV vector instructions,
+// product, R2 LDS reads, NV vector instructions.
+template <int R1, int R2, int NV>
+__device__ __forceinline__ void sched_step_pair() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (R1 > 0) __builtin_amdgcn_sched_group_barrier(0x100, R1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (R2 > 0) __builtin_amdgcn_sched_group_barrier(0x100, R2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
 }
 
 // Workgroup barrier that settles only this wave's LDS reads (lgkmcnt), not
@@ -801,7 +834,10 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     };
     // softmax terms of tile i, in place: key row rk counts for the lane's
     // query when bit rk of (rk > oq ? hi_m : lo_m) is set
-    auto softmax = [&](int i, f32x16 (&sc)[2]) {
+    // softmax terms of tile i, in place, in three steps.  Masking: key row
+    // rk counts for the lane's query when bit rk of (rk > oq ? hi_m : lo_m)
+    // is set.
+    auto softmax_mask = [&](int i, f32x16 (&sc)[2]) -> bool {
         uint64_t hi_m, lo_m;
         if (i == 0) {  // chunk c-1: window keys (offset above the query's) and routed selected keys
             hi_m = ~0ull;
@@ -826,7 +862,15 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv)
                     if (!((mw[kt] >> (8 * (vv >> 2) + (vv & 3))) & 1u)) sc[kt][vv] = kNegInf;
+            return true;
         }
+        return false;
+    };
+    // reference point: when the tile's maximum exceeds m2 by more than kLazy
+    // (log2 units) the reference moves up to the next integer at or above it
+    // and the running sums scale by al, an exact power of two (returns true;
+    // the caller scales O)
+    auto softmax_ref = [&](const f32x16 (&sc)[2], float& al) -> bool {
         float tmax = kNegInf;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -836,15 +880,15 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         if (__any(tm2 > m2 + kLazy)) {
             // a rare path: keep the compiler from speculating it into every tile
             __asm__ volatile("");
-            const float mn = fmaxf(m2, tm2);
-            const float al = __builtin_amdgcn_exp2f(m2 - mn);
+            const float mn = ceilf(fmaxf(m2, tm2));
+            al = __builtin_amdgcn_exp2f(m2 - mn);
             m2 = mn;
             ls *= al;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int vv = 0; vv < 16; ++vv) o[dt][vv] *= al;
+            return true;
         }
+        return false;
+    };
+    auto softmax_exp = [&](f32x16 (&sc)[2]) {
         const float nm = -m2;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -855,66 +899,184 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 ls += p;
             }
     };
+    auto softmax = [&](int i, f32x16 (&sc)[2]) {
+        softmax_mask(i, sc);
+        float al = 1.f;
+        if (softmax_ref(sc, al)) {
+            __asm__ volatile("");
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) o[dt][vv] *= al;
+        }
+        softmax_exp(sc);
+    };
 
     f32x16 sc[2];
     if constexpr (HB == 4) {
-        // Lock-step ping-pong.  Each wave alternates a matrix phase M(s) (the
-        // value product of tile s-1 and the logits of tile s: 32 products, no
-        // exp) and a vector phase V(s) (softmax of tile s), one barrier after
-        // each.  The second query half starts one phase late, so on every
-        // SIMD one wave's products overlap the other's exp arithmetic.
-        // During step s (M(s) of the first half, then its V(s)) K of tile s
-        // and V of tile s-1 are read.  M(first) runs its value product on zero probabilities
-        // over the zero-filled other V buffer, and the logits of M(ntile) are
-        // never used.
-        bf16x8 pb[4];  // probabilities of the last softmaxed tile (value-product operand)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) pb[ks] = zero_bf8();
-        // The second half stages, in its vector phases (their exp work
-        // leaves issue slots free): K of tile s+2 and V of tile s+1 during
-        // step s+1, while that step reads K of s+1 and V of s; it settles
-        // them at the end of its own matrix phase of that step.
+        // Software-pipelined loop, the same in every wave: iteration s runs
+        // the value product of tile s-1 and the logits of tile s+1 on the
+        // matrix cores while the vector units work through the softmax of
+        // tile s, all in one instruction stream, so each wave keeps its
+        // products and its exp arithmetic in flight together.  Iteration s
+        // reads K of s+1 and V of s-1 and stages K of s+2 and V of s (LDS
+        // straight from global memory, untracked, settled before the
+        // iteration's barrier).  The first value product runs on zero
+        // probabilities over the zero-filled spare V buffer.
         const unsigned lds0 = (unsigned)(size_t)(lds_void*)smem;
-        // source of the rows of tile i (K when is_k, else V)
-        auto rows_of = [&](int i, bool is_k, size_t& ld, int& nv) -> const bf16* {
-            size_t off;
+        auto rows_of = [&](int i, bool is_k, int& ld, int& nv) -> const bf16* {
+            size_t off, ld64;
             bool cp;
-            tile_src(i, off, ld, nv, cp);
+            tile_src(i, off, ld64, nv, cp);
+            ld = (int)ld64;
             return (is_k ? (cp ? kb : k) : (cp ? vb : v)) + off;
         };
-        if (qh == 1) {
-            if (first + 1 < ntile) {  // V of `first` is already in place
-                size_t ld;
-                int nv;
-                const bf16* src = rows_of(first + 1, true, ld, nv);
-                stage_k_share_u<HB>(src, ld, nv, lds0 + 2u * ((first + 1) & 1) * kKTile, wave - HB);
-            }
-            lds_barrier();
-        }
-        for (int s = first;; ++s) {
-            matrix_phase(o, sc, pb, qf[0], voff, kbuf(s), vbuf(s > first ? s - 1 : s + 1));
-            if (qh == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged tiles landed
-            lds_barrier();
-            if (qh == 1 && s == ntile) break;
-            if (qh == 1) {
-                size_t ld;
-                int nv;
-                if (s + 2 < ntile) {
-                    const bf16* src = rows_of(s + 2, true, ld, nv);
-                    stage_k_share_u<HB>(src, ld, nv, lds0 + 2u * (s & 1) * kKTile, wave - HB);
-                }
-                if (s + 1 < ntile) {
-                    const bf16* src = rows_of(s + 1, false, ld, nv);
-                    stage_v_share_u<HB>(src, ld, nv, lds0 + 2u * (2 * kKTile + ((s + 1) & 1) * kVTile), wave - HB);
-                }
-            }
-            if (s < ntile) {
-                softmax(s, sc);
+        // maximum of a tile's logits over the lane's query (both lane halves), log2 units
+        auto tile_max2 = [&](const f32x16 (&x)[2]) {
+            float a = fmaxf(x[0][0], x[0][1]), b2 = fmaxf(x[0][8], x[0][9]);
+            float c2 = fmaxf(x[1][0], x[1][1]), d2 = fmaxf(x[1][8], x[1][9]);
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) pb[ks] = pack_acc(sc[ks >> 1], ks & 1);
+            for (int vv = 2; vv < 8; vv += 2) {
+                a = fmaxf(a, fmaxf(x[0][vv], x[0][vv + 1]));
+                b2 = fmaxf(b2, fmaxf(x[0][vv + 8], x[0][vv + 9]));
+                c2 = fmaxf(c2, fmaxf(x[1][vv], x[1][vv + 1]));
+                d2 = fmaxf(d2, fmaxf(x[1][vv + 8], x[1][vv + 9]));
             }
+            return half_pair_max(fmaxf(fmaxf(a, b2), fmaxf(c2, d2))) * cl2;
+        };
+        bf16x8 pb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) pb[ks] = zero_bf8();
+        // K of first+1 (V of first and K of first are in place; a tile index
+        // past the last one stages the last one again, unused)
+        {
+            int ld, nv;
+            const bf16* src = rows_of(min(first + 1, ntile - 1), true, ld, nv);
+            stage_k_share_u<2 * HB>(src, ld, nv, lds0 + 2u * ((first + 1) & 1) * kKTile, wave);
+        }
+        qk(first, sc);
+        float tm2 = tile_max2(sc);  // maximum of the unmasked logits of tile s
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        lds_barrier();
+        // One iteration: tile s's logits in sc and tile s-1's probabilities in
+        // pb; leaves tile s+1's logits in sn and tile s's probabilities in pn.
+        // Two calls per loop turn with the roles swapped keep every value in
+        // place (no copies).
+        auto iteration = [&](int s, f32x16 (&sc)[2], bf16x8 (&pb)[4], f32x16 (&sn)[2], bf16x8 (&pn)[4])
+                             __attribute__((always_inline)) {
+            // softmax of tile s up to its exps: masking (edge tiles, with their
+            // maximum taken again), rescale decision.  A rescale scales O and
+            // the pending probabilities of tile s-1 alike (exactly: al is a
+            // power of two), which equals scaling after the value product of
+            // tile s-1.
+            if (softmax_mask(s, sc)) tm2 = tile_max2(sc);
+            if (__any(tm2 > m2 + kLazy)) {
+                // a rare path: keep the compiler from speculating it into every tile
+                __asm__ volatile("");
+                const float mn = ceilf(fmaxf(m2, tm2));
+                const float al = __builtin_amdgcn_exp2f(m2 - mn);
+                m2 = mn;
+                ls *= al;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) o[dt][vv] *= al;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) pb[ks][j] = (bf16)((float)pb[ks][j] * al);
+            }
+            // staging sources: K of s+2 (or the last tile again), V of s
+            int kld, knv, vld, vnv;
+            const bf16* ksrc = rows_of(min(s + 2, ntile - 1), true, kld, knv);
+            const bf16* vsrc = rows_of(s, false, vld, vnv);
+            const unsigned kdst = lds0 + 2u * (s & 1) * kKTile;
+            const unsigned vdst = lds0 + 2u * (2 * kKTile + (s & 1) * kVTile);
+            // One stream of 16 steps pinned by scheduling barriers.  Steps 0-7
+            // take the logits of tile s+1 (two products each: keys 0-31 and
+            // 32-63), steps 8-15 the value product of tile s-1 (two each);
+            // every step does the exps of two elements of tile s and issues
+            // the operand reads of the step two ahead; some steps issue a
+            // staging instruction; steps 10-15 take the maximum of the
+            // finished logits.
+            const bf16* vt = vbuf(s > first ? s - 1 : s + 1);
+            const bf16* kt = kbuf(s + 1) + col * kKS + 8 * hf;
+            sn[0] = zero16();
+            sn[1] = zero16();
+            const float nm = -m2;
+            bf16x8 a0[16], a1[16];
+            auto operands = [&](int st) __attribute__((always_inline)) {
+                if (st < 8) {
+                    a0[st] = ld_bf8(kt + 16 * st);
+                    a1[st] = ld_bf8(kt + 32 * kKS + 16 * st);
+                } else {
+                    const int x = 2 * (st - 8);
+                    a0[st] = vt_frag(vt, voff, x & 3, x >> 2);
+                    a1[st] = vt_frag(vt, voff, (x + 1) & 3, (x + 1) >> 2);
+                }
+            };
+            operands(0);
+            operands(1);
+            float ta = kNegInf, tb = kNegInf;
+#pragma unroll
+            for (int st = 0; st < 16; ++st) {
+                if (st + 2 < 16) operands(st + 2);
+                if (st < 8) {
+                    sn[0] = mfma32(a0[st], qf[0][st], sn[0]);
+                    sn[1] = mfma32(a1[st], qf[0][st], sn[1]);
+                } else {
+                    const int x = 2 * (st - 8);
+                    o[x & 3] = mfma32(a0[st], pb[x >> 2], o[x & 3]);
+                    o[(x + 1) & 3] = mfma32(a1[st], pb[(x + 1) >> 2], o[(x + 1) & 3]);
+                }
+#pragma unroll
+                for (int e = 2 * st; e < 2 * st + 2; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], cl2, nm));
+                    sc[e >> 4][e & 15] = p;
+                    ls += p;
+                }
+                if ((st & 3) == 3) pn[st >> 2] = pack_acc(sc[st >> 3], (st >> 2) & 1);
+                if (st == 1 || st == 4 || st == 7)
+                    stage_k_piece_if(wave + 2 * HB * (st / 3), ksrc, kld, knv, kdst);
+                if (st == 9 || st == 12)
+                    stage_v_piece_u(wave + 2 * HB * ((st - 9) / 3), vsrc, vld, vnv, vdst);
+                if (st >= 10) {
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) {
+                        const int e = 6 * (st - 10) + j;  // 0..35, elements 0..31
+                        if (e < 16) ta = fmaxf(ta, fmaxf(sn[0][e], sn[1][e]));
+                    }
+#pragma unroll
+                    for (int j = 3; j < 6; ++j) {
+                        const int e = 6 * (st - 10) + j;
+                        if (e < 16) tb = fmaxf(tb, fmaxf(sn[0][e], sn[1][e]));
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            tm2 = half_pair_max(fmaxf(ta, tb)) * cl2;
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged tiles landed
             lds_barrier();
-            if (s == ntile) break;
+        };
+        f32x16 sc2[2];
+        bf16x8 pb2[4];
+        int s = first;
+        for (; s + 1 < ntile; s += 2) {
+            iteration(s, sc, pb, sc2, pb2);
+            iteration(s + 1, sc2, pb2, sc, pb);
+        }
+        if (s < ntile) {
+            iteration(s, sc, pb, sc2, pb2);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) pb[ks] = pb2[ks];
+        }
+        {
+            // value product of the last tile
+            const bf16* vt = vbuf(ntile - 1);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vt_frag(vt, voff, dt, ks), pb[ks], o[dt]);
         }
     } else {
         // The first query half runs [logits, softmax, values] of tile i; the
