@@ -59,15 +59,19 @@ bool mfma_fwd_supported(const Dims& D);
 hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const void* v,
                              float* scores, int32_t* sel_idx, uint8_t* route, void* ksel,
                              void* vsel, hipStream_t s);
+// NP-Map projections as bf16 high/low parts: hl = [wq hi, wq lo, wk hi, wk lo],
+// each Hkv * (d'/2) * d elements
+hipError_t launch_np_weight_split(const Dims& D, const float* wphi_q, const float* wphi_k, void* hl,
+                                  hipStream_t s);
 // phi_k rows [B, Hkv, N, d'] (bf16, features in kperm order) and per-chunk
 // linear sums [B, Hkv, n_full, d + 1, d'] (S^T rows then z, kperm order)
-hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const float* wphi_k,
+hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const void* wsplit,
                            const uint8_t* route, void* phik, float* lin, hipStream_t s);
 // gpre [B, Hkv, ceil(n_full / ng), d + 1, d']: exclusive prefix over runs
 hipError_t launch_la_group_scan(const Dims& D, const float* lin, float* gpre, int cap_chunk,
                                 float* cap_S, float* cap_z, hipStream_t s);
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
-                              const float* wphi_q, const void* phik, const uint8_t* route,
+                              const void* wsplit, const void* phik, const uint8_t* route,
                               const void* ksel, const void* vsel, const float* lin,
                               const float* gpre, void* out, hipStream_t s);
 

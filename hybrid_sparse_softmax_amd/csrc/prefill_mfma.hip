@@ -34,6 +34,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kC = 64;          // chunk = window
@@ -101,14 +102,16 @@ __device__ __forceinline__ void load_vt_tile(const bf16* __restrict__ src, size_
 }
 
 // NP-Map (Sec. 3.2, Hedgehog form of Sec. 2) of NT*32 tokens by one wave.
-//   u = P x (P: [64][128] fp32 as bf16 high + low parts on MFMA),
+//   u = P x (P: [64][128] fp32, given as bf16 high and low parts Ph, Pl with
+//   P = Ph + Pl up to the rounding of Pl; both go through the MFMA),
 //   z = ||x|| u / ||u|| (0 if u = 0),  phi = [softmax(z); softmax(-z)].
+// The softmax exps are exp2 of (z - max) log2(e), one fma each.
 // xb[tt][s]: token 32tt + l%32, dims 16s + 8(l/32) .. +7.
 // phi[tt][sgn][ft]: accumulator layout, rows = feature 64 sgn + 32 ft +
 // acc_row(v, l/32), column = token.
 template <int NT>
-__device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const float* __restrict__ P,
-                                            f32x16 (&phi)[NT][2][2]) {
+__device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const bf16* __restrict__ Ph,
+                                            const bf16* __restrict__ Pl, f32x16 (&phi)[NT][2][2]) {
     const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
     f32x16 u[NT][2];
 #pragma unroll
@@ -120,8 +123,8 @@ __device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const flo
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft) {
-            bf16x8 hi, lo;
-            ld_split8(P + (32 * ft + col) * kD + 16 * s + 8 * hf, hi, lo);
+            const bf16x8 hi = ld_bf8(Ph + (32 * ft + col) * kD + 16 * s + 8 * hf);
+            const bf16x8 lo = ld_bf8(Pl + (32 * ft + col) * kD + 16 * s + 8 * hf);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 u[tt][ft] = mfma32(hi, xb[tt][s], u[tt][ft]);
@@ -135,36 +138,34 @@ __device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const flo
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = (float)xb[tt][s][j];
-                nx = fmaf(x, x, nx);
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2 x2 = {xb[tt][s][2 * j], xb[tt][s][2 * j + 1]};
+                nx = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, nx, false);
             }
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) nu = fmaf(u[tt][ft][v], u[tt][ft][v], nu);
-        nx += xor32(nx);
-        nu += xor32(nu);
-        const float sc = nu > 0.f ? sqrtf(nx) / sqrtf(nu) : 0.f;
-        float mp = kNegInf, mn = kNegInf;
+        float umax = kNegInf, umin = __builtin_inff();
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float z = u[tt][ft][v] * sc;
-                u[tt][ft][v] = z;
-                mp = fmaxf(mp, z);
-                mn = fmaxf(mn, -z);
+                nu = fmaf(u[tt][ft][v], u[tt][ft][v], nu);
+                umax = fmaxf(umax, u[tt][ft][v]);
+                umin = fminf(umin, u[tt][ft][v]);
             }
-        mp = fmaxf(mp, xor32(mp));
-        mn = fmaxf(mn, xor32(mn));
+        nx += xor32(nx);
+        nu += xor32(nu);
+        umax = fmaxf(umax, xor32(umax));
+        umin = fminf(umin, xor32(umin));
+        // z = sc u with sc >= 0, so max z = sc umax and max(-z) = -sc umin
+        const float scl = (nu > 0.f ? sqrtf(nx) / sqrtf(nu) : 0.f) * kLog2e;
+        const float mp = scl * umax, mn = -scl * umin;
         float sp = 0.f, sn = 0.f;
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float z = u[tt][ft][v];
-                const float ep = expf(z - mp), en = expf(-z - mn);
+                const float uu = u[tt][ft][v];
+                const float ep = __builtin_amdgcn_exp2f(fmaf(uu, scl, -mp));
+                const float en = __builtin_amdgcn_exp2f(fmaf(uu, -scl, -mn));
                 phi[tt][0][ft][v] = ep;
                 phi[tt][1][ft][v] = en;
                 sp += ep;
@@ -180,6 +181,20 @@ __device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const flo
                 phi[tt][0][ft][v] *= ip;
                 phi[tt][1][ft][v] *= in;
             }
+    }
+}
+
+// NP-Map projections of queries and keys as bf16 high and low parts (one
+// pass over wq then wk, n floats each): hl = [wq high, wq low, wk high, wk low]
+__global__ __launch_bounds__(256) void np_weight_split_kernel(const float* __restrict__ wq,
+                                                              const float* __restrict__ wk,
+                                                              bf16* __restrict__ hl, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < 2 * n; i += gridDim.x * 256) {
+        const float x = i < n ? wq[i] : wk[i - n];
+        const bf16 h = (bf16)x;
+        const int j = i < n ? i : i + n;  // high part of wq at i, of wk at 2n + (i - n)
+        hl[j] = h;
+        hl[j + n] = (bf16)(x - (float)h);
     }
 }
 
@@ -338,7 +353,8 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
 // earlier runs, so the full prefix of chunk c is lin[c] + gpre[c / ng].
 __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v,
-                                                       const float* __restrict__ wk,
+                                                       const bf16* __restrict__ wkh,
+                                                       const bf16* __restrict__ wkl,
                                                        const uint8_t* __restrict__ route,
                                                        bf16* __restrict__ phik,
                                                        float* __restrict__ lin, Dims D) {
@@ -363,7 +379,7 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
 #pragma unroll
             for (int s = 0; s < 8; ++s) xb[0][s] = ld_bf8(kr + 16 * s);
             f32x16 phi[1][2][2];
-            np_map_mfma<1>(xb, wk + (size_t)g * (kD / 2) * kD, phi);
+            np_map_mfma<1>(xb, wkh + (size_t)g * (kD / 2) * kD, wkl + (size_t)g * (kD / 2) * kD, phi);
             // phi_k row of the token, features in kperm order, for the read-out
             bf16* pr = phik + (bg * D.N + tok) * kD;
 #pragma unroll
@@ -631,7 +647,8 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&o)[4], f32x16 (&sc)[2], co
 template <int HB>
 __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ wq, const bf16* __restrict__ phik, const uint8_t* __restrict__ route,
+    const bf16* __restrict__ wqh, const bf16* __restrict__ wql, const bf16* __restrict__ phik,
+    const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const float* __restrict__ lin,
     const float* __restrict__ gpre, bf16* __restrict__ out, Dims D) {
     constexpr int NW = HB * 2;  // waves
@@ -746,7 +763,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         }
         __syncthreads();
         f32x16 phi[1][2][2];
-        np_map_mfma<1>(qf, wq + (size_t)g * (kD / 2) * kD, phi);
+        np_map_mfma<1>(qf, wqh + (size_t)g * (kD / 2) * kD, wql + (size_t)g * (kD / 2) * kD, phi);
         if (c >= 2) {
             // normaliser of the linear prefix (chunks <= c-2): phi_q . z
             float acc = 0.f;
@@ -1155,12 +1172,23 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
     return hipGetLastError();
 }
 
-hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const float* wphi_k,
+hipError_t launch_np_weight_split(const Dims& D, const float* wphi_q, const float* wphi_k, void* hl,
+                                  hipStream_t s) {
+    const int n = D.Hkv * (kD / 2) * kD;
+    hipLaunchKernelGGL(np_weight_split_kernel, dim3((2 * n + 255) / 256 < 256 ? (2 * n + 255) / 256 : 256),
+                       dim3(256), 0, s, wphi_q, wphi_k, reinterpret_cast<bf16*>(hl), n);
+    return hipGetLastError();
+}
+
+hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const void* wsplit,
                            const uint8_t* route, void* phik, float* lin, hipStream_t s) {
     if (D.n_full == 0) return hipSuccess;
+    const int n = D.Hkv * (kD / 2) * kD;
+    const bf16* wkh = reinterpret_cast<const bf16*>(wsplit) + 2 * (size_t)n;
+    const bf16* wkl = wkh + n;
     dim3 grid((D.n_full + D.ng - 1) / D.ng, D.Hkv, D.B);
     hipLaunchKernelGGL(la_state_kernel, grid, dim3(256), 0, s, reinterpret_cast<const bf16*>(k),
-                       reinterpret_cast<const bf16*>(v), wphi_k, route, reinterpret_cast<bf16*>(phik),
+                       reinterpret_cast<const bf16*>(v), wkh, wkl, route, reinterpret_cast<bf16*>(phik),
                        lin, D);
     return hipGetLastError();
 }
@@ -1176,15 +1204,18 @@ hipError_t launch_la_group_scan(const Dims& D, const float* lin, float* gpre, in
 }
 
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
-                              const float* wphi_q, const void* phik, const uint8_t* route,
+                              const void* wsplit, const void* phik, const uint8_t* route,
                               const void* ksel, const void* vsel, const float* lin,
                               const float* gpre, void* out, hipStream_t s) {
+    const int n = D.Hkv * (kD / 2) * kD;
+    const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
+    const bf16* wql = wqh + n;
     const int HB = D.G >= 4 ? 4 : D.G;  // query heads per block, two waves each
     const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
 #define STILL_MAIN(H)                                                                            \
     hipLaunchKernelGGL(hybrid_main_kernel<H>, dim3(nblk), dim3(128 * H), 0, s,                  \
                        reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),      \
-                       reinterpret_cast<const bf16*>(v), wphi_q,                                \
+                       reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
                        lin, gpre, reinterpret_cast<bf16*>(out), D)

@@ -106,7 +106,7 @@ struct MfmaBuffers {
     float *scores, *lin, *gpre;
     int32_t* sel;
     uint8_t* route;
-    void *ksel, *vsel, *phik;
+    void *ksel, *vsel, *phik, *wsplit;
 };
 
 static MfmaBuffers carve_mfma(const Dims& D, Carver& cv) {
@@ -122,6 +122,7 @@ static MfmaBuffers carve_mfma(const Dims& D, Carver& cv) {
     f.lin = cv.take<float>(BG * D.n_full * (size_t)(D.d + 1) * D.fd);
     const size_t ngroups = D.n_full == 0 ? 0 : (size_t)(D.n_full + D.ng - 1) / D.ng;
     f.gpre = cv.take<float>(BG * ngroups * (size_t)(D.d + 1) * D.fd);
+    f.wsplit = cv.take<uint16_t>((size_t)4 * D.Hkv * (D.fd / 2) * D.d);
     return f;
 }
 
@@ -200,7 +201,7 @@ struct Timeline {
     } while (0)
 
 static int fwd_launches(const Dims& D, const still_shape* sh, bool with_cache) {
-    if (use_mfma(D, sh)) return 4 + (with_cache ? 1 : 0);
+    if (use_mfma(D, sh)) return 5 + (with_cache ? 1 : 0);
     return 6 + (D.W > 0 ? 1 : 0) + (with_cache ? 1 : 0);
 }
 
@@ -234,14 +235,15 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
         MfmaBuffers f = carve_mfma(D, cv);
         float* scores = scores_opt ? scores_opt : f.scores;
         int32_t* sel = sel_idx_opt ? sel_idx_opt : f.sel;
+        STILL_LAUNCH(tl, s, "np_split", launch_np_weight_split(D, wq, wk, f.wsplit, s));
         STILL_LAUNCH(tl, s, "win_select",
                      launch_win_select(D, q, k, v, scores, sel, f.route, f.ksel, f.vsel, s));
-        STILL_LAUNCH(tl, s, "la_state", launch_la_state(D, k, v, wk, f.route, f.phik, f.lin, s));
+        STILL_LAUNCH(tl, s, "la_state", launch_la_state(D, k, v, f.wsplit, f.route, f.phik, f.lin, s));
         STILL_LAUNCH(tl, s, "la_scan",
                      launch_la_group_scan(D, f.lin, f.gpre, cap_chunk, cache ? cache->lin_S : nullptr,
                                           cache ? cache->lin_z : nullptr, s));
         STILL_LAUNCH(tl, s, "hybrid_main",
-                     launch_hybrid_main(D, q, k, v, wq, f.phik, f.route, f.ksel, f.vsel, f.lin, f.gpre,
+                     launch_hybrid_main(D, q, k, v, f.wsplit, f.phik, f.route, f.ksel, f.vsel, f.lin, f.gpre,
                                         out, s));
         if (cache)
             STILL_LAUNCH(tl, s, "handoff",
