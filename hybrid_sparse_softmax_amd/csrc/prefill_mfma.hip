@@ -42,7 +42,7 @@ constexpr int kD = 128;         // head_dim = NP-Map feature dim
 constexpr int kKS = kD + 8;     // LDS row stride (elements) of a K tile
 constexpr int kVS = kC + 8;     // LDS row stride (elements) of a transposed V tile
 constexpr int kFS = kC + 4;     // LDS row stride (floats) of transposed phi_k
-constexpr int kSS = kD + 4;     // LDS row stride (floats) of a staged linear state
+constexpr int kHS = kD + 8;     // LDS row stride (elements) of a staged state's bf16 parts
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;   // rescale only when the running max grows by more (log2 units)
 
@@ -111,7 +111,7 @@ __device__ __forceinline__ void load_vt_tile(const bf16* __restrict__ src, size_
 // acc_row(v, l/32), column = token.
 template <int NT>
 __device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const bf16* __restrict__ Ph,
-                                            const bf16* __restrict__ Pl, f32x16 (&phi)[NT][2][2]) {
+                                            const bf16* __restrict__ Pl, int ldp, f32x16 (&phi)[NT][2][2]) {
     const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
     f32x16 u[NT][2];
 #pragma unroll
@@ -123,8 +123,8 @@ __device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const bf1
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft) {
-            const bf16x8 hi = ld_bf8(Ph + (32 * ft + col) * kD + 16 * s + 8 * hf);
-            const bf16x8 lo = ld_bf8(Pl + (32 * ft + col) * kD + 16 * s + 8 * hf);
+            const bf16x8 hi = ld_bf8(Ph + (32 * ft + col) * ldp + 16 * s + 8 * hf);
+            const bf16x8 lo = ld_bf8(Pl + (32 * ft + col) * ldp + 16 * s + 8 * hf);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 u[tt][ft] = mfma32(hi, xb[tt][s], u[tt][ft]);
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
 #pragma unroll
             for (int s = 0; s < 8; ++s) xb[0][s] = ld_bf8(kr + 16 * s);
             f32x16 phi[1][2][2];
-            np_map_mfma<1>(xb, wkh + (size_t)g * (kD / 2) * kD, wkl + (size_t)g * (kD / 2) * kD, phi);
+            np_map_mfma<1>(xb, wkh + (size_t)g * (kD / 2) * kD, wkl + (size_t)g * (kD / 2) * kD, kD, phi);
             // phi_k row of the token, features in kperm order, for the read-out
             bf16* pr = phik + (bg * D.N + tok) * kD;
 #pragma unroll
@@ -675,7 +675,10 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // when the second half only trails the first by part of a tile.  The
     // linear prefix S^T rows (then z) follow; the epilogue reuses the front.
     constexpr int kNV = HB == 4 ? 2 : 3;
-    constexpr int kStsFloats = (kD + 1) * kSS > HB * 32 * kKS ? (kD + 1) * kSS : HB * 32 * kKS;
+    // staged linear prefix: S^T rows as bf16 high and low parts [kD][kHS]
+    // each, then z as kD floats; the epilogue reuses the same bytes
+    constexpr int kPrefixFloats = kD * kHS + kD;
+    constexpr int kStsFloats = kPrefixFloats > HB * 32 * kKS ? kPrefixFloats : HB * 32 * kKS;
     __shared__ __align__(16) bf16 smem[2 * kKTile + kNV * kVTile];
     __shared__ __align__(16) float sts[kStsFloats];
     auto kbuf = [&](int i) { return smem + (i & 1) * kKTile; };
@@ -719,13 +722,33 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     int voff[4];
     vt_lane_offsets(voff);
 
-    stage(first, true, true);
+    // The prologue's reads are requested together: the first tile; into the
+    // prefix area (free until the prefix itself is written there) the NP-Map
+    // projection parts and the phi_k rows of chunk c-1, in the K tile
+    // layout; the route flags of chunk c-1; Q.  The prefix rows follow once
+    // the projections and phi_k rows have been used.
+    // (written before the staging below is issued)
     if constexpr (HB == 4) {
         // the V buffer tile `first` does not use holds zeros: the first value
         // product reads it (with zero probabilities)
         bf16* vz = vbuf(first + 1);
         for (int x = tid; x < kVTile / 8; x += 64 * NW) st_bf8(vz + 8 * x, zero_bf8());
     }
+    stage(first, true, true);
+    bf16* pre = reinterpret_cast<bf16*>(sts);  // [W high | W low | phi_k rows], kKTile each
+    {
+        const bf16* wh = wqh + (size_t)g * (kD / 2) * kD;
+        const bf16* wl_ = wql + (size_t)g * (kD / 2) * kD;
+        for (int j = wave; j < kKPieces; j += NW) {
+            stage_k_piece(j, wh, kD, kD / 2, pre);
+            stage_k_piece(j, wl_, kD, kD / 2, pre + kKTile);
+        }
+        if (c >= 1) {
+            const bf16* pk = phik + (bg * D.N + (t0 - kC)) * kD;
+            for (int j = wave; j < kKPieces; j += NW) stage_k_piece(j, pk, kD, kC, pre + 2 * kKTile);
+        }
+    }
+    const uint8_t rt = c >= 1 ? route[bg * D.N + (t0 - kC) + lane] : 0;
     // Q operand: qf[s] holds query t0 + oq (tokens past N repeat N-1, never
     // written), dims 16 s + 8 hf .. +7
     bf16x8 qf[1][8];
@@ -735,7 +758,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[0][s] = ld_bf8(row + 16 * s);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): everything above
     __syncthreads();
 
     // running state of the lane's query: reference point m2 (log2 units,
@@ -748,35 +771,10 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     uint64_t selmask = 0;
 
     if (c >= 1) {
-        selmask = __ballot(route[bg * D.N + (t0 - kC) + lane] == kRouteSA);
-        if (c >= 2) {
-            // prefix of chunks <= c-2 (within-run part + earlier runs), staged
-            // in LDS once for all waves; rows padded to kSS floats
-            const int cp = c - 2;
-            const f32x4* st4 = reinterpret_cast<const f32x4*>(lin + (bg * D.n_full + cp) * (size_t)((kD + 1) * kD));
-            const f32x4* gs4 = reinterpret_cast<const f32x4*>(
-                gpre + (bg * ((D.n_full + D.ng - 1) / D.ng) + cp / D.ng) * (size_t)((kD + 1) * kD));
-            for (int x = tid; x < (kD + 1) * kD / 4; x += 64 * NW) {
-                const int row = (4 * x) / kD, c4 = (4 * x) % kD;
-                *reinterpret_cast<f32x4*>(&sts[row * kSS + c4]) = st4[x] + gs4[x];
-            }
-        }
-        __syncthreads();
+        selmask = __ballot(rt == kRouteSA);
         f32x16 phi[1][2][2];
-        np_map_mfma<1>(qf, wqh + (size_t)g * (kD / 2) * kD, wql + (size_t)g * (kD / 2) * kD, phi);
-        if (c >= 2) {
-            // normaliser of the linear prefix (chunks <= c-2): phi_q . z
-            float acc = 0.f;
-#pragma unroll
-            for (int sgn = 0; sgn < 2; ++sgn)
-#pragma unroll
-                for (int f2 = 0; f2 < 2; ++f2)
-#pragma unroll
-                    for (int vv = 0; vv < 16; ++vv)
-                        acc = fmaf(sts[kD * kSS + kperm(64 * sgn + 32 * f2 + acc_row(vv, hf))],
-                                   phi[0][sgn][f2][vv], acc);
-            ls = acc;
-        }
+        np_map_mfma<1>(qf, pre, pre + kKTile, kKS, phi);
+
         bf16x8 phb[2][2][2];  // [sgn][ft][s2]
 #pragma unroll
         for (int sgn = 0; sgn < 2; ++sgn)
@@ -792,7 +790,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 wl[kt] = zero16();
-                const bf16* pk = phik + (bg * D.N + (t0 - kC) + 32 * kt + col) * kD + 8 * hf;
+                const bf16* pk = pre + 2 * kKTile + (32 * kt + col) * kKS + 8 * hf;
 #pragma unroll
                 for (int sgn = 0; sgn < 2; ++sgn)
 #pragma unroll
@@ -820,6 +818,59 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             }
         }
         if (c >= 2) {
+            // prefix of chunks <= c-2 (within-run part + earlier runs), staged
+            // in LDS once for all waves (over the projections and phi_k rows,
+            // now read): S^T split into bf16 high and low parts (the MFMA
+            // operands), z in fp32
+            constexpr int kPrePieces = (kD + 1) * kD / 4, kPrePer = (kPrePieces + 64 * NW - 1) / (64 * NW);
+            f32x4 va[kPrePer], vg[kPrePer];
+            {
+                const int cp = c - 2;
+                const f32x4* st4 =
+                    reinterpret_cast<const f32x4*>(lin + (bg * D.n_full + cp) * (size_t)((kD + 1) * kD));
+                const f32x4* gs4 = reinterpret_cast<const f32x4*>(
+                    gpre + (bg * ((D.n_full + D.ng - 1) / D.ng) + cp / D.ng) * (size_t)((kD + 1) * kD));
+#pragma unroll
+                for (int t = 0; t < kPrePer; ++t) {
+                    const int x = min(tid + 64 * NW * t, kPrePieces - 1);
+                    va[t] = st4[x];
+                    vg[t] = gs4[x];
+                }
+            }
+            __syncthreads();
+            bf16* sth = reinterpret_cast<bf16*>(sts);
+#pragma unroll
+            for (int t = 0; t < kPrePer; ++t) {
+                const int x = tid + 64 * NW * t;
+                if (x >= kPrePieces) break;
+                const int row = (4 * x) / kD, c4 = (4 * x) % kD;
+                const f32x4 val = va[t] + vg[t];
+                if (row < kD) {
+                    bf16x4 hi, lo;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        hi[j] = (bf16)val[j];
+                        lo[j] = (bf16)(val[j] - (float)hi[j]);
+                    }
+                    *reinterpret_cast<bf16x4*>(sth + row * kHS + c4) = hi;
+                    *reinterpret_cast<bf16x4*>(sth + kD * kHS + row * kHS + c4) = lo;
+                } else {
+                    *reinterpret_cast<f32x4*>(&sts[kD * kHS + c4]) = val;
+                }
+            }
+            __syncthreads();
+            // normaliser of the linear prefix (chunks <= c-2): phi_q . z, with
+            // the same bf16 features as the numerator's products
+            float acc = 0.f;
+#pragma unroll
+            for (int sgn = 0; sgn < 2; ++sgn)
+#pragma unroll
+                for (int f2 = 0; f2 < 2; ++f2)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv)
+                        acc = fmaf(sts[kD * kHS + kperm(64 * sgn + 32 * f2 + acc_row(vv, hf))],
+                                   (float)phb[sgn][f2][vv >> 3][vv & 7], acc);
+            ls += acc;
             // numerator of the linear prefix: O^T += S^T phi_q
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
@@ -829,10 +880,10 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     for (int f2 = 0; f2 < 2; ++f2)
 #pragma unroll
                         for (int s2 = 0; s2 < 2; ++s2) {
-                            bf16x8 hi, lo;
-                            ld_split8(&sts[(32 * dt + col) * kSS + 64 * sgn + 32 * f2 + 16 * s2 + 8 * hf], hi, lo);
-                            o[dt] = mfma32(hi, phb[sgn][f2][s2], o[dt]);
-                            o[dt] = mfma32(lo, phb[sgn][f2][s2], o[dt]);
+                            const bf16* sr = reinterpret_cast<const bf16*>(sts) + (32 * dt + col) * kHS +
+                                             64 * sgn + 32 * f2 + 16 * s2 + 8 * hf;
+                            o[dt] = mfma32(ld_bf8(sr), phb[sgn][f2][s2], o[dt]);
+                            o[dt] = mfma32(ld_bf8(sr + kD * kHS), phb[sgn][f2][s2], o[dt]);
                         }
         }
     }
