@@ -184,6 +184,84 @@ __device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const bf1
     }
 }
 
+// Tile staging (window scores and output kernels): global memory straight into LDS
+// (global_load_lds, 16 bytes per lane; lane l of one instruction lands at
+// byte 16 l of that instruction's 1 KB).  Rows at or beyond a tile's valid
+// count nv (>= 1) repeat row nv-1, so every address stays in bounds; those
+// keys are masked out of every sum.
+//   K tile: 64 rows of kKS elements (17 slots of 16 bytes, the last one
+//     padding); 17 instructions cover its 1088 slots, padding slots load a
+//     slot of the same row.  The logits read a K row per lane at a fixed slot:
+//     the 17-slot stride spreads 16 rows over all banks.
+//   V tile: 64 unpadded rows of 128 elements; slot x of row r is stored at
+//     x ^ vswz(r); 16 instructions.  The value product reads it transposed.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kKTile = kC * kKS;  // elements of a staged K tile
+constexpr int kVTile = kC * kD;   // elements of a staged V tile
+constexpr int kKPieces = kKTile / 512;  // 17 staging instructions
+constexpr int kVPieces = kVTile / 512;  // 16
+
+__device__ __forceinline__ int vswz(int r) { return 4 * (r & 3) + 2 * ((r >> 2) & 1); }
+
+__device__ __forceinline__ void dma16(const bf16* g, bf16* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// The same load written out, for the lock-step loop: the compiler does not
+// track it, so it places no wait for it before later LDS reads of other
+// buffers; its users wait for it (vmcnt) explicitly.  M0 holds the LDS
+// destination (wave-uniform); one wait state separates the M0 write from the
+// load that reads it.
+__device__ __forceinline__ void dma16_untracked(const bf16* g, unsigned lds_byte) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(g), "s"(m0)
+                     : "memory", "m0");
+}
+
+// staging instruction j (0..16) of a K tile
+__device__ __forceinline__ void stage_k_piece(int j, const bf16* __restrict__ src, size_t ld, int nv,
+                                              bf16* __restrict__ dst) {
+    const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
+    dma16(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 512 * j);
+}
+
+// The same, issued only when en != 0 (wave-uniform); the test and skip sit
+// inside the asm statement, so the surrounding code stays one basic block.
+__device__ __forceinline__ void dma16_untracked_if(const bf16* g, unsigned lds_byte, int en) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+    const int e = __builtin_amdgcn_readfirstlane(en);
+    __asm__ volatile("s_cmp_eq_u32 %2, 0\n\ts_cbranch_scc1 1f\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %0, off\n1:"
+                     :
+                     : "v"(g), "s"(m0), "s"(e)
+                     : "memory", "m0", "scc");
+}
+
+// staging instruction j (0..16) of a K tile, untracked load; dst = LDS
+// byte address of the tile; ld (elements) and row offsets fit 24 bits
+__device__ __forceinline__ void stage_k_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
+                                                unsigned dst) {
+    const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
+    dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
+}
+
+// staging instruction j of a K tile when j < 17 (no branch around it)
+__device__ __forceinline__ void stage_k_piece_if(int j, const bf16* __restrict__ src, int ld, int nv,
+                                                 unsigned dst) {
+    const int jj = min(j, kKPieces - 1);
+    const int p = 64 * jj + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
+    dma16_untracked_if(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * jj, j < kKPieces);
+}
+
+// staging instruction j (0..15) of a V tile, untracked load
+__device__ __forceinline__ void stage_v_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
+                                                unsigned dst) {
+    const int l = threadIdx.x & 63, row = 4 * j + (l >> 4), slot = (l & 15) ^ vswz(row);
+    dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
+}
+
 // NP-Map projections of queries and keys as bf16 high and low parts (one
 // pass over wq then wk, n floats each): hl = [wq high, wq low, wk high, wk low]
 __global__ __launch_bounds__(256) void np_weight_split_kernel(const float* __restrict__ wq,
@@ -214,6 +292,21 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     __shared__ float key_s[kC];
     __shared__ int flag_s[kC];
     __shared__ int src_s[kC];
+    // K rows of chunks c-1 and c, staged once for all heads (K tile layout;
+    // rows before token 0 are never loaded and only ever masked)
+    __shared__ __align__(16) bf16 kwin[2 * kKTile];
+    {
+        const size_t ldkv = (size_t)D.Hkv * kD;
+        for (int i = 0; i < 2; ++i) {
+            const int tc = c - 1 + i;
+            if (tc < 0) continue;
+            const bf16* src = k + (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
+            for (int j = wave; j < kKPieces; j += NW) stage_k_piece(j, src, ldkv, min(kC, D.N - tc * kC), kwin + i * kKTile);
+        }
+    }
+    const float tl2 = D.tau * kLog2e;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
 
     for (int hh = wave; hh < D.G; hh += NW) {
         const int h = g * D.G + hh;
@@ -236,9 +329,8 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
             for (int s = 0; s < 8; ++s) {
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
-                    const int key = max(0, t0 - kC + 32 * (qt + j) + col);
-                    const bf16x8 a = ld_bf8(k + (((size_t)b * D.N + min(key, D.N - 1)) * D.Hkv + g) * kD +
-                                            16 * s + 8 * hf);
+                    const int kt = qt + j;
+                    const bf16x8 a = ld_bf8(kwin + (kt >> 1) * kKTile + (32 * (kt & 1) + col) * kKS + 16 * s + 8 * hf);
                     sc[j] = mfma32(a, qf[s], sc[j]);
                 }
             }
@@ -250,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 for (int vv = 0; vv < 16; ++vv) {
                     const int kk = 32 * (qt + j) + acc_row(vv, hf);
                     const bool ok = kk >= qo + 1 && kk <= qo + kC && t0 - kC + kk >= 0;
-                    const float x = ok ? D.tau * sc[j][vv] : kNegInf;
+                    const float x = ok ? tl2 * sc[j][vv] : kNegInf;  // log2 units
                     sc[j][vv] = x;
                     mx = fmaxf(mx, x);
                 }
@@ -262,7 +354,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 for (int vv = 0; vv < 16; ++vv) {
                     const int kk = 32 * (qt + j) + acc_row(vv, hf);
                     const float x = sc[j][vv];
-                    const float e = x == kNegInf ? 0.f : expf(x - mx);
+                    const float e = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x - mx);
                     sc[j][vv] = e;
                     sa += e;
                     if (kk == qo + kC) et += e;
@@ -336,7 +428,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     for (int x = tid; x < D.lam * 16; x += NW * 64) {
         const int p = x >> 4, piece = x & 15;
         const size_t src = (((size_t)b * D.N + t0 + src_s[p]) * D.Hkv + g) * kD + 8 * piece;
-        st_bf8(ksel + (base + p) * kD + 8 * piece, ld_bf8(k + src));
+        st_bf8(ksel + (base + p) * kD + 8 * piece, ld_bf8(kwin + kKTile + src_s[p] * kKS + 8 * piece));
         st_bf8(vsel + (base + p) * kD + 8 * piece, ld_bf8(v + src));
     }
 }
@@ -459,84 +551,6 @@ __global__ __launch_bounds__(256) void la_group_scan_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 // hybrid output
 // ---------------------------------------------------------------------------
-// Tile staging for the output kernel: global memory straight into LDS
-// (global_load_lds, 16 bytes per lane; lane l of one instruction lands at
-// byte 16 l of that instruction's 1 KB).  Rows at or beyond a tile's valid
-// count nv (>= 1) repeat row nv-1, so every address stays in bounds; those
-// keys are masked out of every sum.
-//   K tile: 64 rows of kKS elements (17 slots of 16 bytes, the last one
-//     padding); 17 instructions cover its 1088 slots, padding slots load a
-//     slot of the same row.  The logits read a K row per lane at a fixed slot:
-//     the 17-slot stride spreads 16 rows over all banks.
-//   V tile: 64 unpadded rows of 128 elements; slot x of row r is stored at
-//     x ^ vswz(r); 16 instructions.  The value product reads it transposed.
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kKTile = kC * kKS;  // elements of a staged K tile
-constexpr int kVTile = kC * kD;   // elements of a staged V tile
-constexpr int kKPieces = kKTile / 512;  // 17 staging instructions
-constexpr int kVPieces = kVTile / 512;  // 16
-
-__device__ __forceinline__ int vswz(int r) { return 4 * (r & 3) + 2 * ((r >> 2) & 1); }
-
-__device__ __forceinline__ void dma16(const bf16* g, bf16* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
-}
-
-// The same load written out, for the lock-step loop: the compiler does not
-// track it, so it places no wait for it before later LDS reads of other
-// buffers; its users wait for it (vmcnt) explicitly.  M0 holds the LDS
-// destination (wave-uniform); one wait state separates the M0 write from the
-// load that reads it.
-__device__ __forceinline__ void dma16_untracked(const bf16* g, unsigned lds_byte) {
-    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
-    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(g), "s"(m0)
-                     : "memory", "m0");
-}
-
-// staging instruction j (0..16) of a K tile
-__device__ __forceinline__ void stage_k_piece(int j, const bf16* __restrict__ src, size_t ld, int nv,
-                                              bf16* __restrict__ dst) {
-    const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
-    dma16(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 512 * j);
-}
-
-// The same, issued only when en != 0 (wave-uniform); the test and skip sit
-// inside the asm statement, so the surrounding code stays one basic block.
-__device__ __forceinline__ void dma16_untracked_if(const bf16* g, unsigned lds_byte, int en) {
-    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
-    const int e = __builtin_amdgcn_readfirstlane(en);
-    __asm__ volatile("s_cmp_eq_u32 %2, 0\n\ts_cbranch_scc1 1f\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                     "global_load_lds_dwordx4 %0, off\n1:"
-                     :
-                     : "v"(g), "s"(m0), "s"(e)
-                     : "memory", "m0", "scc");
-}
-
-// staging instruction j (0..16) of a K tile, untracked load; dst = LDS
-// byte address of the tile; ld (elements) and row offsets fit 24 bits
-__device__ __forceinline__ void stage_k_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
-                                                unsigned dst) {
-    const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
-    dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
-}
-
-// staging instruction j of a K tile when j < 17 (no branch around it)
-__device__ __forceinline__ void stage_k_piece_if(int j, const bf16* __restrict__ src, int ld, int nv,
-                                                 unsigned dst) {
-    const int jj = min(j, kKPieces - 1);
-    const int p = 64 * jj + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
-    dma16_untracked_if(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * jj, j < kKPieces);
-}
-
-// staging instruction j (0..15) of a V tile, untracked load
-__device__ __forceinline__ void stage_v_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
-                                                unsigned dst) {
-    const int l = threadIdx.x & 63, row = 4 * j + (l >> 4), slot = (l & 15) ^ vswz(row);
-    dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
-}
-
 // one staging wave's instructions w, w + NS, ... of a K or V tile
 template <int NS>
 __device__ __forceinline__ void stage_k_share_u(const bf16* __restrict__ src, int ld, int nv, unsigned dst,
