@@ -353,7 +353,7 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
         if (lane < n_win && e > 0.f) {
             const float a = e / sa;
             if (lane == n_win - 1) term = a * log1pf(a / D.eps);
-            else term = -a * log1p_fast(__fdividef((et / so) * e, e + D.eps * sa));
+            else term = -a * log1p_fast(fast_div((et / so) * e, e + D.eps * sa));
         }
         term = wave_sum(term);
         if (lane == 0) hsc[hh] = term;

@@ -377,7 +377,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 for (int vv = 0; vv < 16; ++vv) {
                     const int kk = 32 * (qt + j) + acc_row(vv, hf);
                     const float e = sc[j][vv];
-                    const float tj = -(e * isa) * log1p_fast(__fdividef(r * e, e + esa));
+                    const float tj = -(e * isa) * log1p_fast(fast_div(r * e, e + esa));
                     term += (e > 0.f && kk != qo + kC) ? tj : 0.f;
                 }
             term += xor32(term);
