@@ -89,13 +89,19 @@ __device__ __forceinline__ bf16x8 pack_acc(const f32x16& x, int s2) {
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, kWave); }
 
+// IEEE 754-2019 maximum / minimum (a NaN operand gives NaN).  On gfx950 these
+// become v_maximum3_f32 / v_minimum3_f32 with no canonicalising of the
+// operands, which fmaxf needs after matrix-core results.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
 // max of x over lanes l and l ^ 32: the lane-half swap hands each lane both
 // halves' values (in one order or the other), so the max of the two results
 // is the same in every lane
 __device__ __forceinline__ float half_pair_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
                                                     __builtin_bit_cast(unsigned, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    return vmax(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
 }
 
 }  // namespace still

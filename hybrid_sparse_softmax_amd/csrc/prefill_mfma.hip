@@ -148,13 +148,13 @@ __device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const bf1
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 nu = fmaf(u[tt][ft][v], u[tt][ft][v], nu);
-                umax = fmaxf(umax, u[tt][ft][v]);
-                umin = fminf(umin, u[tt][ft][v]);
+                umax = vmax(umax, u[tt][ft][v]);
+                umin = vmin(umin, u[tt][ft][v]);
             }
         nx += xor32(nx);
         nu += xor32(nu);
-        umax = fmaxf(umax, xor32(umax));
-        umin = fminf(umin, xor32(umin));
+        umax = vmax(umax, xor32(umax));
+        umin = vmin(umin, xor32(umin));
         // z = sc u with sc >= 0, so max z = sc umax and max(-z) = -sc umin
         const float scl = (nu > 0.f ? sqrtf(nx) / sqrtf(nu) : 0.f) * kLog2e;
         const float mp = scl * umax, mn = -scl * umin;
@@ -344,9 +344,9 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                     const bool ok = kk >= qo + 1 && kk <= qo + kC && t0 - kC + kk >= 0;
                     const float x = ok ? tl2 * sc[j][vv] : kNegInf;  // log2 units
                     sc[j][vv] = x;
-                    mx = fmaxf(mx, x);
+                    mx = vmax(mx, x);
                 }
-            mx = fmaxf(mx, xor32(mx));
+            mx = vmax(mx, xor32(mx));
             float sa = 0.f, so = 0.f, et = 0.f;
 #pragma unroll
             for (int j = 0; j < 3; ++j)
@@ -957,7 +957,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int vv = 0; vv < 16; ++vv) tmax = fmaxf(tmax, sc[kt][vv]);
+            for (int vv = 0; vv < 16; ++vv) tmax = vmax(tmax, sc[kt][vv]);
         const float tm2 = half_pair_max(tmax) * cl2;
         if (__any(tm2 > m2 + kLazy)) {
             // a rare path: keep the compiler from speculating it into every tile
@@ -1015,16 +1015,16 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         };
         // maximum of a tile's logits over the lane's query (both lane halves), log2 units
         auto tile_max2 = [&](const f32x16 (&x)[2]) {
-            float a = fmaxf(x[0][0], x[0][1]), b2 = fmaxf(x[0][8], x[0][9]);
-            float c2 = fmaxf(x[1][0], x[1][1]), d2 = fmaxf(x[1][8], x[1][9]);
+            float a = vmax(x[0][0], x[0][1]), b2 = vmax(x[0][8], x[0][9]);
+            float c2 = vmax(x[1][0], x[1][1]), d2 = vmax(x[1][8], x[1][9]);
 #pragma unroll
             for (int vv = 2; vv < 8; vv += 2) {
-                a = fmaxf(a, fmaxf(x[0][vv], x[0][vv + 1]));
-                b2 = fmaxf(b2, fmaxf(x[0][vv + 8], x[0][vv + 9]));
-                c2 = fmaxf(c2, fmaxf(x[1][vv], x[1][vv + 1]));
-                d2 = fmaxf(d2, fmaxf(x[1][vv + 8], x[1][vv + 9]));
+                a = vmax(a, vmax(x[0][vv], x[0][vv + 1]));
+                b2 = vmax(b2, vmax(x[0][vv + 8], x[0][vv + 9]));
+                c2 = vmax(c2, vmax(x[1][vv], x[1][vv + 1]));
+                d2 = vmax(d2, vmax(x[1][vv + 8], x[1][vv + 9]));
             }
-            return half_pair_max(fmaxf(fmaxf(a, b2), fmaxf(c2, d2))) * cl2;
+            return half_pair_max(vmax(vmax(a, b2), vmax(c2, d2))) * cl2;
         };
         bf16x8 pb[4];
 #pragma unroll
@@ -1112,12 +1112,20 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     o[(x + 1) & 3] = mfma32(a1[st], pb[(x + 1) >> 2], o[(x + 1) & 3]);
                 }
 #pragma unroll
-                for (int e = 2 * st; e < 2 * st + 2; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], cl2, nm));
-                    sc[e >> 4][e & 15] = p;
-                    ls += p;
+                for (int e = 2 * st; e < 2 * st + 2; ++e)
+                    sc[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], cl2, nm));
+                if ((st & 3) == 3) {
+                    // the normaliser sums the same bf16 probabilities the value
+                    // product uses (two per dot instruction)
+                    const bf16x8 pk = pack_acc(sc[st >> 3], (st >> 2) & 1);
+                    pn[st >> 2] = pk;
+                    const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bf16x2 pr = {pk[2 * j], pk[2 * j + 1]};
+                        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
+                    }
                 }
-                if ((st & 3) == 3) pn[st >> 2] = pack_acc(sc[st >> 3], (st >> 2) & 1);
                 if (st == 1 || st == 4 || st == 7)
                     stage_k_piece_if(wave + 2 * HB * (st / 3), ksrc, kld, knv, kdst);
                 if (st == 9 || st == 12)
@@ -1126,17 +1134,17 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
                     for (int j = 0; j < 3; ++j) {
                         const int e = 6 * (st - 10) + j;  // 0..35, elements 0..31
-                        if (e < 16) ta = fmaxf(ta, fmaxf(sn[0][e], sn[1][e]));
+                        if (e < 16) ta = vmax(ta, vmax(sn[0][e], sn[1][e]));
                     }
 #pragma unroll
                     for (int j = 3; j < 6; ++j) {
                         const int e = 6 * (st - 10) + j;
-                        if (e < 16) tb = fmaxf(tb, fmaxf(sn[0][e], sn[1][e]));
+                        if (e < 16) tb = vmax(tb, vmax(sn[0][e], sn[1][e]));
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            tm2 = half_pair_max(fmaxf(ta, tb)) * cl2;
+            tm2 = half_pair_max(vmax(ta, tb)) * cl2;
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged tiles landed
             lds_barrier();
         };
