@@ -1112,8 +1112,13 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     o[(x + 1) & 3] = mfma32(a1[st], pb[(x + 1) >> 2], o[(x + 1) & 3]);
                 }
 #pragma unroll
-                for (int e = 2 * st; e < 2 * st + 2; ++e)
+                for (int e = 2 * st; e < 2 * st + 2; ++e) {
                     sc[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], cl2, nm));
+                    // the empty asm needs the result here, which keeps the exp in
+                    // this step (otherwise the exps of the first of two unrolled
+                    // iterations sink below its products, into one block of their own)
+                    __asm__ volatile("" ::"v"(sc[e >> 4][e & 15]));
+                }
                 if ((st & 3) == 3) {
                     // the normaliser sums the same bf16 probabilities the value
                     // product uses (two per dot instruction)
