@@ -255,6 +255,40 @@ __device__ __forceinline__ void stage_k_piece_if(int j, const bf16* __restrict__
     dma16_untracked_if(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * jj, j < kKPieces);
 }
 
+// Untracked load in the scalar-base form: the address is base (wave-uniform,
+// 64-bit) plus the lane's unsigned 32-bit byte offset, so no per-lane 64-bit
+// arithmetic is needed.  Issued only when en != 0 (wave-uniform), the test
+// and skip inside the asm statement as above.
+__device__ __forceinline__ void dma16_sbase_if(const bf16* base, unsigned off, unsigned lds_byte, int en) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
+    const int e = __builtin_amdgcn_readfirstlane(en);
+    __asm__ volatile("s_cmp_eq_u32 %3, 0\n\ts_cbranch_scc1 1f\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %0, %1\n1:"
+                     :
+                     : "v"(off), "s"(base), "s"(m0), "s"(e)
+                     : "memory", "m0", "scc");
+}
+
+// Lane constants of one staging instruction j of a K or V tile: the row the
+// lane's 16 bytes come from and the byte offset of its slot within the row.
+struct StagePiece {
+    unsigned row, slot16;
+};
+__device__ __forceinline__ StagePiece k_piece_lane(int j) {
+    const int p = 64 * j + (threadIdx.x & 63), row = p / 17;
+    return {(unsigned)row, 16u * (unsigned)min(p - 17 * row, 15)};
+}
+__device__ __forceinline__ StagePiece v_piece_lane(int j) {
+    const int l = threadIdx.x & 63, row = 4 * j + (l >> 4);
+    return {(unsigned)row, 16u * (unsigned)((l & 15) ^ vswz(row))};
+}
+// one staging instruction of a tile whose rows start at base, ld2 bytes
+// apart, nvm1 = valid rows - 1 (later rows repeat the last valid one)
+__device__ __forceinline__ void stage_piece_sb(const StagePiece& pc, const bf16* base, unsigned ld2,
+                                               unsigned nvm1, unsigned lds_byte, int en) {
+    dma16_sbase_if(base, __umul24(min(pc.row, nvm1), ld2) + pc.slot16, lds_byte, en);
+}
+
 // staging instruction j (0..15) of a V tile, untracked load
 __device__ __forceinline__ void stage_v_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
                                                 unsigned dst) {
@@ -627,6 +661,18 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
+// Workgroup barrier taken only when en != 0 (wave-uniform), after this wave's
+// staging loads have landed (vmcnt); its LDS reads are not waited for.  The
+// test and skip sit inside the asm statement, so the caller's code stays one
+// basic block and its scheduling barriers keep their hold.
+__device__ __forceinline__ void staged_barrier_if(int en) {
+    const int e = __builtin_amdgcn_readfirstlane(en);
+    __asm__ volatile("s_cmp_eq_u32 %0, 0\n\ts_cbranch_scc1 1f\n\ts_waitcnt vmcnt(0)\n\ts_barrier\n1:"
+                     :
+                     : "s"(e)
+                     : "memory", "scc");
+}
+
 // Matrix phase of the lock-step output loop: the value product of the
 // previous tile (V in vread, operand pb) and the logits of the current one
 // (K in kread) on the matrix cores.
@@ -684,11 +730,11 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const size_t bg = (size_t)b * D.Hkv + g;
     const float cl2 = D.tau * kLog2e;
 
-    // K of tile i in kbuf(i) (two buffers), V of tile i in vbuf(i): two
-    // buffers when the two query halves alternate in lock step (HB = 4), three
-    // when the second half only trails the first by part of a tile.  The
-    // linear prefix S^T rows (then z) follow; the epilogue reuses the front.
-    constexpr int kNV = HB == 4 ? 2 : 3;
+    // K of tile i in kbuf(i) (two buffers), V of tile i in vbuf(i) (three: the
+    // second query half still reads the previous tile's values after the
+    // barrier that lets the first half stage the next ones).  The linear
+    // prefix S^T rows (then z) follow; the epilogue reuses the front.
+    constexpr int kNV = 3;
     // staged linear prefix: S^T rows as bf16 high and low parts [kD][kHS]
     // each, then z as kD floats; the epilogue reuses the same bytes
     constexpr int kPrefixFloats = kD * kHS + kD;
@@ -696,7 +742,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     __shared__ __align__(16) bf16 smem[2 * kKTile + kNV * kVTile];
     __shared__ __align__(16) float sts[kStsFloats];
     auto kbuf = [&](int i) { return smem + (i & 1) * kKTile; };
-    auto vbuf = [&](int i) { return smem + 2 * kKTile + (kNV == 2 ? (i & 1) : i % 3) * kVTile; };
+    auto vbuf = [&](int i) { return smem + 2 * kKTile + ((i + 3) % 3) * kVTile; };  // i >= -1
 
     // tiles: 0 = chunk c-1 (c >= 1), 1 = chunk c, 2.. = compact selected rows
     const int nrows = c >= 2 ? (c - 1) * D.lam : 0;
@@ -743,9 +789,9 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // the projections and phi_k rows have been used.
     // (written before the staging below is issued)
     if constexpr (HB == 4) {
-        // the V buffer tile `first` does not use holds zeros: the first value
-        // product reads it (with zero probabilities)
-        bf16* vz = vbuf(first + 1);
+        // the V buffer of tile first-1 holds zeros: the first value product
+        // reads it (with zero probabilities)
+        bf16* vz = vbuf(first - 1);
         for (int x = tid; x < kVTile / 8; x += 64 * NW) st_bf8(vz + 8 * x, zero_bf8());
     }
     stage(first, true, true);
@@ -1029,6 +1075,13 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         bf16x8 pb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) pb[ks] = zero_bf8();
+        // lane constants of this wave's staging instructions (pieces wave,
+        // wave + 8 and, for K, wave + 16 when it exists)
+        StagePiece kpc[3], vpc[2];
+#pragma unroll
+        for (int x = 0; x < 3; ++x) kpc[x] = k_piece_lane(min(wave + 2 * HB * x, kKPieces - 1));
+#pragma unroll
+        for (int x = 0; x < 2; ++x) vpc[x] = v_piece_lane(wave + 2 * HB * x);
         // K of first+1 (V of first and K of first are in place; a tile index
         // past the last one stages the last one again, unused)
         {
@@ -1044,6 +1097,12 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         // pb; leaves tile s+1's logits in sn and tile s's probabilities in pn.
         // Two calls per loop turn with the roles swapped keep every value in
         // place (no copies).
+        // The first query half, which the SIMD's issue order favours, reaches
+        // the iteration's barrier at the end of its stream; the second half
+        // (late != 0) reaches it after step 11 and runs its last value
+        // products (of tile s-1, whose V buffer stays intact until iteration
+        // s+2) beyond it, so the two halves arrive together.  Both issue their
+        // staging in steps 1-5, well before either barrier point.
         auto iteration = [&](int s, f32x16 (&sc)[2], bf16x8 (&pb)[4], f32x16 (&sn)[2], bf16x8 (&pn)[4])
                              __attribute__((always_inline)) {
             // softmax of tile s up to its exps: masking (edge tiles, with their
@@ -1072,8 +1131,12 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             int kld, knv, vld, vnv;
             const bf16* ksrc = rows_of(min(s + 2, ntile - 1), true, kld, knv);
             const bf16* vsrc = rows_of(s, false, vld, vnv);
+            const unsigned kld2 = 2u * kld, knm1 = knv - 1, vld2 = 2u * vld, vnm1 = vnv - 1;
             const unsigned kdst = lds0 + 2u * (s & 1) * kKTile;
-            const unsigned vdst = lds0 + 2u * (2 * kKTile + (s & 1) * kVTile);
+            // V buffers of tiles s (staged now) and s-1 (read now), as scalars
+            const int vcur = __builtin_amdgcn_readfirstlane(s % 3);
+            const int vprv = __builtin_amdgcn_readfirstlane(vcur == 0 ? 2 : vcur - 1);
+            const unsigned vdst = lds0 + 2u * (2 * kKTile + vcur * kVTile);
             // One stream of 16 steps pinned by scheduling barriers.  Steps 0-7
             // take the logits of tile s+1 (two products each: keys 0-31 and
             // 32-63), steps 8-15 the value product of tile s-1 (two each);
@@ -1081,7 +1144,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             // the operand reads of the step two ahead; some steps issue a
             // staging instruction; steps 10-15 take the maximum of the
             // finished logits.
-            const bf16* vt = vbuf(s > first ? s - 1 : s + 1);
+            const bf16* vt = smem + 2 * kKTile + vprv * kVTile;
             const bf16* kt = kbuf(s + 1) + col * kKS + 8 * hf;
             sn[0] = zero16();
             sn[1] = zero16();
@@ -1130,11 +1193,18 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                         const bf16x2 pr = {pk[2 * j], pk[2 * j + 1]};
                         ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
                     }
+                    // keeps the pack and the sums in this step (as for the exps)
+                    __asm__ volatile("" ::"v"(pk), "v"(ls));
                 }
-                if (st == 1 || st == 4 || st == 7)
-                    stage_k_piece_if(wave + 2 * HB * (st / 3), ksrc, kld, knv, kdst);
-                if (st == 9 || st == 12)
-                    stage_v_piece_u(wave + 2 * HB * ((st - 9) / 3), vsrc, vld, vnv, vdst);
+                if (st == 1 || st == 3 || st == 5) {
+                    const int x = st / 2;  // the third piece (16) is wave 0's alone
+                    stage_piece_sb(kpc[x], ksrc, kld2, knm1, kdst + 1024u * (wave + 2 * HB * x),
+                                   x < 2 || wave + 2 * HB * x < kKPieces);
+                }
+                if (st == 2 || st == 4) {
+                    const int x = st / 2 - 1;
+                    stage_piece_sb(vpc[x], vsrc, vld2, vnm1, vdst + 1024u * (wave + 2 * HB * x), 1);
+                }
                 if (st >= 10) {
 #pragma unroll
                     for (int j = 0; j < 3; ++j) {
@@ -1147,11 +1217,11 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                         if (e < 16) tb = vmax(tb, vmax(sn[0][e], sn[1][e]));
                     }
                 }
+                if (st == 11) staged_barrier_if(qh);
                 __builtin_amdgcn_sched_barrier(0);
             }
             tm2 = half_pair_max(vmax(ta, tb)) * cl2;
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged tiles landed
-            lds_barrier();
+            staged_barrier_if(qh ^ 1);
         };
         f32x16 sc2[2];
         bf16x8 pb2[4];
