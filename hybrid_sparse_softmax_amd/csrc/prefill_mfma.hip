@@ -1135,7 +1135,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             const unsigned kdst = lds0 + 2u * (s & 1) * kKTile;
             // V buffers of tiles s (staged now) and s-1 (read now), as scalars
             const int vcur = __builtin_amdgcn_readfirstlane(s % 3);
-            const int vprv = __builtin_amdgcn_readfirstlane(vcur == 0 ? 2 : vcur - 1);
+            const int vprv = __builtin_amdgcn_readfirstlane((s + 2) % 3);
             const unsigned vdst = lds0 + 2u * (2 * kKTile + vcur * kVTile);
             // One stream of 16 steps pinned by scheduling barriers.  Steps 0-7
             // take the logits of tile s+1 (two products each: keys 0-31 and
@@ -1209,12 +1209,20 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
                     for (int j = 0; j < 3; ++j) {
                         const int e = 6 * (st - 10) + j;  // 0..35, elements 0..31
-                        if (e < 16) ta = vmax(ta, vmax(sn[0][e], sn[1][e]));
+                        if (e < 16) {
+                            // one three-way maximum per pair: the empty asm keeps
+                            // the compiler from re-associating the chain
+                            ta = vmax(ta, vmax(sn[0][e], sn[1][e]));
+                            __asm__ volatile("" : "+v"(ta));
+                        }
                     }
 #pragma unroll
                     for (int j = 3; j < 6; ++j) {
                         const int e = 6 * (st - 10) + j;
-                        if (e < 16) tb = vmax(tb, vmax(sn[0][e], sn[1][e]));
+                        if (e < 16) {
+                            tb = vmax(tb, vmax(sn[0][e], sn[1][e]));
+                            __asm__ volatile("" : "+v"(tb));
+                        }
                     }
                 }
                 if (st == 11) staged_barrier_if(qh);
