@@ -735,10 +735,15 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // barrier that lets the first half stage the next ones).  The linear
     // prefix S^T rows (then z) follow; the epilogue reuses the front.
     constexpr int kNV = 3;
-    // staged linear prefix: S^T rows as bf16 high and low parts [kD][kHS]
-    // each, then z as kD floats; the epilogue reuses the same bytes
-    constexpr int kPrefixFloats = kD * kHS + kD;
-    constexpr int kStsFloats = kPrefixFloats > HB * 32 * kKS ? kPrefixFloats : HB * 32 * kKS;
+    // staged linear prefix: S^T rows in bf16 [kD][kHS], then z as kD floats
+    // (from float kZOff); the epilogue reuses the same bytes
+    constexpr int kZOff = kD * kHS / 2;
+    constexpr int kPrefixFloats = kZOff + kD;
+    // the same bytes first hold the prologue's projection parts and phi_k rows
+    // (three K-tile layouts) and last the output tiles (HB * 32 * kKS floats)
+    constexpr int kPreFloats = 3 * kKTile / 2;
+    constexpr int kStsA = kPrefixFloats > kPreFloats ? kPrefixFloats : kPreFloats;
+    constexpr int kStsFloats = kStsA > HB * 32 * kKS ? kStsA : HB * 32 * kKS;
     __shared__ __align__(16) bf16 smem[2 * kKTile + kNV * kVTile];
     __shared__ __align__(16) float sts[kStsFloats];
     auto kbuf = [&](int i) { return smem + (i & 1) * kKTile; };
@@ -880,8 +885,8 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         if (c >= 2) {
             // prefix of chunks <= c-2 (within-run part + earlier runs), staged
             // in LDS once for all waves (over the projections and phi_k rows,
-            // now read): S^T split into bf16 high and low parts (the MFMA
-            // operands), z in fp32
+            // now read): S^T rounded to bf16 (the MFMA operand, the precision
+            // of every other product on this path), z in fp32
             constexpr int kPrePieces = (kD + 1) * kD / 4, kPrePer = (kPrePieces + 64 * NW - 1) / (64 * NW);
             f32x4 va[kPrePer], vg[kPrePer];
             {
@@ -906,16 +911,12 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 const int row = (4 * x) / kD, c4 = (4 * x) % kD;
                 const f32x4 val = va[t] + vg[t];
                 if (row < kD) {
-                    bf16x4 hi, lo;
+                    bf16x4 hi;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        hi[j] = (bf16)val[j];
-                        lo[j] = (bf16)(val[j] - (float)hi[j]);
-                    }
+                    for (int j = 0; j < 4; ++j) hi[j] = (bf16)val[j];
                     *reinterpret_cast<bf16x4*>(sth + row * kHS + c4) = hi;
-                    *reinterpret_cast<bf16x4*>(sth + kD * kHS + row * kHS + c4) = lo;
                 } else {
-                    *reinterpret_cast<f32x4*>(&sts[kD * kHS + c4]) = val;
+                    *reinterpret_cast<f32x4*>(&sts[kZOff + c4]) = val;
                 }
             }
             __syncthreads();
@@ -928,7 +929,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 for (int f2 = 0; f2 < 2; ++f2)
 #pragma unroll
                     for (int vv = 0; vv < 16; ++vv)
-                        acc = fmaf(sts[kD * kHS + kperm(64 * sgn + 32 * f2 + acc_row(vv, hf))],
+                        acc = fmaf(sts[kZOff + kperm(64 * sgn + 32 * f2 + acc_row(vv, hf))],
                                    (float)phb[sgn][f2][vv >> 3][vv & 7], acc);
             ls += acc;
             // numerator of the linear prefix: O^T += S^T phi_q
@@ -943,7 +944,6 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                             const bf16* sr = reinterpret_cast<const bf16*>(sts) + (32 * dt + col) * kHS +
                                              64 * sgn + 32 * f2 + 16 * s2 + 8 * hf;
                             o[dt] = mfma32(ld_bf8(sr), phb[sgn][f2][s2], o[dt]);
-                            o[dt] = mfma32(ld_bf8(sr + kD * kHS), phb[sgn][f2][s2], o[dt]);
                         }
         }
     }
