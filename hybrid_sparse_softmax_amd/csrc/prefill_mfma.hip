@@ -369,29 +369,41 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 }
             }
             const int qo = 32 * qt + col;  // query offset in the chunk; its own key is kk = qo + 64
+            // The window [qo+1, qo+64] holds all of subtile qt+1, the rows of
+            // subtile qt above the query's offset and the other rows of
+            // subtile qt+2: the last two are complementary, so each lane
+            // keeps 32 entries, w[0] (subtile qt+1) and w[1] (merged).
+            // Keys before token 0 (chunk -1) drop out.
+            f32x16 w[2];
             float mx = kNegInf;
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
-#pragma unroll
-                for (int vv = 0; vv < 16; ++vv) {
-                    const int kk = 32 * (qt + j) + acc_row(vv, hf);
-                    const bool ok = kk >= qo + 1 && kk <= qo + kC && t0 - kC + kk >= 0;
-                    const float x = ok ? tl2 * sc[j][vv] : kNegInf;  // log2 units
-                    sc[j][vv] = x;
+            for (int vv = 0; vv < 16; ++vv) {
+                const int r = acc_row(vv, hf);
+                {
+                    const int kk = 32 * (qt + 1) + r;
+                    const float x = t0 - kC + kk >= 0 ? tl2 * sc[1][vv] : kNegInf;  // log2 units
+                    w[0][vv] = x;
                     mx = vmax(mx, x);
                 }
+                {
+                    const bool lo = r > col;
+                    const int kk = lo ? 32 * qt + r : 32 * qt + kC + r;
+                    const float x = t0 - kC + kk >= 0 ? tl2 * (lo ? sc[0][vv] : sc[2][vv]) : kNegInf;
+                    w[1][vv] = x;
+                    mx = vmax(mx, x);
+                }
+            }
             mx = vmax(mx, xor32(mx));
             float sa = 0.f, so = 0.f, et = 0.f;
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    const int kk = 32 * (qt + j) + acc_row(vv, hf);
-                    const float x = sc[j][vv];
+                    const float x = w[j][vv];
                     const float e = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x - mx);
-                    sc[j][vv] = e;
+                    w[j][vv] = e;
                     sa += e;
-                    if (kk == qo + kC) et += e;
+                    if (j == 1 && acc_row(vv, hf) == col) et += e;  // the query's own key
                     else so += e;
                 }
             sa += xor32(sa);
@@ -406,13 +418,12 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
             const float esa = D.eps * sa;
             float term = 0.f;
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    const int kk = 32 * (qt + j) + acc_row(vv, hf);
-                    const float e = sc[j][vv];
+                    const float e = w[j][vv];
                     const float tj = -(e * isa) * log1p_fast(fast_div(r * e, e + esa));
-                    term += (e > 0.f && kk != qo + kC) ? tj : 0.f;
+                    term += (e > 0.f && !(j == 1 && acc_row(vv, hf) == col)) ? tj : 0.f;
                 }
             term += xor32(term);
             {
