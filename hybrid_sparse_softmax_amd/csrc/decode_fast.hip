@@ -38,6 +38,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;  // rescale only when the running max grows by more (log2 units)
 
 __device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+// the same for rows read once per step: non-temporal, so the stream does not
+// displace cached data (and streams faster)
+__device__ __forceinline__ bf16x8 ld8_stream(const bf16* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+}
 
 // sum over the 16 lanes of a DPP row; every lane of the row gets the sum
 __device__ __forceinline__ float row_sum16(float x) {
@@ -123,8 +128,8 @@ __device__ __forceinline__ void stream_role(const bf16* __restrict__ q, const Ca
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rc = min(r0 + 4 * i + grp, hi - 1);  // rows past the end repeat a valid row
-            kr[i] = ld8(sk + (size_t)rc * kD);
-            vr[i] = ld8(sv + (size_t)rc * kD);
+            kr[i] = ld8_stream(sk + (size_t)rc * kD);
+            vr[i] = ld8_stream(sv + (size_t)rc * kD);
         }
         float s[4][G];
 #pragma unroll
