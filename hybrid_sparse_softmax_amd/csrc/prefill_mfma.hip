@@ -580,16 +580,31 @@ __global__ __launch_bounds__(256) void la_group_scan_kernel(const float* __restr
     const float* base = lin + bg * D.n_full * (size_t)E1 + e;
     float* gp = gpre + bg * (size_t)ngroups * E1 + e;
     float run = 0.f;
-    for (int grp = 0; grp < ngroups; ++grp) {
-        gp[(size_t)grp * E1] = run;
-        const int first = grp * D.ng, last = min(D.n_full, first + D.ng) - 1;
-        if (cap_S && cap_chunk >= first && cap_chunk <= last) {
-            const float val = run + base[(size_t)cap_chunk * E1];
-            const int row = e / kD, f = kperm(e % kD);
-            if (row < kD) cap_S[(bg * kD + f) * kD + row] = val;
-            else cap_z[bg * kD + f] = val;
+    // the runs' totals are requested 16 at a time (independent loads), then
+    // summed in order
+    constexpr int kBatch = 16;
+    for (int g0 = 0; g0 < ngroups; g0 += kBatch) {
+        float tot[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int grp = min(g0 + i, ngroups - 1);
+            const int last = min(D.n_full, (grp + 1) * D.ng) - 1;
+            tot[i] = base[(size_t)last * E1];
         }
-        run += base[(size_t)last * E1];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int grp = g0 + i;
+            if (grp >= ngroups) break;
+            gp[(size_t)grp * E1] = run;
+            const int first = grp * D.ng, last = min(D.n_full, first + D.ng) - 1;
+            if (cap_S && cap_chunk >= first && cap_chunk <= last) {
+                const float val = run + base[(size_t)cap_chunk * E1];
+                const int row = e / kD, f = kperm(e % kD);
+                if (row < kD) cap_S[(bg * kD + f) * kD + row] = val;
+                else cap_z[bg * kD + f] = val;
+            }
+            run += tot[i];
+        }
     }
 }
 
