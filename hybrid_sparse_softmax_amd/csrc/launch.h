@@ -63,17 +63,29 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
 // each Hkv * (d'/2) * d elements
 hipError_t launch_np_weight_split(const Dims& D, const float* wphi_q, const float* wphi_k, void* hl,
                                   hipStream_t s);
-// phi_k rows [B, Hkv, N, d'] (bf16, features in kperm order) and per-chunk
-// linear sums [B, Hkv, n_full, d + 1, d'] (S^T rows then z, kperm order)
+// Linear-attention prefixes of the MFMA path.  A state is S^T [d][d'] plus
+// z [d'] (features in kperm order), E1 = (d + 1) d' entries in fp32 form.
+// ngroups = ceil(n_full / ng) runs of ng chunks.
+struct LinBufs {
+    void* sh;     // [B, Hkv, n_full, d, d'] bf16: within-run prefix of each chunk, S^T rows
+    float* lz;    // [B, Hkv, n_full, d']    its z
+    float* ltot;  // [B, Hkv, ngroups, E1]   fp32 within-run prefix at each run's last chunk
+    float* lcap;  // [B, Hkv, E1]            fp32 within-run prefix at the hand-off chunk
+    void* gh;     // [B, Hkv, ngroups, d, d'] bf16: exclusive prefix over the earlier runs, S^T rows
+    float* gz;    // [B, Hkv, ngroups, d']    its z
+};
+// phi_k rows [B, Hkv, N, d'] (bf16, features in kperm order) and the
+// within-run prefixes (L.sh, L.lz, L.ltot; L.lcap when cap_chunk >= 0)
 hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const void* wsplit,
-                           const uint8_t* route, void* phik, float* lin, hipStream_t s);
-// gpre [B, Hkv, ceil(n_full / ng), d + 1, d']: exclusive prefix over runs
-hipError_t launch_la_group_scan(const Dims& D, const float* lin, float* gpre, int cap_chunk,
-                                float* cap_S, float* cap_z, hipStream_t s);
+                           const uint8_t* route, void* phik, const LinBufs& L, int cap_chunk,
+                           hipStream_t s);
+// exclusive prefix over runs (L.gh, L.gz) and the decode hand-off state
+hipError_t launch_la_group_scan(const Dims& D, const LinBufs& L, int cap_chunk, float* cap_S,
+                                float* cap_z, hipStream_t s);
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const void* wsplit, const void* phik, const uint8_t* route,
-                              const void* ksel, const void* vsel, const float* lin,
-                              const float* gpre, void* out, hipStream_t s);
+                              const void* ksel, const void* vsel, const LinBufs& L, void* out,
+                              hipStream_t s);
 
 // ---- decode step ------------------------------------------------------------
 struct DecodeWork {

@@ -483,18 +483,21 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
 // ---------------------------------------------------------------------------
 // One block walks a run of D.ng consecutive chunks of one (b, KV head),
 // keeping the running sums in its MFMA accumulators, and writes for each
-// chunk c the prefix within its run:
-//   lin[c] rows 0..127 = S^T[dim][kperm(f)] = sum over the LA tokens of the
-//   run's chunks <= c of v[dim] phi_k[f];  row 128 = z[kperm(f)] = sum phi_k[f].
-// la_group_scan_kernel then forms each run's exclusive prefix over the
-// earlier runs, so the full prefix of chunk c is lin[c] + gpre[c / ng].
+// chunk c the prefix within its run,
+//   S^T[dim][kperm(f)] = sum over the LA tokens of the run's chunks <= c of
+//   v[dim] phi_k[f],   z[kperm(f)] = sum of phi_k[f],
+// as S^T rows in bf16 (the read-out's operand precision, L.sh) and z in fp32
+// (L.lz).  The fp32 state at the run's last chunk (its total, L.ltot) and at
+// the hand-off chunk (L.lcap) is kept for the scan.  la_group_scan_kernel
+// then forms each run's exclusive prefix over the earlier runs, so the full
+// prefix of chunk c is the within-run prefix plus the prefix of run c / ng.
 __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v,
                                                        const bf16* __restrict__ wkh,
                                                        const bf16* __restrict__ wkl,
                                                        const uint8_t* __restrict__ route,
-                                                       bf16* __restrict__ phik,
-                                                       float* __restrict__ lin, Dims D) {
+                                                       bf16* __restrict__ phik, LinBufs L,
+                                                       int cap_chunk, Dims D) {
     const int grp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
     const size_t bg = (size_t)b * D.Hkv + g;
@@ -540,7 +543,12 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
                          tid - 128, 128);
         }
         __syncthreads();
-        float* out = lin + (bg * D.n_full + c) * (size_t)((kD + 1) * kD);
+        constexpr int E1 = (kD + 1) * kD;
+        const int ngroups = (D.n_full + D.ng - 1) / D.ng;
+        bf16* oh = reinterpret_cast<bf16*>(L.sh) + (bg * D.n_full + c) * (size_t)(kD * kD);
+        // fp32 copies: the run total (last chunk of the run), the hand-off chunk
+        float* of = c == c_hi - 1 ? L.ltot + (bg * ngroups + grp) * (size_t)E1 : nullptr;
+        float* oc = c == cap_chunk ? L.lcap + bg * (size_t)E1 : nullptr;
         const int dt = wave;  // dims 32 dt .. 32 dt + 31
 #pragma unroll
         for (int f4 = 0; f4 < 4; ++f4) {
@@ -552,33 +560,44 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
                 acc[f4] = mfma32(a, hi, acc[f4]);
                 acc[f4] = mfma32(a, lo, acc[f4]);
             }
-            const int sp = kperm(32 * f4 + col);
+            const int e0 = (32 * dt + 4 * hf) * kD + kperm(32 * f4 + col);  // element vv at e0 + kD * (acc_row(vv, 0))
 #pragma unroll
-            for (int vv = 0; vv < 16; ++vv) out[(size_t)(32 * dt + acc_row(vv, hf)) * kD + sp] = acc[f4][vv];
+            for (int vv = 0; vv < 16; ++vv) oh[e0 + kD * acc_row(vv, 0)] = (bf16)acc[f4][vv];
+            if (of)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) of[e0 + kD * acc_row(vv, 0)] = acc[f4][vv];
+            if (oc)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) oc[e0 + kD * acc_row(vv, 0)] = acc[f4][vv];
         }
         if (tid < kD) {
             float z = 0.f;
             for (int t = 0; t < kC; ++t) z += ft[tid * kFS + t];
             zacc += z;
-            out[(size_t)kD * kD + kperm(tid)] = zacc;
+            const int fz = kperm(tid);
+            L.lz[(bg * D.n_full + c) * kD + fz] = zacc;
+            if (of) of[kD * kD + fz] = zacc;
+            if (oc) oc[kD * kD + fz] = zacc;
         }
         __syncthreads();  // the next chunk overwrites vt and ft
     }
 }
 
-// gpre[run] = sum of the totals of the runs before it (exclusive), per entry;
-// the full prefix of chunk cap_chunk also goes into the decode cache's
-// lin_S [f][dim] / lin_z [f].
-__global__ __launch_bounds__(256) void la_group_scan_kernel(const float* __restrict__ lin,
-                                                            float* __restrict__ gpre, int ngroups,
-                                                            int cap_chunk, float* __restrict__ cap_S,
+// Exclusive prefix over runs: the prefix of run r is the sum of the totals of
+// runs < r, written as S^T rows in bf16 (L.gh) and z in fp32 (L.gz); the full
+// fp32 prefix of chunk cap_chunk also goes into the decode cache's lin_S
+// [f][dim] / lin_z [f].
+__global__ __launch_bounds__(256) void la_group_scan_kernel(LinBufs L, int ngroups, int cap_chunk,
+                                                            float* __restrict__ cap_S,
                                                             float* __restrict__ cap_z, Dims D) {
     constexpr int E1 = (kD + 1) * kD;
     const int e = blockIdx.x * 256 + threadIdx.x, g = blockIdx.y, b = blockIdx.z;
     if (e >= E1) return;
     const size_t bg = (size_t)b * D.Hkv + g;
-    const float* base = lin + bg * D.n_full * (size_t)E1 + e;
-    float* gp = gpre + bg * (size_t)ngroups * E1 + e;
+    const float* tot_e = L.ltot + bg * ngroups * (size_t)E1 + e;
+    const bool is_s = e < kD * kD;
+    bf16* gh = reinterpret_cast<bf16*>(L.gh) + bg * (size_t)ngroups * (kD * kD) + e;
+    float* gz = L.gz + bg * (size_t)ngroups * kD + (is_s ? 0 : e - kD * kD);
     float run = 0.f;
     // the runs' totals are requested 16 at a time (independent loads), then
     // summed in order
@@ -586,19 +605,16 @@ __global__ __launch_bounds__(256) void la_group_scan_kernel(const float* __restr
     for (int g0 = 0; g0 < ngroups; g0 += kBatch) {
         float tot[kBatch];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int grp = min(g0 + i, ngroups - 1);
-            const int last = min(D.n_full, (grp + 1) * D.ng) - 1;
-            tot[i] = base[(size_t)last * E1];
-        }
+        for (int i = 0; i < kBatch; ++i) tot[i] = tot_e[(size_t)min(g0 + i, ngroups - 1) * E1];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int grp = g0 + i;
             if (grp >= ngroups) break;
-            gp[(size_t)grp * E1] = run;
+            if (is_s) gh[(size_t)grp * (kD * kD)] = (bf16)run;
+            else gz[(size_t)grp * kD] = run;
             const int first = grp * D.ng, last = min(D.n_full, first + D.ng) - 1;
             if (cap_S && cap_chunk >= first && cap_chunk <= last) {
-                const float val = run + base[(size_t)cap_chunk * E1];
+                const float val = run + L.lcap[bg * E1 + e];
                 const int row = e / kD, f = kperm(e % kD);
                 if (row < kD) cap_S[(bg * kD + f) * kD + row] = val;
                 else cap_z[bg * kD + f] = val;
@@ -735,8 +751,8 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wqh, const bf16* __restrict__ wql, const bf16* __restrict__ phik,
     const uint8_t* __restrict__ route,
-    const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const float* __restrict__ lin,
-    const float* __restrict__ gpre, bf16* __restrict__ out, Dims D) {
+    const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, LinBufs L, bf16* __restrict__ out,
+    Dims D) {
     constexpr int NW = HB * 2;  // waves
     const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
@@ -913,38 +929,41 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             // in LDS once for all waves (over the projections and phi_k rows,
             // now read): S^T rounded to bf16 (the MFMA operand, the precision
             // of every other product on this path), z in fp32
-            constexpr int kPrePieces = (kD + 1) * kD / 4, kPrePer = (kPrePieces + 64 * NW - 1) / (64 * NW);
-            f32x4 va[kPrePer], vg[kPrePer];
+            // within-run prefix of chunk c-2 plus the prefix of its run: the
+            // S^T rows arrive in bf16 (pieces of 4) and are added in fp32 and
+            // rounded once; z is fp32 throughout
+            constexpr int kSPieces = kD * kD / 4, kSPer = (kSPieces + 64 * NW - 1) / (64 * NW);
+            bf16x4 sa[kSPer], sg[kSPer];
+            f32x4 za, zg;
             {
-                const int cp = c - 2;
-                const f32x4* st4 =
-                    reinterpret_cast<const f32x4*>(lin + (bg * D.n_full + cp) * (size_t)((kD + 1) * kD));
-                const f32x4* gs4 = reinterpret_cast<const f32x4*>(
-                    gpre + (bg * ((D.n_full + D.ng - 1) / D.ng) + cp / D.ng) * (size_t)((kD + 1) * kD));
+                const int cp = c - 2, run = cp / D.ng, ngroups = (D.n_full + D.ng - 1) / D.ng;
+                const bf16x4* lh = reinterpret_cast<const bf16x4*>(
+                    reinterpret_cast<const bf16*>(L.sh) + (bg * D.n_full + cp) * (size_t)(kD * kD));
+                const bf16x4* gh = reinterpret_cast<const bf16x4*>(
+                    reinterpret_cast<const bf16*>(L.gh) + (bg * ngroups + run) * (size_t)(kD * kD));
 #pragma unroll
-                for (int t = 0; t < kPrePer; ++t) {
-                    const int x = min(tid + 64 * NW * t, kPrePieces - 1);
-                    va[t] = st4[x];
-                    vg[t] = gs4[x];
+                for (int t = 0; t < kSPer; ++t) {
+                    const int x = min(tid + 64 * NW * t, kSPieces - 1);
+                    sa[t] = lh[x];
+                    sg[t] = gh[x];
                 }
+                const int zx = min(tid, kD / 4 - 1);
+                za = reinterpret_cast<const f32x4*>(L.lz + (bg * D.n_full + cp) * kD)[zx];
+                zg = reinterpret_cast<const f32x4*>(L.gz + (bg * ngroups + run) * kD)[zx];
             }
             __syncthreads();
             bf16* sth = reinterpret_cast<bf16*>(sts);
 #pragma unroll
-            for (int t = 0; t < kPrePer; ++t) {
+            for (int t = 0; t < kSPer; ++t) {
                 const int x = tid + 64 * NW * t;
-                if (x >= kPrePieces) break;
-                const int row = (4 * x) / kD, c4 = (4 * x) % kD;
-                const f32x4 val = va[t] + vg[t];
-                if (row < kD) {
+                if (x < kSPieces) {
                     bf16x4 hi;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) hi[j] = (bf16)val[j];
-                    *reinterpret_cast<bf16x4*>(sth + row * kHS + c4) = hi;
-                } else {
-                    *reinterpret_cast<f32x4*>(&sts[kZOff + c4]) = val;
+                    for (int j = 0; j < 4; ++j) hi[j] = (bf16)((float)sa[t][j] + (float)sg[t][j]);
+                    *reinterpret_cast<bf16x4*>(sth + (4 * x / kD) * kHS + (4 * x) % kD) = hi;
                 }
             }
+            if (tid < kD / 4) *reinterpret_cast<f32x4*>(&sts[kZOff + 4 * tid]) = za + zg;
             __syncthreads();
             // normaliser of the linear prefix (chunks <= c-2): phi_q . z, with
             // the same bf16 features as the numerator's products
@@ -1363,7 +1382,8 @@ hipError_t launch_np_weight_split(const Dims& D, const float* wphi_q, const floa
 }
 
 hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const void* wsplit,
-                           const uint8_t* route, void* phik, float* lin, hipStream_t s) {
+                           const uint8_t* route, void* phik, const LinBufs& L, int cap_chunk,
+                           hipStream_t s) {
     if (D.n_full == 0) return hipSuccess;
     const int n = D.Hkv * (kD / 2) * kD;
     const bf16* wkh = reinterpret_cast<const bf16*>(wsplit) + 2 * (size_t)n;
@@ -1371,24 +1391,24 @@ hipError_t launch_la_state(const Dims& D, const void* k, const void* v, const vo
     dim3 grid((D.n_full + D.ng - 1) / D.ng, D.Hkv, D.B);
     hipLaunchKernelGGL(la_state_kernel, grid, dim3(256), 0, s, reinterpret_cast<const bf16*>(k),
                        reinterpret_cast<const bf16*>(v), wkh, wkl, route, reinterpret_cast<bf16*>(phik),
-                       lin, D);
+                       L, cap_chunk, D);
     return hipGetLastError();
 }
 
-hipError_t launch_la_group_scan(const Dims& D, const float* lin, float* gpre, int cap_chunk,
-                                float* cap_S, float* cap_z, hipStream_t s) {
+hipError_t launch_la_group_scan(const Dims& D, const LinBufs& L, int cap_chunk, float* cap_S,
+                                float* cap_z, hipStream_t s) {
     constexpr int E1 = (kD + 1) * kD;
     const int ngroups = D.n_full == 0 ? 0 : (D.n_full + D.ng - 1) / D.ng;
     dim3 grid((E1 + 255) / 256, D.Hkv, D.B);
-    hipLaunchKernelGGL(la_group_scan_kernel, grid, dim3(256), 0, s, lin, gpre, ngroups, cap_chunk,
-                       cap_S, cap_z, D);
+    hipLaunchKernelGGL(la_group_scan_kernel, grid, dim3(256), 0, s, L, ngroups, cap_chunk, cap_S, cap_z,
+                       D);
     return hipGetLastError();
 }
 
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const void* wsplit, const void* phik, const uint8_t* route,
-                              const void* ksel, const void* vsel, const float* lin,
-                              const float* gpre, void* out, hipStream_t s) {
+                              const void* ksel, const void* vsel, const LinBufs& L, void* out,
+                              hipStream_t s) {
     const int n = D.Hkv * (kD / 2) * kD;
     const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
     const bf16* wql = wqh + n;
@@ -1400,7 +1420,7 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       lin, gpre, reinterpret_cast<bf16*>(out), D)
+                       L, reinterpret_cast<bf16*>(out), D)
     if (HB == 4) STILL_MAIN(4);
     else if (HB == 2) STILL_MAIN(2);
     else STILL_MAIN(1);

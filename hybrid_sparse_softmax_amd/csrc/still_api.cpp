@@ -103,10 +103,11 @@ static FwdBuffers carve_fwd(const Dims& D, Carver& cv) {
 }
 
 struct MfmaBuffers {
-    float *scores, *lin, *gpre;
+    float* scores;
     int32_t* sel;
     uint8_t* route;
     void *ksel, *vsel, *phik, *wsplit;
+    LinBufs lin;
 };
 
 static MfmaBuffers carve_mfma(const Dims& D, Carver& cv) {
@@ -119,9 +120,14 @@ static MfmaBuffers carve_mfma(const Dims& D, Carver& cv) {
     f.ksel = cv.take<uint16_t>(nsel * D.d);
     f.vsel = cv.take<uint16_t>(nsel * D.d);
     f.phik = cv.take<uint16_t>(BG * D.N * D.fd);
-    f.lin = cv.take<float>(BG * D.n_full * (size_t)(D.d + 1) * D.fd);
     const size_t ngroups = D.n_full == 0 ? 0 : (size_t)(D.n_full + D.ng - 1) / D.ng;
-    f.gpre = cv.take<float>(BG * ngroups * (size_t)(D.d + 1) * D.fd);
+    const size_t E1 = (size_t)(D.d + 1) * D.fd;
+    f.lin.sh = cv.take<uint16_t>(BG * D.n_full * (size_t)D.d * D.fd);
+    f.lin.lz = cv.take<float>(BG * D.n_full * (size_t)D.fd);
+    f.lin.ltot = cv.take<float>(BG * ngroups * E1);
+    f.lin.lcap = cv.take<float>(BG * E1);
+    f.lin.gh = cv.take<uint16_t>(BG * ngroups * (size_t)D.d * D.fd);
+    f.lin.gz = cv.take<float>(BG * ngroups * (size_t)D.fd);
     f.wsplit = cv.take<uint16_t>((size_t)4 * D.Hkv * (D.fd / 2) * D.d);
     return f;
 }
@@ -238,13 +244,13 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
         STILL_LAUNCH(tl, s, "np_split", launch_np_weight_split(D, wq, wk, f.wsplit, s));
         STILL_LAUNCH(tl, s, "win_select",
                      launch_win_select(D, q, k, v, scores, sel, f.route, f.ksel, f.vsel, s));
-        STILL_LAUNCH(tl, s, "la_state", launch_la_state(D, k, v, f.wsplit, f.route, f.phik, f.lin, s));
+        STILL_LAUNCH(tl, s, "la_state",
+                     launch_la_state(D, k, v, f.wsplit, f.route, f.phik, f.lin, cap_chunk, s));
         STILL_LAUNCH(tl, s, "la_scan",
-                     launch_la_group_scan(D, f.lin, f.gpre, cap_chunk, cache ? cache->lin_S : nullptr,
+                     launch_la_group_scan(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
                                           cache ? cache->lin_z : nullptr, s));
         STILL_LAUNCH(tl, s, "hybrid_main",
-                     launch_hybrid_main(D, q, k, v, f.wsplit, f.phik, f.route, f.ksel, f.vsel, f.lin, f.gpre,
-                                        out, s));
+                     launch_hybrid_main(D, q, k, v, f.wsplit, f.phik, f.route, f.ksel, f.vsel, f.lin, out, s));
         if (cache)
             STILL_LAUNCH(tl, s, "handoff",
                          launch_handoff(D, k, v, wk, scores, sel, f.route, cap_chunk, view_of(cache), s));
