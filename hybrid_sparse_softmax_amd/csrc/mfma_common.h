@@ -95,13 +95,11 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, kWave
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 
-// max of x over lanes l and l ^ 32: the lane-half swap hands each lane both
-// halves' values (in one order or the other), so the max of the two results
-// is the same in every lane
-__device__ __forceinline__ float half_pair_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                    __builtin_bit_cast(unsigned, x), false, false);
-    return vmax(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-}
+// max of x over lanes l and l ^ 32 (the two halves of a query's accumulator
+// column).  A lane-half swap (v_permlane32_swap) would do it without the
+// LDS crossbar, but the compiler folds the maximum of the swap's two
+// results into its first result alone, which keeps only the lower half's
+// value; the cross-lane read below has no such fold.
+__device__ __forceinline__ float half_pair_max(float x) { return vmax(x, xor32(x)); }
 
 }  // namespace still

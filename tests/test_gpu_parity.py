@@ -33,7 +33,12 @@ CASES = {
     "bf16_swa_la_W_lt_C": (make_case("j", 1, 300, 4, 1, 128, 40, 64, 0), 22),
     # matrix-core path with two query heads per KV head, three sequences, a ragged tail
     "bf16_G2_B3_ragged": (make_case("k", 3, 777, 4, 2, 128, 64, 64, 20, outlier_frac=0.02, heavy_scale=6.0), 23),
+    # keys scaled x80 at 2% of positions: logits beyond 2^128 in exp2 units, so
+    # the matrix-core path's fixed-reference pass overflows and its second
+    # pass (running reference) recomputes those blocks
+    "bf16_overflow_G4": (make_case("o", 1, 700, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=80.0), 24),
 }
+OVERFLOW_CASES = {"bf16_overflow_G4"}
 
 
 def run_case(gpu_lib, cfg, seed, general):
@@ -76,6 +81,17 @@ def test_fwd_matches_oracle(gpu_lib, name, general):
         serr = float(np.max(np.abs(gs - sigma) / np.maximum(1.0, np.abs(sigma))))
     else:
         serr = 0.0
+    if name in OVERFLOW_CASES:
+        # the case must reach logits whose exp2 overflows fp32 (> 128 in log2 units)
+        _, ref = prepare(workloads.make_prefill(cfg, seed), torch.bfloat16, device="cpu")
+        G = cfg["n_q_heads"] // cfg["n_kv_heads"]
+        n = cfg["seqlen"]
+        causal = np.tril(np.ones((n, n), dtype=bool))
+        top = max(float(np.max(np.where(causal, ref["q"][0, :, h] @ ref["k"][0, :, h // G].T, -np.inf)))
+                  for h in range(cfg["n_q_heads"]))
+        top *= np.log2(np.e) / np.sqrt(cfg["head_dim"])
+        say(f"  largest causal logit {top:.1f} (log2 units)")
+        assert top > 130.0
     say(f"  out rel-L2 {err:.3e} (tol {tol:g}), score max rel err {serr:.3e}")
     assert err <= tol
     assert serr <= 1e-4
