@@ -1104,19 +1104,6 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             ld = (int)ld64;
             return (is_k ? (cp ? kb : k) : (cp ? vb : v)) + off;
         };
-        // maximum of a tile's logits over the lane's query (both lane halves), log2 units
-        auto tile_max2 = [&](const f32x16 (&x)[2]) {
-            float a = vmax(x[0][0], x[0][1]), b2 = vmax(x[0][8], x[0][9]);
-            float c2 = vmax(x[1][0], x[1][1]), d2 = vmax(x[1][8], x[1][9]);
-#pragma unroll
-            for (int vv = 2; vv < 8; vv += 2) {
-                a = vmax(a, vmax(x[0][vv], x[0][vv + 1]));
-                b2 = vmax(b2, vmax(x[0][vv + 8], x[0][vv + 9]));
-                c2 = vmax(c2, vmax(x[1][vv], x[1][vv + 1]));
-                d2 = vmax(d2, vmax(x[1][vv + 8], x[1][vv + 9]));
-            }
-            return half_pair_max(vmax(vmax(a, b2), vmax(c2, d2))) * cl2;
-        };
         bf16x8 pb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) pb[ks] = zero_bf8();
@@ -1135,7 +1122,6 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             stage_k_share_u<2 * HB>(src, ld, nv, lds0 + 2u * ((first + 1) & 1) * kKTile, wave);
         }
         qk(first, sc);
-        float tm2 = tile_max2(sc);  // maximum of the unmasked logits of tile s
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         lds_barrier();
         // One iteration: tile s's logits in sc and tile s-1's probabilities in
@@ -1150,28 +1136,11 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         // staging in steps 1-5, well before either barrier point.
         auto iteration = [&](int s, f32x16 (&sc)[2], bf16x8 (&pb)[4], f32x16 (&sn)[2], bf16x8 (&pn)[4])
                              __attribute__((always_inline)) {
-            // softmax of tile s up to its exps: masking (edge tiles, with their
-            // maximum taken again), rescale decision.  A rescale scales O and
-            // the pending probabilities of tile s-1 alike (exactly: al is a
-            // power of two), which equals scaling after the value product of
-            // tile s-1.
-            if (softmax_mask(s, sc)) tm2 = tile_max2(sc);
-            if (__any(tm2 > m2 + kLazy)) {
-                // a rare path: keep the compiler from speculating it into every tile
-                __asm__ volatile("");
-                const float mn = ceilf(fmaxf(m2, tm2));
-                const float al = __builtin_amdgcn_exp2f(m2 - mn);
-                m2 = mn;
-                ls *= al;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int vv = 0; vv < 16; ++vv) o[dt][vv] *= al;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) pb[ks][j] = (bf16)((float)pb[ks][j] * al);
-            }
+            // softmax of tile s: masking (edge tiles only), then the exps
+            // against the current reference m2 in the stream below; their
+            // sums (ls - ls0) are checked after it
+            softmax_mask(s, sc);
+            const float ls0 = ls;
             // staging sources: K of s+2 (or the last tile again), V of s
             int kld, knv, vld, vnv;
             const bf16* ksrc = rows_of(min(s + 2, ntile - 1), true, kld, knv);
@@ -1187,13 +1156,13 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             // 32-63), steps 8-15 the value product of tile s-1 (two each);
             // every step does the exps of two elements of tile s and issues
             // the operand reads of the step two ahead; some steps issue a
-            // staging instruction; steps 10-15 take the maximum of the
-            // finished logits.
+            // staging instruction.
             const bf16* vt = smem + 2 * kKTile + vprv * kVTile;
             const bf16* kt = kbuf(s + 1) + col * kKS + 8 * hf;
             sn[0] = zero16();
             sn[1] = zero16();
             const float nm = -m2;
+            float pt[8];
             bf16x8 a0[16], a1[16];
             auto operands = [&](int st) __attribute__((always_inline)) {
                 if (st < 8) {
@@ -1207,7 +1176,6 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             };
             operands(0);
             operands(1);
-            float ta = kNegInf, tb = kNegInf;
 #pragma unroll
             for (int st = 0; st < 16; ++st) {
                 if (st + 2 < 16) operands(st + 2);
@@ -1221,16 +1189,19 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 }
 #pragma unroll
                 for (int e = 2 * st; e < 2 * st + 2; ++e) {
-                    sc[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], cl2, nm));
+                    // the logits stay in sc (the overflow check may need them)
+                    pt[e & 7] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], cl2, nm));
                     // the empty asm needs the result here, which keeps the exp in
                     // this step (otherwise the exps of the first of two unrolled
                     // iterations sink below its products, into one block of their own)
-                    __asm__ volatile("" ::"v"(sc[e >> 4][e & 15]));
+                    __asm__ volatile("" ::"v"(pt[e & 7]));
                 }
                 if ((st & 3) == 3) {
                     // the normaliser sums the same bf16 probabilities the value
                     // product uses (two per dot instruction)
-                    const bf16x8 pk = pack_acc(sc[st >> 3], (st >> 2) & 1);
+                    bf16x8 pk;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) pk[j] = (bf16)pt[j];
                     pn[st >> 2] = pk;
                     const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
@@ -1250,31 +1221,48 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     const int x = st / 2 - 1;
                     stage_piece_sb(vpc[x], vsrc, vld2, vnm1, vdst + 1024u * (wave + 2 * HB * x), 1);
                 }
-                if (st >= 10) {
-#pragma unroll
-                    for (int j = 0; j < 3; ++j) {
-                        const int e = 6 * (st - 10) + j;  // 0..35, elements 0..31
-                        if (e < 16) {
-                            // one three-way maximum per pair: the empty asm keeps
-                            // the compiler from re-associating the chain
-                            ta = vmax(ta, vmax(sn[0][e], sn[1][e]));
-                            __asm__ volatile("" : "+v"(ta));
-                        }
-                    }
-#pragma unroll
-                    for (int j = 3; j < 6; ++j) {
-                        const int e = 6 * (st - 10) + j;
-                        if (e < 16) {
-                            tb = vmax(tb, vmax(sn[0][e], sn[1][e]));
-                            __asm__ volatile("" : "+v"(tb));
-                        }
-                    }
-                }
                 if (st == 11) staged_barrier_if(qh);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            tm2 = half_pair_max(vmax(ta, tb)) * cl2;
             staged_barrier_if(qh ^ 1);
+            // Reference point.  The exps above were taken against m2, which
+            // starts at the linear terms' reference 0 and is kept unless a
+            // tile's exps come out too large: when some lane's sum for this
+            // tile reaches 2^64 (or is not finite), m2 moves up to the next
+            // integer at or above the tile's maximum, O and the normaliser
+            // scale by al (a power of two, so exactly) and the tile's
+            // probabilities are formed again from its logits.  Weights below
+            // 2^64 keep their relative precision in fp32 and bf16, so no
+            // running maximum is needed on the common path.
+            if (__any(!(ls - ls0 < 0x1p64f))) {
+                // a rare path: keep the compiler from speculating it into every tile
+                __asm__ volatile("");
+                float mx = kNegInf;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) mx = vmax(mx, sc[kt][vv]);
+                const float mn = ceilf(fmaxf(m2, half_pair_max(mx) * cl2));
+                const float al = __builtin_amdgcn_exp2f(m2 - mn);
+                m2 = mn;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) o[dt][vv] *= al;
+                ls = ls0 * al;
+                const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        pn[ks][j] = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][8 * (ks & 1) + j], cl2, -mn));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bf16x2 pr = {pn[ks][2 * j], pn[ks][2 * j + 1]};
+                        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
+                    }
+                }
+            }
         };
         f32x16 sc2[2];
         bf16x8 pb2[4];
