@@ -17,6 +17,13 @@ struct Dims {
     bool bf16;
 };
 
+// Rows per (sequence) of the MFMA path's compact selected K / V lists, laid
+// out [B, rows, Hkv, d] like k and v: every complete chunk's lam selected
+// rows in order, then 64 rows holding the last chunk's tokens when it is
+// incomplete (later rows repeat the last token) and zeros otherwise, so any
+// 64-row window a key tile stages lies inside the list.
+__host__ __device__ inline int sel_list_rows(const Dims& D) { return D.n_full * D.lam + 64; }
+
 // Cache pointers as the kernels see them.
 struct CacheView {
     void *win_k, *win_v;

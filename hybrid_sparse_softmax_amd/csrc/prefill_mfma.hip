@@ -269,24 +269,16 @@ __device__ __forceinline__ void dma16_sbase_if(const bf16* base, unsigned off, u
                      : "memory", "m0", "scc");
 }
 
-// Lane constants of one staging instruction j of a K or V tile: the row the
-// lane's 16 bytes come from and the byte offset of its slot within the row.
-struct StagePiece {
-    unsigned row, slot16;
-};
-__device__ __forceinline__ StagePiece k_piece_lane(int j) {
+// Byte offset, from a tile's first row, of the lane's 16 bytes in staging
+// instruction j of a K or V tile whose 64 rows are all readable and ld2
+// bytes apart (the same for every tile of the output kernel's loop).
+__device__ __forceinline__ unsigned k_piece_off(int j, unsigned ld2) {
     const int p = 64 * j + (threadIdx.x & 63), row = p / 17;
-    return {(unsigned)row, 16u * (unsigned)min(p - 17 * row, 15)};
+    return (unsigned)row * ld2 + 16u * (unsigned)min(p - 17 * row, 15);
 }
-__device__ __forceinline__ StagePiece v_piece_lane(int j) {
+__device__ __forceinline__ unsigned v_piece_off(int j, unsigned ld2) {
     const int l = threadIdx.x & 63, row = 4 * j + (l >> 4);
-    return {(unsigned)row, 16u * (unsigned)((l & 15) ^ vswz(row))};
-}
-// one staging instruction of a tile whose rows start at base, ld2 bytes
-// apart, nvm1 = valid rows - 1 (later rows repeat the last valid one)
-__device__ __forceinline__ void stage_piece_sb(const StagePiece& pc, const bf16* base, unsigned ld2,
-                                               unsigned nvm1, unsigned lds_byte, int en) {
-    dma16_sbase_if(base, __umul24(min(pc.row, nvm1), ld2) + pc.slot16, lds_byte, en);
+    return (unsigned)row * ld2 + 16u * (unsigned)((l & 15) ^ vswz(row));
 }
 
 // staging instruction j (0..15) of a V tile, untracked load
@@ -444,6 +436,20 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     }
     __syncthreads();
     uint8_t* rt = route + bg * D.N + t0;
+    // the compact lists' last 64 rows: this chunk's tokens when it is the
+    // open one (rows past N repeat token N-1), zeros after a complete last chunk
+    const size_t ldkv = (size_t)D.Hkv * kD;
+    const size_t list0 = ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD;  // row 0 of (b, g)
+    if (c == D.T - 1) {
+        const size_t pad = list0 + (size_t)D.n_full * D.lam * ldkv;
+        const bool open = c >= D.n_full;
+        for (int x = tid; x < kC * 16; x += NW * 64) {
+            const int p = x >> 4, piece = x & 15;
+            const size_t src = (((size_t)b * D.N + min(t0 + p, D.N - 1)) * D.Hkv + g) * kD + 8 * piece;
+            st_bf8(ksel + pad + p * ldkv + 8 * piece, open ? ld_bf8(k + src) : zero_bf8());
+            st_bf8(vsel + pad + p * ldkv + 8 * piece, open ? ld_bf8(v + src) : zero_bf8());
+        }
+    }
     if (c >= D.n_full) {  // the open chunk: no decision yet
         if (tid < nq) rt[tid] = kPending;
         return;
@@ -473,8 +479,9 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     for (int x = tid; x < D.lam * 16; x += NW * 64) {
         const int p = x >> 4, piece = x & 15;
         const size_t src = (((size_t)b * D.N + t0 + src_s[p]) * D.Hkv + g) * kD + 8 * piece;
-        st_bf8(ksel + (base + p) * kD + 8 * piece, ld_bf8(kwin + kKTile + src_s[p] * kKS + 8 * piece));
-        st_bf8(vsel + (base + p) * kD + 8 * piece, ld_bf8(v + src));
+        const size_t dst = list0 + ((size_t)c * D.lam + p) * ldkv + 8 * piece;
+        st_bf8(ksel + dst, ld_bf8(kwin + kKTile + src_s[p] * kKS + 8 * piece));
+        st_bf8(vsel + dst, ld_bf8(v + src));
     }
 }
 
@@ -795,21 +802,25 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const int nrows = c >= 2 ? (c - 1) * D.lam : 0;
     const int ntile = 2 + (nrows + kC - 1) / kC;
     const int first = c >= 1 ? 0 : 1;
-    const bf16* kb = ksel + bg * (size_t)D.n_full * D.lam * kD;
-    const bf16* vb = vsel + bg * (size_t)D.n_full * D.lam * kD;
+    // compact lists of (b, g): rows ldkv elements apart, like k and v
     const size_t ldkv = (size_t)D.Hkv * kD;
-    // rows of tile i: source offset (elements, K and V alike), row stride, valid count
+    const bf16* kb = ksel + ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD;
+    const bf16* vb = vsel + ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD;
+    // rows of tile i: source offset (elements, K and V alike), row stride,
+    // valid count, and whether the rows come from the compact lists.  Every
+    // tile has 64 readable rows ldkv apart: an incomplete last chunk is read
+    // from its copy at the end of the compact lists.
     auto tile_src = [&](int i, size_t& off, size_t& ld, int& nv, bool& compact) {
+        ld = ldkv;
         if (i < 2) {
             const int tc = c - 1 + i;
-            off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
-            ld = ldkv;
             nv = min(kC, D.N - tc * kC);
-            compact = false;
+            compact = nv < kC;
+            off = compact ? (size_t)D.n_full * D.lam * ldkv
+                          : (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
         } else {
             const int r0 = (i - 2) * kC;
-            off = (size_t)r0 * kD;
-            ld = kD;
+            off = (size_t)r0 * ldkv;
             nv = min(kC, nrows - r0);
             compact = true;
         }
@@ -1107,13 +1118,14 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         bf16x8 pb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) pb[ks] = zero_bf8();
-        // lane constants of this wave's staging instructions (pieces wave,
+        // lane offsets of this wave's staging instructions (pieces wave,
         // wave + 8 and, for K, wave + 16 when it exists)
-        StagePiece kpc[3], vpc[2];
+        const unsigned ld2 = 2u * (unsigned)ldkv;
+        unsigned kpo[3], vpo[2];
 #pragma unroll
-        for (int x = 0; x < 3; ++x) kpc[x] = k_piece_lane(min(wave + 2 * HB * x, kKPieces - 1));
+        for (int x = 0; x < 3; ++x) kpo[x] = k_piece_off(min(wave + 2 * HB * x, kKPieces - 1), ld2);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) vpc[x] = v_piece_lane(wave + 2 * HB * x);
+        for (int x = 0; x < 2; ++x) vpo[x] = v_piece_off(wave + 2 * HB * x, ld2);
         // K of first+1 (V of first and K of first are in place; a tile index
         // past the last one stages the last one again, unused)
         {
@@ -1145,7 +1157,6 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             int kld, knv, vld, vnv;
             const bf16* ksrc = rows_of(min(s + 2, ntile - 1), true, kld, knv);
             const bf16* vsrc = rows_of(s, false, vld, vnv);
-            const unsigned kld2 = 2u * kld, knm1 = knv - 1, vld2 = 2u * vld, vnm1 = vnv - 1;
             const unsigned kdst = lds0 + 2u * (s & 1) * kKTile;
             // V buffers of tiles s (staged now) and s-1 (read now), as scalars
             const int vcur = __builtin_amdgcn_readfirstlane(s % 3);
@@ -1214,12 +1225,12 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 }
                 if (st == 1 || st == 3 || st == 5) {
                     const int x = st / 2;  // the third piece (16) is wave 0's alone
-                    stage_piece_sb(kpc[x], ksrc, kld2, knm1, kdst + 1024u * (wave + 2 * HB * x),
+                    dma16_sbase_if(ksrc, kpo[x], kdst + 1024u * (wave + 2 * HB * x),
                                    x < 2 || wave + 2 * HB * x < kKPieces);
                 }
                 if (st == 2 || st == 4) {
                     const int x = st / 2 - 1;
-                    stage_piece_sb(vpc[x], vsrc, vld2, vnm1, vdst + 1024u * (wave + 2 * HB * x), 1);
+                    dma16_sbase_if(vsrc, vpo[x], vdst + 1024u * (wave + 2 * HB * x), 1);
                 }
                 if (st == 11) staged_barrier_if(qh);
                 __builtin_amdgcn_sched_barrier(0);

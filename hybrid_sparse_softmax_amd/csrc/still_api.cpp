@@ -117,8 +117,9 @@ static MfmaBuffers carve_mfma(const Dims& D, Carver& cv) {
     f.scores = cv.take<float>(BG * D.N);
     f.sel = cv.take<int32_t>(nsel);
     f.route = cv.take<uint8_t>(BG * D.N);
-    f.ksel = cv.take<uint16_t>(nsel * D.d);
-    f.vsel = cv.take<uint16_t>(nsel * D.d);
+    const size_t nlist = BG * (size_t)sel_list_rows(D);
+    f.ksel = cv.take<uint16_t>(nlist * D.d);
+    f.vsel = cv.take<uint16_t>(nlist * D.d);
     f.phik = cv.take<uint16_t>(BG * D.N * D.fd);
     const size_t ngroups = D.n_full == 0 ? 0 : (size_t)(D.n_full + D.ng - 1) / D.ng;
     const size_t E1 = (size_t)(D.d + 1) * D.fd;
