@@ -485,6 +485,18 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     }
 }
 
+// Workgroup barrier that settles only this wave's LDS accesses (lgkmcnt), not
+// its outstanding global loads, stores or tile staging: staged rows are
+// waited for explicitly (vmcnt) at the barrier that publishes them.  The
+// empty asm statements keep the compiler from moving memory accesses across
+// the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // NP-Map of keys and linear-attention prefixes (complete chunks only)
 // ---------------------------------------------------------------------------
@@ -516,15 +528,38 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
 #pragma unroll
     for (int f4 = 0; f4 < 4; ++f4) acc[f4] = zero16();
     float zacc = 0.f;  // threads < 128: z of feature tid
+    // Each chunk's keys (waves 0-1, one token per lane) and values (waves
+    // 2-3, four rows x 8 dims per item, two items per lane) are loaded into
+    // registers one chunk ahead, so their latency overlaps the previous
+    // chunk's products; barriers wait for LDS only, never for the stores.
+    bf16x8 xb[1][8];
+    uint8_t rtok = 0;
+    bf16x8 vr[2][4];
+    auto load_chunk = [&](int c) {
+        const int t0 = c * kC;
+        if (wave < 2) {
+            const int tok = t0 + 32 * wave + col;
+            const bf16* kr = k + (((size_t)b * D.N + tok) * D.Hkv + g) * kD + 8 * hf;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) xb[0][s] = ld_bf8(kr + 16 * s);
+            rtok = route[bg * D.N + tok];
+        } else {
+            const bf16* src = v + (((size_t)b * D.N + t0) * D.Hkv + g) * kD;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int x = tid - 128 + 128 * it, kq = x & 15, oct = x >> 4;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    vr[it][rr] = ld_bf8(src + (size_t)(4 * kq + rr) * D.Hkv * kD + 8 * oct);
+            }
+        }
+    };
+    if (c_lo < c_hi) load_chunk(c_lo);
     for (int c = c_lo; c < c_hi; ++c) {
         const int t0 = c * kC;
         if (wave < 2) {
             const int tt = wave;
             const int tok = t0 + 32 * tt + col;
-            bf16x8 xb[1][8];
-            const bf16* kr = k + (((size_t)b * D.N + tok) * D.Hkv + g) * kD + 8 * hf;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) xb[0][s] = ld_bf8(kr + 16 * s);
             f32x16 phi[1][2][2];
             np_map_mfma<1>(xb, wkh + (size_t)g * (kD / 2) * kD, wkl + (size_t)g * (kD / 2) * kD, kD, phi);
             // phi_k row of the token, features in kperm order, for the read-out
@@ -536,7 +571,7 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2)
                         st_bf8(pr + 64 * sgn + 32 * f2 + 16 * s2 + 8 * hf, pack_acc(phi[0][sgn][f2], s2));
-            const bool la = route[bg * D.N + tok] == kRouteLA;
+            const bool la = rtok == kRouteLA;
             const int tp = kperm(32 * tt + col);
 #pragma unroll
             for (int sgn = 0; sgn < 2; ++sgn)
@@ -546,10 +581,24 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
                     for (int vv = 0; vv < 16; ++vv)
                         ft[(64 * sgn + 32 * f2 + acc_row(vv, hf)) * kFS + tp] = la ? phi[0][sgn][f2][vv] : 0.f;
         } else {
-            load_vt_tile(v + (((size_t)b * D.N + t0) * D.Hkv + g) * kD, (size_t)D.Hkv * kD, kC, vt,
-                         tid - 128, 128);
+            // values transposed into LDS: vt[dim][kperm(token)], as load_vt_tile
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int x = tid - 128 + 128 * it, kq = x & 15, oct = x >> 4;
+                const int pos = kperm(4 * kq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bf16x4 t4;
+                    t4[0] = vr[it][0][e];
+                    t4[1] = vr[it][1][e];
+                    t4[2] = vr[it][2][e];
+                    t4[3] = vr[it][3][e];
+                    *reinterpret_cast<bf16x4*>(vt + (8 * oct + e) * kVS + pos) = t4;
+                }
+            }
         }
-        __syncthreads();
+        if (c + 1 < c_hi) load_chunk(c + 1);
+        lds_barrier();
         constexpr int E1 = (kD + 1) * kD;
         const int ngroups = (D.n_full + D.ng - 1) / D.ng;
         bf16* oh = reinterpret_cast<bf16*>(L.sh) + (bg * D.n_full + c) * (size_t)(kD * kD);
@@ -557,6 +606,10 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
         float* of = c == c_hi - 1 ? L.ltot + (bg * ngroups + grp) * (size_t)E1 : nullptr;
         float* oc = c == cap_chunk ? L.lcap + bg * (size_t)E1 : nullptr;
         const int dt = wave;  // dims 32 dt .. 32 dt + 31
+        // S (rows = features, columns = dims) on the matrix cores, so a lane
+        // holds dim 32 dt + l%32 and features 32 f4 + acc_row(vv, l/32):
+        // elements 0-7 and 8-15 land at kperm positions 32 f4 + 8 hf + 0..7
+        // and 32 f4 + 16 + 8 hf + 0..7 of the S^T row, two 16-byte stores
 #pragma unroll
         for (int f4 = 0; f4 < 4; ++f4) {
 #pragma unroll
@@ -564,18 +617,26 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
                 const bf16x8 a = ld_bf8(vt + (32 * dt + col) * kVS + 16 * ks + 8 * hf);
                 bf16x8 hi, lo;
                 ld_split8(ft + (32 * f4 + col) * kFS + 16 * ks + 8 * hf, hi, lo);
-                acc[f4] = mfma32(a, hi, acc[f4]);
-                acc[f4] = mfma32(a, lo, acc[f4]);
+                acc[f4] = mfma32(hi, a, acc[f4]);
+                acc[f4] = mfma32(lo, a, acc[f4]);
             }
-            const int e0 = (32 * dt + 4 * hf) * kD + kperm(32 * f4 + col);  // element vv at e0 + kD * (acc_row(vv, 0))
+            const int e0 = (32 * dt + col) * kD + 32 * f4 + 8 * hf;  // elements 0-7; 8-15 at e0 + 16
 #pragma unroll
-            for (int vv = 0; vv < 16; ++vv) oh[e0 + kD * acc_row(vv, 0)] = (bf16)acc[f4][vv];
-            if (of)
-#pragma unroll
-                for (int vv = 0; vv < 16; ++vv) of[e0 + kD * acc_row(vv, 0)] = acc[f4][vv];
-            if (oc)
-#pragma unroll
-                for (int vv = 0; vv < 16; ++vv) oc[e0 + kD * acc_row(vv, 0)] = acc[f4][vv];
+            for (int h2 = 0; h2 < 2; ++h2) {
+                st_bf8(oh + e0 + 16 * h2, pack_acc(acc[f4], h2));
+                if (of) {
+                    *reinterpret_cast<f32x4*>(of + e0 + 16 * h2) =
+                        f32x4{acc[f4][8 * h2], acc[f4][8 * h2 + 1], acc[f4][8 * h2 + 2], acc[f4][8 * h2 + 3]};
+                    *reinterpret_cast<f32x4*>(of + e0 + 16 * h2 + 4) =
+                        f32x4{acc[f4][8 * h2 + 4], acc[f4][8 * h2 + 5], acc[f4][8 * h2 + 6], acc[f4][8 * h2 + 7]};
+                }
+                if (oc) {
+                    *reinterpret_cast<f32x4*>(oc + e0 + 16 * h2) =
+                        f32x4{acc[f4][8 * h2], acc[f4][8 * h2 + 1], acc[f4][8 * h2 + 2], acc[f4][8 * h2 + 3]};
+                    *reinterpret_cast<f32x4*>(oc + e0 + 16 * h2 + 4) =
+                        f32x4{acc[f4][8 * h2 + 4], acc[f4][8 * h2 + 5], acc[f4][8 * h2 + 6], acc[f4][8 * h2 + 7]};
+                }
+            }
         }
         if (tid < kD) {
             float z = 0.f;
@@ -586,7 +647,7 @@ __global__ __launch_bounds__(256) void la_state_kernel(const bf16* __restrict__ 
             if (of) of[kD * kD + fz] = zacc;
             if (oc) oc[kD * kD + fz] = zacc;
         }
-        __syncthreads();  // the next chunk overwrites vt and ft
+        lds_barrier();  // the next chunk overwrites vt and ft
     }
 }
 
@@ -699,16 +760,6 @@ __device__ __forceinline__ void sched_step_pair() {
     __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
 }
 
-// Workgroup barrier that settles only this wave's LDS reads (lgkmcnt), not
-// its outstanding tile staging: staged rows are waited for explicitly
-// (vmcnt) at the barrier that publishes them.  The empty asm statements keep
-// the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-}
 
 // Workgroup barrier taken only when en != 0 (wave-uniform), after this wave's
 // staging loads have landed (vmcnt); its LDS reads are not waited for.  The
