@@ -317,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     __shared__ float hsc[8][kC];
     __shared__ float key_s[kC];
     __shared__ int flag_s[kC];
-    __shared__ int src_s[kC];
+    __shared__ int pos_s[kC];
     // K rows of chunks c-1 and c, staged once for all heads (K tile layout;
     // rows before token 0 are never loaded and only ever masked)
     __shared__ __align__(16) bf16 kwin[2 * kKTile];
@@ -330,20 +330,37 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
             for (int j = wave; j < kKPieces; j += NW) stage_k_piece(j, src, ldkv, min(kC, D.N - tc * kC), kwin + i * kKTile);
         }
     }
+    // this chunk's value rows, requested now for the gather at the end:
+    // piece x = tid + 64 NW i is row x / 16, dims 8 (x % 16) .. +7
+    constexpr int kVP = kC * 16 / (NW * 64);
+    bf16x8 vrow[kVP];
+    if (c < D.n_full) {
+#pragma unroll
+        for (int i = 0; i < kVP; ++i) {
+            const int x = tid + NW * 64 * i;
+            vrow[i] = ld_bf8(v + (((size_t)b * D.N + t0 + (x >> 4)) * D.Hkv + g) * kD + 8 * (x & 15));
+        }
+    }
+    // Q operand of query half qt of head hh (the next one is requested while
+    // the current one is scored)
+    auto load_q = [&](bf16x8 (&qd)[8], int hh, int qt) {
+        const int t = min(t0 + 32 * qt + col, D.N - 1);
+        const bf16* row = q + (((size_t)b * D.N + t) * D.Hq + g * D.G + hh) * kD + 8 * hf;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qd[s] = ld_bf8(row + 16 * s);
+    };
+    bf16x8 qf[8], qn[8];
+    if (wave < D.G) load_q(qf, wave, 0);
     const float tl2 = D.tau * kLog2e;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     for (int hh = wave; hh < D.G; hh += NW) {
-        const int h = g * D.G + hh;
 #pragma unroll 1
         for (int qt = 0; qt < 2; ++qt) {
-            bf16x8 qf[8];
             {
-                const int t = min(t0 + 32 * qt + col, D.N - 1);
-                const bf16* row = q + (((size_t)b * D.N + t) * D.Hq + h) * kD + 8 * hf;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) qf[s] = ld_bf8(row + 16 * s);
+                const int nh = qt == 0 ? hh : hh + NW, nq = qt ^ 1;
+                if (nh < D.G) load_q(qn, nh, nq);
             }
             // logits against keys t0-64 .. t0+63 (key index kk = 32 kt + row);
             // the window of query offset qo is kk in [qo+1, qo+64], inside key
@@ -423,6 +440,8 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 term += at * log1pf(at / D.eps);
             }
             if (hf == 0) hsc[hh][qo] = term;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) qf[s] = qn[s];
         }
     }
     __syncthreads();
@@ -470,18 +489,20 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
         int before = 0;
         for (int j = 0; j < tid; ++j) before += flag_s[j];
         rt[tid] = f ? kRouteSA : kRouteLA;
-        if (f) {
-            sel_idx[base + before] = t0 + tid;
-            src_s[before] = tid;
-        }
+        if (f) sel_idx[base + before] = t0 + tid;
+        pos_s[tid] = f ? before : -1;
     }
     __syncthreads();
-    for (int x = tid; x < D.lam * 16; x += NW * 64) {
-        const int p = x >> 4, piece = x & 15;
-        const size_t src = (((size_t)b * D.N + t0 + src_s[p]) * D.Hkv + g) * kD + 8 * piece;
-        const size_t dst = list0 + ((size_t)c * D.lam + p) * ldkv + 8 * piece;
-        st_bf8(ksel + dst, ld_bf8(kwin + kKTile + src_s[p] * kKS + 8 * piece));
-        st_bf8(vsel + dst, ld_bf8(v + src));
+    // each selected row goes to its place in the compact lists (K from LDS,
+    // V from the rows requested at the start)
+#pragma unroll
+    for (int i = 0; i < kVP; ++i) {
+        const int x = tid + NW * 64 * i, p = x >> 4, piece = x & 15, at = pos_s[p];
+        if (at >= 0) {
+            const size_t dst = list0 + ((size_t)c * D.lam + at) * ldkv + 8 * piece;
+            st_bf8(ksel + dst, ld_bf8(kwin + kKTile + p * kKS + 8 * piece));
+            st_bf8(vsel + dst, vrow[i]);
+        }
     }
 }
 
