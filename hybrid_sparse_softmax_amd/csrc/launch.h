@@ -62,14 +62,13 @@ hipError_t launch_handoff(const Dims& D, const void* k, const void* v, const flo
 
 // ---- gfx950 MFMA forward (bf16, d = d' = 128, window = chunk = 64, topk > 0) ----
 bool mfma_fwd_supported(const Dims& D);
-// scores, top-k, route flags, compact selected K/V [B, Hkv, n_full * lam, d]
+// scores, top-k, route flags, compact selected K/V lists [B, sel_list_rows,
+// Hkv, d], and the NP-Map projections as bf16 high/low parts:
+// wsplit = [wq hi, wq lo, wk hi, wk lo], each Hkv * (d'/2) * d elements
 hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const void* v,
                              float* scores, int32_t* sel_idx, uint8_t* route, void* ksel,
-                             void* vsel, hipStream_t s);
-// NP-Map projections as bf16 high/low parts: hl = [wq hi, wq lo, wk hi, wk lo],
-// each Hkv * (d'/2) * d elements
-hipError_t launch_np_weight_split(const Dims& D, const float* wphi_q, const float* wphi_k, void* hl,
-                                  hipStream_t s);
+                             void* vsel, const float* wphi_q, const float* wphi_k, void* wsplit,
+                             hipStream_t s);
 // Linear-attention prefixes of the MFMA path.  A state is S^T [d][d'] plus
 // z [d'] (features in kperm order), E1 = (d + 1) d' entries in fp32 form.
 // ngroups = ceil(n_full / ng) runs of ng chunks.

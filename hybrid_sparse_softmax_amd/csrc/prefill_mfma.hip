@@ -288,28 +288,46 @@ __device__ __forceinline__ void stage_v_piece_u(int j, const bf16* __restrict__ 
     dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
 }
 
-// NP-Map projections of queries and keys as bf16 high and low parts (one
-// pass over wq then wk, n floats each): hl = [wq high, wq low, wk high, wk low]
-__global__ __launch_bounds__(256) void np_weight_split_kernel(const float* __restrict__ wq,
-                                                              const float* __restrict__ wk,
-                                                              bf16* __restrict__ hl, int n) {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < 2 * n; i += gridDim.x * 256) {
-        const float x = i < n ? wq[i] : wk[i - n];
-        const bf16 h = (bf16)x;
-        const int j = i < n ? i : i + n;  // high part of wq at i, of wk at 2n + (i - n)
-        hl[j] = h;
-        hl[j + n] = (bf16)(x - (float)h);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // window scores, selection, gather
 // ---------------------------------------------------------------------------
+// NP-Map projections of KV head g (fp32) as bf16 high and low parts for the
+// matrix-core products that use them (the projection equals high + low up to
+// the rounding of low): wsplit = [wq high, wq low, wk high, wk low], each
+// Hkv * (d'/2) * d elements.  nthr threads, 16 floats each per pass.
+__device__ __forceinline__ void split_projections(const float* __restrict__ wq, const float* __restrict__ wk,
+                                                  bf16* __restrict__ wsplit, int Hkv, int g, int nthr) {
+    const int n = Hkv * (kD / 2) * kD, per = (kD / 2) * kD;
+    for (int i0 = 4 * threadIdx.x; i0 < 2 * per; i0 += 16 * nthr) {
+        f32x4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = min(i0 + 4 * nthr * u, 2 * per - 4), which = i / per, e = g * per + i % per;
+            x[u] = *reinterpret_cast<const f32x4*>((which ? wk : wq) + e);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + 4 * nthr * u;
+            if (i >= 2 * per) break;
+            const int which = i / per, e = g * per + i % per;
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hi[j] = (bf16)x[u][j];
+                lo[j] = (bf16)(x[u][j] - (float)hi[j]);
+            }
+            *reinterpret_cast<bf16x4*>(wsplit + (size_t)2 * n * which + e) = hi;
+            *reinterpret_cast<bf16x4*>(wsplit + (size_t)2 * n * which + n + e) = lo;
+        }
+    }
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     float* __restrict__ scores, int32_t* __restrict__ sel_idx, uint8_t* __restrict__ route,
-    bf16* __restrict__ ksel, bf16* __restrict__ vsel, Dims D) {
+    bf16* __restrict__ ksel, bf16* __restrict__ vsel, const float* __restrict__ wq,
+    const float* __restrict__ wk, bf16* __restrict__ wsplit, Dims D) {
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
     const int t0 = c * kC;
@@ -469,6 +487,8 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
             st_bf8(vsel + pad + p * ldkv + 8 * piece, open ? ld_bf8(v + src) : zero_bf8());
         }
     }
+    // the first chunk's blocks of sequence 0 also split the projections
+    if (c == 0 && b == 0) split_projections(wq, wk, wsplit, D.Hkv, g, NW * 64);
     if (c >= D.n_full) {  // the open chunk: no decision yet
         if (tid < nq) rt[tid] = kPending;
         return;
@@ -1428,7 +1448,8 @@ bool mfma_fwd_supported(const Dims& D) {
 
 hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const void* v,
                              float* scores, int32_t* sel_idx, uint8_t* route, void* ksel,
-                             void* vsel, hipStream_t s) {
+                             void* vsel, const float* wphi_q, const float* wphi_k, void* wsplit,
+                             hipStream_t s) {
     dim3 grid(D.T, D.Hkv, D.B);
     const bf16* qq = reinterpret_cast<const bf16*>(q);
     const bf16* kk = reinterpret_cast<const bf16*>(k);
@@ -1436,19 +1457,11 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
     bf16* ks = reinterpret_cast<bf16*>(ksel);
     bf16* vs = reinterpret_cast<bf16*>(vsel);
     if (D.G >= 4)
-        hipLaunchKernelGGL(win_select_kernel<4>, grid, dim3(256), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, D);
+        hipLaunchKernelGGL(win_select_kernel<4>, grid, dim3(256), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D);
     else if (D.G == 2)
-        hipLaunchKernelGGL(win_select_kernel<2>, grid, dim3(128), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, D);
+        hipLaunchKernelGGL(win_select_kernel<2>, grid, dim3(128), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D);
     else
-        hipLaunchKernelGGL(win_select_kernel<1>, grid, dim3(64), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, D);
-    return hipGetLastError();
-}
-
-hipError_t launch_np_weight_split(const Dims& D, const float* wphi_q, const float* wphi_k, void* hl,
-                                  hipStream_t s) {
-    const int n = D.Hkv * (kD / 2) * kD;
-    hipLaunchKernelGGL(np_weight_split_kernel, dim3((2 * n + 255) / 256 < 256 ? (2 * n + 255) / 256 : 256),
-                       dim3(256), 0, s, wphi_q, wphi_k, reinterpret_cast<bf16*>(hl), n);
+        hipLaunchKernelGGL(win_select_kernel<1>, grid, dim3(64), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D);
     return hipGetLastError();
 }
 

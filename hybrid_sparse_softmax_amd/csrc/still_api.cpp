@@ -208,7 +208,7 @@ struct Timeline {
     } while (0)
 
 static int fwd_launches(const Dims& D, const still_shape* sh, bool with_cache) {
-    if (use_mfma(D, sh)) return 5 + (with_cache ? 1 : 0);
+    if (use_mfma(D, sh)) return 4 + (with_cache ? 1 : 0);
     return 6 + (D.W > 0 ? 1 : 0) + (with_cache ? 1 : 0);
 }
 
@@ -242,9 +242,8 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
         MfmaBuffers f = carve_mfma(D, cv);
         float* scores = scores_opt ? scores_opt : f.scores;
         int32_t* sel = sel_idx_opt ? sel_idx_opt : f.sel;
-        STILL_LAUNCH(tl, s, "np_split", launch_np_weight_split(D, wq, wk, f.wsplit, s));
         STILL_LAUNCH(tl, s, "win_select",
-                     launch_win_select(D, q, k, v, scores, sel, f.route, f.ksel, f.vsel, s));
+                     launch_win_select(D, q, k, v, scores, sel, f.route, f.ksel, f.vsel, wq, wk, f.wsplit, s));
         STILL_LAUNCH(tl, s, "la_state",
                      launch_la_state(D, k, v, f.wsplit, f.route, f.phik, f.lin, cap_chunk, s));
         STILL_LAUNCH(tl, s, "la_scan",
