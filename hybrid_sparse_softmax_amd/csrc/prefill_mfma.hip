@@ -884,7 +884,11 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // (three K-tile layouts) and last the output tiles (HB * 32 * kKS floats)
     constexpr int kPreFloats = 3 * kKTile / 2;
     constexpr int kStsA = kPrefixFloats > kPreFloats ? kPrefixFloats : kPreFloats;
-    constexpr int kStsFloats = kStsA > HB * 32 * kKS ? kStsA : HB * 32 * kKS;
+    // behind the prologue data: rows 64-127 of the earlier runs' prefix
+    // (16 KB) and the two z vectors (1 KB), parked there by the first round trip
+    constexpr int kParkFloats = kPreFloats + kD * kD / 4 + 2 * kD;
+    constexpr int kStsB = kStsA > kParkFloats ? kStsA : kParkFloats;
+    constexpr int kStsFloats = kStsB > HB * 32 * kKS ? kStsB : HB * 32 * kKS;
     __shared__ __align__(16) bf16 smem[2 * kKTile + kNV * kVTile];
     __shared__ __align__(16) float sts[kStsFloats];
     auto kbuf = [&](int i) { return smem + (i & 1) * kKTile; };
@@ -938,12 +942,6 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // layout; the route flags of chunk c-1; Q.  The prefix rows follow once
     // the projections and phi_k rows have been used.
     // (written before the staging below is issued)
-    if constexpr (HB == 4) {
-        // the V buffer of tile first-1 holds zeros: the first value product
-        // reads it (with zero probabilities)
-        bf16* vz = vbuf(first - 1);
-        for (int x = tid; x < kVTile / 8; x += 64 * NW) st_bf8(vz + 8 * x, zero_bf8());
-    }
     stage(first, true, true);
     bf16* pre = reinterpret_cast<bf16*>(sts);  // [W high | W low | phi_k rows], kKTile each
     {
@@ -956,6 +954,33 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         if (c >= 1) {
             const bf16* pk = phik + (bg * D.N + (t0 - kC)) * kD;
             for (int j = wave; j < kKPieces; j += NW) stage_k_piece(j, pk, kD, kC, pre + 2 * kKTile);
+        }
+    }
+    // The linear prefix of chunks <= c-2 (bf16 S^T rows, 32 KB each: the
+    // within-run part sh of chunk c-2 and the earlier runs' part gh) and
+    // their z vectors come with the same round trip, straight into LDS areas
+    // the prologue leaves free: sh into V buffers 1-2, gh rows 0-63 into K
+    // buffer 1, rows 64-127 and the z vectors (lz | gz) behind the prologue
+    // data in sts.  (For c >= 2 the first tile is tile 0 in K buffer 0 and V
+    // buffer 0.)
+    const int ngroups = (D.n_full + D.ng - 1) / D.ng;
+    const char* park_sh = reinterpret_cast<const char*>(smem + 2 * kKTile + kVTile);
+    const char* park_gh0 = reinterpret_cast<const char*>(smem + kKTile);
+    const char* park_gh1 = reinterpret_cast<const char*>(sts + kPreFloats);
+    const float* park_z = sts + kPreFloats + kD * kD / 4;
+    if (c >= 2) {
+        const int cp = c - 2, run = cp / D.ng;
+        const bf16* shg = reinterpret_cast<const bf16*>(L.sh) + (bg * D.n_full + cp) * (size_t)(kD * kD);
+        const bf16* ghg = reinterpret_cast<const bf16*>(L.gh) + (bg * ngroups + run) * (size_t)(kD * kD);
+        // instruction j moves bytes 1024 j .. 1024 j + 1023 of a matrix
+        for (int j = wave; j < 32; j += NW) {
+            dma16(shg + 512 * j + 8 * lane, (bf16*)park_sh + 512 * j);
+            dma16(ghg + 512 * j + 8 * lane, (bf16*)(j < 16 ? park_gh0 : park_gh1) + 512 * (j & 15));
+        }
+        if (wave == NW - 1) {
+            const float* zsrc = lane < 32 ? L.lz + (bg * D.n_full + cp) * kD + 4 * lane
+                                          : L.gz + (bg * ngroups + run) * kD + 4 * (lane - 32);
+            dma16(reinterpret_cast<const bf16*>(zsrc), (bf16*)park_z);
         }
     }
     const uint8_t rt = c >= 1 ? route[bg * D.N + (t0 - kC) + lane] : 0;
@@ -1036,37 +1061,26 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             // S^T rows arrive in bf16 (pieces of 4) and are added in fp32 and
             // rounded once; z is fp32 throughout
             constexpr int kSPieces = kD * kD / 4, kSPer = (kSPieces + 64 * NW - 1) / (64 * NW);
-            bf16x4 sa[kSPer], sg[kSPer];
-            f32x4 za, zg;
-            {
-                const int cp = c - 2, run = cp / D.ng, ngroups = (D.n_full + D.ng - 1) / D.ng;
-                const bf16x4* lh = reinterpret_cast<const bf16x4*>(
-                    reinterpret_cast<const bf16*>(L.sh) + (bg * D.n_full + cp) * (size_t)(kD * kD));
-                const bf16x4* gh = reinterpret_cast<const bf16x4*>(
-                    reinterpret_cast<const bf16*>(L.gh) + (bg * ngroups + run) * (size_t)(kD * kD));
-#pragma unroll
-                for (int t = 0; t < kSPer; ++t) {
-                    const int x = min(tid + 64 * NW * t, kSPieces - 1);
-                    sa[t] = lh[x];
-                    sg[t] = gh[x];
-                }
-                const int zx = min(tid, kD / 4 - 1);
-                za = reinterpret_cast<const f32x4*>(L.lz + (bg * D.n_full + cp) * kD)[zx];
-                zg = reinterpret_cast<const f32x4*>(L.gz + (bg * ngroups + run) * kD)[zx];
-            }
             __syncthreads();
             bf16* sth = reinterpret_cast<bf16*>(sts);
+            // piece x: elements 4x .. 4x+3 of the S^T rows (row 4x / kD)
 #pragma unroll
             for (int t = 0; t < kSPer; ++t) {
                 const int x = tid + 64 * NW * t;
                 if (x < kSPieces) {
+                    const bf16x4 sa = *reinterpret_cast<const bf16x4*>(park_sh + 8 * x);
+                    const bf16x4 sg = *reinterpret_cast<const bf16x4*>(
+                        x < kSPieces / 2 ? park_gh0 + 8 * x : park_gh1 + 8 * (x - kSPieces / 2));
                     bf16x4 hi;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) hi[j] = (bf16)((float)sa[t][j] + (float)sg[t][j]);
+                    for (int j = 0; j < 4; ++j) hi[j] = (bf16)((float)sa[j] + (float)sg[j]);
                     *reinterpret_cast<bf16x4*>(sth + (4 * x / kD) * kHS + (4 * x) % kD) = hi;
                 }
             }
-            if (tid < kD / 4) *reinterpret_cast<f32x4*>(&sts[kZOff + 4 * tid]) = za + zg;
+            if (tid < kD / 4)
+                *reinterpret_cast<f32x4*>(&sts[kZOff + 4 * tid]) =
+                    *reinterpret_cast<const f32x4*>(park_z + 4 * tid) +
+                    *reinterpret_cast<const f32x4*>(park_z + kD + 4 * tid);
             __syncthreads();
             // normaliser of the linear prefix (chunks <= c-2): phi_q . z, with
             // the same bf16 features as the numerator's products
@@ -1207,6 +1221,13 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             ld = (int)ld64;
             return (is_k ? (cp ? kb : k) : (cp ? vb : v)) + off;
         };
+        // the V buffer of tile first-1 holds zeros: the first value product
+        // reads it (with zero probabilities); the prologue's parked prefix
+        // there has been read (barrier after its use above)
+        {
+            bf16* vz = vbuf(first - 1);
+            for (int x = tid; x < kVTile / 8; x += 64 * NW) st_bf8(vz + 8 * x, zero_bf8());
+        }
         bf16x8 pb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) pb[ks] = zero_bf8();
