@@ -123,17 +123,20 @@ __device__ __forceinline__ void stream_role(const bf16* __restrict__ q, const Ca
     }
     const bf16* sk = reinterpret_cast<const bf16*>(c.sel_k) + bg * c.cap * kD + 8 * sub;
     const bf16* sv = reinterpret_cast<const bf16*>(c.sel_v) + bg * c.cap * kD + 8 * sub;
-    for (int r0 = lo; r0 < hi; r0 += 16) {
-        bf16x8 kr[4], vr[4];
+    // kRI rows per lane group and iteration (4 kRI rows per wave), all
+    // requested before any is used
+    constexpr int kRI = 8;
+    for (int r0 = lo; r0 < hi; r0 += 4 * kRI) {
+        bf16x8 kr[kRI], vr[kRI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kRI; ++i) {
             const int rc = min(r0 + 4 * i + grp, hi - 1);  // rows past the end repeat a valid row
             kr[i] = ld8_stream(sk + (size_t)rc * kD);
             vr[i] = ld8_stream(sv + (size_t)rc * kD);
         }
-        float s[4][G];
+        float s[kRI][G];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kRI; ++i) {
             const bool valid = r0 + 4 * i + grp < hi;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -145,7 +148,9 @@ __device__ __forceinline__ void stream_role(const bf16* __restrict__ q, const Ca
         bool need = false;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float x = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
+            float x = s[0][h];
+#pragma unroll
+            for (int i = 1; i < kRI; ++i) x = fmaxf(x, s[i][h]);
             x = fmaxf(x, __shfl_xor(x, 16, kWave));
             x = fmaxf(x, __shfl_xor(x, 32, kWave));
             tm[h] = x;
@@ -164,7 +169,7 @@ __device__ __forceinline__ void stream_role(const bf16* __restrict__ q, const Ca
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kRI; ++i) {
             float vf[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) vf[e] = (float)vr[i][e];
