@@ -25,6 +25,10 @@ DEC_CASES = {
     # window wider than the chunk, two query heads per KV head (bf16 d=128 decode path)
     "bf16_W48_C16_G2": (make_case("g", 2, 90 + 60, 4, 2, 128, 48, 16, 4, outlier_frac=0.03, heavy_scale=6.0), 90, 37),
     "bf16_W64_C32_G1": (make_case("h", 1, 100 + 50, 2, 2, 128, 64, 32, 8), 100, 38),
+    # keys x80 at 3% of positions: logits far beyond 2^128 in exp2 units in
+    # both the prefill and the decode steps
+    "bf16_huge_logits_G4": (make_case("i", 1, 200 + 60, 8, 2, 128, 64, 64, 16, outlier_frac=0.03,
+                                      heavy_scale=80.0), 200, 39),
 }
 
 
