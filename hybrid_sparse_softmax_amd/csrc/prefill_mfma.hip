@@ -1346,6 +1346,12 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     dma16_sbase_if(vsrc, vpo[x], vdst + 1024u * (wave + 2 * HB * x), 1);
                 }
                 if (st == 11) staged_barrier_if(qh);
+                // within the step: both products first, then the operand
+                // reads, then the vector instructions (measured 1% faster
+                // than leaving the order to the scheduler, which splits them)
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 30, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
             staged_barrier_if(qh ^ 1);
