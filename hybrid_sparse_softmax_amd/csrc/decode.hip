@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const T* __restrict__ 
     const int wave = tid / kWave, lane = tid % kWave;
     const size_t bg = (size_t)b * D.Hkv + g;
     const int W = D.W, C = D.C, G = D.G;
-    const int64_t t = c.pos;
+    const int64_t t = c.pos_dev ? c.pos_dev[b] : c.pos;
     const T* kt = k + bg * DD;
     const T* vt = v + bg * DD;
     T* ring_k = W > 0 ? reinterpret_cast<T*>(c.win_k) + bg * W * DD : nullptr;
@@ -279,9 +279,11 @@ __global__ __launch_bounds__(64) void decode_sel_kernel(const T* __restrict__ q,
 
 template <typename T, int DD>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeWork w, T* __restrict__ out,
-                                                            Dims D) {
+                                                            int64_t* __restrict__ pos_dev, Dims D) {
     constexpr int PL = DD / kWave;
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    // the last launch of the step: every read of this step's positions is done
+    if (pos_dev && h == 0 && lane == 0) pos_dev[b] += 1;
     const size_t bh = (size_t)b * D.Hq + h;
     const float* la = w.la + bh * (DD + 1);
     const float* wp = w.win + bh * (DD + 2);
@@ -358,9 +360,10 @@ hipError_t launch_decode_sel(const Dims& D, const void* q, const CacheView& c, c
     return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const Dims& D, const DecodeWork& w, void* out, hipStream_t s) {
+hipError_t launch_decode_combine(const Dims& D, const DecodeWork& w, void* out, int64_t* pos_dev,
+                                 hipStream_t s) {
     dim3 grid(D.Hq, D.B);
-#define STILL_COMB(T, DD) hipLaunchKernelGGL((decode_combine_kernel<T, DD>), grid, dim3(64), 0, s, w, reinterpret_cast<T*>(out), D)
+#define STILL_COMB(T, DD) hipLaunchKernelGGL((decode_combine_kernel<T, DD>), grid, dim3(64), 0, s, w, reinterpret_cast<T*>(out), pos_dev, D)
     if (D.d == 128) {
         if (D.bf16) STILL_COMB(__bf16, 128); else STILL_COMB(float, 128);
     } else {

@@ -245,7 +245,7 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bg = (size_t)b * D.Hkv + g;
     const int W = D.W, C = D.C, G = D.G;
-    const int64_t t = c.pos;
+    const int64_t t = c.pos_dev ? c.pos_dev[b] : c.pos;
     const int slot_t = (int)(t % W);
     bf16* ring_k = reinterpret_cast<bf16*>(c.win_k) + bg * W * kD;
     bf16* ring_v = reinterpret_cast<bf16*>(c.win_v) + bg * W * kD;
@@ -452,6 +452,8 @@ __global__ __launch_bounds__(kD) void dec_combine_kernel(FastWork w, CacheView c
                                                          Dims D) {
     const int h = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
     const int g = h / D.G, hh = h % D.G;
+    // the last launch of the step: every read of this step's positions is done
+    if (c.pos_dev && h == 0 && dim == 0) c.pos_dev[b] += 1;
     const size_t bh = (size_t)b * D.Hq + h, bg = (size_t)b * D.Hkv + g;
     const float* la = w.la + bh * (kD + 1);
     const float* wp = w.win + bh * (kD + 2);

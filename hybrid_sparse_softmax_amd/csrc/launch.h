@@ -34,6 +34,7 @@ struct CacheView {
     int32_t cap;
     float *lin_S, *lin_z;
     int64_t pos;
+    int64_t* pos_dev;  // [B] per-sequence positions (ragged decode step) or nullptr
 };
 
 // ---- general kernels (any supported shape, f32 or bf16 storage) ----------
@@ -106,7 +107,9 @@ hipError_t launch_decode_prep(const Dims& D, const void* q, const void* k, const
                               const DecodeWork& w, hipStream_t s);
 hipError_t launch_decode_sel(const Dims& D, const void* q, const CacheView& c, const DecodeWork& w,
                              hipStream_t s);
-hipError_t launch_decode_combine(const Dims& D, const DecodeWork& w, void* out, hipStream_t s);
+// advances pos_dev[b] by one when pos_dev is not null (ragged decode step)
+hipError_t launch_decode_combine(const Dims& D, const DecodeWork& w, void* out, int64_t* pos_dev,
+                                 hipStream_t s);
 
 // ---- fast decode step (bf16, d = d' = 128, window 1..64, G in {1,2,4,8}) --------
 bool fast_decode_supported(const Dims& D);

@@ -144,10 +144,12 @@ static size_t fwd_bytes(const Dims& D, const still_shape* sh) {
     return cv.off + 256;
 }
 
+// pos >= 0: cache->pos must equal it; pos == -1: any cache->pos >= 0;
+// pos == -2: cache->pos is not used (ragged decode step)
 static int check_cache(const Dims& D, const still_cache* c, int64_t pos, int64_t need_sel) {
     if (!c) return STILL_ERR_INVALID_ARG;
     if (c->pos != pos && pos >= 0) return STILL_ERR_INVALID_ARG;
-    if (c->pos < 0) return STILL_ERR_INVALID_ARG;
+    if (c->pos < 0 && pos != -2) return STILL_ERR_INVALID_ARG;
     if (!c->lin_S || !c->lin_z) return STILL_ERR_INVALID_ARG;
     if (D.W > 0 && (!c->win_k || !c->win_v || !c->win_route || !c->pend_score))
         return STILL_ERR_INVALID_ARG;
@@ -173,6 +175,7 @@ static CacheView view_of(const still_cache* c) {
     v.lin_S = c->lin_S;
     v.lin_z = c->lin_z;
     v.pos = c->pos;
+    v.pos_dev = nullptr;
     return v;
 }
 
@@ -303,23 +306,31 @@ static size_t decode_bytes(const Dims& D, const still_shape* sh, int cap) {
     return cv.off + 256;
 }
 
+// pos_dev == nullptr: one position for the batch, cache->pos (advanced here).
+// Otherwise the ragged form: pos_dev [B] device positions, advanced by the
+// step's last kernel, and max_pos >= every one of them for the capacity check.
 static int decode(const still_shape* sh, const void* q, const void* k, const void* v,
                   const float* wq, const float* wk, still_cache* cache, void* out, void* ws,
-                  size_t ws_bytes, hipStream_t s, Timeline& tl) {
+                  size_t ws_bytes, hipStream_t s, Timeline& tl, int64_t* pos_dev = nullptr,
+                  int64_t max_pos = 0) {
     int st = check_shape(sh, true);
     if (st) return st;
     const Dims D = make_dims(sh, 1);
     if (!cache) return STILL_ERR_INVALID_ARG;
+    const bool ragged = pos_dev != nullptr;
+    if (ragged && max_pos < 0) return STILL_ERR_INVALID_ARG;
     if (D.B == 0) {  // nothing to compute; the batch's position still advances
+        if (ragged) return STILL_OK;
         if (cache->pos < 0) return STILL_ERR_INVALID_ARG;
         cache->pos += 1;
         return STILL_OK;
     }
     if (!q || !k || !v || !wq || !wk || !out) return STILL_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return STILL_ERR_INVALID_ARG;
-    const int64_t t = cache->pos;
+    if (ragged && (reinterpret_cast<uintptr_t>(pos_dev) & 7u)) return STILL_ERR_INVALID_ARG;
+    const int64_t t = ragged ? max_pos : cache->pos;
     const int64_t need = D.lam * ceil_div(t + 1 - D.W, D.C);
-    st = check_cache(D, cache, -1, need);
+    st = check_cache(D, cache, ragged ? -2 : -1, need);
     if (st) return st;
     if (D.lam > 0 && cache->sel_cap < 1) return STILL_ERR_CAPACITY;
     const size_t need_ws = decode_bytes(D, sh, cache->sel_cap);
@@ -327,23 +338,25 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
     if (tl.ev && tl.max_ev < 4) return STILL_ERR_INVALID_ARG;
     void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     if (use_fast_decode(D, sh)) {
-        const CacheView cvw = view_of(cache);
+        CacheView cvw = view_of(cache);
+        cvw.pos_dev = pos_dev;
         const int nsplit = fast_decode_splits(cache->sel_cap);
         float* fw = static_cast<float*>(wsa);
         STILL_LAUNCH(tl, s, "dec_stream", launch_fast_decode(D, q, k, v, wq, wk, cvw, fw, nsplit, out, 0, s));
         STILL_LAUNCH(tl, s, "dec_combine", launch_fast_decode(D, q, k, v, wq, wk, cvw, fw, nsplit, out, 1, s));
         STILL_TRY(tl.end(s));
-        cache->pos = t + 1;
+        if (!ragged) cache->pos = t + 1;
         return STILL_OK;
     }
     Carver cv(wsa);
     DecodeWork w = carve_decode(D, cache->sel_cap, cv);
-    const CacheView cvw = view_of(cache);
+    CacheView cvw = view_of(cache);
+    cvw.pos_dev = pos_dev;
     STILL_LAUNCH(tl, s, "decode_prep", launch_decode_prep(D, q, k, v, wq, wk, cvw, w, s));
     STILL_LAUNCH(tl, s, "decode_sel", launch_decode_sel(D, q, cvw, w, s));
-    STILL_LAUNCH(tl, s, "decode_combine", launch_decode_combine(D, w, out, s));
+    STILL_LAUNCH(tl, s, "decode_combine", launch_decode_combine(D, w, out, pos_dev, s));
     STILL_TRY(tl.end(s));
-    cache->pos = t + 1;
+    if (!ragged) cache->pos = t + 1;
     return STILL_OK;
 }
 
@@ -441,6 +454,17 @@ int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q,
                                  workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
+}
+
+int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q, const void* k,
+                                         const void* v, const float* wphi_q, const float* wphi_k,
+                                         still_cache* cache, int64_t* pos_dev, int64_t max_pos,
+                                         void* out, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+    if (!pos_dev) return STILL_ERR_INVALID_ARG;
+    still::Timeline tl;
+    return still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, workspace, workspace_bytes,
+                         stream, tl, pos_dev, max_pos);
 }
 
 }  // extern "C"

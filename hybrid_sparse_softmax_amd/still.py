@@ -26,6 +26,7 @@ EXPORTED = (
     "still_fwd_workspace_size", "still_hybrid_attn_fwd",
     "still_decode_workspace_size", "still_hybrid_attn_decode_step",
     "still_hybrid_attn_fwd_timed", "still_hybrid_attn_decode_step_timed",
+    "still_hybrid_attn_decode_step_ragged",
 )
 
 
@@ -78,6 +79,10 @@ def lib() -> ct.CDLL:
         L.still_hybrid_attn_decode_step.restype = ct.c_int
         L.still_hybrid_attn_decode_step.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
                                                     ct.POINTER(CacheStruct), vp, vp, sz, vp]
+        L.still_hybrid_attn_decode_step_ragged.restype = ct.c_int
+        L.still_hybrid_attn_decode_step_ragged.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
+                                                           ct.POINTER(CacheStruct), vp, ct.c_int64,
+                                                           vp, vp, sz, vp]
         ev = [ct.POINTER(ct.c_void_p), ct.c_int32, ct.POINTER(ct.c_int32), ct.POINTER(ct.c_char_p)]
         L.still_hybrid_attn_fwd_timed.restype = ct.c_int
         L.still_hybrid_attn_fwd_timed.argtypes = L.still_hybrid_attn_fwd.argtypes + ev
@@ -271,4 +276,33 @@ def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softma
         _check(lib().still_hybrid_attn_decode_step_timed(*args, *timer.args()),
                "still_hybrid_attn_decode_step_timed")
     cache.pos = int(cs.pos)
+    return out
+
+
+def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.Tensor, max_pos: int,
+                       *, eps=1e-6, softmax_scale=0.0, out=None, workspace=None, general=False):
+    """still_hybrid_attn_decode_step_ragged: one step with a position per
+    sequence.  pos is an int64 device tensor [B] (advanced by one on the
+    stream), max_pos a host bound on its entries; cache.pos is not used.
+    q [B,1,Hq,d], k/v [B,1,Hkv,d].  Returns out [B,1,Hq,d]."""
+    B, one, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sh = make_shape(batch=B, seqlen=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                    window=cache.window, chunk=cache.chunk, topk=cache.topk, eps=eps,
+                    softmax_scale=softmax_scale, dtype=q.dtype, feat_dim=2 * wphi_q.shape[1],
+                    general=general)
+    _expect(q, "q", q.dtype, (B, 1, Hq, d))
+    _expect(k, "k", q.dtype, (B, 1, Hkv, d))
+    _expect(v, "v", q.dtype, (B, 1, Hkv, d))
+    _expect(pos, "pos", torch.int64, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = decode_workspace_size(sh, cache.sel_cap)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    cs = cache.struct()
+    _check(lib().still_hybrid_attn_decode_step_ragged(
+        ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), ct.byref(cs), _ptr(pos),
+        int(max_pos), _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
+        "still_hybrid_attn_decode_step_ragged")
     return out

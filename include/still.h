@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define STILL_ABI_VERSION 1
+#define STILL_ABI_VERSION 2
 
 typedef enum {
     STILL_OK = 0,
@@ -186,6 +186,25 @@ int still_hybrid_attn_decode_step(const still_shape* shape, const void* q, const
                                   const void* v, const float* wphi_q, const float* wphi_k,
                                   still_cache* cache, void* out, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/* Serving form of the decode step: the same step (1-5 above) with one
+ * position per sequence, for a batch whose sequences have different lengths
+ * (each sequence's cache filled by its own forward, or by earlier steps).
+ *   pos_dev   [B] int64 device memory, 8-byte aligned: the next position t_b
+ *             of sequence b; read by the step's kernels and advanced by one
+ *             (on the stream) by its last kernel
+ *   max_pos   host value >= every t_b, used for the capacity check
+ *             min(topk,C) * ceil((max_pos + 1 - W) / C) <= sel_cap
+ *   cache->pos is neither read nor written.
+ * Chunk-end selection (step 5) happens per sequence, when t_b closes a chunk
+ * of sequence b.  Errors as for still_hybrid_attn_decode_step; a NULL or
+ * misaligned pos_dev or a negative max_pos is STILL_ERR_INVALID_ARG.  (The
+ * serving setting of Sec. 4.6: every request decodes at its own length.) */
+int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q, const void* k,
+                                         const void* v, const float* wphi_q, const float* wphi_k,
+                                         still_cache* cache, int64_t* pos_dev, int64_t max_pos,
+                                         void* out, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
 
 /* Instrumented forms of the two entry points, for measurement (they compute
  * exactly what the plain calls compute).  Before the i-th kernel launch the

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert S.abi_version() == 1
+    assert S.abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5):
         assert S.status_str(code) and S.status_str(code) != "unknown status"
     assert S.status_str(7) == "unknown status"
@@ -152,3 +152,25 @@ def test_decode_empty_batch_advances_position():
     c = fake_cache(64, 100)
     assert decode_status(sh, c, ws_bytes=0, ptr=None) == S.STILL_OK
     assert c.pos == 101
+
+
+def ragged_status(sh, cache, pos_dev, max_pos, ws_bytes=1 << 40, ptr=FAKE):
+    return S.lib().still_hybrid_attn_decode_step_ragged(ct.byref(sh), ptr, ptr, ptr, ptr, ptr,
+                                                        ct.byref(cache), pos_dev, max_pos, ptr,
+                                                        FAKE, ws_bytes, None)
+
+
+def test_ragged_decode_checks():
+    sh = shape(seqlen=1, topk=32)
+    t = 16384
+    need = 32 * ((t + 1 - 64 + 63) // 64)
+    # capacity is checked against max_pos; cache.pos is not used (here -1)
+    assert ragged_status(sh, fake_cache(need - 1, -1), FAKE, t) == S.STILL_ERR_CAPACITY
+    assert ragged_status(sh, fake_cache(need, -1), FAKE, t, ws_bytes=16) == S.STILL_ERR_WORKSPACE
+    assert ragged_status(sh, fake_cache(need, -1), None, t) == S.STILL_ERR_INVALID_ARG
+    assert ragged_status(sh, fake_cache(need, -1), MISALIGNED, t) == S.STILL_ERR_INVALID_ARG
+    assert ragged_status(sh, fake_cache(need, -1), FAKE, -1) == S.STILL_ERR_INVALID_ARG
+    # an empty batch launches nothing and leaves cache.pos alone
+    c = fake_cache(64, 7)
+    assert ragged_status(shape(seqlen=1, batch=0), c, FAKE, 100, ws_bytes=0, ptr=None) == S.STILL_OK
+    assert c.pos == 7

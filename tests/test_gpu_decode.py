@@ -3,6 +3,8 @@ the oracle's recurrent form (Sec. 3.3 "Recurrent Form"): the cache the
 forward leaves behind must equal the oracle's cache after the same tokens,
 and each decode step must match the oracle's step, including the chunk-end
 routing decisions."""
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -165,3 +167,80 @@ def test_cache_checkpoint_restore_is_bit_exact(gpu_lib):
     b = run()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ragged batches: each sequence at its own position (serving form of the step)
+RAGGED_CASES = {
+    # name: (cfg with seqlen = max(N0) + steps, per-sequence N0, steps, seed)
+    "bf16_G4": (make_case("r", 3, 191 + 70, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0),
+                [70, 130, 191], 70, 51),
+    "f32_W32_C16": (make_case("s", 3, 77 + 40, 4, 1, 64, 32, 16, 4, dtype="f32"), [0, 40, 77], 40, 52),
+}
+
+
+def cache_slice(gc, b):
+    """A batch-1 view of sequence b of a DecodeCache (same memory)."""
+    sl = copy.copy(gc)
+    for key in ("win_k", "win_v", "win_route", "pend_score", "sel_k", "sel_v", "sel_count", "lin_S",
+                "lin_z"):
+        setattr(sl, key, getattr(gc, key)[b:b + 1])
+    sl._struct = None
+    return sl
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
+@pytest.mark.parametrize("name", list(RAGGED_CASES))
+def test_ragged_positions_decode(gpu_lib, name, general):
+    """Sequences prefilled to different lengths (each by its own forward into
+    its slice of one cache), then decoded together with one position per
+    sequence: every step's output and the final caches match the oracle's
+    recurrent form run per sequence, and the positions advance on the GPU."""
+    cfg, n0s, steps, seed = RAGGED_CASES[name]
+    say(f"[ragged] case={name} general={general} shape={workloads.shape_of(cfg)} N0={n0s} "
+        f"steps={steps} seed={seed}")
+    raw = workloads.make_prefill(cfg, seed)
+    dt = torch_dtype(cfg["dtype"])
+    dev, ref = prepare(raw, dt)
+    B = cfg["batch"]
+    Hkv, d = cfg["n_kv_heads"], cfg["head_dim"]
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    p = O.Params(window=W, chunk=C, topk=lam)
+    cap = p.topk_eff() * (-(-cfg["seqlen"] // C)) + 1
+    tol = F32_TOL if cfg["dtype"] == "f32" else BF16_TOL
+    one = dict(cfg, batch=1)
+
+    gc = gpu_lib.DecodeCache(batch=B, n_kv_heads=Hkv, head_dim=d, window=W, chunk=C, topk=lam,
+                             sel_cap=cap, dtype=dt)
+    ocs = []
+    for b, n0 in enumerate(n0s):
+        sl = cache_slice(gc, b)
+        sl.pos = n0
+        if n0 > 0:
+            gpu_lib.fwd(dev["q"][b:b + 1, :n0].contiguous(), dev["k"][b:b + 1, :n0].contiguous(),
+                        dev["v"][b:b + 1, :n0].contiguous(), dev["wphi_q"], dev["wphi_k"], window=W,
+                        chunk=C, topk=lam, cache=sl, general=general)
+        _, oc = O.fwd_recurrent(ref["q"][b:b + 1, :n0], ref["k"][b:b + 1, :n0], ref["v"][b:b + 1, :n0],
+                                ref["wphi_q"], ref["wphi_k"], p, cap=cap)
+        ocs.append(oc)
+    torch.cuda.synchronize()
+    pos = torch.tensor(n0s, dtype=torch.int64, device="cuda")
+    worst = 0.0
+    for s in range(steps):
+        idx = [n0 + s for n0 in n0s]
+        q_t = torch.stack([dev["q"][b, t] for b, t in enumerate(idx)])[:, None].contiguous()
+        k_t = torch.stack([dev["k"][b, t] for b, t in enumerate(idx)])[:, None].contiguous()
+        v_t = torch.stack([dev["v"][b, t] for b, t in enumerate(idx)])[:, None].contiguous()
+        g_out = gpu_lib.decode_step_ragged(q_t, k_t, v_t, dev["wphi_q"], dev["wphi_k"], gc, pos,
+                                           max(idx), general=general)
+        torch.cuda.synchronize()
+        g = g_out[:, 0].double().cpu().numpy()
+        for b, t in enumerate(idx):
+            o_out = O.decode_step(ocs[b], ref["q"][b:b + 1, t], ref["k"][b:b + 1, t],
+                                  ref["v"][b:b + 1, t], ref["wphi_q"], ref["wphi_k"], p)
+            err = rel_l2(g[b:b + 1], o_out)
+            worst = max(worst, err)
+            assert err <= tol, f"sequence {b} step t={t}: rel-L2 {err:.3e}"
+    assert pos.cpu().tolist() == [n0 + steps for n0 in n0s]
+    for b, n0 in enumerate(n0s):
+        compare_cache(cache_slice(gc, b), ocs[b], one, n0 + steps, 1e-5)
+    say(f"  {steps} ragged steps, worst rel-L2 {worst:.3e}; caches match")
