@@ -5,7 +5,9 @@ selection, sparse softmax + NP-Map linear attention, aggregation) over the
 Llama-3-8B-shaped 16K-token prefill (batch 1, 32 query / 8 KV heads,
 head_dim 128, window = chunk = 64, top-32 per chunk, bf16 storage with fp32
 accumulation), inputs resident in HBM.  The decode step (batch 64 at
-position 16384) is timed the same way and reported in the "decode" object.
+position 16384) is timed the same way and reported in the "decode" object,
+and its serving form (the same batch with one position per sequence) in
+"decode_ragged".
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
 the launch stream by the library's *_timed entry points; the roofline uses
@@ -242,6 +244,68 @@ def bench_decode(still, torch, steps, warmup):
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()}, "roofline": roof}
 
 
+def bench_decode_ragged(still, torch, steps, warmup):
+    """The decode step in its serving form: the same batch-64 shape with one
+    position per sequence (multiples of 64 drawn from [1024, 16384]), each
+    sequence's selected list as long as its position implies."""
+    name = "decode_b64_16k"
+    cfg = workloads.CONFIGS[name]
+    seed = workloads.seed_of(name)
+    B, Hq, Hkv, d = cfg["batch"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    positions = workloads.decode_positions(cfg, seed)
+    t0 = time.time()
+    full = workloads.make_decode_cache(cfg, seed, positions=positions)
+    cache = still.DecodeCache(batch=B, n_kv_heads=Hkv, head_dim=d, window=cfg["window"],
+                              chunk=cfg["chunk"], topk=cfg["topk"], sel_cap=cfg["sel_cap"])
+    for key, arr in full.items():
+        t = getattr(cache, key)
+        t.copy_(torch.from_numpy(arr).to(t.dtype))
+    del full
+    n_tok = warmup + steps
+    toks = workloads.make_decode_tokens(cfg, seed, n_tok)
+    q = torch.from_numpy(toks["q"]).to(torch.bfloat16).cuda()
+    k = torch.from_numpy(toks["k"]).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(toks["v"]).to(torch.bfloat16).cuda()
+    wq = torch.from_numpy(toks["wphi_q"]).cuda()
+    wk = torch.from_numpy(toks["wphi_k"]).cuda()
+    log(f"[bench] {name} ragged: cache ready in {time.time() - t0:.1f}s "
+        f"(positions {int(positions.min())}..{int(positions.max())}, mean {positions.mean():.0f})")
+    pos = torch.from_numpy(positions).cuda()
+    top = int(positions.max())
+    sh = still.make_shape(batch=B, seqlen=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                          window=cfg["window"], chunk=cfg["chunk"], topk=cfg["topk"])
+    ws = torch.empty(still.decode_workspace_size(sh, cfg["sel_cap"]), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, 1, Hq, d), dtype=torch.bfloat16, device="cuda")
+    qs = [q[i][:, None].contiguous() for i in range(n_tok)]
+    ks = [k[i][:, None].contiguous() for i in range(n_tok)]
+    vs = [v[i][:, None].contiguous() for i in range(n_tok)]
+    for i in range(warmup):
+        still.decode_step_ragged(qs[i], ks[i], vs[i], wq, wk, cache, pos, top + i, out=out, workspace=ws)
+    sel_before = cache.sel_count.cpu().numpy().copy()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        j = warmup + i
+        still.decode_step_ragged(qs[j], ks[j], vs[j], wq, wk, cache, pos, top + j, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    mid = (sel_before.astype(np.float64) + cache.sel_count.cpu().numpy()) / 2
+    by = decode_bytes(cfg, mid)
+    gbs = by["total"] / (ms * 1e-3) / 1e9
+    log(f"[bench] {name} ragged: {ms:.3f} ms/step, {gbs:.0f} GB/s algorithmic")
+    return {"metric": "decode tokens/s, ragged positions (batch 64)", "value": round(B / (ms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+            "config": {"workload": "decode_b64 ragged: batch 64, one token per sequence, positions "
+                       "multiples of 64 drawn from [1024, 16384], 32 q / 8 KV heads, d 128, window 64, "
+                       "chunk 64, top-32", "batch": B,
+                       "positions": {"min": int(positions.min()), "max": int(positions.max()),
+                                     "mean": round(float(positions.mean()), 1)}},
+            "step_algorithmic_bytes": by["total"], "step_GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(raw, cfg, n_rows=12):
     """The oracle as it stands, on a bounded sample: group scores and
     selection over the whole sequence, then n_rows output rows evaluated one
@@ -314,6 +378,7 @@ def main():
     pre = bench_prefill(still, torch, args.workload, args.steps, args.warmup)
     cfg = pre["cfg"]
     dec = None if args.no_decode else bench_decode(still, torch, args.steps, args.warmup)
+    dec_r = None if args.no_decode else bench_decode_ragged(still, torch, args.steps, args.warmup)
     cpu = None if args.no_cpu else cpu_baseline(pre["raw"], cfg)
     tok_s = pre["tokens"] / (pre["ms"] * 1e-3)
     line = {
@@ -330,6 +395,7 @@ def main():
         "whole_step_TFLOPs": round(pre["total_alg"] / (pre["ms"] * 1e-3) / 1e12, 2),
         "kernels_ms": {k: round(v, 4) for k, v in pre["kern"].items()},
         "decode": dec,
+        "decode_ragged": dec_r,
     }
     print(json.dumps(line), flush=True)
 

@@ -126,10 +126,19 @@ def make_decode_tokens(cfg: dict, seed: int, n_steps: int) -> dict:
     return dict(q=q, k=k, v=v, wphi_q=wq, wphi_k=wk)
 
 
-def make_decode_cache(cfg: dict, seed: int, batches=None) -> dict:
+def decode_positions(cfg: dict, seed: int) -> np.ndarray:
+    """Per-sequence positions of a ragged decode batch (the serving mix):
+    multiples of the chunk drawn uniformly from [1024, pos] (int64 [B])."""
+    C = cfg["chunk"]
+    rng = np.random.default_rng([seed, 1 << 21])
+    return (C * rng.integers(1024 // C, cfg["pos"] // C + 1, size=cfg["batch"])).astype(np.int64)
+
+
+def make_decode_cache(cfg: dict, seed: int, batches=None, positions=None) -> dict:
     """Whole-cache arrays in the library's cache layout for the sequences in
     ``batches`` (default: all), built from the per-stream draws of
-    make_decode_stream.  bf16 callers round sel/win K and V themselves."""
+    make_decode_stream; ``positions`` (per sequence, default cfg["pos"] for
+    all) gives a ragged batch.  bf16 callers round sel/win K and V themselves."""
     B = cfg["batch"] if batches is None else len(batches)
     bs = list(range(cfg["batch"])) if batches is None else list(batches)
     Hkv, d, W, C, cap = cfg["n_kv_heads"], cfg["head_dim"], cfg["window"], cfg["chunk"], cfg["sel_cap"]
@@ -142,7 +151,8 @@ def make_decode_cache(cfg: dict, seed: int, batches=None) -> dict:
     )
     for i, b in enumerate(bs):
         for g in range(Hkv):
-            s = make_decode_stream(cfg, seed, b, g)
+            s = make_decode_stream(cfg if positions is None else dict(cfg, pos=int(positions[b])),
+                                   seed, b, g)
             n = s["sel_count"]
             out["win_k"][i, g] = s["win_k"]
             out["win_v"][i, g] = s["win_v"]
