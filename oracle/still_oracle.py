@@ -44,6 +44,18 @@ R-AGG     One shared normaliser: SA tokens weigh exp(tau q.k), LA tokens weigh
           phi_q(q).phi_k(k); out = sum w v / sum w  (Fig. 2 "hybrid
           aggregation"; Fig. 1: the context is kept without loss).
 R-SCALE   tau = 1/sqrt(d) unless given.
+R-ROUTE   The routing criteria the pages compare with Self-Saliency under the
+          same routing and cache settings (full text Sec. 4 ablation, Table 7;
+          list view Tab. 10-11): "diagonal" = the token's own weight a_tt in
+          its window row; "qk" = its own logit tau q_t.k_t; both averaged over
+          the group's query heads like the Self-Saliency.  "keynorm" = ||k_t||,
+          "uniform" = lambda tokens evenly spaced in each chunk (offsets
+          floor(i C / lambda)), "random" = lambda tokens drawn uniformly per
+          chunk; these three do not depend on the queries, so the KV head's
+          score is the value itself.  The random draw is a counter-based
+          uniform: splitmix64 (Steele, Lea and Flood 2014, in Vigna's
+          formulation) of the counter ((b * Hkv + g) << 32) | t, top 24 bits
+          times 2^-24, so any implementation reproduces it exactly.
 
 Parity unpinned: the pages fix neither the exact Self-Saliency formula
 (R-SCORE), nor the exact NP-Map (R-NPMAP), nor the exact weighting of the two
@@ -69,6 +81,7 @@ class Params:
     topk: int            # lambda, per chunk
     eps: float = 1e-6    # Self-Saliency smoothing (A.3: "infinitesimally small")
     scale: float = 0.0   # tau; 0 -> 1/sqrt(d)
+    route: str = "saliency"   # routing criterion (R-ROUTE)
 
     def tau(self, d: int) -> float:
         return self.scale if self.scale > 0 else 1.0 / math.sqrt(d)
@@ -89,6 +102,8 @@ def validate(p: Params, n_q_heads: int, n_kv_heads: int, feat_dim: int) -> None:
         raise ValueError("delayed selection needs window >= chunk")
     if feat_dim % 2:
         raise ValueError("NP-Map feature dimension must be even")
+    if p.route not in ROUTES:
+        raise ValueError(f"unknown routing criterion {p.route}")
 
 
 def topk_for_budget(m: int, window: int, chunk: int, n_max: int) -> int:
@@ -139,6 +154,50 @@ def self_saliency(logits: np.ndarray, diag: np.ndarray, eps: float) -> np.ndarra
     return term.sum(axis=1)
 
 
+ROUTES = ("saliency", "diagonal", "qk", "keynorm", "uniform", "random")
+QUERY_FREE_ROUTES = ("keynorm", "uniform", "random")
+
+
+def splitmix64(x: int) -> int:
+    """One output of the splitmix64 generator for state x (R-ROUTE)."""
+    m = (1 << 64) - 1
+    z = (x + 0x9E3779B97F4A7C15) & m
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & m
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+    return z ^ (z >> 31)
+
+
+def random_score(b: int, g: int, t: int, n_kv_heads: int) -> float:
+    """Uniform draw in [0, 1) of token t of (sequence b, KV head g)."""
+    return (splitmix64(((b * n_kv_heads + g) << 32) | t) >> 40) * 2.0 ** -24
+
+
+def query_free_score(route: str, k_t: np.ndarray, t: int, b: int, g: int, n_kv_heads: int,
+                     p: Params) -> float:
+    """Score of token t under a criterion that ignores the queries."""
+    if route == "keynorm":
+        return float(np.linalg.norm(np.asarray(k_t, np.float64)))
+    if route == "uniform":
+        C, lam = p.chunk, p.topk_eff()
+        return 1.0 if (t % C) in {(i * C) // lam for i in range(lam)} else 0.0
+    if route == "random":
+        return random_score(b, g, t, n_kv_heads)
+    raise ValueError(route)
+
+
+def head_score(route: str, logits: np.ndarray, diag: np.ndarray, eps: float) -> np.ndarray:
+    """Per-query-head routing score of each row of window logits (R-SCORE,
+    R-ROUTE): Self-Saliency, the diagonal weight, or the own logit."""
+    if route == "saliency":
+        return self_saliency(logits, diag, eps)
+    rows = np.arange(logits.shape[0])
+    if route == "diagonal":
+        return _masked_softmax(np.asarray(logits, np.float64))[rows, diag]
+    if route == "qk":
+        return np.asarray(logits, np.float64)[rows, diag]
+    raise ValueError(route)
+
+
 def _masked_softmax(s: np.ndarray) -> np.ndarray:
     """Row softmax where -inf entries get weight 0; an all -inf row gives 0."""
     finite = np.isfinite(s)
@@ -163,6 +222,13 @@ def window_scores(q: np.ndarray, k: np.ndarray, p: Params, n_kv_heads: int,
         raise ValueError("scores need a window")
     G = Hq // n_kv_heads
     tau = p.tau(d)
+    if p.route in QUERY_FREE_ROUTES and not per_head:
+        sig = np.zeros((B, n_kv_heads, N))
+        for b in range(B):
+            for g in range(n_kv_heads):
+                for t in range(N):
+                    sig[b, g, t] = query_free_score(p.route, k[b, t, g], t, b, g, n_kv_heads, p)
+        return sig
     out = np.zeros((B, Hq, N))
     for b in range(B):
         for t0 in range(0, N, block):
@@ -177,7 +243,7 @@ def window_scores(q: np.ndarray, k: np.ndarray, p: Params, n_kv_heads: int,
                 g = h // G
                 lg = tau * (q[b, t0:t1, h, :] @ k[b, j0:t1, g, :].T)
                 lg = np.where(mask, lg, -np.inf)
-                out[b, h, t0:t1] = self_saliency(lg, diag, p.eps)
+                out[b, h, t0:t1] = head_score(p.route, lg, diag, p.eps)
     if per_head:
         return out
     sig = np.zeros((B, n_kv_heads, N))
@@ -395,7 +461,8 @@ def decode_step(cache: dict, q_t, k_t, v_t, wq, wk, p: Params, sel_override=None
                 qv = q_t[b, h]
                 if W > 0:
                     lw = tau * (wk_ @ qv)
-                    score_sum += self_saliency(lw[None, :], np.array([len(lw) - 1]), p.eps)[0]
+                    if p.route not in QUERY_FREE_ROUTES:
+                        score_sum += head_score(p.route, lw[None, :], np.array([len(lw) - 1]), p.eps)[0]
                     s = np.concatenate([tau * (sk @ qv), lw])
                     vv = np.concatenate([sv, wv_])
                 else:
@@ -409,7 +476,9 @@ def decode_step(cache: dict, q_t, k_t, v_t, wq, wk, p: Params, sel_override=None
                 out[b, h] = num / den
             # 3. pending score
             if W > 0:
-                cache["pend_score"][b, g, t % C] = score_sum / G
+                cache["pend_score"][b, g, t % C] = (
+                    query_free_score(p.route, k_t[b, g], t, b, g, Hkv, p)
+                    if p.route in QUERY_FREE_ROUTES else score_sum / G)
             # 5. chunk end
             if W > 0 and t % C == C - 1:
                 pos = np.arange(t - C + 1, t + 1)

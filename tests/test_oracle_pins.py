@@ -336,3 +336,82 @@ def test_validation_rules():
     with pytest.raises(ValueError):
         O.validate(O.Params(window=8, chunk=8, topk=1), 3, 2, 8)
     O.validate(O.Params(window=4, chunk=8, topk=0), 4, 2, 8)
+
+
+# ---------------------------------------------------------------- routing criteria (R-ROUTE)
+def test_splitmix64_known_answers():
+    """The published splitmix64 sequence started from state 0 (each call
+    advances the state by the golden gamma before mixing)."""
+    gamma = 0x9E3779B97F4A7C15
+    want = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    got = [O.splitmix64((i * gamma) & ((1 << 64) - 1)) for i in range(3)]
+    assert got == want
+
+
+def test_random_route_is_uniform_and_reproducible():
+    u = np.array([O.random_score(b, g, t, 8) for b in range(2) for g in range(8) for t in range(512)])
+    assert ((u >= 0) & (u < 1)).all()
+    assert abs(u.mean() - 0.5) < 0.01
+    hist = np.histogram(u, bins=16, range=(0, 1))[0]
+    assert hist.min() > 0.8 * len(u) / 16
+    assert u[0] == O.random_score(0, 0, 0, 8)
+    # every value is a multiple of 2^-24 (exact in fp32 as well)
+    assert np.all(u * 2 ** 24 == np.floor(u * 2 ** 24))
+
+
+def test_query_free_routes_pick_by_their_definition():
+    q, k, v, wq, wk = rand_inputs(21, 2, 70, 4, 2, 8)
+    for route in ("keynorm", "uniform", "random"):
+        p = O.Params(window=16, chunk=16, topk=3, route=route)
+        sig = O.window_scores(q, k, p, 2)
+        sel, _ = O.select_chunks(sig, p)
+        for b in range(2):
+            for g in range(2):
+                for c in range(70 // 16):
+                    pos = np.arange(16 * c, 16 * c + 16)
+                    if route == "keynorm":
+                        val = np.linalg.norm(k[b, pos, g], axis=1)
+                    elif route == "uniform":
+                        val = np.isin(pos % 16, [0, 5, 10]).astype(float)   # floor(16 i / 3)
+                    else:
+                        val = np.array([O.random_score(b, g, int(t), 2) for t in pos])
+                    want = np.sort(pos[np.argsort(-val, kind="stable")[:3]])
+                    np.testing.assert_array_equal(sel[b, g, c], want)
+
+
+def test_diagonal_and_qk_routes_closed_forms():
+    q, k, v, wq, wk = rand_inputs(22, 1, 20, 2, 1, 8)
+    tau = 1 / math.sqrt(8)
+    for route in ("diagonal", "qk"):
+        p = O.Params(window=4, chunk=4, topk=1, route=route)
+        sig = O.window_scores(q, k, p, 1)
+        for t in range(20):
+            vals = []
+            for h in range(2):
+                js = range(max(0, t - 3), t + 1)
+                lg = np.array([tau * q[0, t, h] @ k[0, j, 0] for j in js])
+                vals.append(math.exp(lg[-1]) / np.exp(lg).sum() if route == "diagonal" else lg[-1])
+            assert abs(sig[0, 0, t] - (vals[0] + vals[1]) / 2) < 1e-12
+
+
+def test_diagonal_route_ranks_like_saliency_as_eps_vanishes():
+    """Lemma 1 again, through the whole selection: with eps -> 0 the
+    Self-Saliency picks the same tokens as the diagonal weight."""
+    q, k, v, wq, wk = rand_inputs(23, 1, 96, 2, 1, 8, scale_k=2.0)
+    pd = O.Params(window=16, chunk=16, topk=4, route="diagonal")
+    # per head the rankings agree (the group mean of two heads can re-rank),
+    # so one query head per KV head
+    q1, k1 = q[:, :, :1], k
+    s1, _ = O.select_chunks(O.window_scores(q1, k1, O.Params(window=16, chunk=16, topk=4, eps=1e-200), 1),
+                            O.Params(window=16, chunk=16, topk=4))
+    s2, _ = O.select_chunks(O.window_scores(q1, k1, pd, 1), pd)
+    np.testing.assert_array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("route", ["diagonal", "qk", "keynorm", "uniform", "random"])
+def test_direct_equals_recurrent_for_each_route(route):
+    q, k, v, wq, wk = rand_inputs(24, 2, 45, 4, 2, 8, scale_k=1.5)
+    p = O.Params(window=8, chunk=8, topk=3, route=route)
+    direct = O.fwd_direct(q, k, v, wq, wk, p)
+    rec, cache = O.fwd_recurrent(q, k, v, wq, wk, p)
+    np.testing.assert_allclose(rec, direct["out"], rtol=1e-10, atol=1e-12)
