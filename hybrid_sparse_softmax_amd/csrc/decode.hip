@@ -127,12 +127,22 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const T* __restrict__ 
                 }
                 sa = wave_sum(sa); so = wave_sum(so); et = wave_sum(et);
                 float term = 0.f;
+                if (D.route == kRouteSaliency) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int idx = r * kWave + lane;
-                    if (idx < n_win) term += saliency_term(e[r], idx == n_win - 1, et, sa, so, D.eps);
+                    for (int r = 0; r < R; ++r) {
+                        const int idx = r * kWave + lane;
+                        if (idx < n_win) term += saliency_term(e[r], idx == n_win - 1, et, sa, so, D.eps);
+                    }
+                    term = wave_sum(term);
+                } else if (D.route == kRouteDiagonal) {
+                    term = et / sa;  // the own weight a_tt
+                } else {
+                    // the own logit tau q_t.k_t (query-free criteria ignore it)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        if (r * kWave + lane == n_win - 1) term = s[r];
+                    term = wave_sum(term);
                 }
-                term = wave_sum(term);
                 if (lane == 0) hscore[hh] = term;
                 // window partial at reference mx: l = sum e_j, acc = sum e_j v_j
                 float acc[DD / kWave];
@@ -177,9 +187,16 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const T* __restrict__ 
     }
     // group-mean score of t into the open chunk
     if (W > 0 && tid == 0) {
-        float acc = 0.f;
-        for (int hh = 0; hh < G; ++hh) acc += hscore[hh];
-        c.pend[bg * C + (int)(t % C)] = acc / (float)G;
+        if (route_query_free(D.route)) {
+            float kn = 0.f;
+            if (D.route == kRouteKeyNorm)
+                for (int i = 0; i < DD; ++i) kn = fmaf(to_f32(kt[i]), to_f32(kt[i]), kn);
+            c.pend[bg * C + (int)(t % C)] = query_free_score(D.route, sqrtf(kn), t, b, g, D.Hkv, C, D.lam);
+        } else {
+            float acc = 0.f;
+            for (int hh = 0; hh < G; ++hh) acc += hscore[hh];
+            c.pend[bg * C + (int)(t % C)] = acc / (float)G;
+        }
     }
     __syncthreads();
     // 5. t closes its chunk: top-lam of the chunk's pending scores

@@ -360,12 +360,18 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
         const float et = __shfl(e, n_win - 1, kWave);
         const float so = wave_sum(lane < n_win - 1 ? e : 0.f);
         float term = 0.f;
-        if (lane < n_win && e > 0.f) {
-            const float a = e / sa;
-            if (lane == n_win - 1) term = a * log1pf(a / D.eps);
-            else term = -a * log1p_fast(fast_div((et / so) * e, e + D.eps * sa));
+        if (D.route == kRouteSaliency) {
+            if (lane < n_win && e > 0.f) {
+                const float a = e / sa;
+                if (lane == n_win - 1) term = a * log1pf(a / D.eps);
+                else term = -a * log1p_fast(fast_div((et / so) * e, e + D.eps * sa));
+            }
+            term = wave_sum(term);
+        } else if (D.route == kRouteDiagonal) {
+            term = et / sa;  // the own weight a_tt
+        } else {
+            term = __shfl(sj, n_win - 1, kWave);  // the own logit tau q_t.k_t
         }
-        term = wave_sum(term);
         if (lane == 0) hsc[hh] = term;
         // the evicted token when it joined the selected list this step
         float sev = kNegInf;
@@ -403,9 +409,17 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
     // 5. group-mean score of t; chunk end: top-k of the chunk's scores
     __shared__ float sig_s;
     if (tid == 0) {
-        float acc = 0.f;
-        for (int hh = 0; hh < G; ++hh) acc += hsc[hh];
-        const float sig = acc / (float)G;
+        float sig;
+        if (route_query_free(D.route)) {
+            float kn = 0.f;
+            if (D.route == kRouteKeyNorm)
+                for (int e = 0; e < kD; ++e) kn = fmaf((float)kt[e], (float)kt[e], kn);
+            sig = query_free_score(D.route, sqrtf(kn), t, b, g, D.Hkv, C, D.lam);
+        } else {
+            float acc = 0.f;
+            for (int hh = 0; hh < G; ++hh) acc += hsc[hh];
+            sig = acc / (float)G;
+        }
         c.pend[bg * C + (int)(t % C)] = sig;
         sig_s = sig;
     }

@@ -10,6 +10,35 @@ constexpr int kWave = 64;
 // route flag bytes (same values as the cache's win_route)
 constexpr uint8_t kPending = 0, kRouteSA = 1, kRouteLA = 2;
 
+// routing criteria (still.h STILL_ROUTE_*)
+constexpr int kRouteSaliency = 0, kRouteDiagonal = 1, kRouteQK = 2, kRouteKeyNorm = 3,
+              kRouteUniform = 4, kRouteRandom = 5;
+__host__ __device__ constexpr bool route_query_free(int r) { return r >= kRouteKeyNorm; }
+
+// splitmix64 (Steele, Lea and Flood 2014, in Vigna's formulation): one output
+// for state x
+__host__ __device__ inline uint64_t splitmix64(uint64_t x) {
+    uint64_t z = x + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// score of token t of (sequence b, KV head g) under a query-free criterion;
+// knorm = ||k_t|| (computed by the caller)
+__host__ __device__ inline float query_free_score(int route, float knorm, int64_t t, int b, int g,
+                                                  int Hkv, int C, int lam) {
+    if (route == kRouteKeyNorm) return knorm;
+    if (route == kRouteUniform) {
+        const int off = (int)(t % C);  // selected offsets: floor(i C / lam), i < lam
+        for (int i = 0; i < lam; ++i)
+            if ((i * C) / lam == off) return 1.f;
+        return 0.f;
+    }
+    const uint64_t x = ((uint64_t)((int64_t)b * Hkv + g) << 32) | (uint64_t)(uint32_t)t;
+    return (float)(splitmix64(x) >> 40) * 0x1p-24f;
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 

@@ -77,21 +77,33 @@ __global__ __launch_bounds__(64) void head_scores_kernel(const T* __restrict__ q
     so = wave_sum(so);
     et = wave_sum(et);
     float term = 0.f;
+    if (D.route == kRouteSaliency) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int idx = r * kWave + lane;
-        if (idx < n) term += saliency_term(e[r], idx == n - 1, et, sa, so, D.eps);
+        for (int r = 0; r < R; ++r) {
+            const int idx = r * kWave + lane;
+            if (idx < n) term += saliency_term(e[r], idx == n - 1, et, sa, so, D.eps);
+        }
+        term = wave_sum(term);
+    } else if (D.route == kRouteDiagonal) {
+        term = et / sa;  // the own weight a_tt
+    } else {
+        // the own logit tau q_t.k_t (query-free criteria ignore this value)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r * kWave + lane == n - 1) term = s[r];
+        term = wave_sum(term);
     }
-    term = wave_sum(term);
     if (lane == 0) hs[((size_t)b * D.Hq + h) * D.N + t] = term;
 }
 
 // One block per (b, g, chunk): group mean of the head scores, then for a
 // complete chunk the top-lam tokens by (score desc, position asc).
+template <typename T>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ hs,
                                                      float* __restrict__ scores,
                                                      int32_t* __restrict__ sel_idx,
-                                                     uint8_t* __restrict__ route, Dims D) {
+                                                     uint8_t* __restrict__ route,
+                                                     const T* __restrict__ k, Dims D) {
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     extern __shared__ float sh[];
     float* key = sh;
@@ -100,7 +112,15 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ h
     const size_t row = ((size_t)b * D.Hkv + g) * D.N + c0;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
         float acc = 0.f;
-        if (D.W > 0) {
+        if (D.W > 0 && route_query_free(D.route)) {
+            float kn = 0.f;
+            if (D.route == kRouteKeyNorm) {
+                const T* kr = k + (((size_t)b * D.N + c0 + i) * D.Hkv + g) * D.d;
+                for (int e = 0; e < D.d; ++e) kn = fmaf(to_f32(kr[e]), to_f32(kr[e]), kn);
+                kn = sqrtf(kn);
+            }
+            acc = query_free_score(D.route, kn, c0 + i, b, g, D.Hkv, D.C, D.lam);
+        } else if (D.W > 0) {
             for (int hh = 0; hh < D.G; ++hh)
                 acc += hs[((size_t)b * D.Hq + g * D.G + hh) * D.N + c0 + i];
             acc = acc / (float)D.G;
@@ -430,10 +450,15 @@ hipError_t launch_head_scores(const Dims& D, const void* q, const void* k, float
 }
 
 hipError_t launch_select(const Dims& D, const float* hs, float* scores, int32_t* sel_idx,
-                         uint8_t* route, hipStream_t s) {
+                         uint8_t* route, const void* k, hipStream_t s) {
     dim3 grid(D.T, D.Hkv, D.B);
     const size_t shm = (size_t)D.C * (sizeof(float) + sizeof(int));
-    hipLaunchKernelGGL(select_kernel, grid, dim3(256), shm, s, hs, scores, sel_idx, route, D);
+    if (D.bf16)
+        hipLaunchKernelGGL(select_kernel<__bf16>, grid, dim3(256), shm, s, hs, scores, sel_idx, route,
+                           reinterpret_cast<const __bf16*>(k), D);
+    else
+        hipLaunchKernelGGL(select_kernel<float>, grid, dim3(256), shm, s, hs, scores, sel_idx, route,
+                           reinterpret_cast<const float*>(k), D);
     return hipGetLastError();
 }
 

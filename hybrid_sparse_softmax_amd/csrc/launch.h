@@ -13,6 +13,7 @@ struct Dims {
     int T;                        // ceil(N / C)
     int n_full;                   // N / C complete chunks
     int ng;                       // chunks per run of the MFMA path's linear-state kernel
+    int route;                    // routing criterion (kRoute*)
     float eps, tau;
     bool bf16;
 };
@@ -45,7 +46,7 @@ hipError_t launch_phi(const Dims& D, const void* x, int H, int heads_per_proj, c
 hipError_t launch_head_scores(const Dims& D, const void* q, const void* k, float* hs, hipStream_t s);
 // group mean, per-chunk top-k, route flags, selected positions
 hipError_t launch_select(const Dims& D, const float* hs, float* scores, int32_t* sel_idx,
-                         uint8_t* route, hipStream_t s);
+                         uint8_t* route, const void* k, hipStream_t s);
 // per-chunk linear-attention sums (S then z, fd*(d+1) floats per chunk), then
 // in-place inclusive prefix over chunks; optional fp32 copy of chunk `cap_chunk`
 hipError_t launch_la_chunks(const Dims& D, const float* phik, const void* v, const uint8_t* route,

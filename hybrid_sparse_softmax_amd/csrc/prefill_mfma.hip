@@ -373,7 +373,8 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
-    for (int hh = wave; hh < D.G; hh += NW) {
+    // query-free criteria need no window rows
+    for (int hh = route_query_free(D.route) ? D.G : wave; hh < D.G; hh += NW) {
 #pragma unroll 1
         for (int qt = 0; qt < 2; ++qt) {
             {
@@ -402,10 +403,11 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
             // keeps 32 entries, w[0] (subtile qt+1) and w[1] (merged).
             // Keys before token 0 (chunk -1) drop out.
             f32x16 w[2];
-            float mx = kNegInf;
+            float mx = kNegInf, lown = 0.f;  // lown: the own logit (one lane of the pair)
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
                 const int r = acc_row(vv, hf);
+                if (r == col) lown = D.tau * sc[2][vv];
                 {
                     const int kk = 32 * (qt + 1) + r;
                     const float x = t0 - kC + kk >= 0 ? tl2 * sc[1][vv] : kNegInf;  // log2 units
@@ -441,21 +443,25 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
             //   own key:    a_t log1p(a_t / eps)
             //   other keys: -a_j log1p(r e_j / (e_j + eps sa)),  r = e_t / so
             const float isa = 1.f / sa;
-            const float r = so > 0.f ? et / so : 0.f;
-            const float esa = D.eps * sa;
             float term = 0.f;
+            if (D.route == kRouteSaliency) {
+                const float r = so > 0.f ? et / so : 0.f;
+                const float esa = D.eps * sa;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int vv = 0; vv < 16; ++vv) {
-                    const float e = w[j][vv];
-                    const float tj = -(e * isa) * log1p_fast(fast_div(r * e, e + esa));
-                    term += (e > 0.f && !(j == 1 && acc_row(vv, hf) == col)) ? tj : 0.f;
-                }
-            term += xor32(term);
-            {
+                    for (int vv = 0; vv < 16; ++vv) {
+                        const float e = w[j][vv];
+                        const float tj = -(e * isa) * log1p_fast(fast_div(r * e, e + esa));
+                        term += (e > 0.f && !(j == 1 && acc_row(vv, hf) == col)) ? tj : 0.f;
+                    }
+                term += xor32(term);
                 const float at = et * isa;  // the query's own key, once
                 term += at * log1pf(at / D.eps);
+            } else if (D.route == kRouteDiagonal) {
+                term = et * isa;  // the own weight a_tt
+            } else {
+                term = lown + xor32(lown);  // the own logit tau q_t.k_t
             }
             if (hf == 0) hsc[hh][qo] = term;
 #pragma unroll
@@ -465,9 +471,20 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     __syncthreads();
     const int nq = min(kC, D.N - t0);
     if (tid < nq) {
-        float acc = 0.f;
-        for (int hh = 0; hh < D.G; ++hh) acc += hsc[hh][tid];
-        const float sig = acc / (float)D.G;
+        float sig;
+        if (route_query_free(D.route)) {
+            float kn = 0.f;
+            if (D.route == kRouteKeyNorm) {
+                const bf16* kr = kwin + kKTile + tid * kKS;  // this chunk's key rows
+                for (int e = 0; e < kD; ++e) kn = fmaf((float)kr[e], (float)kr[e], kn);
+                kn = sqrtf(kn);
+            }
+            sig = query_free_score(D.route, kn, t0 + tid, b, g, D.Hkv, kC, D.lam);
+        } else {
+            float acc = 0.f;
+            for (int hh = 0; hh < D.G; ++hh) acc += hsc[hh][tid];
+            sig = acc / (float)D.G;
+        }
         scores[bg * D.N + t0 + tid] = sig;
         key_s[tid] = route_key(sig);
     }

@@ -28,7 +28,8 @@ static int check_shape(const still_shape* sh, bool decode) {
     if (!(sh->softmax_scale >= 0.f) || !std::isfinite(sh->softmax_scale)) return STILL_ERR_INVALID_ARG;
     if (sh->dtype != STILL_F32 && sh->dtype != STILL_BF16) return STILL_ERR_INVALID_ARG;
     if (sh->head_dim < 1 || sh->feat_dim < 2 || (sh->feat_dim & 1)) return STILL_ERR_INVALID_ARG;
-    if (sh->flags & ~STILL_FLAG_GENERAL_KERNELS) return STILL_ERR_INVALID_ARG;
+    if (sh->flags & ~(STILL_FLAG_GENERAL_KERNELS | STILL_ROUTE_MASK)) return STILL_ERR_INVALID_ARG;
+    if (((sh->flags & STILL_ROUTE_MASK) >> STILL_ROUTE_SHIFT) > STILL_ROUTE_RANDOM) return STILL_ERR_INVALID_ARG;
     // built variants
     if (sh->head_dim != 64 && sh->head_dim != 128) return STILL_ERR_UNSUPPORTED;
     if (sh->feat_dim != sh->head_dim) return STILL_ERR_UNSUPPORTED;
@@ -59,6 +60,7 @@ static Dims make_dims(const still_shape* sh, int seqlen) {
         const int64_t ng = chunks / 256;
         D.ng = ng < 1 ? 1 : (ng > 16 ? 16 : (int)ng);
     }
+    D.route = (int)((sh->flags & STILL_ROUTE_MASK) >> STILL_ROUTE_SHIFT);
     D.eps = sh->eps;
     D.tau = sh->softmax_scale > 0.f ? sh->softmax_scale : 1.0f / std::sqrt((float)D.d);
     D.bf16 = sh->dtype == STILL_BF16;
@@ -267,7 +269,7 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
     STILL_LAUNCH(tl, s, "phi_q", launch_phi(D, q, D.Hq, D.G, wq, f.phiq, s));
     STILL_LAUNCH(tl, s, "phi_k", launch_phi(D, k, D.Hkv, 1, wk, f.phik, s));
     if (D.W > 0) STILL_LAUNCH(tl, s, "head_scores", launch_head_scores(D, q, k, f.hs, s));
-    STILL_LAUNCH(tl, s, "select", launch_select(D, f.hs, scores, sel, f.route, s));
+    STILL_LAUNCH(tl, s, "select", launch_select(D, f.hs, scores, sel, f.route, k, s));
     STILL_LAUNCH(tl, s, "la_chunk", launch_la_chunks(D, f.phik, v, f.route, f.lin, s));
     STILL_LAUNCH(tl, s, "la_scan", launch_la_scan(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
                                                   cache ? cache->lin_z : nullptr, s));

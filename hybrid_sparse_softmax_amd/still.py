@@ -18,6 +18,9 @@ STILL_OK, STILL_ERR_INVALID_ARG, STILL_ERR_UNSUPPORTED = 0, -1, -2
 STILL_ERR_WORKSPACE, STILL_ERR_CAPACITY, STILL_ERR_HIP = -3, -4, -5
 STILL_F32, STILL_BF16 = 0, 1
 STILL_FLAG_GENERAL_KERNELS = 1
+STILL_ROUTE_SHIFT = 1
+# routing criteria (STILL_ROUTE_* of still.h), by name
+ROUTES = {"saliency": 0, "diagonal": 1, "qk": 2, "keynorm": 3, "uniform": 4, "random": 5}
 
 STILL_MAX_LAUNCHES = 16
 
@@ -114,10 +117,11 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 def make_shape(*, batch, seqlen, n_q_heads, n_kv_heads, head_dim, window, chunk, topk,
                eps=1e-6, softmax_scale=0.0, dtype=torch.bfloat16, feat_dim=None,
-               general=False) -> Shape:
+               general=False, route="saliency") -> Shape:
+    flags = (STILL_FLAG_GENERAL_KERNELS if general else 0) | (ROUTES[route] << STILL_ROUTE_SHIFT)
     return Shape(batch, seqlen, n_q_heads, n_kv_heads, head_dim,
                  head_dim if feat_dim is None else feat_dim, window, chunk, topk, eps,
-                 softmax_scale, _dtype_code(dtype), STILL_FLAG_GENERAL_KERNELS if general else 0)
+                 softmax_scale, _dtype_code(dtype), flags)
 
 
 def _ptr(t):
@@ -212,14 +216,15 @@ class DecodeCache:
 
 def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale=0.0,
         return_scores=False, return_sel=False, cache: DecodeCache | None = None,
-        out=None, workspace=None, general=False, timer: LaunchTimer | None = None) -> dict:
+        out=None, workspace=None, general=False, timer: LaunchTimer | None = None,
+        route="saliency") -> dict:
     """still_hybrid_attn_fwd.  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or f32),
     wphi_* [Hkv, d'/2, d] f32.  Returns dict(out, scores?, sel_idx?)."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
                     chunk=chunk, topk=topk, eps=eps, softmax_scale=softmax_scale, dtype=q.dtype,
-                    feat_dim=2 * wphi_q.shape[1], general=general)
+                    feat_dim=2 * wphi_q.shape[1], general=general, route=route)
     _expect(q, "q", q.dtype, (B, N, Hq, d))
     _expect(k, "k", q.dtype, (B, N, Hkv, d))
     _expect(v, "v", q.dtype, (B, N, Hkv, d))
@@ -250,7 +255,8 @@ def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale
 
 
 def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softmax_scale=0.0,
-                out=None, workspace=None, general=False, timer: LaunchTimer | None = None):
+                out=None, workspace=None, general=False, timer: LaunchTimer | None = None,
+                route="saliency"):
     """still_hybrid_attn_decode_step at position cache.pos; q [B,1,Hq,d],
     k/v [B,1,Hkv,d].  Advances cache.pos.  Returns out [B,1,Hq,d]."""
     B, one, Hq, d = q.shape
@@ -258,7 +264,7 @@ def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softma
     sh = make_shape(batch=B, seqlen=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
                     window=cache.window, chunk=cache.chunk, topk=cache.topk, eps=eps,
                     softmax_scale=softmax_scale, dtype=q.dtype, feat_dim=2 * wphi_q.shape[1],
-                    general=general)
+                    general=general, route=route)
     _expect(q, "q", q.dtype, (B, 1, Hq, d))
     _expect(k, "k", q.dtype, (B, 1, Hkv, d))
     _expect(v, "v", q.dtype, (B, 1, Hkv, d))
@@ -280,7 +286,8 @@ def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softma
 
 
 def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.Tensor, max_pos: int,
-                       *, eps=1e-6, softmax_scale=0.0, out=None, workspace=None, general=False):
+                       *, eps=1e-6, softmax_scale=0.0, out=None, workspace=None, general=False,
+                       route="saliency"):
     """still_hybrid_attn_decode_step_ragged: one step with a position per
     sequence.  pos is an int64 device tensor [B] (advanced by one on the
     stream), max_pos a host bound on its entries; cache.pos is not used.
@@ -290,7 +297,7 @@ def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.T
     sh = make_shape(batch=B, seqlen=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
                     window=cache.window, chunk=cache.chunk, topk=cache.topk, eps=eps,
                     softmax_scale=softmax_scale, dtype=q.dtype, feat_dim=2 * wphi_q.shape[1],
-                    general=general)
+                    general=general, route=route)
     _expect(q, "q", q.dtype, (B, 1, Hq, d))
     _expect(k, "k", q.dtype, (B, 1, Hkv, d))
     _expect(v, "v", q.dtype, (B, 1, Hkv, d))

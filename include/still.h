@@ -74,6 +74,27 @@ typedef enum { STILL_F32 = 0, STILL_BF16 = 1 } still_dtype;
 /* Force the general kernels even where the gfx950 MFMA kernels apply
  * (cross-checking; both compute the same operator). */
 #define STILL_FLAG_GENERAL_KERNELS 1u
+/* Routing criterion, in bits 1-3 of flags (shifted by STILL_ROUTE_SHIFT):
+ * the per-chunk top-k ranks tokens by the Self-Saliency score (Sec. 3.1,
+ * default) or by one of the criteria the pages compare it with under the same
+ * routing and cache settings (full text Sec. 4 ablation, Table 7):
+ *   DIAGONAL  the token's own weight a_tt in its window row, mean over the
+ *             group's query heads
+ *   QK        its own logit tau q_t.k_t, mean over the group's query heads
+ *   KEYNORM   ||k_t||
+ *   UNIFORM   lambda tokens evenly spaced in each chunk (offsets floor(i C/lambda))
+ *   RANDOM    lambda tokens drawn uniformly per chunk: score = top 24 bits of
+ *             splitmix64(((b * Hkv + g) << 32) | t) times 2^-24
+ * Scores returned by the forward and kept in the decode cache are the
+ * criterion's values. */
+#define STILL_ROUTE_SHIFT 1
+#define STILL_ROUTE_MASK (7u << STILL_ROUTE_SHIFT)
+#define STILL_ROUTE_SALIENCY 0u
+#define STILL_ROUTE_DIAGONAL 1u
+#define STILL_ROUTE_QK 2u
+#define STILL_ROUTE_KEYNORM 3u
+#define STILL_ROUTE_UNIFORM 4u
+#define STILL_ROUTE_RANDOM 5u
 
 /* Problem statement (Sec. 3.3 and Appendix A.4: window W, chunk C, per-chunk
  * quota lambda; Sec. 3.2: NP-Map feature size d').

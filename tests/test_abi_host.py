@@ -86,6 +86,13 @@ def test_bad_dtype_and_flags():
     sh = shape()
     sh.flags = 0x80
     assert fwd_status(sh) == S.STILL_ERR_INVALID_ARG
+    # routing criteria 0-5 in bits 1-3; 6 and 7 are not defined
+    for r in (6, 7):
+        sh = shape()
+        sh.flags = r << S.STILL_ROUTE_SHIFT
+        assert fwd_status(sh) == S.STILL_ERR_INVALID_ARG
+    for name in S.ROUTES:
+        assert fwd_status(shape(route=name), ws_bytes=16) == S.STILL_ERR_WORKSPACE
     assert S.lib().still_fwd_workspace_size(None, ct.byref(ct.c_size_t())) == S.STILL_ERR_INVALID_ARG
     assert S.lib().still_fwd_workspace_size(ct.byref(shape()), None) == S.STILL_ERR_INVALID_ARG
 

@@ -244,3 +244,41 @@ def test_ragged_positions_decode(gpu_lib, name, general):
     for b, n0 in enumerate(n0s):
         compare_cache(cache_slice(gc, b), ocs[b], one, n0 + steps, 1e-5)
     say(f"  {steps} ragged steps, worst rel-L2 {worst:.3e}; caches match")
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
+@pytest.mark.parametrize("route", ["diagonal", "qk", "keynorm", "uniform", "random"])
+def test_decode_routing_criteria(gpu_lib, route, general):
+    """Hand-off and decode steps under each routing criterion: the chunk-end
+    decisions of the recurrent form use the criterion's pending scores."""
+    cfg = make_case("j", 2, 130 + 70, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0)
+    N0, seed = 130, 61
+    say(f"[decode route] {route} general={general} shape={workloads.shape_of(cfg)} N0={N0}")
+    raw = workloads.make_prefill(cfg, seed)
+    dev, ref = prepare(raw, torch.bfloat16)
+    B, N, Hkv, d = cfg["batch"], cfg["seqlen"], cfg["n_kv_heads"], cfg["head_dim"]
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    p = O.Params(window=W, chunk=C, topk=lam, route=route)
+    cap = p.topk_eff() * (-(-N // C)) + 1
+    gc = gpu_lib.DecodeCache(batch=B, n_kv_heads=Hkv, head_dim=d, window=W, chunk=C, topk=lam,
+                             sel_cap=cap, pos=N0)
+    gpu_lib.fwd(dev["q"][:, :N0].contiguous(), dev["k"][:, :N0].contiguous(), dev["v"][:, :N0].contiguous(),
+                dev["wphi_q"], dev["wphi_k"], window=W, chunk=C, topk=lam, cache=gc, general=general,
+                route=route)
+    _, oc = O.fwd_recurrent(ref["q"][:, :N0], ref["k"][:, :N0], ref["v"][:, :N0], ref["wphi_q"],
+                            ref["wphi_k"], p, cap=cap)
+    torch.cuda.synchronize()
+    compare_cache(gc, oc, cfg, N0, 1e-5)
+    worst = 0.0
+    for t in range(N0, N):
+        g_out = gpu_lib.decode_step(dev["q"][:, t:t + 1].contiguous(), dev["k"][:, t:t + 1].contiguous(),
+                                    dev["v"][:, t:t + 1].contiguous(), dev["wphi_q"], dev["wphi_k"], gc,
+                                    general=general, route=route)
+        o_out = O.decode_step(oc, ref["q"][:, t], ref["k"][:, t], ref["v"][:, t], ref["wphi_q"],
+                              ref["wphi_k"], p)
+        torch.cuda.synchronize()
+        err = rel_l2(g_out[:, 0].double().cpu().numpy(), o_out)
+        worst = max(worst, err)
+        assert err <= BF16_TOL, f"step t={t}: rel-L2 {err:.3e}"
+    compare_cache(gc, oc, cfg, N, 1e-5)
+    say(f"  {N - N0} steps, worst rel-L2 {worst:.3e}")

@@ -114,3 +114,37 @@ def test_empty_sequence_is_noop(gpu_lib):
     w = torch.zeros((2, 64, 128), dtype=torch.float32, device="cuda")
     res = gpu_lib.fwd(q, k, k, w, w, window=64, chunk=64, topk=16)
     assert res["out"].shape == (1, 0, 4, 128)
+
+
+ROUTE_CASE = (make_case("q", 1, 400, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 25)
+ROUTE_NAMES = ["diagonal", "qk", "keynorm", "uniform", "random"]
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
+@pytest.mark.parametrize("route", ROUTE_NAMES)
+def test_routing_criteria_match_oracle(gpu_lib, route, general):
+    """The routing criteria the pages compare with Self-Saliency: same scores,
+    same selections (or near-ties the oracle adopts), same outputs."""
+    cfg, seed = ROUTE_CASE
+    say(f"[route] {route} general={general} shape={workloads.shape_of(cfg)} seed={seed}")
+    raw = workloads.make_prefill(cfg, seed)
+    dev, ref = prepare(raw, torch.bfloat16)
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    res = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W, chunk=C,
+                      topk=lam, return_scores=True, return_sel=True, general=general, route=route)
+    torch.cuda.synchronize()
+    p = O.Params(window=W, chunk=C, topk=lam, route=route)
+    sigma = O.window_scores(ref["q"], ref["k"], p, cfg["n_kv_heads"])
+    gs = res["scores"].cpu().numpy()
+    serr = float(np.max(np.abs(gs - sigma) / np.maximum(1.0, np.abs(sigma))))
+    gsel = res["sel_idx"].cpu().numpy().astype(np.int64)
+    osel, _ = O.select_chunks(sigma, p)
+    n_bad, worst = check_selection(gsel, sigma, osel, C)
+    o = O.fwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"], p,
+                     sel_override=gsel if n_bad else None, scores=sigma)
+    err = rel_l2(res["out"].double().cpu().numpy(), o["out"])
+    say(f"  score max rel err {serr:.2e}; {n_bad} near-tie chunks; out rel-L2 {err:.3e}")
+    assert serr <= 1e-4
+    if route in ("uniform", "random"):
+        np.testing.assert_array_equal(gsel, osel)
+    assert err <= BF16_TOL
