@@ -56,6 +56,12 @@ R-ROUTE   The routing criteria the pages compare with Self-Saliency under the
           uniform: splitmix64 (Steele, Lea and Flood 2014, in Vigna's
           formulation) of the counter ((b * Hkv + g) << 32) | t, top 24 bits
           times 2^-24, so any implementation reproduces it exactly.
+R-BWD     Gradients (the backward pass the pages need for their two-stage
+          linearization: Sec. 4.1 "Experimental Setups", training strategy;
+          App. A.6.1, primary configuration) treat the routing as a
+          constant mask: nothing flows through the scores or the top-lambda,
+          and where the NP-Map projection P x is zero the map is taken as
+          locally constant.
 
 Parity unpinned: the pages fix neither the exact Self-Saliency formula
 (R-SCORE), nor the exact NP-Map (R-NPMAP), nor the exact weighting of the two
@@ -509,3 +515,124 @@ def fwd_recurrent(q, k, v, wq, wk, p: Params, cap: int | None = None, sel_overri
     for t in range(N):
         out[:, t] = decode_step(cache, q[:, t], k[:, t], v[:, t], wq, wk, p, sel_override)
     return out, cache
+
+
+# --------------------------------------------------------------------------
+# Backward pass (gradients of the chunk-parallel form with the routing held
+# fixed).  R-BWD: the selection is a constant mask -- no gradient flows
+# through the scores, the top-lambda or the route flags; M = max(0, max s)
+# cancels between numerator and denominator, so it carries none either.
+# The gradient is the chain rule of fwd_direct's formulas, written out per
+# query; every step below is the derivative of one step there.
+# --------------------------------------------------------------------------
+def np_map_vjp(x, P, dphi):
+    """Vector-Jacobian product of np_map at x [..., d] with projection P
+    [d'/2, d]: returns (dx [..., d], dP [d'/2, d]) for the cotangent dphi
+    [..., d'].  Where u = P x is zero the map is taken as locally constant
+    (zero gradient): z is pinned to 0 there by R-NPMAP.
+
+    Steps (reverse order of np_map):
+      a = softmax(z), b = softmax(-z):
+          dz = a * (da - <da, a>) - b * (db - <db, b>)
+      z = ||x|| * uh with uh = u / ||u||:
+          d||x|| = <dz, uh>,  duh = ||x|| dz
+      uh = u / ||u||:   du = (duh - <duh, uh> uh) / ||u||
+      ||x||:            dx = d||x|| * x / ||x||
+      u = P x:          dx += P^T du,  dP = du x^T (summed over rows)"""
+    x = np.asarray(x, np.float64)
+    P = np.asarray(P, np.float64)
+    dphi = np.asarray(dphi, np.float64)
+    half = P.shape[0]
+    u = x @ P.T
+    nu = np.linalg.norm(u, axis=-1, keepdims=True)
+    nx = np.linalg.norm(x, axis=-1, keepdims=True)
+    ok = nu > 0
+    uh = np.where(ok, u / np.where(ok, nu, 1.0), 0.0)
+    z = nx * uh
+    a, bm = _softmax(z), _softmax(-z)
+    da, db = dphi[..., :half], dphi[..., half:]
+    dz = a * (da - (da * a).sum(-1, keepdims=True)) - bm * (db - (db * bm).sum(-1, keepdims=True))
+    dnx = (dz * uh).sum(-1, keepdims=True)
+    duh = nx * dz
+    du = np.where(ok, (duh - (duh * uh).sum(-1, keepdims=True) * uh) / np.where(ok, nu, 1.0), 0.0)
+    dnx = np.where(ok, dnx, 0.0)
+    dx = np.where(nx > 0, dnx * x / np.where(nx > 0, nx, 1.0), 0.0) + du @ P
+    dP = du.reshape(-1, half).T @ x.reshape(-1, x.shape[-1])
+    return dx, dP
+
+
+def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None):
+    """Gradients of L = sum(dout * out) with out = fwd_direct(q, k, v, wq,
+    wk, p) and the routing fixed to ``sel_idx`` [B, Hkv, N//C, lambda]
+    (the forward's own selection when None).
+
+    Returns dict(dq, dk, dv [shapes of q, k, v], dwq, dwk [shape of wq]).
+
+    Per query t of head h (KV head g), with the sets of fwd_direct:
+      w_j = exp(s_j - M) on SA_t, exp(-M) kappa_j on LA_t, kappa_j = phi_q . phi_k(k_j)
+      den = sum w_j,  out = sum w_j v_j / den,  Dt = dout . out
+      SA:  ds_j = (w_j / den) (dout . v_j - Dt);  dq += tau ds_j k_j;
+           dk_j += tau ds_j q;  dv_j += (w_j / den) dout
+      LA:  dkappa_j = (exp(-M) / den) (dout . v_j - Dt);
+           dphi_q += dkappa_j phi_k(k_j);  dphi_k(k_j) += dkappa_j phi_q;
+           dv_j += (w_j / den) dout
+    then the NP-Map's vector-Jacobian product carries dphi_q to q and W_phi_q,
+    dphi_k to k and W_phi_k."""
+    q, k, v, dout = (np.asarray(a, np.float64) for a in (q, k, v, dout))
+    wq, wk = np.asarray(wq, np.float64), np.asarray(wk, np.float64)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    validate(p, Hq, Hkv, 2 * wq.shape[1])
+    G = Hq // Hkv
+    W, tau = p.window, p.tau(d)
+    if p.topk_eff() > 0:
+        if sel_idx is None:
+            sel_idx = select_chunks(window_scores(q, k, p, Hkv), p)[0]
+        route = route_from_selection(np.asarray(sel_idx, np.int64), N, p.chunk)
+    else:
+        route = np.full((B, Hkv, N), ROUTE_LA, np.uint8)
+
+    phik = np.stack([np_map(k[:, :, g, :], wk[g]) for g in range(Hkv)], axis=2)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dphiq = np.zeros(q.shape[:3] + (2 * wq.shape[1],))
+    dphik = np.zeros_like(phik)
+    for b in range(B):
+        for t in range(N):
+            r_end = t - W + 1
+            for g in range(Hkv):
+                win = np.arange(max(0, t - W + 1), t + 1) if W > 0 else np.arange(0)
+                routed = np.arange(0, max(0, r_end))
+                rr = route[b, g, routed]
+                if np.any(rr == PENDING):
+                    raise AssertionError("a routed token has no decision")
+                sa = np.concatenate([routed[rr == ROUTE_SA], win])
+                la = routed[rr == ROUTE_LA]
+                for h in range(g * G, (g + 1) * G):
+                    qv, do = q[b, t, h], dout[b, t, h]
+                    s = tau * (k[b, sa, g, :] @ qv)
+                    fq = np_map(qv, wq[g])
+                    kap = phik[b, la, g, :] @ fq
+                    M = max(0.0, s.max()) if s.size else 0.0
+                    w_sa = np.exp(s - M)
+                    w_la = math.exp(-M) * kap
+                    den = w_sa.sum() + w_la.sum()
+                    o = (w_sa @ v[b, sa, g, :] + w_la @ v[b, la, g, :]) / den
+                    Dt = do @ o
+                    ds = (w_sa / den) * (v[b, sa, g, :] @ do - Dt)
+                    dq[b, t, h] += tau * (ds @ k[b, sa, g, :])
+                    np.add.at(dk[b, :, g, :], sa, tau * np.outer(ds, qv))
+                    np.add.at(dv[b, :, g, :], sa, np.outer(w_sa / den, do))
+                    dkap = (math.exp(-M) / den) * (v[b, la, g, :] @ do - Dt)
+                    dphiq[b, t, h] += dkap @ phik[b, la, g, :]
+                    np.add.at(dphik[b, :, g, :], la, np.outer(dkap, fq))
+                    np.add.at(dv[b, :, g, :], la, np.outer(w_la / den, do))
+    dwq, dwk = np.zeros_like(wq), np.zeros_like(wk)
+    for g in range(Hkv):
+        for h in range(g * G, (g + 1) * G):
+            dx, dP = np_map_vjp(q[:, :, h, :], wq[g], dphiq[:, :, h, :])
+            dq[:, :, h, :] += dx
+            dwq[g] += dP
+        dx, dP = np_map_vjp(k[:, :, g, :], wk[g], dphik[:, :, g, :])
+        dk[:, :, g, :] += dx
+        dwk[g] += dP
+    return dict(dq=dq, dk=dk, dv=dv, dwq=dwq, dwk=dwk)
