@@ -18,7 +18,8 @@ OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libstill.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["still_api.cpp", "general.hip", "decode.hip", "decode_fast.hip", "prefill_mfma.hip"]
+SOURCES = ["still_api.cpp", "general.hip", "decode.hip", "decode_fast.hip", "prefill_mfma.hip",
+           "backward.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -1,0 +1,615 @@
+// Backward pass of the STILL hybrid attention operator: gradients of
+// L = sum(dout * out) w.r.t. q, k, v and the two NP-Map projections, with the
+// routing held fixed (the selection is a constant mask; no gradient flows
+// through the scores or the top-k).  The training this serves is the paper's
+// two-stage linearization (Sec. 4.1 "Experimental Setups", training
+// strategy; App. A.6.1), which backpropagates through the chunk-wise
+// parallel form of Sec. 3.3.  Every supported shape, f32 or bf16 storage,
+// fp32 arithmetic, fp32 gradients.
+//
+// Per query t of head h, with the sets of the forward (window + visible
+// selected tokens SA_t, routed unselected tokens LA_t), weights
+// w_j = exp(s_j - m) on SA_t and exp(-m) kappa_j on LA_t
+// (kappa_j = phi_q(q_t) . phi_k(k_j)), l = sum w_j, o = sum w_j v_j / l and
+// D_t = dout_t . o:
+//   SA:  ds_j = (w_j / l)(dout_t . v_j - D_t)
+//        dq_t += tau ds_j k_j,  dk_j += tau ds_j q_t,  dv_j += (w_j / l) dout_t
+//   LA:  dkappa_j = c_t (dout_t . v_j - D_t)  with c_t = exp(-m) / l
+//        dphi_q(t) = c_t (S_t dout_t - D_t z_t)    S_t, z_t: the LA state t reads
+//        dphi_k(j) = U_j v_j - u_j,  dv_j = U_j^T phi_k(j)
+//        with U_j = sum over t >= j + W (all heads of the group) of
+//        c_t phi_q(t) dout_t^T and u_j = sum c_t D_t phi_q(t): a suffix sum
+//        over query chunks plus the queries of one partial chunk.
+// Then the NP-Map's vector-Jacobian product carries dphi to x and to P.
+//
+// Kernels, in launch order:
+//   bwd_route_kernel   route flags and a clean ascending selected list per
+//                      chunk from the caller's selection
+//   (phi, la_chunk, la_scan of the forward: phi_q, phi_k and the LA prefix)
+//   bwd_query_kernel   one wave per (b, t, h): forward statistics m, l, D_t
+//                      recomputed, dq's softmax part, dphi_q
+//   bwd_uchunk_kernel  per query chunk: sum of c_t phi_q dout^T and c_t D_t phi_q
+//   bwd_suffix_kernel  inclusive suffix of those sums over chunks
+//   bwd_key_kernel     one wave per (b, j, g): dk's softmax part, dv, dphi_k
+//   np_vjp_kernel      NP-Map backward per (token, head): dx += ..., du
+//   dw_partial_kernel  dP = sum du x^T over a slice of tokens
+//   dw_reduce_kernel   sum of the slices
+#include "device_common.h"
+#include "launch.h"
+
+namespace still {
+
+namespace {
+
+constexpr float kNegInfB = -__builtin_inff();
+
+__global__ __launch_bounds__(256) void bwd_route_kernel(const int32_t* __restrict__ sel_in,
+                                                        uint8_t* __restrict__ route,
+                                                        int32_t* __restrict__ selw, Dims D) {
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    extern __shared__ int flag[];
+    const int c0 = c * D.C, n = min(D.C, D.N - c0);
+    uint8_t* rt = route + ((size_t)b * D.Hkv + g) * D.N + c0;
+    if (D.lam == 0 || n < D.C) {
+        const uint8_t f = D.lam == 0 ? kRouteLA : kPending;
+        for (int i = threadIdx.x; i < n; i += blockDim.x) rt[i] = f;
+        return;
+    }
+    for (int i = threadIdx.x; i < n; i += blockDim.x) flag[i] = 0;
+    __syncthreads();
+    const size_t row = (((size_t)b * D.Hkv + g) * D.n_full + c) * D.lam;
+    for (int i = threadIdx.x; i < D.lam; i += blockDim.x) {
+        const int pos = sel_in[row + i];
+        if (pos >= c0 && pos < c0 + D.C) flag[pos - c0] = 1;  // other entries are ignored
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) rt[i] = flag[i] ? kRouteSA : kRouteLA;
+    if (threadIdx.x == 0) {
+        int cnt = 0;
+        for (int i = 0; i < n && cnt < D.lam; ++i)
+            if (flag[i]) selw[row + cnt++] = c0 + i;
+        for (; cnt < D.lam; ++cnt) selw[row + cnt] = -1;
+    }
+}
+
+// One wave per query (b, t, h).  Lane owns output dims and features
+// lane + 64 p.  stat[(b, t, h)] = (m, l, D_t).
+template <typename T, int DD>
+__global__ __launch_bounds__(64) void bwd_query_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
+    const uint8_t* __restrict__ route, const int32_t* __restrict__ selw,
+    const float* __restrict__ lin, float* __restrict__ dq, float* __restrict__ dphiq,
+    float* __restrict__ stat, Dims D) {
+    constexpr int PL = DD / kWave;
+    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int g = h / D.G;
+    __shared__ float qs[DD];
+    __shared__ float fq[DD];
+    __shared__ float ds_[DD];
+    const size_t qoff = (((size_t)b * D.N + t) * D.Hq + h);
+    for (int i = lane; i < DD; i += kWave) {
+        qs[i] = to_f32(q[qoff * DD + i]);
+        fq[i] = phiq[qoff * DD + i];
+        ds_[i] = to_f32(dout[qoff * DD + i]);
+    }
+    __syncthreads();
+    auto krow = [&](int j) { return k + (((size_t)b * D.N + j) * D.Hkv + g) * DD; };
+    auto vrow = [&](int j) { return v + (((size_t)b * D.N + j) * D.Hkv + g) * DD; };
+    auto dot_row = [&](const float* a, const T* r) {
+        float x = 0.f;
+        for (int i = 0; i < DD; ++i) x = fmaf(a[i], to_f32(r[i]), x);
+        return x;
+    };
+
+    // ---- forward statistics (the forward's read-out, repeated) ----
+    float acc[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) acc[p] = 0.f;
+    float l = 0.f, m = 0.f;
+    const int r_end = max(0, t - D.W + 1);  // routed tokens j < r_end
+    const int c_full = r_end / D.C;
+    const float* st = c_full >= 1
+        ? lin + (((size_t)b * D.Hkv + g) * D.T + (c_full - 1)) * (size_t)(DD * (DD + 1))
+        : nullptr;
+    if (st) {
+        for (int i = 0; i < DD; ++i) {
+            const float f = fq[i];
+#pragma unroll
+            for (int p = 0; p < PL; ++p) acc[p] = fmaf(f, st[i * DD + lane + kWave * p], acc[p]);
+        }
+        float lp = 0.f;
+        for (int i = lane; i < DD; i += kWave) lp = fmaf(fq[i], st[DD * DD + i], lp);
+        l = wave_sum(lp);
+    }
+    const uint8_t* rt = route + ((size_t)b * D.Hkv + g) * D.N;
+    for (int j0 = c_full * D.C; j0 < r_end; j0 += kWave) {
+        const int j = j0 + lane;
+        float w = 0.f;
+        if (j < r_end && rt[j] == kRouteLA) {
+            const float* pk = phik + (((size_t)b * D.N + j) * D.Hkv + g) * DD;
+            for (int i = 0; i < DD; ++i) w = fmaf(fq[i], pk[i], w);
+        }
+        l += wave_sum(w);
+        const int nb = min(kWave, r_end - j0);
+        for (int jj = 0; jj < nb; ++jj) {
+            const float wj = __shfl(w, jj, kWave);
+            if (wj != 0.f) {
+                const T* vr = vrow(j0 + jj);
+#pragma unroll
+                for (int p = 0; p < PL; ++p) acc[p] = fmaf(wj, to_f32(vr[lane + kWave * p]), acc[p]);
+            }
+        }
+    }
+    auto sa_fwd = [&](int jpos) {
+        const float s = jpos >= 0 ? D.tau * dot_row(qs, krow(jpos)) : kNegInfB;
+        const float m_new = fmaxf(m, wave_max(s));
+        const float sc = expf(m - m_new);
+        const float pj = jpos >= 0 ? expf(s - m_new) : 0.f;
+        l = l * sc + wave_sum(pj);
+#pragma unroll
+        for (int p = 0; p < PL; ++p) acc[p] *= sc;
+        for (int jj = 0; jj < kWave; ++jj) {
+            const int jp = __shfl(jpos, jj, kWave);
+            if (jp >= 0) {
+                const float pv = __shfl(pj, jj, kWave);
+                const T* vr = vrow(jp);
+#pragma unroll
+                for (int p = 0; p < PL; ++p) acc[p] = fmaf(pv, to_f32(vr[lane + kWave * p]), acc[p]);
+            }
+        }
+        m = m_new;
+    };
+    const int32_t* sel = selw + ((size_t)b * D.Hkv + g) * D.n_full * D.lam;
+    const int n_cand = D.lam > 0 ? min(D.n_full, (r_end + D.C - 1) / D.C) * D.lam : 0;
+    auto sel_pos = [&](int i) {
+        if (i >= n_cand) return -1;
+        const int pos = sel[i];
+        return pos < r_end ? pos : -1;  // -1 entries and not yet visible tokens
+    };
+    if (D.W > 0)
+        for (int j0 = max(0, t - D.W + 1); j0 <= t; j0 += kWave) sa_fwd(j0 + lane <= t ? j0 + lane : -1);
+    for (int i0 = 0; i0 < n_cand; i0 += kWave) sa_fwd(sel_pos(i0 + lane));
+
+    const float inv = 1.0f / l;
+    float dpart = 0.f;
+#pragma unroll
+    for (int p = 0; p < PL; ++p) dpart = fmaf(acc[p] * inv, ds_[lane + kWave * p], dpart);
+    const float Dt = wave_sum(dpart);
+
+    // ---- softmax part of dq ----
+    float dqa[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) dqa[p] = 0.f;
+    auto sa_bwd = [&](int jpos) {
+        float dsj = 0.f;
+        if (jpos >= 0) {
+            const float s = D.tau * dot_row(qs, krow(jpos));
+            const float pj = expf(s - m) * inv;
+            dsj = pj * (dot_row(ds_, vrow(jpos)) - Dt);
+        }
+        for (int jj = 0; jj < kWave; ++jj) {
+            const int jp = __shfl(jpos, jj, kWave);
+            if (jp >= 0) {
+                const float w = __shfl(dsj, jj, kWave);
+                const T* kr = krow(jp);
+#pragma unroll
+                for (int p = 0; p < PL; ++p) dqa[p] = fmaf(w, to_f32(kr[lane + kWave * p]), dqa[p]);
+            }
+        }
+    };
+    if (D.W > 0)
+        for (int j0 = max(0, t - D.W + 1); j0 <= t; j0 += kWave) sa_bwd(j0 + lane <= t ? j0 + lane : -1);
+    for (int i0 = 0; i0 < n_cand; i0 += kWave) sa_bwd(sel_pos(i0 + lane));
+#pragma unroll
+    for (int p = 0; p < PL; ++p) dq[qoff * DD + lane + kWave * p] = D.tau * dqa[p];
+
+    // ---- dphi_q = c (S_t dout - D_t z_t) ----
+    const float cf = expf(-m) * inv;
+    float dfq[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) dfq[p] = 0.f;
+    if (st) {
+#pragma unroll
+        for (int p = 0; p < PL; ++p) {
+            const int i = lane + kWave * p;
+            const float4* row = reinterpret_cast<const float4*>(st + (size_t)i * DD);
+            float x = 0.f;
+            for (int e4 = 0; e4 < DD / 4; ++e4) {
+                const float4 r = row[e4];
+                x = fmaf(r.x, ds_[4 * e4], x);
+                x = fmaf(r.y, ds_[4 * e4 + 1], x);
+                x = fmaf(r.z, ds_[4 * e4 + 2], x);
+                x = fmaf(r.w, ds_[4 * e4 + 3], x);
+            }
+            dfq[p] = x - Dt * st[DD * DD + i];
+        }
+    }
+    for (int j0 = c_full * D.C; j0 < r_end; j0 += kWave) {
+        const int j = j0 + lane;
+        float w = 0.f;
+        const bool la = j < r_end && rt[j] == kRouteLA;
+        if (la) w = dot_row(ds_, vrow(j)) - Dt;
+        const int nb = min(kWave, r_end - j0);
+        for (int jj = 0; jj < nb; ++jj) {
+            const int laj = __shfl((int)la, jj, kWave);
+            if (laj) {
+                const float wj = __shfl(w, jj, kWave);
+                const float* pk = phik + (((size_t)b * D.N + j0 + jj) * D.Hkv + g) * DD;
+#pragma unroll
+                for (int p = 0; p < PL; ++p) dfq[p] = fmaf(wj, pk[lane + kWave * p], dfq[p]);
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PL; ++p) dphiq[qoff * DD + lane + kWave * p] = cf * dfq[p];
+    if (lane == 0) {
+        stat[qoff * 4 + 0] = m;
+        stat[qoff * 4 + 1] = l;
+        stat[qoff * 4 + 2] = Dt;
+        stat[qoff * 4 + 3] = cf;
+    }
+}
+
+// Per query chunk c of (b, g): U[i][e] = sum over its queries t and the
+// group's heads of c_t phi_q[i] dout[e], u[i] = sum c_t D_t phi_q[i]
+// (same (d + 1) fd layout as the LA state).  Thread tid owns entries tid + 256 r.
+template <typename T, int DD>
+__global__ __launch_bounds__(256) void bwd_uchunk_kernel(const float* __restrict__ phiq,
+                                                         const T* __restrict__ dout,
+                                                         const float* __restrict__ stat,
+                                                         float* __restrict__ ust, Dims D) {
+    constexpr int E = DD * DD, PER = E / 256;
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    __shared__ float ph[32][DD];
+    __shared__ float dd[32][DD];
+    __shared__ float cd[32];
+    float acc[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) acc[r] = 0.f;
+    float uacc = 0.f;
+    const int c0 = c * D.C, n = min(D.C, D.N - c0) * D.G;  // (t, h) pairs
+    for (int r0 = 0; r0 < n; r0 += 32) {
+        const int nb = min(32, n - r0);
+        __syncthreads();
+        for (int x = tid; x < nb * DD; x += 256) {
+            const int rr = x / DD, i = x % DD, pr = r0 + rr;
+            const int t = c0 + pr / D.G, h = g * D.G + pr % D.G;
+            const size_t off = ((size_t)b * D.N + t) * D.Hq + h;
+            ph[rr][i] = stat[off * 4 + 3] * phiq[off * DD + i];
+            dd[rr][i] = to_f32(dout[off * DD + i]);
+            if (i == 0) cd[rr] = stat[off * 4 + 2];
+        }
+        __syncthreads();
+        for (int rr = 0; rr < nb; ++rr) {
+#pragma unroll
+            for (int r = 0; r < PER; ++r) {
+                const int e = tid + 256 * r;
+                acc[r] = fmaf(ph[rr][e / DD], dd[rr][e % DD], acc[r]);
+            }
+            if (tid < DD) uacc = fmaf(cd[rr], ph[rr][tid], uacc);
+        }
+    }
+    float* out = ust + (((size_t)b * D.Hkv + g) * D.T + c) * (size_t)(DD * (DD + 1));
+#pragma unroll
+    for (int r = 0; r < PER; ++r) out[tid + 256 * r] = acc[r];
+    if (tid < DD) out[E + tid] = uacc;
+}
+
+__global__ __launch_bounds__(256) void bwd_suffix_kernel(float* __restrict__ ust, Dims D) {
+    const int E1 = D.fd * (D.d + 1);
+    const int e = blockIdx.x * 256 + threadIdx.x, g = blockIdx.y, b = blockIdx.z;
+    if (e >= E1) return;
+    float* base = ust + ((size_t)b * D.Hkv + g) * D.T * (size_t)E1 + e;
+    float run = 0.f;
+    for (int c = D.T - 1; c >= 0; --c) {
+        run += base[(size_t)c * E1];
+        base[(size_t)c * E1] = run;
+    }
+}
+
+// One wave per key (b, j, g).  Lane owns dims / features lane + 64 p.
+template <typename T, int DD>
+__global__ __launch_bounds__(64) void bwd_key_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
+    const uint8_t* __restrict__ route, const float* __restrict__ stat,
+    const float* __restrict__ ust, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ dphik, Dims D) {
+    constexpr int PL = DD / kWave;
+    const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    __shared__ float ks[DD];
+    __shared__ float vs[DD];
+    __shared__ float fk[DD];
+    const size_t koff = ((size_t)b * D.N + j) * D.Hkv + g;
+    for (int i = lane; i < DD; i += kWave) {
+        ks[i] = to_f32(k[koff * DD + i]);
+        vs[i] = to_f32(v[koff * DD + i]);
+        fk[i] = phik[koff * DD + i];
+    }
+    __syncthreads();
+    float dka[PL], dva[PL], dfa[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) dka[p] = dva[p] = dfa[p] = 0.f;
+    const uint8_t rj = route[((size_t)b * D.Hkv + g) * D.N + j];
+    const int G = D.G;
+    auto qoff = [&](int t, int h) { return ((size_t)b * D.N + t) * D.Hq + h; };
+
+    // softmax queries: the window's t in [j, j + W - 1], and every later t
+    // when j is selected
+    const int t_last = rj == kRouteSA ? D.N - 1 : min(D.N - 1, j + D.W - 1);
+    const int n_sa = D.W > 0 ? (t_last - j + 1) * G : 0;
+    for (int i0 = 0; i0 < n_sa; i0 += kWave) {
+        const int pr = i0 + lane;
+        float dsj = 0.f, pj = 0.f;
+        if (pr < n_sa) {
+            const size_t o = qoff(j + pr / G, g * G + pr % G);
+            const T* qr = q + o * DD;
+            const T* dr = dout + o * DD;
+            float s = 0.f, dv_ = 0.f;
+            for (int i = 0; i < DD; ++i) {
+                s = fmaf(ks[i], to_f32(qr[i]), s);
+                dv_ = fmaf(vs[i], to_f32(dr[i]), dv_);
+            }
+            pj = expf(D.tau * s - stat[o * 4 + 0]) / stat[o * 4 + 1];
+            dsj = pj * (dv_ - stat[o * 4 + 2]);
+        }
+        const int nb = min(kWave, n_sa - i0);
+        for (int jj = 0; jj < nb; ++jj) {
+            const int pr2 = i0 + jj;
+            const size_t o = qoff(j + pr2 / G, g * G + pr2 % G);
+            const float w = __shfl(dsj, jj, kWave), pv = __shfl(pj, jj, kWave);
+            const T* qr = q + o * DD;
+            const T* dr = dout + o * DD;
+#pragma unroll
+            for (int p = 0; p < PL; ++p) {
+                dka[p] = fmaf(w, to_f32(qr[lane + kWave * p]), dka[p]);
+                dva[p] = fmaf(pv, to_f32(dr[lane + kWave * p]), dva[p]);
+            }
+        }
+    }
+    // linear queries: every t >= j + W (j routed, not selected)
+    const int t0 = j + D.W;
+    if (rj == kRouteLA && t0 <= D.N - 1) {
+        const int c0 = t0 / D.C;
+        if (c0 + 1 < D.T) {
+            const float* U = ust + (((size_t)b * D.Hkv + g) * D.T + c0 + 1) * (size_t)(DD * (DD + 1));
+            for (int i = 0; i < DD; ++i) {
+                const float f = fk[i];
+#pragma unroll
+                for (int p = 0; p < PL; ++p) dva[p] = fmaf(f, U[(size_t)i * DD + lane + kWave * p], dva[p]);
+            }
+#pragma unroll
+            for (int p = 0; p < PL; ++p) {
+                const int i = lane + kWave * p;
+                const float4* row = reinterpret_cast<const float4*>(U + (size_t)i * DD);
+                float x = 0.f;
+                for (int e4 = 0; e4 < DD / 4; ++e4) {
+                    const float4 r = row[e4];
+                    x = fmaf(r.x, vs[4 * e4], x);
+                    x = fmaf(r.y, vs[4 * e4 + 1], x);
+                    x = fmaf(r.z, vs[4 * e4 + 2], x);
+                    x = fmaf(r.w, vs[4 * e4 + 3], x);
+                }
+                dfa[p] = x - U[DD * DD + i];
+            }
+        }
+        const int t1 = min(D.N - 1, (c0 + 1) * D.C - 1);
+        const int n_la = (t1 - t0 + 1) * G;
+        for (int i0 = 0; i0 < n_la; i0 += kWave) {
+            const int pr = i0 + lane;
+            float wk_ = 0.f, wf = 0.f;
+            if (pr < n_la) {
+                const size_t o = qoff(t0 + pr / G, g * G + pr % G);
+                const float* fr = phiq + o * DD;
+                const T* dr = dout + o * DD;
+                float kap = 0.f, dv_ = 0.f;
+                for (int i = 0; i < DD; ++i) {
+                    kap = fmaf(fk[i], fr[i], kap);
+                    dv_ = fmaf(vs[i], to_f32(dr[i]), dv_);
+                }
+                const float cf = stat[o * 4 + 3];
+                wk_ = cf * kap;
+                wf = cf * (dv_ - stat[o * 4 + 2]);
+            }
+            const int nb = min(kWave, n_la - i0);
+            for (int jj = 0; jj < nb; ++jj) {
+                const int pr2 = i0 + jj;
+                const size_t o = qoff(t0 + pr2 / G, g * G + pr2 % G);
+                const float a = __shfl(wk_, jj, kWave), c = __shfl(wf, jj, kWave);
+                const float* fr = phiq + o * DD;
+                const T* dr = dout + o * DD;
+#pragma unroll
+                for (int p = 0; p < PL; ++p) {
+                    dva[p] = fmaf(a, to_f32(dr[lane + kWave * p]), dva[p]);
+                    dfa[p] = fmaf(c, fr[lane + kWave * p], dfa[p]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PL; ++p) {
+        const size_t e = koff * DD + lane + kWave * p;
+        dk[e] = D.tau * dka[p];
+        dv[e] = dva[p];
+        dphik[e] = dfa[p];
+    }
+}
+
+// NP-Map backward for x[tok, h] with projection P[h / hpp] (fd / 2 <= 64
+// rows, one per lane):
+//   a = softmax(z), bb = softmax(-z):  dz = a (da - <da, a>) - bb (db - <db, bb>)
+//   z = ||x|| uh, uh = u / ||u||:       d||x|| = <dz, uh>, duh = ||x|| dz
+//   du = (duh - <duh, uh> uh) / ||u||   (zero where u = 0: z is pinned to 0)
+//   dx = d||x|| x / ||x|| + P^T du  (added into dx_out),  du stored for dP
+template <typename T, int DD>
+__global__ __launch_bounds__(64) void np_vjp_kernel(const T* __restrict__ x,
+                                                    const float* __restrict__ Pall,
+                                                    const float* __restrict__ dphi,
+                                                    float* __restrict__ dx_out,
+                                                    float* __restrict__ du_out, int H, int hpp,
+                                                    int fd) {
+    constexpr int PL = DD / kWave;
+    const int tok = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+    const int half = fd / 2;
+    __shared__ float xs[DD];
+    __shared__ float dus[64];
+    const size_t row = (size_t)tok * H + h;
+    for (int i = lane; i < DD; i += kWave) xs[i] = to_f32(x[row * DD + i]);
+    __syncthreads();
+    const float* P = Pall + (size_t)(h / hpp) * half * DD;
+    float ss = 0.f;
+    for (int i = lane; i < DD; i += kWave) ss = fmaf(xs[i], xs[i], ss);
+    const float nx = sqrtf(wave_sum(ss));
+    const bool act = lane < half;
+    float u = 0.f;
+    if (act) {
+        const float* pr = P + (size_t)lane * DD;
+        for (int i = 0; i < DD; ++i) u = fmaf(pr[i], xs[i], u);
+    }
+    const float nu = sqrtf(wave_sum(u * u));
+    const float uh = nu > 0.f ? u / nu : 0.f;
+    const float z = nx * uh;
+    const float m1 = wave_max(act ? z : kNegInfB), m2 = wave_max(act ? -z : kNegInfB);
+    const float e1 = act ? expf(z - m1) : 0.f, e2 = act ? expf(-z - m2) : 0.f;
+    const float a = e1 / wave_sum(e1), bb = e2 / wave_sum(e2);
+    const float da = act ? dphi[row * fd + lane] : 0.f;
+    const float db = act ? dphi[row * fd + half + lane] : 0.f;
+    const float sa = wave_sum(da * a), sb = wave_sum(db * bb);
+    const float dz = act ? a * (da - sa) - bb * (db - sb) : 0.f;
+    const float dnx = nu > 0.f ? wave_sum(dz * uh) : 0.f;
+    const float duh = nx * dz;
+    const float proj = wave_sum(duh * uh);
+    const float du = (nu > 0.f && act) ? (duh - proj * uh) / nu : 0.f;
+    dus[lane] = du;
+    __syncthreads();
+    const float rn = nx > 0.f ? dnx / nx : 0.f;
+#pragma unroll
+    for (int p = 0; p < PL; ++p) {
+        const int e = lane + kWave * p;
+        float acc = rn * xs[e];
+        for (int i = 0; i < half; ++i) acc = fmaf(dus[i], P[(size_t)i * DD + e], acc);
+        dx_out[row * DD + e] += acc;
+    }
+    if (act) du_out[row * half + lane] = du;
+}
+
+// Partial dP[g] over token slice s: thread e owns column e of every row.
+template <typename T, int DD>
+__global__ __launch_bounds__(DD) void dw_partial_kernel(const T* __restrict__ x,
+                                                        const float* __restrict__ du,
+                                                        float* __restrict__ part, int ntok, int H,
+                                                        int hpp, int half, int nslice) {
+    const int g = blockIdx.x, sl = blockIdx.y, e = threadIdx.x;
+    const int per = (ntok + nslice - 1) / nslice;
+    const int tk0 = sl * per, tk1 = min(ntok, tk0 + per);
+    float acc[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) acc[i] = 0.f;
+    for (int tk = tk0; tk < tk1; ++tk) {
+        for (int hh = 0; hh < hpp; ++hh) {
+            const size_t row = (size_t)tk * H + g * hpp + hh;
+            const float xe = to_f32(x[row * DD + e]);
+            const float* dr = du + row * half;
+#pragma unroll
+            for (int i = 0; i < 64; ++i)
+                if (i < half) acc[i] = fmaf(dr[i], xe, acc[i]);
+        }
+    }
+    float* out = part + (((size_t)sl * gridDim.x + g) * half) * DD + e;
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+        if (i < half) out[(size_t)i * DD] = acc[i];
+}
+
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part,
+                                                        float* __restrict__ dw, int n, int nslice) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    float s = 0.f;
+    for (int sl = 0; sl < nslice; ++sl) s += part[(size_t)sl * n + e];
+    dw[e] = s;
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int n) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e < n) p[e] = 0.f;
+}
+
+template <typename T, int DD>
+hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s, BwdMark mark) {
+    const T* q = reinterpret_cast<const T*>(a.q);
+    const T* k = reinterpret_cast<const T*>(a.k);
+    const T* v = reinterpret_cast<const T*>(a.v);
+    const T* dout = reinterpret_cast<const T*>(a.dout);
+    hipError_t e;
+#define STILL_STEP(name, launch)                       \
+    do {                                               \
+        if ((e = mark.fn(mark.ctx, name)) != hipSuccess) return e; \
+        launch;                                        \
+        if ((e = hipGetLastError()) != hipSuccess) return e; \
+    } while (0)
+    STILL_STEP("bwd_route", hipLaunchKernelGGL(bwd_route_kernel, dim3(D.T, D.Hkv, D.B), dim3(256),
+                                               (size_t)D.C * sizeof(int), s, a.sel_idx, w.route,
+                                               w.selw, D));
+    if ((e = mark.fn(mark.ctx, "phi_q")) != hipSuccess) return e;
+    if ((e = launch_phi(D, a.q, D.Hq, D.G, a.wq, w.phiq, s)) != hipSuccess) return e;
+    if ((e = mark.fn(mark.ctx, "phi_k")) != hipSuccess) return e;
+    if ((e = launch_phi(D, a.k, D.Hkv, 1, a.wk, w.phik, s)) != hipSuccess) return e;
+    if ((e = mark.fn(mark.ctx, "la_chunk")) != hipSuccess) return e;
+    if ((e = launch_la_chunks(D, w.phik, a.v, w.route, w.lin, s)) != hipSuccess) return e;
+    if ((e = mark.fn(mark.ctx, "la_scan")) != hipSuccess) return e;
+    if ((e = launch_la_scan(D, w.lin, -1, nullptr, nullptr, s)) != hipSuccess) return e;
+    STILL_STEP("bwd_query",
+               hipLaunchKernelGGL((bwd_query_kernel<T, DD>), dim3(D.N, D.Hq, D.B), dim3(64), 0, s,
+                                  q, k, v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.dq,
+                                  w.dphiq, w.stat, D));
+    STILL_STEP("bwd_uchunk",
+               hipLaunchKernelGGL((bwd_uchunk_kernel<T, DD>), dim3(D.T, D.Hkv, D.B), dim3(256), 0,
+                                  s, w.phiq, dout, w.stat, w.ust, D));
+    STILL_STEP("bwd_suffix",
+               hipLaunchKernelGGL(bwd_suffix_kernel, dim3((D.fd * (D.d + 1) + 255) / 256, D.Hkv, D.B),
+                                  dim3(256), 0, s, w.ust, D));
+    STILL_STEP("bwd_key",
+               hipLaunchKernelGGL((bwd_key_kernel<T, DD>), dim3(D.N, D.Hkv, D.B), dim3(64), 0, s,
+                                  q, k, v, dout, w.phiq, w.phik, w.route, w.stat, w.ust, a.dk,
+                                  a.dv, w.dphik, D));
+    const int ntok = D.B * D.N, half = D.fd / 2;
+    STILL_STEP("np_vjp_q",
+               hipLaunchKernelGGL((np_vjp_kernel<T, DD>), dim3(ntok, D.Hq), dim3(64), 0, s, q,
+                                  a.wq, w.dphiq, a.dq, w.duq, D.Hq, D.G, D.fd));
+    STILL_STEP("np_vjp_k",
+               hipLaunchKernelGGL((np_vjp_kernel<T, DD>), dim3(ntok, D.Hkv), dim3(64), 0, s, k,
+                                  a.wk, w.dphik, a.dk, w.duk, D.Hkv, 1, D.fd));
+    STILL_STEP("dw_q",
+               hipLaunchKernelGGL((dw_partial_kernel<T, DD>), dim3(D.Hkv, w.nslice), dim3(DD), 0, s,
+                                  q, w.duq, w.dwpart, ntok, D.Hq, D.G, half, w.nslice));
+    const int nw = D.Hkv * half * DD;
+    STILL_STEP("dw_q_reduce", hipLaunchKernelGGL(dw_reduce_kernel, dim3((nw + 255) / 256), dim3(256),
+                                                 0, s, w.dwpart, a.dwq, nw, w.nslice));
+    STILL_STEP("dw_k",
+               hipLaunchKernelGGL((dw_partial_kernel<T, DD>), dim3(D.Hkv, w.nslice), dim3(DD), 0, s,
+                                  k, w.duk, w.dwpart, ntok, D.Hkv, 1, half, w.nslice));
+    STILL_STEP("dw_k_reduce", hipLaunchKernelGGL(dw_reduce_kernel, dim3((nw + 255) / 256), dim3(256),
+                                                 0, s, w.dwpart, a.dwk, nw, w.nslice));
+#undef STILL_STEP
+    return hipSuccess;
+}
+
+}  // namespace
+
+int bwd_launch_count() { return 15; }
+
+hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s,
+                      BwdMark mark) {
+    if (D.d == 128) return D.bf16 ? bwd_t<__bf16, 128>(D, a, w, s, mark) : bwd_t<float, 128>(D, a, w, s, mark);
+    return D.bf16 ? bwd_t<__bf16, 64>(D, a, w, s, mark) : bwd_t<float, 64>(D, a, w, s, mark);
+}
+
+hipError_t launch_zero(float* p, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace still

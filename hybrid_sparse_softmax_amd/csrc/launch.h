@@ -120,4 +120,32 @@ hipError_t launch_fast_decode(const Dims& D, const void* q, const void* k, const
                               const float* wq, const float* wk, const CacheView& c, float* ws,
                               int nsplit, void* out, int phase, hipStream_t s);  // phase 0, then 1
 
+// ---- backward (general kernels; routing held fixed) ----------------------
+struct BwdArgs {
+    const void *q, *k, *v, *dout;       // dtype, layouts of the forward
+    const float *wq, *wk;               // [Hkv, fd/2, d]
+    const int32_t* sel_idx;             // [B, Hkv, n_full, lam] the forward's selection
+    float *dq, *dk, *dv, *dwq, *dwk;    // fp32 gradients, overwritten
+};
+struct BwdWork {
+    float *phiq, *phik;   // [B, N, Hq | Hkv, fd]
+    float* lin;           // [B, Hkv, T, fd (d + 1)] LA prefix states
+    float* stat;          // [B, N, Hq, 4] m, l, D_t, exp(-m) / l
+    float *dphiq, *dphik; // [B, N, Hq | Hkv, fd]
+    float* ust;           // [B, Hkv, T, fd (d + 1)] suffix sums of c phi_q dout^T, c D phi_q
+    float *duq, *duk;     // [B, N, Hq | Hkv, fd / 2]
+    float* dwpart;        // [nslice, Hkv, fd / 2, d]
+    uint8_t* route;       // [B, Hkv, N]
+    int32_t* selw;        // [B, Hkv, n_full, lam] ascending, -1 padded
+    int nslice;
+};
+// called before each launch with the kernel's name (per-launch events)
+struct BwdMark {
+    hipError_t (*fn)(void* ctx, const char* name);
+    void* ctx;
+};
+int bwd_launch_count();
+hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s, BwdMark mark);
+hipError_t launch_zero(float* p, int n, hipStream_t s);
+
 }  // namespace still

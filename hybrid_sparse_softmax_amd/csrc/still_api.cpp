@@ -362,6 +362,96 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
     return STILL_OK;
 }
 
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+static int bwd_slices(const Dims& D) {
+    // token slices of the projection-gradient sums: about 512 blocks in all
+    const int64_t ntok = (int64_t)D.B * D.N;
+    int64_t n = (512 + D.Hkv - 1) / D.Hkv;
+    if (n > ntok) n = ntok;
+    return n < 1 ? 1 : (int)n;
+}
+
+static BwdWork carve_bwd(const Dims& D, Carver& cv) {
+    BwdWork w;
+    const size_t BN = (size_t)D.B * D.N, BG = (size_t)D.B * D.Hkv;
+    const size_t E1 = (size_t)D.fd * (D.d + 1);
+    w.nslice = bwd_slices(D);
+    w.phiq = cv.take<float>(BN * D.Hq * D.fd);
+    w.phik = cv.take<float>(BN * D.Hkv * D.fd);
+    w.lin = cv.take<float>(BG * D.T * E1);
+    w.stat = cv.take<float>(BN * D.Hq * 4);
+    w.dphiq = cv.take<float>(BN * D.Hq * D.fd);
+    w.dphik = cv.take<float>(BN * D.Hkv * D.fd);
+    w.ust = cv.take<float>(BG * D.T * E1);
+    w.duq = cv.take<float>(BN * D.Hq * (D.fd / 2));
+    w.duk = cv.take<float>(BN * D.Hkv * (D.fd / 2));
+    w.dwpart = cv.take<float>((size_t)w.nslice * D.Hkv * (D.fd / 2) * D.d);
+    w.route = cv.take<uint8_t>(BG * D.N);
+    w.selw = cv.take<int32_t>(BG * D.n_full * D.lam);
+    return w;
+}
+
+static size_t bwd_bytes(const Dims& D) {
+    Carver cv(nullptr);
+    carve_bwd(D, cv);
+    return cv.off + 256;
+}
+
+struct MarkCtx {
+    Timeline* tl;
+    hipStream_t s;
+};
+static hipError_t mark_launch(void* ctx, const char* name) {
+    MarkCtx* m = static_cast<MarkCtx*>(ctx);
+    return m->tl->mark(m->s, name);
+}
+
+static int bwd(const still_shape* sh, const void* q, const void* k, const void* v,
+               const float* wq, const float* wk, const int32_t* sel_idx, const void* dout,
+               float* dq, float* dk, float* dv, float* dwq, float* dwk, void* ws,
+               size_t ws_bytes, hipStream_t s, Timeline& tl) {
+    int st = check_shape(sh, false);
+    if (st) return st;
+    const Dims D = make_dims(sh, sh->seqlen);
+    const int nw = D.Hkv * (D.fd / 2) * D.d;
+    if (D.B == 0 || D.N == 0) {  // no tokens: the projections get zero gradient
+        if (dwq) STILL_TRY(launch_zero(dwq, nw, s));
+        if (dwk) STILL_TRY(launch_zero(dwk, nw, s));
+        return STILL_OK;
+    }
+    if (!q || !k || !v || !wq || !wk || !dout || !dq || !dk || !dv || !dwq || !dwk)
+        return STILL_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, wq, wk, dout, dq, dk, dv, dwq, dwk};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return STILL_ERR_INVALID_ARG;
+    if (D.lam > 0 && D.n_full > 0 && (!sel_idx || (reinterpret_cast<uintptr_t>(sel_idx) & 3u)))
+        return STILL_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < bwd_bytes(D)) return STILL_ERR_WORKSPACE;
+    if (tl.ev && tl.max_ev < bwd_launch_count() + 1) return STILL_ERR_INVALID_ARG;
+    void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    Carver cv(wsa);
+    const BwdWork w = carve_bwd(D, cv);
+    BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.wq = wq;
+    a.wk = wk;
+    a.sel_idx = sel_idx;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dwq = dwq;
+    a.dwk = dwk;
+    MarkCtx mc{&tl, s};
+    STILL_TRY(launch_bwd(D, a, w, s, BwdMark{mark_launch, &mc}));
+    STILL_TRY(tl.end(s));
+    return STILL_OK;
+}
+
 }  // namespace still
 
 // ---------------------------------------------------------------------------
@@ -467,6 +557,42 @@ int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q
     still::Timeline tl;
     return still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, workspace, workspace_bytes,
                          stream, tl, pos_dev, max_pos);
+}
+
+int still_bwd_workspace_size(const still_shape* shape, size_t* bytes) {
+    if (!bytes) return STILL_ERR_INVALID_ARG;
+    const int st = still::check_shape(shape, false);
+    if (st) return st;
+    *bytes = still::bwd_bytes(still::make_dims(shape, shape->seqlen));
+    return STILL_OK;
+}
+
+int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k, const void* v,
+                          const float* wphi_q, const float* wphi_k, const int32_t* sel_idx,
+                          const void* dout, float* dq, float* dk, float* dv, float* dwphi_q,
+                          float* dwphi_k, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    still::Timeline tl;
+    return still::bwd(shape, q, k, v, wphi_q, wphi_k, sel_idx, dout, dq, dk, dv, dwphi_q, dwphi_k,
+                      workspace, workspace_bytes, stream, tl);
+}
+
+int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const void* k,
+                                const void* v, const float* wphi_q, const float* wphi_k,
+                                const int32_t* sel_idx, const void* dout, float* dq, float* dk,
+                                float* dv, float* dwphi_q, float* dwphi_k, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                                int32_t max_events, int32_t* n_launches,
+                                const char** kernel_names_opt) {
+    if (!events || !n_launches || max_events < 1) return STILL_ERR_INVALID_ARG;
+    still::Timeline tl;
+    tl.ev = events;
+    tl.max_ev = max_events;
+    tl.names = kernel_names_opt;
+    const int st = still::bwd(shape, q, k, v, wphi_q, wphi_k, sel_idx, dout, dq, dk, dv, dwphi_q,
+                              dwphi_k, workspace, workspace_bytes, stream, tl);
+    *n_launches = tl.n;
+    return st;
 }
 
 }  // extern "C"

@@ -30,6 +30,7 @@ EXPORTED = (
     "still_decode_workspace_size", "still_hybrid_attn_decode_step",
     "still_hybrid_attn_fwd_timed", "still_hybrid_attn_decode_step_timed",
     "still_hybrid_attn_decode_step_ragged",
+    "still_bwd_workspace_size", "still_hybrid_attn_bwd", "still_hybrid_attn_bwd_timed",
 )
 
 
@@ -86,7 +87,14 @@ def lib() -> ct.CDLL:
         L.still_hybrid_attn_decode_step_ragged.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
                                                            ct.POINTER(CacheStruct), vp, ct.c_int64,
                                                            vp, vp, sz, vp]
+        L.still_bwd_workspace_size.restype = ct.c_int
+        L.still_bwd_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
+        L.still_hybrid_attn_bwd.restype = ct.c_int
+        L.still_hybrid_attn_bwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, sz, vp]
         ev = [ct.POINTER(ct.c_void_p), ct.c_int32, ct.POINTER(ct.c_int32), ct.POINTER(ct.c_char_p)]
+        L.still_hybrid_attn_bwd_timed.restype = ct.c_int
+        L.still_hybrid_attn_bwd_timed.argtypes = L.still_hybrid_attn_bwd.argtypes + ev
         L.still_hybrid_attn_fwd_timed.restype = ct.c_int
         L.still_hybrid_attn_fwd_timed.argtypes = L.still_hybrid_attn_fwd.argtypes + ev
         L.still_hybrid_attn_decode_step_timed.restype = ct.c_int
@@ -140,6 +148,12 @@ def _check(status: int, where: str):
 def fwd_workspace_size(shape: Shape) -> int:
     n = ct.c_size_t(0)
     _check(lib().still_fwd_workspace_size(ct.byref(shape), ct.byref(n)), "still_fwd_workspace_size")
+    return n.value
+
+
+def bwd_workspace_size(shape: Shape) -> int:
+    n = ct.c_size_t(0)
+    _check(lib().still_bwd_workspace_size(ct.byref(shape), ct.byref(n)), "still_bwd_workspace_size")
     return n.value
 
 
@@ -313,3 +327,40 @@ def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.T
         int(max_pos), _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
         "still_hybrid_attn_decode_step_ragged")
     return out
+
+
+def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6,
+        softmax_scale=0.0, workspace=None, timer: LaunchTimer | None = None) -> dict:
+    """still_hybrid_attn_bwd: gradients of sum(dout * out) for the forward
+    with the same arguments, under the routing sel_idx [B, Hkv, N/C, lambda]
+    (the forward's sel_idx output; None when there is nothing selected).
+    Returns dict(dq, dk, dv, dwphi_q, dwphi_k), all fp32."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
+                    chunk=chunk, topk=topk, eps=eps, softmax_scale=softmax_scale, dtype=q.dtype,
+                    feat_dim=2 * wphi_q.shape[1])
+    _expect(q, "q", q.dtype, (B, N, Hq, d))
+    _expect(k, "k", q.dtype, (B, N, Hkv, d))
+    _expect(v, "v", q.dtype, (B, N, Hkv, d))
+    _expect(dout, "dout", q.dtype, (B, N, Hq, d))
+    _expect(wphi_q, "wphi_q", torch.float32, (Hkv, wphi_q.shape[1], d))
+    _expect(wphi_k, "wphi_k", torch.float32, (Hkv, wphi_q.shape[1], d))
+    if sel_idx is not None:
+        _expect(sel_idx, "sel_idx", torch.int32, (B, Hkv, N // chunk, min(topk, chunk)))
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32),
+           "dv": torch.empty(v.shape, **f32), "dwphi_q": torch.empty(wphi_q.shape, **f32),
+           "dwphi_k": torch.empty(wphi_k.shape, **f32)}
+    nbytes = bwd_workspace_size(sh)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(sel_idx),
+            _ptr(dout), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dwphi_q"]),
+            _ptr(res["dwphi_k"]), _ptr(workspace), workspace.numel(), _stream()]
+    if timer is None:
+        _check(lib().still_hybrid_attn_bwd(*args), "still_hybrid_attn_bwd")
+    else:
+        _check(lib().still_hybrid_attn_bwd_timed(*args, *timer.args()), "still_hybrid_attn_bwd_timed")
+    return res

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define STILL_ABI_VERSION 2
+#define STILL_ABI_VERSION 3
 
 typedef enum {
     STILL_OK = 0,
@@ -227,7 +227,40 @@ int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q
                                          void* out, void* workspace, size_t workspace_bytes,
                                          hipStream_t stream);
 
-/* Instrumented forms of the two entry points, for measurement (they compute
+/* Bytes of device workspace still_hybrid_attn_bwd needs for `shape`. */
+int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
+
+/* Backward pass of still_hybrid_attn_fwd: gradients of
+ * L = sum(dout * out) with respect to q, k, v and the two NP-Map
+ * projections, for the training the paper's linearization runs through the
+ * chunk-wise parallel form (Sec. 3.3; Sec. 4.1 "Experimental Setups",
+ * training strategy; App. A.6.1).  The routing is held fixed: the selection
+ * is a constant mask, so nothing flows through the scores or the top-k, and
+ * M = max(0, max logit) cancels between numerator and denominator.  Where
+ * an NP-Map projection P x is zero the map is taken as locally constant
+ * (zero gradient).
+ *   q, k, v, wphi_q, wphi_k  as given to the forward, read only
+ *   sel_idx   [B, Hkv, N / C, min(topk, C)] int32, the forward's sel_idx
+ *             output (the routing to differentiate under); entries outside
+ *             their chunk, and repeats, are ignored.  May be NULL when
+ *             min(topk, C) == 0 or N < C.
+ *   dout      [B, N, Hq, d] dtype, the gradient of L w.r.t. out
+ *   dq        [B, N, Hq, d] fp32, written
+ *   dk, dv    [B, N, Hkv, d] fp32, written
+ *   dwphi_q, dwphi_k  [Hkv, d'/2, d] fp32, written
+ *   workspace >= still_bwd_workspace_size bytes of device memory
+ * Computed by the general kernels for every supported shape; the shape's
+ * routing-criterion and kernel flags are accepted and do not matter.  N == 0
+ * or B == 0 writes zeros to dwphi_q and dwphi_k (when not NULL) and nothing
+ * else.  Errors as for the forward; a missing sel_idx where it is needed is
+ * STILL_ERR_INVALID_ARG. */
+int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k, const void* v,
+                          const float* wphi_q, const float* wphi_k, const int32_t* sel_idx,
+                          const void* dout, float* dq, float* dk, float* dv, float* dwphi_q,
+                          float* dwphi_k, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Instrumented forms of the entry points, for measurement (they compute
  * exactly what the plain calls compute).  Before the i-th kernel launch the
  * call records events[i] on `stream`, and events[n] after the last launch,
  * so hipEventElapsedTime(events[i], events[i+1]) is launch i's duration on
@@ -249,6 +282,13 @@ int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q,
                                         hipStream_t stream, hipEvent_t* events,
                                         int32_t max_events, int32_t* n_launches,
                                         const char** kernel_names_opt);
+int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const void* k,
+                                const void* v, const float* wphi_q, const float* wphi_k,
+                                const int32_t* sel_idx, const void* dout, float* dq, float* dk,
+                                float* dv, float* dwphi_q, float* dwphi_k, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                                int32_t max_events, int32_t* n_launches,
+                                const char** kernel_names_opt);
 
 #ifdef __cplusplus
 }

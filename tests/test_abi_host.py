@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert S.abi_version() == 2
+    assert S.abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5):
         assert S.status_str(code) and S.status_str(code) != "unknown status"
     assert S.status_str(7) == "unknown status"
@@ -181,3 +181,38 @@ def test_ragged_decode_checks():
     c = fake_cache(64, 7)
     assert ragged_status(shape(seqlen=1, batch=0), c, FAKE, 100, ws_bytes=0, ptr=None) == S.STILL_OK
     assert c.pos == 7
+
+
+def bwd_status(sh, sel=FAKE, ws_bytes=1 << 40, ptr=FAKE, ws=FAKE, dw=FAKE):
+    return S.lib().still_hybrid_attn_bwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, sel, ptr, ptr, ptr,
+                                         ptr, dw, dw, ws, ws_bytes, None)
+
+
+def test_bwd_checks():
+    sh = shape()
+    need = S.bwd_workspace_size(sh)
+    assert need > 0 and S.bwd_workspace_size(shape(seqlen=4096)) > need
+    assert bwd_status(sh, ws_bytes=need - 1) == S.STILL_ERR_WORKSPACE
+    assert bwd_status(sh, ws=None) == S.STILL_ERR_WORKSPACE
+    # the routing to differentiate under is required once a chunk is complete
+    assert bwd_status(sh, sel=None) == S.STILL_ERR_INVALID_ARG
+    assert bwd_status(sh, sel=ct.c_void_p(0x1002)) == S.STILL_ERR_INVALID_ARG
+    assert bwd_status(shape(topk=0), sel=None, ws_bytes=16) == S.STILL_ERR_WORKSPACE
+    assert bwd_status(shape(seqlen=40), sel=None, ws_bytes=16) == S.STILL_ERR_WORKSPACE  # N < C
+    assert bwd_status(sh, ptr=None) == S.STILL_ERR_INVALID_ARG
+    assert bwd_status(sh, ptr=MISALIGNED) == S.STILL_ERR_INVALID_ARG
+    assert bwd_status(sh, dw=None) == S.STILL_ERR_INVALID_ARG
+    for kw, st in ((dict(n_q_heads=6, n_kv_heads=4), S.STILL_ERR_INVALID_ARG),
+                   (dict(head_dim=96), S.STILL_ERR_UNSUPPORTED)):
+        assert bwd_status(shape(**kw)) == st
+    timed = S.lib().still_hybrid_attn_bwd_timed
+    n = ct.c_int32(0)
+    evs = (ct.c_void_p * 4)()
+    # 15 launches need 16 events; too few is rejected before anything runs
+    assert timed(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, 1 << 40, None, evs, 4, ct.byref(n), None) == S.STILL_ERR_INVALID_ARG
+
+
+def test_bwd_empty_problem_without_projection_gradients_is_noop():
+    for kw in (dict(seqlen=0), dict(batch=0)):
+        assert bwd_status(shape(**kw), sel=None, ws=None, ws_bytes=0, ptr=None, dw=None) == S.STILL_OK

@@ -1,0 +1,150 @@
+"""GPU parity of the backward pass (gradients of sum(dout * out) w.r.t. q,
+k, v and both NP-Map projections, routing held fixed) against the float64
+oracle's bwd_direct, whole tensors, at sizes the oracle finishes in seconds
+(several chunks and a ragged tail), plus the method's degenerate cases and a
+property check at the 4K prefill size.
+
+The routing differentiated under is the GPU forward's own selection, handed
+to both sides, so selection near-ties cannot matter here.  Bar: rel-L2 of
+every gradient tensor <= 1e-4.  The gradients are fp32 sums of fp32 terms
+from the same (dtype-rounded) inputs the oracle gets in float64; the longest
+sums have a few thousand terms, whose rounding stays near 1e-6 relative, so
+1e-4 leaves two orders of magnitude of room while a wrong term, sign or
+index shows up at 1e-2 or more."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from parity import make_case, prepare, rel_l2, say, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 1e-4
+NAMES = (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dwphi_q", "dwq"), ("dwphi_k", "dwk"))
+
+CASES = {
+    "bf16_ragged_G2": (make_case("r", 1, 300, 4, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 31),
+    "f32_d64_W32_C32": (make_case("a", 2, 200, 2, 1, 64, 32, 32, 8, dtype="f32"), 32),
+    "f32_W_gt_C_G8": (make_case("b", 1, 150, 8, 1, 64, 48, 16, 4, dtype="f32"), 33),
+    "bf16_swa_la": (make_case("c", 1, 230, 4, 2, 128, 64, 64, 0), 34),
+    "f32_pure_linear": (make_case("d", 1, 130, 2, 1, 64, 0, 32, 0, dtype="f32"), 35),
+    "bf16_all_selected": (make_case("e", 1, 200, 4, 2, 128, 64, 64, 64), 36),
+    "bf16_short_no_chunk": (make_case("f", 2, 40, 4, 2, 128, 64, 64, 16), 37),
+    "bf16_single_token": (make_case("g", 1, 1, 4, 2, 128, 64, 64, 16), 38),
+}
+
+
+def run(gpu_lib, cfg, seed, corrupt=False):
+    raw = workloads.make_prefill(cfg, seed)
+    dt = torch_dtype(cfg["dtype"])
+    dev, ref = prepare(raw, dt)
+    dout = torch.from_numpy(workloads.make_grad_out(cfg, seed)).to(dt)
+    ref_dout = dout.double().numpy()
+    dout = dout.cuda().contiguous()
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    sel = None
+    if min(lam, C) > 0:
+        sel = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W,
+                          chunk=C, topk=lam, return_sel=True)["sel_idx"]
+    osel = None if sel is None else sel.cpu().numpy().astype(np.int64)
+    if corrupt and sel is not None and sel.shape[2] > 1:
+        # a repeated entry and an out-of-chunk entry are ignored by the library;
+        # the oracle gets the same routing with the bad entry as a repeat
+        bad = sel.clone()
+        bad[:, :, 0, 1] = bad[:, :, 0, 0]
+        bad[:, :, 1, 0] = 1 << 30
+        osel = bad.cpu().numpy().astype(np.int64)
+        osel[:, :, 1, 0] = osel[:, :, 1, 1]
+        sel = bad
+    g = gpu_lib.bwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], sel, dout,
+                    window=W, chunk=C, topk=lam)
+    torch.cuda.synchronize()
+    p = O.Params(window=W, chunk=C, topk=lam)
+    o = O.bwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"], ref_dout, p,
+                     sel_idx=osel)
+    return g, o
+
+
+def compare(g, o):
+    errs = {}
+    for gname, oname in NAMES:
+        x = g[gname].double().cpu().numpy()
+        assert np.isfinite(x).all(), gname
+        errs[gname] = rel_l2(x, o[oname]) if np.any(o[oname]) else float(np.abs(x).max())
+    say("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= GRAD_TOL, (k, v)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_bwd_matches_oracle(gpu_lib, name):
+    cfg, seed = CASES[name]
+    say(f"[bwd] case={name} shape={workloads.shape_of(cfg)} seed={seed}")
+    g, o = run(gpu_lib, cfg, seed)
+    compare(g, o)
+
+
+def test_bwd_ignores_repeated_and_foreign_selection_entries(gpu_lib):
+    cfg, seed = CASES["bf16_ragged_G2"]
+    say(f"[bwd] corrupted selection shape={workloads.shape_of(cfg)} seed={seed}")
+    g, o = run(gpu_lib, cfg, seed, corrupt=True)
+    compare(g, o)
+
+
+def test_bwd_is_deterministic(gpu_lib):
+    cfg, seed = CASES["bf16_ragged_G2"]
+    raw = workloads.make_prefill(cfg, seed)
+    dev, _ = prepare(raw, torch.bfloat16)
+    dout = torch.from_numpy(workloads.make_grad_out(cfg, seed)).to(torch.bfloat16).cuda()
+    sel = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=64,
+                      chunk=64, topk=16, return_sel=True)["sel_idx"]
+    runs = [gpu_lib.bwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], sel, dout,
+                        window=64, chunk=64, topk=16) for _ in range(2)]
+    torch.cuda.synchronize()
+    for key in runs[0]:
+        assert torch.equal(runs[0][key], runs[1][key]), key
+
+
+def test_bwd_empty_sequence_zeroes_projection_gradients(gpu_lib):
+    q = torch.zeros((1, 0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((2, 64, 128), dtype=torch.float32, device="cuda")
+    g = gpu_lib.bwd(q, k, k, w, w, None, q, window=64, chunk=64, topk=16)
+    torch.cuda.synchronize()
+    assert g["dq"].shape == (1, 0, 4, 128)
+    assert torch.count_nonzero(g["dwphi_q"]) == 0 and torch.count_nonzero(g["dwphi_k"]) == 0
+
+
+def test_bwd_all_selected_at_4k_is_causal_softmax_gradient(gpu_lib):
+    """At the 4K prefill shape (32 / 8 heads, d 128) with every routed token
+    selected (topk = C) the operator is causal softmax attention, a property
+    that holds at any size: its gradients must be those of torch's SDPA
+    (float32 autograd on the GPU) and the projections get none."""
+    cfg = dict(workloads.CONFIGS["prefill_4k"], topk=64)
+    seed = workloads.seed_of("prefill_4k")
+    say(f"[bwd] 4k all-selected shape={workloads.shape_of(cfg)} seed={seed}")
+    raw = workloads.make_prefill(cfg, seed)
+    dev, _ = prepare(raw, torch.bfloat16)
+    dout = torch.from_numpy(workloads.make_grad_out(cfg, seed)).to(torch.bfloat16).cuda()
+    sel = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=64,
+                      chunk=64, topk=64, return_sel=True)["sel_idx"]
+    g = gpu_lib.bwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], sel, dout,
+                    window=64, chunk=64, topk=64)
+    G = cfg["n_q_heads"] // cfg["n_kv_heads"]
+    tq = dev["q"].float().permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    tk = dev["k"].float().permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    tv = dev["v"].float().permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    with torch.nn.attention.sdpa_kernel(torch.nn.attention.SDPBackend.MATH):
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1), is_causal=True)
+    (o * dout.float().permute(0, 2, 1, 3)).sum().backward()
+    torch.cuda.synchronize()
+    ref = {"dq": tq.grad.permute(0, 2, 1, 3), "dk": tk.grad.permute(0, 2, 1, 3),
+           "dv": tv.grad.permute(0, 2, 1, 3)}
+    for key, r in ref.items():
+        err = rel_l2(g[key].double().cpu().numpy(), r.double().cpu().numpy())
+        say(f"  {key} rel-L2 vs SDPA {err:.2e}")
+        assert err <= GRAD_TOL
+    assert torch.count_nonzero(g["dwphi_q"]) == 0 and torch.count_nonzero(g["dwphi_k"]) == 0

@@ -87,6 +87,15 @@ def make_prefill(cfg: dict, seed: int) -> dict:
     return dict(q=q, k=k, v=v, wphi_q=wq, wphi_k=wk, needle=needle)
 
 
+def make_grad_out(cfg: dict, seed: int) -> np.ndarray:
+    """Upstream gradient of the output for the backward pass: dout
+    [B, N, Hq, d] ~ N(0, 1), float32, from its own stream (seed + 1000003)
+    so that it does not disturb the forward's draws."""
+    rng = np.random.default_rng(seed + 1000003)
+    return rng.standard_normal((cfg["batch"], cfg["seqlen"], cfg["n_q_heads"], cfg["head_dim"]),
+                               dtype=np.float32)
+
+
 def make_decode_stream(cfg: dict, seed: int, b: int, g: int) -> dict:
     """Cache contents of one (sequence, KV head) at position ``pos``:
     ring K/V of the last W tokens ~ N(0,1); route flags of the last complete
