@@ -7,7 +7,8 @@ head_dim 128, window = chunk = 64, top-32 per chunk, bf16 storage with fp32
 accumulation), inputs resident in HBM.  The decode step (batch 64 at
 position 16384) is timed the same way and reported in the "decode" object,
 and its serving form (the same batch with one position per sequence) in
-"decode_ragged".
+"decode_ragged"; the backward pass (gradients w.r.t. q, k, v and the NP-Map
+projections) on the 8 x 2048 training batch in "backward".
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
 the launch stream by the library's *_timed entry points; the roofline uses
@@ -306,6 +307,115 @@ def bench_decode_ragged(still, torch, steps, warmup):
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs at 2.4 GHz)
+
+
+def backward_flops(cfg: dict, sel_idx: np.ndarray) -> dict:
+    """Algorithmic flops of the backward, per kernel that does them (exp
+    excluded).  A softmax pair (query, visible key) costs the query side 6d
+    (logit recompute, dout.v, ds k) and the key side 8d (logit recompute,
+    dout.v, ds q, p dout): the two reductions run in separate kernels, so
+    each recomputes the logit.  Linear terms: S_t dout per query head
+    (2 d' d), the suffix sums per query head (2 d' d), U^T phi_k and U v per
+    routed linear key (4 d' d), explicit pairs of the partly covered chunk
+    (4d + 4d' per pair on each side), NP-Map backward 2 d' d per token-head
+    and its projection gradient d' d per token-head."""
+    B, N, Hq, Hkv = cfg["batch"], cfg["seqlen"], cfg["n_q_heads"], cfg["n_kv_heads"]
+    d = fd = cfg["head_dim"]
+    W, C = cfg["window"], cfg["chunk"]
+    lam = min(cfg["topk"], C)
+    G = Hq // Hkv
+    t = np.arange(N)
+    win_pairs = float(np.minimum(t + 1, W).sum()) * Hq * B
+    r_end = np.maximum(0, t - W + 1)
+    c_full = r_end // C
+    n_full = N // C
+    sel_pairs = q_part = k_part = la_keys = 0.0
+    for b in range(B):
+        for g in range(Hkv):
+            pos = np.sort(sel_idx[b, g].reshape(-1)) if lam > 0 else np.zeros(0, np.int64)
+            sel_pairs += float(np.searchsorted(pos, r_end, side="left").sum()) * G
+            la = np.ones(N, np.int64)
+            if lam > 0:
+                la[n_full * C:] = 0
+                la[pos] = 0
+            cum = np.concatenate([[0], np.cumsum(la)])
+            q_part += float((cum[r_end] - cum[c_full * C]).sum()) * G
+            j = np.arange(max(0, N - W))
+            jl = j[la[j] == 1]
+            t1 = np.minimum(N - 1, ((jl + W) // C + 1) * C - 1)
+            k_part += float((t1 - (jl + W) + 1).sum()) * G
+            la_keys += float(jl.size)
+    sa = win_pairs + sel_pairs
+    tok_q, tok_k = float(B * N * Hq), float(B * N * Hkv)
+    return dict(
+        bwd_query=6.0 * d * sa + 2.0 * fd * d * tok_q + (4.0 * d + 4.0 * fd) * q_part,
+        bwd_uchunk=2.0 * fd * d * tok_q,
+        bwd_key=8.0 * d * sa + 4.0 * fd * d * la_keys + (4.0 * d + 4.0 * fd) * k_part,
+        np_vjp=2.0 * fd * d * (tok_q + tok_k),
+        dw=1.0 * fd * d * (tok_q + tok_k),
+    )
+
+
+def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
+    """The backward pass on the training-shaped batch (8 sequences of 2048
+    tokens): gradients w.r.t. q, k, v and both NP-Map projections under the
+    forward's own routing, dout ~ N(0, 1)."""
+    cfg = workloads.CONFIGS[name]
+    seed = workloads.seed_of(name)
+    raw = workloads.make_prefill(cfg, seed)
+    dev = {k: torch.from_numpy(raw[k]).to(torch.bfloat16).cuda() for k in ("q", "k", "v")}
+    for k in ("wphi_q", "wphi_k"):
+        dev[k] = torch.from_numpy(raw[k]).cuda()
+    dout = torch.from_numpy(workloads.make_grad_out(cfg, seed)).to(torch.bfloat16).cuda()
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    kw = dict(window=W, chunk=C, topk=lam)
+    args = (dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"])
+    sel = still.fwd(*args, **kw, return_sel=True)["sel_idx"]
+    sh = still.make_shape(batch=cfg["batch"], seqlen=cfg["seqlen"], n_q_heads=cfg["n_q_heads"],
+                          n_kv_heads=cfg["n_kv_heads"], head_dim=cfg["head_dim"], **kw)
+    ws = torch.empty(still.bwd_workspace_size(sh), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        still.bwd(*args, sel, dout, **kw, workspace=ws)
+    timers = [still.LaunchTimer() for _ in range(steps)]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        still.bwd(*args, sel, dout, **kw, workspace=ws, timer=timers[i])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per = {}
+    for tm in timers:
+        for kname, dur in tm.durations_ms():
+            per.setdefault(kname, []).append(dur)
+    kern = {k: float(np.mean(v)) for k, v in per.items()}
+    log(f"[bench] {name} backward: {ms:.3f} ms/step; kernels (ms): " +
+        ", ".join(f"{k}={v:.3f}" for k, v in kern.items()))
+    fl = backward_flops(cfg, sel.cpu().numpy())
+    dom = max(kern, key=kern.get)
+    roof = None
+    if dom in fl:
+        achieved = fl[dom] / (kern[dom] * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP32_VALU_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_VALU_TFLOPS, 4),
+                "traffic": None, "kernel": dom, "avg_ms": round(kern[dom], 4),
+                "algorithmic_flop_per_launch": fl[dom]}
+    total = sum(fl.values())
+    tokens = cfg["batch"] * cfg["seqlen"]
+    return {"metric": "backward tokens/s (8 x 2048 training batch)",
+            "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+            "config": {"workload": f"{name}: batch {cfg['batch']}, seq {cfg['seqlen']}, "
+                       f"{cfg['n_q_heads']} q / {cfg['n_kv_heads']} KV heads, d {cfg['head_dim']}, "
+                       f"window {W}, chunk {C}, top-{lam}; gradients of q, k, v, both NP-Map "
+                       "projections (fp32) under the forward's routing", "batch": cfg["batch"],
+                       "seq_len": cfg["seqlen"]},
+            "whole_step_TFLOPs": round(total / (ms * 1e-3) / 1e12, 2),
+            "kernels_ms": {k: round(v, 4) for k, v in kern.items()}, "roofline": roof}
+
+
 def cpu_baseline(raw, cfg, n_rows=12):
     """The oracle as it stands, on a bounded sample: group scores and
     selection over the whole sequence, then n_rows output rows evaluated one
@@ -345,6 +455,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_16k", choices=["prefill_4k", "prefill_16k", "train_8x2k"])
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step and print its JSON object")
@@ -379,6 +490,8 @@ def main():
     cfg = pre["cfg"]
     dec = None if args.no_decode else bench_decode(still, torch, args.steps, args.warmup)
     dec_r = None if args.no_decode else bench_decode_ragged(still, torch, args.steps, args.warmup)
+    bwd = None if args.no_backward else bench_backward(still, torch, max(3, args.steps // 4),
+                                                         args.warmup)
     cpu = None if args.no_cpu else cpu_baseline(pre["raw"], cfg)
     tok_s = pre["tokens"] / (pre["ms"] * 1e-3)
     line = {
@@ -396,6 +509,7 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in pre["kern"].items()},
         "decode": dec,
         "decode_ragged": dec_r,
+        "backward": bwd,
     }
     print(json.dumps(line), flush=True)
 

@@ -72,9 +72,88 @@ __global__ __launch_bounds__(256) void bwd_route_kernel(const int32_t* __restric
     }
 }
 
-// One wave per query (b, t, h).  Lane owns output dims and features
-// lane + 64 p.  stat[(b, t, h)] = (m, l, D_t).
-template <typename T, int DD>
+// 8 consecutive elements of a row as fp32 (16-byte loads; rows are 16-byte
+// aligned: every row starts at a multiple of d elements of an aligned tensor)
+__device__ __forceinline__ void load8(const __bf16* p, float* x) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float* p, float* x) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// a . r and c . s for LDS vectors a, c (read by the whole wave) and rows r, s
+template <int DD, typename T1, typename T2>
+__device__ __forceinline__ float2 dot2_rows(const float* a, const T1* r, const float* c, const T2* s) {
+    float x0 = 0.f, x1 = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < DD; i += 8) {
+        float xr[8], xs[8];
+        load8(r + i, xr);
+        load8(s + i, xs);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x0 = fmaf(a[i + e], xr[e], x0);
+            x1 = fmaf(c[i + e], xs[e], x1);
+        }
+    }
+    return make_float2(x0, x1);
+}
+
+template <int DD, typename T1>
+__device__ __forceinline__ float dot_row(const float* a, const T1* r) {
+    float x0 = 0.f, x1 = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < DD; i += 8) {
+        float xr[8];
+        load8(r + i, xr);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            x0 = fmaf(a[i + e], xr[e], x0);
+            x1 = fmaf(a[i + e + 1], xr[e + 1], x1);
+        }
+    }
+    return x0 + x1;
+}
+
+// dots of one row r (DD elements) with G LDS vectors a[h], h < G <= GM
+template <int DD, int GM, typename T1>
+__device__ __forceinline__ void dot_multi(const float (*a)[DD], const T1* r, int G, float* out) {
+#pragma unroll
+    for (int h = 0; h < GM; ++h) out[h] = 0.f;
+#pragma unroll 2
+    for (int i = 0; i < DD; i += 8) {
+        float xr[8];
+        load8(r + i, xr);
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            if (h < G) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[h] = fmaf(a[h][i + e], xr[e], out[h]);
+            }
+    }
+}
+
+// One wave per query position and KV head (b, t, g), for all G query heads
+// of the group at once (they read the same keys: every key row loaded serves
+// G queries).  Lane owns output dims and features lane + 64 p.  Two passes
+// over the softmax keys:
+//   1. logits s_j and vd_j = dout . v_j: the reference m (max(0, max s)),
+//      l = sum of weights and D_t = sum w_j vd_j / l (= dout . out), the
+//      linear tokens entering through S_t, z_t and the partly covered chunk;
+//   2. ds_j = (w_j / l)(vd_j - D_t), dq = tau sum ds_j k_j.
+// Then dphi_q = c_t (S_t dout - D_t z_t + sum over the partly covered chunk's
+// linear tokens of (vd_j - D_t) phi_k(j)), c_t = exp(-m) / l.
+// stat[(b, t, h)] = (m, l, D_t, c_t).
+template <typename T, int DD, int GM>
 __global__ __launch_bounds__(64) void bwd_query_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
@@ -82,84 +161,95 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
     const float* __restrict__ lin, float* __restrict__ dq, float* __restrict__ dphiq,
     float* __restrict__ stat, Dims D) {
     constexpr int PL = DD / kWave;
-    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-    const int g = h / D.G;
-    __shared__ float qs[DD];
-    __shared__ float fq[DD];
-    __shared__ float ds_[DD];
-    const size_t qoff = (((size_t)b * D.N + t) * D.Hq + h);
-    for (int i = lane; i < DD; i += kWave) {
-        qs[i] = to_f32(q[qoff * DD + i]);
-        fq[i] = phiq[qoff * DD + i];
-        ds_[i] = to_f32(dout[qoff * DD + i]);
+    const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int G = D.G;
+    __shared__ float qs[GM][DD];
+    __shared__ float fq[GM][DD];
+    __shared__ float ds_[GM][DD];
+    const size_t qoff0 = ((size_t)b * D.N + t) * D.Hq + (size_t)g * G;  // row of head g G + h: qoff0 + h
+    for (int x = lane; x < G * DD; x += kWave) {
+        const int h = x / DD, i = x % DD;
+        qs[h][i] = to_f32(q[(qoff0 + h) * DD + i]);
+        fq[h][i] = phiq[(qoff0 + h) * DD + i];
+        ds_[h][i] = to_f32(dout[(qoff0 + h) * DD + i]);
     }
     __syncthreads();
     auto krow = [&](int j) { return k + (((size_t)b * D.N + j) * D.Hkv + g) * DD; };
     auto vrow = [&](int j) { return v + (((size_t)b * D.N + j) * D.Hkv + g) * DD; };
-    auto dot_row = [&](const float* a, const T* r) {
-        float x = 0.f;
-        for (int i = 0; i < DD; ++i) x = fmaf(a[i], to_f32(r[i]), x);
-        return x;
-    };
+    auto pkrow = [&](int j) { return phik + (((size_t)b * D.N + j) * D.Hkv + g) * DD; };
 
-    // ---- forward statistics (the forward's read-out, repeated) ----
-    float acc[PL];
-#pragma unroll
-    for (int p = 0; p < PL; ++p) acc[p] = 0.f;
-    float l = 0.f, m = 0.f;
     const int r_end = max(0, t - D.W + 1);  // routed tokens j < r_end
     const int c_full = r_end / D.C;
     const float* st = c_full >= 1
         ? lin + (((size_t)b * D.Hkv + g) * D.T + (c_full - 1)) * (size_t)(DD * (DD + 1))
         : nullptr;
-    if (st) {
-        for (int i = 0; i < DD; ++i) {
-            const float f = fq[i];
-#pragma unroll
-            for (int p = 0; p < PL; ++p) acc[p] = fmaf(f, st[i * DD + lane + kWave * p], acc[p]);
-        }
-        float lp = 0.f;
-        for (int i = lane; i < DD; i += kWave) lp = fmaf(fq[i], st[DD * DD + i], lp);
-        l = wave_sum(lp);
-    }
     const uint8_t* rt = route + ((size_t)b * D.Hkv + g) * D.N;
+
+    // ---- linear part of pass 1 (reference 0): y = S_t dout, l, D numerator ----
+    float y[GM][PL];
+    float l[GM], dn[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+        l[h] = dn[h] = 0.f;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) y[h][p] = 0.f;
+    }
+    if (st) {
+        float lp[GM], dp[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) lp[h] = dp[h] = 0.f;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) {
+            const int i = lane + kWave * p;
+            const float4* row = reinterpret_cast<const float4*>(st + (size_t)i * DD);
+            for (int e4 = 0; e4 < DD / 4; ++e4) {
+                const float4 r = row[e4];
+#pragma unroll
+                for (int h = 0; h < GM; ++h)
+                    if (h < G) {
+                        float x = y[h][p];
+                        x = fmaf(r.x, ds_[h][4 * e4], x);
+                        x = fmaf(r.y, ds_[h][4 * e4 + 1], x);
+                        x = fmaf(r.z, ds_[h][4 * e4 + 2], x);
+                        x = fmaf(r.w, ds_[h][4 * e4 + 3], x);
+                        y[h][p] = x;
+                    }
+            }
+            const float zi = st[DD * DD + i];
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                lp[h] = fmaf(fq[h][i], zi, lp[h]);
+                dp[h] = fmaf(fq[h][i], y[h][p], dp[h]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            if (h < G) {
+                l[h] = wave_sum(lp[h]);
+                dn[h] = wave_sum(dp[h]);
+            }
+    }
     for (int j0 = c_full * D.C; j0 < r_end; j0 += kWave) {
         const int j = j0 + lane;
-        float w = 0.f;
+        float kap[GM], vd[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) kap[h] = vd[h] = 0.f;
         if (j < r_end && rt[j] == kRouteLA) {
-            const float* pk = phik + (((size_t)b * D.N + j) * D.Hkv + g) * DD;
-            for (int i = 0; i < DD; ++i) w = fmaf(fq[i], pk[i], w);
+            dot_multi<DD, GM>(fq, pkrow(j), G, kap);
+            dot_multi<DD, GM>(ds_, vrow(j), G, vd);
         }
-        l += wave_sum(w);
-        const int nb = min(kWave, r_end - j0);
-        for (int jj = 0; jj < nb; ++jj) {
-            const float wj = __shfl(w, jj, kWave);
-            if (wj != 0.f) {
-                const T* vr = vrow(j0 + jj);
 #pragma unroll
-                for (int p = 0; p < PL; ++p) acc[p] = fmaf(wj, to_f32(vr[lane + kWave * p]), acc[p]);
+        for (int h = 0; h < GM; ++h)
+            if (h < G) {
+                l[h] += wave_sum(kap[h]);
+                dn[h] += wave_sum(kap[h] * vd[h]);
             }
-        }
     }
-    auto sa_fwd = [&](int jpos) {
-        const float s = jpos >= 0 ? D.tau * dot_row(qs, krow(jpos)) : kNegInfB;
-        const float m_new = fmaxf(m, wave_max(s));
-        const float sc = expf(m - m_new);
-        const float pj = jpos >= 0 ? expf(s - m_new) : 0.f;
-        l = l * sc + wave_sum(pj);
+
+    // ---- softmax part of pass 1 ----
+    float m[GM];
 #pragma unroll
-        for (int p = 0; p < PL; ++p) acc[p] *= sc;
-        for (int jj = 0; jj < kWave; ++jj) {
-            const int jp = __shfl(jpos, jj, kWave);
-            if (jp >= 0) {
-                const float pv = __shfl(pj, jj, kWave);
-                const T* vr = vrow(jp);
-#pragma unroll
-                for (int p = 0; p < PL; ++p) acc[p] = fmaf(pv, to_f32(vr[lane + kWave * p]), acc[p]);
-            }
-        }
-        m = m_new;
-    };
+    for (int h = 0; h < GM; ++h) m[h] = 0.f;
     const int32_t* sel = selw + ((size_t)b * D.Hkv + g) * D.n_full * D.lam;
     const int n_cand = D.lam > 0 ? min(D.n_full, (r_end + D.C - 1) / D.C) * D.lam : 0;
     auto sel_pos = [&](int i) {
@@ -167,88 +257,128 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
         const int pos = sel[i];
         return pos < r_end ? pos : -1;  // -1 entries and not yet visible tokens
     };
-    if (D.W > 0)
-        for (int j0 = max(0, t - D.W + 1); j0 <= t; j0 += kWave) sa_fwd(j0 + lane <= t ? j0 + lane : -1);
-    for (int i0 = 0; i0 < n_cand; i0 += kWave) sa_fwd(sel_pos(i0 + lane));
-
-    const float inv = 1.0f / l;
-    float dpart = 0.f;
-#pragma unroll
-    for (int p = 0; p < PL; ++p) dpart = fmaf(acc[p] * inv, ds_[lane + kWave * p], dpart);
-    const float Dt = wave_sum(dpart);
-
-    // ---- softmax part of dq ----
-    float dqa[PL];
-#pragma unroll
-    for (int p = 0; p < PL; ++p) dqa[p] = 0.f;
-    auto sa_bwd = [&](int jpos) {
-        float dsj = 0.f;
+    auto pass1 = [&](int jpos) {
+        float s[GM], vd[GM];
         if (jpos >= 0) {
-            const float s = D.tau * dot_row(qs, krow(jpos));
-            const float pj = expf(s - m) * inv;
-            dsj = pj * (dot_row(ds_, vrow(jpos)) - Dt);
+            dot_multi<DD, GM>(qs, krow(jpos), G, s);
+            dot_multi<DD, GM>(ds_, vrow(jpos), G, vd);
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            if (h < G) {
+                const float sh = jpos >= 0 ? D.tau * s[h] : kNegInfB;
+                const float m_new = fmaxf(m[h], wave_max(sh));
+                const float sc = expf(m[h] - m_new);
+                const float pj = jpos >= 0 ? expf(sh - m_new) : 0.f;
+                l[h] = l[h] * sc + wave_sum(pj);
+                dn[h] = dn[h] * sc + wave_sum(jpos >= 0 ? pj * vd[h] : 0.f);
+                m[h] = m_new;
+            }
+    };
+    if (D.W > 0)
+        for (int j0 = max(0, t - D.W + 1); j0 <= t; j0 += kWave) pass1(j0 + lane <= t ? j0 + lane : -1);
+    for (int i0 = 0; i0 < n_cand; i0 += kWave) pass1(sel_pos(i0 + lane));
+    float inv[GM], Dt[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+        inv[h] = h < G ? 1.0f / l[h] : 0.f;
+        Dt[h] = dn[h] * inv[h];
+    }
+
+    // ---- pass 2: softmax part of dq ----
+    float dqa[GM][PL];
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+        for (int p = 0; p < PL; ++p) dqa[h][p] = 0.f;
+    auto pass2 = [&](int jpos) {
+        float dsj[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) dsj[h] = 0.f;
+        if (jpos >= 0) {
+            float s[GM], vd[GM];
+            dot_multi<DD, GM>(qs, krow(jpos), G, s);
+            dot_multi<DD, GM>(ds_, vrow(jpos), G, vd);
+#pragma unroll
+            for (int h = 0; h < GM; ++h)
+                if (h < G) dsj[h] = expf(D.tau * s[h] - m[h]) * inv[h] * (vd[h] - Dt[h]);
         }
         for (int jj = 0; jj < kWave; ++jj) {
             const int jp = __shfl(jpos, jj, kWave);
             if (jp >= 0) {
-                const float w = __shfl(dsj, jj, kWave);
                 const T* kr = krow(jp);
+                float kv[PL];
 #pragma unroll
-                for (int p = 0; p < PL; ++p) dqa[p] = fmaf(w, to_f32(kr[lane + kWave * p]), dqa[p]);
+                for (int p = 0; p < PL; ++p) kv[p] = to_f32(kr[lane + kWave * p]);
+#pragma unroll
+                for (int h = 0; h < GM; ++h)
+                    if (h < G) {
+                        const float w = __shfl(dsj[h], jj, kWave);
+#pragma unroll
+                        for (int p = 0; p < PL; ++p) dqa[h][p] = fmaf(w, kv[p], dqa[h][p]);
+                    }
             }
         }
     };
     if (D.W > 0)
-        for (int j0 = max(0, t - D.W + 1); j0 <= t; j0 += kWave) sa_bwd(j0 + lane <= t ? j0 + lane : -1);
-    for (int i0 = 0; i0 < n_cand; i0 += kWave) sa_bwd(sel_pos(i0 + lane));
+        for (int j0 = max(0, t - D.W + 1); j0 <= t; j0 += kWave) pass2(j0 + lane <= t ? j0 + lane : -1);
+    for (int i0 = 0; i0 < n_cand; i0 += kWave) pass2(sel_pos(i0 + lane));
 #pragma unroll
-    for (int p = 0; p < PL; ++p) dq[qoff * DD + lane + kWave * p] = D.tau * dqa[p];
+    for (int h = 0; h < GM; ++h)
+        if (h < G)
+#pragma unroll
+            for (int p = 0; p < PL; ++p) dq[(qoff0 + h) * DD + lane + kWave * p] = D.tau * dqa[h][p];
 
-    // ---- dphi_q = c (S_t dout - D_t z_t) ----
-    const float cf = expf(-m) * inv;
-    float dfq[PL];
+    // ---- dphi_q ----
+    float dfq[GM][PL];
 #pragma unroll
-    for (int p = 0; p < PL; ++p) dfq[p] = 0.f;
-    if (st) {
+    for (int h = 0; h < GM; ++h)
 #pragma unroll
-        for (int p = 0; p < PL; ++p) {
-            const int i = lane + kWave * p;
-            const float4* row = reinterpret_cast<const float4*>(st + (size_t)i * DD);
-            float x = 0.f;
-            for (int e4 = 0; e4 < DD / 4; ++e4) {
-                const float4 r = row[e4];
-                x = fmaf(r.x, ds_[4 * e4], x);
-                x = fmaf(r.y, ds_[4 * e4 + 1], x);
-                x = fmaf(r.z, ds_[4 * e4 + 2], x);
-                x = fmaf(r.w, ds_[4 * e4 + 3], x);
-            }
-            dfq[p] = x - Dt * st[DD * DD + i];
-        }
-    }
+        for (int p = 0; p < PL; ++p)
+            dfq[h][p] = st ? y[h][p] - Dt[h] * st[DD * DD + lane + kWave * p] : 0.f;
     for (int j0 = c_full * D.C; j0 < r_end; j0 += kWave) {
         const int j = j0 + lane;
-        float w = 0.f;
+        float w[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) w[h] = 0.f;
         const bool la = j < r_end && rt[j] == kRouteLA;
-        if (la) w = dot_row(ds_, vrow(j)) - Dt;
+        if (la) {
+            dot_multi<DD, GM>(ds_, vrow(j), G, w);
+#pragma unroll
+            for (int h = 0; h < GM; ++h) w[h] -= Dt[h];
+        }
         const int nb = min(kWave, r_end - j0);
         for (int jj = 0; jj < nb; ++jj) {
             const int laj = __shfl((int)la, jj, kWave);
             if (laj) {
-                const float wj = __shfl(w, jj, kWave);
-                const float* pk = phik + (((size_t)b * D.N + j0 + jj) * D.Hkv + g) * DD;
+                const float* pk = pkrow(j0 + jj);
+                float pv[PL];
 #pragma unroll
-                for (int p = 0; p < PL; ++p) dfq[p] = fmaf(wj, pk[lane + kWave * p], dfq[p]);
+                for (int p = 0; p < PL; ++p) pv[p] = pk[lane + kWave * p];
+#pragma unroll
+                for (int h = 0; h < GM; ++h)
+                    if (h < G) {
+                        const float wj = __shfl(w[h], jj, kWave);
+#pragma unroll
+                        for (int p = 0; p < PL; ++p) dfq[h][p] = fmaf(wj, pv[p], dfq[h][p]);
+                    }
             }
         }
     }
 #pragma unroll
-    for (int p = 0; p < PL; ++p) dphiq[qoff * DD + lane + kWave * p] = cf * dfq[p];
-    if (lane == 0) {
-        stat[qoff * 4 + 0] = m;
-        stat[qoff * 4 + 1] = l;
-        stat[qoff * 4 + 2] = Dt;
-        stat[qoff * 4 + 3] = cf;
-    }
+    for (int h = 0; h < GM; ++h)
+        if (h < G) {
+            const size_t o = qoff0 + h;
+            const float cf = expf(-m[h]) * inv[h];
+#pragma unroll
+            for (int p = 0; p < PL; ++p) dphiq[o * DD + lane + kWave * p] = cf * dfq[h][p];
+            if (lane == 0) {
+                stat[o * 4 + 0] = m[h];
+                stat[o * 4 + 1] = l[h];
+                stat[o * 4 + 2] = Dt[h];
+                stat[o * 4 + 3] = cf;
+            }
+        }
 }
 
 // Per query chunk c of (b, g): U[i][e] = sum over its queries t and the
@@ -308,76 +438,125 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(float* __restrict__ ust
     }
 }
 
-// One wave per key (b, j, g).  Lane owns dims / features lane + 64 p.
+constexpr int kKB = 4;  // keys per wave in the key-side kernels
+
+// Softmax terms of KB keys (rows ks[i], vs[i] in LDS, positions jk[i], -1
+// for none) against the query rows (t, h) with t in [t_lo, t_hi] and h in
+// KV head g's group: each query row and dout row is loaded once for all KB
+// keys.  A pair counts when mode 0: t in [j, j + W - 1] (the key's window
+// queries), mode 1: t >= j + W (later queries of a selected key).
+//   p = exp(s - m_t) / l_t,  ds = p (dout_t . v_j - D_t)
+//   dka[i] += ds q_t,  dva[i] += p dout_t   (lane owns dims lane + 64 p)
 template <typename T, int DD>
-__global__ __launch_bounds__(64) void bwd_key_kernel(
+__device__ __forceinline__ void key_group_softmax(const T* __restrict__ q, const T* __restrict__ dout,
+                                                  const float* __restrict__ stat,
+                                                  const float (*ks)[DD], const float (*vs)[DD],
+                                                  const int* jk, int t_lo, int t_hi, int mode,
+                                                  int b, int g, const Dims& D, int lane,
+                                                  float (*dka)[DD / kWave],
+                                                  float (*dva)[DD / kWave]) {
+    constexpr int PL = DD / kWave;
+    const int G = D.G;
+    const int n = t_hi >= t_lo ? (t_hi - t_lo + 1) * G : 0;
+    auto row_of = [&](int pr) { return ((size_t)b * D.N + t_lo + pr / G) * D.Hq + (size_t)g * G + pr % G; };
+    for (int i0 = 0; i0 < n; i0 += kWave) {
+        const int pr = i0 + lane;
+        float pj[kKB], dsj[kKB];
+#pragma unroll
+        for (int i = 0; i < kKB; ++i) pj[i] = dsj[i] = 0.f;
+        if (pr < n) {
+            const size_t o = row_of(pr);
+            const int t = t_lo + pr / G;
+            float s[kKB], vd[kKB];
+            dot_multi<DD, kKB>(ks, q + o * DD, kKB, s);
+            dot_multi<DD, kKB>(vs, dout + o * DD, kKB, vd);
+            const float m = stat[o * 4 + 0], il = 1.0f / stat[o * 4 + 1], Dt = stat[o * 4 + 2];
+#pragma unroll
+            for (int i = 0; i < kKB; ++i) {
+                const int j = jk[i];
+                const bool ok = j >= 0 && (mode == 0 ? (t >= j && t <= j + D.W - 1) : t >= j + D.W);
+                if (ok) {
+                    pj[i] = expf(D.tau * s[i] - m) * il;
+                    dsj[i] = pj[i] * (vd[i] - Dt);
+                }
+            }
+        }
+        const int nb = min(kWave, n - i0);
+        for (int jj = 0; jj < nb; ++jj) {
+            const size_t o = row_of(i0 + jj);
+            float qe[PL], de[PL];
+#pragma unroll
+            for (int p = 0; p < PL; ++p) {
+                qe[p] = to_f32(q[o * DD + lane + kWave * p]);
+                de[p] = to_f32(dout[o * DD + lane + kWave * p]);
+            }
+#pragma unroll
+            for (int i = 0; i < kKB; ++i) {
+                const float w = __shfl(dsj[i], jj, kWave), pv = __shfl(pj[i], jj, kWave);
+#pragma unroll
+                for (int p = 0; p < PL; ++p) {
+                    dka[i][p] = fmaf(w, qe[p], dka[i][p]);
+                    dva[i][p] = fmaf(pv, de[p], dva[i][p]);
+                }
+            }
+        }
+    }
+}
+
+// One wave per (b, g, four consecutive keys j0 .. j0 + 3): the softmax terms
+// of each key's window queries, and for a routed linear key everything its
+// later queries contribute through the linear branch:
+//   dv_j = U_j^T phi_k(j),  dphi_k(j) = U_j v_j - u_j
+// (U_j: the inclusive suffix sum from the first chunk after j + W's chunk,
+// plus the queries of j + W's chunk from j + W on, taken one by one).
+// Writes dk (softmax part), dv and dphi_k of its keys.
+template <typename T, int DD>
+__global__ __launch_bounds__(64) void bwd_key_win_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
     const uint8_t* __restrict__ route, const float* __restrict__ stat,
     const float* __restrict__ ust, float* __restrict__ dk, float* __restrict__ dv,
     float* __restrict__ dphik, Dims D) {
     constexpr int PL = DD / kWave;
-    const int j = blockIdx.x, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-    __shared__ float ks[DD];
-    __shared__ float vs[DD];
-    __shared__ float fk[DD];
-    const size_t koff = ((size_t)b * D.N + j) * D.Hkv + g;
-    for (int i = lane; i < DD; i += kWave) {
-        ks[i] = to_f32(k[koff * DD + i]);
-        vs[i] = to_f32(v[koff * DD + i]);
-        fk[i] = phik[koff * DD + i];
+    const int j0 = blockIdx.x * kKB, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    __shared__ float ks[kKB][DD];
+    __shared__ float vs[kKB][DD];
+    __shared__ float fk[kKB][DD];
+    int jk[kKB];
+#pragma unroll
+    for (int i = 0; i < kKB; ++i) jk[i] = j0 + i < D.N ? j0 + i : -1;
+    auto koff = [&](int j) { return ((size_t)b * D.N + j) * D.Hkv + g; };
+    for (int x = lane; x < kKB * DD; x += kWave) {
+        const int i = x / DD, e = x % DD, j = min(j0 + i, D.N - 1);
+        ks[i][e] = to_f32(k[koff(j) * DD + e]);
+        vs[i][e] = to_f32(v[koff(j) * DD + e]);
+        fk[i][e] = phik[koff(j) * DD + e];
     }
     __syncthreads();
-    float dka[PL], dva[PL], dfa[PL];
+    float dka[kKB][PL], dva[kKB][PL], dfa[kKB][PL];
 #pragma unroll
-    for (int p = 0; p < PL; ++p) dka[p] = dva[p] = dfa[p] = 0.f;
-    const uint8_t rj = route[((size_t)b * D.Hkv + g) * D.N + j];
+    for (int i = 0; i < kKB; ++i)
+#pragma unroll
+        for (int p = 0; p < PL; ++p) dka[i][p] = dva[i][p] = dfa[i][p] = 0.f;
+    if (D.W > 0)
+        key_group_softmax<T, DD>(q, dout, stat, ks, vs, jk, j0, min(D.N - 1, j0 + kKB - 1 + D.W - 1),
+                                 0, b, g, D, lane, dka, dva);
     const int G = D.G;
     auto qoff = [&](int t, int h) { return ((size_t)b * D.N + t) * D.Hq + h; };
-
-    // softmax queries: the window's t in [j, j + W - 1], and every later t
-    // when j is selected
-    const int t_last = rj == kRouteSA ? D.N - 1 : min(D.N - 1, j + D.W - 1);
-    const int n_sa = D.W > 0 ? (t_last - j + 1) * G : 0;
-    for (int i0 = 0; i0 < n_sa; i0 += kWave) {
-        const int pr = i0 + lane;
-        float dsj = 0.f, pj = 0.f;
-        if (pr < n_sa) {
-            const size_t o = qoff(j + pr / G, g * G + pr % G);
-            const T* qr = q + o * DD;
-            const T* dr = dout + o * DD;
-            float s = 0.f, dv_ = 0.f;
-            for (int i = 0; i < DD; ++i) {
-                s = fmaf(ks[i], to_f32(qr[i]), s);
-                dv_ = fmaf(vs[i], to_f32(dr[i]), dv_);
-            }
-            pj = expf(D.tau * s - stat[o * 4 + 0]) / stat[o * 4 + 1];
-            dsj = pj * (dv_ - stat[o * 4 + 2]);
-        }
-        const int nb = min(kWave, n_sa - i0);
-        for (int jj = 0; jj < nb; ++jj) {
-            const int pr2 = i0 + jj;
-            const size_t o = qoff(j + pr2 / G, g * G + pr2 % G);
-            const float w = __shfl(dsj, jj, kWave), pv = __shfl(pj, jj, kWave);
-            const T* qr = q + o * DD;
-            const T* dr = dout + o * DD;
 #pragma unroll
-            for (int p = 0; p < PL; ++p) {
-                dka[p] = fmaf(w, to_f32(qr[lane + kWave * p]), dka[p]);
-                dva[p] = fmaf(pv, to_f32(dr[lane + kWave * p]), dva[p]);
-            }
-        }
-    }
-    // linear queries: every t >= j + W (j routed, not selected)
-    const int t0 = j + D.W;
-    if (rj == kRouteLA && t0 <= D.N - 1) {
+    for (int kk = 0; kk < kKB; ++kk) {
+        const int j = jk[kk];
+        if (j < 0) continue;
+        const int t0 = j + D.W;
+        if (route[((size_t)b * D.Hkv + g) * D.N + j] != kRouteLA || t0 > D.N - 1) continue;
         const int c0 = t0 / D.C;
         if (c0 + 1 < D.T) {
             const float* U = ust + (((size_t)b * D.Hkv + g) * D.T + c0 + 1) * (size_t)(DD * (DD + 1));
             for (int i = 0; i < DD; ++i) {
-                const float f = fk[i];
+                const float f = fk[kk][i];
 #pragma unroll
-                for (int p = 0; p < PL; ++p) dva[p] = fmaf(f, U[(size_t)i * DD + lane + kWave * p], dva[p]);
+                for (int p = 0; p < PL; ++p)
+                    dva[kk][p] = fmaf(f, U[(size_t)i * DD + lane + kWave * p], dva[kk][p]);
             }
 #pragma unroll
             for (int p = 0; p < PL; ++p) {
@@ -386,12 +565,12 @@ __global__ __launch_bounds__(64) void bwd_key_kernel(
                 float x = 0.f;
                 for (int e4 = 0; e4 < DD / 4; ++e4) {
                     const float4 r = row[e4];
-                    x = fmaf(r.x, vs[4 * e4], x);
-                    x = fmaf(r.y, vs[4 * e4 + 1], x);
-                    x = fmaf(r.z, vs[4 * e4 + 2], x);
-                    x = fmaf(r.w, vs[4 * e4 + 3], x);
+                    x = fmaf(r.x, vs[kk][4 * e4], x);
+                    x = fmaf(r.y, vs[kk][4 * e4 + 1], x);
+                    x = fmaf(r.z, vs[kk][4 * e4 + 2], x);
+                    x = fmaf(r.w, vs[kk][4 * e4 + 3], x);
                 }
-                dfa[p] = x - U[DD * DD + i];
+                dfa[kk][p] = x - U[DD * DD + i];
             }
         }
         const int t1 = min(D.N - 1, (c0 + 1) * D.C - 1);
@@ -401,13 +580,8 @@ __global__ __launch_bounds__(64) void bwd_key_kernel(
             float wk_ = 0.f, wf = 0.f;
             if (pr < n_la) {
                 const size_t o = qoff(t0 + pr / G, g * G + pr % G);
-                const float* fr = phiq + o * DD;
-                const T* dr = dout + o * DD;
-                float kap = 0.f, dv_ = 0.f;
-                for (int i = 0; i < DD; ++i) {
-                    kap = fmaf(fk[i], fr[i], kap);
-                    dv_ = fmaf(vs[i], to_f32(dr[i]), dv_);
-                }
+                const float kap = dot_row<DD>(fk[kk], phiq + o * DD);
+                const float dv_ = dot_row<DD>(vs[kk], dout + o * DD);
                 const float cf = stat[o * 4 + 3];
                 wk_ = cf * kap;
                 wf = cf * (dv_ - stat[o * 4 + 2]);
@@ -421,18 +595,70 @@ __global__ __launch_bounds__(64) void bwd_key_kernel(
                 const T* dr = dout + o * DD;
 #pragma unroll
                 for (int p = 0; p < PL; ++p) {
-                    dva[p] = fmaf(a, to_f32(dr[lane + kWave * p]), dva[p]);
-                    dfa[p] = fmaf(c, fr[lane + kWave * p], dfa[p]);
+                    dva[kk][p] = fmaf(a, to_f32(dr[lane + kWave * p]), dva[kk][p]);
+                    dfa[kk][p] = fmaf(c, fr[lane + kWave * p], dfa[kk][p]);
                 }
             }
         }
     }
 #pragma unroll
-    for (int p = 0; p < PL; ++p) {
-        const size_t e = koff * DD + lane + kWave * p;
-        dk[e] = D.tau * dka[p];
-        dv[e] = dva[p];
-        dphik[e] = dfa[p];
+    for (int i = 0; i < kKB; ++i) {
+        if (jk[i] < 0) continue;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) {
+            const size_t e = koff(jk[i]) * DD + lane + kWave * p;
+            dk[e] = D.tau * dka[i][p];
+            dv[e] = dva[i][p];
+            dphik[e] = dfa[i][p];
+        }
+    }
+}
+
+// One wave per (b, g, four entries of the selected list): the softmax terms
+// of every query after the selected key's window (t >= j + W), added to dk
+// and dv (after bwd_key_win_kernel has written them; the entries of one
+// (b, g) list are distinct positions, so no two waves share a key).
+template <typename T, int DD>
+__global__ __launch_bounds__(64) void bwd_key_sel_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const int32_t* __restrict__ selw, const float* __restrict__ stat,
+    float* __restrict__ dk, float* __restrict__ dv, Dims D) {
+    constexpr int PL = DD / kWave;
+    const int e0 = blockIdx.x * kKB, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int n_list = D.n_full * D.lam;
+    const int32_t* sel = selw + ((size_t)b * D.Hkv + g) * n_list;
+    __shared__ float ks[kKB][DD];
+    __shared__ float vs[kKB][DD];
+    int jk[kKB];
+    int t_lo = D.N;
+#pragma unroll
+    for (int i = 0; i < kKB; ++i) {
+        jk[i] = e0 + i < n_list ? sel[e0 + i] : -1;
+        if (jk[i] >= 0) t_lo = min(t_lo, jk[i] + D.W);
+    }
+    auto koff = [&](int j) { return ((size_t)b * D.N + j) * D.Hkv + g; };
+    for (int x = lane; x < kKB * DD; x += kWave) {
+        const int i = x / DD, e = x % DD, j = max(jk[i], 0);
+        ks[i][e] = to_f32(k[koff(j) * DD + e]);
+        vs[i][e] = to_f32(v[koff(j) * DD + e]);
+    }
+    __syncthreads();
+    if (t_lo > D.N - 1) return;
+    float dka[kKB][PL], dva[kKB][PL];
+#pragma unroll
+    for (int i = 0; i < kKB; ++i)
+#pragma unroll
+        for (int p = 0; p < PL; ++p) dka[i][p] = dva[i][p] = 0.f;
+    key_group_softmax<T, DD>(q, dout, stat, ks, vs, jk, t_lo, D.N - 1, 1, b, g, D, lane, dka, dva);
+#pragma unroll
+    for (int i = 0; i < kKB; ++i) {
+        if (jk[i] < 0) continue;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) {
+            const size_t e = koff(jk[i]) * DD + lane + kWave * p;
+            dk[e] += D.tau * dka[i][p];
+            dv[e] += dva[i][p];
+        }
     }
 }
 
@@ -560,20 +786,27 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     if ((e = launch_la_chunks(D, w.phik, a.v, w.route, w.lin, s)) != hipSuccess) return e;
     if ((e = mark.fn(mark.ctx, "la_scan")) != hipSuccess) return e;
     if ((e = launch_la_scan(D, w.lin, -1, nullptr, nullptr, s)) != hipSuccess) return e;
-    STILL_STEP("bwd_query",
-               hipLaunchKernelGGL((bwd_query_kernel<T, DD>), dim3(D.N, D.Hq, D.B), dim3(64), 0, s,
-                                  q, k, v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.dq,
-                                  w.dphiq, w.stat, D));
+#define STILL_BWD_QUERY(GM)                                                                     \
+    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM>), dim3(D.N, D.Hkv, D.B), dim3(64), 0, s, q, k, \
+                       v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.dq, w.dphiq, w.stat, D)
+    STILL_STEP("bwd_query", if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
+                            else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));
+#undef STILL_BWD_QUERY
     STILL_STEP("bwd_uchunk",
                hipLaunchKernelGGL((bwd_uchunk_kernel<T, DD>), dim3(D.T, D.Hkv, D.B), dim3(256), 0,
                                   s, w.phiq, dout, w.stat, w.ust, D));
     STILL_STEP("bwd_suffix",
                hipLaunchKernelGGL(bwd_suffix_kernel, dim3((D.fd * (D.d + 1) + 255) / 256, D.Hkv, D.B),
                                   dim3(256), 0, s, w.ust, D));
-    STILL_STEP("bwd_key",
-               hipLaunchKernelGGL((bwd_key_kernel<T, DD>), dim3(D.N, D.Hkv, D.B), dim3(64), 0, s,
-                                  q, k, v, dout, w.phiq, w.phik, w.route, w.stat, w.ust, a.dk,
-                                  a.dv, w.dphik, D));
+    STILL_STEP("bwd_key_win",
+               hipLaunchKernelGGL((bwd_key_win_kernel<T, DD>), dim3((D.N + kKB - 1) / kKB, D.Hkv, D.B),
+                                  dim3(64), 0, s, q, k, v, dout, w.phiq, w.phik, w.route, w.stat,
+                                  w.ust, a.dk, a.dv, w.dphik, D));
+    if (D.lam > 0 && D.n_full > 0)
+        STILL_STEP("bwd_key_sel",
+                   hipLaunchKernelGGL((bwd_key_sel_kernel<T, DD>),
+                                      dim3((D.n_full * D.lam + kKB - 1) / kKB, D.Hkv, D.B), dim3(64),
+                                      0, s, q, k, v, dout, w.selw, w.stat, a.dk, a.dv, D));
     const int ntok = D.B * D.N, half = D.fd / 2;
     STILL_STEP("np_vjp_q",
                hipLaunchKernelGGL((np_vjp_kernel<T, DD>), dim3(ntok, D.Hq), dim3(64), 0, s, q,
@@ -598,7 +831,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 
 }  // namespace
 
-int bwd_launch_count() { return 15; }
+int bwd_launch_count() { return 16; }
 
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s,
                       BwdMark mark) {
