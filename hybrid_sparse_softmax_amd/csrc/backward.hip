@@ -541,63 +541,118 @@ __global__ __launch_bounds__(64) void bwd_key_win_kernel(
     if (D.W > 0)
         key_group_softmax<T, DD>(q, dout, stat, ks, vs, jk, j0, min(D.N - 1, j0 + kKB - 1 + D.W - 1),
                                  0, b, g, D, lane, dka, dva);
+    // linear part, one pass per chunk c0 holding some key's first linear
+    // query j + W: the suffix block c0 + 1 and the queries of chunk c0 are
+    // read once for all keys of the group that share c0
     const int G = D.G;
-    auto qoff = [&](int t, int h) { return ((size_t)b * D.N + t) * D.Hq + h; };
+    bool lak[kKB];
+    int c0k[kKB];
 #pragma unroll
-    for (int kk = 0; kk < kKB; ++kk) {
-        const int j = jk[kk];
-        if (j < 0) continue;
-        const int t0 = j + D.W;
-        if (route[((size_t)b * D.Hkv + g) * D.N + j] != kRouteLA || t0 > D.N - 1) continue;
-        const int c0 = t0 / D.C;
+    for (int i = 0; i < kKB; ++i) {
+        const int j = jk[i];
+        lak[i] = j >= 0 && j + D.W <= D.N - 1 && route[((size_t)b * D.Hkv + g) * D.N + j] == kRouteLA;
+        c0k[i] = lak[i] ? (j + D.W) / D.C : -1;
+    }
+    int c_lo = D.T, c_hi = -1;
+#pragma unroll
+    for (int i = 0; i < kKB; ++i)
+        if (lak[i]) {
+            c_lo = min(c_lo, c0k[i]);
+            c_hi = max(c_hi, c0k[i]);
+        }
+#pragma unroll 1
+    for (int c0 = c_lo; c0 <= c_hi; ++c0) {
+        bool mk[kKB];
+        bool any = false;
+        int t_a = D.N;
+#pragma unroll
+        for (int i = 0; i < kKB; ++i) {
+            mk[i] = lak[i] && c0k[i] == c0;
+            any = any || mk[i];
+            if (mk[i]) t_a = min(t_a, jk[i] + D.W);
+        }
+        if (!any) continue;
         if (c0 + 1 < D.T) {
             const float* U = ust + (((size_t)b * D.Hkv + g) * D.T + c0 + 1) * (size_t)(DD * (DD + 1));
+#pragma unroll 4
             for (int i = 0; i < DD; ++i) {
-                const float f = fk[kk][i];
+                float uv[PL];
 #pragma unroll
-                for (int p = 0; p < PL; ++p)
-                    dva[kk][p] = fmaf(f, U[(size_t)i * DD + lane + kWave * p], dva[kk][p]);
+                for (int p = 0; p < PL; ++p) uv[p] = U[(size_t)i * DD + lane + kWave * p];
+#pragma unroll
+                for (int kk = 0; kk < kKB; ++kk)
+                    if (mk[kk]) {
+                        const float f = fk[kk][i];
+#pragma unroll
+                        for (int p = 0; p < PL; ++p) dva[kk][p] = fmaf(f, uv[p], dva[kk][p]);
+                    }
             }
 #pragma unroll
             for (int p = 0; p < PL; ++p) {
                 const int i = lane + kWave * p;
                 const float4* row = reinterpret_cast<const float4*>(U + (size_t)i * DD);
-                float x = 0.f;
+                float x[kKB];
+#pragma unroll
+                for (int kk = 0; kk < kKB; ++kk) x[kk] = 0.f;
+#pragma unroll 4
                 for (int e4 = 0; e4 < DD / 4; ++e4) {
                     const float4 r = row[e4];
-                    x = fmaf(r.x, vs[kk][4 * e4], x);
-                    x = fmaf(r.y, vs[kk][4 * e4 + 1], x);
-                    x = fmaf(r.z, vs[kk][4 * e4 + 2], x);
-                    x = fmaf(r.w, vs[kk][4 * e4 + 3], x);
+#pragma unroll
+                    for (int kk = 0; kk < kKB; ++kk) {
+                        x[kk] = fmaf(r.x, vs[kk][4 * e4], x[kk]);
+                        x[kk] = fmaf(r.y, vs[kk][4 * e4 + 1], x[kk]);
+                        x[kk] = fmaf(r.z, vs[kk][4 * e4 + 2], x[kk]);
+                        x[kk] = fmaf(r.w, vs[kk][4 * e4 + 3], x[kk]);
+                    }
                 }
-                dfa[kk][p] = x - U[DD * DD + i];
+                const float zi = U[DD * DD + i];
+#pragma unroll
+                for (int kk = 0; kk < kKB; ++kk)
+                    if (mk[kk]) dfa[kk][p] += x[kk] - zi;
             }
         }
+        // queries of chunk c0 from the group's first linear query on
         const int t1 = min(D.N - 1, (c0 + 1) * D.C - 1);
-        const int n_la = (t1 - t0 + 1) * G;
+        const int n_la = (t1 - t_a + 1) * G;
+        auto row_of = [&](int pr) { return ((size_t)b * D.N + t_a + pr / G) * D.Hq + (size_t)g * G + pr % G; };
         for (int i0 = 0; i0 < n_la; i0 += kWave) {
             const int pr = i0 + lane;
-            float wk_ = 0.f, wf = 0.f;
+            float wk_[kKB], wf[kKB];
+#pragma unroll
+            for (int kk = 0; kk < kKB; ++kk) wk_[kk] = wf[kk] = 0.f;
             if (pr < n_la) {
-                const size_t o = qoff(t0 + pr / G, g * G + pr % G);
-                const float kap = dot_row<DD>(fk[kk], phiq + o * DD);
-                const float dv_ = dot_row<DD>(vs[kk], dout + o * DD);
-                const float cf = stat[o * 4 + 3];
-                wk_ = cf * kap;
-                wf = cf * (dv_ - stat[o * 4 + 2]);
+                const size_t o = row_of(pr);
+                const int t = t_a + pr / G;
+                float kap[kKB], vd[kKB];
+                dot_multi<DD, kKB>(fk, phiq + o * DD, kKB, kap);
+                dot_multi<DD, kKB>(vs, dout + o * DD, kKB, vd);
+                const float cf = stat[o * 4 + 3], Dt = stat[o * 4 + 2];
+#pragma unroll
+                for (int kk = 0; kk < kKB; ++kk)
+                    if (mk[kk] && t >= jk[kk] + D.W) {
+                        wk_[kk] = cf * kap[kk];
+                        wf[kk] = cf * (vd[kk] - Dt);
+                    }
             }
             const int nb = min(kWave, n_la - i0);
             for (int jj = 0; jj < nb; ++jj) {
-                const int pr2 = i0 + jj;
-                const size_t o = qoff(t0 + pr2 / G, g * G + pr2 % G);
-                const float a = __shfl(wk_, jj, kWave), c = __shfl(wf, jj, kWave);
-                const float* fr = phiq + o * DD;
-                const T* dr = dout + o * DD;
+                const size_t o = row_of(i0 + jj);
+                float de[PL], fe[PL];
 #pragma unroll
                 for (int p = 0; p < PL; ++p) {
-                    dva[kk][p] = fmaf(a, to_f32(dr[lane + kWave * p]), dva[kk][p]);
-                    dfa[kk][p] = fmaf(c, fr[lane + kWave * p], dfa[kk][p]);
+                    de[p] = to_f32(dout[o * DD + lane + kWave * p]);
+                    fe[p] = phiq[o * DD + lane + kWave * p];
                 }
+#pragma unroll
+                for (int kk = 0; kk < kKB; ++kk)
+                    if (mk[kk]) {
+                        const float a = __shfl(wk_[kk], jj, kWave), c = __shfl(wf[kk], jj, kWave);
+#pragma unroll
+                        for (int p = 0; p < PL; ++p) {
+                            dva[kk][p] = fmaf(a, de[p], dva[kk][p]);
+                            dfa[kk][p] = fmaf(c, fe[p], dfa[kk][p]);
+                        }
+                    }
             }
         }
     }
@@ -689,9 +744,16 @@ __global__ __launch_bounds__(64) void np_vjp_kernel(const T* __restrict__ x,
     const float nx = sqrtf(wave_sum(ss));
     const bool act = lane < half;
     float u = 0.f;
-    if (act) {
-        const float* pr = P + (size_t)lane * DD;
-        for (int i = 0; i < DD; ++i) u = fmaf(pr[i], xs[i], u);
+    if (act) {  // P rows are 16-byte aligned: the projections are checked aligned, d is 64 or 128
+        const float4* pr = reinterpret_cast<const float4*>(P + (size_t)lane * DD);
+#pragma unroll 8
+        for (int i = 0; i < DD / 4; ++i) {
+            const float4 w = pr[i];
+            u = fmaf(w.x, xs[4 * i], u);
+            u = fmaf(w.y, xs[4 * i + 1], u);
+            u = fmaf(w.z, xs[4 * i + 2], u);
+            u = fmaf(w.w, xs[4 * i + 3], u);
+        }
     }
     const float nu = sqrtf(wave_sum(u * u));
     const float uh = nu > 0.f ? u / nu : 0.f;

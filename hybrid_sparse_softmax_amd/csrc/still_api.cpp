@@ -366,9 +366,9 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
 // backward
 // ---------------------------------------------------------------------------
 static int bwd_slices(const Dims& D) {
-    // token slices of the projection-gradient sums: about 512 blocks in all
+    // token slices of the projection-gradient sums: about 2048 blocks in all
     const int64_t ntok = (int64_t)D.B * D.N;
-    int64_t n = (512 + D.Hkv - 1) / D.Hkv;
+    int64_t n = (2048 + D.Hkv - 1) / D.Hkv;
     if (n > ntok) n = ntok;
     return n < 1 ? 1 : (int)n;
 }
