@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "hybrid_main": ["hybrid_sparse_softmax_amd/csrc/prefill_mfma.hip",
                     "hybrid_sparse_softmax_amd/csrc/mfma_common.h"],
     "dec_stream": ["hybrid_sparse_softmax_amd/csrc/decode_fast.hip"],
+    "bwd_query": ["hybrid_sparse_softmax_amd/csrc/backward.hip"],
 }
 
 
@@ -400,7 +401,7 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
         achieved = fl[dom] / (kern[dom] * 1e-3) / 1e12
         roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP32_VALU_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_VALU_TFLOPS, 4),
-                "traffic": None, "kernel": dom, "avg_ms": round(kern[dom], 4),
+                "traffic": measured_traffic(dom, name), "kernel": dom, "avg_ms": round(kern[dom], 4),
                 "algorithmic_flop_per_launch": fl[dom]}
     total = sum(fl.values())
     tokens = cfg["batch"] * cfg["seqlen"]
@@ -459,6 +460,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step and print its JSON object")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward pass and print its JSON object")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 256 MiB device copy three times (counter calibration)")
     args = ap.parse_args()
@@ -485,6 +488,9 @@ def main():
         return
     if args.decode_only:
         print(json.dumps(bench_decode(still, torch, args.steps, args.warmup)), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps(bench_backward(still, torch, args.steps, args.warmup)), flush=True)
         return
     pre = bench_prefill(still, torch, args.workload, args.steps, args.warmup)
     cfg = pre["cfg"]

@@ -43,6 +43,19 @@ namespace {
 
 constexpr float kNegInfB = -__builtin_inff();
 
+// Work item of a 1-D launch of nx * ny * nz blocks, laid out so that the
+// blocks of one (y, z) pair -- one (sequence, KV head), whose waves read the
+// same query and key rows -- run on one XCD and share its L2: the hardware
+// hands block L to XCD L mod 8, so block L takes item (L mod 8) * per + L / 8.
+struct Item {
+    int x, y, z;
+};
+__device__ __forceinline__ Item xcd_item(int nx, int ny) {
+    const int L = blockIdx.x, total = gridDim.x, per = total / 8;
+    const int w = L < per * 8 ? (L % 8) * per + L / 8 : L;
+    return Item{w % nx, (w / nx) % ny, w / (nx * ny)};
+}
+
 __global__ __launch_bounds__(256) void bwd_route_kernel(const int32_t* __restrict__ sel_in,
                                                         uint8_t* __restrict__ route,
                                                         int32_t* __restrict__ selw, Dims D) {
@@ -161,7 +174,8 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
     const float* __restrict__ lin, float* __restrict__ dq, float* __restrict__ dphiq,
     float* __restrict__ stat, Dims D) {
     constexpr int PL = DD / kWave;
-    const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const Item it = xcd_item(D.N, D.Hkv);
+    const int t = it.x, g = it.y, b = it.z, lane = threadIdx.x;
     const int G = D.G;
     __shared__ float qs[GM][DD];
     __shared__ float fq[GM][DD];
@@ -518,7 +532,8 @@ __global__ __launch_bounds__(64) void bwd_key_win_kernel(
     const float* __restrict__ ust, float* __restrict__ dk, float* __restrict__ dv,
     float* __restrict__ dphik, Dims D) {
     constexpr int PL = DD / kWave;
-    const int j0 = blockIdx.x * kKB, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const Item it = xcd_item((D.N + kKB - 1) / kKB, D.Hkv);
+    const int j0 = it.x * kKB, g = it.y, b = it.z, lane = threadIdx.x;
     __shared__ float ks[kKB][DD];
     __shared__ float vs[kKB][DD];
     __shared__ float fk[kKB][DD];
@@ -679,7 +694,8 @@ __global__ __launch_bounds__(64) void bwd_key_sel_kernel(
     const T* __restrict__ dout, const int32_t* __restrict__ selw, const float* __restrict__ stat,
     float* __restrict__ dk, float* __restrict__ dv, Dims D) {
     constexpr int PL = DD / kWave;
-    const int e0 = blockIdx.x * kKB, g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const Item it = xcd_item((D.n_full * D.lam + kKB - 1) / kKB, D.Hkv);
+    const int e0 = it.x * kKB, g = it.y, b = it.z, lane = threadIdx.x;
     const int n_list = D.n_full * D.lam;
     const int32_t* sel = selw + ((size_t)b * D.Hkv + g) * n_list;
     __shared__ float ks[kKB][DD];
@@ -849,7 +865,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     if ((e = mark.fn(mark.ctx, "la_scan")) != hipSuccess) return e;
     if ((e = launch_la_scan(D, w.lin, -1, nullptr, nullptr, s)) != hipSuccess) return e;
 #define STILL_BWD_QUERY(GM)                                                                     \
-    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM>), dim3(D.N, D.Hkv, D.B), dim3(64), 0, s, q, k, \
+    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM>), dim3(D.N * D.Hkv * D.B), dim3(64), 0, s, q, k, \
                        v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.dq, w.dphiq, w.stat, D)
     STILL_STEP("bwd_query", if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
                             else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));
@@ -861,13 +877,13 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
                hipLaunchKernelGGL(bwd_suffix_kernel, dim3((D.fd * (D.d + 1) + 255) / 256, D.Hkv, D.B),
                                   dim3(256), 0, s, w.ust, D));
     STILL_STEP("bwd_key_win",
-               hipLaunchKernelGGL((bwd_key_win_kernel<T, DD>), dim3((D.N + kKB - 1) / kKB, D.Hkv, D.B),
+               hipLaunchKernelGGL((bwd_key_win_kernel<T, DD>), dim3((D.N + kKB - 1) / kKB * D.Hkv * D.B),
                                   dim3(64), 0, s, q, k, v, dout, w.phiq, w.phik, w.route, w.stat,
                                   w.ust, a.dk, a.dv, w.dphik, D));
     if (D.lam > 0 && D.n_full > 0)
         STILL_STEP("bwd_key_sel",
                    hipLaunchKernelGGL((bwd_key_sel_kernel<T, DD>),
-                                      dim3((D.n_full * D.lam + kKB - 1) / kKB, D.Hkv, D.B), dim3(64),
+                                      dim3((D.n_full * D.lam + kKB - 1) / kKB * D.Hkv * D.B), dim3(64),
                                       0, s, q, k, v, dout, w.selw, w.stat, a.dk, a.dv, D));
     const int ntok = D.B * D.N, half = D.fd / 2;
     STILL_STEP("np_vjp_q",
