@@ -56,6 +56,11 @@ R-ROUTE   The routing criteria the pages compare with Self-Saliency under the
           uniform: splitmix64 (Steele, Lea and Flood 2014, in Vigna's
           formulation) of the counter ((b * Hkv + g) << 32) | t, top 24 bits
           times 2^-24, so any implementation reproduces it exactly.
+R-UTIL    The future-KV-utility diagnostic (full text App. A.7.4, Table 12):
+          a remote key's utility is the total full causal attention weight
+          that every query after its window (t >= j + W) gives it, summed
+          over the group's query heads; the selected remote tokens are
+          compared with as many eligible keys ranked by that utility.
 R-BWD     Gradients (the backward pass the pages need for their two-stage
           linearization: Sec. 4.1 "Experimental Setups", training strategy;
           App. A.6.1, primary configuration) treat the routing as a
@@ -636,3 +641,50 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None):
         dk[:, :, g, :] += dx
         dwk[g] += dP
     return dict(dq=dq, dk=dk, dv=dv, dwq=dwq, dwk=dwk)
+
+
+# --------------------------------------------------------------------------
+# Future KV utility (full text App. A.7.4, Table 12).  R-UTIL: a remote key
+# j (one that has left the window of some later query, j <= N-1-W) is worth
+# the total full-attention weight the queries after its window give it,
+#     u[b, g, j] = sum over the query heads h of KV head g and the queries
+#                  t >= j + W of softmax_j'(tau q_t,h . k_j'), j' <= t
+# (full causal attention, nothing routed).  The diagnostic compares the
+# routed-out tokens a criterion selected with the same number of eligible
+# keys ranked by u (higher first, then lower position).
+# --------------------------------------------------------------------------
+def future_kv_utility(q, k, p: Params, n_kv_heads: int) -> np.ndarray:
+    """u [B, Hkv, N] for q [B,N,Hq,d], k [B,N,Hkv,d] (float64)."""
+    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    B, N, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    W, tau = p.window, p.tau(d)
+    t = np.arange(N)
+    causal = t[None, :] <= t[:, None]                 # [query t, key j]: j <= t
+    remote = t[None, :] <= t[:, None] - W             # j <= t - W, i.e. t >= j + W
+    u = np.zeros((B, n_kv_heads, N))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = tau * (q[b, :, h, :] @ k[b, :, g, :].T)
+            a = _masked_softmax(np.where(causal, s, -np.inf))
+            u[b, g] += np.where(remote, a, 0.0).sum(axis=0)
+    return u
+
+
+def kv_utility_overlap(sel_idx, util, N: int, W: int) -> np.ndarray:
+    """[B, Hkv, 2]: (m, overlap) per (sequence, KV head): m = selected tokens
+    that are eligible remote keys (j <= N-1-W), overlap = how many of them
+    are among the top-m eligible keys by utility."""
+    sel_idx = np.asarray(sel_idx, np.int64)
+    B, Hkv = util.shape[:2]
+    elig = np.arange(max(0, N - W))
+    out = np.zeros((B, Hkv, 2), np.int64)
+    for b in range(B):
+        for g in range(Hkv):
+            chosen = set(int(j) for j in sel_idx[b, g].reshape(-1) if 0 <= j < elig.size)
+            m = len(chosen)
+            order = rank_order(util[b, g, elig], elig)
+            top = set(elig[order[:m]].tolist())
+            out[b, g] = (m, len(chosen & top))
+    return out

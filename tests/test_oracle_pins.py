@@ -415,3 +415,60 @@ def test_direct_equals_recurrent_for_each_route(route):
     direct = O.fwd_direct(q, k, v, wq, wk, p)
     rec, cache = O.fwd_recurrent(q, k, v, wq, wk, p)
     np.testing.assert_allclose(rec, direct["out"], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------- future KV utility (App. A.7.4)
+def _sdpa_attention_matrix(q, k, h, g):
+    """The full causal attention matrix of head h from torch's SDPA with the
+    identity as values (out = A I = A), float64."""
+    N, d = q.shape[1], q.shape[3]
+    tq = torch.from_numpy(q[0, :, h, :])[None, None]
+    tk = torch.from_numpy(k[0, :, g, :])[None, None]
+    eye = torch.eye(N, dtype=torch.float64)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, eye, is_causal=True)[0, 0].numpy()
+
+
+@pytest.mark.parametrize("W", [0, 4, 9])
+def test_future_utility_against_sdpa_attention_matrix(W):
+    q, k, v, wq, wk = rand_inputs(21, 1, 23, 4, 2, 8, scale_k=1.5)
+    p = O.Params(window=W, chunk=4, topk=0)
+    u = O.future_kv_utility(q, k, p, 2)
+    t = np.arange(23)
+    remote = t[None, :] <= t[:, None] - W
+    for g in range(2):
+        ref = sum(np.where(remote, _sdpa_attention_matrix(q, k, h, g), 0.0).sum(0) for h in (2 * g, 2 * g + 1))
+        np.testing.assert_allclose(u[0, g], ref, rtol=1e-12, atol=1e-14)
+    if W == 0:
+        # every query row sums to one: the utilities of a KV head add up to G N
+        np.testing.assert_allclose(u[0].sum(-1), 2 * 23, rtol=1e-12)
+    else:
+        # keys with no query after their window carry nothing
+        assert np.all(u[0, :, 23 - W:] == 0)
+
+
+def test_future_utility_two_tokens_closed_form():
+    """N = 2, W = 1: only query 1 looks past key 0's window, so
+    u[0] = e^{s10} / (e^{s10} + e^{s11}) and u[1] = 0."""
+    q = np.array([[[[0.3, -1.2]], [[0.7, 0.4]]]])
+    k = np.array([[[[1.0, 0.5]], [[-0.2, 0.9]]]])
+    p = O.Params(window=1, chunk=1, topk=0)
+    u = O.future_kv_utility(q, k, p, 1)
+    tau = 1 / math.sqrt(2)
+    s10, s11 = tau * q[0, 1, 0] @ k[0, 0, 0], tau * q[0, 1, 0] @ k[0, 1, 0]
+    assert abs(u[0, 0, 0] - math.exp(s10) / (math.exp(s10) + math.exp(s11))) < 1e-15
+    assert u[0, 0, 1] == 0.0
+
+
+def test_utility_overlap_counts_by_brute_force():
+    rng = np.random.default_rng(4)
+    N, W = 40, 8
+    util = rng.random((1, 1, N))
+    sel = np.array([[[[3, 7], [9, 14], [17, 20], [25, 30], [33, 36]]]])  # 33, 36 are in the window region
+    m, ov = O.kv_utility_overlap(sel, util, N, W)[0, 0]
+    elig = list(range(N - W))
+    chosen = {3, 7, 9, 14, 17, 20, 25, 30}
+    top = sorted(elig, key=lambda j: (-util[0, 0, j], j))[:len(chosen)]
+    assert m == 8 and ov == len(chosen & set(top))
+    # selecting exactly the top keys gives full overlap
+    sel2 = np.array(sorted(top)).reshape(1, 1, 4, 2)
+    assert tuple(O.kv_utility_overlap(sel2, util, N, W)[0, 0]) == (8, 8)
