@@ -19,7 +19,7 @@ LIB = os.path.join(OUT_DIR, "libstill.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["still_api.cpp", "general.hip", "decode.hip", "decode_fast.hip", "prefill_mfma.hip",
-           "backward.hip"]
+           "backward.hip", "utility.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -148,4 +148,9 @@ int bwd_launch_count();
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s, BwdMark mark);
 hipError_t launch_zero(float* p, int n, hipStream_t s);
 
+// ---- future-KV-utility diagnostic (general kernels) ----------------------
+// stat [B, N, Hq, 2] fp32 scratch; util [B, Hkv, N] fp32, written
+hipError_t launch_future_utility(const Dims& D, const void* q, const void* k, float* stat,
+                                 float* util, hipStream_t s);
+
 }  // namespace still

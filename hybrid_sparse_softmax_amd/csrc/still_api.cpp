@@ -452,6 +452,25 @@ static int bwd(const still_shape* sh, const void* q, const void* k, const void* 
     return STILL_OK;
 }
 
+// ---------------------------------------------------------------------------
+// future-KV-utility diagnostic
+// ---------------------------------------------------------------------------
+static size_t util_bytes(const Dims& D) { return (size_t)D.B * D.N * D.Hq * 2 * sizeof(float) + 256; }
+
+static int future_utility(const still_shape* sh, const void* q, const void* k, float* util,
+                          void* ws, size_t ws_bytes, hipStream_t s) {
+    int st = check_shape(sh, false);
+    if (st) return st;
+    const Dims D = make_dims(sh, sh->seqlen);
+    if (D.B == 0 || D.N == 0) return STILL_OK;
+    if (!q || !k || !util) return STILL_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(util) & 3u)) return STILL_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < util_bytes(D)) return STILL_ERR_WORKSPACE;
+    float* stat = reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    STILL_TRY(launch_future_utility(D, q, k, stat, util, s));
+    return STILL_OK;
+}
+
 }  // namespace still
 
 // ---------------------------------------------------------------------------
@@ -593,6 +612,19 @@ int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const v
                               dwphi_k, workspace, workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
+}
+
+int still_future_kv_utility_workspace_size(const still_shape* shape, size_t* bytes) {
+    if (!bytes) return STILL_ERR_INVALID_ARG;
+    const int st = still::check_shape(shape, false);
+    if (st) return st;
+    *bytes = still::util_bytes(still::make_dims(shape, shape->seqlen));
+    return STILL_OK;
+}
+
+int still_future_kv_utility(const still_shape* shape, const void* q, const void* k, float* util,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return still::future_utility(shape, q, k, util, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -31,6 +31,7 @@ EXPORTED = (
     "still_hybrid_attn_fwd_timed", "still_hybrid_attn_decode_step_timed",
     "still_hybrid_attn_decode_step_ragged",
     "still_bwd_workspace_size", "still_hybrid_attn_bwd", "still_hybrid_attn_bwd_timed",
+    "still_future_kv_utility_workspace_size", "still_future_kv_utility",
 )
 
 
@@ -92,6 +93,10 @@ def lib() -> ct.CDLL:
         L.still_hybrid_attn_bwd.restype = ct.c_int
         L.still_hybrid_attn_bwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, sz, vp]
+        L.still_future_kv_utility_workspace_size.restype = ct.c_int
+        L.still_future_kv_utility_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
+        L.still_future_kv_utility.restype = ct.c_int
+        L.still_future_kv_utility.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, sz, vp]
         ev = [ct.POINTER(ct.c_void_p), ct.c_int32, ct.POINTER(ct.c_int32), ct.POINTER(ct.c_char_p)]
         L.still_hybrid_attn_bwd_timed.restype = ct.c_int
         L.still_hybrid_attn_bwd_timed.argtypes = L.still_hybrid_attn_bwd.argtypes + ev
@@ -364,3 +369,24 @@ def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6
     else:
         _check(lib().still_hybrid_attn_bwd_timed(*args, *timer.args()), "still_hybrid_attn_bwd_timed")
     return res
+
+
+def future_kv_utility(q, k, *, window, chunk=64, softmax_scale=0.0, workspace=None):
+    """still_future_kv_utility: util [B, Hkv, N] fp32, the full causal
+    attention weight each key receives from the queries after its window,
+    summed over the group's query heads."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
+                    chunk=chunk, topk=0, softmax_scale=softmax_scale, dtype=q.dtype)
+    _expect(q, "q", q.dtype, (B, N, Hq, d))
+    _expect(k, "k", q.dtype, (B, N, Hkv, d))
+    util = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device)
+    n = ct.c_size_t(0)
+    _check(lib().still_future_kv_utility_workspace_size(ct.byref(sh), ct.byref(n)),
+           "still_future_kv_utility_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=q.device)
+    _check(lib().still_future_kv_utility(ct.byref(sh), _ptr(q), _ptr(k), _ptr(util), _ptr(workspace),
+                                         workspace.numel(), _stream()), "still_future_kv_utility")
+    return util

@@ -260,6 +260,26 @@ int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k
                           float* dwphi_k, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* Bytes of device workspace still_future_kv_utility needs for `shape`. */
+int still_future_kv_utility_workspace_size(const still_shape* shape, size_t* bytes);
+
+/* Future-KV-utility diagnostic (full text App. A.7.4, Table 12): how much
+ * full causal attention each remote key receives from the queries after its
+ * window,
+ *   util[b, g, j] = sum over the query heads h of KV head g and the queries
+ *                   t >= j + W of softmax over j' <= t of (tau q_t,h . k_j')
+ * (plain causal softmax attention: nothing is routed).  Keys with no query
+ * after their window (j > N - 1 - W) get 0.  Ranking the eligible keys
+ * j <= N - 1 - W by util and comparing the top ones with the tokens a
+ * routing criterion selected measures how well a causal local score
+ * predicts future use.
+ *   q [B, N, Hq, d], k [B, N, Hkv, d] dtype, read only; util [B, Hkv, N]
+ *   fp32, written.  Only batch, seqlen, heads, head_dim, window, eps,
+ *   softmax_scale and dtype of the shape matter; it must still be valid.
+ * N == 0 or B == 0 is a no-op.  Errors as for the forward. */
+int still_future_kv_utility(const still_shape* shape, const void* q, const void* k, float* util,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Instrumented forms of the entry points, for measurement (they compute
  * exactly what the plain calls compute).  Before the i-th kernel launch the
  * call records events[i] on `stream`, and events[n] after the last launch,

@@ -216,3 +216,17 @@ def test_bwd_checks():
 def test_bwd_empty_problem_without_projection_gradients_is_noop():
     for kw in (dict(seqlen=0), dict(batch=0)):
         assert bwd_status(shape(**kw), sel=None, ws=None, ws_bytes=0, ptr=None, dw=None) == S.STILL_OK
+
+
+def test_future_utility_checks():
+    sh = shape()
+    n = ct.c_size_t(0)
+    assert S.lib().still_future_kv_utility_workspace_size(ct.byref(sh), ct.byref(n)) == S.STILL_OK
+    assert n.value >= 1 * 256 * 4 * 2 * 4
+    f = S.lib().still_future_kv_utility
+    assert f(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, n.value - 1, None) == S.STILL_ERR_WORKSPACE
+    assert f(ct.byref(sh), None, FAKE, FAKE, FAKE, n.value, None) == S.STILL_ERR_INVALID_ARG
+    assert f(ct.byref(sh), MISALIGNED, FAKE, FAKE, FAKE, n.value, None) == S.STILL_ERR_INVALID_ARG
+    assert f(ct.byref(sh), FAKE, FAKE, ct.c_void_p(0x1002), FAKE, n.value, None) == S.STILL_ERR_INVALID_ARG
+    assert f(ct.byref(shape(head_dim=96)), FAKE, FAKE, FAKE, FAKE, n.value, None) == S.STILL_ERR_UNSUPPORTED
+    assert f(ct.byref(shape(seqlen=0)), None, None, None, None, 0, None) == S.STILL_OK
