@@ -8,7 +8,8 @@ accumulation), inputs resident in HBM.  The decode step (batch 64 at
 position 16384) is timed the same way and reported in the "decode" object,
 and its serving form (the same batch with one position per sequence) in
 "decode_ragged"; the backward pass (gradients w.r.t. q, k, v and the NP-Map
-projections) on the 8 x 2048 training batch in "backward".
+projections) on the 8 x 2048 training batch in "backward"; the future-KV-utility
+diagnostic of the routing criteria on the 4K prefill in "future_kv_utility".
 
 Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
 the launch stream by the library's *_timed entry points; the roofline uses
@@ -417,6 +418,51 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()}, "roofline": roof}
 
 
+def bench_utility(still, torch, name="prefill_4k"):
+    """Future-KV-utility diagnostic (full text App. A.7.4, Table 12) on the
+    4K prefill: the library's utilities of every remote key, then for each
+    routing criterion the share of its selected remote tokens that are
+    among as many keys ranked by utility (higher first, then lower
+    position).  Synthetic inputs: the shares say how each criterion behaves
+    on this distribution, not on a trained model."""
+    cfg = workloads.CONFIGS[name]
+    seed = workloads.seed_of(name)
+    raw = workloads.make_prefill(cfg, seed)
+    dev = {k: torch.from_numpy(raw[k]).to(torch.bfloat16).cuda() for k in ("q", "k", "v")}
+    for k in ("wphi_q", "wphi_k"):
+        dev[k] = torch.from_numpy(raw[k]).cuda()
+    W, C, lam, N = cfg["window"], cfg["chunk"], cfg["topk"], cfg["seqlen"]
+    still.future_kv_utility(dev["q"], dev["k"], window=W, chunk=C)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    u = still.future_kv_utility(dev["q"], dev["k"], window=W, chunk=C)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    u = u.cpu().numpy()
+    elig = np.arange(max(0, N - W))
+    shares = {}
+    for route in still.ROUTES:
+        sel = still.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W, chunk=C,
+                        topk=lam, return_sel=True, route=route)["sel_idx"].cpu().numpy()
+        hit = tot = 0
+        for b in range(sel.shape[0]):
+            for g in range(sel.shape[1]):
+                chosen = set(int(j) for j in sel[b, g].ravel() if j < elig.size)
+                order = np.lexsort((elig, -u[b, g, elig]))
+                top = set(elig[order[:len(chosen)]].tolist())
+                hit += len(chosen & top)
+                tot += len(chosen)
+        shares[route] = round(hit / max(tot, 1), 4)
+    log(f"[bench] {name} future-KV utility: {ms:.2f} ms; overlap " +
+        ", ".join(f"{k}={v:.1%}" for k, v in shares.items()))
+    return {"metric": "share of selected remote tokens among the top keys by future full-attention weight",
+            "workload": f"{name}: batch {cfg['batch']}, seq {N}, {cfg['n_q_heads']} q / {cfg['n_kv_heads']} KV "
+                        f"heads, window {W}, chunk {C}, top-{lam}; synthetic inputs",
+            "utility_ms": round(ms, 3), "overlap": shares}
+
+
 def cpu_baseline(raw, cfg, n_rows=12):
     """The oracle as it stands, on a bounded sample: group scores and
     selection over the whole sequence, then n_rows output rows evaluated one
@@ -457,6 +503,7 @@ def main():
     ap.add_argument("--workload", default="prefill_16k", choices=["prefill_4k", "prefill_16k", "train_8x2k"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-utility", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step and print its JSON object")
@@ -498,6 +545,7 @@ def main():
     dec_r = None if args.no_decode else bench_decode_ragged(still, torch, args.steps, args.warmup)
     bwd = None if args.no_backward else bench_backward(still, torch, max(3, args.steps // 4),
                                                          args.warmup)
+    util = None if args.no_utility else bench_utility(still, torch)
     cpu = None if args.no_cpu else cpu_baseline(pre["raw"], cfg)
     tok_s = pre["tokens"] / (pre["ms"] * 1e-3)
     line = {
@@ -516,6 +564,7 @@ def main():
         "decode": dec,
         "decode_ragged": dec_r,
         "backward": bwd,
+        "future_kv_utility": util,
     }
     print(json.dumps(line), flush=True)
 
