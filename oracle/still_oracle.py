@@ -566,12 +566,15 @@ def np_map_vjp(x, P, dphi):
     return dx, dP
 
 
-def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None):
+def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None):
     """Gradients of L = sum(dout * out) with out = fwd_direct(q, k, v, wq,
     wk, p) and the routing fixed to ``sel_idx`` [B, Hkv, N//C, lambda]
     (the forward's own selection when None).
 
     Returns dict(dq, dk, dv [shapes of q, k, v], dwq, dwk [shape of wq]).
+    rows: optional list of distinct (b, t); then only those queries are visited and
+    only dq is returned (NaN elsewhere): dq of a query depends on that query
+    alone, while every key-side gradient sums over all queries.
 
     Per query t of head h (KV head g), with the sets of fwd_direct:
       w_j = exp(s_j - M) on SA_t, exp(-M) kappa_j on LA_t, kappa_j = phi_q . phi_k(k_j)
@@ -601,36 +604,44 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None):
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     dphiq = np.zeros(q.shape[:3] + (2 * wq.shape[1],))
     dphik = np.zeros_like(phik)
-    for b in range(B):
-        for t in range(N):
-            r_end = t - W + 1
+    visit = [(b, t) for b in range(B) for t in range(N)] if rows is None else list(rows)
+    for b, t in visit:
+        r_end = t - W + 1
+        for g in range(Hkv):
+            win = np.arange(max(0, t - W + 1), t + 1) if W > 0 else np.arange(0)
+            routed = np.arange(0, max(0, r_end))
+            rr = route[b, g, routed]
+            if np.any(rr == PENDING):
+                raise AssertionError("a routed token has no decision")
+            sa = np.concatenate([routed[rr == ROUTE_SA], win])
+            la = routed[rr == ROUTE_LA]
+            for h in range(g * G, (g + 1) * G):
+                qv, do = q[b, t, h], dout[b, t, h]
+                s = tau * (k[b, sa, g, :] @ qv)
+                fq = np_map(qv, wq[g])
+                kap = phik[b, la, g, :] @ fq
+                M = max(0.0, s.max()) if s.size else 0.0
+                w_sa = np.exp(s - M)
+                w_la = math.exp(-M) * kap
+                den = w_sa.sum() + w_la.sum()
+                o = (w_sa @ v[b, sa, g, :] + w_la @ v[b, la, g, :]) / den
+                Dt = do @ o
+                ds = (w_sa / den) * (v[b, sa, g, :] @ do - Dt)
+                dq[b, t, h] += tau * (ds @ k[b, sa, g, :])
+                np.add.at(dk[b, :, g, :], sa, tau * np.outer(ds, qv))
+                np.add.at(dv[b, :, g, :], sa, np.outer(w_sa / den, do))
+                dkap = (math.exp(-M) / den) * (v[b, la, g, :] @ do - Dt)
+                dphiq[b, t, h] += dkap @ phik[b, la, g, :]
+                np.add.at(dphik[b, :, g, :], la, np.outer(dkap, fq))
+                np.add.at(dv[b, :, g, :], la, np.outer(w_la / den, do))
+    if rows is not None:
+        dq_rows = np.full(q.shape, np.nan)
+        for b, t in visit:
             for g in range(Hkv):
-                win = np.arange(max(0, t - W + 1), t + 1) if W > 0 else np.arange(0)
-                routed = np.arange(0, max(0, r_end))
-                rr = route[b, g, routed]
-                if np.any(rr == PENDING):
-                    raise AssertionError("a routed token has no decision")
-                sa = np.concatenate([routed[rr == ROUTE_SA], win])
-                la = routed[rr == ROUTE_LA]
                 for h in range(g * G, (g + 1) * G):
-                    qv, do = q[b, t, h], dout[b, t, h]
-                    s = tau * (k[b, sa, g, :] @ qv)
-                    fq = np_map(qv, wq[g])
-                    kap = phik[b, la, g, :] @ fq
-                    M = max(0.0, s.max()) if s.size else 0.0
-                    w_sa = np.exp(s - M)
-                    w_la = math.exp(-M) * kap
-                    den = w_sa.sum() + w_la.sum()
-                    o = (w_sa @ v[b, sa, g, :] + w_la @ v[b, la, g, :]) / den
-                    Dt = do @ o
-                    ds = (w_sa / den) * (v[b, sa, g, :] @ do - Dt)
-                    dq[b, t, h] += tau * (ds @ k[b, sa, g, :])
-                    np.add.at(dk[b, :, g, :], sa, tau * np.outer(ds, qv))
-                    np.add.at(dv[b, :, g, :], sa, np.outer(w_sa / den, do))
-                    dkap = (math.exp(-M) / den) * (v[b, la, g, :] @ do - Dt)
-                    dphiq[b, t, h] += dkap @ phik[b, la, g, :]
-                    np.add.at(dphik[b, :, g, :], la, np.outer(dkap, fq))
-                    np.add.at(dv[b, :, g, :], la, np.outer(w_la / den, do))
+                    dx, _ = np_map_vjp(q[b, t, h], wq[g], dphiq[b, t, h])
+                    dq_rows[b, t, h] = dq[b, t, h] + dx
+        return dict(dq=dq_rows)
     dwq, dwk = np.zeros_like(wq), np.zeros_like(wk)
     for g in range(Hkv):
         for h in range(g * G, (g + 1) * G):

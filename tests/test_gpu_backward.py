@@ -148,3 +148,43 @@ def test_bwd_all_selected_at_4k_is_causal_softmax_gradient(gpu_lib):
         say(f"  {key} rel-L2 vs SDPA {err:.2e}")
         assert err <= GRAD_TOL
     assert torch.count_nonzero(g["dwphi_q"]) == 0 and torch.count_nonzero(g["dwphi_k"]) == 0
+
+
+def test_bwd_train_8x2k_sampled_rows_and_value_sums(gpu_lib):
+    """At the full training-batch size (8 x 2048, 32 / 8 heads, d 128, top-16)
+    in the bench's launch configuration: dq on sampled query rows against the
+    oracle, one row at a time; and sum_j dv_j = the sum of dout over the
+    group's queries, because every query's weights over its softmax and
+    linear tokens sum to one -- a property of the whole routing at any size,
+    held to the fp32 rounding of the sums (1e-5 of sum_j |dv_j|)."""
+    from parity import sampled_rows
+    name = "train_8x2k"
+    cfg, seed = workloads.CONFIGS[name], workloads.seed_of(name)
+    say(f"[bwd] {name} sampled rows shape={workloads.shape_of(cfg)} seed={seed}")
+    raw = workloads.make_prefill(cfg, seed)
+    dev, ref = prepare(raw, torch.bfloat16)
+    dout_h = torch.from_numpy(workloads.make_grad_out(cfg, seed)).to(torch.bfloat16)
+    dout = dout_h.cuda()
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    sel = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W, chunk=C,
+                      topk=lam, return_sel=True)["sel_idx"]
+    g = gpu_lib.bwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], sel, dout,
+                    window=W, chunk=C, topk=lam)
+    torch.cuda.synchronize()
+    B, N, Hq, d = dev["q"].shape
+    Hkv = cfg["n_kv_heads"]
+    rows = sampled_rows(B, N, C, n_per_batch=3, seed=5)
+    p = O.Params(window=W, chunk=C, topk=lam)
+    o = O.bwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"],
+                     dout_h.double().numpy(), p, sel_idx=sel.cpu().numpy().astype(np.int64), rows=rows)
+    bi, ti = np.array([r[0] for r in rows]), np.array([r[1] for r in rows])
+    err = rel_l2(g["dq"].double().cpu().numpy()[bi, ti], o["dq"][bi, ti])
+    say(f"  dq rel-L2 over {len(rows)} sampled rows: {err:.2e}")
+    assert err <= GRAD_TOL
+    dv = g["dv"].double()
+    lhs = dv.sum(dim=1)                                           # [B, Hkv, d]
+    rhs = dout_h.double().cuda().reshape(B, N, Hkv, Hq // Hkv, d).sum(dim=(1, 3))
+    bound = 1e-5 * dv.abs().sum(dim=1) + 1e-6
+    worst = float(((lhs - rhs).abs() / bound).max())
+    say(f"  sum_j dv_j vs sum of dout: worst |diff| / bound {worst:.3f}")
+    assert worst <= 1.0

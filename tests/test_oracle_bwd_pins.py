@@ -146,3 +146,16 @@ def test_bwd_pure_linear_attention_values_gradient():
     A = A / A.sum(1, keepdims=True)
     g = O.bwd_direct(q, k, v, wq, wk, dout, p)
     np.testing.assert_allclose(g["dv"][0, :, 0], A.T @ dout[0, :, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_bwd_sampled_rows_equal_full_dq():
+    """The sampled-rows mode (used for full-size parity) visits only the
+    given queries; their dq must equal the full computation's."""
+    q, k, v, wq, wk, dout = rand_inputs(9, 2, 21, 4, 2, 8, scale_k=1.5)
+    p = O.Params(window=4, chunk=4, topk=2)
+    full = O.bwd_direct(q, k, v, wq, wk, dout, p)
+    rows = [(0, 0), (0, 7), (1, 12), (1, 20)]
+    part = O.bwd_direct(q, k, v, wq, wk, dout, p, rows=rows)
+    for b, t in rows:
+        np.testing.assert_allclose(part["dq"][b, t], full["dq"][b, t], rtol=1e-13, atol=1e-14)
+    assert np.isnan(part["dq"][0, 1]).all() and set(part) == {"dq"}
