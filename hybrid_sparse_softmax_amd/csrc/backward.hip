@@ -602,22 +602,36 @@ __global__ __launch_bounds__(64) void bwd_key_win_kernel(
     }
 }
 
-// One wave per (b, g, four entries of the selected list): the softmax terms
-// of every query after the selected key's window (t >= j + W), added to dk
-// and dv (after bwd_key_win_kernel has written them; the entries of one
-// (b, g) list are distinct positions, so no two waves share a key).
+// One block of kSW waves per (b, g, kSW * kKB entries of the selected list);
+// wave w takes entries kKB w .. kKB w + kKB - 1.  The softmax terms of every
+// query after each selected key's window (t >= j + W), added to dk and dv
+// (after bwd_key_win_kernel has written them; the entries of one (b, g)
+// list are distinct positions, so no two waves share a key).  Tiles of 64
+// query rows and their dout rows are loaded once per block, coalesced, into
+// LDS (rows padded by 16 bytes so that 16 lanes reading 16 lanes' rows hit
+// distinct banks), and every wave dots its keys against them.
+constexpr int kSW = 4;
 template <typename T, int DD>
-__global__ __launch_bounds__(64) void bwd_key_sel_kernel(
+__global__ __launch_bounds__(256) void bwd_key_sel_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const int32_t* __restrict__ selw, const float* __restrict__ stat,
     float* __restrict__ dk, float* __restrict__ dv, Dims D) {
     constexpr int PL = DD / kWave;
-    const Item it = xcd_item((D.n_full * D.lam + kKB - 1) / kKB, D.Hkv);
-    const int e0 = it.x * kKB, g = it.y, b = it.z, lane = threadIdx.x;
+    constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
+    constexpr int RS = DD + EPC;                 // padded row stride (elements)
+    constexpr int CH = DD / EPC;                 // chunks per row
     const int n_list = D.n_full * D.lam;
+    const Item it = xcd_item((n_list + kSW * kKB - 1) / (kSW * kKB), D.Hkv);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int e0 = it.x * kSW * kKB + wave * kKB, g = it.y, b = it.z;
+    const int G = D.G;
     const int32_t* sel = selw + ((size_t)b * D.Hkv + g) * n_list;
-    __shared__ float ks[kKB][DD];
-    __shared__ float vs[kKB][DD];
+    __shared__ float ks[kSW][kKB][DD];
+    __shared__ float vs[kSW][kKB][DD];
+    __shared__ __align__(16) T qt[kWave][RS];
+    __shared__ __align__(16) T dt[kWave][RS];
+    __shared__ float st3[kWave][3];
+    __shared__ int tlo_w[kSW];
     int jk[kKB];
     int t_lo = D.N;
 #pragma unroll
@@ -628,17 +642,74 @@ __global__ __launch_bounds__(64) void bwd_key_sel_kernel(
     auto koff = [&](int j) { return ((size_t)b * D.N + j) * D.Hkv + g; };
     for (int x = lane; x < kKB * DD; x += kWave) {
         const int i = x / DD, e = x % DD, j = max(jk[i], 0);
-        ks[i][e] = to_f32(k[koff(j) * DD + e]);
-        vs[i][e] = to_f32(v[koff(j) * DD + e]);
+        ks[wave][i][e] = to_f32(k[koff(j) * DD + e]);
+        vs[wave][i][e] = to_f32(v[koff(j) * DD + e]);
     }
+    if (lane == 0) tlo_w[wave] = t_lo;
     __syncthreads();
-    if (t_lo > D.N - 1) return;
+    int tb = D.N;
+#pragma unroll
+    for (int w = 0; w < kSW; ++w) tb = min(tb, tlo_w[w]);
+    const int n = tb <= D.N - 1 ? (D.N - tb) * G : 0;  // (t, h) rows from the block's first query on
+    auto row_of = [&](int pr) { return ((size_t)b * D.N + tb + pr / G) * D.Hq + (size_t)g * G + pr % G; };
     float dka[kKB][PL], dva[kKB][PL];
 #pragma unroll
     for (int i = 0; i < kKB; ++i)
 #pragma unroll
         for (int p = 0; p < PL; ++p) dka[i][p] = dva[i][p] = 0.f;
-    key_group_softmax<T, DD>(q, dout, stat, ks, vs, jk, t_lo, D.N - 1, 1, b, g, D, lane, dka, dva);
+    for (int i0 = 0; i0 < n; i0 += kWave) {
+        __syncthreads();  // the previous tile is consumed
+        for (int c = threadIdx.x; c < kWave * CH; c += kSW * kWave) {
+            const int r = c / CH, part = c % CH, pr = i0 + r;
+            if (pr < n) {
+                const size_t o = row_of(pr) * DD + (size_t)part * EPC;
+                *reinterpret_cast<uint4*>(&qt[r][part * EPC]) = *reinterpret_cast<const uint4*>(q + o);
+                *reinterpret_cast<uint4*>(&dt[r][part * EPC]) = *reinterpret_cast<const uint4*>(dout + o);
+            }
+        }
+        if (threadIdx.x < kWave && i0 + threadIdx.x < n) {
+            const size_t o = row_of(i0 + threadIdx.x);
+            st3[threadIdx.x][0] = stat[o * 4 + 0];
+            st3[threadIdx.x][1] = 1.0f / stat[o * 4 + 1];
+            st3[threadIdx.x][2] = stat[o * 4 + 2];
+        }
+        __syncthreads();
+        const int pr = i0 + lane;
+        float pj[kKB], dsj[kKB];
+#pragma unroll
+        for (int i = 0; i < kKB; ++i) pj[i] = dsj[i] = 0.f;
+        if (pr < n) {
+            const int t = tb + pr / G;
+            float sv[kKB], vd[kKB];
+            dot_multi<DD, kKB>(ks[wave], &qt[lane][0], kKB, sv);
+            dot_multi<DD, kKB>(vs[wave], &dt[lane][0], kKB, vd);
+            const float m = st3[lane][0], il = st3[lane][1], Dt = st3[lane][2];
+#pragma unroll
+            for (int i = 0; i < kKB; ++i)
+                if (jk[i] >= 0 && t >= jk[i] + D.W) {
+                    pj[i] = expf(D.tau * sv[i] - m) * il;
+                    dsj[i] = pj[i] * (vd[i] - Dt);
+                }
+        }
+        const int nb = min(kWave, n - i0);
+        for (int jj = 0; jj < nb; ++jj) {
+            float qe[PL], de[PL];
+#pragma unroll
+            for (int p = 0; p < PL; ++p) {
+                qe[p] = to_f32(qt[jj][lane + kWave * p]);
+                de[p] = to_f32(dt[jj][lane + kWave * p]);
+            }
+#pragma unroll
+            for (int i = 0; i < kKB; ++i) {
+                const float w = __shfl(dsj[i], jj, kWave), pv = __shfl(pj[i], jj, kWave);
+#pragma unroll
+                for (int p = 0; p < PL; ++p) {
+                    dka[i][p] = fmaf(w, qe[p], dka[i][p]);
+                    dva[i][p] = fmaf(pv, de[p], dva[i][p]);
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < kKB; ++i) {
         if (jk[i] < 0) continue;
@@ -801,7 +872,8 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     if (D.lam > 0 && D.n_full > 0)
         STILL_STEP("bwd_key_sel",
                    hipLaunchKernelGGL((bwd_key_sel_kernel<T, DD>),
-                                      dim3((D.n_full * D.lam + kKB - 1) / kKB * D.Hkv * D.B), dim3(64),
+                                      dim3((D.n_full * D.lam + kSW * kKB - 1) / (kSW * kKB) * D.Hkv * D.B),
+                                      dim3(kSW * kWave),
                                       0, s, q, k, v, dout, w.selw, w.stat, a.dk, a.dv, D));
     const int ntok = D.B * D.N, half = D.fd / 2;
     STILL_STEP("np_vjp_q",
