@@ -17,9 +17,15 @@ __device__ inline void np_map_wave(const float* xs, const float* __restrict__ P,
     const int half = fd / 2;
     const bool act = lane < half;
     float u = 0.f;
-    if (act) {
-        const float* pr = P + (size_t)lane * d;
-        for (int i = 0; i < d; ++i) u = fmaf(pr[i], xs[i], u);
+    if (act) {  // P is 16-byte aligned (the C ABI checks the projections) and d is a multiple of 4
+        const float4* pr = reinterpret_cast<const float4*>(P + (size_t)lane * d);
+        for (int i = 0; i < d / 4; ++i) {
+            const float4 w = pr[i];
+            u = fmaf(w.x, xs[4 * i], u);
+            u = fmaf(w.y, xs[4 * i + 1], u);
+            u = fmaf(w.z, xs[4 * i + 2], u);
+            u = fmaf(w.w, xs[4 * i + 3], u);
+        }
     }
     const float nu = sqrtf(wave_sum(u * u));
     const float z = nu > 0.f ? nx * (u / nu) : 0.f;

@@ -328,7 +328,9 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
         return STILL_OK;
     }
     if (!q || !k || !v || !wq || !wk || !out) return STILL_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return STILL_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(wq) ||
+        !aligned16(wk))
+        return STILL_ERR_INVALID_ARG;
     if (ragged && (reinterpret_cast<uintptr_t>(pos_dev) & 7u)) return STILL_ERR_INVALID_ARG;
     const int64_t t = ragged ? max_pos : cache->pos;
     const int64_t need = D.lam * ceil_div(t + 1 - D.W, D.C);

@@ -230,3 +230,13 @@ def test_future_utility_checks():
     assert f(ct.byref(sh), FAKE, FAKE, ct.c_void_p(0x1002), FAKE, n.value, None) == S.STILL_ERR_INVALID_ARG
     assert f(ct.byref(shape(head_dim=96)), FAKE, FAKE, FAKE, FAKE, n.value, None) == S.STILL_ERR_UNSUPPORTED
     assert f(ct.byref(shape(seqlen=0)), None, None, None, None, 0, None) == S.STILL_OK
+
+
+def test_decode_rejects_misaligned_projections():
+    sh = shape(seqlen=1, topk=32)
+    need = 32 * ((16384 + 1 - 64 + 63) // 64)
+    c = fake_cache(need, 16384)
+    L = S.lib()
+    for wq, wk in ((MISALIGNED, FAKE), (FAKE, MISALIGNED)):
+        assert L.still_hybrid_attn_decode_step(ct.byref(sh), FAKE, FAKE, FAKE, wq, wk, ct.byref(c), FAKE,
+                                               FAKE, 1 << 40, None) == S.STILL_ERR_INVALID_ARG
