@@ -26,11 +26,15 @@
 //   bwd_route_kernel   route flags and a clean ascending selected list per
 //                      chunk from the caller's selection
 //   (phi, la_chunk, la_scan of the forward: phi_q, phi_k and the LA prefix)
-//   bwd_query_kernel   one wave per (b, t, h): forward statistics m, l, D_t
-//                      recomputed, dq's softmax part, dphi_q
+//   bwd_query_kernel   one wave per (b, t, g) for the group's heads: forward
+//                      statistics m, l, D_t recomputed, dq's softmax part, dphi_q
 //   bwd_uchunk_kernel  per query chunk: sum of c_t phi_q dout^T and c_t D_t phi_q
 //   bwd_suffix_kernel  inclusive suffix of those sums over chunks
-//   bwd_key_kernel     one wave per (b, j, g): dk's softmax part, dv, dphi_k
+//   bwd_key_win_kernel one wave per four consecutive keys: their window
+//                      queries' softmax terms (dk, dv) and the linear terms
+//                      (dv, dphi_k)
+//   bwd_key_sel_kernel one block per 16 selected keys: the softmax terms of
+//                      the queries after their windows, added to dk, dv
 //   np_vjp_kernel      NP-Map backward per (token, head): dx += ..., du
 //   dw_partial_kernel  dP = sum du x^T over a slice of tokens
 //   dw_reduce_kernel   sum of the slices
