@@ -26,7 +26,7 @@
 //   bwd_route_kernel   route flags and a clean ascending selected list per
 //                      chunk from the caller's selection
 //   (phi, la_chunk, la_scan of the forward: phi_q, phi_k and the LA prefix)
-//   bwd_query_kernel   one wave per (b, t, g) for the group's heads: forward
+//   bwd_query_kernel   one wave per (b, two positions, g) for the group's heads:
 //                      statistics m, l, D_t recomputed, dq's softmax part, dphi_q
 //   bwd_uchunk_kernel  per query chunk: sum of c_t phi_q dout^T and c_t D_t phi_q
 //   bwd_suffix_kernel  inclusive suffix of those sums over chunks
@@ -77,10 +77,12 @@ __global__ __launch_bounds__(256) void bwd_route_kernel(const int32_t* __restric
     }
 }
 
-// One wave per query position and KV head (b, t, g), for all G query heads
-// of the group at once (they read the same keys: every key row loaded serves
-// G queries).  Lane owns output dims and features lane + 64 p.  Two passes
-// over the softmax keys:
+// One wave per KV head and two consecutive query positions (b, t0, t0 + 1,
+// g), for all G query heads of the group: every key row a lane loads serves
+// 2 G queries.  The query and dout rows, the same in every lane, are read
+// through the scalar cache.  Lane owns output dims and features lane + 64 p.
+// Two passes over the union of the two positions' softmax keys (each
+// position masks the keys it does not see, so every pair counts once):
 //   1. logits s_j and vd_j = dout . v_j: the reference m (max(0, max s)),
 //      l = sum of weights and D_t = sum w_j vd_j / l (= dout . out), the
 //      linear tokens entering through S_t, z_t and the partly covered chunk;
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(256) void bwd_route_kernel(const int32_t* __restric
 // Then dphi_q = c_t (S_t dout - D_t z_t + sum over the partly covered chunk's
 // linear tokens of (vd_j - D_t) phi_k(j)), c_t = exp(-m) / l.
 // stat[(b, t, h)] = (m, l, D_t, c_t).
+constexpr int kNP = 2;  // query positions per wave
 template <typename T, int DD, int GM>
 __global__ __launch_bounds__(64) void bwd_query_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -96,225 +99,276 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
     const float* __restrict__ lin, float* __restrict__ dq, float* __restrict__ dphiq,
     float* __restrict__ stat, Dims D) {
     constexpr int PL = DD / kWave;
-    const Item it = xcd_item(D.N, D.Hkv);
-    const int t = it.x, g = it.y, b = it.z, lane = threadIdx.x;
+    constexpr int R = kNP * GM;  // rows: position pp, head h -> pp GM + h
+    const Item it = xcd_item((D.N + kNP - 1) / kNP, D.Hkv);
+    const int t0 = it.x * kNP, g = it.y, b = it.z, lane = threadIdx.x;
     const int G = D.G;
-    __shared__ float qs[GM][DD];
-    __shared__ float fq[GM][DD];
-    __shared__ float ds_[GM][DD];
-    const size_t qoff0 = ((size_t)b * D.N + t) * D.Hq + (size_t)g * G;  // row of head g G + h: qoff0 + h
-    for (int x = lane; x < G * DD; x += kWave) {
-        const int h = x / DD, i = x % DD;
-        qs[h][i] = to_f32(q[(qoff0 + h) * DD + i]);
-        fq[h][i] = phiq[(qoff0 + h) * DD + i];
-        ds_[h][i] = to_f32(dout[(qoff0 + h) * DD + i]);
+    int tp[kNP], r_end[kNP];
+    bool act[kNP];
+#pragma unroll
+    for (int pp = 0; pp < kNP; ++pp) {
+        act[pp] = t0 + pp < D.N;  // a position past the end repeats the last one, writes nothing
+        tp[pp] = min(t0 + pp, D.N - 1);
+        r_end[pp] = max(0, tp[pp] - D.W + 1);  // routed tokens j < r_end
+    }
+    auto qoff = [&](int pp, int h) { return ((size_t)b * D.N + tp[pp]) * D.Hq + (size_t)g * G + h; };
+    const T* qr[R];
+    const T* dr[R];
+    bool use[R];
+#pragma unroll
+    for (int pp = 0; pp < kNP; ++pp)
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            const int r = pp * GM + h;
+            use[r] = h < G;
+            const size_t o = qoff(pp, min(h, G - 1));
+            qr[r] = q + o * DD;
+            dr[r] = dout + o * DD;
+        }
+    __shared__ float fq[kNP][GM][DD];
+    __shared__ float ds_[kNP][GM][DD];
+    for (int x = lane; x < kNP * G * DD; x += kWave) {
+        const int pp = x / (G * DD), h = (x / DD) % G, i = x % DD;
+        const size_t o = qoff(pp, h);
+        fq[pp][h][i] = phiq[o * DD + i];
+        ds_[pp][h][i] = to_f32(dout[o * DD + i]);
     }
     __syncthreads();
     auto krow = [&](int j) { return k + (((size_t)b * D.N + j) * D.Hkv + g) * DD; };
     auto vrow = [&](int j) { return v + (((size_t)b * D.N + j) * D.Hkv + g) * DD; };
     auto pkrow = [&](int j) { return phik + (((size_t)b * D.N + j) * D.Hkv + g) * DD; };
-
-    const int r_end = max(0, t - D.W + 1);  // routed tokens j < r_end
-    const int c_full = r_end / D.C;
-    const float* st = c_full >= 1
-        ? lin + (((size_t)b * D.Hkv + g) * D.T + (c_full - 1)) * (size_t)(DD * (DD + 1))
-        : nullptr;
     const uint8_t* rt = route + ((size_t)b * D.Hkv + g) * D.N;
-
-    // ---- linear part of pass 1 (reference 0): y = S_t dout, l, D numerator ----
-    float y[GM][PL];
-    float l[GM], dn[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        l[h] = dn[h] = 0.f;
-#pragma unroll
-        for (int p = 0; p < PL; ++p) y[h][p] = 0.f;
-    }
-    if (st) {
-        float lp[GM], dp[GM];
-#pragma unroll
-        for (int h = 0; h < GM; ++h) lp[h] = dp[h] = 0.f;
-#pragma unroll
-        for (int p = 0; p < PL; ++p) {
-            const int i = lane + kWave * p;
-            const float4* row = reinterpret_cast<const float4*>(st + (size_t)i * DD);
-            for (int e4 = 0; e4 < DD / 4; ++e4) {
-                const float4 r = row[e4];
-#pragma unroll
-                for (int h = 0; h < GM; ++h)
-                    if (h < G) {
-                        float x = y[h][p];
-                        x = fmaf(r.x, ds_[h][4 * e4], x);
-                        x = fmaf(r.y, ds_[h][4 * e4 + 1], x);
-                        x = fmaf(r.z, ds_[h][4 * e4 + 2], x);
-                        x = fmaf(r.w, ds_[h][4 * e4 + 3], x);
-                        y[h][p] = x;
-                    }
-            }
-            const float zi = st[DD * DD + i];
-#pragma unroll
-            for (int h = 0; h < GM; ++h) {
-                lp[h] = fmaf(fq[h][i], zi, lp[h]);
-                dp[h] = fmaf(fq[h][i], y[h][p], dp[h]);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < GM; ++h)
-            if (h < G) {
-                l[h] = wave_sum(lp[h]);
-                dn[h] = wave_sum(dp[h]);
-            }
-    }
-    for (int j0 = c_full * D.C; j0 < r_end; j0 += kWave) {
-        const int j = j0 + lane;
-        float kap[GM], vd[GM];
-#pragma unroll
-        for (int h = 0; h < GM; ++h) kap[h] = vd[h] = 0.f;
-        if (j < r_end && rt[j] == kRouteLA) {
-            dot_multi<DD, GM>(fq, pkrow(j), G, kap);
-            dot_multi<DD, GM>(ds_, vrow(j), G, vd);
-        }
-#pragma unroll
-        for (int h = 0; h < GM; ++h)
-            if (h < G) {
-                l[h] += wave_sum(kap[h]);
-                dn[h] += wave_sum(kap[h] * vd[h]);
-            }
-    }
-
-    // ---- softmax part of pass 1 ----
-    float m[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) m[h] = 0.f;
-    const int32_t* sel = selw + ((size_t)b * D.Hkv + g) * D.n_full * D.lam;
-    const int n_cand = D.lam > 0 ? min(D.n_full, (r_end + D.C - 1) / D.C) * D.lam : 0;
-    auto sel_pos = [&](int i) {
-        if (i >= n_cand) return -1;
-        const int pos = sel[i];
-        return pos < r_end ? pos : -1;  // -1 entries and not yet visible tokens
+    auto state_of = [&](int pp) {
+        const int c_full = r_end[pp] / D.C;
+        return c_full >= 1
+            ? lin + (((size_t)b * D.Hkv + g) * D.T + (c_full - 1)) * (size_t)(DD * (DD + 1))
+            : (const float*)nullptr;
     };
-    auto pass1 = [&](int jpos) {
-        float s[GM], vd[GM];
-        if (jpos >= 0) {
-            dot_multi<DD, GM>(qs, krow(jpos), G, s);
-            dot_multi<DD, GM>(ds_, vrow(jpos), G, vd);
+
+    // ---- linear part of pass 1 (reference 0), per position ----
+    float y[R][PL];
+    float l[R], dn[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        l[r] = dn[r] = 0.f;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) y[r][p] = 0.f;
+    }
+#pragma unroll
+    for (int pp = 0; pp < kNP; ++pp) {
+        const float* st = state_of(pp);
+        if (st) {
+            float lp[GM], dp[GM];
+#pragma unroll
+            for (int h = 0; h < GM; ++h) lp[h] = dp[h] = 0.f;
+#pragma unroll
+            for (int p = 0; p < PL; ++p) {
+                const int i = lane + kWave * p;
+                const float4* row = reinterpret_cast<const float4*>(st + (size_t)i * DD);
+                for (int e4 = 0; e4 < DD / 4; ++e4) {
+                    const float4 rv = row[e4];
+#pragma unroll
+                    for (int h = 0; h < GM; ++h)
+                        if (h < G) {
+                            float x = y[pp * GM + h][p];
+                            x = fmaf(rv.x, ds_[pp][h][4 * e4], x);
+                            x = fmaf(rv.y, ds_[pp][h][4 * e4 + 1], x);
+                            x = fmaf(rv.z, ds_[pp][h][4 * e4 + 2], x);
+                            x = fmaf(rv.w, ds_[pp][h][4 * e4 + 3], x);
+                            y[pp * GM + h][p] = x;
+                        }
+                }
+                const float zi = st[DD * DD + i];
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+                    lp[h] = fmaf(fq[pp][h][i], zi, lp[h]);
+                    dp[h] = fmaf(fq[pp][h][i], y[pp * GM + h][p], dp[h]);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < GM; ++h)
+                if (h < G) {
+                    l[pp * GM + h] = wave_sum(lp[h]);
+                    dn[pp * GM + h] = wave_sum(dp[h]);
+                }
+        }
+        const int cf0 = (r_end[pp] / D.C) * D.C;
+        for (int j0 = cf0; j0 < r_end[pp]; j0 += kWave) {
+            const int j = j0 + lane;
+            float kap[GM], vd[GM];
+#pragma unroll
+            for (int h = 0; h < GM; ++h) kap[h] = vd[h] = 0.f;
+            if (j < r_end[pp] && rt[j] == kRouteLA) {
+                dot_multi<DD, GM>(fq[pp], pkrow(j), G, kap);
+                dot_multi<DD, GM>(ds_[pp], vrow(j), G, vd);
+            }
+#pragma unroll
+            for (int h = 0; h < GM; ++h)
+                if (h < G) {
+                    l[pp * GM + h] += wave_sum(kap[h]);
+                    dn[pp * GM + h] += wave_sum(kap[h] * vd[h]);
+                }
+        }
+    }
+
+    // ---- the union of the positions' softmax keys ----
+    const int t_hi = tp[kNP - 1];
+    const int jw0 = max(0, tp[0] - D.W + 1);
+    const int32_t* sel = selw + ((size_t)b * D.Hkv + g) * D.n_full * D.lam;
+    const int n_cand = D.lam > 0 ? min(D.n_full, (r_end[kNP - 1] + D.C - 1) / D.C) * D.lam : 0;
+    auto sees = [&](int pp, int jpos, bool win) {
+        if (jpos < 0) return false;
+        return win ? (jpos >= tp[pp] - D.W + 1 && jpos <= tp[pp]) : jpos < r_end[pp];
+    };
+    float m[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) m[r] = 0.f;
+    auto pass1 = [&](int jpos, bool win) {
+        bool ok[kNP];
+        bool any = false;
+#pragma unroll
+        for (int pp = 0; pp < kNP; ++pp) {
+            ok[pp] = sees(pp, jpos, win);
+            any = any || ok[pp];
+        }
+        float s[R], vd[R];
+        if (any) {
+            dot_rows_u<DD, R>(qr, use, krow(jpos), s);
+            dot_rows_u<DD, R>(dr, use, vrow(jpos), vd);
         }
 #pragma unroll
-        for (int h = 0; h < GM; ++h)
-            if (h < G) {
-                const float sh = jpos >= 0 ? D.tau * s[h] : kNegInfB;
-                const float m_new = fmaxf(m[h], wave_max(sh));
-                const float sc = expf(m[h] - m_new);
-                const float pj = jpos >= 0 ? expf(sh - m_new) : 0.f;
-                l[h] = l[h] * sc + wave_sum(pj);
-                dn[h] = dn[h] * sc + wave_sum(jpos >= 0 ? pj * vd[h] : 0.f);
-                m[h] = m_new;
+        for (int r = 0; r < R; ++r)
+            if (use[r]) {
+                const bool o = ok[r / GM];
+                const float sh = o ? D.tau * s[r] : kNegInfB;
+                const float m_new = fmaxf(m[r], wave_max(sh));
+                const float sc = expf(m[r] - m_new);
+                const float pj = o ? expf(sh - m_new) : 0.f;
+                l[r] = l[r] * sc + wave_sum(pj);
+                dn[r] = dn[r] * sc + wave_sum(o ? pj * vd[r] : 0.f);
+                m[r] = m_new;
             }
     };
     if (D.W > 0)
-        for (int j0 = max(0, t - D.W + 1); j0 <= t; j0 += kWave) pass1(j0 + lane <= t ? j0 + lane : -1);
-    for (int i0 = 0; i0 < n_cand; i0 += kWave) pass1(sel_pos(i0 + lane));
-    float inv[GM], Dt[GM];
+        for (int j0 = jw0; j0 <= t_hi; j0 += kWave) pass1(j0 + lane <= t_hi ? j0 + lane : -1, true);
+    for (int i0 = 0; i0 < n_cand; i0 += kWave) pass1(i0 + lane < n_cand ? sel[i0 + lane] : -1, false);
+    float inv[R], Dt[R];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        inv[h] = h < G ? 1.0f / l[h] : 0.f;
-        Dt[h] = dn[h] * inv[h];
+    for (int r = 0; r < R; ++r) {
+        inv[r] = use[r] ? 1.0f / l[r] : 0.f;
+        Dt[r] = dn[r] * inv[r];
     }
 
     // ---- pass 2: softmax part of dq ----
-    float dqa[GM][PL];
+    float dqa[R][PL];
 #pragma unroll
-    for (int h = 0; h < GM; ++h)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int p = 0; p < PL; ++p) dqa[h][p] = 0.f;
-    auto pass2 = [&](int jpos) {
-        float dsj[GM];
+        for (int p = 0; p < PL; ++p) dqa[r][p] = 0.f;
+    auto pass2 = [&](int jpos, bool win) {
+        bool ok[kNP];
+        bool any = false;
 #pragma unroll
-        for (int h = 0; h < GM; ++h) dsj[h] = 0.f;
-        if (jpos >= 0) {
-            float s[GM], vd[GM];
-            dot_multi<DD, GM>(qs, krow(jpos), G, s);
-            dot_multi<DD, GM>(ds_, vrow(jpos), G, vd);
+        for (int pp = 0; pp < kNP; ++pp) {
+            ok[pp] = sees(pp, jpos, win);
+            any = any || ok[pp];
+        }
+        float dsj[R];
 #pragma unroll
-            for (int h = 0; h < GM; ++h)
-                if (h < G) dsj[h] = expf(D.tau * s[h] - m[h]) * inv[h] * (vd[h] - Dt[h]);
+        for (int r = 0; r < R; ++r) dsj[r] = 0.f;
+        if (any) {
+            float s[R], vd[R];
+            dot_rows_u<DD, R>(qr, use, krow(jpos), s);
+            dot_rows_u<DD, R>(dr, use, vrow(jpos), vd);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (use[r] && ok[r / GM]) dsj[r] = expf(D.tau * s[r] - m[r]) * inv[r] * (vd[r] - Dt[r]);
         }
         for (int jj = 0; jj < kWave; ++jj) {
-            const int jp = __shfl(jpos, jj, kWave);
+            const int jp = __shfl(any ? jpos : -1, jj, kWave);
             if (jp >= 0) {
                 const T* kr = krow(jp);
                 float kv[PL];
 #pragma unroll
                 for (int p = 0; p < PL; ++p) kv[p] = to_f32(kr[lane + kWave * p]);
 #pragma unroll
-                for (int h = 0; h < GM; ++h)
-                    if (h < G) {
-                        const float w = __shfl(dsj[h], jj, kWave);
+                for (int r = 0; r < R; ++r)
+                    if (use[r]) {
+                        const float w = __shfl(dsj[r], jj, kWave);
 #pragma unroll
-                        for (int p = 0; p < PL; ++p) dqa[h][p] = fmaf(w, kv[p], dqa[h][p]);
+                        for (int p = 0; p < PL; ++p) dqa[r][p] = fmaf(w, kv[p], dqa[r][p]);
                     }
             }
         }
     };
     if (D.W > 0)
-        for (int j0 = max(0, t - D.W + 1); j0 <= t; j0 += kWave) pass2(j0 + lane <= t ? j0 + lane : -1);
-    for (int i0 = 0; i0 < n_cand; i0 += kWave) pass2(sel_pos(i0 + lane));
+        for (int j0 = jw0; j0 <= t_hi; j0 += kWave) pass2(j0 + lane <= t_hi ? j0 + lane : -1, true);
+    for (int i0 = 0; i0 < n_cand; i0 += kWave) pass2(i0 + lane < n_cand ? sel[i0 + lane] : -1, false);
 #pragma unroll
-    for (int h = 0; h < GM; ++h)
-        if (h < G)
+    for (int pp = 0; pp < kNP; ++pp)
 #pragma unroll
-            for (int p = 0; p < PL; ++p) dq[(qoff0 + h) * DD + lane + kWave * p] = D.tau * dqa[h][p];
+        for (int h = 0; h < GM; ++h)
+            if (h < G && act[pp])
+#pragma unroll
+                for (int p = 0; p < PL; ++p)
+                    dq[qoff(pp, h) * DD + lane + kWave * p] = D.tau * dqa[pp * GM + h][p];
 
-    // ---- dphi_q ----
-    float dfq[GM][PL];
+    // ---- dphi_q, per position ----
 #pragma unroll
-    for (int h = 0; h < GM; ++h)
+    for (int pp = 0; pp < kNP; ++pp) {
+        const float* st = state_of(pp);
+        float dfq[GM][PL];
 #pragma unroll
-        for (int p = 0; p < PL; ++p)
-            dfq[h][p] = st ? y[h][p] - Dt[h] * st[DD * DD + lane + kWave * p] : 0.f;
-    for (int j0 = c_full * D.C; j0 < r_end; j0 += kWave) {
-        const int j = j0 + lane;
-        float w[GM];
+        for (int h = 0; h < GM; ++h)
 #pragma unroll
-        for (int h = 0; h < GM; ++h) w[h] = 0.f;
-        const bool la = j < r_end && rt[j] == kRouteLA;
-        if (la) {
-            dot_multi<DD, GM>(ds_, vrow(j), G, w);
+            for (int p = 0; p < PL; ++p)
+                dfq[h][p] = st ? y[pp * GM + h][p] - Dt[pp * GM + h] * st[DD * DD + lane + kWave * p] : 0.f;
+        const int cf0 = (r_end[pp] / D.C) * D.C;
+        for (int j0 = cf0; j0 < r_end[pp]; j0 += kWave) {
+            const int j = j0 + lane;
+            float w[GM];
 #pragma unroll
-            for (int h = 0; h < GM; ++h) w[h] -= Dt[h];
-        }
-        const int nb = min(kWave, r_end - j0);
-        for (int jj = 0; jj < nb; ++jj) {
-            const int laj = __shfl((int)la, jj, kWave);
-            if (laj) {
-                const float* pk = pkrow(j0 + jj);
-                float pv[PL];
+            for (int h = 0; h < GM; ++h) w[h] = 0.f;
+            const bool la = j < r_end[pp] && rt[j] == kRouteLA;
+            if (la) {
+                dot_multi<DD, GM>(ds_[pp], vrow(j), G, w);
 #pragma unroll
-                for (int p = 0; p < PL; ++p) pv[p] = pk[lane + kWave * p];
+                for (int h = 0; h < GM; ++h) w[h] -= Dt[pp * GM + h];
+            }
+            const int nb = min(kWave, r_end[pp] - j0);
+            for (int jj = 0; jj < nb; ++jj) {
+                const int laj = __shfl((int)la, jj, kWave);
+                if (laj) {
+                    const float* pk = pkrow(j0 + jj);
+                    float pv[PL];
 #pragma unroll
-                for (int h = 0; h < GM; ++h)
-                    if (h < G) {
-                        const float wj = __shfl(w[h], jj, kWave);
+                    for (int p = 0; p < PL; ++p) pv[p] = pk[lane + kWave * p];
 #pragma unroll
-                        for (int p = 0; p < PL; ++p) dfq[h][p] = fmaf(wj, pv[p], dfq[h][p]);
-                    }
+                    for (int h = 0; h < GM; ++h)
+                        if (h < G) {
+                            const float wj = __shfl(w[h], jj, kWave);
+#pragma unroll
+                            for (int p = 0; p < PL; ++p) dfq[h][p] = fmaf(wj, pv[p], dfq[h][p]);
+                        }
+                }
             }
         }
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            if (h < G && act[pp]) {
+                const int r = pp * GM + h;
+                const size_t o = qoff(pp, h);
+                const float cf = expf(-m[r]) * inv[r];
+#pragma unroll
+                for (int p = 0; p < PL; ++p) dphiq[o * DD + lane + kWave * p] = cf * dfq[h][p];
+                if (lane == 0) {
+                    stat[o * 4 + 0] = m[r];
+                    stat[o * 4 + 1] = l[r];
+                    stat[o * 4 + 2] = Dt[r];
+                    stat[o * 4 + 3] = cf;
+                }
+            }
     }
-#pragma unroll
-    for (int h = 0; h < GM; ++h)
-        if (h < G) {
-            const size_t o = qoff0 + h;
-            const float cf = expf(-m[h]) * inv[h];
-#pragma unroll
-            for (int p = 0; p < PL; ++p) dphiq[o * DD + lane + kWave * p] = cf * dfq[h][p];
-            if (lane == 0) {
-                stat[o * 4 + 0] = m[h];
-                stat[o * 4 + 1] = l[h];
-                stat[o * 4 + 2] = Dt[h];
-                stat[o * 4 + 3] = cf;
-            }
-        }
 }
 
 // Per query chunk c of (b, g): U[i][e] = sum over its queries t and the
@@ -858,7 +912,8 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     if ((e = mark.fn(mark.ctx, "la_scan")) != hipSuccess) return e;
     if ((e = launch_la_scan(D, w.lin, -1, nullptr, nullptr, s)) != hipSuccess) return e;
 #define STILL_BWD_QUERY(GM)                                                                     \
-    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM>), dim3(D.N * D.Hkv * D.B), dim3(64), 0, s, q, k, \
+    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM>), dim3((D.N + kNP - 1) / kNP * D.Hkv * D.B), dim3(64), \
+                       0, s, q, k,                                                                  \
                        v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.dq, w.dphiq, w.stat, D)
     STILL_STEP("bwd_query", if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
                             else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));

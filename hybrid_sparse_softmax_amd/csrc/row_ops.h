@@ -59,6 +59,50 @@ __device__ __forceinline__ void dot_multi(const float (*a)[DD], const T1* r, int
     }
 }
 
+// 8 consecutive elements at an address that is the same in every lane,
+// read as constant memory (through the scalar cache; such rows are not
+// written while the kernel runs)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) u32x4* const_u4_ptr;
+__device__ __forceinline__ void load8_u(const __bf16* p, float* x) {
+    const u32x4 u = *reinterpret_cast<const_u4_ptr>(reinterpret_cast<uintptr_t>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(u[i] << 16);
+        x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8_u(const float* p, float* x) {
+    const const_u4_ptr q = reinterpret_cast<const_u4_ptr>(reinterpret_cast<uintptr_t>(p));
+    const u32x4 a = q[0], b = q[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = __uint_as_float(a[i]);
+        x[4 + i] = __uint_as_float(b[i]);
+    }
+}
+
+// dots of one row r (DD elements) with the rows a[i], i < R, whose
+// addresses are the same in every lane (rows with use[i] false are skipped)
+template <int DD, int R, typename TA, typename T1>
+__device__ __forceinline__ void dot_rows_u(const TA* const* a, const bool* use, const T1* r, float* out) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) out[h] = 0.f;
+#pragma unroll 2
+    for (int i = 0; i < DD; i += 8) {
+        float xr[8];
+        load8(r + i, xr);
+#pragma unroll
+        for (int h = 0; h < R; ++h)
+            if (use[h]) {
+                float xa[8];
+                load8_u(a[h] + i, xa);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[h] = fmaf(xa[e], xr[e], out[h]);
+            }
+    }
+}
+
 // Work item of a 1-D launch of nx * ny * nz blocks, laid out so that the
 // blocks of one (y, z) pair -- one (sequence, KV head), whose waves read the
 // same query and key rows -- run on one XCD and share its L2: the hardware
