@@ -35,7 +35,7 @@
 //                      (dv, dphi_k)
 //   bwd_key_sel_kernel one block per 16 selected keys: the softmax terms of
 //                      the queries after their windows, added to dk, dv
-//   np_vjp_kernel      NP-Map backward per (token, head): dx += ..., du
+//   np_vjp_kernel      NP-Map backward per (token, KV group): dx += ..., du
 //   dw_partial_kernel  dP = sum du x^T over a slice of tokens
 //   dw_reduce_kernel   sum of the slices
 #include "device_common.h"
@@ -780,13 +780,14 @@ __global__ __launch_bounds__(256) void bwd_key_sel_kernel(
     }
 }
 
-// NP-Map backward for x[tok, h] with projection P[h / hpp] (fd / 2 <= 64
-// rows, one per lane):
+// NP-Map backward for the hpp heads of group gp of token tok, x[tok, gp hpp + h]
+// with projection P[gp] (fd / 2 <= 64 rows, one per lane), one wave: the
+// projection is read once for all hpp <= GM heads.  Per head:
 //   a = softmax(z), bb = softmax(-z):  dz = a (da - <da, a>) - bb (db - <db, bb>)
 //   z = ||x|| uh, uh = u / ||u||:       d||x|| = <dz, uh>, duh = ||x|| dz
 //   du = (duh - <duh, uh> uh) / ||u||   (zero where u = 0: z is pinned to 0)
 //   dx = d||x|| x / ||x|| + P^T du  (added into dx_out),  du stored for dP
-template <typename T, int DD>
+template <typename T, int DD, int GM>
 __global__ __launch_bounds__(64) void np_vjp_kernel(const T* __restrict__ x,
                                                     const float* __restrict__ Pall,
                                                     const float* __restrict__ dphi,
@@ -794,55 +795,81 @@ __global__ __launch_bounds__(64) void np_vjp_kernel(const T* __restrict__ x,
                                                     float* __restrict__ du_out, int H, int hpp,
                                                     int fd) {
     constexpr int PL = DD / kWave;
-    const int tok = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+    const int tok = blockIdx.x, gp = blockIdx.y, lane = threadIdx.x;
     const int half = fd / 2;
-    __shared__ float xs[DD];
-    __shared__ float dus[64];
-    const size_t row = (size_t)tok * H + h;
-    for (int i = lane; i < DD; i += kWave) xs[i] = to_f32(x[row * DD + i]);
+    __shared__ float xs[GM][DD];
+    __shared__ float dus[GM][64];
+    const size_t row0 = (size_t)tok * H + (size_t)gp * hpp;  // head h: row0 + h
+    for (int i = lane; i < hpp * DD; i += kWave) xs[i / DD][i % DD] = to_f32(x[row0 * DD + i]);
     __syncthreads();
-    const float* P = Pall + (size_t)(h / hpp) * half * DD;
-    float ss = 0.f;
-    for (int i = lane; i < DD; i += kWave) ss = fmaf(xs[i], xs[i], ss);
-    const float nx = sqrtf(wave_sum(ss));
+    const float* P = Pall + (size_t)gp * half * DD;
     const bool act = lane < half;
-    float u = 0.f;
+    float u[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) u[h] = 0.f;
     if (act) {  // P rows are 16-byte aligned: the projections are checked aligned, d is 64 or 128
         const float4* pr = reinterpret_cast<const float4*>(P + (size_t)lane * DD);
-#pragma unroll 8
+#pragma unroll 4
         for (int i = 0; i < DD / 4; ++i) {
             const float4 w = pr[i];
-            u = fmaf(w.x, xs[4 * i], u);
-            u = fmaf(w.y, xs[4 * i + 1], u);
-            u = fmaf(w.z, xs[4 * i + 2], u);
-            u = fmaf(w.w, xs[4 * i + 3], u);
+#pragma unroll
+            for (int h = 0; h < GM; ++h)
+                if (h < hpp) {
+                    u[h] = fmaf(w.x, xs[h][4 * i], u[h]);
+                    u[h] = fmaf(w.y, xs[h][4 * i + 1], u[h]);
+                    u[h] = fmaf(w.z, xs[h][4 * i + 2], u[h]);
+                    u[h] = fmaf(w.w, xs[h][4 * i + 3], u[h]);
+                }
         }
     }
-    const float nu = sqrtf(wave_sum(u * u));
-    const float uh = nu > 0.f ? u / nu : 0.f;
-    const float z = nx * uh;
-    const float m1 = wave_max(act ? z : kNegInfB), m2 = wave_max(act ? -z : kNegInfB);
-    const float e1 = act ? expf(z - m1) : 0.f, e2 = act ? expf(-z - m2) : 0.f;
-    const float a = e1 / wave_sum(e1), bb = e2 / wave_sum(e2);
-    const float da = act ? dphi[row * fd + lane] : 0.f;
-    const float db = act ? dphi[row * fd + half + lane] : 0.f;
-    const float sa = wave_sum(da * a), sb = wave_sum(db * bb);
-    const float dz = act ? a * (da - sa) - bb * (db - sb) : 0.f;
-    const float dnx = nu > 0.f ? wave_sum(dz * uh) : 0.f;
-    const float duh = nx * dz;
-    const float proj = wave_sum(duh * uh);
-    const float du = (nu > 0.f && act) ? (duh - proj * uh) / nu : 0.f;
-    dus[lane] = du;
-    __syncthreads();
-    const float rn = nx > 0.f ? dnx / nx : 0.f;
+    float rn[GM];
 #pragma unroll
-    for (int p = 0; p < PL; ++p) {
-        const int e = lane + kWave * p;
-        float acc = rn * xs[e];
-        for (int i = 0; i < half; ++i) acc = fmaf(dus[i], P[(size_t)i * DD + e], acc);
-        dx_out[row * DD + e] += acc;
+    for (int h = 0; h < GM; ++h) {
+        rn[h] = 0.f;
+        if (h >= hpp) continue;
+        float ss = 0.f;
+        for (int i = lane; i < DD; i += kWave) ss = fmaf(xs[h][i], xs[h][i], ss);
+        const float nx = sqrtf(wave_sum(ss));
+        const float nu = sqrtf(wave_sum(u[h] * u[h]));
+        const float uh = nu > 0.f ? u[h] / nu : 0.f;
+        const float z = nx * uh;
+        const float m1 = wave_max(act ? z : kNegInfB), m2 = wave_max(act ? -z : kNegInfB);
+        const float e1 = act ? expf(z - m1) : 0.f, e2 = act ? expf(-z - m2) : 0.f;
+        const float a = e1 / wave_sum(e1), bb = e2 / wave_sum(e2);
+        const size_t row = row0 + h;
+        const float da = act ? dphi[row * fd + lane] : 0.f;
+        const float db = act ? dphi[row * fd + half + lane] : 0.f;
+        const float sa = wave_sum(da * a), sb = wave_sum(db * bb);
+        const float dz = act ? a * (da - sa) - bb * (db - sb) : 0.f;
+        const float dnx = nu > 0.f ? wave_sum(dz * uh) : 0.f;
+        const float duh = nx * dz;
+        const float proj = wave_sum(duh * uh);
+        const float du = (nu > 0.f && act) ? (duh - proj * uh) / nu : 0.f;
+        dus[h][lane] = du;
+        rn[h] = nx > 0.f ? dnx / nx : 0.f;
+        if (act) du_out[row * half + lane] = du;
     }
-    if (act) du_out[row * half + lane] = du;
+    __syncthreads();
+    float acc[GM][PL];
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+        for (int p = 0; p < PL; ++p) acc[h][p] = h < hpp ? rn[h] * xs[h][lane + kWave * p] : 0.f;
+    for (int i = 0; i < half; ++i) {
+        float pv[PL];
+#pragma unroll
+        for (int p = 0; p < PL; ++p) pv[p] = P[(size_t)i * DD + lane + kWave * p];
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            if (h < hpp)
+#pragma unroll
+                for (int p = 0; p < PL; ++p) acc[h][p] = fmaf(dus[h][i], pv[p], acc[h][p]);
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+        if (h < hpp)
+#pragma unroll
+            for (int p = 0; p < PL; ++p) dx_out[(row0 + h) * DD + lane + kWave * p] += acc[h][p];
 }
 
 // Partial dP[g] over token slice s: thread e owns column e of every row.
@@ -935,11 +962,14 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
                                       dim3(kSW * kWave),
                                       0, s, q, k, v, dout, w.selw, w.stat, a.dk, a.dv, D));
     const int ntok = D.B * D.N, half = D.fd / 2;
-    STILL_STEP("np_vjp_q",
-               hipLaunchKernelGGL((np_vjp_kernel<T, DD>), dim3(ntok, D.Hq), dim3(64), 0, s, q,
-                                  a.wq, w.dphiq, a.dq, w.duq, D.Hq, D.G, D.fd));
+#define STILL_NP_VJP_Q(GM)                                                                       \
+    hipLaunchKernelGGL((np_vjp_kernel<T, DD, GM>), dim3(ntok, D.Hkv), dim3(64), 0, s, q, a.wq, w.dphiq, \
+                       a.dq, w.duq, D.Hq, D.G, D.fd)
+    STILL_STEP("np_vjp_q", if (D.G == 1) STILL_NP_VJP_Q(1); else if (D.G == 2) STILL_NP_VJP_Q(2);
+                           else if (D.G <= 4) STILL_NP_VJP_Q(4); else STILL_NP_VJP_Q(8));
+#undef STILL_NP_VJP_Q
     STILL_STEP("np_vjp_k",
-               hipLaunchKernelGGL((np_vjp_kernel<T, DD>), dim3(ntok, D.Hkv), dim3(64), 0, s, k,
+               hipLaunchKernelGGL((np_vjp_kernel<T, DD, 1>), dim3(ntok, D.Hkv), dim3(64), 0, s, k,
                                   a.wk, w.dphik, a.dk, w.duk, D.Hkv, 1, D.fd));
     STILL_STEP("dw_q",
                hipLaunchKernelGGL((dw_partial_kernel<T, DD>), dim3(D.Hkv, w.nslice), dim3(DD), 0, s,
