@@ -220,9 +220,18 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
         if (jpos < 0) return false;
         return win ? (jpos >= tp[pp] - D.W + 1 && jpos <= tp[pp]) : jpos < r_end[pp];
     };
+    // Reference point of the weights: max(0, max s) when the query has linear
+    // mass (both kinds of weight stay <= 1); the plain running maximum, which
+    // may be negative, when it has none (t < W, every routed token selected),
+    // so logits far below 0 cannot underflow every weight.  The key kernels
+    // read the same reference from stat.
     float m[R];
+    bool la_mass[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) m[r] = 0.f;
+    for (int r = 0; r < R; ++r) {
+        la_mass[r] = l[r] > 0.f;
+        m[r] = la_mass[r] ? 0.f : kNegInfB;
+    }
     auto pass1 = [&](int jpos, bool win) {
         bool ok[kNP];
         bool any = false;
@@ -242,6 +251,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
                 const bool o = ok[r / GM];
                 const float sh = o ? D.tau * s[r] : kNegInfB;
                 const float m_new = fmaxf(m[r], wave_max(sh));
+                if (m_new == kNegInfB) continue;  // nothing visible yet
                 const float sc = expf(m[r] - m_new);
                 const float pj = o ? expf(sh - m_new) : 0.f;
                 l[r] = l[r] * sc + wave_sum(pj);
@@ -358,7 +368,8 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
             if (h < G && act[pp]) {
                 const int r = pp * GM + h;
                 const size_t o = qoff(pp, h);
-                const float cf = expf(-m[r]) * inv[r];
+                // no linear mass: no linear term to differentiate
+                const float cf = la_mass[r] ? expf(-m[r]) * inv[r] : 0.f;
 #pragma unroll
                 for (int p = 0; p < PL; ++p) dphiq[o * DD + lane + kWave * p] = cf * dfq[h][p];
                 if (lane == 0) {

@@ -305,11 +305,15 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeWork w, T* __r
     const float* la = w.la + bh * (DD + 1);
     const float* wp = w.win + bh * (DD + 2);
     const float* pp = w.part + bh * w.splits * (DD + 2);
-    float M = 0.f;  // linear terms sit at reference 0
+    // Linear terms sit at reference 0, so with linear mass the common
+    // reference is max(0, the partials' maxima); without it (no routed linear
+    // token) it is the partials' maximum alone, which may be negative: logits
+    // far below 0 would otherwise underflow every weight and leave 0 / 0.
+    float M = la[DD] > 0.f ? 0.f : kNegInf;
     if (wp[1] > 0.f) M = fmaxf(M, wp[0]);
     for (int s = 0; s < w.splits; ++s)
         if (pp[s * (DD + 2) + 1] > 0.f) M = fmaxf(M, pp[s * (DD + 2)]);
-    const float fl = expf(-M);
+    const float fl = la[DD] > 0.f ? expf(-M) : 0.f;
     float l = la[DD] * fl;
     float acc[PL];
 #pragma unroll

@@ -471,13 +471,18 @@ __global__ __launch_bounds__(kD) void dec_combine_kernel(FastWork w, CacheView c
     const size_t bh = (size_t)b * D.Hq + h, bg = (size_t)b * D.Hkv + g;
     const float* la = w.la + bh * (kD + 1);
     const float* wp = w.win + bh * (kD + 2);
-    float M = 0.f;  // linear terms sit at reference 0
+    // Linear terms sit at reference 0 (log2 units), so with linear mass the
+    // common reference is max(0, the partials' maxima); without it (no routed
+    // linear token) it is the partials' maximum alone, which may be negative:
+    // logits far below 0 would otherwise underflow every weight and leave 0 / 0.
+    const bool has_la = la[kD] > 0.f;
+    float M = has_la ? 0.f : -__builtin_inff();
     if (wp[1] > 0.f) M = fmaxf(M, wp[0]);
     for (int s = 0; s < w.nsplit; ++s) {
         const float* pp = w.part + ((bg * w.nsplit + s) * D.G + hh) * (kD + 2);
         if (pp[1] > 0.f) M = fmaxf(M, pp[0]);
     }
-    const float fl = __builtin_amdgcn_exp2f(-M);
+    const float fl = has_la ? __builtin_amdgcn_exp2f(-M) : 0.f;
     float num = la[dim] * fl, den = la[kD] * fl;
     if (wp[1] > 0.f) {
         const float f = __builtin_amdgcn_exp2f(wp[0] - M);

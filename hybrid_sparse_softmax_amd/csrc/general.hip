@@ -237,7 +237,7 @@ __global__ __launch_bounds__(64) void main_general_kernel(
     float acc[PL];
 #pragma unroll
     for (int p = 0; p < PL; ++p) acc[p] = 0.f;
-    float l = 0.f, m = 0.f;  // reference point M starts at 0 (max(0, max s))
+    float l = 0.f, m = 0.f;  // the linear terms' reference point is 0
     const int r_end = max(0, t - D.W + 1);  // routed tokens: j < r_end
     const int c_full = r_end / D.C;
 
@@ -273,7 +273,13 @@ __global__ __launch_bounds__(64) void main_general_kernel(
             }
         }
     }
-    // softmax terms, 64 keys at a time; jpos < 0 marks an empty lane
+    // Softmax terms, 64 keys at a time; jpos < 0 marks an empty lane.  With
+    // linear mass the reference is max(0, max s), which keeps both kinds of
+    // weight <= 1.  Without it (no routed linear token: t < W, every routed
+    // token selected) the reference is the plain running maximum, which may
+    // be negative: all logits far below 0 would otherwise underflow every
+    // weight and leave 0 / 0.
+    if (!(l > 0.f)) m = kNegInf;
     auto sa_batch = [&](int jpos) {
         float s = kNegInf;
         if (jpos >= 0) {
@@ -283,6 +289,7 @@ __global__ __launch_bounds__(64) void main_general_kernel(
             s = D.tau * dot;
         }
         const float m_new = fmaxf(m, wave_max(s));
+        if (m_new == kNegInf) return;  // nothing visible yet
         const float sc = expf(m - m_new);
         const float pj = jpos >= 0 ? expf(s - m_new) : 0.f;
         l = l * sc + wave_sum(pj);

@@ -1014,7 +1014,8 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     __syncthreads();
 
     // running state of the lane's query: reference point m2 (log2 units,
-    // starts at 0, the linear terms' reference), partial normaliser ls of
+    // starts at 0, the linear terms' reference; see nola below for queries
+    // without linear terms), partial normaliser ls of
     // this half's rows; O^T tiles o[dt]: rows = dims 32 dt + .., column = query
     f32x16 o[4];
 #pragma unroll
@@ -1127,6 +1128,14 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         }
     }
 
+    // A query with no linear mass (t < W, or every routed token of its
+    // chunks selected) has nothing at the linear reference 0, so its
+    // reference need not stay >= 0: at the first tile with a key it can see,
+    // m2 moves to that tile's maximum, up or down.  Logits far below 0
+    // would otherwise underflow every weight and leave 0 / 0.  The flag is
+    // the same in both lanes of a query.
+    bool nola = !(ls + xor32(ls) > 0.f);
+
     // logits of tile i (K^T Q on the matrix cores)
     auto qk = [&](int i, f32x16 (&sc)[2]) {
         const bf16* ks = kbuf(i);
@@ -1184,11 +1193,20 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) tmax = vmax(tmax, sc[kt][vv]);
         const float tm2 = half_pair_max(tmax) * cl2;
-        if (__any(tm2 > m2 + kLazy)) {
+        const bool down = nola && tm2 > kNegInf;
+        if (__any(tm2 > m2 + kLazy || down)) {
             // a rare path: keep the compiler from speculating it into every tile
             __asm__ volatile("");
-            const float mn = ceilf(fmaxf(m2, tm2));
+            float mn = ceilf(fmaxf(m2, tm2));
             al = __builtin_amdgcn_exp2f(m2 - mn);
+            if (down) {
+                // first visible key of a query without linear mass: nothing
+                // is summed yet (O and ls are 0), the reference takes this
+                // tile's maximum
+                mn = ceilf(tm2);
+                al = 0.f;
+                nola = false;
+            }
             m2 = mn;
             ls *= al;
             return true;
@@ -1381,7 +1399,10 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             // probabilities are formed again from its logits.  Weights below
             // 2^64 keep their relative precision in fp32 and bf16, so no
             // running maximum is needed on the common path.
-            if (__any(!(ls - ls0 < 0x1p64f))) {
+            // A query without linear mass takes this path at each tile until
+            // the first one with a key it can see, whose maximum becomes its
+            // reference (earlier tiles summed nothing: O and ls are 0).
+            if (__any(!(ls - ls0 < 0x1p64f) || nola)) {
                 // a rare path: keep the compiler from speculating it into every tile
                 __asm__ volatile("");
                 float mx = kNegInf;
@@ -1389,8 +1410,14 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int vv = 0; vv < 16; ++vv) mx = vmax(mx, sc[kt][vv]);
-                const float mn = ceilf(fmaxf(m2, half_pair_max(mx) * cl2));
-                const float al = __builtin_amdgcn_exp2f(m2 - mn);
+                const float pm = half_pair_max(mx) * cl2;
+                float mn = ceilf(fmaxf(m2, pm));
+                float al = __builtin_amdgcn_exp2f(m2 - mn);
+                if (nola && pm > kNegInf) {
+                    mn = ceilf(pm);
+                    al = 0.f;
+                    nola = false;
+                }
                 m2 = mn;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)

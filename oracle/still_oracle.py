@@ -566,7 +566,7 @@ def np_map_vjp(x, P, dphi):
     return dx, dP
 
 
-def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None):
+def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=None):
     """Gradients of L = sum(dout * out) with out = fwd_direct(q, k, v, wq,
     wk, p) and the routing fixed to ``sel_idx`` [B, Hkv, N//C, lambda]
     (the forward's own selection when None).
@@ -575,6 +575,10 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None):
     rows: optional list of distinct (b, t); then only those queries are visited and
     only dq is returned (NaN elsewhere): dq of a query depends on that query
     alone, while every key-side gradient sums over all queries.
+    keys: optional list of (b, g, j); then only the queries that can see key
+    j of (b, g) are visited -- t >= j of the heads of KV head g -- and only
+    dk and dv are returned, at those keys (NaN elsewhere).  A key's gradient
+    sums over exactly those queries.
 
     Per query t of head h (KV head g), with the sets of fwd_direct:
       w_j = exp(s_j - M) on SA_t, exp(-M) kappa_j on LA_t, kappa_j = phi_q . phi_k(k_j)
@@ -604,10 +608,21 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None):
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     dphiq = np.zeros(q.shape[:3] + (2 * wq.shape[1],))
     dphik = np.zeros_like(phik)
-    visit = [(b, t) for b in range(B) for t in range(N)] if rows is None else list(rows)
+    groups = {b: range(Hkv) for b in range(B)}
+    if keys is not None:
+        keys = [tuple(int(x) for x in key) for key in keys]
+        first = {}
+        for b, g, j in keys:
+            first[b] = min(first.get(b, N), j)
+        visit = [(b, t) for b in sorted(first) for t in range(first[b], N)]
+        groups = {b: sorted({g for bb, g, _ in keys if bb == b}) for b in first}
+    elif rows is None:
+        visit = [(b, t) for b in range(B) for t in range(N)]
+    else:
+        visit = list(rows)
     for b, t in visit:
         r_end = t - W + 1
-        for g in range(Hkv):
+        for g in groups[b]:
             win = np.arange(max(0, t - W + 1), t + 1) if W > 0 else np.arange(0)
             routed = np.arange(0, max(0, r_end))
             rr = route[b, g, routed]
@@ -634,6 +649,13 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None):
                 dphiq[b, t, h] += dkap @ phik[b, la, g, :]
                 np.add.at(dphik[b, :, g, :], la, np.outer(dkap, fq))
                 np.add.at(dv[b, :, g, :], la, np.outer(w_la / den, do))
+    if keys is not None:
+        dk_keys, dv_keys = np.full(k.shape, np.nan), np.full(v.shape, np.nan)
+        for b, g, j in keys:
+            dx, _ = np_map_vjp(k[b, j, g], wk[g], dphik[b, j, g])
+            dk_keys[b, j, g] = dk[b, j, g] + dx
+            dv_keys[b, j, g] = dv[b, j, g]
+        return dict(dk=dk_keys, dv=dv_keys)
     if rows is not None:
         dq_rows = np.full(q.shape, np.nan)
         for b, t in visit:

@@ -17,7 +17,7 @@ import torch
 
 import oracle as O
 import workloads
-from parity import make_case, prepare, rel_l2, say, torch_dtype
+from parity import check_rows, make_case, prepare, rel_l2, say, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,18 @@ CASES = {
     "bf16_all_selected": (make_case("e", 1, 200, 4, 2, 128, 64, 64, 64), 36),
     "bf16_short_no_chunk": (make_case("f", 2, 40, 4, 2, 128, 64, 64, 16), 37),
     "bf16_single_token": (make_case("g", 1, 1, 4, 2, 128, 64, 64, 16), 38),
+    # one query head per KV head, and the Llama 32 / 8 grouping (four per KV
+    # head) with linear tokens present, so the projection gradients are not 0
+    "bf16_G1": (make_case("h", 1, 300, 2, 2, 128, 64, 64, 16), 39),
+    "bf16_G4_linear": (make_case("i", 1, 300, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 40),
+    # three query heads per KV head: the padded heads of the grouped kernels
+    "f32_G3_d64": (make_case("j", 1, 200, 6, 2, 64, 32, 32, 8, dtype="f32"), 41),
+    # fp32 storage at d = 128
+    "f32_d128_G2": (make_case("k", 1, 200, 4, 2, 128, 64, 64, 16, dtype="f32"), 42),
+    # every logit far below -100 (queries along +56 u, keys along -56 u):
+    # queries with no linear term must keep finite softmax statistics
+    "bf16_underflow_all_selected": (make_case("u", 1, 200, 4, 2, 128, 64, 64, 64, anti_align=56.0), 43),
+    "bf16_underflow_G2": (make_case("v", 1, 300, 4, 2, 128, 64, 64, 16, anti_align=56.0), 44),
 }
 
 
@@ -181,6 +193,26 @@ def test_bwd_train_8x2k_sampled_rows_and_value_sums(gpu_lib):
     err = rel_l2(g["dq"].double().cpu().numpy()[bi, ti], o["dq"][bi, ti])
     say(f"  dq rel-L2 over {len(rows)} sampled rows: {err:.2e}")
     assert err <= GRAD_TOL
+    # key side on sampled keys of one sequence and KV head: selected keys,
+    # linear keys, keys still in the window at the end, the last chunk's keys
+    b0, g0 = 3, 5
+    sel_np = sel.cpu().numpy().astype(np.int64)
+    picked = sorted(set(sel_np[b0, g0].reshape(-1).tolist()))
+    linear = [j for j in range(0, N - W) if j not in set(picked)]
+    rng = np.random.default_rng(7)
+    js = set(rng.choice(picked, 6, replace=False).tolist()) | set(rng.choice(linear, 6, replace=False).tolist())
+    js |= {0, 1, C - 1, N - W - 1, N - W, N - C, N - 2, N - 1} | {picked[-1], linear[-1]}
+    keys = [(b0, g0, j) for j in sorted(js)]
+    ok = O.bwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"],
+                      dout_h.double().numpy(), p, sel_idx=sel_np, keys=keys)
+    jj = np.array(sorted(js))
+    for gname in ("dk", "dv"):
+        got = g[gname].double().cpu().numpy()[b0, jj, g0]
+        want = ok[gname][b0, jj, g0]
+        err = rel_l2(got, want)
+        say(f"  {gname} rel-L2 over {len(jj)} sampled keys of (b={b0}, g={g0}): {err:.2e}")
+        assert err <= GRAD_TOL
+        check_rows(got, want, 10 * GRAD_TOL, what=gname)
     dv = g["dv"].double()
     lhs = dv.sum(dim=1)                                           # [B, Hkv, d]
     rhs = dout_h.double().cuda().reshape(B, N, Hkv, Hq // Hkv, d).sum(dim=(1, 3))
@@ -188,3 +220,14 @@ def test_bwd_train_8x2k_sampled_rows_and_value_sums(gpu_lib):
     worst = float(((lhs - rhs).abs() / bound).max())
     say(f"  sum_j dv_j vs sum of dout: worst |diff| / bound {worst:.3f}")
     assert worst <= 1.0
+
+
+def test_bwd_projection_gradients_mid_size(gpu_lib):
+    """The NP-Map projection gradients, which sum over every token of every
+    head of a KV group, at a mid size (1 x 1024, 8 / 2 heads, d 128, top-16):
+    whole tensors against the oracle, with dq, dk and dv."""
+    cfg = make_case("m", 1, 1024, 8, 2, 128, 64, 64, 16, outlier_frac=0.01, heavy_scale=6.0)
+    seed = 45
+    say(f"[bwd] mid-size projections shape={workloads.shape_of(cfg)} seed={seed}")
+    g, o = run(gpu_lib, cfg, seed)
+    compare(g, o)

@@ -14,7 +14,7 @@ import torch
 
 import oracle as O
 import workloads
-from parity import BF16_TOL, check_selection, prepare, rel_l2, sampled_rows, say
+from parity import BF16_TOL, ROW_TOL_BF16, check_rows, check_selection, prepare, rel_l2, sampled_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,7 @@ def test_prefill_config_matches_oracle(gpu_lib, name):
     err = rel_l2(got, want)
     say(f"  {len(rows)} sampled rows: rel-L2 {err:.3e}; score max rel err {serr:.2e}")
     assert err <= BF16_TOL
+    check_rows(got, want, ROW_TOL_BF16)
     assert serr <= 1e-4
 
 
@@ -83,9 +84,11 @@ def test_ragged_multi_sequence_prefill_matches_oracle(gpu_lib):
                      sel_override=gsel if n_bad else None, scores=sigma)
     bi = np.array([r[0] for r in rows])
     ti = np.array([r[1] for r in rows])
-    err = rel_l2(res["out"][bi, ti].double().cpu().numpy(), o["out"][bi, ti])
+    got = res["out"][bi, ti].double().cpu().numpy()
+    err = rel_l2(got, o["out"][bi, ti])
     say(f"  {n_bad} near-tie swaps; {len(rows)} sampled rows: rel-L2 {err:.3e}")
     assert err <= BF16_TOL
+    check_rows(got, o["out"][bi, ti], ROW_TOL_BF16)
 
 
 def test_decode_config_matches_oracle(gpu_lib):
@@ -128,7 +131,9 @@ def test_decode_config_matches_oracle(gpu_lib):
                              vt[bs].double().numpy(), toks["wphi_q"].astype(np.float64),
                              toks["wphi_k"].astype(np.float64), p)
         torch.cuda.synchronize()
-        err = rel_l2(out[bs, 0].double().cpu().numpy(), want)
+        got = out[bs, 0].double().cpu().numpy()
+        err = rel_l2(got, want)
         say(f"  step {s} (t={cfg['pos'] + s}): sampled sequences {bs} rel-L2 {err:.3e}")
         assert err <= BF16_TOL
+        check_rows(got, want, ROW_TOL_BF16, what=f"step {s}")
     np.testing.assert_array_equal(gc.sel_count.cpu().numpy()[bs], oc["sel_count"])

@@ -11,8 +11,8 @@ import torch
 
 import oracle as O
 import workloads
-from parity import (BF16_TOL, F32_TOL, TIE_TOL, check_selection, make_case, prepare, rel_l2,
-                    say, torch_dtype)
+from parity import (BF16_TOL, F32_TOL, TIE_TOL, check_rows, check_selection, make_case, prepare,
+                    rel_l2, row_tol, say, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,14 @@ DEC_CASES = {
     # both the prefill and the decode steps
     "bf16_huge_logits_G4": (make_case("i", 1, 200 + 60, 8, 2, 128, 64, 64, 16, outlier_frac=0.03,
                                       heavy_scale=80.0), 200, 39),
+    # every logit far below -100 (queries along +56 u, keys along -56 u): the
+    # steps without a linear term (every routed token selected; the first
+    # chunks) must keep their softmax finite
+    "bf16_underflow_all_selected": (make_case("u", 1, 150 + 70, 8, 2, 128, 64, 64, 64, anti_align=56.0),
+                                    150, 40),
+    "bf16_underflow_G4": (make_case("v", 1, 40 + 100, 8, 2, 128, 64, 64, 16, anti_align=56.0), 40, 41),
+    "f32_underflow_d64": (make_case("w", 1, 60 + 40, 4, 1, 64, 32, 16, 16, dtype="f32", anti_align=48.0),
+                          60, 42),
 }
 
 
@@ -116,9 +124,12 @@ def test_prefill_handoff_then_decode(gpu_lib, name, general):
                               ref["wphi_k"], p)
         torch.cuda.synchronize()
         assert gc.pos == oc["pos"] == t + 1
-        err = rel_l2(g_out[:, 0].double().cpu().numpy(), o_out)
+        g_np = g_out[:, 0].double().cpu().numpy()
+        assert np.isfinite(g_np).all(), f"step t={t}: non-finite output"
+        err = rel_l2(g_np, o_out)
         worst = max(worst, err)
         assert err <= tol, f"step t={t}: rel-L2 {err:.3e}"
+        check_rows(g_np, o_out, row_tol(cfg["dtype"]), what=f"step t={t}")
         if W > 0 and t % C == C - 1 and lam > 0:
             # chunk-end decision: same flags, or a near-tie that the oracle adopts
             gf = gc.win_route.cpu().numpy()
@@ -240,6 +251,7 @@ def test_ragged_positions_decode(gpu_lib, name, general):
             err = rel_l2(g[b:b + 1], o_out)
             worst = max(worst, err)
             assert err <= tol, f"sequence {b} step t={t}: rel-L2 {err:.3e}"
+            check_rows(g[b:b + 1], o_out, row_tol(cfg["dtype"]), what=f"sequence {b} step t={t}")
     assert pos.cpu().tolist() == [n0 + steps for n0 in n0s]
     for b, n0 in enumerate(n0s):
         compare_cache(cache_slice(gc, b), ocs[b], one, n0 + steps, 1e-5)
@@ -277,8 +289,10 @@ def test_decode_routing_criteria(gpu_lib, route, general):
         o_out = O.decode_step(oc, ref["q"][:, t], ref["k"][:, t], ref["v"][:, t], ref["wphi_q"],
                               ref["wphi_k"], p)
         torch.cuda.synchronize()
-        err = rel_l2(g_out[:, 0].double().cpu().numpy(), o_out)
+        g_np = g_out[:, 0].double().cpu().numpy()
+        err = rel_l2(g_np, o_out)
         worst = max(worst, err)
         assert err <= BF16_TOL, f"step t={t}: rel-L2 {err:.3e}"
+        check_rows(g_np, o_out, row_tol("bf16"), what=f"step t={t}")
     compare_cache(gc, oc, cfg, N, 1e-5)
     say(f"  {N - N0} steps, worst rel-L2 {worst:.3e}")

@@ -12,8 +12,8 @@ import torch
 
 import oracle as O
 import workloads
-from parity import (BF16_TOL, F32_TOL, check_selection, make_case, prepare, rel_l2, say,
-                    torch_dtype)
+from parity import (BF16_TOL, F32_TOL, check_rows, check_selection, make_case, prepare, rel_l2,
+                    row_tol, say, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,8 +37,30 @@ CASES = {
     # the matrix-core path's fixed-reference pass overflows and its second
     # pass (running reference) recomputes those blocks
     "bf16_overflow_G4": (make_case("o", 1, 700, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=80.0), 24),
+    # queries along +56 u and keys along -56 u: every logit lies far below -100
+    # (natural units), below fp32's exp range.  Queries with no linear term
+    # (the first chunks; every query when every routed token is selected, or
+    # when the window covers the sequence) must keep their softmax finite.
+    "bf16_underflow_all_selected": (make_case("u", 1, 333, 8, 2, 128, 64, 64, 64, anti_align=56.0), 26),
+    "bf16_underflow_G4": (make_case("v", 2, 300, 8, 2, 128, 64, 64, 16, anti_align=56.0), 27),
+    "bf16_underflow_G2": (make_case("w", 1, 260, 4, 2, 128, 64, 64, 16, anti_align=56.0), 28),
+    "bf16_underflow_window_covers": (make_case("x", 1, 150, 4, 2, 128, 256, 64, 0, anti_align=56.0), 29),
+    "f32_underflow_d64": (make_case("y", 1, 200, 4, 1, 64, 32, 16, 16, dtype="f32", anti_align=48.0), 30),
 }
 OVERFLOW_CASES = {"bf16_overflow_G4"}
+UNDERFLOW_CASES = {n for n in CASES if "underflow" in n}
+
+
+def largest_causal_logit(cfg, seed):
+    """max over heads and causal pairs of tau q.k, natural units, on the
+    dtype-rounded inputs."""
+    _, ref = prepare(workloads.make_prefill(cfg, seed), torch_dtype(cfg["dtype"]), device="cpu")
+    G = cfg["n_q_heads"] // cfg["n_kv_heads"]
+    n = cfg["seqlen"]
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    top = max(float(np.max(np.where(causal, ref["q"][b, :, h] @ ref["k"][b, :, h // G].T, -np.inf)))
+              for b in range(cfg["batch"]) for h in range(cfg["n_q_heads"]))
+    return top / np.sqrt(cfg["head_dim"])
 
 
 def run_case(gpu_lib, cfg, seed, general):
@@ -83,17 +105,17 @@ def test_fwd_matches_oracle(gpu_lib, name, general):
         serr = 0.0
     if name in OVERFLOW_CASES:
         # the case must reach logits whose exp2 overflows fp32 (> 128 in log2 units)
-        _, ref = prepare(workloads.make_prefill(cfg, seed), torch.bfloat16, device="cpu")
-        G = cfg["n_q_heads"] // cfg["n_kv_heads"]
-        n = cfg["seqlen"]
-        causal = np.tril(np.ones((n, n), dtype=bool))
-        top = max(float(np.max(np.where(causal, ref["q"][0, :, h] @ ref["k"][0, :, h // G].T, -np.inf)))
-                  for h in range(cfg["n_q_heads"]))
-        top *= np.log2(np.e) / np.sqrt(cfg["head_dim"])
+        top = largest_causal_logit(cfg, seed) * np.log2(np.e)
         say(f"  largest causal logit {top:.1f} (log2 units)")
         assert top > 130.0
+    if name in UNDERFLOW_CASES:
+        # every logit must lie below -100 (natural units): exp underflows in fp32
+        top = largest_causal_logit(cfg, seed)
+        say(f"  largest causal logit {top:.1f} (natural units)")
+        assert top < -100.0
     say(f"  out rel-L2 {err:.3e} (tol {tol:g}), score max rel err {serr:.3e}")
     assert err <= tol
+    check_rows(out, o["out"], row_tol(cfg["dtype"]))
     assert serr <= 1e-4
 
 
@@ -142,9 +164,11 @@ def test_routing_criteria_match_oracle(gpu_lib, route, general):
     n_bad, worst = check_selection(gsel, sigma, osel, C)
     o = O.fwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"], p,
                      sel_override=gsel if n_bad else None, scores=sigma)
-    err = rel_l2(res["out"].double().cpu().numpy(), o["out"])
+    out = res["out"].double().cpu().numpy()
+    err = rel_l2(out, o["out"])
     say(f"  score max rel err {serr:.2e}; {n_bad} near-tie chunks; out rel-L2 {err:.3e}")
     assert serr <= 1e-4
     if route in ("uniform", "random"):
         np.testing.assert_array_equal(gsel, osel)
     assert err <= BF16_TOL
+    check_rows(out, o["out"], row_tol("bf16"))

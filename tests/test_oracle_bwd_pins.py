@@ -159,3 +159,23 @@ def test_bwd_sampled_rows_equal_full_dq():
     for b, t in rows:
         np.testing.assert_allclose(part["dq"][b, t], full["dq"][b, t], rtol=1e-13, atol=1e-14)
     assert np.isnan(part["dq"][0, 1]).all() and set(part) == {"dq"}
+
+
+def test_bwd_sampled_keys_equal_full_dk_dv():
+    """The sampled-keys mode (used for full-size parity of the key side)
+    visits only the queries that can see the given keys; their dk and dv
+    must equal the full computation's.  The keys cover a selected key, a
+    linear key, a key still in its window at the end and the last token."""
+    q, k, v, wq, wk, dout = rand_inputs(10, 2, 23, 4, 2, 8, scale_k=1.5)
+    p = O.Params(window=4, chunk=4, topk=2)
+    full = O.bwd_direct(q, k, v, wq, wk, dout, p)
+    sel = O.select_chunks(O.window_scores(q, k, p, 2), p)[0]
+    picked = int(sel[1, 0, 1, 0])                     # a selected key of chunk 1
+    unpicked = [j for j in range(4, 8) if j not in set(sel[1, 1, 1].tolist())][0]
+    keys = [(0, 1, 0), (1, 0, picked), (1, 1, unpicked), (0, 0, 20), (1, 1, 22)]
+    part = O.bwd_direct(q, k, v, wq, wk, dout, p, keys=keys)
+    assert set(part) == {"dk", "dv"}
+    for b, g, j in keys:
+        np.testing.assert_allclose(part["dk"][b, j, g], full["dk"][b, j, g], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(part["dv"][b, j, g], full["dv"][b, j, g], rtol=1e-12, atol=1e-13)
+    assert np.isnan(part["dk"][0, 1, 0]).all() and np.isnan(part["dv"][1, 0, 1]).all()

@@ -394,6 +394,38 @@ def test_diagonal_and_qk_routes_closed_forms():
             assert abs(sig[0, 0, t] - (vals[0] + vals[1]) / 2) < 1e-12
 
 
+@pytest.mark.parametrize("route", ["saliency", "diagonal"])
+def test_window_scores_past_the_first_query_block(route):
+    """window_scores evaluates queries in blocks (for memory); the rows of the
+    blocks after the first (their key offset j0, the diagonal column and the
+    window mask) must be each row's own window, scored on its own.  At
+    N = 700 with blocks of 256 and 100 every row is compared with a
+    brute-force per-row window: its logits written out one key at a time,
+    the pinned single-row Self-Saliency (closed forms and Lemma 1 above) or
+    the diagonal weight from explicit exponentials."""
+    q, k, v, wq, wk = rand_inputs(24, 2, 700, 4, 2, 8, scale_k=1.5)
+    W = 37
+    p = O.Params(window=W, chunk=37, topk=1, route=route)
+    tau = 1 / math.sqrt(8)
+    per_head = {blk: O.window_scores(q, k, p, 2, per_head=True, block=blk) for blk in (256, 100)}
+    sig = O.window_scores(q, k, p, 2)
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            for t in range(700):
+                js = range(max(0, t - W + 1), t + 1)
+                lg = np.array([tau * float(q[b, t, h] @ k[b, j, g]) for j in js])
+                if route == "saliency":
+                    want = O.self_saliency(lg[None, :], np.array([len(lg) - 1]), p.eps)[0]
+                else:
+                    e = [math.exp(x - lg.max()) for x in lg]
+                    want = e[-1] / sum(e)
+                for blk, got in per_head.items():
+                    assert abs(got[b, h, t] - want) <= 1e-12 * max(1.0, abs(want)), (blk, b, h, t)
+    np.testing.assert_allclose(sig, per_head[256].reshape(2, 2, 2, 700).mean(axis=2), rtol=1e-13,
+                               atol=1e-14)
+
+
 def test_diagonal_route_ranks_like_saliency_as_eps_vanishes():
     """Lemma 1 again, through the whole selection: with eps -> 0 the
     Self-Saliency picks the same tokens as the diagonal weight."""

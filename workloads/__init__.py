@@ -49,7 +49,10 @@ def make_prefill(cfg: dict, seed: int) -> dict:
 
     Order of draws: q, k, v, per-token key-norm factors (lognormal(0, 0.5),
     shared by a token's KV heads), heavy/outlier positions (key scaled),
-    the optional needle pair, then the NP-Map projections ~ N(0, 1/d)."""
+    the optional needle pair, the optional anti-aligned offsets (knob
+    ``anti_align`` = a: queries + a u, keys - a u for a unit u per sequence
+    and KV head, so every logit lies far below 0), then the NP-Map
+    projections ~ N(0, 1/d)."""
     B, N = cfg["batch"], cfg["seqlen"]
     Hq, Hkv, d = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     rng = np.random.default_rng(seed)
@@ -81,6 +84,17 @@ def make_prefill(cfg: dict, seed: int) -> dict:
                     q[b, N - 1, h] = np.linalg.norm(q[b, N - 1, h]) * u
                 kn = np.linalg.norm(k[b, p_key, g])
                 k[b, p_key, g] = kn * (0.9 * u + np.sqrt(0.19) * w)
+    if cfg.get("anti_align"):
+        # every query pushed along +a u_g and every key along -a u_g (one unit
+        # direction per sequence and KV head): all logits sit far below 0
+        a = np.float32(cfg["anti_align"])
+        G = Hq // Hkv
+        for b in range(B):
+            for g in range(Hkv):
+                u = rng.standard_normal(d)
+                u = (u / np.linalg.norm(u)).astype(np.float32)
+                q[b, :, g * G:(g + 1) * G] += a * u
+                k[b, :, g] -= a * u
     sd = 1.0 / np.sqrt(d)
     wq = (rng.standard_normal((Hkv, d // 2, d)) * sd).astype(np.float32)
     wk = (rng.standard_normal((Hkv, d // 2, d)) * sd).astype(np.float32)
