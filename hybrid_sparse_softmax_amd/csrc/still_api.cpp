@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -308,13 +309,41 @@ static size_t decode_bytes(const Dims& D, const still_shape* sh, int cap) {
     return cv.off + 256;
 }
 
+// Scratch of still_hybrid_attn_decode_step_noalloc: one array per GPU, part
+// of the library's device code, so it exists wherever that code is loaded.
+// Host code never uses the array's name as an address: the device address is
+// looked up once per GPU (with that GPU current) and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[STILL_DECODE_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch (looked up on first use).
+static int current_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return STILL_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return STILL_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return STILL_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return STILL_OK;
+}
+
 // pos_dev == nullptr: one position for the batch, cache->pos (advanced here).
 // Otherwise the ragged form: pos_dev [B] device positions, advanced by the
 // step's last kernel, and max_pos >= every one of them for the capacity check.
+// use_scratch: ws is ignored; after every check (with ws_bytes =
+// STILL_DECODE_SCRATCH_BYTES) the current GPU's scratch array serves instead.
 static int decode(const still_shape* sh, const void* q, const void* k, const void* v,
                   const float* wq, const float* wk, still_cache* cache, void* out, void* ws,
                   size_t ws_bytes, hipStream_t s, Timeline& tl, int64_t* pos_dev = nullptr,
-                  int64_t max_pos = 0) {
+                  int64_t max_pos = 0, bool use_scratch = false) {
+    if (use_scratch) ws_bytes = STILL_DECODE_SCRATCH_BYTES;
     int st = check_shape(sh, true);
     if (st) return st;
     const Dims D = make_dims(sh, 1);
@@ -338,8 +367,12 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
     if (st) return st;
     if (D.lam > 0 && cache->sel_cap < 1) return STILL_ERR_CAPACITY;
     const size_t need_ws = decode_bytes(D, sh, cache->sel_cap);
-    if (!ws || ws_bytes < need_ws) return STILL_ERR_WORKSPACE;
+    if ((!ws && !use_scratch) || ws_bytes < need_ws) return STILL_ERR_WORKSPACE;
     if (tl.ev && tl.max_ev < 4) return STILL_ERR_INVALID_ARG;
+    if (use_scratch) {
+        st = current_scratch(&ws);
+        if (st) return st;
+    }
     void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     if (use_fast_decode(D, sh)) {
         CacheView cvw = view_of(cache);
@@ -567,6 +600,15 @@ int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q,
                                  workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
+}
+
+int still_hybrid_attn_decode_step_noalloc(const still_shape* shape, const void* q, const void* k,
+                                          const void* v, const float* wphi_q,
+                                          const float* wphi_k, still_cache* cache, void* out,
+                                          hipStream_t stream) {
+    still::Timeline tl;
+    return still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, nullptr, 0, stream, tl,
+                         nullptr, 0, true);
 }
 
 int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q, const void* k,

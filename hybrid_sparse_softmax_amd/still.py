@@ -29,7 +29,7 @@ EXPORTED = (
     "still_fwd_workspace_size", "still_hybrid_attn_fwd",
     "still_decode_workspace_size", "still_hybrid_attn_decode_step",
     "still_hybrid_attn_fwd_timed", "still_hybrid_attn_decode_step_timed",
-    "still_hybrid_attn_decode_step_ragged",
+    "still_hybrid_attn_decode_step_ragged", "still_hybrid_attn_decode_step_noalloc",
     "still_bwd_workspace_size", "still_hybrid_attn_bwd", "still_hybrid_attn_bwd_timed",
     "still_future_kv_utility_workspace_size", "still_future_kv_utility",
 )
@@ -84,6 +84,9 @@ def lib() -> ct.CDLL:
         L.still_hybrid_attn_decode_step.restype = ct.c_int
         L.still_hybrid_attn_decode_step.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
                                                     ct.POINTER(CacheStruct), vp, vp, sz, vp]
+        L.still_hybrid_attn_decode_step_noalloc.restype = ct.c_int
+        L.still_hybrid_attn_decode_step_noalloc.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
+                                                            ct.POINTER(CacheStruct), vp, vp]
         L.still_hybrid_attn_decode_step_ragged.restype = ct.c_int
         L.still_hybrid_attn_decode_step_ragged.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
                                                            ct.POINTER(CacheStruct), vp, ct.c_int64,
@@ -300,6 +303,34 @@ def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softma
     else:
         _check(lib().still_hybrid_attn_decode_step_timed(*args, *timer.args()),
                "still_hybrid_attn_decode_step_timed")
+    cache.pos = int(cs.pos)
+    return out
+
+
+DECODE_SCRATCH_BYTES = 32 << 20  # STILL_DECODE_SCRATCH_BYTES
+
+
+def decode_step_noalloc(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6,
+                        softmax_scale=0.0, out=None, general=False, route="saliency"):
+    """still_hybrid_attn_decode_step_noalloc: the decode step at cache.pos
+    with the library's own per-GPU scratch instead of a workspace (nothing is
+    allocated when ``out`` is given).  Advances cache.pos.  Returns out
+    [B,1,Hq,d]."""
+    B, one, Hq, d = q.shape
+    Hkv = k.shape[2]
+    sh = make_shape(batch=B, seqlen=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                    window=cache.window, chunk=cache.chunk, topk=cache.topk, eps=eps,
+                    softmax_scale=softmax_scale, dtype=q.dtype, feat_dim=2 * wphi_q.shape[1],
+                    general=general, route=route)
+    _expect(q, "q", q.dtype, (B, 1, Hq, d))
+    _expect(k, "k", q.dtype, (B, 1, Hkv, d))
+    _expect(v, "v", q.dtype, (B, 1, Hkv, d))
+    if out is None:
+        out = torch.empty_like(q)
+    cs = cache.struct()
+    _check(lib().still_hybrid_attn_decode_step_noalloc(
+        ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), ct.byref(cs), _ptr(out),
+        _stream()), "still_hybrid_attn_decode_step_noalloc")
     cache.pos = int(cs.pos)
     return out
 

@@ -227,6 +227,33 @@ int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q
                                          void* out, void* workspace, size_t workspace_bytes,
                                          hipStream_t stream);
 
+/* Size of the device scratch that still_hybrid_attn_decode_step_noalloc
+ * keeps per GPU (32 MiB: a batch of 64 Llama-3-8B-shaped sequences, 32 / 8
+ * heads, d = 128, with selected caches of up to about 24K rows per KV head). */
+#define STILL_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* still_hybrid_attn_decode_step without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (less the
+ * workspace), same computation, same validation and errors as
+ * still_hybrid_attn_decode_step.  Its kernels use a scratch array that the
+ * library holds in device memory instead: STILL_DECODE_SCRATCH_BYTES on each
+ * GPU the library runs on, reserved with the library's device code on that
+ * GPU and kept until the process ends.  A step that needs more scratch than
+ * that (still_decode_workspace_size reports the need) returns
+ * STILL_ERR_WORKSPACE before anything is launched.  The call allocates no
+ * memory and calls no allocating routine.  Every call on one GPU uses that
+ * GPU's one scratch array: calls whose work can overlap on the same GPU
+ * (unordered streams, several threads) race and give undefined results;
+ * calls ordered on one stream are safe.  Nothing in the scratch needs
+ * clearing: every byte a step reads is written earlier in the same step.
+ * The first call on a GPU looks up the array's device address there (with
+ * that GPU current); a failed lookup returns STILL_ERR_HIP. */
+int still_hybrid_attn_decode_step_noalloc(const still_shape* shape, const void* q, const void* k,
+                                          const void* v, const float* wphi_q,
+                                          const float* wphi_k, still_cache* cache, void* out,
+                                          hipStream_t stream);
+
 /* Bytes of device workspace still_hybrid_attn_bwd needs for `shape`. */
 int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
 

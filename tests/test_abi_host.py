@@ -240,3 +240,31 @@ def test_decode_rejects_misaligned_projections():
     for wq, wk in ((MISALIGNED, FAKE), (FAKE, MISALIGNED)):
         assert L.still_hybrid_attn_decode_step(ct.byref(sh), FAKE, FAKE, FAKE, wq, wk, ct.byref(c), FAKE,
                                                FAKE, 1 << 40, None) == S.STILL_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_checks_before_touching_the_gpu():
+    """The no-allocation decode step validates like the plain step, and a
+    step whose scratch need exceeds STILL_DECODE_SCRATCH_BYTES is refused
+    with STILL_ERR_WORKSPACE before the scratch is looked up or anything is
+    launched (no GPU here, so any HIP call would fail differently)."""
+    L = S.lib()
+    assert S.DECODE_SCRATCH_BYTES == 32 << 20
+    sh = shape(batch=64, seqlen=1, n_q_heads=32, n_kv_heads=8)
+    n = ct.c_size_t(0)
+    # 64 sequences, 32 / 8 heads, d 128: a 8192-row cache fits, a 65536-row one does not
+    for cap, fits in ((8192, True), (65536, False)):
+        assert L.still_decode_workspace_size(ct.byref(sh), cap, ct.byref(n)) == S.STILL_OK
+        assert (n.value <= S.DECODE_SCRATCH_BYTES) == fits
+    cache = S.CacheStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, 4096)
+    st = L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                 ct.byref(cache), FAKE, None)
+    assert st == S.STILL_ERR_WORKSPACE
+    assert cache.pos == 4096
+    # the plain step's argument checks come first
+    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), None, FAKE, FAKE, FAKE, FAKE,
+                                                   ct.byref(cache), FAKE, None) == S.STILL_ERR_INVALID_ARG
+    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                   None, FAKE, None) == S.STILL_ERR_INVALID_ARG
+    cache.pos = 1 << 40   # capacity: lambda * ceil((t + 1 - W) / C) > cap
+    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                   ct.byref(cache), FAKE, None) == S.STILL_ERR_CAPACITY
