@@ -9,5 +9,5 @@ from .still_oracle import (  # noqa: F401
     self_saliency, window_scores, rank_order, select_chunks,
     route_from_selection, fwd_direct, new_cache, decode_step, fwd_recurrent,
     ROUTES, QUERY_FREE_ROUTES, splitmix64, random_score, query_free_score, head_score,
-    np_map_vjp, bwd_direct, future_kv_utility, kv_utility_overlap,
+    np_map_vjp, bwd_direct, future_kv_utility, kv_utility_overlap, gate_weight,
 )

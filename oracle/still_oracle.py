@@ -44,6 +44,16 @@ R-AGG     One shared normaliser: SA tokens weigh exp(tau q.k), LA tokens weigh
           phi_q(q).phi_k(k); out = sum w v / sum w  (Fig. 2 "hybrid
           aggregation"; Fig. 1: the context is kept without loss).
 R-SCALE   tau = 1/sqrt(d) unless given.
+R-GATE    The gate W_g (list view Table 9, module ablation; full text Sec. 4.1
+          training strategy and App. A.6.1: a gating projection trained with
+          the feature map, adapted by LoRA beside W_q, W_k, W_v, W_o) is taken
+          as one weight per token and query head on the linear branch, inside
+          the shared normaliser:  gamma_t,h = sigmoid(g_t,h), where the logit
+          g = x W_g is a projection of the layer input computed outside the
+          operator like q, k and v, and the linear weights become
+          gamma * phi_q(q).phi_k(k).  No gate (None) is gamma = 1, the
+          operator without the component; gamma = 0 leaves window + selected
+          softmax attention.
 R-ROUTE   The routing criteria the pages compare with Self-Saliency under the
           same routing and cache settings (full text Sec. 4 ablation, Table 7;
           list view Tab. 10-11): "diagonal" = the token's own weight a_tt in
@@ -70,7 +80,7 @@ R-BWD     Gradients (the backward pass the pages need for their two-stage
 
 Parity unpinned: the pages fix neither the exact Self-Saliency formula
 (R-SCORE), nor the exact NP-Map (R-NPMAP), nor the exact weighting of the two
-branches (R-AGG).  The functions implementing them are pinned to closed
+branches (R-AGG), nor the gate's form (R-GATE).  The functions implementing them are pinned to closed
 forms, invariants and the method's endpoints (causal softmax, causal linear
 attention, Lemma 1), but the readings themselves are the contract.
 """
@@ -267,6 +277,20 @@ def window_scores(q: np.ndarray, k: np.ndarray, p: Params, n_kv_heads: int,
 
 
 # --------------------------------------------------------------------------
+# Gate (R-GATE)
+# --------------------------------------------------------------------------
+def gate_weight(logits) -> np.ndarray:
+    """gamma = sigmoid(g) = 1 / (1 + exp(-g)), evaluated without overflow:
+    exp(g) / (1 + exp(g)) for g < 0.  g = -inf gives 0, g = +inf gives 1."""
+    g = np.asarray(logits, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        pos = 1.0 / (1.0 + np.exp(-np.where(g >= 0, g, 0.0)))
+        e = np.exp(np.where(g < 0, g, 0.0))
+        neg = e / (1.0 + e)
+    return np.where(g >= 0, pos, neg)
+
+
+# --------------------------------------------------------------------------
 # Per-chunk selection (Sec. 3.3 Chunk-Wise Parallel Form; R-SELECT)
 # --------------------------------------------------------------------------
 def rank_order(scores: np.ndarray, positions: np.ndarray) -> np.ndarray:
@@ -314,7 +338,7 @@ def route_from_selection(sel_idx: np.ndarray, N: int, C: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Chunk-parallel forward, direct per-query form (Sec. 3.3; R-DELAY, R-AGG)
 # --------------------------------------------------------------------------
-def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=None):
+def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=None, gate=None):
     """Hybrid attention output from the explicit per-query index sets.
 
     q [B,N,Hq,d], k/v [B,N,Hkv,d], wq/wk [Hkv, d'/2, d]  (float64 views).
@@ -323,6 +347,7 @@ def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=
     of the oracle's own selection (near-tie protocol).
     scores: optional group scores [B,Hkv,N] already computed by window_scores
     (saves recomputing them when only a few rows are evaluated).
+    gate: optional gate logits [B,N,Hq] (R-GATE); None is no gate.
 
     Returns dict(out [B,N,Hq,d] (NaN where not evaluated), scores, sel_idx, route).
 
@@ -330,7 +355,7 @@ def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=
       J_t  = [max(0, t-W+1), t]                       window (softmax)
       R_t  = {j <= t-W}                               routed region
       SA_t = J_t  U  {j in R_t : route_j = SA}        exp(tau q.k) weights
-      LA_t = R_t \\ SA_t                              phi_q(q).phi_k(k) weights
+      LA_t = R_t \\ SA_t                              gamma phi_q(q).phi_k(k) weights
       out  = sum_{SA_t u LA_t} w_j v_j / sum w_j
     """
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
@@ -356,6 +381,7 @@ def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=
         route = np.full((B, Hkv, N), ROUTE_LA, np.uint8)
 
     phik = np.stack([np_map(k[:, :, g, :], wk[g]) for g in range(Hkv)], axis=2)  # [B,N,Hkv,d']
+    gam = np.ones((B, N, Hq)) if gate is None else gate_weight(gate)
 
     out = np.full(q.shape, np.nan)
     if rows is None:
@@ -378,6 +404,7 @@ def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=
                 qv = q[b, t, h]
                 s = tau * (k[b, sa, g, :] @ qv)
                 w_la = phik[b, la_routed, g, :] @ np_map(qv, wq[g]) if la_routed.size else np.zeros(0)
+                w_la = gam[b, t, h] * w_la
                 # shared normaliser; subtracting M = max(0, max s) changes nothing
                 M = max(0.0, s.max()) if s.size else 0.0
                 w_sa = np.exp(s - M)
@@ -405,10 +432,11 @@ def new_cache(B, Hkv, d, feat_dim, p: Params, cap: int) -> dict:
     )
 
 
-def decode_step(cache: dict, q_t, k_t, v_t, wq, wk, p: Params, sel_override=None):
+def decode_step(cache: dict, q_t, k_t, v_t, wq, wk, p: Params, sel_override=None, gate_t=None):
     """One recurrent step at position t = cache['pos'] for every sequence.
 
-    q_t [B,Hq,d], k_t/v_t [B,Hkv,d].  Mutates the cache; returns out [B,Hq,d].
+    q_t [B,Hq,d], k_t/v_t [B,Hkv,d], gate_t: optional gate logits [B,Hq]
+    (R-GATE).  Mutates the cache; returns out [B,Hq,d].
 
     Steps per (b, g):
       1. token j = t-W leaves the window: SA -> appended to the selected
@@ -429,6 +457,7 @@ def decode_step(cache: dict, q_t, k_t, v_t, wq, wk, p: Params, sel_override=None
     W, C, lam = p.window, p.chunk, p.topk_eff()
     tau = p.tau(d)
     t = cache["pos"]
+    gam = np.ones((B, Hq)) if gate_t is None else gate_weight(gate_t)
     out = np.zeros((B, Hq, d))
     for b in range(B):
         for g in range(Hkv):
@@ -479,7 +508,7 @@ def decode_step(cache: dict, q_t, k_t, v_t, wq, wk, p: Params, sel_override=None
                 else:
                     s = tau * (sk @ qv)
                     vv = sv
-                fq = np_map(qv, wq[g])
+                fq = gam[b, h] * np_map(qv, wq[g])
                 M = max(0.0, s.max()) if s.size else 0.0
                 w_sa = np.exp(s - M)
                 num = w_sa @ vv + math.exp(-M) * (fq @ cache["lin_S"][b, g])
@@ -506,9 +535,10 @@ def decode_step(cache: dict, q_t, k_t, v_t, wq, wk, p: Params, sel_override=None
     return out
 
 
-def fwd_recurrent(q, k, v, wq, wk, p: Params, cap: int | None = None, sel_override=None):
-    """Run the recurrent form token by token from an empty cache.
-    Returns (out [B,N,Hq,d], cache after N tokens)."""
+def fwd_recurrent(q, k, v, wq, wk, p: Params, cap: int | None = None, sel_override=None,
+                  gate=None):
+    """Run the recurrent form token by token from an empty cache (gate:
+    optional logits [B,N,Hq]).  Returns (out [B,N,Hq,d], cache after N tokens)."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -518,7 +548,8 @@ def fwd_recurrent(q, k, v, wq, wk, p: Params, cap: int | None = None, sel_overri
     cache = new_cache(B, Hkv, d, 2 * wq.shape[1], p, cap)
     out = np.zeros(q.shape)
     for t in range(N):
-        out[:, t] = decode_step(cache, q[:, t], k[:, t], v[:, t], wq, wk, p, sel_override)
+        out[:, t] = decode_step(cache, q[:, t], k[:, t], v[:, t], wq, wk, p, sel_override,
+                                None if gate is None else np.asarray(gate)[:, t])
     return out, cache
 
 
@@ -566,28 +597,32 @@ def np_map_vjp(x, P, dphi):
     return dx, dP
 
 
-def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=None):
+def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=None, gate=None):
     """Gradients of L = sum(dout * out) with out = fwd_direct(q, k, v, wq,
     wk, p) and the routing fixed to ``sel_idx`` [B, Hkv, N//C, lambda]
     (the forward's own selection when None).
 
-    Returns dict(dq, dk, dv [shapes of q, k, v], dwq, dwk [shape of wq]).
+    Returns dict(dq, dk, dv [shapes of q, k, v], dwq, dwk [shape of wq]), plus
+    dgate [B, N, Hq] when gate logits [B, N, Hq] are given (R-GATE).
     rows: optional list of distinct (b, t); then only those queries are visited and
-    only dq is returned (NaN elsewhere): dq of a query depends on that query
-    alone, while every key-side gradient sums over all queries.
+    only dq (and dgate) is returned (NaN elsewhere): dq of a query depends on
+    that query alone, while every key-side gradient sums over all queries.
     keys: optional list of (b, g, j); then only the queries that can see key
     j of (b, g) are visited -- t >= j of the heads of KV head g -- and only
     dk and dv are returned, at those keys (NaN elsewhere).  A key's gradient
     sums over exactly those queries.
 
     Per query t of head h (KV head g), with the sets of fwd_direct:
-      w_j = exp(s_j - M) on SA_t, exp(-M) kappa_j on LA_t, kappa_j = phi_q . phi_k(k_j)
+      w_j = exp(s_j - M) on SA_t, gamma exp(-M) kappa_j on LA_t,
+      kappa_j = phi_q . phi_k(k_j), gamma = sigmoid(gate) (1 without a gate)
       den = sum w_j,  out = sum w_j v_j / den,  Dt = dout . out
       SA:  ds_j = (w_j / den) (dout . v_j - Dt);  dq += tau ds_j k_j;
            dk_j += tau ds_j q;  dv_j += (w_j / den) dout
-      LA:  dkappa_j = (exp(-M) / den) (dout . v_j - Dt);
+      LA:  dkappa_j = (gamma exp(-M) / den) (dout . v_j - Dt);
            dphi_q += dkappa_j phi_k(k_j);  dphi_k(k_j) += dkappa_j phi_q;
            dv_j += (w_j / den) dout
+      gate: dgamma = sum over LA_t of (exp(-M) kappa_j / den) (dout . v_j - Dt),
+           dgate = gamma (1 - gamma) dgamma
     then the NP-Map's vector-Jacobian product carries dphi_q to q and W_phi_q,
     dphi_k to k and W_phi_k."""
     q, k, v, dout = (np.asarray(a, np.float64) for a in (q, k, v, dout))
@@ -605,6 +640,8 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=N
         route = np.full((B, Hkv, N), ROUTE_LA, np.uint8)
 
     phik = np.stack([np_map(k[:, :, g, :], wk[g]) for g in range(Hkv)], axis=2)
+    gam = np.ones((B, N, Hq)) if gate is None else gate_weight(gate)
+    dgate = np.zeros((B, N, Hq))
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     dphiq = np.zeros(q.shape[:3] + (2 * wq.shape[1],))
     dphik = np.zeros_like(phik)
@@ -637,7 +674,8 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=N
                 kap = phik[b, la, g, :] @ fq
                 M = max(0.0, s.max()) if s.size else 0.0
                 w_sa = np.exp(s - M)
-                w_la = math.exp(-M) * kap
+                gm = gam[b, t, h]
+                w_la = gm * math.exp(-M) * kap
                 den = w_sa.sum() + w_la.sum()
                 o = (w_sa @ v[b, sa, g, :] + w_la @ v[b, la, g, :]) / den
                 Dt = do @ o
@@ -645,7 +683,9 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=N
                 dq[b, t, h] += tau * (ds @ k[b, sa, g, :])
                 np.add.at(dk[b, :, g, :], sa, tau * np.outer(ds, qv))
                 np.add.at(dv[b, :, g, :], sa, np.outer(w_sa / den, do))
-                dkap = (math.exp(-M) / den) * (v[b, la, g, :] @ do - Dt)
+                vd_la = v[b, la, g, :] @ do - Dt
+                dgate[b, t, h] = gm * (1.0 - gm) * ((math.exp(-M) / den) * (kap @ vd_la))
+                dkap = (gm * math.exp(-M) / den) * vd_la
                 dphiq[b, t, h] += dkap @ phik[b, la, g, :]
                 np.add.at(dphik[b, :, g, :], la, np.outer(dkap, fq))
                 np.add.at(dv[b, :, g, :], la, np.outer(w_la / den, do))
@@ -656,6 +696,7 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=N
             dk_keys[b, j, g] = dk[b, j, g] + dx
             dv_keys[b, j, g] = dv[b, j, g]
         return dict(dk=dk_keys, dv=dv_keys)
+    dgate_out = {} if gate is None else {"dgate": dgate}
     if rows is not None:
         dq_rows = np.full(q.shape, np.nan)
         for b, t in visit:
@@ -663,7 +704,12 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=N
                 for h in range(g * G, (g + 1) * G):
                     dx, _ = np_map_vjp(q[b, t, h], wq[g], dphiq[b, t, h])
                     dq_rows[b, t, h] = dq[b, t, h] + dx
-        return dict(dq=dq_rows)
+        if gate is not None:
+            dg_rows = np.full(dgate.shape, np.nan)
+            for b, t in visit:
+                dg_rows[b, t] = dgate[b, t]
+            dgate_out = {"dgate": dg_rows}
+        return dict(dq=dq_rows, **dgate_out)
     dwq, dwk = np.zeros_like(wq), np.zeros_like(wk)
     for g in range(Hkv):
         for h in range(g * G, (g + 1) * G):
@@ -673,7 +719,7 @@ def bwd_direct(q, k, v, wq, wk, dout, p: Params, sel_idx=None, rows=None, keys=N
         dx, dP = np_map_vjp(k[:, :, g, :], wk[g], dphik[:, :, g, :])
         dk[:, :, g, :] += dx
         dwk[g] += dP
-    return dict(dq=dq, dk=dk, dv=dv, dwq=dwq, dwk=dwk)
+    return dict(dq=dq, dk=dk, dv=dv, dwq=dwq, dwk=dwk, **dgate_out)
 
 
 # --------------------------------------------------------------------------
