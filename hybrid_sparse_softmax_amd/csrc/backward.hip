@@ -88,7 +88,9 @@ __global__ __launch_bounds__(256) void bwd_route_kernel(const int32_t* __restric
 //      linear tokens entering through S_t, z_t and the partly covered chunk;
 //   2. ds_j = (w_j / l)(vd_j - D_t), dq = tau sum ds_j k_j.
 // Then dphi_q = c_t (S_t dout - D_t z_t + sum over the partly covered chunk's
-// linear tokens of (vd_j - D_t) phi_k(j)), c_t = exp(-m) / l.
+// linear tokens of (vd_j - D_t) phi_k(j)), c_t = exp(-m) / l.  phi_q here is
+// the gated feature gamma phi_q (gamma = 1 without a gate); the kernel writes
+// gamma dphi_q for the NP-Map's VJP and dgate = (1 - gamma) phi_q . dphi_q.
 // stat[(b, t, h)] = (m, l, D_t, c_t).
 constexpr int kNP = 2;  // query positions per wave
 template <typename T, int DD, int GM>
@@ -96,8 +98,8 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
     const uint8_t* __restrict__ route, const int32_t* __restrict__ selw,
-    const float* __restrict__ lin, float* __restrict__ dq, float* __restrict__ dphiq,
-    float* __restrict__ stat, Dims D) {
+    const float* __restrict__ lin, const float* __restrict__ gate, float* __restrict__ dq,
+    float* __restrict__ dphiq, float* __restrict__ dgate, float* __restrict__ stat, Dims D) {
     constexpr int PL = DD / kWave;
     constexpr int R = kNP * GM;  // rows: position pp, head h -> pp GM + h
     const Item it = xcd_item((D.N + kNP - 1) / kNP, D.Hkv);
@@ -370,8 +372,18 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
                 const size_t o = qoff(pp, h);
                 // no linear mass: no linear term to differentiate
                 const float cf = la_mass[r] ? expf(-m[r]) * inv[r] : 0.f;
+                // cf dfq is the gradient w.r.t. the gated features fq = gamma phi_q:
+                // phi_q gets gamma times it, the gate logit (1 - gamma) fq . (cf dfq)
+                const float gw = gate_weight(gate, o);
 #pragma unroll
-                for (int p = 0; p < PL; ++p) dphiq[o * DD + lane + kWave * p] = cf * dfq[h][p];
+                for (int p = 0; p < PL; ++p) dphiq[o * DD + lane + kWave * p] = gw * cf * dfq[h][p];
+                if (dgate) {
+                    float fd = 0.f;
+#pragma unroll
+                    for (int p = 0; p < PL; ++p) fd = fmaf(fq[pp][h][lane + kWave * p], dfq[h][p], fd);
+                    fd = wave_sum(fd);
+                    if (lane == 0) dgate[o] = (1.f - gw) * cf * fd;
+                }
                 if (lane == 0) {
                     stat[o * 4 + 0] = m[r];
                     stat[o * 4 + 1] = l[r];
@@ -942,9 +954,11 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
                                                (size_t)D.C * sizeof(int), s, a.sel_idx, w.route,
                                                w.selw, D));
     if ((e = mark.fn(mark.ctx, "phi_q")) != hipSuccess) return e;
-    if ((e = launch_phi(D, a.q, D.Hq, D.G, a.wq, w.phiq, s)) != hipSuccess) return e;
+    // the queries' features carry their gate weights (phi~_q = gamma phi_q), so
+    // every linear term below is the gated one
+    if ((e = launch_phi(D, a.q, D.Hq, D.G, a.wq, a.gate, w.phiq, s)) != hipSuccess) return e;
     if ((e = mark.fn(mark.ctx, "phi_k")) != hipSuccess) return e;
-    if ((e = launch_phi(D, a.k, D.Hkv, 1, a.wk, w.phik, s)) != hipSuccess) return e;
+    if ((e = launch_phi(D, a.k, D.Hkv, 1, a.wk, nullptr, w.phik, s)) != hipSuccess) return e;
     if ((e = mark.fn(mark.ctx, "la_chunk")) != hipSuccess) return e;
     if ((e = launch_la_chunks(D, w.phik, a.v, w.route, w.lin, s)) != hipSuccess) return e;
     if ((e = mark.fn(mark.ctx, "la_scan")) != hipSuccess) return e;
@@ -952,7 +966,8 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 #define STILL_BWD_QUERY(GM)                                                                     \
     hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM>), dim3((D.N + kNP - 1) / kNP * D.Hkv * D.B), dim3(64), \
                        0, s, q, k,                                                                  \
-                       v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.dq, w.dphiq, w.stat, D)
+                       v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.gate, a.dq, w.dphiq,    \
+                       a.dgate, w.stat, D)
     STILL_STEP("bwd_query", if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
                             else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));
 #undef STILL_BWD_QUERY

@@ -24,6 +24,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const T* __restrict__ 
                                                           const T* __restrict__ v,
                                                           const float* __restrict__ wq,
                                                           const float* __restrict__ wk,
+                                                          const float* __restrict__ gate,
                                                           CacheView c, DecodeWork w, Dims D) {
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
@@ -167,7 +168,9 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const T* __restrict__ 
                 if (lane == 0) { win_part[0] = kNegInf; win_part[1] = 0.f; }
                 for (int i = lane; i < DD; i += kWave) win_part[2 + i] = 0.f;
             }
-            np_map_wave(qs[wave], wq + (size_t)g * (D.fd / 2) * DD, DD, D.fd, fq[wave], lane);
+            // the query's features carry its gate weight (the linear branch's weight)
+            np_map_wave(qs[wave], wq + (size_t)g * (D.fd / 2) * DD, DD, D.fd, fq[wave], lane,
+                        gate_weight(gate, (size_t)b * D.Hq + h));
         }
         __syncthreads();
         if (act) {
@@ -340,13 +343,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeWork w, T* __r
 
 template <typename T, int DD>
 hipError_t prep_t(const Dims& D, const void* q, const void* k, const void* v, const float* wq,
-                  const float* wk, const CacheView& c, const DecodeWork& w, hipStream_t s) {
+                  const float* wk, const float* gate, const CacheView& c, const DecodeWork& w,
+                  hipStream_t s) {
     dim3 grid(D.Hkv, D.B);
     const T* qq = reinterpret_cast<const T*>(q);
     const T* kk = reinterpret_cast<const T*>(k);
     const T* vv = reinterpret_cast<const T*>(v);
     const int R = (D.W + kWave - 1) / kWave;
-#define STILL_PREP(RR) hipLaunchKernelGGL((decode_prep_kernel<T, DD, RR>), grid, dim3(256), 0, s, qq, kk, vv, wq, wk, c, w, D)
+#define STILL_PREP(RR) hipLaunchKernelGGL((decode_prep_kernel<T, DD, RR>), grid, dim3(256), 0, s, qq, kk, vv, wq, wk, gate, c, w, D)
     if (R <= 1) STILL_PREP(1);
     else if (R <= 2) STILL_PREP(2);
     else if (R <= 4) STILL_PREP(4);
@@ -358,13 +362,13 @@ hipError_t prep_t(const Dims& D, const void* q, const void* k, const void* v, co
 }  // namespace
 
 hipError_t launch_decode_prep(const Dims& D, const void* q, const void* k, const void* v,
-                              const float* wphi_q, const float* wphi_k, const CacheView& c,
-                              const DecodeWork& w, hipStream_t s) {
+                              const float* wphi_q, const float* wphi_k, const float* gate,
+                              const CacheView& c, const DecodeWork& w, hipStream_t s) {
     if (D.d == 128)
-        return D.bf16 ? prep_t<__bf16, 128>(D, q, k, v, wphi_q, wphi_k, c, w, s)
-                      : prep_t<float, 128>(D, q, k, v, wphi_q, wphi_k, c, w, s);
-    return D.bf16 ? prep_t<__bf16, 64>(D, q, k, v, wphi_q, wphi_k, c, w, s)
-                  : prep_t<float, 64>(D, q, k, v, wphi_q, wphi_k, c, w, s);
+        return D.bf16 ? prep_t<__bf16, 128>(D, q, k, v, wphi_q, wphi_k, gate, c, w, s)
+                      : prep_t<float, 128>(D, q, k, v, wphi_q, wphi_k, gate, c, w, s);
+    return D.bf16 ? prep_t<__bf16, 64>(D, q, k, v, wphi_q, wphi_k, gate, c, w, s)
+                  : prep_t<float, 64>(D, q, k, v, wphi_q, wphi_k, gate, c, w, s);
 }
 
 hipError_t launch_decode_sel(const Dims& D, const void* q, const CacheView& c, const DecodeWork& w,

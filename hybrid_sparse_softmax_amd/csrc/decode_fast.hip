@@ -64,9 +64,10 @@ __device__ __forceinline__ float dot8(bf16x8 a, bf16x8 b, float acc) {
 
 // NP-Map of one 128-vector by one wave (Sec. 3.2): lane f < 64 forms
 // u_f = P[f] . x from its projection row (float4 loads), z = ||x|| u / ||u||,
-// phi = [softmax(z); softmax(-z)].  xs, out: LDS.
+// phi = [softmax(z); softmax(-z)], times `scale` (a query's gate weight; 1
+// for keys).  xs, out: LDS.
 __device__ __forceinline__ void np_map_wave128(const float* xs, const float* __restrict__ P,
-                                               float* out, int lane) {
+                                               float* out, int lane, float scale = 1.f) {
     float ss = xs[lane] * xs[lane] + xs[lane + 64] * xs[lane + 64];
     const float nx = sqrtf(wave_sum(ss));
     const f32x4* pr = reinterpret_cast<const f32x4*>(P + (size_t)lane * kD);
@@ -84,8 +85,8 @@ __device__ __forceinline__ void np_map_wave128(const float* xs, const float* __r
     const float m1 = wave_max(z), m2 = wave_max(-z);
     const float e1 = expf(z - m1), e2 = expf(-z - m2);
     const float s1 = wave_sum(e1), s2 = wave_sum(e2);
-    out[lane] = e1 / s1;
-    out[64 + lane] = e2 / s2;
+    out[lane] = scale * (e1 / s1);
+    out[64 + lane] = scale * (e2 / s2);
 }
 
 struct FastWork {
@@ -240,7 +241,8 @@ __device__ __forceinline__ void stream_role(const bf16* __restrict__ q, const Ca
 // --------------------------------------------------------------------------
 __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                            const bf16* __restrict__ v, const float* __restrict__ wq,
-                                           const float* __restrict__ wk, const CacheView& c,
+                                           const float* __restrict__ wk,
+                                           const float* __restrict__ gate, const CacheView& c,
                                            const FastWork& w, const Dims& D, int b, int g) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t bg = (size_t)b * D.Hkv + g;
@@ -274,7 +276,9 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
     // NP-Map of the query heads and, for a linear eviction, of the leaving key
     const int items = G + (ev == kRouteLA ? 1 : 0);
     for (int it = wave; it < items; it += 4) {
-        if (it < G) np_map_wave128(qs[it], wq + (size_t)g * (kD / 2) * kD, phq[it], lane);
+        if (it < G)  // the query's features carry its gate weight
+            np_map_wave128(qs[it], wq + (size_t)g * (kD / 2) * kD, phq[it], lane,
+                           gate_weight(gate, (size_t)b * D.Hq + g * G + it));
         else np_map_wave128(xs, wk + (size_t)g * (kD / 2) * kD, ph, lane);
     }
     int appended = 0;
@@ -449,12 +453,13 @@ __global__ __launch_bounds__(256) void dec_stream_kernel(const bf16* __restrict_
                                                          const bf16* __restrict__ k,
                                                          const bf16* __restrict__ v,
                                                          const float* __restrict__ wq,
-                                                         const float* __restrict__ wk, CacheView c,
+                                                         const float* __restrict__ wk,
+                                                         const float* __restrict__ gate, CacheView c,
                                                          FastWork w, Dims D) {
     const int nstate = D.B * D.Hkv;
     const int bid = blockIdx.x;
     if (bid < nstate) {
-        state_role(q, k, v, wq, wk, c, w, D, bid / D.Hkv, bid % D.Hkv);
+        state_role(q, k, v, wq, wk, gate, c, w, D, bid / D.Hkv, bid % D.Hkv);
     } else {
         const int x = bid - nstate;
         const int split = x % w.nsplit, bg = x / w.nsplit;
@@ -515,7 +520,8 @@ size_t fast_decode_floats(const Dims& D, int nsplit) {
 }
 
 hipError_t launch_fast_decode(const Dims& D, const void* q, const void* k, const void* v,
-                              const float* wq, const float* wk, const CacheView& c, float* ws,
+                              const float* wq, const float* wk, const float* gate,
+                              const CacheView& c, float* ws,
                               int nsplit, void* out, int phase, hipStream_t s) {
     FastWork w;
     w.nsplit = D.lam > 0 ? nsplit : 0;
@@ -532,7 +538,7 @@ hipError_t launch_fast_decode(const Dims& D, const void* q, const void* k, const
     const bf16* qq = reinterpret_cast<const bf16*>(q);
     const bf16* kk = reinterpret_cast<const bf16*>(k);
     const bf16* vv = reinterpret_cast<const bf16*>(v);
-#define STILL_DEC(GG) hipLaunchKernelGGL(dec_stream_kernel<GG>, dim3(nblk), dim3(256), 0, s, qq, kk, vv, wq, wk, c, w, D)
+#define STILL_DEC(GG) hipLaunchKernelGGL(dec_stream_kernel<GG>, dim3(nblk), dim3(256), 0, s, qq, kk, vv, wq, wk, gate, c, w, D)
     if (D.G == 1) STILL_DEC(1);
     else if (D.G == 2) STILL_DEC(2);
     else if (D.G == 4) STILL_DEC(4);

@@ -77,6 +77,12 @@ __device__ __forceinline__ float log1p_fast(float x) {
 // x / y through the hardware reciprocal (about 1 ulp each)
 __device__ __forceinline__ float fast_div(float x, float y) { return x * __builtin_amdgcn_rcpf(y); }
 
+// Weight of the linear branch from the gate logit of one (token, query head):
+// gamma = sigmoid(g) (g = -inf gives 0, +inf gives 1); 1 without a gate.
+__device__ __forceinline__ float gate_weight(const float* __restrict__ gate, size_t i) {
+    return gate ? 1.f / (1.f + expf(-gate[i])) : 1.f;
+}
+
 // Sort key of a routing score: -0 counts as +0 and NaN ranks below every
 // number, so that float comparison of keys gives the selection order.
 __device__ __forceinline__ float route_key(float s) {

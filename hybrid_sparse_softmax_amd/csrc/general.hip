@@ -21,6 +21,7 @@ constexpr float kNegInf = -__builtin_inff();
 
 template <typename T>
 __global__ __launch_bounds__(64) void phi_kernel(const T* __restrict__ x, const float* __restrict__ P,
+                                                 const float* __restrict__ gate,
                                                  float* __restrict__ phi, int H, int hpp, int d,
                                                  int fd) {
     const int tok = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
@@ -29,7 +30,9 @@ __global__ __launch_bounds__(64) void phi_kernel(const T* __restrict__ x, const 
     const T* xr = x + ((size_t)tok * H + h) * d;
     for (int i = lane; i < d; i += kWave) xs[i] = to_f32(xr[i]);
     __syncthreads();
-    np_map_wave(xs, P + (size_t)(h / hpp) * (fd / 2) * d, d, fd, ph, lane);
+    // a query's features carry its gate weight (the linear branch's weight)
+    np_map_wave(xs, P + (size_t)(h / hpp) * (fd / 2) * d, d, fd, ph, lane,
+                gate_weight(gate, (size_t)tok * H + h));
     __syncthreads();
     float* pr = phi + ((size_t)tok * H + h) * fd;
     for (int i = lane; i < fd; i += kWave) pr[i] = ph[i];
@@ -412,11 +415,11 @@ __global__ __launch_bounds__(256) void handoff_kernel(const T* __restrict__ k,
 }
 
 template <typename T>
-hipError_t phi_t(const Dims& D, const void* x, int H, int hpp, const float* P, float* phi,
-                 hipStream_t s) {
+hipError_t phi_t(const Dims& D, const void* x, int H, int hpp, const float* P, const float* gate,
+                 float* phi, hipStream_t s) {
     dim3 grid(D.B * D.N, H);
-    hipLaunchKernelGGL(phi_kernel<T>, grid, dim3(64), 0, s, reinterpret_cast<const T*>(x), P, phi,
-                       H, hpp, D.d, D.fd);
+    hipLaunchKernelGGL(phi_kernel<T>, grid, dim3(64), 0, s, reinterpret_cast<const T*>(x), P, gate,
+                       phi, H, hpp, D.d, D.fd);
     return hipGetLastError();
 }
 
@@ -447,9 +450,10 @@ hipError_t main_t(const Dims& D, const void* q, const void* k, const void* v, co
 }
 }  // namespace
 
-hipError_t launch_phi(const Dims& D, const void* x, int H, int hpp, const float* P, float* phi,
-                      hipStream_t s) {
-    return D.bf16 ? phi_t<__bf16>(D, x, H, hpp, P, phi, s) : phi_t<float>(D, x, H, hpp, P, phi, s);
+hipError_t launch_phi(const Dims& D, const void* x, int H, int hpp, const float* P,
+                      const float* gate, float* phi, hipStream_t s) {
+    return D.bf16 ? phi_t<__bf16>(D, x, H, hpp, P, gate, phi, s)
+                  : phi_t<float>(D, x, H, hpp, P, gate, phi, s);
 }
 
 hipError_t launch_head_scores(const Dims& D, const void* q, const void* k, float* hs, hipStream_t s) {

@@ -40,8 +40,10 @@ struct CacheView {
 
 // ---- general kernels (any supported shape, f32 or bf16 storage) ----------
 // phi[tok, h, :] = NP-Map of x[tok, h, :] with projection P[h / heads_per_proj]
+// gate: logits [B, N, H] whose sigmoid scales each phi row (queries with a
+// gate), or nullptr
 hipError_t launch_phi(const Dims& D, const void* x, int H, int heads_per_proj, const float* P,
-                      float* phi, hipStream_t s);
+                      const float* gate, float* phi, hipStream_t s);
 // per-query-head Self-Saliency hs[b, h, t]
 hipError_t launch_head_scores(const Dims& D, const void* q, const void* k, float* hs, hipStream_t s);
 // group mean, per-chunk top-k, route flags, selected positions
@@ -92,8 +94,8 @@ hipError_t launch_la_group_scan(const Dims& D, const LinBufs& L, int cap_chunk, 
                                 float* cap_z, hipStream_t s);
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const void* wsplit, const void* phik, const uint8_t* route,
-                              const void* ksel, const void* vsel, const LinBufs& L, void* out,
-                              hipStream_t s);
+                              const void* ksel, const void* vsel, const LinBufs& L,
+                              const float* gate, void* out, hipStream_t s);
 
 // ---- decode step ------------------------------------------------------------
 struct DecodeWork {
@@ -104,8 +106,8 @@ struct DecodeWork {
     int rows_per_split;
 };
 hipError_t launch_decode_prep(const Dims& D, const void* q, const void* k, const void* v,
-                              const float* wphi_q, const float* wphi_k, const CacheView& c,
-                              const DecodeWork& w, hipStream_t s);
+                              const float* wphi_q, const float* wphi_k, const float* gate,
+                              const CacheView& c, const DecodeWork& w, hipStream_t s);
 hipError_t launch_decode_sel(const Dims& D, const void* q, const CacheView& c, const DecodeWork& w,
                              hipStream_t s);
 // advances pos_dev[b] by one when pos_dev is not null (ragged decode step)
@@ -117,8 +119,9 @@ bool fast_decode_supported(const Dims& D);
 int fast_decode_splits(int cap);                     // stream splits of 1024 selected rows
 size_t fast_decode_floats(const Dims& D, int nsplit);  // workspace, in floats
 hipError_t launch_fast_decode(const Dims& D, const void* q, const void* k, const void* v,
-                              const float* wq, const float* wk, const CacheView& c, float* ws,
-                              int nsplit, void* out, int phase, hipStream_t s);  // phase 0, then 1
+                              const float* wq, const float* wk, const float* gate,
+                              const CacheView& c, float* ws, int nsplit, void* out, int phase,
+                              hipStream_t s);  // phase 0, then 1
 
 // ---- backward (general kernels; routing held fixed) ----------------------
 struct BwdArgs {
@@ -126,6 +129,8 @@ struct BwdArgs {
     const float *wq, *wk;               // [Hkv, fd/2, d]
     const int32_t* sel_idx;             // [B, Hkv, n_full, lam] the forward's selection
     float *dq, *dk, *dv, *dwq, *dwk;    // fp32 gradients, overwritten
+    const float* gate;                  // [B, N, Hq] gate logits, or nullptr
+    float* dgate;                       // [B, N, Hq] fp32, written when gate and dgate are set
 };
 struct BwdWork {
     float *phiq, *phik;   // [B, N, Hq | Hkv, fd]

@@ -3,14 +3,15 @@
 //   u = P x                       P: [fd/2, d], the learned direction
 //   z = ||x|| * u / ||u||         pretrained norm re-injected (z = 0 if u = 0)
 //   phi = [softmax(z); softmax(-z)]  (fd values)
-// xs: d floats readable by the whole wave (LDS); out: fd floats (LDS).
+// xs: d floats readable by the whole wave (LDS); out: fd floats (LDS), each
+// times `scale` (the gate weight of a query; 1 for keys).
 #pragma once
 #include "device_common.h"
 
 namespace still {
 
 __device__ inline void np_map_wave(const float* xs, const float* __restrict__ P, int d, int fd,
-                                   float* out, int lane) {
+                                   float* out, int lane, float scale = 1.f) {
     float ss = 0.f;
     for (int i = lane; i < d; i += kWave) ss = fmaf(xs[i], xs[i], ss);
     const float nx = sqrtf(wave_sum(ss));
@@ -34,8 +35,8 @@ __device__ inline void np_map_wave(const float* xs, const float* __restrict__ P,
     const float e1 = act ? expf(z - m1) : 0.f, e2 = act ? expf(-z - m2) : 0.f;
     const float s1 = wave_sum(e1), s2 = wave_sum(e2);
     if (act) {
-        out[lane] = e1 / s1;
-        out[half + lane] = e2 / s2;
+        out[lane] = scale * (e1 / s1);
+        out[half + lane] = scale * (e2 / s2);
     }
 }
 

@@ -867,8 +867,8 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wqh, const bf16* __restrict__ wql, const bf16* __restrict__ phik,
     const uint8_t* __restrict__ route,
-    const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, LinBufs L, bf16* __restrict__ out,
-    Dims D) {
+    const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, LinBufs L,
+    const float* __restrict__ gate, bf16* __restrict__ out, Dims D) {
     constexpr int NW = HB * 2;  // waves
     const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
@@ -1027,6 +1027,18 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         selmask = __ballot(rt == kRouteSA);
         f32x16 phi[1][2][2];
         np_map_mfma<1>(qf, pre, pre + kKTile, kKS, phi);
+        if (gate) {
+            // the query's features carry its gate weight, so both the linear
+            // numerator and denominator below do
+            const int tg = min(t0 + oq, D.N - 1);
+            const float gw = gate_weight(gate, ((size_t)b * D.N + tg) * D.Hq + h);
+#pragma unroll
+            for (int sgn = 0; sgn < 2; ++sgn)
+#pragma unroll
+                for (int f2 = 0; f2 < 2; ++f2)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv) phi[0][sgn][f2][vv] *= gw;
+        }
 
         bf16x8 phb[2][2][2];  // [sgn][ft][s2]
 #pragma unroll
@@ -1562,8 +1574,8 @@ hipError_t launch_la_group_scan(const Dims& D, const LinBufs& L, int cap_chunk, 
 
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const void* wsplit, const void* phik, const uint8_t* route,
-                              const void* ksel, const void* vsel, const LinBufs& L, void* out,
-                              hipStream_t s) {
+                              const void* ksel, const void* vsel, const LinBufs& L,
+                              const float* gate, void* out, hipStream_t s) {
     const int n = D.Hkv * (kD / 2) * kD;
     const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
     const bf16* wql = wqh + n;
@@ -1575,7 +1587,7 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       L, reinterpret_cast<bf16*>(out), D)
+                       L, gate, reinterpret_cast<bf16*>(out), D)
     if (HB == 4) STILL_MAIN(4);
     else if (HB == 2) STILL_MAIN(2);
     else STILL_MAIN(1);

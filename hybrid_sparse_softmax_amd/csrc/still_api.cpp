@@ -16,6 +16,7 @@ namespace still {
 // validation
 // ---------------------------------------------------------------------------
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 static int check_shape(const still_shape* sh, bool decode) {
     if (!sh) return STILL_ERR_INVALID_ARG;
@@ -219,7 +220,7 @@ static int fwd_launches(const Dims& D, const still_shape* sh, bool with_cache) {
 }
 
 static int fwd(const still_shape* sh, const void* q, const void* k, const void* v,
-               const float* wq, const float* wk, void* out, float* scores_opt,
+               const float* wq, const float* wk, const float* gate, void* out, float* scores_opt,
                int32_t* sel_idx_opt, still_cache* cache, void* ws, size_t ws_bytes,
                hipStream_t s, Timeline& tl) {
     int st = check_shape(sh, false);
@@ -228,7 +229,7 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
     if (D.B == 0 || D.N == 0) return STILL_OK;  // nothing to compute; pointers unused
     if (!q || !k || !v || !wq || !wk || !out) return STILL_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(wq) ||
-        !aligned16(wk))
+        !aligned16(wk) || !aligned4(gate))
         return STILL_ERR_INVALID_ARG;
     if (cache) {
         const int64_t need = D.lam * ceil_div((int64_t)D.N - D.W, D.C);
@@ -256,7 +257,7 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
                      launch_la_group_scan(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
                                           cache ? cache->lin_z : nullptr, s));
         STILL_LAUNCH(tl, s, "hybrid_main",
-                     launch_hybrid_main(D, q, k, v, f.wsplit, f.phik, f.route, f.ksel, f.vsel, f.lin, out, s));
+                     launch_hybrid_main(D, q, k, v, f.wsplit, f.phik, f.route, f.ksel, f.vsel, f.lin, gate, out, s));
         if (cache)
             STILL_LAUNCH(tl, s, "handoff",
                          launch_handoff(D, k, v, wk, scores, sel, f.route, cap_chunk, view_of(cache), s));
@@ -267,8 +268,8 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
     float* scores = scores_opt ? scores_opt : f.scores;
     int32_t* sel = sel_idx_opt ? sel_idx_opt : f.sel;
 
-    STILL_LAUNCH(tl, s, "phi_q", launch_phi(D, q, D.Hq, D.G, wq, f.phiq, s));
-    STILL_LAUNCH(tl, s, "phi_k", launch_phi(D, k, D.Hkv, 1, wk, f.phik, s));
+    STILL_LAUNCH(tl, s, "phi_q", launch_phi(D, q, D.Hq, D.G, wq, gate, f.phiq, s));
+    STILL_LAUNCH(tl, s, "phi_k", launch_phi(D, k, D.Hkv, 1, wk, nullptr, f.phik, s));
     if (D.W > 0) STILL_LAUNCH(tl, s, "head_scores", launch_head_scores(D, q, k, f.hs, s));
     STILL_LAUNCH(tl, s, "select", launch_select(D, f.hs, scores, sel, f.route, k, s));
     STILL_LAUNCH(tl, s, "la_chunk", launch_la_chunks(D, f.phik, v, f.route, f.lin, s));
@@ -340,7 +341,8 @@ static int current_scratch(void** out) {
 // use_scratch: ws is ignored; after every check (with ws_bytes =
 // STILL_DECODE_SCRATCH_BYTES) the current GPU's scratch array serves instead.
 static int decode(const still_shape* sh, const void* q, const void* k, const void* v,
-                  const float* wq, const float* wk, still_cache* cache, void* out, void* ws,
+                  const float* wq, const float* wk, const float* gate, still_cache* cache,
+                  void* out, void* ws,
                   size_t ws_bytes, hipStream_t s, Timeline& tl, int64_t* pos_dev = nullptr,
                   int64_t max_pos = 0, bool use_scratch = false) {
     if (use_scratch) ws_bytes = STILL_DECODE_SCRATCH_BYTES;
@@ -358,7 +360,7 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
     }
     if (!q || !k || !v || !wq || !wk || !out) return STILL_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(wq) ||
-        !aligned16(wk))
+        !aligned16(wk) || !aligned4(gate))
         return STILL_ERR_INVALID_ARG;
     if (ragged && (reinterpret_cast<uintptr_t>(pos_dev) & 7u)) return STILL_ERR_INVALID_ARG;
     const int64_t t = ragged ? max_pos : cache->pos;
@@ -379,8 +381,8 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
         cvw.pos_dev = pos_dev;
         const int nsplit = fast_decode_splits(cache->sel_cap);
         float* fw = static_cast<float*>(wsa);
-        STILL_LAUNCH(tl, s, "dec_stream", launch_fast_decode(D, q, k, v, wq, wk, cvw, fw, nsplit, out, 0, s));
-        STILL_LAUNCH(tl, s, "dec_combine", launch_fast_decode(D, q, k, v, wq, wk, cvw, fw, nsplit, out, 1, s));
+        STILL_LAUNCH(tl, s, "dec_stream", launch_fast_decode(D, q, k, v, wq, wk, gate, cvw, fw, nsplit, out, 0, s));
+        STILL_LAUNCH(tl, s, "dec_combine", launch_fast_decode(D, q, k, v, wq, wk, gate, cvw, fw, nsplit, out, 1, s));
         STILL_TRY(tl.end(s));
         if (!ragged) cache->pos = t + 1;
         return STILL_OK;
@@ -389,7 +391,7 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
     DecodeWork w = carve_decode(D, cache->sel_cap, cv);
     CacheView cvw = view_of(cache);
     cvw.pos_dev = pos_dev;
-    STILL_LAUNCH(tl, s, "decode_prep", launch_decode_prep(D, q, k, v, wq, wk, cvw, w, s));
+    STILL_LAUNCH(tl, s, "decode_prep", launch_decode_prep(D, q, k, v, wq, wk, gate, cvw, w, s));
     STILL_LAUNCH(tl, s, "decode_sel", launch_decode_sel(D, q, cvw, w, s));
     STILL_LAUNCH(tl, s, "decode_combine", launch_decode_combine(D, w, out, pos_dev, s));
     STILL_TRY(tl.end(s));
@@ -444,9 +446,9 @@ static hipError_t mark_launch(void* ctx, const char* name) {
 }
 
 static int bwd(const still_shape* sh, const void* q, const void* k, const void* v,
-               const float* wq, const float* wk, const int32_t* sel_idx, const void* dout,
-               float* dq, float* dk, float* dv, float* dwq, float* dwk, void* ws,
-               size_t ws_bytes, hipStream_t s, Timeline& tl) {
+               const float* wq, const float* wk, const float* gate, const int32_t* sel_idx,
+               const void* dout, float* dq, float* dk, float* dv, float* dwq, float* dwk,
+               float* dgate, void* ws, size_t ws_bytes, hipStream_t s, Timeline& tl) {
     int st = check_shape(sh, false);
     if (st) return st;
     const Dims D = make_dims(sh, sh->seqlen);
@@ -461,6 +463,7 @@ static int bwd(const still_shape* sh, const void* q, const void* k, const void* 
     const void* ptrs[] = {q, k, v, wq, wk, dout, dq, dk, dv, dwq, dwk};
     for (const void* p : ptrs)
         if (!aligned16(p)) return STILL_ERR_INVALID_ARG;
+    if (!aligned4(gate) || !aligned4(dgate)) return STILL_ERR_INVALID_ARG;
     if (D.lam > 0 && D.n_full > 0 && (!sel_idx || (reinterpret_cast<uintptr_t>(sel_idx) & 3u)))
         return STILL_ERR_INVALID_ARG;
     if (!ws || ws_bytes < bwd_bytes(D)) return STILL_ERR_WORKSPACE;
@@ -481,6 +484,8 @@ static int bwd(const still_shape* sh, const void* q, const void* k, const void* 
     a.dv = dv;
     a.dwq = dwq;
     a.dwk = dwk;
+    a.gate = gate;
+    a.dgate = gate ? dgate : nullptr;
     MarkCtx mc{&tl, s};
     STILL_TRY(launch_bwd(D, a, w, s, BwdMark{mark_launch, &mc}));
     STILL_TRY(tl.end(s));
@@ -542,17 +547,19 @@ int still_fwd_workspace_size(const still_shape* shape, size_t* bytes) {
 }
 
 int still_hybrid_attn_fwd(const still_shape* shape, const void* q, const void* k, const void* v,
-                          const float* wphi_q, const float* wphi_k, void* out, float* scores_opt,
-                          int32_t* sel_idx_opt, still_cache* cache_opt, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+                          const float* wphi_q, const float* wphi_k, const float* gate_opt,
+                          void* out, float* scores_opt, int32_t* sel_idx_opt,
+                          still_cache* cache_opt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
     still::Timeline tl;
-    return still::fwd(shape, q, k, v, wphi_q, wphi_k, out, scores_opt, sel_idx_opt, cache_opt,
-                      workspace, workspace_bytes, stream, tl);
+    return still::fwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, out, scores_opt, sel_idx_opt,
+                      cache_opt, workspace, workspace_bytes, stream, tl);
 }
 
 int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
-                                void* out, float* scores_opt, int32_t* sel_idx_opt,
+                                const float* gate_opt, void* out, float* scores_opt,
+                                int32_t* sel_idx_opt,
                                 still_cache* cache_opt, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream, hipEvent_t* events, int32_t max_events,
                                 int32_t* n_launches, const char** kernel_names_opt) {
@@ -561,8 +568,8 @@ int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const v
     tl.ev = events;
     tl.max_ev = max_events;
     tl.names = kernel_names_opt;
-    const int st = still::fwd(shape, q, k, v, wphi_q, wphi_k, out, scores_opt, sel_idx_opt,
-                              cache_opt, workspace, workspace_bytes, stream, tl);
+    const int st = still::fwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, out, scores_opt,
+                              sel_idx_opt, cache_opt, workspace, workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
 }
@@ -577,16 +584,17 @@ int still_decode_workspace_size(const still_shape* shape, int32_t sel_cap, size_
 
 int still_hybrid_attn_decode_step(const still_shape* shape, const void* q, const void* k,
                                   const void* v, const float* wphi_q, const float* wphi_k,
-                                  still_cache* cache, void* out, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+                                  const float* gate_opt, still_cache* cache, void* out,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     still::Timeline tl;
-    return still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, workspace, workspace_bytes,
-                         stream, tl);
+    return still::decode(shape, q, k, v, wphi_q, wphi_k, gate_opt, cache, out, workspace,
+                         workspace_bytes, stream, tl);
 }
 
 int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q, const void* k,
                                         const void* v, const float* wphi_q,
-                                        const float* wphi_k, still_cache* cache, void* out,
+                                        const float* wphi_k, const float* gate_opt,
+                                        still_cache* cache, void* out,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream, hipEvent_t* events,
                                         int32_t max_events, int32_t* n_launches,
@@ -596,30 +604,31 @@ int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q,
     tl.ev = events;
     tl.max_ev = max_events;
     tl.names = kernel_names_opt;
-    const int st = still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, workspace,
-                                 workspace_bytes, stream, tl);
+    const int st = still::decode(shape, q, k, v, wphi_q, wphi_k, gate_opt, cache, out,
+                                 workspace, workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
 }
 
 int still_hybrid_attn_decode_step_noalloc(const still_shape* shape, const void* q, const void* k,
                                           const void* v, const float* wphi_q,
-                                          const float* wphi_k, still_cache* cache, void* out,
-                                          hipStream_t stream) {
+                                          const float* wphi_k, const float* gate_opt,
+                                          still_cache* cache, void* out, hipStream_t stream) {
     still::Timeline tl;
-    return still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, nullptr, 0, stream, tl,
-                         nullptr, 0, true);
+    return still::decode(shape, q, k, v, wphi_q, wphi_k, gate_opt, cache, out, nullptr, 0, stream,
+                         tl, nullptr, 0, true);
 }
 
 int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q, const void* k,
                                          const void* v, const float* wphi_q, const float* wphi_k,
-                                         still_cache* cache, int64_t* pos_dev, int64_t max_pos,
-                                         void* out, void* workspace, size_t workspace_bytes,
+                                         const float* gate_opt, still_cache* cache,
+                                         int64_t* pos_dev, int64_t max_pos, void* out,
+                                         void* workspace, size_t workspace_bytes,
                                          hipStream_t stream) {
     if (!pos_dev) return STILL_ERR_INVALID_ARG;
     still::Timeline tl;
-    return still::decode(shape, q, k, v, wphi_q, wphi_k, cache, out, workspace, workspace_bytes,
-                         stream, tl, pos_dev, max_pos);
+    return still::decode(shape, q, k, v, wphi_q, wphi_k, gate_opt, cache, out, workspace,
+                         workspace_bytes, stream, tl, pos_dev, max_pos);
 }
 
 int still_bwd_workspace_size(const still_shape* shape, size_t* bytes) {
@@ -631,19 +640,20 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes) {
 }
 
 int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k, const void* v,
-                          const float* wphi_q, const float* wphi_k, const int32_t* sel_idx,
-                          const void* dout, float* dq, float* dk, float* dv, float* dwphi_q,
-                          float* dwphi_k, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+                          const float* wphi_q, const float* wphi_k, const float* gate_opt,
+                          const int32_t* sel_idx, const void* dout, float* dq, float* dk,
+                          float* dv, float* dwphi_q, float* dwphi_k, float* dgate_opt,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     still::Timeline tl;
-    return still::bwd(shape, q, k, v, wphi_q, wphi_k, sel_idx, dout, dq, dk, dv, dwphi_q, dwphi_k,
-                      workspace, workspace_bytes, stream, tl);
+    return still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, dq, dk, dv, dwphi_q,
+                      dwphi_k, dgate_opt, workspace, workspace_bytes, stream, tl);
 }
 
 int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
-                                const int32_t* sel_idx, const void* dout, float* dq, float* dk,
-                                float* dv, float* dwphi_q, float* dwphi_k, void* workspace,
+                                const float* gate_opt, const int32_t* sel_idx, const void* dout,
+                                float* dq, float* dk, float* dv, float* dwphi_q, float* dwphi_k,
+                                float* dgate_opt, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                                 int32_t max_events, int32_t* n_launches,
                                 const char** kernel_names_opt) {
@@ -652,8 +662,8 @@ int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const v
     tl.ev = events;
     tl.max_ev = max_events;
     tl.names = kernel_names_opt;
-    const int st = still::bwd(shape, q, k, v, wphi_q, wphi_k, sel_idx, dout, dq, dk, dv, dwphi_q,
-                              dwphi_k, workspace, workspace_bytes, stream, tl);
+    const int st = still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, dq, dk, dv,
+                              dwphi_q, dwphi_k, dgate_opt, workspace, workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
 }

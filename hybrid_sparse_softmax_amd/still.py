@@ -77,25 +77,25 @@ def lib() -> ct.CDLL:
         L.still_fwd_workspace_size.restype = ct.c_int
         L.still_fwd_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
         L.still_hybrid_attn_fwd.restype = ct.c_int
-        L.still_hybrid_attn_fwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp,
+        L.still_hybrid_attn_fwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             ct.POINTER(CacheStruct), vp, sz, vp]
         L.still_decode_workspace_size.restype = ct.c_int
         L.still_decode_workspace_size.argtypes = [ct.POINTER(Shape), ct.c_int32, ct.POINTER(sz)]
         L.still_hybrid_attn_decode_step.restype = ct.c_int
-        L.still_hybrid_attn_decode_step.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
+        L.still_hybrid_attn_decode_step.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp,
                                                     ct.POINTER(CacheStruct), vp, vp, sz, vp]
         L.still_hybrid_attn_decode_step_noalloc.restype = ct.c_int
         L.still_hybrid_attn_decode_step_noalloc.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
-                                                            ct.POINTER(CacheStruct), vp, vp]
+                                                            vp, ct.POINTER(CacheStruct), vp, vp]
         L.still_hybrid_attn_decode_step_ragged.restype = ct.c_int
         L.still_hybrid_attn_decode_step_ragged.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp,
-                                                           ct.POINTER(CacheStruct), vp, ct.c_int64,
-                                                           vp, vp, sz, vp]
+                                                           vp, ct.POINTER(CacheStruct), vp,
+                                                           ct.c_int64, vp, vp, sz, vp]
         L.still_bwd_workspace_size.restype = ct.c_int
         L.still_bwd_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
         L.still_hybrid_attn_bwd.restype = ct.c_int
         L.still_hybrid_attn_bwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                            vp, vp, vp, vp, sz, vp]
+                                            vp, vp, vp, vp, vp, vp, sz, vp]
         L.still_future_kv_utility_workspace_size.restype = ct.c_int
         L.still_future_kv_utility_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
         L.still_future_kv_utility.restype = ct.c_int
@@ -239,9 +239,10 @@ class DecodeCache:
 def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale=0.0,
         return_scores=False, return_sel=False, cache: DecodeCache | None = None,
         out=None, workspace=None, general=False, timer: LaunchTimer | None = None,
-        route="saliency") -> dict:
+        route="saliency", gate=None) -> dict:
     """still_hybrid_attn_fwd.  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or f32),
-    wphi_* [Hkv, d'/2, d] f32.  Returns dict(out, scores?, sel_idx?)."""
+    wphi_* [Hkv, d'/2, d] f32, gate: optional gate logits [B,N,Hq] f32.
+    Returns dict(out, scores?, sel_idx?)."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
@@ -252,6 +253,8 @@ def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale
     _expect(v, "v", q.dtype, (B, N, Hkv, d))
     _expect(wphi_q, "wphi_q", torch.float32, (Hkv, wphi_q.shape[1], d))
     _expect(wphi_k, "wphi_k", torch.float32, (Hkv, wphi_q.shape[1], d))
+    if gate is not None:
+        _expect(gate, "gate", torch.float32, (B, N, Hq))
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -262,8 +265,8 @@ def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     cs = ct.byref(cache.struct()) if cache is not None else None
-    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(out),
-            _ptr(scores), _ptr(sel), cs, _ptr(workspace), workspace.numel(), _stream()]
+    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(gate),
+            _ptr(out), _ptr(scores), _ptr(sel), cs, _ptr(workspace), workspace.numel(), _stream()]
     if timer is None:
         _check(lib().still_hybrid_attn_fwd(*args), "still_hybrid_attn_fwd")
     else:
@@ -278,9 +281,10 @@ def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale
 
 def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softmax_scale=0.0,
                 out=None, workspace=None, general=False, timer: LaunchTimer | None = None,
-                route="saliency"):
+                route="saliency", gate=None):
     """still_hybrid_attn_decode_step at position cache.pos; q [B,1,Hq,d],
-    k/v [B,1,Hkv,d].  Advances cache.pos.  Returns out [B,1,Hq,d]."""
+    k/v [B,1,Hkv,d], gate: optional gate logits [B,1,Hq] f32.  Advances
+    cache.pos.  Returns out [B,1,Hq,d]."""
     B, one, Hq, d = q.shape
     Hkv = k.shape[2]
     sh = make_shape(batch=B, seqlen=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
@@ -296,8 +300,9 @@ def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softma
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     cs = cache.struct()
-    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), ct.byref(cs),
-            _ptr(out), _ptr(workspace), workspace.numel(), _stream()]
+    _gate_check(gate, B, Hq)
+    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(gate),
+            ct.byref(cs), _ptr(out), _ptr(workspace), workspace.numel(), _stream()]
     if timer is None:
         _check(lib().still_hybrid_attn_decode_step(*args), "still_hybrid_attn_decode_step")
     else:
@@ -310,8 +315,13 @@ def decode_step(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6, softma
 DECODE_SCRATCH_BYTES = 32 << 20  # STILL_DECODE_SCRATCH_BYTES
 
 
+def _gate_check(gate, B, Hq):
+    if gate is not None:
+        _expect(gate, "gate", torch.float32, (B, 1, Hq))
+
+
 def decode_step_noalloc(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6,
-                        softmax_scale=0.0, out=None, general=False, route="saliency"):
+                        softmax_scale=0.0, out=None, general=False, route="saliency", gate=None):
     """still_hybrid_attn_decode_step_noalloc: the decode step at cache.pos
     with the library's own per-GPU scratch instead of a workspace (nothing is
     allocated when ``out`` is given).  Advances cache.pos.  Returns out
@@ -327,17 +337,18 @@ def decode_step_noalloc(q, k, v, wphi_q, wphi_k, cache: DecodeCache, *, eps=1e-6
     _expect(v, "v", q.dtype, (B, 1, Hkv, d))
     if out is None:
         out = torch.empty_like(q)
+    _gate_check(gate, B, Hq)
     cs = cache.struct()
     _check(lib().still_hybrid_attn_decode_step_noalloc(
-        ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), ct.byref(cs), _ptr(out),
-        _stream()), "still_hybrid_attn_decode_step_noalloc")
+        ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(gate), ct.byref(cs),
+        _ptr(out), _stream()), "still_hybrid_attn_decode_step_noalloc")
     cache.pos = int(cs.pos)
     return out
 
 
 def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.Tensor, max_pos: int,
                        *, eps=1e-6, softmax_scale=0.0, out=None, workspace=None, general=False,
-                       route="saliency"):
+                       route="saliency", gate=None):
     """still_hybrid_attn_decode_step_ragged: one step with a position per
     sequence.  pos is an int64 device tensor [B] (advanced by one on the
     stream), max_pos a host bound on its entries; cache.pos is not used.
@@ -357,20 +368,23 @@ def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.T
     nbytes = decode_workspace_size(sh, cache.sel_cap)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _gate_check(gate, B, Hq)
     cs = cache.struct()
     _check(lib().still_hybrid_attn_decode_step_ragged(
-        ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), ct.byref(cs), _ptr(pos),
+        ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(gate), ct.byref(cs),
+        _ptr(pos),
         int(max_pos), _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
         "still_hybrid_attn_decode_step_ragged")
     return out
 
 
 def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6,
-        softmax_scale=0.0, workspace=None, timer: LaunchTimer | None = None) -> dict:
+        softmax_scale=0.0, workspace=None, timer: LaunchTimer | None = None, gate=None) -> dict:
     """still_hybrid_attn_bwd: gradients of sum(dout * out) for the forward
     with the same arguments, under the routing sel_idx [B, Hkv, N/C, lambda]
     (the forward's sel_idx output; None when there is nothing selected).
-    Returns dict(dq, dk, dv, dwphi_q, dwphi_k), all fp32."""
+    Returns dict(dq, dk, dv, dwphi_q, dwphi_k), all fp32, plus dgate
+    [B, N, Hq] when gate logits [B, N, Hq] are given."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
@@ -389,12 +403,16 @@ def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6
     res = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32),
            "dv": torch.empty(v.shape, **f32), "dwphi_q": torch.empty(wphi_q.shape, **f32),
            "dwphi_k": torch.empty(wphi_k.shape, **f32)}
+    if gate is not None:
+        _expect(gate, "gate", torch.float32, (B, N, Hq))
+        res["dgate"] = torch.empty(gate.shape, **f32)
     nbytes = bwd_workspace_size(sh)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(sel_idx),
-            _ptr(dout), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dwphi_q"]),
-            _ptr(res["dwphi_k"]), _ptr(workspace), workspace.numel(), _stream()]
+    args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(gate),
+            _ptr(sel_idx), _ptr(dout), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]),
+            _ptr(res["dwphi_q"]), _ptr(res["dwphi_k"]), _ptr(res.get("dgate")), _ptr(workspace),
+            workspace.numel(), _stream()]
     if timer is None:
         _check(lib().still_hybrid_attn_bwd(*args), "still_hybrid_attn_bwd")
     else:

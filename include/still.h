@@ -28,8 +28,11 @@
  *     therefore complete in time only when window >= chunk (Appendix A.7.5:
  *     the window spans one chunk);
  *   - phi(x) = [softmax(z); softmax(-z)], z = ||x|| P x / ||P x||;
- *   - out = (sum_SA e^{tau q.k} v + sum_LA phi_q.phi_k v) /
- *           (sum_SA e^{tau q.k}   + sum_LA phi_q.phi_k).
+ *   - the gate W_g (list view Table 9; full text Sec. 4.1, App. A.6.1) is a
+ *     weight gamma = sigmoid(g) per token and query head on the linear
+ *     branch, whose logits g = x W_g the caller computes like q, k, v;
+ *   - out = (sum_SA e^{tau q.k} v + gamma sum_LA phi_q.phi_k v) /
+ *           (sum_SA e^{tau q.k}   + gamma sum_LA phi_q.phi_k).
  *
  * Conventions for every call
  *   - Tensors are dense row-major, innermost dimension last, on the current
@@ -46,6 +49,10 @@
  *     device properties, so calls on distinct buffers are thread-safe.
  *   - Every entry point validates all arguments on the host before
  *     launching anything, returns a still_status, and never aborts.
+ *   - gate_opt (every compute call): gate logits g [B, N, Hq] fp32 (N = 1 for
+ *     a decode step), 4-byte aligned, read only; NULL means no gate
+ *     (gamma = 1, the operator without the component).  gamma = 0 leaves
+ *     window + selected softmax attention.
  */
 #ifndef STILL_H
 #define STILL_H
@@ -58,7 +65,7 @@
 extern "C" {
 #endif
 
-#define STILL_ABI_VERSION 3
+#define STILL_ABI_VERSION 4
 
 typedef enum {
     STILL_OK = 0,
@@ -179,7 +186,8 @@ int still_fwd_workspace_size(const still_shape* shape, size_t* bytes);
  * N == 0 or B == 0 is a no-op returning STILL_OK once the shape is valid (no
  * pointer is inspected). */
 int still_hybrid_attn_fwd(const still_shape* shape, const void* q, const void* k, const void* v,
-                          const float* wphi_q, const float* wphi_k, void* out, float* scores_opt,
+                          const float* wphi_q, const float* wphi_k, const float* gate_opt,
+                          void* out, float* scores_opt,
                           int32_t* sel_idx_opt, still_cache* cache_opt, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
@@ -205,7 +213,7 @@ int still_decode_workspace_size(const still_shape* shape, int32_t sel_cap, size_
  * incremented. */
 int still_hybrid_attn_decode_step(const still_shape* shape, const void* q, const void* k,
                                   const void* v, const float* wphi_q, const float* wphi_k,
-                                  still_cache* cache, void* out, void* workspace,
+                                  const float* gate_opt, still_cache* cache, void* out, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /* Serving form of the decode step: the same step (1-5 above) with one
@@ -223,7 +231,8 @@ int still_hybrid_attn_decode_step(const still_shape* shape, const void* q, const
  * serving setting of Sec. 4.6: every request decodes at its own length.) */
 int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q, const void* k,
                                          const void* v, const float* wphi_q, const float* wphi_k,
-                                         still_cache* cache, int64_t* pos_dev, int64_t max_pos,
+                                         const float* gate_opt, still_cache* cache, int64_t* pos_dev,
+                                         int64_t max_pos,
                                          void* out, void* workspace, size_t workspace_bytes,
                                          hipStream_t stream);
 
@@ -251,8 +260,8 @@ int still_hybrid_attn_decode_step_ragged(const still_shape* shape, const void* q
  * that GPU current); a failed lookup returns STILL_ERR_HIP. */
 int still_hybrid_attn_decode_step_noalloc(const still_shape* shape, const void* q, const void* k,
                                           const void* v, const float* wphi_q,
-                                          const float* wphi_k, still_cache* cache, void* out,
-                                          hipStream_t stream);
+                                          const float* wphi_k, const float* gate_opt,
+                                          still_cache* cache, void* out, hipStream_t stream);
 
 /* Bytes of device workspace still_hybrid_attn_bwd needs for `shape`. */
 int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
@@ -275,6 +284,9 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
  *   dq        [B, N, Hq, d] fp32, written
  *   dk, dv    [B, N, Hkv, d] fp32, written
  *   dwphi_q, dwphi_k  [Hkv, d'/2, d] fp32, written
+ *   dgate_opt [B, N, Hq] fp32: the gradient w.r.t. the gate logits, written
+ *             when gate_opt is given and this is not NULL; ignored without
+ *             a gate
  *   workspace >= still_bwd_workspace_size bytes of device memory
  * Computed by the general kernels for every supported shape; the shape's
  * routing-criterion and kernel flags are accepted and do not matter.  N == 0
@@ -282,10 +294,10 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
  * else.  Errors as for the forward; a missing sel_idx where it is needed is
  * STILL_ERR_INVALID_ARG. */
 int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k, const void* v,
-                          const float* wphi_q, const float* wphi_k, const int32_t* sel_idx,
-                          const void* dout, float* dq, float* dk, float* dv, float* dwphi_q,
-                          float* dwphi_k, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream);
+                          const float* wphi_q, const float* wphi_k, const float* gate_opt,
+                          const int32_t* sel_idx, const void* dout, float* dq, float* dk,
+                          float* dv, float* dwphi_q, float* dwphi_k, float* dgate_opt,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace still_future_kv_utility needs for `shape`. */
 int still_future_kv_utility_workspace_size(const still_shape* shape, size_t* bytes);
@@ -318,21 +330,23 @@ int still_future_kv_utility(const still_shape* shape, const void* q, const void*
 #define STILL_MAX_LAUNCHES 16
 int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
-                                void* out, float* scores_opt, int32_t* sel_idx_opt,
+                                const float* gate_opt, void* out, float* scores_opt, int32_t* sel_idx_opt,
                                 still_cache* cache_opt, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream, hipEvent_t* events, int32_t max_events,
                                 int32_t* n_launches, const char** kernel_names_opt);
 int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q, const void* k,
                                         const void* v, const float* wphi_q,
-                                        const float* wphi_k, still_cache* cache, void* out,
+                                        const float* wphi_k, const float* gate_opt,
+                                        still_cache* cache, void* out,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream, hipEvent_t* events,
                                         int32_t max_events, int32_t* n_launches,
                                         const char** kernel_names_opt);
 int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
-                                const int32_t* sel_idx, const void* dout, float* dq, float* dk,
-                                float* dv, float* dwphi_q, float* dwphi_k, void* workspace,
+                                const float* gate_opt, const int32_t* sel_idx, const void* dout,
+                                float* dq, float* dk, float* dv, float* dwphi_q, float* dwphi_k,
+                                float* dgate_opt, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                                 int32_t max_events, int32_t* n_launches,
                                 const char** kernel_names_opt);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert S.abi_version() == 3
+    assert S.abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5):
         assert S.status_str(code) and S.status_str(code) != "unknown status"
     assert S.status_str(7) == "unknown status"
@@ -52,9 +52,9 @@ def shape(**kw):
     return S.make_shape(**base)
 
 
-def fwd_status(sh, ws_bytes=1 << 40, cache=None, ptr=FAKE, ws=FAKE):
-    return S.lib().still_hybrid_attn_fwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, ptr, None, None,
-                                         ct.byref(cache) if cache is not None else None, ws,
+def fwd_status(sh, ws_bytes=1 << 40, cache=None, ptr=FAKE, ws=FAKE, gate=None):
+    return S.lib().still_hybrid_attn_fwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, gate, ptr, None,
+                                         None, ct.byref(cache) if cache is not None else None, ws,
                                          ws_bytes, None)
 
 
@@ -137,8 +137,8 @@ def test_handoff_capacity_and_position_checks():
     assert fwd_status(sh, cache=fake_cache(need, 1024), ws_bytes=16) == S.STILL_ERR_WORKSPACE
 
 
-def decode_status(sh, cache, ws_bytes=1 << 40, ptr=FAKE):
-    return S.lib().still_hybrid_attn_decode_step(ct.byref(sh), ptr, ptr, ptr, ptr, ptr,
+def decode_status(sh, cache, ws_bytes=1 << 40, ptr=FAKE, gate=None):
+    return S.lib().still_hybrid_attn_decode_step(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, gate,
                                                  ct.byref(cache), ptr, FAKE, ws_bytes, None)
 
 
@@ -162,7 +162,7 @@ def test_decode_empty_batch_advances_position():
 
 
 def ragged_status(sh, cache, pos_dev, max_pos, ws_bytes=1 << 40, ptr=FAKE):
-    return S.lib().still_hybrid_attn_decode_step_ragged(ct.byref(sh), ptr, ptr, ptr, ptr, ptr,
+    return S.lib().still_hybrid_attn_decode_step_ragged(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, None,
                                                         ct.byref(cache), pos_dev, max_pos, ptr,
                                                         FAKE, ws_bytes, None)
 
@@ -183,9 +183,9 @@ def test_ragged_decode_checks():
     assert c.pos == 7
 
 
-def bwd_status(sh, sel=FAKE, ws_bytes=1 << 40, ptr=FAKE, ws=FAKE, dw=FAKE):
-    return S.lib().still_hybrid_attn_bwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, sel, ptr, ptr, ptr,
-                                         ptr, dw, dw, ws, ws_bytes, None)
+def bwd_status(sh, sel=FAKE, ws_bytes=1 << 40, ptr=FAKE, ws=FAKE, dw=FAKE, gate=None, dgate=None):
+    return S.lib().still_hybrid_attn_bwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, gate, sel, ptr, ptr,
+                                         ptr, ptr, dw, dw, dgate, ws, ws_bytes, None)
 
 
 def test_bwd_checks():
@@ -209,8 +209,8 @@ def test_bwd_checks():
     n = ct.c_int32(0)
     evs = (ct.c_void_p * 4)()
     # 16 launches need 17 events; too few is rejected before anything runs
-    assert timed(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                 FAKE, 1 << 40, None, evs, 4, ct.byref(n), None) == S.STILL_ERR_INVALID_ARG
+    assert timed(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, None, FAKE, 1 << 40, None, evs, 4, ct.byref(n), None) == S.STILL_ERR_INVALID_ARG
 
 
 def test_bwd_empty_problem_without_projection_gradients_is_noop():
@@ -238,8 +238,8 @@ def test_decode_rejects_misaligned_projections():
     c = fake_cache(need, 16384)
     L = S.lib()
     for wq, wk in ((MISALIGNED, FAKE), (FAKE, MISALIGNED)):
-        assert L.still_hybrid_attn_decode_step(ct.byref(sh), FAKE, FAKE, FAKE, wq, wk, ct.byref(c), FAKE,
-                                               FAKE, 1 << 40, None) == S.STILL_ERR_INVALID_ARG
+        assert L.still_hybrid_attn_decode_step(ct.byref(sh), FAKE, FAKE, FAKE, wq, wk, None, ct.byref(c),
+                                               FAKE, FAKE, 1 << 40, None) == S.STILL_ERR_INVALID_ARG
 
 
 def test_noalloc_decode_checks_before_touching_the_gpu():
@@ -256,15 +256,30 @@ def test_noalloc_decode_checks_before_touching_the_gpu():
         assert L.still_decode_workspace_size(ct.byref(sh), cap, ct.byref(n)) == S.STILL_OK
         assert (n.value <= S.DECODE_SCRATCH_BYTES) == fits
     cache = S.CacheStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, 4096)
-    st = L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE,
+    st = L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                                  ct.byref(cache), FAKE, None)
     assert st == S.STILL_ERR_WORKSPACE
     assert cache.pos == 4096
     # the plain step's argument checks come first
-    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), None, FAKE, FAKE, FAKE, FAKE,
+    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), None, FAKE, FAKE, FAKE, FAKE, None,
                                                    ct.byref(cache), FAKE, None) == S.STILL_ERR_INVALID_ARG
-    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                                    None, FAKE, None) == S.STILL_ERR_INVALID_ARG
     cache.pos = 1 << 40   # capacity: lambda * ceil((t + 1 - W) / C) > cap
-    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert L.still_hybrid_attn_decode_step_noalloc(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                                    ct.byref(cache), FAKE, None) == S.STILL_ERR_CAPACITY
+
+
+def test_gate_pointers_are_checked():
+    """Gate logits (and their gradient) must be 4-byte aligned; NULL is no gate."""
+    sh = shape()
+    odd = ct.c_void_p(0x1002)
+    assert fwd_status(sh, ws_bytes=16, gate=FAKE) == S.STILL_ERR_WORKSPACE   # accepted, then too small
+    assert fwd_status(sh, gate=odd) == S.STILL_ERR_INVALID_ARG
+    sd = shape(seqlen=1, topk=32)
+    need = 32 * ((16384 + 1 - 64 + 63) // 64)
+    assert decode_status(sd, fake_cache(need, 16384), gate=odd) == S.STILL_ERR_INVALID_ARG
+    assert decode_status(sd, fake_cache(need, 16384), ws_bytes=16, gate=FAKE) == S.STILL_ERR_WORKSPACE
+    assert bwd_status(sh, gate=odd) == S.STILL_ERR_INVALID_ARG
+    assert bwd_status(sh, gate=FAKE, dgate=odd) == S.STILL_ERR_INVALID_ARG
+    assert bwd_status(sh, gate=FAKE, dgate=FAKE, ws_bytes=16) == S.STILL_ERR_WORKSPACE

@@ -110,6 +110,13 @@ def make_grad_out(cfg: dict, seed: int) -> np.ndarray:
                                dtype=np.float32)
 
 
+def make_gate(cfg: dict, seed: int) -> np.ndarray:
+    """Gate logits g [B, N, Hq] ~ N(0, 2^2), float32, from their own stream
+    (seed + 2000003): gate weights sigmoid(g) spread over (0, 1)."""
+    rng = np.random.default_rng(seed + 2000003)
+    return (2.0 * rng.standard_normal((cfg["batch"], cfg["seqlen"], cfg["n_q_heads"]))).astype(np.float32)
+
+
 def make_decode_stream(cfg: dict, seed: int, b: int, g: int) -> dict:
     """Cache contents of one (sequence, KV head) at position ``pos``:
     ring K/V of the last W tokens ~ N(0,1); route flags of the last complete
