@@ -237,8 +237,11 @@ def bench_decode(still, torch, steps, warmup):
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(dom, name), "kernel": dom,
             "avg_ms": round(kern[dom], 4), "algorithmic_bytes_per_launch": dom_bytes}
     step_gbs = by["total"] / (ms * 1e-3) / 1e9
+    t_first = cfg["pos"] + warmup
+    chunk_ends = sum(1 for t in range(t_first, t_first + steps) if t % cfg["chunk"] == cfg["chunk"] - 1)
     return {"metric": "decode tokens/s (batch 64 at position 16384)", "value": round(B / (ms * 1e-3), 1),
             "unit": "tokens/s", "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+            "timed_positions": [t_first, t_first + steps - 1], "chunk_end_steps_timed": chunk_ends,
             "config": {"workload": "decode_b64_16k: batch 64, one token per sequence at position "
                        "16384, 32 q / 8 KV heads, d 128, window 64, chunk 64, top-32, "
                        "8160 selected rows per (sequence, KV head), fp32 128x128 state",
@@ -298,8 +301,11 @@ def bench_decode_ragged(still, torch, steps, warmup):
     by = decode_bytes(cfg, mid)
     gbs = by["total"] / (ms * 1e-3) / 1e9
     log(f"[bench] {name} ragged: {ms:.3f} ms/step, {gbs:.0f} GB/s algorithmic")
+    C = cfg["chunk"]
+    chunk_ends = int(sum(((positions + warmup + i) % C == C - 1).sum() for i in range(steps)))
     return {"metric": "decode tokens/s, ragged positions (batch 64)", "value": round(B / (ms * 1e-3), 1),
             "unit": "tokens/s", "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+            "chunk_end_sequence_steps_timed": chunk_ends,
             "config": {"workload": "decode_b64 ragged: batch 64, one token per sequence, positions "
                        "multiples of 64 drawn from [1024, 16384], 32 q / 8 KV heads, d 128, window 64, "
                        "chunk 64, top-32", "batch": B,
@@ -501,12 +507,17 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_16k", choices=["prefill_4k", "prefill_16k", "train_8x2k"])
+    ap.add_argument("--decode-steps", type=int, default=80,
+                    help="timed decode steps (80 from position 16384 + warm-up cross the chunk "
+                         "end at 16447, so a chunk-end top-k is inside the figure)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-utility", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step and print its JSON object")
+    ap.add_argument("--ragged-only", action="store_true",
+                    help="time only the ragged (serving-form) decode step and print its JSON object")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward pass and print its JSON object")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -534,15 +545,19 @@ def main():
               flush=True)
         return
     if args.decode_only:
-        print(json.dumps(bench_decode(still, torch, args.steps, args.warmup)), flush=True)
+        print(json.dumps(bench_decode(still, torch, args.decode_steps, args.warmup)), flush=True)
         return
     if args.backward_only:
         print(json.dumps(bench_backward(still, torch, args.steps, args.warmup)), flush=True)
         return
+    if args.ragged_only:
+        print(json.dumps(bench_decode_ragged(still, torch, args.decode_steps, args.warmup)), flush=True)
+        return
     pre = bench_prefill(still, torch, args.workload, args.steps, args.warmup)
     cfg = pre["cfg"]
-    dec = None if args.no_decode else bench_decode(still, torch, args.steps, args.warmup)
-    dec_r = None if args.no_decode else bench_decode_ragged(still, torch, args.steps, args.warmup)
+    dec = None if args.no_decode else bench_decode(still, torch, args.decode_steps, args.warmup)
+    dec_r = None if args.no_decode else bench_decode_ragged(still, torch, args.decode_steps,
+                                                             args.warmup)
     bwd = None if args.no_backward else bench_backward(still, torch, max(3, args.steps // 4),
                                                          args.warmup)
     util = None if args.no_utility else bench_utility(still, torch)

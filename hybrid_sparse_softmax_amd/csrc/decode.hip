@@ -18,6 +18,25 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kMaxG = 8;
 
+// Chunk-end top-lam of the C pending scores (slot i = position c0 + i) by
+// one wave: route flags of the chunk's ring slots.
+template <int R>
+__device__ __forceinline__ void decode_topk(const float* pend, int C, int lam, int64_t c0, int W,
+                                            uint8_t* flags) {
+    const int lane = threadIdx.x & 63;
+    uint32_t kb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) kb[r] = 64 * r + lane < C ? key_bits(route_key(pend[64 * r + lane])) : 0u;
+    bool f[R];
+    int at[R];
+    wave_topk<R>(kb, C, lam, f, at);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = 64 * r + lane;
+        if (i < C) flags[(int)((c0 + i) % W)] = f[r] ? kRouteSA : kRouteLA;
+    }
+}
+
 template <typename T, int DD, int R>
 __global__ __launch_bounds__(256) void decode_prep_kernel(const T* __restrict__ q,
                                                           const T* __restrict__ k,
@@ -206,18 +225,12 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const T* __restrict__ 
     if (W > 0 && (t % C) == C - 1) {
         const int64_t c0 = t - C + 1;
         const float* pend = c.pend + bg * C;
-        for (int i = tid; i < C; i += 256) {
-            uint8_t f = kRouteLA;
-            if (D.lam > 0) {
-                const float ki = route_key(pend[i]);
-                int rank = 0;
-                for (int j = 0; j < C; ++j) {
-                    const float kj = route_key(pend[j]);
-                    rank += (kj > ki) || (kj == ki && j < i);
-                }
-                f = rank < D.lam ? kRouteSA : kRouteLA;
-            }
-            flags[(int)((c0 + i) % W)] = f;
+        if (D.lam == 0) {
+            for (int i = tid; i < C; i += 256) flags[(int)((c0 + i) % W)] = kRouteLA;
+        } else if (tid < kWave) {  // radix top-lam of the chunk's pending scores by one wave
+            if (C <= kWave) decode_topk<1>(pend, C, D.lam, c0, W, flags);
+            else if (C <= 4 * kWave) decode_topk<4>(pend, C, D.lam, c0, W, flags);
+            else decode_topk<16>(pend, C, D.lam, c0, W, flags);
         }
     }
 }

@@ -432,18 +432,24 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
         const int64_t c0 = t - C + 1;
         const int own = (int)(t % C);
         const float* pend = c.pend + bg * C;
-        for (int i = tid; i < C; i += 256) {
-            uint8_t f = kRouteLA;
-            if (D.lam > 0) {
-                const float ki = route_key(i == own ? sig_s : pend[i]);
-                int rank = 0;
-                for (int j = 0; j < C; ++j) {
-                    const float kj = route_key(j == own ? sig_s : pend[j]);
-                    rank += (kj > ki) || (kj == ki && j < i);
-                }
-                f = rank < D.lam ? kRouteSA : kRouteLA;
+        if (D.lam == 0) {
+            for (int i = tid; i < C; i += 256) flags[(int)((c0 + i) % W)] = kRouteLA;
+        } else if (tid < 64) {
+            // radix top-lam of the chunk's scores by one wave (C <= 256: four per lane)
+            uint32_t kb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 64 * r + lane;
+                kb[r] = i < C ? key_bits(route_key(i == own ? sig_s : pend[i])) : 0u;
             }
-            flags[(int)((c0 + i) % W)] = f;
+            bool f[4];
+            int at[4];
+            wave_topk<4>(kb, C, D.lam, f, at);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 64 * r + lane;
+                if (i < C) flags[(int)((c0 + i) % W)] = f[r] ? kRouteSA : kRouteLA;
+            }
         }
     }
 }

@@ -90,6 +90,58 @@ __device__ __forceinline__ float route_key(float s) {
     return s == 0.0f ? 0.0f : s;
 }
 
+// Order-preserving map of a sort key (route_key: no NaN, no -0) to 32 bits:
+// a larger key gives a larger unsigned value.
+__device__ __forceinline__ uint32_t key_bits(float k) {
+    const uint32_t u = __float_as_uint(k);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Per-chunk top-lam (full text Sec. 3.3, chunk-level selection) by one wave:
+// the lam largest of the n <= 64 R keys it holds (position p = 64 r + lane in
+// key[r], mapped by key_bits), ties to the lower position.  A radix select
+// finds the lam-th largest value T from the top bit down, one ballot per
+// bit and register (a candidate matches the bits fixed so far; if at least
+// `need` candidates have the bit set, T has it, else those candidates are
+// all kept and need shrinks by their count); then every key above T is
+// kept, and of the keys equal to T the first `need` in position order (one
+// more ballot per register gives each its rank).  O(32 R) wave steps
+// instead of a rank count's O(C^2).  Every lane of the wave must call it;
+// sel[r] says whether position 64 r + lane is kept, rank[r] its index among
+// the kept positions in position order.
+template <int R>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[R], int n, int lam, bool (&sel)[R],
+                                          int (&rank)[R]) {
+    const int lane = threadIdx.x & 63;
+    uint32_t prefix = 0u, fixed = 0u;
+    int need = lam;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t b = 1u << bit;
+        int cnt = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool cand = 64 * r + lane < n && (key[r] & fixed) == prefix && (key[r] & b) != 0u;
+            cnt += __popcll(__ballot(cand));
+        }
+        if (cnt >= need) prefix |= b;
+        else need -= cnt;
+        fixed |= b;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+    int ties = 0, kept = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const bool valid = 64 * r + lane < n;
+        const uint64_t eq = __ballot(valid && key[r] == prefix);
+        const bool s = valid && (key[r] > prefix || (key[r] == prefix && ties + __popcll(eq & below) < need));
+        const uint64_t sm = __ballot(s);
+        sel[r] = s;
+        rank[r] = kept + __popcll(sm & below);
+        ties += __popcll(eq);
+        kept += __popcll(sm);
+    }
+}
+
 // One Self-Saliency term.  For the diagonal (own) key:
 //   a_t ln((a_t + eps)/eps) = a_t log1p(a_t / eps).
 // For another key j of the row, with e_j the unnormalised weight, sa the row

@@ -99,6 +99,28 @@ __global__ __launch_bounds__(64) void head_scores_kernel(const T* __restrict__ q
     if (lane == 0) hs[((size_t)b * D.Hq + h) * D.N + t] = term;
 }
 
+// Top-lam of one complete chunk's n keys (sort keys in LDS) by one wave:
+// route flags and the selected positions, ascending.
+template <int R>
+__device__ __forceinline__ void chunk_topk(const float* key, int n, int lam, int c0, int32_t* out,
+                                           uint8_t* rt) {
+    const int lane = threadIdx.x & 63;
+    uint32_t kb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) kb[r] = 64 * r + lane < n ? key_bits(key[64 * r + lane]) : 0u;
+    bool f[R];
+    int at[R];
+    wave_topk<R>(kb, n, lam, f, at);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = 64 * r + lane;
+        if (i < n) {
+            rt[i] = f[r] ? kRouteSA : kRouteLA;
+            if (f[r]) out[at[r]] = c0 + i;
+        }
+    }
+}
+
 // One block per (b, g, chunk): group mean of the head scores, then for a
 // complete chunk the top-lam tokens by (score desc, position asc).
 template <typename T>
@@ -138,22 +160,12 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ h
         for (int i = threadIdx.x; i < n; i += blockDim.x) rt[i] = f;
         return;
     }
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const float ki = key[i];
-        int rank = 0;
-        for (int j = 0; j < n; ++j) {
-            const float kj = key[j];
-            rank += (kj > ki) || (kj == ki && j < i);
-        }
-        flag[i] = rank < D.lam;
-    }
-    __syncthreads();
-    int32_t* out = sel_idx + (((size_t)b * D.Hkv + g) * D.n_full + c) * D.lam;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        int before = 0;
-        for (int j = 0; j < i; ++j) before += flag[j];
-        if (flag[i]) out[before] = c0 + i;
-        rt[i] = flag[i] ? kRouteSA : kRouteLA;
+    // radix top-lam of the chunk's keys by the first wave (R keys per lane)
+    if (threadIdx.x < kWave) {
+        int32_t* out = sel_idx + (((size_t)b * D.Hkv + g) * D.n_full + c) * D.lam;
+        if (n <= kWave) chunk_topk<1>(key, n, D.lam, c0, out, rt);
+        else if (n <= 4 * kWave) chunk_topk<4>(key, n, D.lam, c0, out, rt);
+        else chunk_topk<16>(key, n, D.lam, c0, out, rt);
     }
 }
 

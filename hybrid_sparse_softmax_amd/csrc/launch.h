@@ -64,7 +64,7 @@ hipError_t launch_handoff(const Dims& D, const void* k, const void* v, const flo
                           const float* scores, const int32_t* sel_idx, const uint8_t* route,
                           int cap_chunk, const CacheView& c, hipStream_t s);
 
-// ---- gfx950 MFMA forward (bf16, d = d' = 128, window = chunk = 64, topk > 0) ----
+// ---- gfx950 MFMA forward (bf16, d = d' = 128, window = chunk = 64, any topk) ----
 bool mfma_fwd_supported(const Dims& D);
 // scores, top-k, route flags, compact selected K/V lists [B, sel_list_rows,
 // Hkv, d], and the NP-Map projections as bf16 high/low parts:

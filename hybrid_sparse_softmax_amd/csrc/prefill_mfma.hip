@@ -510,24 +510,16 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
         if (tid < nq) rt[tid] = kPending;
         return;
     }
-    if (tid < kC) {
-        const float ki = key_s[tid];
-        int rank = 0;
-        for (int j = 0; j < kC; ++j) {
-            const float kj = key_s[j];
-            rank += (kj > ki) || (kj == ki && j < tid);
-        }
-        flag_s[tid] = rank < D.lam ? 1 : 0;
-    }
-    __syncthreads();
     const size_t base = (bg * D.n_full + c) * D.lam;
-    if (tid < kC) {
-        const int f = flag_s[tid];
-        int before = 0;
-        for (int j = 0; j < tid; ++j) before += flag_s[j];
-        rt[tid] = f ? kRouteSA : kRouteLA;
-        if (f) sel_idx[base + before] = t0 + tid;
-        pos_s[tid] = f ? before : -1;
+    if (wave == 0) {
+        // the chunk's 64 keys, one per lane: radix top-lam by ballots
+        const uint32_t kb[1] = {key_bits(key_s[lane])};
+        bool f[1] = {false};
+        int at[1] = {0};
+        if (D.lam > 0) wave_topk<1>(kb, kC, D.lam, f, at);
+        rt[lane] = f[0] ? kRouteSA : kRouteLA;
+        if (f[0]) sel_idx[base + at[0]] = t0 + lane;
+        pos_s[lane] = f[0] ? at[0] : -1;
     }
     __syncthreads();
     // each selected row goes to its place in the compact lists (K from LDS,
@@ -1525,7 +1517,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 }  // namespace
 
 bool mfma_fwd_supported(const Dims& D) {
-    return D.bf16 && D.d == kD && D.fd == kD && D.W == kC && D.C == kC && D.lam > 0 &&
+    return D.bf16 && D.d == kD && D.fd == kD && D.W == kC && D.C == kC &&
            (D.G == 1 || D.G == 2 || D.G == 4 || D.G == 8);
 }
 

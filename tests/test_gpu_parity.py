@@ -31,6 +31,9 @@ CASES = {
     "bf16_G8": (make_case("h", 1, 320, 8, 1, 128, 64, 64, 8), 20),
     "f32_lam_gt_C": (make_case("i", 1, 256, 4, 1, 64, 32, 32, 40, dtype="f32"), 21),
     "bf16_swa_la_W_lt_C": (make_case("j", 1, 300, 4, 1, 128, 40, 64, 0), 22),
+    # SWA + linear (no selection) at W = C = 64: the matrix-core path with no
+    # compact rows, every routed token linear
+    "bf16_swa_la_W_eq_C": (make_case("l", 2, 333, 8, 2, 128, 64, 64, 0, outlier_frac=0.01, heavy_scale=6.0), 31),
     # matrix-core path with two query heads per KV head, three sequences, a ragged tail
     "bf16_G2_B3_ragged": (make_case("k", 3, 777, 4, 2, 128, 64, 64, 20, outlier_frac=0.02, heavy_scale=6.0), 23),
     # keys scaled x80 at 2% of positions: logits beyond 2^128 in exp2 units, so
@@ -172,3 +175,34 @@ def test_routing_criteria_match_oracle(gpu_lib, route, general):
         np.testing.assert_array_equal(gsel, osel)
     assert err <= BF16_TOL
     check_rows(out, o["out"], row_tol("bf16"))
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
+@pytest.mark.parametrize("route", ["saliency", "keynorm"])
+def test_selection_with_exact_ties(gpu_lib, route, general):
+    """Every token of a KV head carries the same key (and every query head the
+    same query), so every full-window score in a chunk is the same number:
+    the top-lambda threshold falls inside one run of equal keys and the lower
+    positions must win, as the oracle's stable order says."""
+    cfg = make_case("t", 1, 300, 8, 2, 128, 64, 64, 20)
+    raw = workloads.make_prefill(cfg, 32)
+    raw["q"][:] = raw["q"][:, :1]
+    raw["k"][:] = raw["k"][:, :1]
+    dev, ref = prepare(raw, torch.bfloat16)
+    res = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=64, chunk=64,
+                      topk=20, return_scores=True, return_sel=True, general=general, route=route)
+    torch.cuda.synchronize()
+    p = O.Params(window=64, chunk=64, topk=20, route=route)
+    sigma = O.window_scores(ref["q"], ref["k"], p, 2)
+    osel, _ = O.select_chunks(sigma, p)
+    gsel = res["sel_idx"].cpu().numpy().astype(np.int64)
+    if route == "keynorm":
+        # one key norm per KV head: exact ties everywhere, the first 20 positions win
+        first = np.arange(20)[None, None, None, :] + 64 * np.arange(4)[None, None, :, None]
+        np.testing.assert_array_equal(gsel, np.broadcast_to(first, gsel.shape))
+        np.testing.assert_array_equal(gsel, osel)
+    else:
+        # the Self-Saliency of equal full-window rows agrees to the last bits
+        # only: the near-tie protocol decides, and must find nothing else
+        n_bad, worst = check_selection(gsel, sigma, osel, 64)
+        say(f"  {n_bad} chunks differ by near-ties (worst margin {worst:.2g})")

@@ -30,7 +30,7 @@ CONFIGS: dict[str, dict] = {
     "train_8x2k": dict(index=4, batch=8, seqlen=2048, n_q_heads=32, n_kv_heads=8, head_dim=128,
                        window=64, chunk=64, topk=16, dtype="bf16"),
     "decode_b64_16k": dict(index=5, batch=64, pos=16384, n_q_heads=32, n_kv_heads=8, head_dim=128,
-                           window=64, chunk=64, topk=32, dtype="bf16", sel_cap=8192),
+                           window=64, chunk=64, topk=32, dtype="bf16", sel_cap=8448),
 }
 
 
