@@ -13,14 +13,16 @@
 //                       phi_k v^T over unselected tokens (MFMA; Appendix A.2
 //                       state) along runs of consecutive chunks
 //   la_group_scan_kernel  prefix over the runs' totals
-//   hybrid_main_kernel  per query chunk: linear prefix read-out, chunk c-1
+//   hybrid_main_kernel  per query chunk: linear prefix read-out, chunk c-NWT
 //                       (window, routed selected and routed linear tokens),
-//                       chunk c (causal window), then every selected token of
-//                       chunks <= c-2 from the compact list; one online
-//                       normaliser shared by both branches (Fig. 2)
+//                       chunks c-NWT+1 .. c (window; causal in chunk c),
+//                       then every selected token of chunks <= c-NWT-1
+//                       from the compact list; one online normaliser shared
+//                       by both branches (Fig. 2)
 //
-// Routing: token j is routed for query t once j <= t - 64, so for a query of
-// chunk c the tokens of chunk c-1 at an offset <= its own are routed (their
+// Chunks are 64 tokens and the window W = 64 NWT (NWT = 1 or 2).  Routing:
+// token j is routed for query t once j <= t - W, so for a query of chunk c
+// the tokens of chunk c-NWT at an offset <= its own are routed (their
 // chunk's decision is final), later ones are still in its window.
 #include <type_traits>
 
@@ -322,7 +324,8 @@ __device__ __forceinline__ void split_projections(const float* __restrict__ wq, 
     }
 }
 
-template <int NW>
+// NWT = W / 64: the window of a query spans NWT chunks back from its own.
+template <int NW, int NWT>
 __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     float* __restrict__ scores, int32_t* __restrict__ sel_idx, uint8_t* __restrict__ route,
@@ -336,13 +339,14 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     __shared__ float key_s[kC];
     __shared__ int flag_s[kC];
     __shared__ int pos_s[kC];
-    // K rows of chunks c-1 and c, staged once for all heads (K tile layout;
+    // K rows of chunks c-NWT .. c, staged once for all heads (K tile layout;
     // rows before token 0 are never loaded and only ever masked)
-    __shared__ __align__(16) bf16 kwin[2 * kKTile];
+    __shared__ __align__(16) bf16 kwin[(NWT + 1) * kKTile];
+    const bf16* kown = kwin + NWT * kKTile;  // this chunk's key rows
     {
         const size_t ldkv = (size_t)D.Hkv * kD;
-        for (int i = 0; i < 2; ++i) {
-            const int tc = c - 1 + i;
+        for (int i = 0; i <= NWT; ++i) {
+            const int tc = c - NWT + i;
             if (tc < 0) continue;
             const bf16* src = k + (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
             for (int j = wave; j < kKPieces; j += NW) stage_k_piece(j, src, ldkv, min(kC, D.N - tc * kC), kwin + i * kKTile);
@@ -381,58 +385,61 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 const int nh = qt == 0 ? hh : hh + NW, nq = qt ^ 1;
                 if (nh < D.G) load_q(qn, nh, nq);
             }
-            // logits against keys t0-64 .. t0+63 (key index kk = 32 kt + row);
-            // the window of query offset qo is kk in [qo+1, qo+64], inside key
-            // subtiles kt = qt .. qt+2
-            f32x16 sc[3];
+            // logits against keys t0-64 NWT .. t0+63 (key index kk = 32 kt +
+            // row); the window of query offset qo is kk in [qo+1, qo+64 NWT],
+            // inside key subtiles kt = qt .. qt+2 NWT
+            constexpr int NS = 2 * NWT + 1, NSLOT = 2 * NWT;
+            f32x16 sc[NS];
 #pragma unroll
-            for (int j = 0; j < 3; ++j) sc[j] = zero16();
+            for (int j = 0; j < NS; ++j) sc[j] = zero16();
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
+                for (int j = 0; j < NS; ++j) {
                     const int kt = qt + j;
                     const bf16x8 a = ld_bf8(kwin + (kt >> 1) * kKTile + (32 * (kt & 1) + col) * kKS + 16 * s + 8 * hf);
                     sc[j] = mfma32(a, qf[s], sc[j]);
                 }
             }
-            const int qo = 32 * qt + col;  // query offset in the chunk; its own key is kk = qo + 64
-            // The window [qo+1, qo+64] holds all of subtile qt+1, the rows of
-            // subtile qt above the query's offset and the other rows of
-            // subtile qt+2: the last two are complementary, so each lane
-            // keeps 32 entries, w[0] (subtile qt+1) and w[1] (merged).
-            // Keys before token 0 (chunk -1) drop out.
-            f32x16 w[2];
+            const int qo = 32 * qt + col;  // query offset in the chunk; its own key is kk = qo + 64 NWT
+            // The window [qo+1, qo+64 NWT] holds all of subtiles qt+1 ..
+            // qt+2NWT-1, the rows of subtile qt above the query's offset and
+            // the other rows of subtile qt+2NWT: the last two are
+            // complementary, so each lane keeps 32 NWT entries: sc[1 ..
+            // 2NWT-1] in place and the merged pair in sc[0] (the query's own
+            // key among them).  Keys before token 0 drop out.
+            const int kbase = t0 - NWT * kC;  // position of kk = 0
             float mx = kNegInf, lown = 0.f;  // lown: the own logit (one lane of the pair)
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
                 const int r = acc_row(vv, hf);
-                if (r == col) lown = D.tau * sc[2][vv];
-                {
-                    const int kk = 32 * (qt + 1) + r;
-                    const float x = t0 - kC + kk >= 0 ? tl2 * sc[1][vv] : kNegInf;  // log2 units
-                    w[0][vv] = x;
+                if (r == col) lown = D.tau * sc[NSLOT][vv];
+#pragma unroll
+                for (int j = 1; j < NSLOT; ++j) {
+                    const int kk = 32 * (qt + j) + r;
+                    const float x = kbase + kk >= 0 ? tl2 * sc[j][vv] : kNegInf;  // log2 units
+                    sc[j][vv] = x;
                     mx = vmax(mx, x);
                 }
                 {
                     const bool lo = r > col;
-                    const int kk = lo ? 32 * qt + r : 32 * qt + kC + r;
-                    const float x = t0 - kC + kk >= 0 ? tl2 * (lo ? sc[0][vv] : sc[2][vv]) : kNegInf;
-                    w[1][vv] = x;
+                    const int kk = lo ? 32 * qt + r : 32 * (qt + NSLOT) + r;
+                    const float x = kbase + kk >= 0 ? tl2 * (lo ? sc[0][vv] : sc[NSLOT][vv]) : kNegInf;
+                    sc[0][vv] = x;
                     mx = vmax(mx, x);
                 }
             }
             mx = vmax(mx, xor32(mx));
             float sa = 0.f, so = 0.f, et = 0.f;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NSLOT; ++j)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
-                    const float x = w[j][vv];
+                    const float x = sc[j][vv];
                     const float e = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x - mx);
-                    w[j][vv] = e;
+                    sc[j][vv] = e;
                     sa += e;
-                    if (j == 1 && acc_row(vv, hf) == col) et += e;  // the query's own key
+                    if (j == 0 && acc_row(vv, hf) == col) et += e;  // the query's own key
                     else so += e;
                 }
             sa += xor32(sa);
@@ -448,12 +455,12 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 const float r = so > 0.f ? et / so : 0.f;
                 const float esa = D.eps * sa;
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NSLOT; ++j)
 #pragma unroll
                     for (int vv = 0; vv < 16; ++vv) {
-                        const float e = w[j][vv];
+                        const float e = sc[j][vv];
                         const float tj = -(e * isa) * log1p_fast(fast_div(r * e, e + esa));
-                        term += (e > 0.f && !(j == 1 && acc_row(vv, hf) == col)) ? tj : 0.f;
+                        term += (e > 0.f && !(j == 0 && acc_row(vv, hf) == col)) ? tj : 0.f;
                     }
                 term += xor32(term);
                 const float at = et * isa;  // the query's own key, once
@@ -475,7 +482,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
         if (route_query_free(D.route)) {
             float kn = 0.f;
             if (D.route == kRouteKeyNorm) {
-                const bf16* kr = kwin + kKTile + tid * kKS;  // this chunk's key rows
+                const bf16* kr = kown + tid * kKS;  // this chunk's key rows
                 for (int e = 0; e < kD; ++e) kn = fmaf((float)kr[e], (float)kr[e], kn);
                 kn = sqrtf(kn);
             }
@@ -529,7 +536,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
         const int x = tid + NW * 64 * i, p = x >> 4, piece = x & 15, at = pos_s[p];
         if (at >= 0) {
             const size_t dst = list0 + ((size_t)c * D.lam + at) * ldkv + 8 * piece;
-            st_bf8(ksel + dst, ld_bf8(kwin + kKTile + p * kKS + 8 * piece));
+            st_bf8(ksel + dst, ld_bf8(kown + p * kKS + 8 * piece));
             st_bf8(vsel + dst, vrow[i]);
         }
     }
@@ -849,12 +856,13 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&o)[4], f32x16 (&sc)[2], co
 // Block = HB query heads of KV head g x the 64 tokens of chunk c; two waves
 // per head, each owning 32 queries, so two waves share every SIMD and one's
 // softmax arithmetic overlaps the other's matrix products.  Key tiles, in
-// order: chunk c-1, chunk c, then the compact selected rows of chunks <= c-2,
-// 64 at a time; each tile is staged in one of two LDS buffers while the
-// previous one is computed.  Blocks are issued longest first (largest c);
-// consecutive blocks take different KV heads, so each XCD's L2 keeps few
-// compact lists.
-template <int HB>
+// order: chunks c-NWT .. c (the window, NWT = W / 64; chunk c-NWT also holds
+// the routed selected tokens at or below the query's offset), then the
+// compact selected rows of chunks <= c-NWT-1, 64 at a time; each tile is
+// staged in one of two LDS buffers while the previous one is computed.
+// Blocks are issued longest first (largest c); consecutive blocks take
+// different KV heads, so each XCD's L2 keeps few compact lists.
+template <int HB, int NWT>
 __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wqh, const bf16* __restrict__ wql, const bf16* __restrict__ phik,
@@ -903,10 +911,12 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     auto kbuf = [&](int i) { return smem + (i & 1) * kKTile; };
     auto vbuf = [&](int i) { return smem + 2 * kKTile + ((i + 3) % 3) * kVTile; };  // i >= -1
 
-    // tiles: 0 = chunk c-1 (c >= 1), 1 = chunk c, 2.. = compact selected rows
-    const int nrows = c >= 2 ? (c - 1) * D.lam : 0;
-    const int ntile = 2 + (nrows + kC - 1) / kC;
-    const int first = c >= 1 ? 0 : 1;
+    // tiles: i <= NWT = chunk c-NWT+i (those before chunk 0 are skipped),
+    // NWT+1.. = compact selected rows of chunks <= c-NWT-1
+    const int nrows = c > NWT ? (c - NWT) * D.lam : 0;
+    const int ntile = NWT + 1 + (nrows + kC - 1) / kC;
+    const int first = c >= NWT ? 0 : NWT - c;
+    const int tla = t0 - NWT * kC;  // first token of chunk c-NWT (the partly routed one)
     // compact lists of (b, g): rows ldkv elements apart, like k and v
     const size_t ldkv = (size_t)D.Hkv * kD;
     const bf16* kb = ksel + ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD;
@@ -917,14 +927,14 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // from its copy at the end of the compact lists.
     auto tile_src = [&](int i, size_t& off, size_t& ld, int& nv, bool& compact) {
         ld = ldkv;
-        if (i < 2) {
-            const int tc = c - 1 + i;
+        if (i <= NWT) {
+            const int tc = c - NWT + i;
             nv = min(kC, D.N - tc * kC);
             compact = nv < kC;
             off = compact ? (size_t)D.n_full * D.lam * ldkv
                           : (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
         } else {
-            const int r0 = (i - 2) * kC;
+            const int r0 = (i - NWT - 1) * kC;
             off = (size_t)r0 * ldkv;
             nv = min(kC, nrows - r0);
             compact = true;
@@ -947,8 +957,8 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 
     // The prologue's reads are requested together: the first tile; into the
     // prefix area (free until the prefix itself is written there) the NP-Map
-    // projection parts and the phi_k rows of chunk c-1, in the K tile
-    // layout; the route flags of chunk c-1; Q.  The prefix rows follow once
+    // projection parts and the phi_k rows of chunk c-NWT, in the K tile
+    // layout; the route flags of chunk c-NWT; Q.  The prefix rows follow once
     // the projections and phi_k rows have been used.
     // (written before the staging below is issued)
     stage(first, true, true);
@@ -960,25 +970,25 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             stage_k_piece(j, wh, kD, kD / 2, pre);
             stage_k_piece(j, wl_, kD, kD / 2, pre + kKTile);
         }
-        if (c >= 1) {
-            const bf16* pk = phik + (bg * D.N + (t0 - kC)) * kD;
+        if (c >= NWT) {
+            const bf16* pk = phik + (bg * D.N + tla) * kD;
             for (int j = wave; j < kKPieces; j += NW) stage_k_piece(j, pk, kD, kC, pre + 2 * kKTile);
         }
     }
-    // The linear prefix of chunks <= c-2 (bf16 S^T rows, 32 KB each: the
-    // within-run part sh of chunk c-2 and the earlier runs' part gh) and
+    // The linear prefix of chunks <= c-NWT-1 (bf16 S^T rows, 32 KB each: the
+    // within-run part sh of chunk c-NWT-1 and the earlier runs' part gh) and
     // their z vectors come with the same round trip, straight into LDS areas
     // the prologue leaves free: sh into V buffers 1-2, gh rows 0-63 into K
     // buffer 1, rows 64-127 and the z vectors (lz | gz) behind the prologue
-    // data in sts.  (For c >= 2 the first tile is tile 0 in K buffer 0 and V
+    // data in sts.  (When there is a prefix, c > NWT, the first tile is tile 0 in K buffer 0 and V
     // buffer 0.)
     const int ngroups = (D.n_full + D.ng - 1) / D.ng;
     const char* park_sh = reinterpret_cast<const char*>(smem + 2 * kKTile + kVTile);
     const char* park_gh0 = reinterpret_cast<const char*>(smem + kKTile);
     const char* park_gh1 = reinterpret_cast<const char*>(sts + kPreFloats);
     const float* park_z = sts + kPreFloats + kD * kD / 4;
-    if (c >= 2) {
-        const int cp = c - 2, run = cp / D.ng;
+    if (c > NWT) {
+        const int cp = c - NWT - 1, run = cp / D.ng;
         const bf16* shg = reinterpret_cast<const bf16*>(L.sh) + (bg * D.n_full + cp) * (size_t)(kD * kD);
         const bf16* ghg = reinterpret_cast<const bf16*>(L.gh) + (bg * ngroups + run) * (size_t)(kD * kD);
         // instruction j moves bytes 1024 j .. 1024 j + 1023 of a matrix
@@ -992,7 +1002,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             dma16(reinterpret_cast<const bf16*>(zsrc), (bf16*)park_z);
         }
     }
-    const uint8_t rt = c >= 1 ? route[bg * D.N + (t0 - kC) + lane] : 0;
+    const uint8_t rt = c >= NWT ? route[bg * D.N + tla + lane] : 0;
     // Q operand: qf[s] holds query t0 + oq (tokens past N repeat N-1, never
     // written), dims 16 s + 8 hf .. +7
     bf16x8 qf[1][8];
@@ -1015,7 +1025,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     float m2 = 0.f, ls = 0.f;
     uint64_t selmask = 0;
 
-    if (c >= 1) {
+    if (c >= NWT) {
         selmask = __ballot(rt == kRouteSA);
         f32x16 phi[1][2][2];
         np_map_mfma<1>(qf, pre, pre + kKTile, kKS, phi);
@@ -1041,7 +1051,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 phb[sgn][f2][1] = pack_acc(phi[0][sgn][f2], 1);
             }
         {
-            // routed linear tokens of chunk c-1 (offset <= the query's, not
+            // routed linear tokens of chunk c-NWT (offset <= the query's, not
             // selected): weight phi_k(k_j) . phi_q(q_t) at reference point 0
             f32x16 wl[2];  // rows = keys, column = query
 #pragma unroll
@@ -1066,7 +1076,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     wl[kt][vv] = p;
                     ls += p;
                 }
-            const bf16* vt = vbuf(first);  // tile 0 = chunk c-1
+            const bf16* vt = vbuf(first);  // tile 0 = chunk c-NWT
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 pa = pack_acc(wl[ks >> 1], ks & 1);
@@ -1074,12 +1084,12 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                 for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vt_frag(vt, voff, dt, ks), pa, o[dt]);
             }
         }
-        if (c >= 2) {
-            // prefix of chunks <= c-2 (within-run part + earlier runs), staged
+        if (c > NWT) {
+            // prefix of chunks <= c-NWT-1 (within-run part + earlier runs), staged
             // in LDS once for all waves (over the projections and phi_k rows,
             // now read): S^T rounded to bf16 (the MFMA operand, the precision
             // of every other product on this path), z in fp32
-            // within-run prefix of chunk c-2 plus the prefix of its run: the
+            // within-run prefix of chunk c-NWT-1 plus the prefix of its run: the
             // S^T rows arrive in bf16 (pieces of 4) and are added in fp32 and
             // rounded once; z is fp32 throughout
             constexpr int kSPieces = kD * kD / 4, kSPer = (kSPieces + 64 * NW - 1) / (64 * NW);
@@ -1104,7 +1114,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     *reinterpret_cast<const f32x4*>(park_z + 4 * tid) +
                     *reinterpret_cast<const f32x4*>(park_z + kD + 4 * tid);
             __syncthreads();
-            // normaliser of the linear prefix (chunks <= c-2): phi_q . z, with
+            // normaliser of the linear prefix (chunks <= c-NWT-1): phi_q . z, with
             // the same bf16 features as the numerator's products
             float acc = 0.f;
 #pragma unroll
@@ -1159,14 +1169,16 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // is set.
     auto softmax_mask = [&](int i, f32x16 (&sc)[2]) -> bool {
         uint64_t hi_m, lo_m;
-        if (i == 0) {  // chunk c-1: window keys (offset above the query's) and routed selected keys
+        if (i == 0) {  // chunk c-NWT: window keys (offset above the query's) and routed selected keys
             hi_m = ~0ull;
             lo_m = selmask;
-        } else if (i == 1) {  // chunk c: causal
+        } else if (i == NWT) {  // chunk c: causal
             hi_m = 0ull;
             lo_m = ~0ull;
+        } else if (i < NWT) {  // chunks c-NWT+1 .. c-1: inside every query's window
+            hi_m = lo_m = ~0ull;
         } else {
-            const int nv = min(kC, nrows - (i - 2) * kC);
+            const int nv = min(kC, nrows - (i - NWT - 1) * kC);
             hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
         }
         if ((hi_m & lo_m) != ~0ull) {
@@ -1517,7 +1529,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 }  // namespace
 
 bool mfma_fwd_supported(const Dims& D) {
-    return D.bf16 && D.d == kD && D.fd == kD && D.W == kC && D.C == kC &&
+    return D.bf16 && D.d == kD && D.fd == kD && (D.W == kC || D.W == 2 * kC) && D.C == kC &&
            (D.G == 1 || D.G == 2 || D.G == 4 || D.G == 8);
 }
 
@@ -1531,12 +1543,21 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
     const bf16* vv = reinterpret_cast<const bf16*>(v);
     bf16* ks = reinterpret_cast<bf16*>(ksel);
     bf16* vs = reinterpret_cast<bf16*>(vsel);
-    if (D.G >= 4)
-        hipLaunchKernelGGL(win_select_kernel<4>, grid, dim3(256), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D);
-    else if (D.G == 2)
-        hipLaunchKernelGGL(win_select_kernel<2>, grid, dim3(128), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D);
-    else
-        hipLaunchKernelGGL(win_select_kernel<1>, grid, dim3(64), 0, s, qq, kk, vv, scores, sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D);
+#define STILL_WS(NW, NWT)                                                                          \
+    hipLaunchKernelGGL((win_select_kernel<NW, NWT>), grid, dim3(64 * NW), 0, s, qq, kk, vv, scores, \
+                       sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D)
+    const int nwt = D.W / kC;
+    if (D.G >= 4) {
+        if (nwt == 1) STILL_WS(4, 1);
+        else STILL_WS(4, 2);
+    } else if (D.G == 2) {
+        if (nwt == 1) STILL_WS(2, 1);
+        else STILL_WS(2, 2);
+    } else {
+        if (nwt == 1) STILL_WS(1, 1);
+        else STILL_WS(1, 2);
+    }
+#undef STILL_WS
     return hipGetLastError();
 }
 
@@ -1573,17 +1594,26 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
     const bf16* wql = wqh + n;
     const int HB = D.G >= 4 ? 4 : D.G;  // query heads per block, two waves each
     const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
-#define STILL_MAIN(H)                                                                            \
-    hipLaunchKernelGGL(hybrid_main_kernel<H>, dim3(nblk), dim3(128 * H), 0, s,                  \
+    const int nwt = D.W / kC;
+#define STILL_MAIN1(H, NWT)                                                                      \
+    hipLaunchKernelGGL((hybrid_main_kernel<H, NWT>), dim3(nblk), dim3(128 * H), 0, s,           \
                        reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),      \
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
                        L, gate, reinterpret_cast<bf16*>(out), D)
+#define STILL_MAIN(H)              \
+    do {                           \
+        if (nwt == 1)              \
+            STILL_MAIN1(H, 1);     \
+        else                       \
+            STILL_MAIN1(H, 2);     \
+    } while (0)
     if (HB == 4) STILL_MAIN(4);
     else if (HB == 2) STILL_MAIN(2);
     else STILL_MAIN(1);
 #undef STILL_MAIN
+#undef STILL_MAIN1
     return hipGetLastError();
 }
 

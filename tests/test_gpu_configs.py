@@ -60,6 +60,38 @@ def test_prefill_config_matches_oracle(gpu_lib, name):
     assert serr <= 1e-4
 
 
+def test_prefill_4k_two_chunk_window_matches_oracle(gpu_lib):
+    """The 4K Llama-3-8B-shaped prefill with the pages' full-RULER window
+    (W = 128 over chunks of 64, top-16) on the matrix-core path: every
+    selection and group score compared, sampled rows evaluated by the oracle."""
+    cfg = dict(workloads.CONFIGS["prefill_4k"], window=128)
+    seed = workloads.seed_of("prefill_4k")
+    say(f"[config] prefill_4k W=128 shape={workloads.shape_of(cfg)} seed={seed}")
+    raw = workloads.make_prefill(cfg, seed)
+    dev, ref = prepare(raw, torch.bfloat16)
+    B, N, Hkv, C = cfg["batch"], cfg["seqlen"], cfg["n_kv_heads"], cfg["chunk"]
+    res = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=128,
+                      chunk=C, topk=16, return_scores=True, return_sel=True)
+    torch.cuda.synchronize()
+    p = O.Params(window=128, chunk=C, topk=16)
+    sigma = O.window_scores(ref["q"], ref["k"], p, Hkv)
+    osel, _ = O.select_chunks(sigma, p)
+    gsel = res["sel_idx"].cpu().numpy().astype(np.int64)
+    n_bad, worst = check_selection(gsel, sigma, osel, C)
+    serr = float(np.max(np.abs(res["scores"].cpu().numpy() - sigma) / np.maximum(1.0, np.abs(sigma))))
+    rows = sampled_rows(B, N, C, n_per_batch=24, seed=seed, extra=[127, 128, 191, 192])
+    o = O.fwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"], p, rows=rows,
+                     sel_override=gsel if n_bad else None, scores=sigma)
+    bi = np.array([r[0] for r in rows])
+    ti = np.array([r[1] for r in rows])
+    got = res["out"][bi, ti].double().cpu().numpy()
+    err = rel_l2(got, o["out"][bi, ti])
+    say(f"  {n_bad} near-tie swaps; score max rel err {serr:.2e}; {len(rows)} sampled rows: rel-L2 {err:.3e}")
+    assert err <= BF16_TOL
+    check_rows(got, o["out"][bi, ti], ROW_TOL_BF16)
+    assert serr <= 1e-4
+
+
 def test_ragged_multi_sequence_prefill_matches_oracle(gpu_lib):
     """A 4K+37-token, two-sequence prefill on the matrix-core path: several
     runs of chunks in the linear-state kernel, a ragged last chunk, every

@@ -22,6 +22,7 @@ FWD_CASES = {
     "bf16_G2": (make_case("b", 1, 300, 4, 2, 128, 64, 64, 8), 82),
     "f32_d64_W48_C16": (make_case("c", 1, 150, 4, 1, 64, 48, 16, 4, dtype="f32"), 83),
     "bf16_swa_la": (make_case("d", 1, 200, 4, 2, 128, 64, 64, 0), 84),
+    "bf16_W128_G4": (make_case("j", 1, 400, 8, 2, 128, 128, 64, 16), 90),
 }
 
 

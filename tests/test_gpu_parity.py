@@ -34,6 +34,13 @@ CASES = {
     # SWA + linear (no selection) at W = C = 64: the matrix-core path with no
     # compact rows, every routed token linear
     "bf16_swa_la_W_eq_C": (make_case("l", 2, 333, 8, 2, 128, 64, 64, 0, outlier_frac=0.01, heavy_scale=6.0), 31),
+    # window of two chunks (W = 128, C = 64: the pages' full-RULER window):
+    # the matrix-core path with the window spanning chunks c-2 .. c
+    "bf16_W128_C64_G4": (make_case("m", 2, 700, 8, 2, 128, 128, 64, 16, outlier_frac=0.01, heavy_scale=6.0), 32),
+    "bf16_W128_C64_G1": (make_case("n", 1, 450, 2, 2, 128, 128, 64, 8), 33),
+    "bf16_W128_C64_G8_swa_la": (make_case("o", 1, 400, 8, 1, 128, 128, 64, 0), 34),
+    "bf16_W128_C64_all_selected": (make_case("p", 1, 333, 4, 2, 128, 128, 64, 64), 35),
+    "bf16_W128_C64_underflow": (make_case("q", 1, 350, 8, 2, 128, 128, 64, 16, anti_align=56.0), 36),
     # matrix-core path with two query heads per KV head, three sequences, a ragged tail
     "bf16_G2_B3_ragged": (make_case("k", 3, 777, 4, 2, 128, 64, 64, 20, outlier_frac=0.02, heavy_scale=6.0), 23),
     # keys scaled x80 at 2% of positions: logits beyond 2^128 in exp2 units, so
