@@ -1,5 +1,5 @@
 // STILL decode step (Sec. 3.3 "Recurrent Form" of the STILL paper) for bf16
-// storage, head_dim = feature dim = 128, window 1..64, GQA group 1/2/4/8.
+// storage, head_dim = feature dim = 128, window 1..256, GQA group 1/2/4/8.
 //
 // One launch of dec_stream_kernel does all per-step work; one launch of
 // dec_combine_kernel merges it:
@@ -239,6 +239,8 @@ __device__ __forceinline__ void stream_role(const bf16* __restrict__ q, const Ca
 // --------------------------------------------------------------------------
 // state role: one (sequence, KV head)
 // --------------------------------------------------------------------------
+// R: window keys per lane (the window holds up to 64 R tokens)
+template <int R>
 __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                            const bf16* __restrict__ v, const float* __restrict__ wq,
                                            const float* __restrict__ wk,
@@ -341,40 +343,63 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
         w.la[((size_t)b * D.Hq + g * G + h) * (kD + 1) + dim] = numl[0][h][dim] + numl[1][h][dim];
     }
     // 4. per query head: window row, Self-Saliency, window partial, denominator
+    //    (window index i = lane + 64 r in register r; the own key is i = n_win - 1)
     const int n_win = (int)min<int64_t>(t + 1, W);
     for (int hh = wave; hh < G; hh += 4) {
         const float* qh = qs[hh];
-        float sj = kNegInf;
-        if (lane < n_win) {
-            const int64_t pos = t - n_win + 1 + lane;
-            const bf16* kr = lane == n_win - 1 ? kt : ring_k + (size_t)(pos % W) * kD;
-            float d = 0.f;
-#pragma unroll 4
-            for (int i = 0; i < kD / 8; ++i) {
-                const bf16x8 kk = ld8(kr + 8 * i);
+        float sj[R];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) d = fmaf(qh[8 * i + e], (float)kk[e], d);
+        for (int r = 0; r < R; ++r) {
+            const int i = lane + 64 * r;
+            sj[r] = kNegInf;
+            if (i < n_win) {
+                const int64_t pos = t - n_win + 1 + i;
+                const bf16* kr = i == n_win - 1 ? kt : ring_k + (size_t)(pos % W) * kD;
+                float d = 0.f;
+#pragma unroll 4
+                for (int x = 0; x < kD / 8; ++x) {
+                    const bf16x8 kk = ld8(kr + 8 * x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d = fmaf(qh[8 * x + e], (float)kk[e], d);
+                }
+                sj[r] = D.tau * d;
             }
-            sj = D.tau * d;
         }
-        // Self-Saliency of t over its window (own key at index n_win - 1)
-        const float mx = wave_max(sj);
-        const float e = lane < n_win ? expf(sj - mx) : 0.f;
-        const float sa = wave_sum(e);
-        const float et = __shfl(e, n_win - 1, kWave);
-        const float so = wave_sum(lane < n_win - 1 ? e : 0.f);
+        // Self-Saliency of t over its window
+        float lmx = sj[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) lmx = fmaxf(lmx, sj[r]);
+        const float mx = wave_max(lmx);
+        float e[R], sal = 0.f, sol = 0.f, etl = 0.f, own = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = lane + 64 * r;
+            e[r] = i < n_win ? expf(sj[r] - mx) : 0.f;
+            sal += e[r];
+            if (i == n_win - 1) {
+                etl += e[r];
+                own += sj[r];
+            } else {
+                sol += e[r];
+            }
+        }
+        const float sa = wave_sum(sal), so = wave_sum(sol), et = wave_sum(etl);
         float term = 0.f;
         if (D.route == kRouteSaliency) {
-            if (lane < n_win && e > 0.f) {
-                const float a = e / sa;
-                if (lane == n_win - 1) term = a * log1pf(a / D.eps);
-                else term = -a * log1p_fast(fast_div((et / so) * e, e + D.eps * sa));
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int i = lane + 64 * r;
+                if (i < n_win && e[r] > 0.f) {
+                    const float a = e[r] / sa;
+                    if (i == n_win - 1) term += a * log1pf(a / D.eps);
+                    else term += -a * log1p_fast(fast_div((et / so) * e[r], e[r] + D.eps * sa));
+                }
             }
             term = wave_sum(term);
         } else if (D.route == kRouteDiagonal) {
             term = et / sa;  // the own weight a_tt
         } else {
-            term = __shfl(sj, n_win - 1, kWave);  // the own logit tau q_t.k_t
+            term = wave_sum(own);  // the own logit tau q_t.k_t (one lane holds it)
         }
         if (lane == 0) hsc[hh] = term;
         // the evicted token when it joined the selected list this step
@@ -384,18 +409,28 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
             sev = D.tau * wave_sum(dp);
         }
         const float mw = fmaxf(mx, sev);
-        const float p = lane < n_win ? expf(sj - mw) : 0.f;
+        float p[R], pl = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            p[r] = lane + 64 * r < n_win ? expf(sj[r] - mw) : 0.f;
+            pl += p[r];
+        }
         const float pev = appended ? expf(sev - mw) : 0.f;
-        float lw = wave_sum(p) + pev;
+        float lw = wave_sum(pl) + pev;
         float a0 = pev * vs[2 * lane], a1 = pev * vs[2 * lane + 1];
         if (!appended) a0 = a1 = 0.f;
-        for (int j = 0; j < n_win; ++j) {
-            const float pj = __shfl(p, j, kWave);
-            const int64_t pos = t - n_win + 1 + j;
-            const bf16* vr = j == n_win - 1 ? vt : ring_v + (size_t)(pos % W) * kD;
-            const bf16x2 v2 = *reinterpret_cast<const bf16x2*>(vr + 2 * lane);
-            a0 = fmaf(pj, (float)v2[0], a0);
-            a1 = fmaf(pj, (float)v2[1], a1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int nb = min(64, n_win - 64 * r);
+            for (int jj = 0; jj < nb; ++jj) {
+                const int j = 64 * r + jj;
+                const float pj = __shfl(p[r], jj, kWave);
+                const int64_t pos = t - n_win + 1 + j;
+                const bf16* vr = j == n_win - 1 ? vt : ring_v + (size_t)(pos % W) * kD;
+                const bf16x2 v2 = *reinterpret_cast<const bf16x2*>(vr + 2 * lane);
+                a0 = fmaf(pj, (float)v2[0], a0);
+                a1 = fmaf(pj, (float)v2[1], a1);
+            }
         }
         float* wp = w.win + ((size_t)b * D.Hq + g * G + hh) * (kD + 2);
         if (lane == 0) {
@@ -454,7 +489,7 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
     }
 }
 
-template <int G>
+template <int G, int R>
 __global__ __launch_bounds__(256) void dec_stream_kernel(const bf16* __restrict__ q,
                                                          const bf16* __restrict__ k,
                                                          const bf16* __restrict__ v,
@@ -465,7 +500,7 @@ __global__ __launch_bounds__(256) void dec_stream_kernel(const bf16* __restrict_
     const int nstate = D.B * D.Hkv;
     const int bid = blockIdx.x;
     if (bid < nstate) {
-        state_role(q, k, v, wq, wk, gate, c, w, D, bid / D.Hkv, bid % D.Hkv);
+        state_role<R>(q, k, v, wq, wk, gate, c, w, D, bid / D.Hkv, bid % D.Hkv);
     } else {
         const int x = bid - nstate;
         const int split = x % w.nsplit, bg = x / w.nsplit;
@@ -514,7 +549,7 @@ __global__ __launch_bounds__(kD) void dec_combine_kernel(FastWork w, CacheView c
 }  // namespace
 
 bool fast_decode_supported(const Dims& D) {
-    return D.bf16 && D.d == kD && D.fd == kD && D.W >= 1 && D.W <= 64 && D.C <= 256 &&
+    return D.bf16 && D.d == kD && D.fd == kD && D.W >= 1 && D.W <= 256 && D.C <= 256 &&
            (D.G == 1 || D.G == 2 || D.G == 4 || D.G == 8);
 }
 
@@ -544,12 +579,20 @@ hipError_t launch_fast_decode(const Dims& D, const void* q, const void* k, const
     const bf16* qq = reinterpret_cast<const bf16*>(q);
     const bf16* kk = reinterpret_cast<const bf16*>(k);
     const bf16* vv = reinterpret_cast<const bf16*>(v);
-#define STILL_DEC(GG) hipLaunchKernelGGL(dec_stream_kernel<GG>, dim3(nblk), dim3(256), 0, s, qq, kk, vv, wq, wk, gate, c, w, D)
+#define STILL_DEC2(GG, RR) \
+    hipLaunchKernelGGL((dec_stream_kernel<GG, RR>), dim3(nblk), dim3(256), 0, s, qq, kk, vv, wq, wk, gate, c, w, D)
+#define STILL_DEC(GG)                     \
+    do {                                  \
+        if (D.W <= 64) STILL_DEC2(GG, 1);  \
+        else if (D.W <= 128) STILL_DEC2(GG, 2); \
+        else STILL_DEC2(GG, 4);           \
+    } while (0)
     if (D.G == 1) STILL_DEC(1);
     else if (D.G == 2) STILL_DEC(2);
     else if (D.G == 4) STILL_DEC(4);
     else STILL_DEC(8);
 #undef STILL_DEC
+#undef STILL_DEC2
     return hipGetLastError();
 }
 

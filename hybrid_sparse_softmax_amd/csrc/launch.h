@@ -114,7 +114,7 @@ hipError_t launch_decode_sel(const Dims& D, const void* q, const CacheView& c, c
 hipError_t launch_decode_combine(const Dims& D, const DecodeWork& w, void* out, int64_t* pos_dev,
                                  hipStream_t s);
 
-// ---- fast decode step (bf16, d = d' = 128, window 1..64, G in {1,2,4,8}) --------
+// ---- fast decode step (bf16, d = d' = 128, window 1..256, G in {1,2,4,8}) -------
 bool fast_decode_supported(const Dims& D);
 int fast_decode_splits(int cap);                     // stream splits of 1024 selected rows
 size_t fast_decode_floats(const Dims& D, int nsplit);  // workspace, in floats

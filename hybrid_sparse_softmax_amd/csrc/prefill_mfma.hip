@@ -20,7 +20,7 @@
 //                       from the compact list; one online normaliser shared
 //                       by both branches (Fig. 2)
 //
-// Chunks are 64 tokens and the window W = 64 NWT (NWT = 1 or 2).  Routing:
+// Chunks are 64 tokens and the window W = 64 NWT (NWT = 1, 2 or 4).  Routing:
 // token j is routed for query t once j <= t - W, so for a query of chunk c
 // the tokens of chunk c-NWT at an offset <= its own are routed (their
 // chunk's decision is final), later ones are still in its window.
@@ -1529,7 +1529,8 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 }  // namespace
 
 bool mfma_fwd_supported(const Dims& D) {
-    return D.bf16 && D.d == kD && D.fd == kD && (D.W == kC || D.W == 2 * kC) && D.C == kC &&
+    return D.bf16 && D.d == kD && D.fd == kD && (D.W == kC || D.W == 2 * kC || D.W == 4 * kC) &&
+           D.C == kC &&
            (D.G == 1 || D.G == 2 || D.G == 4 || D.G == 8);
 }
 
@@ -1547,16 +1548,19 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
     hipLaunchKernelGGL((win_select_kernel<NW, NWT>), grid, dim3(64 * NW), 0, s, qq, kk, vv, scores, \
                        sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D)
     const int nwt = D.W / kC;
-    if (D.G >= 4) {
-        if (nwt == 1) STILL_WS(4, 1);
-        else STILL_WS(4, 2);
-    } else if (D.G == 2) {
-        if (nwt == 1) STILL_WS(2, 1);
-        else STILL_WS(2, 2);
-    } else {
-        if (nwt == 1) STILL_WS(1, 1);
-        else STILL_WS(1, 2);
-    }
+#define STILL_WS_NWT(NW)          \
+    do {                          \
+        if (nwt == 1)             \
+            STILL_WS(NW, 1);      \
+        else if (nwt == 2)        \
+            STILL_WS(NW, 2);      \
+        else                      \
+            STILL_WS(NW, 4);      \
+    } while (0)
+    if (D.G >= 4) STILL_WS_NWT(4);
+    else if (D.G == 2) STILL_WS_NWT(2);
+    else STILL_WS_NWT(1);
+#undef STILL_WS_NWT
 #undef STILL_WS
     return hipGetLastError();
 }
@@ -1606,8 +1610,10 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
     do {                           \
         if (nwt == 1)              \
             STILL_MAIN1(H, 1);     \
-        else                       \
+        else if (nwt == 2)         \
             STILL_MAIN1(H, 2);     \
+        else                       \
+            STILL_MAIN1(H, 4);     \
     } while (0)
     if (HB == 4) STILL_MAIN(4);
     else if (HB == 2) STILL_MAIN(2);

@@ -39,6 +39,7 @@ DEC_CASES = {
     "bf16_underflow_G4": (make_case("v", 1, 40 + 100, 8, 2, 128, 64, 64, 16, anti_align=56.0), 40, 41),
     # two-chunk window (W = 128, C = 64): matrix-core prefill, then the steps
     "bf16_W128_C64_G4": (make_case("x", 1, 330 + 70, 8, 2, 128, 128, 64, 16), 330, 43),
+    "bf16_W256_C64_G2": (make_case("y", 1, 450 + 70, 4, 2, 128, 256, 64, 8), 450, 44),
     "f32_underflow_d64": (make_case("w", 1, 60 + 40, 4, 1, 64, 32, 16, 16, dtype="f32", anti_align=48.0),
                           60, 42),
 }

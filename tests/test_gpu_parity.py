@@ -41,6 +41,9 @@ CASES = {
     "bf16_W128_C64_G8_swa_la": (make_case("o", 1, 400, 8, 1, 128, 128, 64, 0), 34),
     "bf16_W128_C64_all_selected": (make_case("p", 1, 333, 4, 2, 128, 128, 64, 64), 35),
     "bf16_W128_C64_underflow": (make_case("q", 1, 350, 8, 2, 128, 128, 64, 16, anti_align=56.0), 36),
+    # four-chunk window (W = 256, C = 64: the widest S-NIAH window)
+    "bf16_W256_C64_G4": (make_case("r", 2, 700, 8, 2, 128, 256, 64, 16, outlier_frac=0.01, heavy_scale=6.0), 37),
+    "bf16_W256_C64_G2_swa_la": (make_case("s", 1, 500, 4, 2, 128, 256, 64, 0), 38),
     # matrix-core path with two query heads per KV head, three sequences, a ragged tail
     "bf16_G2_B3_ragged": (make_case("k", 3, 777, 4, 2, 128, 64, 64, 20, outlier_frac=0.02, heavy_scale=6.0), 23),
     # keys scaled x80 at 2% of positions: logits beyond 2^128 in exp2 units, so
