@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void bwd_route_kernel(const int32_t* __restric
 // gamma dphi_q for the NP-Map's VJP and dgate = (1 - gamma) phi_q . dphi_q.
 // stat[(b, t, h)] = (m, l, D_t, c_t).
 constexpr int kNP = 2;  // query positions per wave
-template <typename T, int DD, int GM>
+template <typename T, int DD, int GM, bool LA_ONLY = false>
 __global__ __launch_bounds__(64) void bwd_query_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
@@ -227,8 +227,21 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
     // may be negative, when it has none (t < W, every routed token selected),
     // so logits far below 0 cannot underflow every weight.  The key kernels
     // read the same reference from stat.
-    float m[R];
+    float m[R], inv[R], Dt[R], cfs[R];
     bool la_mass[R];
+    if constexpr (LA_ONLY) {
+        // the statistics come from the matrix-core first pass (which also
+        // wrote the softmax part of dq): only the linear terms are left
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float4 s4 = *reinterpret_cast<const float4*>(stat + qoff(r / GM, min(r % GM, G - 1)) * 4);
+            m[r] = s4.x;
+            inv[r] = use[r] ? 1.0f / s4.y : 0.f;
+            Dt[r] = s4.z;
+            cfs[r] = s4.w;
+            la_mass[r] = s4.w > 0.f;
+        }
+    } else {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         la_mass[r] = l[r] > 0.f;
@@ -264,7 +277,6 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
     if (D.W > 0)
         for (int j0 = jw0; j0 <= t_hi; j0 += kWave) pass1(j0 + lane <= t_hi ? j0 + lane : -1, true);
     for (int i0 = 0; i0 < n_cand; i0 += kWave) pass1(i0 + lane < n_cand ? sel[i0 + lane] : -1, false);
-    float inv[R], Dt[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         inv[r] = use[r] ? 1.0f / l[r] : 0.f;
@@ -324,6 +336,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
 #pragma unroll
                 for (int p = 0; p < PL; ++p)
                     dq[qoff(pp, h) * DD + lane + kWave * p] = D.tau * dqa[pp * GM + h][p];
+    }  // !LA_ONLY
 
     // ---- dphi_q, per position ----
 #pragma unroll
@@ -371,7 +384,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
                 const int r = pp * GM + h;
                 const size_t o = qoff(pp, h);
                 // no linear mass: no linear term to differentiate
-                const float cf = la_mass[r] ? expf(-m[r]) * inv[r] : 0.f;
+                const float cf = LA_ONLY ? cfs[r] : (la_mass[r] ? expf(-m[r]) * inv[r] : 0.f);
                 // cf dfq is the gradient w.r.t. the gated features fq = gamma phi_q:
                 // phi_q gets gamma times it, the gate logit (1 - gamma) fq . (cf dfq)
                 const float gw = gate_weight(gate, o);
@@ -384,7 +397,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
                     fd = wave_sum(fd);
                     if (lane == 0) dgate[o] = (1.f - gw) * cf * fd;
                 }
-                if (lane == 0) {
+                if (lane == 0 && !LA_ONLY) {
                     stat[o * 4 + 0] = m[r];
                     stat[o * 4 + 1] = l[r];
                     stat[o * 4 + 2] = Dt[r];
@@ -953,6 +966,26 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     STILL_STEP("bwd_route", hipLaunchKernelGGL(bwd_route_kernel, dim3(D.T, D.Hkv, D.B), dim3(256),
                                                (size_t)D.C * sizeof(int), s, a.sel_idx, w.route,
                                                w.selw, D));
+    if (w.mfma) {
+        // first pass and the softmax part of dq on the matrix cores
+        if ((e = mark.fn(mark.ctx, "bwd_lists")) != hipSuccess) return e;
+        if ((e = launch_bwd_lists(D, w.selw, a.k, a.v, w.ksel, w.vsel, w.list_off, a.wq, a.wk, w.wsplit,
+                                  s)) != hipSuccess)
+            return e;
+        if ((e = mark.fn(mark.ctx, "la_state")) != hipSuccess) return e;
+        if ((e = launch_la_state(D, a.k, a.v, w.wsplit, w.route, w.phik16, w.lin16, -1, s)) != hipSuccess)
+            return e;
+        if ((e = mark.fn(mark.ctx, "la_scan16")) != hipSuccess) return e;
+        if ((e = launch_la_group_scan(D, w.lin16, -1, nullptr, nullptr, s)) != hipSuccess) return e;
+        if ((e = mark.fn(mark.ctx, "bwd_stats")) != hipSuccess) return e;
+        if ((e = launch_hybrid_stats(D, a.q, a.k, a.v, w.wsplit, w.phik16, w.route, w.ksel, w.vsel,
+                                     w.lin16, a.gate, w.list_off, a.dout, w.stat, s)) != hipSuccess)
+            return e;
+        if ((e = mark.fn(mark.ctx, "bwd_dq")) != hipSuccess) return e;
+        if ((e = launch_bwd_dq(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.list_off, w.stat,
+                               a.dq, s)) != hipSuccess)
+            return e;
+    }
     if ((e = mark.fn(mark.ctx, "phi_q")) != hipSuccess) return e;
     // the queries' features carry their gate weights (phi~_q = gamma phi_q), so
     // every linear term below is the gated one
@@ -963,14 +996,23 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     if ((e = launch_la_chunks(D, w.phik, a.v, w.route, w.lin, s)) != hipSuccess) return e;
     if ((e = mark.fn(mark.ctx, "la_scan")) != hipSuccess) return e;
     if ((e = launch_la_scan(D, w.lin, -1, nullptr, nullptr, s)) != hipSuccess) return e;
-#define STILL_BWD_QUERY(GM)                                                                     \
-    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM>), dim3((D.N + kNP - 1) / kNP * D.Hkv * D.B), dim3(64), \
+#define STILL_BWD_QUERY2(GM, LAO)                                                               \
+    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM, LAO>), dim3((D.N + kNP - 1) / kNP * D.Hkv * D.B), dim3(64), \
                        0, s, q, k,                                                                  \
                        v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.gate, a.dq, w.dphiq,    \
                        a.dgate, w.stat, D)
-    STILL_STEP("bwd_query", if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
-                            else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));
+#define STILL_BWD_QUERY(GM)             \
+    do {                                \
+        if (w.mfma)                     \
+            STILL_BWD_QUERY2(GM, true); \
+        else                            \
+            STILL_BWD_QUERY2(GM, false);\
+    } while (0)
+    STILL_STEP(w.mfma ? "bwd_query_la" : "bwd_query",
+               if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
+               else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));
 #undef STILL_BWD_QUERY
+#undef STILL_BWD_QUERY2
     STILL_STEP("bwd_uchunk",
                hipLaunchKernelGGL((bwd_uchunk_kernel<T, DD>), dim3(D.T, D.Hkv, D.B), dim3(256), 0,
                                   s, w.phiq, dout, w.stat, w.ust, D));
@@ -1014,7 +1056,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 
 }  // namespace
 
-int bwd_launch_count() { return 16; }
+int bwd_launch_count(bool mfma) { return mfma ? 21 : 16; }
 
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s,
                       BwdMark mark) {

@@ -97,6 +97,26 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                               const void* ksel, const void* vsel, const LinBufs& L,
                               const float* gate, void* out, hipStream_t s);
 
+// ---- backward on the matrix cores (bf16, d = 128, C = 64, W = 64 / 128 / 256) ----
+bool mfma_bwd_supported(const Dims& D);
+// compact K / V lists of the selection selw (ascending, -1 padded per chunk):
+// chunk c's rows start at list_off[(b Hkv + g) (n_full + 1) + c]; also the
+// NP-Map projection split (wsplit, as for the forward)
+hipError_t launch_bwd_lists(const Dims& D, const int32_t* selw, const void* k, const void* v,
+                            void* ksel, void* vsel, int* list_off, const float* wq, const float* wk,
+                            void* wsplit, hipStream_t s);
+// the forward's main kernel writing (m, l, D = dout . out, c) per query head
+// to stat [B, N, Hq, 4] instead of the output
+hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, const void* v,
+                               const void* wsplit, const void* phik, const uint8_t* route,
+                               const void* ksel, const void* vsel, const LinBufs& L,
+                               const float* gate, const int* list_off, const void* dout,
+                               float* stat, hipStream_t s);
+// softmax part of dq (fp32, overwritten)
+hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
+                         const uint8_t* route, const void* ksel, const void* vsel,
+                         const int* list_off, const float* stat, float* dq, hipStream_t s);
+
 // ---- decode step ------------------------------------------------------------
 struct DecodeWork {
     float* la;      // [B, Hq, d + 1]   linear numerator, denominator
@@ -143,13 +163,21 @@ struct BwdWork {
     uint8_t* route;       // [B, Hkv, N]
     int32_t* selw;        // [B, Hkv, n_full, lam] ascending, -1 padded
     int nslice;
+    // matrix-core path (mfma): the softmax part of dq and the statistics on
+    // the matrix cores, over compact lists of the given selection
+    bool mfma;
+    void *ksel, *vsel;    // [B, sel_list_rows, Hkv, d] bf16
+    int* list_off;        // [B, Hkv, n_full + 1]
+    void* phik16;         // [B, Hkv, N, d'] bf16 (kperm features)
+    void* wsplit;         // NP-Map projections as bf16 high / low parts
+    LinBufs lin16;        // linear prefixes of the matrix-core path
 };
 // called before each launch with the kernel's name (per-launch events)
 struct BwdMark {
     hipError_t (*fn)(void* ctx, const char* name);
     void* ctx;
 };
-int bwd_launch_count();
+int bwd_launch_count(bool mfma);
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s, BwdMark mark);
 hipError_t launch_zero(float* p, int n, hipStream_t s);
 

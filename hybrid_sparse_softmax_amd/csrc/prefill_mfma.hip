@@ -862,13 +862,23 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&o)[4], f32x16 (&sc)[2], co
 // staged in one of two LDS buffers while the previous one is computed.
 // Blocks are issued longest first (largest c); consecutive blocks take
 // different KV heads, so each XCD's L2 keeps few compact lists.
-template <int HB, int NWT>
+//
+// STATS (the backward's first pass): instead of the output, each query head
+// writes (m, l, D, c) to stat: the reference m in natural units, the
+// normaliser l at that reference (linear terms included), D = dout . out
+// (out = O / l in fp32), and c = exp(-m) / l when the query has linear mass
+// (else 0).  list_off (when not null) gives the compact rows of chunk c as
+// rows list_off[c] .. list_off[c + 1] - 1 of (b, g) (n_full + 1 entries, the
+// last the open chunk's copy), for lists built from a given selection whose
+// chunks may hold fewer than lam rows.
+template <int HB, int NWT, bool STATS = false>
 __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ wqh, const bf16* __restrict__ wql, const bf16* __restrict__ phik,
     const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, LinBufs L,
-    const float* __restrict__ gate, bf16* __restrict__ out, Dims D) {
+    const float* __restrict__ gate, bf16* __restrict__ out, const int* __restrict__ list_off,
+    const bf16* __restrict__ dout, float* __restrict__ stat, Dims D) {
     constexpr int NW = HB * 2;  // waves
     const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
@@ -913,7 +923,9 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 
     // tiles: i <= NWT = chunk c-NWT+i (those before chunk 0 are skipped),
     // NWT+1.. = compact selected rows of chunks <= c-NWT-1
-    const int nrows = c > NWT ? (c - NWT) * D.lam : 0;
+    const int* loff = list_off ? list_off + bg * (D.n_full + 1) : nullptr;
+    const int nrows = c > NWT ? (loff ? loff[c - NWT] : (c - NWT) * D.lam) : 0;
+    const int tail_row = loff ? loff[D.n_full] : D.n_full * D.lam;  // the open chunk's copy
     const int ntile = NWT + 1 + (nrows + kC - 1) / kC;
     const int first = c >= NWT ? 0 : NWT - c;
     const int tla = t0 - NWT * kC;  // first token of chunk c-NWT (the partly routed one)
@@ -931,7 +943,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             const int tc = c - NWT + i;
             nv = min(kC, D.N - tc * kC);
             compact = nv < kC;
-            off = compact ? (size_t)D.n_full * D.lam * ldkv
+            off = compact ? (size_t)tail_row * ldkv
                           : (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
         } else {
             const int r0 = (i - NWT - 1) * kC;
@@ -1149,6 +1161,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // would otherwise underflow every weight and leave 0 / 0.  The flag is
     // the same in both lanes of a query.
     bool nola = !(ls + xor32(ls) > 0.f);
+    const bool lamass = !nola;
 
     // logits of tile i (K^T Q on the matrix cores)
     auto qk = [&](int i, f32x16 (&sc)[2]) {
@@ -1235,7 +1248,9 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][vv], cl2, nm));
+                // the normaliser sums the bf16 probabilities the value product
+                // uses, so O / l is their exact weighted mean
+                const float p = (float)(bf16)__builtin_amdgcn_exp2f(fmaf(sc[kt][vv], cl2, nm));
                 sc[kt][vv] = p;
                 ls += p;
             }
@@ -1503,6 +1518,36 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         }
     }
 
+    if constexpr (STATS) {
+        // statistics of the lane's query: D = dout . O / l over the lane's 64
+        // dims (32 dt + acc_row(..)) plus the other half's
+        const float lsum = ls + xor32(ls);
+        const int tq = min(t0 + oq, D.N - 1);
+        const size_t qo = ((size_t)b * D.N + tq) * D.Hq + h;
+        const bf16* dr = dout + qo * kD;
+        float dp = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const bf16x4 d4 = *reinterpret_cast<const bf16x4*>(dr + 32 * dt + acc_row(4 * v4, hf));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dp = fmaf(o[dt][4 * v4 + j], (float)d4[j], dp);
+            }
+        dp = (dp + xor32(dp)) / lsum;
+        if (hf == 0 && t0 + oq < D.N) {
+            constexpr float kLn2 = 0.6931471805599453f;
+            f32x4 st;
+            st[0] = m2 * kLn2;
+            st[1] = lsum;
+            st[2] = dp;
+            st[3] = lamass ? __builtin_amdgcn_exp2f(-m2) / lsum : 0.f;
+            *reinterpret_cast<f32x4*>(stat + qo * 4) = st;
+        }
+        // tile staging issued by the loop's last steps lands before the wave ends
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        return;
+    }
     // epilogue: normalise, stage each wave's 32 x 128 tile in LDS, write rows
     const float il = 1.f / (ls + xor32(ls));
     bf16* ot = reinterpret_cast<bf16*>(sts) + wave * (32 * kKS);
@@ -1523,6 +1568,209 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         if (row < nq)
             st_bf8(out + (((size_t)b * D.N + t0 + 32 * qh + row) * D.Hq + h) * kD + 8 * piece,
                    ld_bf8(ot + row * kKS + 8 * piece));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward pass on the matrix cores (routing held fixed)
+// ---------------------------------------------------------------------------
+// Compact K / V lists of a given selection: selw [B, Hkv, n_full, lam] holds
+// each complete chunk's selected positions ascending and -1 padded.  Chunk c
+// of (b, g) gets rows off[c] .. off[c] + n_c - 1 (n_c its valid entries,
+// off the exclusive prefix), laid out like the forward's lists; block
+// c = n_full writes the total and the open chunk's 64-row copy (rows past N
+// repeat token N-1; zeros when the last chunk is complete).  The first
+// chunk's blocks of sequence 0 also split the NP-Map projections.
+__global__ __launch_bounds__(256) void bwd_lists_kernel(const int32_t* __restrict__ selw,
+                                                        const bf16* __restrict__ k,
+                                                        const bf16* __restrict__ v,
+                                                        bf16* __restrict__ ksel, bf16* __restrict__ vsel,
+                                                        int* __restrict__ list_off,
+                                                        const float* __restrict__ wq,
+                                                        const float* __restrict__ wk,
+                                                        bf16* __restrict__ wsplit, Dims D) {
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const size_t bg = (size_t)b * D.Hkv + g;
+    const int32_t* sw = selw + bg * D.n_full * D.lam;
+    __shared__ int red[256];
+    int cnt = 0;
+    for (int i = tid; i < c * D.lam; i += 256) cnt += sw[i] >= 0;
+    red[tid] = cnt;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    const int off = red[0];
+    if (tid == 0) list_off[bg * (D.n_full + 1) + c] = off;
+    const size_t ldkv = (size_t)D.Hkv * kD;
+    const size_t list0 = ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD;
+    if (c < D.n_full) {
+        for (int x = tid; x < D.lam * 16; x += 256) {
+            const int i = x >> 4, piece = x & 15;
+            const int pos = sw[c * D.lam + i];  // valid entries come first
+            if (pos >= 0) {
+                const size_t src = (((size_t)b * D.N + pos) * D.Hkv + g) * kD + 8 * piece;
+                const size_t dst = list0 + (size_t)(off + i) * ldkv + 8 * piece;
+                st_bf8(ksel + dst, ld_bf8(k + src));
+                st_bf8(vsel + dst, ld_bf8(v + src));
+            }
+        }
+    } else {
+        const bool open = D.T > D.n_full;
+        const int t0 = D.n_full * kC;
+        for (int x = tid; x < kC * 16; x += 256) {
+            const int p = x >> 4, piece = x & 15;
+            const size_t src = (((size_t)b * D.N + min(t0 + p, D.N - 1)) * D.Hkv + g) * kD + 8 * piece;
+            const size_t dst = list0 + (size_t)(off + p) * ldkv + 8 * piece;
+            st_bf8(ksel + dst, open ? ld_bf8(k + src) : zero_bf8());
+            st_bf8(vsel + dst, open ? ld_bf8(v + src) : zero_bf8());
+        }
+    }
+    if (c == 0 && b == 0) split_projections(wq, wk, wsplit, D.Hkv, g, 256);
+}
+
+// Softmax part of dq on the matrix cores.  Block = HB query heads of KV
+// head g x the 64 queries of chunk c (two waves per head, 32 queries each),
+// the key tiles of the forward in its order (window chunks c-NWT .. c with
+// their masks, then the compact selected rows).  Per tile, with the
+// statistics (m, l, D) of the first pass and P = exp(tau q.k - m) / l:
+//   S^T  = K Q^T           (logits, keys x queries)
+//   dP^T = V dout^T        (dout . v_j)
+//   dS^T = P^T (dP^T - D)  rounded to bf16 as the forward rounds P
+//   dQ^T += K^T dS^T       (K read transposed from LDS)
+// 48 products per wave and tile; dq = tau (dQ^T)^T is written in fp32.
+// The linear terms of dq (through phi_q) are added by other kernels.
+template <int HB, int NWT>
+__global__ __launch_bounds__(HB * 128) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const uint8_t* __restrict__ route,
+    const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const int* __restrict__ list_off,
+    const float* __restrict__ stat, float* __restrict__ dq, Dims D) {
+    constexpr int NW = HB * 2;
+    const int HG = D.G / HB;
+    const int per_c = D.B * D.Hkv * HG;
+    const int c = D.T - 1 - (int)(blockIdx.x / per_c);
+    int r = (int)(blockIdx.x % per_c);
+    const int hg = r % HG;
+    r /= HG;
+    const int g = r % D.Hkv, b = r / D.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = wave / HB;
+    const int h = g * D.G + hg * HB + wave % HB;
+    const int t0 = c * kC;
+    const int oq = 32 * qh + col;
+    const size_t bg = (size_t)b * D.Hkv + g;
+    const float cl2 = D.tau * kLog2e;
+    const int* loff = list_off + bg * (D.n_full + 1);
+    const int nrows = c > NWT ? loff[c - NWT] : 0;
+    const int ntile = NWT + 1 + (nrows + kC - 1) / kC;
+    const int first = c >= NWT ? 0 : NWT - c;
+    const int tla = t0 - NWT * kC;
+    const size_t ldkv = (size_t)D.Hkv * kD;
+
+    __shared__ __align__(16) bf16 ks[kC * kKS];
+    __shared__ __align__(16) bf16 vs[kC * kKS];
+    __shared__ __align__(16) bf16 kt[kD * kVS];
+
+    // the lane's query: Q and dout operands, statistics
+    const int tq = min(t0 + oq, D.N - 1);
+    const size_t qo = ((size_t)b * D.N + tq) * D.Hq + h;
+    bf16x8 qf[8], df[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        qf[s] = ld_bf8(q + qo * kD + 16 * s + 8 * hf);
+        df[s] = ld_bf8(dout + qo * kD + 16 * s + 8 * hf);
+    }
+    const f32x4 st = *reinterpret_cast<const f32x4*>(stat + qo * 4);
+    const float lse2 = st[0] * kLog2e + __log2f(st[1]);  // P = 2^(s cl2 - lse2)
+    const float dq_d = st[2];
+    uint64_t selmask = 0;
+    if (c >= NWT) selmask = __ballot(route[bg * D.N + tla + lane] == kRouteSA);
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
+
+    for (int i = first; i < ntile; ++i) {
+        // rows of tile i: a window chunk from k / v, or compact rows
+        const bf16 *srck, *srcv;
+        int nv;
+        uint64_t hi_m, lo_m;
+        if (i <= NWT) {
+            const int tc = c - NWT + i;
+            nv = min(kC, D.N - tc * kC);
+            const size_t off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
+            srck = k + off;
+            srcv = v + off;
+            if (i == 0) {
+                hi_m = ~0ull;
+                lo_m = selmask;
+            } else if (i == NWT) {
+                hi_m = 0ull;
+                lo_m = ~0ull;
+            } else {
+                hi_m = lo_m = ~0ull;
+            }
+        } else {
+            const int r0 = (i - NWT - 1) * kC;
+            nv = min(kC, nrows - r0);
+            const size_t off = ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD + (size_t)r0 * ldkv;
+            srck = ksel + off;
+            srcv = vsel + off;
+            hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
+        }
+        __syncthreads();  // the previous tile's reads are done
+        load_k_tile(srck, ldkv, nv, ks, tid, NW * 64);
+        load_k_tile(srcv, ldkv, nv, vs, tid, NW * 64);
+        load_vt_tile(srck, ldkv, nv, kt, tid, NW * 64);
+        __syncthreads();
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            sc[j] = zero16();
+            dp[j] = zero16();
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                sc[j] = mfma32(ld_bf8(ks + (32 * j + col) * kKS + 16 * s + 8 * hf), qf[s], sc[j]);
+                dp[j] = mfma32(ld_bf8(vs + (32 * j + col) * kKS + 16 * s + 8 * hf), df[s], dp[j]);
+            }
+        // key row rk counts for the lane's query when bit rk of
+        // (rk > oq ? hi_m : lo_m) is set
+        const uint64_t gt = oq >= 63 ? 0ull : ~0ull << (oq + 1);
+        const uint64_t mm = ((hi_m & gt) | (lo_m & ~gt)) >> (4 * hf);
+        const uint32_t mw[2] = {(uint32_t)mm, (uint32_t)(mm >> 32)};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                const bool ok = (mw[j] >> (8 * (vv >> 2) + (vv & 3))) & 1u;
+                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[j][vv], cl2, -lse2)) : 0.f;
+                sc[j][vv] = p * (dp[j][vv] - dq_d);
+            }
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const bf16x8 pa = pack_acc(sc[s4 >> 1], s4 & 1);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                acc[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 16 * s4 + 8 * hf), pa, acc[dt]);
+        }
+    }
+    if (t0 + oq < D.N) {
+        float* dr = dq + qo * kD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                f32x4 o4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o4[j] = D.tau * acc[dt][4 * v4 + j];
+                *reinterpret_cast<f32x4*>(dr + 32 * dt + acc_row(4 * v4, hf)) = o4;
+            }
     }
 }
 
@@ -1605,7 +1853,7 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       L, gate, reinterpret_cast<bf16*>(out), D)
+                       L, gate, reinterpret_cast<bf16*>(out), nullptr, nullptr, nullptr, D)
 #define STILL_MAIN(H)              \
     do {                           \
         if (nwt == 1)              \
@@ -1620,6 +1868,81 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
     else STILL_MAIN(1);
 #undef STILL_MAIN
 #undef STILL_MAIN1
+    return hipGetLastError();
+}
+
+bool mfma_bwd_supported(const Dims& D) { return mfma_fwd_supported(D); }
+
+hipError_t launch_bwd_lists(const Dims& D, const int32_t* selw, const void* k, const void* v,
+                            void* ksel, void* vsel, int* list_off, const float* wq, const float* wk,
+                            void* wsplit, hipStream_t s) {
+    dim3 grid(D.n_full + 1, D.Hkv, D.B);
+    hipLaunchKernelGGL(bwd_lists_kernel, grid, dim3(256), 0, s, selw, reinterpret_cast<const bf16*>(k),
+                       reinterpret_cast<const bf16*>(v), reinterpret_cast<bf16*>(ksel),
+                       reinterpret_cast<bf16*>(vsel), list_off, wq, wk, reinterpret_cast<bf16*>(wsplit), D);
+    return hipGetLastError();
+}
+
+hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, const void* v,
+                               const void* wsplit, const void* phik, const uint8_t* route,
+                               const void* ksel, const void* vsel, const LinBufs& L,
+                               const float* gate, const int* list_off, const void* dout,
+                               float* stat, hipStream_t s) {
+    const int n = D.Hkv * (kD / 2) * kD;
+    const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
+    const bf16* wql = wqh + n;
+    const int HB = D.G >= 4 ? 4 : D.G;
+    const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
+    const int nwt = D.W / kC;
+#define STILL_STATS1(H, NWT)                                                                     \
+    hipLaunchKernelGGL((hybrid_main_kernel<H, NWT, true>), dim3(nblk), dim3(128 * H), 0, s,     \
+                       reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),      \
+                       reinterpret_cast<const bf16*>(v), wqh, wql,                                \
+                       reinterpret_cast<const bf16*>(phik), route,                              \
+                       reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
+                       L, gate, nullptr, list_off, reinterpret_cast<const bf16*>(dout), stat, D)
+#define STILL_STATS(H)             \
+    do {                           \
+        if (nwt == 1)              \
+            STILL_STATS1(H, 1);    \
+        else if (nwt == 2)         \
+            STILL_STATS1(H, 2);    \
+        else                       \
+            STILL_STATS1(H, 4);    \
+    } while (0)
+    if (HB == 4) STILL_STATS(4);
+    else if (HB == 2) STILL_STATS(2);
+    else STILL_STATS(1);
+#undef STILL_STATS
+#undef STILL_STATS1
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
+                         const uint8_t* route, const void* ksel, const void* vsel,
+                         const int* list_off, const float* stat, float* dq, hipStream_t s) {
+    const int HB = D.G >= 2 ? 2 : 1;
+    const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
+    const int nwt = D.W / kC;
+#define STILL_DQ1(H, NWT)                                                                        \
+    hipLaunchKernelGGL((bwd_dq_kernel<H, NWT>), dim3(nblk), dim3(128 * H), 0, s,                \
+                       reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),      \
+                       reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout),   \
+                       route, reinterpret_cast<const bf16*>(ksel),                                \
+                       reinterpret_cast<const bf16*>(vsel), list_off, stat, dq, D)
+#define STILL_DQ(H)                \
+    do {                           \
+        if (nwt == 1)              \
+            STILL_DQ1(H, 1);       \
+        else if (nwt == 2)         \
+            STILL_DQ1(H, 2);       \
+        else                       \
+            STILL_DQ1(H, 4);       \
+    } while (0)
+    if (HB == 2) STILL_DQ(2);
+    else STILL_DQ(1);
+#undef STILL_DQ
+#undef STILL_DQ1
     return hipGetLastError();
 }
 

@@ -410,7 +410,11 @@ static int bwd_slices(const Dims& D) {
     return n < 1 ? 1 : (int)n;
 }
 
-static BwdWork carve_bwd(const Dims& D, Carver& cv) {
+static bool use_mfma_bwd(const Dims& D, const still_shape* sh) {
+    return !(sh->flags & STILL_FLAG_GENERAL_KERNELS) && mfma_bwd_supported(D);
+}
+
+static BwdWork carve_bwd(const Dims& D, Carver& cv, bool mfma) {
     BwdWork w;
     const size_t BN = (size_t)D.B * D.N, BG = (size_t)D.B * D.Hkv;
     const size_t E1 = (size_t)D.fd * (D.d + 1);
@@ -427,12 +431,31 @@ static BwdWork carve_bwd(const Dims& D, Carver& cv) {
     w.dwpart = cv.take<float>((size_t)w.nslice * D.Hkv * (D.fd / 2) * D.d);
     w.route = cv.take<uint8_t>(BG * D.N);
     w.selw = cv.take<int32_t>(BG * D.n_full * D.lam);
+    w.mfma = mfma;
+    w.ksel = w.vsel = w.phik16 = w.wsplit = nullptr;
+    w.list_off = nullptr;
+    w.lin16 = LinBufs{};
+    if (mfma) {
+        const size_t nlist = BG * (size_t)sel_list_rows(D);
+        w.ksel = cv.take<uint16_t>(nlist * D.d);
+        w.vsel = cv.take<uint16_t>(nlist * D.d);
+        w.list_off = cv.take<int>(BG * (D.n_full + 1));
+        w.phik16 = cv.take<uint16_t>(BG * D.N * D.fd);
+        const size_t ngroups = D.n_full == 0 ? 0 : (size_t)(D.n_full + D.ng - 1) / D.ng;
+        w.lin16.sh = cv.take<uint16_t>(BG * D.n_full * (size_t)D.d * D.fd);
+        w.lin16.lz = cv.take<float>(BG * D.n_full * (size_t)D.fd);
+        w.lin16.ltot = cv.take<float>(BG * ngroups * E1);
+        w.lin16.lcap = cv.take<float>(BG * E1);
+        w.lin16.gh = cv.take<uint16_t>(BG * ngroups * (size_t)D.d * D.fd);
+        w.lin16.gz = cv.take<float>(BG * ngroups * (size_t)D.fd);
+        w.wsplit = cv.take<uint16_t>((size_t)4 * D.Hkv * (D.fd / 2) * D.d);
+    }
     return w;
 }
 
-static size_t bwd_bytes(const Dims& D) {
+static size_t bwd_bytes(const Dims& D, const still_shape* sh) {
     Carver cv(nullptr);
-    carve_bwd(D, cv);
+    carve_bwd(D, cv, use_mfma_bwd(D, sh));
     return cv.off + 256;
 }
 
@@ -466,11 +489,12 @@ static int bwd(const still_shape* sh, const void* q, const void* k, const void* 
     if (!aligned4(gate) || !aligned4(dgate)) return STILL_ERR_INVALID_ARG;
     if (D.lam > 0 && D.n_full > 0 && (!sel_idx || (reinterpret_cast<uintptr_t>(sel_idx) & 3u)))
         return STILL_ERR_INVALID_ARG;
-    if (!ws || ws_bytes < bwd_bytes(D)) return STILL_ERR_WORKSPACE;
-    if (tl.ev && tl.max_ev < bwd_launch_count() + 1) return STILL_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < bwd_bytes(D, sh)) return STILL_ERR_WORKSPACE;
+    const bool mfma = use_mfma_bwd(D, sh);
+    if (tl.ev && tl.max_ev < bwd_launch_count(mfma) + 1) return STILL_ERR_INVALID_ARG;
     void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     Carver cv(wsa);
-    const BwdWork w = carve_bwd(D, cv);
+    const BwdWork w = carve_bwd(D, cv, mfma);
     BwdArgs a;
     a.q = q;
     a.k = k;
@@ -635,7 +659,7 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes) {
     if (!bytes) return STILL_ERR_INVALID_ARG;
     const int st = still::check_shape(shape, false);
     if (st) return st;
-    *bytes = still::bwd_bytes(still::make_dims(shape, shape->seqlen));
+    *bytes = still::bwd_bytes(still::make_dims(shape, shape->seqlen), shape);
     return STILL_OK;
 }
 

@@ -22,7 +22,7 @@ STILL_ROUTE_SHIFT = 1
 # routing criteria (STILL_ROUTE_* of still.h), by name
 ROUTES = {"saliency": 0, "diagonal": 1, "qk": 2, "keynorm": 3, "uniform": 4, "random": 5}
 
-STILL_MAX_LAUNCHES = 16
+STILL_MAX_LAUNCHES = 24
 
 EXPORTED = (
     "still_abi_version", "still_status_str", "still_topk_for_budget",
@@ -379,7 +379,8 @@ def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.T
 
 
 def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6,
-        softmax_scale=0.0, workspace=None, timer: LaunchTimer | None = None, gate=None) -> dict:
+        softmax_scale=0.0, workspace=None, timer: LaunchTimer | None = None, gate=None,
+        general=False) -> dict:
     """still_hybrid_attn_bwd: gradients of sum(dout * out) for the forward
     with the same arguments, under the routing sel_idx [B, Hkv, N/C, lambda]
     (the forward's sel_idx output; None when there is nothing selected).
@@ -389,7 +390,7 @@ def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6
     Hkv = k.shape[2]
     sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
                     chunk=chunk, topk=topk, eps=eps, softmax_scale=softmax_scale, dtype=q.dtype,
-                    feat_dim=2 * wphi_q.shape[1])
+                    feat_dim=2 * wphi_q.shape[1], general=general)
     _expect(q, "q", q.dtype, (B, N, Hq, d))
     _expect(k, "k", q.dtype, (B, N, Hkv, d))
     _expect(v, "v", q.dtype, (B, N, Hkv, d))

@@ -288,8 +288,16 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
  *             when gate_opt is given and this is not NULL; ignored without
  *             a gate
  *   workspace >= still_bwd_workspace_size bytes of device memory
- * Computed by the general kernels for every supported shape; the shape's
- * routing-criterion and kernel flags are accepted and do not matter.  N == 0
+ * For bf16 storage with d = d' = 128, chunk 64, window 64 / 128 / 256 and
+ * 1, 2, 4 or 8 query heads per KV head, the softmax terms run on the
+ * matrix cores: a first pass (the forward's main kernel over compact lists
+ * of the given selection) gives each query's reference, normaliser and
+ * dout . out, and the softmax part of dq is formed from bf16 logit and
+ * dout . v products with dS rounded to bf16, as the forward rounds its
+ * probabilities (gradients to about 1e-2 relative); the other terms and
+ * every other shape use fp32 kernels (about 1e-6).  STILL_FLAG_GENERAL_KERNELS
+ * forces the fp32 kernels everywhere; the routing-criterion flags do not
+ * matter.  N == 0
  * or B == 0 writes zeros to dwphi_q and dwphi_k (when not NULL) and nothing
  * else.  Errors as for the forward; a missing sel_idx where it is needed is
  * STILL_ERR_INVALID_ARG. */
@@ -327,7 +335,7 @@ int still_future_kv_utility(const still_shape* shape, const void* q, const void*
  * launch i.  *n_launches receives n.  Needs max_events >= n + 1, else
  * STILL_ERR_INVALID_ARG before anything is launched; events are created and
  * destroyed by the caller. */
-#define STILL_MAX_LAUNCHES 16
+#define STILL_MAX_LAUNCHES 24
 int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
                                 const float* gate_opt, void* out, float* scores_opt, int32_t* sel_idx_opt,
