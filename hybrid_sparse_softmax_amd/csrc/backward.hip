@@ -979,17 +979,20 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
         if ((e = launch_la_group_scan(D, w.lin16, -1, nullptr, nullptr, s)) != hipSuccess) return e;
         if ((e = mark.fn(mark.ctx, "bwd_stats")) != hipSuccess) return e;
         if ((e = launch_hybrid_stats(D, a.q, a.k, a.v, w.wsplit, w.phik16, w.route, w.ksel, w.vsel,
-                                     w.lin16, a.gate, w.list_off, a.dout, w.stat, s)) != hipSuccess)
+                                     w.lin16, a.gate, w.list_off, a.dout, w.stat, w.phiq, s)) != hipSuccess)
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_dq")) != hipSuccess) return e;
         if ((e = launch_bwd_dq(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.list_off, w.stat,
                                a.dq, s)) != hipSuccess)
             return e;
     }
-    if ((e = mark.fn(mark.ctx, "phi_q")) != hipSuccess) return e;
     // the queries' features carry their gate weights (phi~_q = gamma phi_q), so
-    // every linear term below is the gated one
-    if ((e = launch_phi(D, a.q, D.Hq, D.G, a.wq, a.gate, w.phiq, s)) != hipSuccess) return e;
+    // every linear term below is the gated one (the matrix-core first pass
+    // wrote them already)
+    if (!w.mfma) {
+        if ((e = mark.fn(mark.ctx, "phi_q")) != hipSuccess) return e;
+        if ((e = launch_phi(D, a.q, D.Hq, D.G, a.wq, a.gate, w.phiq, s)) != hipSuccess) return e;
+    }
     if ((e = mark.fn(mark.ctx, "phi_k")) != hipSuccess) return e;
     if ((e = launch_phi(D, a.k, D.Hkv, 1, a.wk, nullptr, w.phik, s)) != hipSuccess) return e;
     if ((e = mark.fn(mark.ctx, "la_chunk")) != hipSuccess) return e;
@@ -1056,7 +1059,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 
 }  // namespace
 
-int bwd_launch_count(bool mfma) { return mfma ? 21 : 16; }
+int bwd_launch_count(bool mfma) { return mfma ? 20 : 16; }
 
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s,
                       BwdMark mark) {

@@ -106,12 +106,13 @@ hipError_t launch_bwd_lists(const Dims& D, const int32_t* selw, const void* k, c
                             void* ksel, void* vsel, int* list_off, const float* wq, const float* wk,
                             void* wsplit, hipStream_t s);
 // the forward's main kernel writing (m, l, D = dout . out, c) per query head
-// to stat [B, N, Hq, 4] instead of the output
+// to stat [B, N, Hq, 4] instead of the output, and the gated NP-Map features
+// of the queries to phiq [B, N, Hq, d'] (fp32)
 hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, const void* v,
                                const void* wsplit, const void* phik, const uint8_t* route,
                                const void* ksel, const void* vsel, const LinBufs& L,
                                const float* gate, const int* list_off, const void* dout,
-                               float* stat, hipStream_t s);
+                               float* stat, float* phiq, hipStream_t s);
 // softmax part of dq (fp32, overwritten)
 hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,

@@ -870,7 +870,9 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&o)[4], f32x16 (&sc)[2], co
 // (else 0).  list_off (when not null) gives the compact rows of chunk c as
 // rows list_off[c] .. list_off[c + 1] - 1 of (b, g) (n_full + 1 entries, the
 // last the open chunk's copy), for lists built from a given selection whose
-// chunks may hold fewer than lam rows.
+// chunks may hold fewer than lam rows.  STATS also writes each query head's
+// gated NP-Map features gamma phi_q (fp32, feature order) to phiq_out (zeros
+// for queries with no routed token).
 template <int HB, int NWT, bool STATS = false>
 __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -878,7 +880,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, LinBufs L,
     const float* __restrict__ gate, bf16* __restrict__ out, const int* __restrict__ list_off,
-    const bf16* __restrict__ dout, float* __restrict__ stat, Dims D) {
+    const bf16* __restrict__ dout, float* __restrict__ stat, float* __restrict__ phiq_out, Dims D) {
     constexpr int NW = HB * 2;  // waves
     const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
@@ -1053,6 +1055,23 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 #pragma unroll
                     for (int vv = 0; vv < 16; ++vv) phi[0][sgn][f2][vv] *= gw;
         }
+        if constexpr (STATS) {
+            // this lane's 64 features of its query: 64 sgn + 32 f2 + acc_row(..)
+            if (t0 + oq < D.N) {
+                float* pr = phiq_out + (((size_t)b * D.N + t0 + oq) * D.Hq + h) * kD;
+#pragma unroll
+                for (int sgn = 0; sgn < 2; ++sgn)
+#pragma unroll
+                    for (int f2 = 0; f2 < 2; ++f2)
+#pragma unroll
+                        for (int v4 = 0; v4 < 4; ++v4) {
+                            f32x4 x4;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) x4[j] = phi[0][sgn][f2][4 * v4 + j];
+                            *reinterpret_cast<f32x4*>(pr + 64 * sgn + 32 * f2 + acc_row(4 * v4, hf)) = x4;
+                        }
+            }
+        }
 
         bf16x8 phb[2][2][2];  // [sgn][ft][s2]
 #pragma unroll
@@ -1154,6 +1173,14 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         }
     }
 
+    if constexpr (STATS) {
+        if (c < NWT && t0 + oq < D.N) {  // no routed token yet: no linear term
+            float* pr = phiq_out + (((size_t)b * D.N + t0 + oq) * D.Hq + h) * kD;
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int x = 0; x < 16; ++x) *reinterpret_cast<f32x4*>(pr + 32 * (x >> 2) + acc_row(4 * (x & 3), hf)) = z4;
+        }
+    }
     // A query with no linear mass (t < W, or every routed token of its
     // chunks selected) has nothing at the linear reference 0, so its
     // reference need not stay >= 0: at the first tile with a key it can see,
@@ -1853,7 +1880,7 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       L, gate, reinterpret_cast<bf16*>(out), nullptr, nullptr, nullptr, D)
+                       L, gate, reinterpret_cast<bf16*>(out), nullptr, nullptr, nullptr, nullptr, D)
 #define STILL_MAIN(H)              \
     do {                           \
         if (nwt == 1)              \
@@ -1887,7 +1914,7 @@ hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, cons
                                const void* wsplit, const void* phik, const uint8_t* route,
                                const void* ksel, const void* vsel, const LinBufs& L,
                                const float* gate, const int* list_off, const void* dout,
-                               float* stat, hipStream_t s) {
+                               float* stat, float* phiq, hipStream_t s) {
     const int n = D.Hkv * (kD / 2) * kD;
     const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
     const bf16* wql = wqh + n;
@@ -1900,7 +1927,7 @@ hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, cons
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       L, gate, nullptr, list_off, reinterpret_cast<const bf16*>(dout), stat, D)
+                       L, gate, nullptr, list_off, reinterpret_cast<const bf16*>(dout), stat, phiq, D)
 #define STILL_STATS(H)             \
     do {                           \
         if (nwt == 1)              \
