@@ -19,17 +19,16 @@ LIB = os.path.join(OUT_DIR, "libstill.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["still_api.cpp", "general.hip", "decode.hip", "decode_fast.hip", "prefill_mfma.hip",
-           "backward.hip", "utility.hip"]
+           "backward.hip", "backward_mfma.hip", "utility.hip"]
+# sources whose matrix-core accumulators stay live across a whole loop and are
+# best left to the compiler's register-file choice (accumulation registers)
+FREE_ACC = {"backward_mfma.hip"}
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in ordinary VGPRs: with the default heuristic the
-    # main kernel's loop copied its whole accumulator tile between register
-    # files on every iteration
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
@@ -37,7 +36,11 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    # keep MFMA accumulators in ordinary VGPRs: with the default heuristic the
+    # forward's main loop copied its whole accumulator tile between register
+    # files on every iteration
+    extra = [] if src in FREE_ACC else ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")

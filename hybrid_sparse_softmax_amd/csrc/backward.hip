@@ -535,8 +535,10 @@ __device__ __forceinline__ void key_group_softmax(const T* __restrict__ q, const
 //   dv_j = U_j^T phi_k(j),  dphi_k(j) = U_j v_j - u_j
 // (U_j: the inclusive suffix sum from the first chunk after j + W's chunk,
 // plus the queries of j + W's chunk from j + W on, taken one by one).
-// Writes dk (softmax part), dv and dphi_k of its keys.
-template <typename T, int DD>
+// Writes dk (softmax part), dv and dphi_k of its keys.  LA_ONLY (the
+// matrix-core path): only the linear terms; writes dv (their part) and
+// dphi_k, and leaves dk and the softmax terms to the matrix-core kernels.
+template <typename T, int DD, bool LA_ONLY = false>
 __global__ __launch_bounds__(64) void bwd_key_win_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
@@ -565,7 +567,7 @@ __global__ __launch_bounds__(64) void bwd_key_win_kernel(
     for (int i = 0; i < kKB; ++i)
 #pragma unroll
         for (int p = 0; p < PL; ++p) dka[i][p] = dva[i][p] = dfa[i][p] = 0.f;
-    if (D.W > 0)
+    if (D.W > 0 && !LA_ONLY)
         key_group_softmax<T, DD>(q, dout, stat, ks, vs, jk, j0, min(D.N - 1, j0 + kKB - 1 + D.W - 1),
                                  0, b, g, D, lane, dka, dva);
     // linear part, one pass per chunk c0 holding some key's first linear
@@ -689,7 +691,7 @@ __global__ __launch_bounds__(64) void bwd_key_win_kernel(
 #pragma unroll
         for (int p = 0; p < PL; ++p) {
             const size_t e = koff(jk[i]) * DD + lane + kWave * p;
-            dk[e] = D.tau * dka[i][p];
+            if (!LA_ONLY) dk[e] = D.tau * dka[i][p];
             dv[e] = dva[i][p];
             dphik[e] = dfa[i][p];
         }
@@ -1022,6 +1024,23 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     STILL_STEP("bwd_suffix",
                hipLaunchKernelGGL(bwd_suffix_kernel, dim3((D.fd * (D.d + 1) + 255) / 256, D.Hkv, D.B),
                                   dim3(256), 0, s, w.ust, D));
+    if (w.mfma) {
+        // linear terms first (dv, dphi_k), then the softmax terms on the matrix
+        // cores: window keys (write dk, add to dv), then selected keys (add)
+        STILL_STEP("bwd_key_la",
+                   hipLaunchKernelGGL((bwd_key_win_kernel<T, DD, true>),
+                                      dim3((D.N + kKB - 1) / kKB * D.Hkv * D.B), dim3(64), 0, s, q, k,
+                                      v, dout, w.phiq, w.phik, w.route, w.stat, w.ust, a.dk, a.dv,
+                                      w.dphik, D));
+        if ((e = mark.fn(mark.ctx, "bwd_kv_win")) != hipSuccess) return e;
+        if ((e = launch_bwd_kv(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw, w.list_off,
+                               w.stat, a.dk, a.dv, 0, s)) != hipSuccess)
+            return e;
+        if ((e = mark.fn(mark.ctx, "bwd_kv_sel")) != hipSuccess) return e;
+        if ((e = launch_bwd_kv(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw, w.list_off,
+                               w.stat, a.dk, a.dv, 1, s)) != hipSuccess)
+            return e;
+    } else {
     STILL_STEP("bwd_key_win",
                hipLaunchKernelGGL((bwd_key_win_kernel<T, DD>), dim3((D.N + kKB - 1) / kKB * D.Hkv * D.B),
                                   dim3(64), 0, s, q, k, v, dout, w.phiq, w.phik, w.route, w.stat,
@@ -1032,6 +1051,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
                                       dim3((D.n_full * D.lam + kSW * kKB - 1) / (kSW * kKB) * D.Hkv * D.B),
                                       dim3(kSW * kWave),
                                       0, s, q, k, v, dout, w.selw, w.stat, a.dk, a.dv, D));
+    }
     const int ntok = D.B * D.N, half = D.fd / 2;
 #define STILL_NP_VJP_Q(GM)                                                                       \
     hipLaunchKernelGGL((np_vjp_kernel<T, DD, GM>), dim3(ntok, D.Hkv), dim3(64), 0, s, q, a.wq, w.dphiq, \
@@ -1059,7 +1079,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 
 }  // namespace
 
-int bwd_launch_count(bool mfma) { return mfma ? 20 : 16; }
+int bwd_launch_count(bool mfma) { return mfma ? 21 : 16; }
 
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s,
                       BwdMark mark) {

@@ -113,6 +113,12 @@ hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, cons
                                const void* ksel, const void* vsel, const LinBufs& L,
                                const float* gate, const int* list_off, const void* dout,
                                float* stat, float* phiq, hipStream_t s);
+// softmax part of dk and dv: phase 0 the window keys (dk written, dv added
+// to), phase 1 the selected keys over the compact rows (both added to)
+hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
+                         const uint8_t* route, const void* ksel, const void* vsel,
+                         const int32_t* selw, const int* list_off, const float* stat, float* dk,
+                         float* dv, int phase, hipStream_t s);
 // softmax part of dq (fp32, overwritten)
 hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,

@@ -28,24 +28,19 @@
 
 #include "launch.h"
 #include "mfma_common.h"
+#include "mfma_tiles.h"
 
 namespace still {
 
 namespace {
-typedef __bf16 bf16;
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+using namespace mt;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kC = 64;          // chunk = window
-constexpr int kD = 128;         // head_dim = NP-Map feature dim
-constexpr int kKS = kD + 8;     // LDS row stride (elements) of a K tile
-constexpr int kVS = kC + 8;     // LDS row stride (elements) of a transposed V tile
 constexpr int kFS = kC + 4;     // LDS row stride (floats) of transposed phi_k
 constexpr int kHS = kD + 8;     // LDS row stride (elements) of a staged state's bf16 parts
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;   // rescale only when the running max grows by more (log2 units)
 
 enum { kModePrev = 0, kModeDiag = 1, kModeSparse = 2 };
@@ -62,44 +57,6 @@ __device__ __forceinline__ void load_q(const bf16* __restrict__ q, const Dims& D
         const bf16* row = q + (((size_t)b * D.N + t) * D.Hq + h) * kD + 8 * hf;
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[qt][s] = ld_bf8(row + 16 * s);
-    }
-}
-
-// 64 rows of a row-major bf16 matrix (row stride ld) into LDS, row-major with
-// stride kKS; rows >= nvalid are zero.
-__device__ __forceinline__ void load_k_tile(const bf16* __restrict__ src, size_t ld, int nvalid,
-                                            bf16* __restrict__ dst, int tid, int nthr) {
-    for (int x = tid; x < kC * 16; x += nthr) {
-        const int row = x >> 4, piece = x & 15;
-        const bf16x8 val = row < nvalid ? ld_bf8(src + (size_t)row * ld + 8 * piece) : zero_bf8();
-        st_bf8(dst + row * kKS + 8 * piece, val);
-    }
-}
-
-// 64 rows x 128 columns of a row-major bf16 matrix into LDS transposed:
-// dst[col * kVS + kperm(row)]; rows >= nvalid are zero.
-__device__ __forceinline__ void load_vt_tile(const bf16* __restrict__ src, size_t ld, int nvalid,
-                                             bf16* __restrict__ dst, int tid, int nthr) {
-    for (int x = tid; x < 16 * 16; x += nthr) {
-        // rows 4kq..4kq+3, columns 8oct..8oct+7; consecutive threads fill one
-        // LDS row (no bank conflicts on the transposed stores)
-        const int kq = x & 15, oct = x >> 4;
-        bf16x8 r[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = 4 * kq + rr;
-            r[rr] = row < nvalid ? ld_bf8(src + (size_t)row * ld + 8 * oct) : zero_bf8();
-        }
-        const int pos = kperm(4 * kq);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 t4;
-            t4[0] = r[0][e];
-            t4[1] = r[1][e];
-            t4[2] = r[2][e];
-            t4[3] = r[3][e];
-            *reinterpret_cast<bf16x4*>(dst + (8 * oct + e) * kVS + pos) = t4;
-        }
     }
 }
 
