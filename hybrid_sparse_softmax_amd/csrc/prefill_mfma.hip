@@ -1165,19 +1165,15 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     // rk counts for the lane's query when bit rk of (rk > oq ? hi_m : lo_m)
     // is set.
     auto softmax_mask = [&](int i, f32x16 (&sc)[2]) -> bool {
-        uint64_t hi_m, lo_m;
-        if (i == 0) {  // chunk c-NWT: window keys (offset above the query's) and routed selected keys
-            hi_m = ~0ull;
-            lo_m = selmask;
-        } else if (i == NWT) {  // chunk c: causal
-            hi_m = 0ull;
-            lo_m = ~0ull;
-        } else if (i < NWT) {  // chunks c-NWT+1 .. c-1: inside every query's window
-            hi_m = lo_m = ~0ull;
-        } else {
-            const int nv = min(kC, nrows - (i - NWT - 1) * kC);
-            hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
-        }
+        // chunk c-NWT (i = 0): window keys (offset above the query's) and
+        // routed selected keys; chunk c (i = NWT): causal; chunks between:
+        // inside every query's window; compact rows: the valid ones.  Written
+        // as selects on wave-uniform values (no branches).
+        const int nvc = nrows - (i - NWT - 1) * kC;
+        const uint64_t part = nvc >= kC ? ~0ull : (1ull << (nvc & 63)) - 1ull;
+        const bool win = i <= NWT;
+        const uint64_t hi_m = win ? (i == NWT ? 0ull : ~0ull) : part;
+        const uint64_t lo_m = win ? (i == 0 ? selmask : ~0ull) : part;
         if ((hi_m & lo_m) != ~0ull) {
             // edge tiles only: masked key rows drop out of the softmax.  The
             // lane's combined mask, shifted down by 4 hf, holds the bit of
@@ -1264,6 +1260,17 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         // iteration's barrier).  The first value product runs on zero
         // probabilities over the zero-filled spare V buffer.
         const unsigned lds0 = (unsigned)(size_t)(lds_void*)smem;
+        // first row of tile i in k / v or the compact lists (every tile has 64
+        // readable rows ldkv apart): window chunks c-NWT+i (chunk c, when
+        // incomplete, from its copy), then compact rows 64 (i - NWT - 1) on
+        const int64_t tstride = (int64_t)kC * (int64_t)ldkv;
+        const int64_t win0 = (((int64_t)b * D.N + (int64_t)(c - NWT) * kC) * D.Hkv + g) * kD;
+        const bool open_c = D.N - t0 < kC;
+        auto tile_ptr = [&](int i, bool is_k) -> const bf16* {
+            if (i > NWT) return (is_k ? kb : vb) + (int64_t)(i - NWT - 1) * tstride;
+            if (i == NWT && open_c) return (is_k ? kb : vb) + (int64_t)tail_row * (int64_t)ldkv;
+            return (is_k ? k : v) + win0 + (int64_t)i * tstride;
+        };
         auto rows_of = [&](int i, bool is_k, int& ld, int& nv) -> const bf16* {
             size_t off, ld64;
             bool cp;
@@ -1311,32 +1318,18 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         // staging in steps 1-5, well before either barrier point.
         auto iteration = [&](int s, f32x16 (&sc)[2], bf16x8 (&pb)[4], f32x16 (&sn)[2], bf16x8 (&pn)[4])
                              __attribute__((always_inline)) {
-            // softmax of tile s: masking (edge tiles only), then the exps
-            // against the current reference m2 in the stream below; their
-            // sums (ls - ls0) are checked after it
-            softmax_mask(s, sc);
-            const float ls0 = ls;
-            // staging sources: K of s+2 (or the last tile again), V of s
-            int kld, knv, vld, vnv;
-            const bf16* ksrc = rows_of(min(s + 2, ntile - 1), true, kld, knv);
-            const bf16* vsrc = rows_of(s, false, vld, vnv);
-            const unsigned kdst = lds0 + 2u * (s & 1) * kKTile;
-            // V buffers of tiles s (staged now) and s-1 (read now), as scalars
-            const int vcur = __builtin_amdgcn_readfirstlane(s % 3);
-            const int vprv = __builtin_amdgcn_readfirstlane((s + 2) % 3);
-            const unsigned vdst = lds0 + 2u * (2 * kKTile + vcur * kVTile);
             // One stream of 16 steps pinned by scheduling barriers.  Steps 0-7
             // take the logits of tile s+1 (two products each: keys 0-31 and
             // 32-63), steps 8-15 the value product of tile s-1 (two each);
             // every step does the exps of two elements of tile s and issues
             // the operand reads of the step two ahead; some steps issue a
-            // staging instruction.
-            const bf16* vt = smem + 2 * kKTile + vprv * kVTile;
+            // staging instruction.  The reads of the first two steps go out
+            // before the iteration's scalar set-up, which runs under them.
             const bf16* kt = kbuf(s + 1) + col * kKS + 8 * hf;
-            sn[0] = zero16();
-            sn[1] = zero16();
-            const float nm = -m2;
-            float pt[8];
+            // V buffers of tiles s (staged now) and s-1 (read now), as scalars
+            const int vcur = __builtin_amdgcn_readfirstlane(s % 3);
+            const int vprv = __builtin_amdgcn_readfirstlane((s + 2) % 3);
+            const bf16* vt = smem + 2 * kKTile + vprv * kVTile;
             bf16x8 a0[16], a1[16];
             auto operands = [&](int st) __attribute__((always_inline)) {
                 if (st < 8) {
@@ -1350,6 +1343,22 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
             };
             operands(0);
             operands(1);
+            __builtin_amdgcn_sched_barrier(0);
+            // softmax of tile s: masking (edge tiles only), then the exps
+            // against the current reference m2 in the stream below; their
+            // sums (ls - ls0) are checked after it
+            softmax_mask(s, sc);
+            const float ls0 = ls;
+            // staging destinations and sources: K of s+2 (or the last tile
+            // again), V of s
+            const bf16* ksrc = tile_ptr(min(s + 2, ntile - 1), true);
+            const bf16* vsrc = tile_ptr(s, false);
+            const unsigned kdst = lds0 + 2u * (s & 1) * kKTile;
+            const unsigned vdst = lds0 + 2u * (2 * kKTile + vcur * kVTile);
+            sn[0] = zero16();
+            sn[1] = zero16();
+            const float nm = -m2;
+            float pt[8];
 #pragma unroll
             for (int st = 0; st < 16; ++st) {
                 if (st + 2 < 16) operands(st + 2);
