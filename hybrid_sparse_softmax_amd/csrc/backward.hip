@@ -38,6 +38,10 @@
 //   np_vjp_kernel      NP-Map backward per (token, KV group): dx += ..., du
 //   dw_partial_kernel  dP = sum du x^T over a slice of tokens
 //   dw_reduce_kernel   sum of the slices
+// On the matrix-core path (bf16, d = 128, chunk 64) the statistics, the
+// softmax parts of dq, dk and dv, the NP-Map backward and the projection
+// gradients run as MFMA kernels (prefill_mfma.hip, backward_mfma.hip); the
+// linear terms stay here.
 #include "device_common.h"
 #include "launch.h"
 #include "row_ops.h"
@@ -1053,6 +1057,24 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
                                       0, s, q, k, v, dout, w.selw, w.stat, a.dk, a.dv, D));
     }
     const int ntok = D.B * D.N, half = D.fd / 2;
+    const int nw = D.Hkv * half * DD;
+    if (w.mfma) {
+        // NP-Map backward and projection gradients on the matrix cores (du in
+        // bf16 in the du buffers)
+        if ((e = mark.fn(mark.ctx, "np_vjp_q")) != hipSuccess) return e;
+        if ((e = launch_np_bwd(D, a.q, w.wsplit, 0, w.dphiq, a.dq, w.duq, s)) != hipSuccess) return e;
+        if ((e = mark.fn(mark.ctx, "np_vjp_k")) != hipSuccess) return e;
+        if ((e = launch_np_bwd(D, a.k, w.wsplit, 1, w.dphik, a.dk, w.duk, s)) != hipSuccess) return e;
+        if ((e = mark.fn(mark.ctx, "dw_q")) != hipSuccess) return e;
+        if ((e = launch_dw_mfma(D, a.q, 0, w.duq, w.dwpart, w.nslice, s)) != hipSuccess) return e;
+        STILL_STEP("dw_q_reduce", hipLaunchKernelGGL(dw_reduce_kernel, dim3((nw + 255) / 256), dim3(256),
+                                                     0, s, w.dwpart, a.dwq, nw, w.nslice));
+        if ((e = mark.fn(mark.ctx, "dw_k")) != hipSuccess) return e;
+        if ((e = launch_dw_mfma(D, a.k, 1, w.duk, w.dwpart, w.nslice, s)) != hipSuccess) return e;
+        STILL_STEP("dw_k_reduce", hipLaunchKernelGGL(dw_reduce_kernel, dim3((nw + 255) / 256), dim3(256),
+                                                     0, s, w.dwpart, a.dwk, nw, w.nslice));
+        return hipSuccess;
+    }
 #define STILL_NP_VJP_Q(GM)                                                                       \
     hipLaunchKernelGGL((np_vjp_kernel<T, DD, GM>), dim3(ntok, D.Hkv), dim3(64), 0, s, q, a.wq, w.dphiq, \
                        a.dq, w.duq, D.Hq, D.G, D.fd)
@@ -1065,7 +1087,6 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     STILL_STEP("dw_q",
                hipLaunchKernelGGL((dw_partial_kernel<T, DD>), dim3(D.Hkv, w.nslice), dim3(DD), 0, s,
                                   q, w.duq, w.dwpart, ntok, D.Hq, D.G, half, w.nslice));
-    const int nw = D.Hkv * half * DD;
     STILL_STEP("dw_q_reduce", hipLaunchKernelGGL(dw_reduce_kernel, dim3((nw + 255) / 256), dim3(256),
                                                  0, s, w.dwpart, a.dwq, nw, w.nslice));
     STILL_STEP("dw_k",

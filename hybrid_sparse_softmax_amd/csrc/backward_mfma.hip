@@ -31,6 +31,8 @@ namespace still {
 namespace {
 using namespace mt;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kKW = 4;  // waves per block: 128 keys
 
 // staged query tile of one head: rows t0 .. t0 + 63 (zero past N)
@@ -257,6 +259,254 @@ __global__ __launch_bounds__(kKW * 64) void bwd_kv_selected_kernel(
         }
 }
 
+
+// ---------------------------------------------------------------------------
+// NP-Map backward on the matrix cores.  The feature map of a row x (a query
+// or key head; full text Sec. 3.2) with its head group's projection P
+// (d/2 x d):  u = P x,  z = ||x|| u / ||u||,  phi = [softmax(z); softmax(-z)].
+// Given dphi (the gradient w.r.t. the ungated phi):
+//   dz = phi+ (dphi+ - <phi+, dphi+>) - phi- (dphi- - <phi-, dphi->)
+//   du = ||x|| (dz - uh <uh, dz>) / ||u||   (uh = u / ||u||)
+//   dx += P^T du + (<uh, dz> / ||x||) x,    dP += du x^T.
+// Rows of KV group g are rho = tok * hpp + hh (x row tok * H + g * hpp +
+// hh).  One wave takes 32 rows at a time: U^T = P X^T on the matrix cores
+// with P as bf16 high + low parts (fp32-grade u, as the forward's map), the
+// feature softmaxes and sums along the accumulator columns, dX^T = P^T dU^T
+// (bf16 P and du), dx updated in place; du goes out as bf16 for the
+// projection gradient.
+// ---------------------------------------------------------------------------
+constexpr int kNPW = 4;  // waves per block
+constexpr int kNPT = 4;  // 32-row tiles per wave
+
+__global__ __launch_bounds__(kNPW * 64) __attribute__((amdgpu_waves_per_eu(2))) void np_bwd_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ phi_hi, const bf16* __restrict__ phi_lo,
+    const float* __restrict__ dphi, float* __restrict__ dx, bf16* __restrict__ du_out, int ntok,
+    int H, int hpp) {
+    constexpr int kF = kD / 2;  // 64 features per sign
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __shared__ __align__(16) bf16 ph[kF * kKS];
+    __shared__ __align__(16) bf16 pl[kF * kKS];
+    __shared__ __align__(16) bf16 pt[kD * kVS];  // P^T, features in kperm order
+    const size_t po = (size_t)g * kF * kD;
+    load_k_tile(phi_hi + po, kD, kF, ph, tid, kNPW * 64);
+    load_k_tile(phi_lo + po, kD, kF, pl, tid, kNPW * 64);
+    load_vt_tile(phi_hi + po, kD, kF, pt, tid, kNPW * 64);
+    __syncthreads();
+    const int nrho = ntok * hpp;
+#pragma unroll 1
+    for (int tt = 0; tt < kNPT; ++tt) {
+        // the projection fragments are read from LDS in every tile rather
+        // than held in registers across tiles
+        __asm__ volatile("" ::: "memory");
+        const int rho0 = ((blockIdx.x * kNPW + wave) * kNPT + tt) * 32;
+        if (rho0 >= nrho) break;  // wave-uniform
+        const bool act = rho0 + col < nrho;
+        const int rho = min(rho0 + col, nrho - 1);
+        const size_t xr = (size_t)(rho / hpp) * H + (size_t)g * hpp + rho % hpp;
+        bf16x8 xb[8];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) xb[st] = ld_bf8(x + xr * kD + 16 * st + 8 * hf);
+        f32x16 u[2];
+        u[0] = zero16();
+        u[1] = zero16();
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int ft = 0; ft < 2; ++ft) {
+                u[ft] = mfma32(ld_bf8(ph + (32 * ft + col) * kKS + 16 * st + 8 * hf), xb[st], u[ft]);
+                u[ft] = mfma32(ld_bf8(pl + (32 * ft + col) * kKS + 16 * st + 8 * hf), xb[st], u[ft]);
+            }
+        // column sums over the row's 64 features: this lane's 32 plus the other half's
+        float nx = 0.f, nu = 0.f, umax = -__builtin_inff(), umin = __builtin_inff();
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2 x2 = {xb[st][2 * j], xb[st][2 * j + 1]};
+                nx = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, nx, false);
+            }
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                nu = fmaf(u[ft][vv], u[ft][vv], nu);
+                umax = vmax(umax, u[ft][vv]);
+                umin = vmin(umin, u[ft][vv]);
+            }
+        nx = sqrtf(nx + xor32(nx));
+        nu = sqrtf(nu + xor32(nu));
+        umax = vmax(umax, xor32(umax));
+        umin = vmin(umin, xor32(umin));
+        const float iu = nu > 0.f ? 1.f / nu : 0.f;  // uh = u iu (0 when u = 0)
+        const float scl = nx * iu * kLog2e;           // z log2(e) = scl u
+        float ep[2][16], en[2][16], sp = 0.f, sn = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                ep[ft][vv] = __builtin_amdgcn_exp2f(fmaf(u[ft][vv], scl, -scl * umax));
+                en[ft][vv] = __builtin_amdgcn_exp2f(fmaf(u[ft][vv], -scl, scl * umin));
+                sp += ep[ft][vv];
+                sn += en[ft][vv];
+            }
+        // dphi of the row (feature order: 64 of softmax(z), then 64 of
+        // softmax(-z)); <phi+-, dphi+-> from the unnormalised weights, then
+        // dz with dphi read again (cache hits) to keep registers low
+        const float* dr = dphi + xr * kD;
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int f = 32 * ft + acc_row(4 * v4, hf);
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(dr + f);
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(dr + kF + f);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sa = fmaf(ep[ft][4 * v4 + j], a4[j], sa);
+                    sb = fmaf(en[ft][4 * v4 + j], b4[j], sb);
+                }
+            }
+        sp = 1.f / (sp + xor32(sp));
+        sn = 1.f / (sn + xor32(sn));
+        sa = (sa + xor32(sa)) * sp;
+        sb = (sb + xor32(sb)) * sn;
+        // dz (in ep), then <uh, dz>
+        float dnx = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int f = 32 * ft + acc_row(4 * v4, hf);
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(dr + f);
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(dr + kF + f);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int vv = 4 * v4 + j;
+                    const float z = ep[ft][vv] * sp * (a4[j] - sa) - en[ft][vv] * sn * (b4[j] - sb);
+                    ep[ft][vv] = z;
+                    dnx = fmaf(z, u[ft][vv] * iu, dnx);
+                }
+            }
+        dnx += xor32(dnx);
+        float (&dz)[2][16] = ep;
+        // du = ||x|| (dz - uh <uh, dz>) / ||u||
+        f32x16 dua[2];
+        const float cu = nx * iu;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) dua[ft][vv] = cu * (dz[ft][vv] - dnx * u[ft][vv] * iu);
+        // dX^T = P^T dU^T (rows: dims 32 dt + acc_row, column: the row rho)
+        f32x16 dxt[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) dxt[dt] = zero16();
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const bf16x8 pd = pack_acc(dua[ft], s2);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    dxt[dt] = mfma32(ld_bf8(pt + (32 * dt + col) * kVS + 32 * ft + 16 * s2 + 8 * hf), pd, dxt[dt]);
+            }
+        if (!act) continue;
+        const float rn = nx > 0.f ? dnx / nx : 0.f;
+        float* dxr = dx + xr * kD;
+        const bf16* xrow = x + xr * kD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int e = 32 * dt + acc_row(4 * v4, hf);
+                f32x4 a4 = *reinterpret_cast<const f32x4*>(dxr + e);
+                const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(xrow + e);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a4[j] += dxt[dt][4 * v4 + j] + rn * (float)x4[j];
+                *reinterpret_cast<f32x4*>(dxr + e) = a4;
+            }
+        bf16* dur = du_out + ((size_t)g * nrho + rho) * kF;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                bf16x4 d4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d4[j] = (bf16)dua[ft][4 * v4 + j];
+                *reinterpret_cast<bf16x4*>(dur + 32 * ft + acc_row(4 * v4, hf)) = d4;
+            }
+    }
+}
+
+// Projection gradient dP[g] = sum over the rows rho of group g of du x^T,
+// partial over one slice of rows per block: 64-row tiles of dU and X staged
+// transposed (rows as the contraction index), each wave one 32-feature by
+// 64-dim quarter of dP.
+__global__ __launch_bounds__(256) void dw_mfma_kernel(const bf16* __restrict__ x,
+                                                      const bf16* __restrict__ du,
+                                                      float* __restrict__ part, int ntok, int H,
+                                                      int hpp, int nslice) {
+    constexpr int kF = kD / 2;
+    const int sl = blockIdx.x, g = blockIdx.y, G8 = gridDim.y;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ftile = wave & 1, dpair = wave >> 1;
+    const int nrho = ntok * hpp;
+    const int per = ((nrho + nslice - 1) / nslice + kC - 1) / kC * kC;
+    const int r0 = sl * per, r1 = min(nrho, r0 + per);
+    __shared__ __align__(16) bf16 dut[kF * kVS];
+    __shared__ __align__(16) bf16 xt[kD * kVS];
+    f32x16 acc[2];
+    acc[0] = zero16();
+    acc[1] = zero16();
+    const bf16* dug = du + (size_t)g * nrho * kF;
+    for (int rb = r0; rb < r1; rb += kC) {
+        const int nv = min(kC, r1 - rb);
+        __syncthreads();
+        // dU^T: dut[f * kVS + kperm(r)] = du[rb + r][f]
+        load_vt_tile64(dug + (size_t)rb * kF, kF, nv, dut, tid, 256);
+        // X^T: xt[e * kVS + kperm(r)] = x[row(rb + r)][e]
+        for (int xi = tid; xi < 16 * 16; xi += 256) {
+            const int kq = xi & 15, oct = xi >> 4;
+            bf16x8 rr[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int r = 4 * kq + q4;
+                const int rho = rb + r;
+                const size_t xr = (size_t)(rho / hpp) * H + (size_t)g * hpp + rho % hpp;
+                rr[q4] = r < nv ? ld_bf8(x + xr * kD + 8 * oct) : zero_bf8();
+            }
+            const int pos = kperm(4 * kq);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16x4 t4;
+                t4[0] = rr[0][e];
+                t4[1] = rr[1][e];
+                t4[2] = rr[2][e];
+                t4[3] = rr[3][e];
+                *reinterpret_cast<bf16x4*>(xt + (8 * oct + e) * kVS + pos) = t4;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a = ld_bf8(dut + (32 * ftile + col) * kVS + 16 * ks + 8 * hf);
+#pragma unroll
+            for (int jd = 0; jd < 2; ++jd)
+                acc[jd] = mfma32(a, ld_bf8(xt + (32 * (2 * dpair + jd) + col) * kVS + 16 * ks + 8 * hf), acc[jd]);
+        }
+    }
+    // rows f = 32 ftile + acc_row, column e = 32 (2 dpair + jd) + col
+    float* out = part + ((size_t)sl * G8 + g) * kF * kD;
+#pragma unroll
+    for (int jd = 0; jd < 2; ++jd)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv)
+            out[(size_t)(32 * ftile + acc_row(vv, hf)) * kD + 32 * (2 * dpair + jd) + col] = acc[jd][vv];
+}
+
 }  // namespace
 
 hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
@@ -289,6 +539,31 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
     else if (nwt == 2) STILL_KVS(2);
     else STILL_KVS(4);
 #undef STILL_KVS
+    return hipGetLastError();
+}
+
+// NP-Map backward of one side (q: H = Hq, hpp = G, projection parts 0 / 1;
+// k: H = Hkv, hpp = 1, parts 2 / 3 of wsplit) and its projection gradient
+hipError_t launch_np_bwd(const Dims& D, const void* x, const void* wsplit, int side, const float* dphi,
+                         float* dx, void* du16, hipStream_t s) {
+    const int H = side == 0 ? D.Hq : D.Hkv, hpp = side == 0 ? D.G : 1;
+    const size_t part = (size_t)D.Hkv * (kD / 2) * kD;
+    const bf16* ws = reinterpret_cast<const bf16*>(wsplit) + (size_t)(2 * side) * part;
+    const int ntok = D.B * D.N;
+    const int rows_per_blk = kNPW * kNPT * 32;
+    const unsigned nblk = (unsigned)((ntok * hpp + rows_per_blk - 1) / rows_per_blk);
+    hipLaunchKernelGGL(np_bwd_kernel, dim3(nblk, D.Hkv), dim3(kNPW * 64), 0, s,
+                       reinterpret_cast<const bf16*>(x), ws, ws + part, dphi, dx,
+                       reinterpret_cast<bf16*>(du16), ntok, H, hpp);
+    return hipGetLastError();
+}
+
+hipError_t launch_dw_mfma(const Dims& D, const void* x, int side, const void* du16, float* part,
+                          int nslice, hipStream_t s) {
+    const int H = side == 0 ? D.Hq : D.Hkv, hpp = side == 0 ? D.G : 1;
+    hipLaunchKernelGGL(dw_mfma_kernel, dim3(nslice, D.Hkv), dim3(256), 0, s,
+                       reinterpret_cast<const bf16*>(x), reinterpret_cast<const bf16*>(du16), part,
+                       D.B * D.N, H, hpp, nslice);
     return hipGetLastError();
 }
 

@@ -119,6 +119,15 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
                          const uint8_t* route, const void* ksel, const void* vsel,
                          const int32_t* selw, const int* list_off, const float* stat, float* dk,
                          float* dv, int phase, hipStream_t s);
+// NP-Map backward of one side (0: queries, 1: keys) on the matrix cores:
+// dx += the map's vector-Jacobian product of dphi; du16 receives du (bf16,
+// [Hkv][rows of the group][d/2]) for the projection gradient
+hipError_t launch_np_bwd(const Dims& D, const void* x, const void* wsplit, int side, const float* dphi,
+                         float* dx, void* du16, hipStream_t s);
+// partial projection gradients of one side over nslice row slices:
+// part [nslice, Hkv, d/2, d] (summed by the reduce kernel)
+hipError_t launch_dw_mfma(const Dims& D, const void* x, int side, const void* du16, float* part,
+                          int nslice, hipStream_t s);
 // softmax part of dq (fp32, overwritten)
 hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,

@@ -53,5 +53,29 @@ __device__ __forceinline__ void load_vt_tile(const bf16* __restrict__ src, size_
     }
 }
 
+// The same for 64 rows x 64 columns: dst[col * kVS + kperm(row)].
+__device__ __forceinline__ void load_vt_tile64(const bf16* __restrict__ src, size_t ld, int nvalid,
+                                               bf16* __restrict__ dst, int tid, int nthr) {
+    for (int x = tid; x < 16 * 8; x += nthr) {
+        const int kq = x & 15, oct = x >> 4;
+        bf16x8 r[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int row = 4 * kq + rr;
+            r[rr] = row < nvalid ? ld_bf8(src + (size_t)row * ld + 8 * oct) : zero_bf8();
+        }
+        const int pos = kperm(4 * kq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bf16x4 t4;
+            t4[0] = r[0][e];
+            t4[1] = r[1][e];
+            t4[2] = r[2][e];
+            t4[3] = r[3][e];
+            *reinterpret_cast<bf16x4*>(dst + (8 * oct + e) * kVS + pos) = t4;
+        }
+    }
+}
+
 }  // namespace mt
 }  // namespace still

@@ -402,10 +402,11 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
-static int bwd_slices(const Dims& D) {
+static int bwd_slices(const Dims& D, bool mfma) {
     // token slices of the projection-gradient sums: about 2048 blocks in all
+    // (256 on the matrix cores, whose blocks take 64-row tiles)
     const int64_t ntok = (int64_t)D.B * D.N;
-    int64_t n = (2048 + D.Hkv - 1) / D.Hkv;
+    int64_t n = ((mfma ? 256 : 2048) + D.Hkv - 1) / D.Hkv;
     if (n > ntok) n = ntok;
     return n < 1 ? 1 : (int)n;
 }
@@ -418,7 +419,7 @@ static BwdWork carve_bwd(const Dims& D, Carver& cv, bool mfma) {
     BwdWork w;
     const size_t BN = (size_t)D.B * D.N, BG = (size_t)D.B * D.Hkv;
     const size_t E1 = (size_t)D.fd * (D.d + 1);
-    w.nslice = bwd_slices(D);
+    w.nslice = bwd_slices(D, mfma);
     w.phiq = cv.take<float>(BN * D.Hq * D.fd);
     w.phik = cv.take<float>(BN * D.Hkv * D.fd);
     w.lin = cv.take<float>(BG * D.T * E1);
