@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void bwd_route_kernel(const int32_t* __restric
 // gamma dphi_q for the NP-Map's VJP and dgate = (1 - gamma) phi_q . dphi_q.
 // stat[(b, t, h)] = (m, l, D_t, c_t).
 constexpr int kNP = 2;  // query positions per wave
-template <typename T, int DD, int GM, bool LA_ONLY = false>
+template <typename T, int DD, int GM>
 __global__ __launch_bounds__(64) void bwd_query_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
@@ -231,21 +231,9 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
     // may be negative, when it has none (t < W, every routed token selected),
     // so logits far below 0 cannot underflow every weight.  The key kernels
     // read the same reference from stat.
-    float m[R], inv[R], Dt[R], cfs[R];
+    float m[R], inv[R], Dt[R];
     bool la_mass[R];
-    if constexpr (LA_ONLY) {
-        // the statistics come from the matrix-core first pass (which also
-        // wrote the softmax part of dq): only the linear terms are left
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float4 s4 = *reinterpret_cast<const float4*>(stat + qoff(r / GM, min(r % GM, G - 1)) * 4);
-            m[r] = s4.x;
-            inv[r] = use[r] ? 1.0f / s4.y : 0.f;
-            Dt[r] = s4.z;
-            cfs[r] = s4.w;
-            la_mass[r] = s4.w > 0.f;
-        }
-    } else {
+    {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         la_mass[r] = l[r] > 0.f;
@@ -340,7 +328,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
 #pragma unroll
                 for (int p = 0; p < PL; ++p)
                     dq[qoff(pp, h) * DD + lane + kWave * p] = D.tau * dqa[pp * GM + h][p];
-    }  // !LA_ONLY
+    }
 
     // ---- dphi_q, per position ----
 #pragma unroll
@@ -388,7 +376,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
                 const int r = pp * GM + h;
                 const size_t o = qoff(pp, h);
                 // no linear mass: no linear term to differentiate
-                const float cf = LA_ONLY ? cfs[r] : (la_mass[r] ? expf(-m[r]) * inv[r] : 0.f);
+                const float cf = la_mass[r] ? expf(-m[r]) * inv[r] : 0.f;
                 // cf dfq is the gradient w.r.t. the gated features fq = gamma phi_q:
                 // phi_q gets gamma times it, the gate logit (1 - gamma) fq . (cf dfq)
                 const float gw = gate_weight(gate, o);
@@ -401,7 +389,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
                     fd = wave_sum(fd);
                     if (lane == 0) dgate[o] = (1.f - gw) * cf * fd;
                 }
-                if (lane == 0 && !LA_ONLY) {
+                if (lane == 0) {
                     stat[o * 4 + 0] = m[r];
                     stat[o * 4 + 1] = l[r];
                     stat[o * 4 + 2] = Dt[r];
@@ -989,7 +977,8 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_dq")) != hipSuccess) return e;
         if ((e = launch_bwd_dq(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.list_off, w.stat,
-                               a.dq, s)) != hipSuccess)
+                               w.phik16, w.lin16, a.gate, w.phiq, a.dq, w.dphiq,
+                               a.gate ? a.dgate : nullptr, s)) != hipSuccess)
             return e;
     }
     // the queries' features carry their gate weights (phi~_q = gamma phi_q), so
@@ -1001,27 +990,24 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     }
     if ((e = mark.fn(mark.ctx, "phi_k")) != hipSuccess) return e;
     if ((e = launch_phi(D, a.k, D.Hkv, 1, a.wk, nullptr, w.phik, s)) != hipSuccess) return e;
-    if ((e = mark.fn(mark.ctx, "la_chunk")) != hipSuccess) return e;
-    if ((e = launch_la_chunks(D, w.phik, a.v, w.route, w.lin, s)) != hipSuccess) return e;
-    if ((e = mark.fn(mark.ctx, "la_scan")) != hipSuccess) return e;
-    if ((e = launch_la_scan(D, w.lin, -1, nullptr, nullptr, s)) != hipSuccess) return e;
-#define STILL_BWD_QUERY2(GM, LAO)                                                               \
-    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM, LAO>), dim3((D.N + kNP - 1) / kNP * D.Hkv * D.B), dim3(64), \
+    if (!w.mfma) {
+        // the fp32 linear prefixes the query kernel reads (the matrix-core
+        // dq kernel reads the bf16 ones)
+        if ((e = mark.fn(mark.ctx, "la_chunk")) != hipSuccess) return e;
+        if ((e = launch_la_chunks(D, w.phik, a.v, w.route, w.lin, s)) != hipSuccess) return e;
+        if ((e = mark.fn(mark.ctx, "la_scan")) != hipSuccess) return e;
+        if ((e = launch_la_scan(D, w.lin, -1, nullptr, nullptr, s)) != hipSuccess) return e;
+    }
+#define STILL_BWD_QUERY(GM)                                                               \
+    hipLaunchKernelGGL((bwd_query_kernel<T, DD, GM>), dim3((D.N + kNP - 1) / kNP * D.Hkv * D.B), dim3(64), \
                        0, s, q, k,                                                                  \
                        v, dout, w.phiq, w.phik, w.route, w.selw, w.lin, a.gate, a.dq, w.dphiq,    \
                        a.dgate, w.stat, D)
-#define STILL_BWD_QUERY(GM)             \
-    do {                                \
-        if (w.mfma)                     \
-            STILL_BWD_QUERY2(GM, true); \
-        else                            \
-            STILL_BWD_QUERY2(GM, false);\
-    } while (0)
-    STILL_STEP(w.mfma ? "bwd_query_la" : "bwd_query",
-               if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
-               else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));
+    if (!w.mfma)
+        STILL_STEP("bwd_query",
+                   if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
+                   else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));
 #undef STILL_BWD_QUERY
-#undef STILL_BWD_QUERY2
     STILL_STEP("bwd_uchunk",
                hipLaunchKernelGGL((bwd_uchunk_kernel<T, DD>), dim3(D.T, D.Hkv, D.B), dim3(256), 0,
                                   s, w.phiq, dout, w.stat, w.ust, D));
@@ -1100,7 +1086,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 
 }  // namespace
 
-int bwd_launch_count(bool mfma) { return mfma ? 21 : 16; }
+int bwd_launch_count(bool mfma) { return mfma ? 18 : 16; }
 
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s,
                       BwdMark mark) {

@@ -261,6 +261,279 @@ __global__ __launch_bounds__(kKW * 64) void bwd_kv_selected_kernel(
 
 
 // ---------------------------------------------------------------------------
+// Query side: dq's softmax part, then the linear terms of the queries' gated
+// features.  Block = HB query heads of KV head g x the 64 queries of chunk c
+// (two waves per head, 32 queries each), the key tiles of the forward in its
+// order (window chunks c-NWT .. c with their masks, then the compact selected
+// rows).  Per tile, with the statistics (m, l, D) of the first pass and
+// P = exp(tau q.k - m) / l:
+//   S^T  = K Q^T           (logits, keys x queries)
+//   dP^T = V dout^T        (dout . v_j)
+//   dS^T = P^T (dP^T - D)  rounded to bf16 as the forward rounds P
+//   dQ^T += K^T dS^T       (K read transposed from LDS)
+// dq = tau (dQ^T)^T is written in fp32.  Then, for a query with linear
+// mass (c_t = exp(-m) / l > 0; full text Sec. 3.3, the chunk-wise linear
+// branch with the shared normaliser), the gradient w.r.t. its gated
+// features fq = gamma phi_q:
+//   dfq = c_t (S dout - D z + sum over the routed unselected keys j of
+//         chunk c-NWT at or below the query's offset of (dout . v_j - D) phi_k(j))
+// with S, z the linear prefix of chunks <= c-NWT-1 (within-run part plus the
+// earlier runs', summed in fp32 and rounded to bf16 once), on the matrix
+// cores in the prefix's feature order; dphi_q = gamma dfq goes to the NP-Map
+// backward and dgate = (1 - gamma) fq . dfq.  Rows with no linear term get
+// zeros.
+template <int HB, int NWT>
+__global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const uint8_t* __restrict__ route,
+    const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const int* __restrict__ list_off,
+    const float* __restrict__ stat, const bf16* __restrict__ phik, LinBufs L,
+    const float* __restrict__ gate, const float* __restrict__ phiq, float* __restrict__ dq,
+    float* __restrict__ dphiq, float* __restrict__ dgate, Dims D) {
+    constexpr int NW = HB * 2;
+    const int HG = D.G / HB;
+    const int per_c = D.B * D.Hkv * HG;
+    const int c = D.T - 1 - (int)(blockIdx.x / per_c);
+    int r = (int)(blockIdx.x % per_c);
+    const int hg = r % HG;
+    r /= HG;
+    const int g = r % D.Hkv, b = r / D.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = wave / HB;
+    const int h = g * D.G + hg * HB + wave % HB;
+    const int t0 = c * kC;
+    const int oq = 32 * qh + col;
+    const size_t bg = (size_t)b * D.Hkv + g;
+    const float cl2 = D.tau * kLog2e;
+    const int* loff = list_off + bg * (D.n_full + 1);
+    const int nrows = c > NWT ? loff[c - NWT] : 0;
+    const int ntile = NWT + 1 + (nrows + kC - 1) / kC;
+    const int first = c >= NWT ? 0 : NWT - c;
+    const int tla = t0 - NWT * kC;
+    const size_t ldkv = (size_t)D.Hkv * kD;
+
+    // K, V (row-major) and K^T tiles; the linear phase reuses the same bytes
+    __shared__ __align__(16) bf16 sm[2 * kC * kKS + kD * kVS];
+    bf16* ks = sm;
+    bf16* vs = sm + kC * kKS;
+    bf16* kt = sm + 2 * kC * kKS;
+
+    // the lane's query: Q and dout operands, statistics
+    const int tq = min(t0 + oq, D.N - 1);
+    const size_t qo = ((size_t)b * D.N + tq) * D.Hq + h;
+    bf16x8 qf[8], df[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        qf[st] = ld_bf8(q + qo * kD + 16 * st + 8 * hf);
+        df[st] = ld_bf8(dout + qo * kD + 16 * st + 8 * hf);
+    }
+    const f32x4 stq = *reinterpret_cast<const f32x4*>(stat + qo * 4);
+    const float lse2 = stq[0] * kLog2e + __log2f(stq[1]);  // P = 2^(s cl2 - lse2)
+    const float dq_d = stq[2];
+    uint64_t selmask = 0;
+    if (c >= NWT) selmask = __ballot(route[bg * D.N + tla + lane] == kRouteSA);
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
+
+    for (int i = first; i < ntile; ++i) {
+        // rows of tile i: a window chunk from k / v, or compact rows
+        const bf16 *srck, *srcv;
+        int nv;
+        uint64_t hi_m, lo_m;
+        if (i <= NWT) {
+            const int tc = c - NWT + i;
+            nv = min(kC, D.N - tc * kC);
+            const size_t off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
+            srck = k + off;
+            srcv = v + off;
+            if (i == 0) {
+                hi_m = ~0ull;
+                lo_m = selmask;
+            } else if (i == NWT) {
+                hi_m = 0ull;
+                lo_m = ~0ull;
+            } else {
+                hi_m = lo_m = ~0ull;
+            }
+        } else {
+            const int r0 = (i - NWT - 1) * kC;
+            nv = min(kC, nrows - r0);
+            const size_t off = ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD + (size_t)r0 * ldkv;
+            srck = ksel + off;
+            srcv = vsel + off;
+            hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
+        }
+        __syncthreads();  // the previous tile's reads are done
+        load_k_tile(srck, ldkv, nv, ks, tid, NW * 64);
+        load_k_tile(srcv, ldkv, nv, vs, tid, NW * 64);
+        load_vt_tile(srck, ldkv, nv, kt, tid, NW * 64);
+        __syncthreads();
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            sc[j] = zero16();
+            dp[j] = zero16();
+        }
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                sc[j] = mfma32(ld_bf8(ks + (32 * j + col) * kKS + 16 * st + 8 * hf), qf[st], sc[j]);
+                dp[j] = mfma32(ld_bf8(vs + (32 * j + col) * kKS + 16 * st + 8 * hf), df[st], dp[j]);
+            }
+        // key row rk counts for the lane's query when bit rk of
+        // (rk > oq ? hi_m : lo_m) is set
+        const uint64_t gt = oq >= 63 ? 0ull : ~0ull << (oq + 1);
+        const uint64_t mm = ((hi_m & gt) | (lo_m & ~gt)) >> (4 * hf);
+        const uint32_t mw[2] = {(uint32_t)mm, (uint32_t)(mm >> 32)};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                const bool ok = (mw[j] >> (8 * (vv >> 2) + (vv & 3))) & 1u;
+                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[j][vv], cl2, -lse2)) : 0.f;
+                sc[j][vv] = p * (dp[j][vv] - dq_d);
+            }
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const bf16x8 pa = pack_acc(sc[s4 >> 1], s4 & 1);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                acc[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 16 * s4 + 8 * hf), pa, acc[dt]);
+        }
+    }
+    const bool qvalid = t0 + oq < D.N;
+    if (qvalid) {
+        float* dr = dq + qo * kD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                f32x4 o4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o4[j] = D.tau * acc[dt][4 * v4 + j];
+                *reinterpret_cast<f32x4*>(dr + 32 * dt + acc_row(4 * v4, hf)) = o4;
+            }
+    }
+
+    // ---- linear terms: dfq^T (rows = feature positions p of the prefix's
+    // order, feature kperm(p); column = the lane's query) ----
+    f32x16 dfq[4];
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft) dfq[ft] = zero16();
+    if (c >= NWT) {
+        // chunk c-NWT: V rows and phi_k^T of its keys
+        const int cp = c - NWT;
+        __syncthreads();
+        load_k_tile(v + (((size_t)b * D.N + (size_t)cp * kC) * D.Hkv + g) * kD, ldkv, kC, vs, tid, NW * 64);
+        load_vt_tile(phik + (bg * D.N + (size_t)cp * kC) * kD, kD, kC, kt, tid, NW * 64);
+        __syncthreads();
+        f32x16 w[2];
+        w[0] = zero16();
+        w[1] = zero16();
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                w[j] = mfma32(ld_bf8(vs + (32 * j + col) * kKS + 16 * st + 8 * hf), df[st], w[j]);
+        // dout . v_j - D on the routed linear keys at or below the query's offset
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                const int rk = 32 * j + acc_row(vv, hf);
+                const bool la = rk <= oq && !((selmask >> rk) & 1ull);
+                w[j][vv] = la ? w[j][vv] - dq_d : 0.f;
+            }
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const bf16x8 pa = pack_acc(w[s4 >> 1], s4 & 1);
+#pragma unroll
+            for (int ft = 0; ft < 4; ++ft)
+                dfq[ft] = mfma32(ld_bf8(kt + (32 * ft + col) * kVS + 16 * s4 + 8 * hf), pa, dfq[ft]);
+        }
+        if (c > NWT) {
+            // prefix of chunks <= c-NWT-1, staged as sT[p][e] (stored S^T rows
+            // are [e][p]): the within-run part of chunk c-NWT-1 plus its run's
+            // exclusive prefix
+            const int cq = c - NWT - 1, run = cq / D.ng;
+            const int ngroups = (D.n_full + D.ng - 1) / D.ng;
+            const bf16* shg = reinterpret_cast<const bf16*>(L.sh) + (bg * D.n_full + cq) * (size_t)(kD * kD);
+            const bf16* ghg = reinterpret_cast<const bf16*>(L.gh) + (bg * ngroups + run) * (size_t)(kD * kD);
+            bf16* sT = sm;  // kD rows of kKS
+            __syncthreads();
+            for (int x = tid; x < 32 * 16; x += NW * 64) {
+                const int eq = x & 31, oct = x >> 5;  // dims 4 eq .. +3, positions 8 oct .. +7
+                bf16x8 rr[4];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const bf16x8 a8 = ld_bf8(shg + (size_t)(4 * eq + e4) * kD + 8 * oct);
+                    const bf16x8 b8 = ld_bf8(ghg + (size_t)(4 * eq + e4) * kD + 8 * oct);
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) rr[e4][jj] = (bf16)((float)a8[jj] + (float)b8[jj]);
+                }
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    bf16x4 t4;
+                    t4[0] = rr[0][jj];
+                    t4[1] = rr[1][jj];
+                    t4[2] = rr[2][jj];
+                    t4[3] = rr[3][jj];
+                    *reinterpret_cast<bf16x4*>(sT + (8 * oct + jj) * kKS + 4 * eq) = t4;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+                for (int st = 0; st < 8; ++st)
+                    dfq[ft] = mfma32(ld_bf8(sT + (32 * ft + col) * kKS + 16 * st + 8 * hf), df[st], dfq[ft]);
+            const float* lz = L.lz + (bg * D.n_full + cq) * (size_t)kD;
+            const float* gz = L.gz + (bg * ngroups + run) * (size_t)kD;
+#pragma unroll
+            for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int p0 = 32 * ft + acc_row(4 * v4, hf);
+                    const f32x4 z1 = *reinterpret_cast<const f32x4*>(lz + p0);
+                    const f32x4 z2 = *reinterpret_cast<const f32x4*>(gz + p0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dfq[ft][4 * v4 + j] -= dq_d * (z1[j] + z2[j]);
+                }
+        }
+    }
+    if (!qvalid) return;
+    // dphi_q = gamma c_t dfq (feature order), dgate = (1 - gamma) c_t fq . dfq
+    const float cf = stq[3];
+    const float gw = gate_weight(gate, qo);
+    float* dpr = dphiq + qo * kD;
+    const float* fqr = phiq + qo * kD;
+    float fdot = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int f0 = kperm(32 * ft + acc_row(4 * v4, hf));  // four consecutive features
+            f32x4 o4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o4[j] = gw * cf * dfq[ft][4 * v4 + j];
+            *reinterpret_cast<f32x4*>(dpr + f0) = o4;
+            if (dgate) {
+                const f32x4 fq4 = *reinterpret_cast<const f32x4*>(fqr + f0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) fdot = fmaf(fq4[j], dfq[ft][4 * v4 + j], fdot);
+            }
+        }
+    if (dgate) {
+        fdot += xor32(fdot);
+        if (hf == 0) dgate[qo] = (1.f - gw) * cf * fdot;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // NP-Map backward on the matrix cores.  The feature map of a row x (a query
 // or key head; full text Sec. 3.2) with its head group's projection P
 // (d/2 x d):  u = P x,  z = ||x|| u / ||u||,  phi = [softmax(z); softmax(-z)].
@@ -508,6 +781,37 @@ __global__ __launch_bounds__(256) void dw_mfma_kernel(const bf16* __restrict__ x
 }
 
 }  // namespace
+
+hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
+                         const uint8_t* route, const void* ksel, const void* vsel,
+                         const int* list_off, const float* stat, const void* phik16, const LinBufs& L,
+                         const float* gate, const float* phiq, float* dq, float* dphiq, float* dgate,
+                         hipStream_t s) {
+    const int HB = D.G >= 2 ? 2 : 1;
+    const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
+    const int nwt = D.W / kC;
+#define STILL_DQ1(H, NWT)                                                                        \
+    hipLaunchKernelGGL((bwd_dq_kernel<H, NWT>), dim3(nblk), dim3(128 * H), 0, s,                \
+                       reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),      \
+                       reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout),   \
+                       route, reinterpret_cast<const bf16*>(ksel),                                \
+                       reinterpret_cast<const bf16*>(vsel), list_off, stat,                       \
+                       reinterpret_cast<const bf16*>(phik16), L, gate, phiq, dq, dphiq, dgate, D)
+#define STILL_DQ(H)                \
+    do {                           \
+        if (nwt == 1)              \
+            STILL_DQ1(H, 1);       \
+        else if (nwt == 2)         \
+            STILL_DQ1(H, 2);       \
+        else                       \
+            STILL_DQ1(H, 4);       \
+    } while (0)
+    if (HB == 2) STILL_DQ(2);
+    else STILL_DQ(1);
+#undef STILL_DQ
+#undef STILL_DQ1
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,

@@ -128,10 +128,14 @@ hipError_t launch_np_bwd(const Dims& D, const void* x, const void* wsplit, int s
 // part [nslice, Hkv, d/2, d] (summed by the reduce kernel)
 hipError_t launch_dw_mfma(const Dims& D, const void* x, int side, const void* du16, float* part,
                           int nslice, hipStream_t s);
-// softmax part of dq (fp32, overwritten)
+// softmax part of dq (fp32, overwritten), then the gradient w.r.t. the
+// queries' NP-Map features dphiq [B, N, Hq, d'] (fp32, feature order,
+// overwritten) and, with a gate, dgate
 hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,
-                         const int* list_off, const float* stat, float* dq, hipStream_t s);
+                         const int* list_off, const float* stat, const void* phik16, const LinBufs& L,
+                         const float* gate, const float* phiq, float* dq, float* dphiq, float* dgate,
+                         hipStream_t s);
 
 // ---- decode step ------------------------------------------------------------
 struct DecodeWork {

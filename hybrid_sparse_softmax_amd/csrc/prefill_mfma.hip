@@ -1623,150 +1623,6 @@ __global__ __launch_bounds__(256) void bwd_lists_kernel(const int32_t* __restric
     if (c == 0 && b == 0) split_projections(wq, wk, wsplit, D.Hkv, g, 256);
 }
 
-// Softmax part of dq on the matrix cores.  Block = HB query heads of KV
-// head g x the 64 queries of chunk c (two waves per head, 32 queries each),
-// the key tiles of the forward in its order (window chunks c-NWT .. c with
-// their masks, then the compact selected rows).  Per tile, with the
-// statistics (m, l, D) of the first pass and P = exp(tau q.k - m) / l:
-//   S^T  = K Q^T           (logits, keys x queries)
-//   dP^T = V dout^T        (dout . v_j)
-//   dS^T = P^T (dP^T - D)  rounded to bf16 as the forward rounds P
-//   dQ^T += K^T dS^T       (K read transposed from LDS)
-// 48 products per wave and tile; dq = tau (dQ^T)^T is written in fp32.
-// The linear terms of dq (through phi_q) are added by other kernels.
-template <int HB, int NWT>
-__global__ __launch_bounds__(HB * 128) void bwd_dq_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dout, const uint8_t* __restrict__ route,
-    const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const int* __restrict__ list_off,
-    const float* __restrict__ stat, float* __restrict__ dq, Dims D) {
-    constexpr int NW = HB * 2;
-    const int HG = D.G / HB;
-    const int per_c = D.B * D.Hkv * HG;
-    const int c = D.T - 1 - (int)(blockIdx.x / per_c);
-    int r = (int)(blockIdx.x % per_c);
-    const int hg = r % HG;
-    r /= HG;
-    const int g = r % D.Hkv, b = r / D.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, col = lane & 31;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qh = wave / HB;
-    const int h = g * D.G + hg * HB + wave % HB;
-    const int t0 = c * kC;
-    const int oq = 32 * qh + col;
-    const size_t bg = (size_t)b * D.Hkv + g;
-    const float cl2 = D.tau * kLog2e;
-    const int* loff = list_off + bg * (D.n_full + 1);
-    const int nrows = c > NWT ? loff[c - NWT] : 0;
-    const int ntile = NWT + 1 + (nrows + kC - 1) / kC;
-    const int first = c >= NWT ? 0 : NWT - c;
-    const int tla = t0 - NWT * kC;
-    const size_t ldkv = (size_t)D.Hkv * kD;
-
-    __shared__ __align__(16) bf16 ks[kC * kKS];
-    __shared__ __align__(16) bf16 vs[kC * kKS];
-    __shared__ __align__(16) bf16 kt[kD * kVS];
-
-    // the lane's query: Q and dout operands, statistics
-    const int tq = min(t0 + oq, D.N - 1);
-    const size_t qo = ((size_t)b * D.N + tq) * D.Hq + h;
-    bf16x8 qf[8], df[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        qf[s] = ld_bf8(q + qo * kD + 16 * s + 8 * hf);
-        df[s] = ld_bf8(dout + qo * kD + 16 * s + 8 * hf);
-    }
-    const f32x4 st = *reinterpret_cast<const f32x4*>(stat + qo * 4);
-    const float lse2 = st[0] * kLog2e + __log2f(st[1]);  // P = 2^(s cl2 - lse2)
-    const float dq_d = st[2];
-    uint64_t selmask = 0;
-    if (c >= NWT) selmask = __ballot(route[bg * D.N + tla + lane] == kRouteSA);
-
-    f32x16 acc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
-
-    for (int i = first; i < ntile; ++i) {
-        // rows of tile i: a window chunk from k / v, or compact rows
-        const bf16 *srck, *srcv;
-        int nv;
-        uint64_t hi_m, lo_m;
-        if (i <= NWT) {
-            const int tc = c - NWT + i;
-            nv = min(kC, D.N - tc * kC);
-            const size_t off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
-            srck = k + off;
-            srcv = v + off;
-            if (i == 0) {
-                hi_m = ~0ull;
-                lo_m = selmask;
-            } else if (i == NWT) {
-                hi_m = 0ull;
-                lo_m = ~0ull;
-            } else {
-                hi_m = lo_m = ~0ull;
-            }
-        } else {
-            const int r0 = (i - NWT - 1) * kC;
-            nv = min(kC, nrows - r0);
-            const size_t off = ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD + (size_t)r0 * ldkv;
-            srck = ksel + off;
-            srcv = vsel + off;
-            hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
-        }
-        __syncthreads();  // the previous tile's reads are done
-        load_k_tile(srck, ldkv, nv, ks, tid, NW * 64);
-        load_k_tile(srcv, ldkv, nv, vs, tid, NW * 64);
-        load_vt_tile(srck, ldkv, nv, kt, tid, NW * 64);
-        __syncthreads();
-        f32x16 sc[2], dp[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            sc[j] = zero16();
-            dp[j] = zero16();
-        }
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                sc[j] = mfma32(ld_bf8(ks + (32 * j + col) * kKS + 16 * s + 8 * hf), qf[s], sc[j]);
-                dp[j] = mfma32(ld_bf8(vs + (32 * j + col) * kKS + 16 * s + 8 * hf), df[s], dp[j]);
-            }
-        // key row rk counts for the lane's query when bit rk of
-        // (rk > oq ? hi_m : lo_m) is set
-        const uint64_t gt = oq >= 63 ? 0ull : ~0ull << (oq + 1);
-        const uint64_t mm = ((hi_m & gt) | (lo_m & ~gt)) >> (4 * hf);
-        const uint32_t mw[2] = {(uint32_t)mm, (uint32_t)(mm >> 32)};
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) {
-                const bool ok = (mw[j] >> (8 * (vv >> 2) + (vv & 3))) & 1u;
-                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[j][vv], cl2, -lse2)) : 0.f;
-                sc[j][vv] = p * (dp[j][vv] - dq_d);
-            }
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const bf16x8 pa = pack_acc(sc[s4 >> 1], s4 & 1);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                acc[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 16 * s4 + 8 * hf), pa, acc[dt]);
-        }
-    }
-    if (t0 + oq < D.N) {
-        float* dr = dq + qo * kD;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                f32x4 o4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) o4[j] = D.tau * acc[dt][4 * v4 + j];
-                *reinterpret_cast<f32x4*>(dr + 32 * dt + acc_row(4 * v4, hf)) = o4;
-            }
-    }
-}
-
 }  // namespace
 
 bool mfma_fwd_supported(const Dims& D) {
@@ -1911,32 +1767,5 @@ hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, cons
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
-                         const uint8_t* route, const void* ksel, const void* vsel,
-                         const int* list_off, const float* stat, float* dq, hipStream_t s) {
-    const int HB = D.G >= 2 ? 2 : 1;
-    const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
-    const int nwt = D.W / kC;
-#define STILL_DQ1(H, NWT)                                                                        \
-    hipLaunchKernelGGL((bwd_dq_kernel<H, NWT>), dim3(nblk), dim3(128 * H), 0, s,                \
-                       reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),      \
-                       reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout),   \
-                       route, reinterpret_cast<const bf16*>(ksel),                                \
-                       reinterpret_cast<const bf16*>(vsel), list_off, stat, dq, D)
-#define STILL_DQ(H)                \
-    do {                           \
-        if (nwt == 1)              \
-            STILL_DQ1(H, 1);       \
-        else if (nwt == 2)         \
-            STILL_DQ1(H, 2);       \
-        else                       \
-            STILL_DQ1(H, 4);       \
-    } while (0)
-    if (HB == 2) STILL_DQ(2);
-    else STILL_DQ(1);
-#undef STILL_DQ
-#undef STILL_DQ1
-    return hipGetLastError();
-}
 
 }  // namespace still
