@@ -527,10 +527,8 @@ __device__ __forceinline__ void key_group_softmax(const T* __restrict__ q, const
 //   dv_j = U_j^T phi_k(j),  dphi_k(j) = U_j v_j - u_j
 // (U_j: the inclusive suffix sum from the first chunk after j + W's chunk,
 // plus the queries of j + W's chunk from j + W on, taken one by one).
-// Writes dk (softmax part), dv and dphi_k of its keys.  LA_ONLY (the
-// matrix-core path): only the linear terms; writes dv (their part) and
-// dphi_k, and leaves dk and the softmax terms to the matrix-core kernels.
-template <typename T, int DD, bool LA_ONLY = false>
+// Writes dk (softmax part), dv and dphi_k of its keys.
+template <typename T, int DD>
 __global__ __launch_bounds__(64) void bwd_key_win_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ phiq, const float* __restrict__ phik,
@@ -559,7 +557,7 @@ __global__ __launch_bounds__(64) void bwd_key_win_kernel(
     for (int i = 0; i < kKB; ++i)
 #pragma unroll
         for (int p = 0; p < PL; ++p) dka[i][p] = dva[i][p] = dfa[i][p] = 0.f;
-    if (D.W > 0 && !LA_ONLY)
+    if (D.W > 0)
         key_group_softmax<T, DD>(q, dout, stat, ks, vs, jk, j0, min(D.N - 1, j0 + kKB - 1 + D.W - 1),
                                  0, b, g, D, lane, dka, dva);
     // linear part, one pass per chunk c0 holding some key's first linear
@@ -683,7 +681,7 @@ __global__ __launch_bounds__(64) void bwd_key_win_kernel(
 #pragma unroll
         for (int p = 0; p < PL; ++p) {
             const size_t e = koff(jk[i]) * DD + lane + kWave * p;
-            if (!LA_ONLY) dk[e] = D.tau * dka[i][p];
+            dk[e] = D.tau * dka[i][p];
             dv[e] = dva[i][p];
             dphik[e] = dfa[i][p];
         }
@@ -988,9 +986,9 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
         if ((e = mark.fn(mark.ctx, "phi_q")) != hipSuccess) return e;
         if ((e = launch_phi(D, a.q, D.Hq, D.G, a.wq, a.gate, w.phiq, s)) != hipSuccess) return e;
     }
-    if ((e = mark.fn(mark.ctx, "phi_k")) != hipSuccess) return e;
-    if ((e = launch_phi(D, a.k, D.Hkv, 1, a.wk, nullptr, w.phik, s)) != hipSuccess) return e;
     if (!w.mfma) {
+        if ((e = mark.fn(mark.ctx, "phi_k")) != hipSuccess) return e;
+        if ((e = launch_phi(D, a.k, D.Hkv, 1, a.wk, nullptr, w.phik, s)) != hipSuccess) return e;
         // the fp32 linear prefixes the query kernel reads (the matrix-core
         // dq kernel reads the bf16 ones)
         if ((e = mark.fn(mark.ctx, "la_chunk")) != hipSuccess) return e;
@@ -1008,20 +1006,26 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
                    if (D.G == 1) STILL_BWD_QUERY(1); else if (D.G == 2) STILL_BWD_QUERY(2);
                    else if (D.G <= 4) STILL_BWD_QUERY(4); else STILL_BWD_QUERY(8));
 #undef STILL_BWD_QUERY
-    STILL_STEP("bwd_uchunk",
-               hipLaunchKernelGGL((bwd_uchunk_kernel<T, DD>), dim3(D.T, D.Hkv, D.B), dim3(256), 0,
-                                  s, w.phiq, dout, w.stat, w.ust, D));
+    if (w.mfma) {
+        if ((e = mark.fn(mark.ctx, "bwd_uchunk")) != hipSuccess) return e;
+        if ((e = launch_bwd_key_lin(D, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, w.dphik,
+                                    0, s)) != hipSuccess)
+            return e;
+    } else {
+        STILL_STEP("bwd_uchunk",
+                   hipLaunchKernelGGL((bwd_uchunk_kernel<T, DD>), dim3(D.T, D.Hkv, D.B), dim3(256), 0,
+                                      s, w.phiq, dout, w.stat, w.ust, D));
+    }
     STILL_STEP("bwd_suffix",
                hipLaunchKernelGGL(bwd_suffix_kernel, dim3((D.fd * (D.d + 1) + 255) / 256, D.Hkv, D.B),
                                   dim3(256), 0, s, w.ust, D));
     if (w.mfma) {
         // linear terms first (dv, dphi_k), then the softmax terms on the matrix
         // cores: window keys (write dk, add to dv), then selected keys (add)
-        STILL_STEP("bwd_key_la",
-                   hipLaunchKernelGGL((bwd_key_win_kernel<T, DD, true>),
-                                      dim3((D.N + kKB - 1) / kKB * D.Hkv * D.B), dim3(64), 0, s, q, k,
-                                      v, dout, w.phiq, w.phik, w.route, w.stat, w.ust, a.dk, a.dv,
-                                      w.dphik, D));
+        if ((e = mark.fn(mark.ctx, "bwd_key_la")) != hipSuccess) return e;
+        if ((e = launch_bwd_key_lin(D, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, w.dphik,
+                                    1, s)) != hipSuccess)
+            return e;
         if ((e = mark.fn(mark.ctx, "bwd_kv_win")) != hipSuccess) return e;
         if ((e = launch_bwd_kv(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw, w.list_off,
                                w.stat, a.dk, a.dv, 0, s)) != hipSuccess)
@@ -1086,7 +1090,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 
 }  // namespace
 
-int bwd_launch_count(bool mfma) { return mfma ? 18 : 16; }
+int bwd_launch_count(bool mfma) { return mfma ? 17 : 16; }
 
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s,
                       BwdMark mark) {

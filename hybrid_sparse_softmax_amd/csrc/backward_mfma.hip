@@ -25,6 +25,7 @@
 #include "launch.h"
 #include "mfma_common.h"
 #include "mfma_tiles.h"
+#include "row_ops.h"
 
 namespace still {
 
@@ -534,6 +535,276 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // ---------------------------------------------------------------------------
+// Key side of the linear branch (full text Sec. 3.3, chunk-wise linear
+// attention under the shared normaliser).  A routed unselected key j of
+// chunk cj reaches every query t >= j + W through the linear state:
+//   dv_j += U_j^T phi_k(j),  dphi_k(j) = U_j v_j - u_j,
+//   U_j = sum over those queries (all heads of the group) of c_t fq_t dout_t^T,
+//   u_j = sum c_t D_t fq_t    (fq = gamma phi_q, c_t = exp(-m) / l)
+// = the chunk sums of chunks >= cj + NWT + 1 (an inclusive suffix over
+// chunks) plus the queries of chunk cj + NWT at or after the key's offset.
+// ---------------------------------------------------------------------------
+
+// fq row (fp32, feature order) -> 8 bf16 features of storage positions
+// 8 oct .. 8 oct + 7 (position p holds feature kperm(p)), times sc
+__device__ __forceinline__ bf16x8 fq_oct_perm(const float* __restrict__ row, int oct, float sc) {
+    // positions 16 b + 8 h + 4 m + l hold features 16 b + 8 m + 4 h + l
+    const int b16 = 16 * (oct >> 1), h4 = 4 * (oct & 1);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + b16 + h4);
+    const f32x4 c = *reinterpret_cast<const f32x4*>(row + b16 + 8 + h4);
+    bf16x8 r;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+        r[l] = (bf16)(sc * a[l]);
+        r[4 + l] = (bf16)(sc * c[l]);
+    }
+    return r;
+}
+
+// Chunk sums per query chunk c of (b, g): U[i][e] = sum over its queries t
+// and the group's heads of c_t fq_t[i] dout_t[e], u[i] = sum c_t D_t fq_t[i]
+// (the fp32 layout [i][e] then u, (d + 1) d' floats).  Per head, (c fq)^T and
+// dout^T are staged with the queries as contraction index; wave w owns
+// features 32 w .. 32 w + 31.
+__global__ __launch_bounds__(256) void bwd_uchunk_mfma_kernel(const float* __restrict__ phiq,
+                                                              const bf16* __restrict__ dout,
+                                                              const float* __restrict__ stat,
+                                                              float* __restrict__ ust, Dims D) {
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __shared__ __align__(16) bf16 ft[kD * kVS];  // (c fq)^T: [feature][kperm(query)]
+    __shared__ __align__(16) bf16 dtt[kD * kVS]; // dout^T:   [dim][kperm(query)]
+    __shared__ float dq_[kC];                     // D_t, at kperm(query)
+    const int t0 = c * kC, nv = min(kC, D.N - t0);
+    f32x16 acc[4];
+#pragma unroll
+    for (int et = 0; et < 4; ++et) acc[et] = zero16();
+    float uacc = 0.f;
+    for (int hh = 0; hh < D.G; ++hh) {
+        const int h = g * D.G + hh;
+        const size_t o0 = ((size_t)b * D.N + t0) * D.Hq + h;
+        __syncthreads();
+        for (int x = tid; x < 16 * 16; x += 256) {
+            const int kq = x & 15, oct = x >> 4;
+            bf16x8 rr[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int row = 4 * kq + q4;
+                if (row < nv) {
+                    const size_t o = o0 + (size_t)row * D.Hq;
+                    // the features in natural order here: position = feature
+                    const float cf = stat[o * 4 + 3];
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(phiq + o * kD + 8 * oct);
+                    const f32x4 bb = *reinterpret_cast<const f32x4*>(phiq + o * kD + 8 * oct + 4);
+#pragma unroll
+                    for (int l = 0; l < 4; ++l) {
+                        rr[q4][l] = (bf16)(cf * a[l]);
+                        rr[q4][4 + l] = (bf16)(cf * bb[l]);
+                    }
+                } else {
+                    rr[q4] = zero_bf8();
+                }
+            }
+            const int pos = kperm(4 * kq);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16x4 t4;
+                t4[0] = rr[0][e];
+                t4[1] = rr[1][e];
+                t4[2] = rr[2][e];
+                t4[3] = rr[3][e];
+                *reinterpret_cast<bf16x4*>(ft + (8 * oct + e) * kVS + pos) = t4;
+            }
+        }
+        load_vt_tile(dout + o0 * kD, (size_t)D.Hq * kD, nv, dtt, tid, 256);
+        if (tid < kC) dq_[kperm(tid)] = tid < nv ? stat[(o0 + (size_t)tid * D.Hq) * 4 + 2] : 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a = ld_bf8(ft + (32 * wave + col) * kVS + 16 * ks + 8 * hf);
+#pragma unroll
+            for (int et = 0; et < 4; ++et)
+                acc[et] = mfma32(a, ld_bf8(dtt + (32 * et + col) * kVS + 16 * ks + 8 * hf), acc[et]);
+        }
+        if (tid < kD) {
+            const bf16* fr = ft + tid * kVS;
+            for (int p = 0; p < kC; ++p) uacc = fmaf((float)fr[p], dq_[p], uacc);
+        }
+    }
+    float* out = ust + (((size_t)b * D.Hkv + g) * D.T + c) * (size_t)(kD * (kD + 1));
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv)
+            out[(size_t)(32 * wave + acc_row(vv, hf)) * kD + 32 * et + col] = acc[et][vv];
+    if (tid < kD) out[kD * kD + tid] = uacc;
+}
+
+// Per key chunk cj of (b, g), 64 keys: the linear terms above.  Waves 0 / 1
+// take keys 0-31 / 32-63 for dphi_k (rows: feature positions p of phi_k's
+// storage order, feature kperm(p)), waves 2 / 3 the same keys for dv (rows:
+// dims).  The suffix sum U of chunks >= cj + NWT + 1 is staged in bf16 twice
+// (rows of positions p, and transposed); then, per head, the 64 queries of
+// chunk cj + NWT (fq with permuted features, fq^T, dout, dout^T).  Writes dv
+// (the linear part; the softmax kernels add theirs) and dphi_k (feature
+// order) of every key of the chunk, zeros for keys with no linear term.
+template <int NWT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_lin_kernel(
+    const bf16* __restrict__ v, const bf16* __restrict__ dout, const float* __restrict__ phiq,
+    const bf16* __restrict__ phik16, const uint8_t* __restrict__ route, const float* __restrict__ stat,
+    const float* __restrict__ ust, float* __restrict__ dv, float* __restrict__ dphik, Dims D) {
+    const Item it = xcd_item(D.T, D.Hkv);
+    const int cj = it.x, g = it.y, b = it.z;
+    const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = wave & 1, role = wave >> 1;  // role 0: dphi_k, 1: dv
+    const size_t bg = (size_t)b * D.Hkv + g;
+    const int rk = 32 * kh + col;  // the lane's key offset in chunk cj
+    const int j = cj * kC + rk;
+    const int c0 = cj + NWT;  // chunk of the first linear query
+    const bool has_q = c0 < D.T;
+    const bool la = j < D.N && has_q && j + D.W <= D.N - 1 && route[bg * D.N + j] == kRouteLA;
+    const int jr = min(j, D.N - 1);
+    bf16x8 bop[8];  // role 0: v_j (dims), role 1: phi_k(j) (storage positions)
+    if (role == 0) load_key_operand(v + (((size_t)b * D.N + jr) * D.Hkv + g) * kD, bop);
+    else load_key_operand(phik16 + (bg * D.N + jr) * kD, bop);
+    // one area: U and U^T (bf16), then per head fq, fq^T, dout, dout^T
+    __shared__ __align__(16) bf16 sm[2 * kC * kKS + 2 * kD * kVS];
+    __shared__ float cq[kC], dq_[kC];
+    f32x16 acc[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) acc[t4] = zero16();
+    if (has_q && c0 + 1 < D.T) {
+        const float* U = ust + (bg * D.T + c0 + 1) * (size_t)(kD * (kD + 1));
+        bf16* ub = sm;              // [p][e], kKS
+        bf16* ut = sm + kD * kKS;   // [e][p], kKS
+        for (int x = tid; x < kD * 16; x += 256) {
+            const int pp = x >> 4, oct = x & 15;
+            const int f = kperm(pp);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(U + (size_t)f * kD + 8 * oct);
+            const f32x4 c = *reinterpret_cast<const f32x4*>(U + (size_t)f * kD + 8 * oct + 4);
+            bf16x8 r;
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                r[l] = (bf16)a[l];
+                r[4 + l] = (bf16)c[l];
+            }
+            st_bf8(ub + pp * kKS + 8 * oct, r);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ut[(8 * oct + e) * kKS + pp] = r[e];
+        }
+        __syncthreads();
+        const bf16* A = role == 0 ? ub : ut;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+            for (int st = 0; st < 8; ++st)
+                acc[t4] = mfma32(ld_bf8(A + (32 * t4 + col) * kKS + 16 * st + 8 * hf), bop[st], acc[t4]);
+        if (role == 0) {
+            // - u (feature order)
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) acc[t4][vv] -= U[kD * kD + kperm(32 * t4 + acc_row(vv, hf))];
+        }
+    }
+    if (has_q) {
+        const int tq0 = c0 * kC, nq = min(kC, D.N - tq0);
+        bf16* fq = sm;                       // [q][p], kKS
+        bf16* dr = sm + kC * kKS;            // [q][e], kKS
+        bf16* fqt = sm + 2 * kC * kKS;       // [p][kperm(q)], kVS
+        bf16* drt = fqt + kD * kVS;          // [e][kperm(q)], kVS
+        for (int hh = 0; hh < D.G; ++hh) {
+            const int h = g * D.G + hh;
+            const size_t o0 = ((size_t)b * D.N + tq0) * D.Hq + h;
+            __syncthreads();
+            for (int x = tid; x < kC * 16; x += 256) {
+                const int row = x >> 4, oct = x & 15;
+                st_bf8(fq + row * kKS + 8 * oct,
+                       row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct, 1.f) : zero_bf8());
+            }
+            for (int x = tid; x < 16 * 16; x += 256) {
+                const int kq = x & 15, oct = x >> 4;
+                bf16x8 rr[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int row = 4 * kq + q4;
+                    rr[q4] = row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct, 1.f) : zero_bf8();
+                }
+                const int pos = kperm(4 * kq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bf16x4 t4;
+                    t4[0] = rr[0][e];
+                    t4[1] = rr[1][e];
+                    t4[2] = rr[2][e];
+                    t4[3] = rr[3][e];
+                    *reinterpret_cast<bf16x4*>(fqt + (8 * oct + e) * kVS + pos) = t4;
+                }
+            }
+            load_k_tile(dout + o0 * kD, (size_t)D.Hq * kD, nq, dr, tid, 256);
+            load_vt_tile(dout + o0 * kD, (size_t)D.Hq * kD, nq, drt, tid, 256);
+            if (tid < kC) {
+                float cf = 0.f, dd = 0.f;
+                if (tid < nq) {
+                    const f32x4 s4 = *reinterpret_cast<const f32x4*>(stat + (o0 + (size_t)tid * D.Hq) * 4);
+                    cf = s4[3];
+                    dd = s4[2];
+                }
+                cq[tid] = cf;
+                dq_[tid] = dd;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                // rows: queries 32 qb + acc_row, column: the lane's key
+                f32x16 x = zero16();
+                const bf16* A = role == 0 ? dr : fq;
+#pragma unroll
+                for (int st = 0; st < 8; ++st)
+                    x = mfma32(ld_bf8(A + (32 * qb + col) * kKS + 16 * st + 8 * hf), bop[st], x);
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int r0 = 32 * qb + acc_row(4 * v4, hf);
+                    const f32x4 c4 = *reinterpret_cast<const f32x4*>(cq + r0);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dq_ + r0);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int vv = 4 * v4 + jj;
+                        const bool ok = la && r0 + jj >= rk;  // query at or after the key's offset
+                        // role 0: c_t (dout . v_j - D_t); role 1: c_t fq . phi_k(j)
+                        x[vv] = ok ? c4[jj] * (role == 0 ? x[vv] - d4[jj] : x[vv]) : 0.f;
+                    }
+                }
+                const bf16* At = role == 0 ? fqt : drt;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const bf16x8 pw = pack_acc(x, s2);
+                    const int ks = 2 * qb + s2;
+#pragma unroll
+                    for (int t4 = 0; t4 < 4; ++t4)
+                        acc[t4] = mfma32(ld_bf8(At + (32 * t4 + col) * kVS + 16 * ks + 8 * hf), pw, acc[t4]);
+                }
+            }
+        }
+    }
+    if (j >= D.N) return;
+    const size_t o = (((size_t)b * D.N + j) * D.Hkv + g) * kD;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int r0 = 32 * t4 + acc_row(4 * v4, hf);
+            f32x4 w4;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) w4[jj] = la ? acc[t4][4 * v4 + jj] : 0.f;
+            if (role == 0) *reinterpret_cast<f32x4*>(dphik + o + kperm(r0)) = w4;
+            else *reinterpret_cast<f32x4*>(dv + o + r0) = w4;
+        }
+}
+
+// ---------------------------------------------------------------------------
 // NP-Map backward on the matrix cores.  The feature map of a row x (a query
 // or key head; full text Sec. 3.2) with its head group's projection P
 // (d/2 x d):  u = P x,  z = ||x|| u / ||u||,  phi = [softmax(z); softmax(-z)].
@@ -810,6 +1081,27 @@ hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void
     else STILL_DQ(1);
 #undef STILL_DQ
 #undef STILL_DQ1
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const float* phiq,
+                              const void* phik16, const uint8_t* route, const float* stat, float* ust,
+                              float* dv, float* dphik, int phase, hipStream_t s) {
+    if (phase == 0) {
+        hipLaunchKernelGGL(bwd_uchunk_mfma_kernel, dim3(D.T, D.Hkv, D.B), dim3(256), 0, s, phiq,
+                           reinterpret_cast<const bf16*>(dout), stat, ust, D);
+        return hipGetLastError();
+    }
+    const unsigned nblk = (unsigned)D.T * D.Hkv * D.B;
+    const int nwt = D.W / kC;
+#define STILL_KL(NWT)                                                                            \
+    hipLaunchKernelGGL((bwd_key_lin_kernel<NWT>), dim3(nblk), dim3(256), 0, s,                  \
+                       reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout), phiq, \
+                       reinterpret_cast<const bf16*>(phik16), route, stat, ust, dv, dphik, D)
+    if (nwt == 1) STILL_KL(1);
+    else if (nwt == 2) STILL_KL(2);
+    else STILL_KL(4);
+#undef STILL_KL
     return hipGetLastError();
 }
 

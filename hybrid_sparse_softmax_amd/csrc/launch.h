@@ -119,6 +119,13 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
                          const uint8_t* route, const void* ksel, const void* vsel,
                          const int32_t* selw, const int* list_off, const float* stat, float* dk,
                          float* dv, int phase, hipStream_t s);
+// linear terms of the keys on the matrix cores: phase 0 the chunk sums
+// ust [B, Hkv, T, d' (d + 1)] (fp32, [i][e] then u; the suffix kernel turns
+// them into suffix sums), phase 1 dv (written: the linear part) and dphik
+// [B, N, Hkv, d'] (fp32, feature order, written) from the suffix sums
+hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const float* phiq,
+                              const void* phik16, const uint8_t* route, const float* stat, float* ust,
+                              float* dv, float* dphik, int phase, hipStream_t s);
 // NP-Map backward of one side (0: queries, 1: keys) on the matrix cores:
 // dx += the map's vector-Jacobian product of dphi; du16 receives du (bf16,
 // [Hkv][rows of the group][d/2]) for the projection gradient
