@@ -338,9 +338,10 @@ def backward_flops(cfg: dict, sel_idx: np.ndarray) -> dict:
     the linear read-out, the NP-Map of the queries) plus dout . out.  Linear
     terms: S_t dout per query head (2 d' d), the chunk sums c phi_q dout^T per
     query head (2 d' d), U^T phi_k and U v per routed linear key (4 d' d),
-    explicit pairs of the partly covered chunk (4d + 4d' per pair on each
-    side); NP-Map backward 2 d' d and its projection gradient d' d per
-    token-head."""
+    explicit pairs of the partly covered chunk (query side 2d + 2d' per pair
+    on the matrix cores, whose first pass has the normaliser; 4d + 4d' in the
+    fp32 kernel; key side 4d + 4d'); NP-Map backward 2 d' d and its
+    projection gradient d' d per token-head."""
     B, N, Hq, Hkv = cfg["batch"], cfg["seqlen"], cfg["n_q_heads"], cfg["n_kv_heads"]
     d = fd = cfg["head_dim"]
     W, C = cfg["window"], cfg["chunk"]
@@ -375,17 +376,16 @@ def backward_flops(cfg: dict, sel_idx: np.ndarray) -> dict:
     out = dict(
         # matrix-core path
         bwd_stats=fwd_like + 2.0 * d * tok_q,
-        bwd_dq=6.0 * d * sa,
+        bwd_dq=6.0 * d * sa + 2.0 * fd * d * tok_q + (2.0 * d + 2.0 * fd) * q_part,
         bwd_kv_win=8.0 * d * win_pairs,
         bwd_kv_sel=8.0 * d * sel_pairs,
-        bwd_query_la=lin_q,
         bwd_key_la=lin_k,
         # general path
         bwd_query=6.0 * d * sa + lin_q,
         bwd_key_win=8.0 * d * win_pairs + lin_k,
         bwd_key_sel=8.0 * d * sel_pairs,
         # both
-        bwd_uchunk=2.0 * fd * d * tok_q,
+        bwd_uchunk=2.0 * fd * d * tok_q + 2.0 * fd * tok_q,
         np_vjp_q=2.0 * fd * d * tok_q,
         np_vjp_k=2.0 * fd * d * tok_k,
         dw_q=1.0 * fd * d * tok_q,
@@ -397,7 +397,8 @@ def backward_flops(cfg: dict, sel_idx: np.ndarray) -> dict:
     return out
 
 
-MFMA_KERNELS = {"bwd_stats", "bwd_dq", "bwd_kv_win", "bwd_kv_sel"}
+MFMA_KERNELS = {"bwd_stats", "bwd_dq", "bwd_kv_win", "bwd_kv_sel", "bwd_uchunk", "bwd_key_la",
+                "np_vjp_q", "np_vjp_k", "dw_q", "dw_k"}
 
 
 def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
@@ -436,6 +437,19 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
     kern = {k: float(np.mean(v)) for k, v in per.items()}
     log(f"[bench] {name} backward: {ms:.3f} ms/step; kernels (ms): " +
         ", ".join(f"{k}={v:.3f}" for k, v in kern.items()))
+    # the forward of the same batch, for the backward / forward ratio
+    fws = torch.empty(still.fwd_workspace_size(sh), dtype=torch.uint8, device="cuda")
+    fout = torch.empty_like(dev["q"])
+    for _ in range(warmup):
+        still.fwd(*args, **kw, out=fout, workspace=fws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        still.fwd(*args, **kw, out=fout, workspace=fws)
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / steps
+    log(f"[bench] {name} forward: {fwd_ms:.3f} ms/step; backward / forward {ms / fwd_ms:.2f}")
     fl = backward_flops(cfg, sel.cpu().numpy())
     dom = max(kern, key=kern.get)
     roof = None
@@ -460,6 +474,7 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
                        f"window {W}, chunk {C}, top-{lam}; gradients of q, k, v, both NP-Map "
                        "projections (fp32) under the forward's routing", "batch": cfg["batch"],
                        "seq_len": cfg["seqlen"]},
+            "forward_ms": round(fwd_ms, 4), "backward_over_forward": round(ms / fwd_ms, 2),
             "whole_step_TFLOPs": round(total / (ms * 1e-3) / 1e12, 2),
             "whole_step_count": "method flops: 10d per softmax pair plus the linear and NP-Map terms",
             "matrix_core_kernels": mfma_kernels,

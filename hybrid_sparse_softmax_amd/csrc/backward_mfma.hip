@@ -1,15 +1,18 @@
-// Key side of the STILL backward pass on the gfx950 matrix cores (bf16
-// storage, head_dim 128, chunk 64, window 64 NWT), routing held fixed.
+// The STILL backward pass on the gfx950 matrix cores (bf16 storage,
+// head_dim 128, chunk 64, window 64 NWT), routing held fixed: every kernel
+// of the matrix-core path but the first pass (the forward's main kernel
+// with statistics, prefill_mfma.hip).
 //
-// For a key j and every query t that attends to it by softmax (its window
-// t in [j, j + W - 1], and every later query t >= j + W when j is selected;
-// full text Sec. 3.3), with P_tj = exp(tau q_t.k_j - m_t) / l_t and the
-// first pass's statistics (m_t, l_t, D_t = dout_t . out_t):
+// Softmax terms.  For a key j and every query t that attends to it by
+// softmax (its window t in [j, j + W - 1], and every later query t >= j + W
+// when j is selected; full text Sec. 3.3), with P_tj = exp(tau q_t.k_j -
+// m_t) / l_t and the first pass's statistics (m_t, l_t, D_t = dout_t . out_t):
 //   dv_j += sum_t P_tj dout_t
 //   dk_j += tau sum_t dS_tj q_t,   dS_tj = P_tj (dout_t . v_j - D_t)
-// summed over the query heads of the KV group.  One wave owns 32 keys (K and
-// V rows in registers as the B operands) and streams 64-query tiles of one
-// head through LDS: per half tile of 32 queries
+//   dq_t += tau sum_j dS_tj k_j
+// summed over the query heads of the KV group.  Key kernels: one wave owns
+// 32 keys (K and V rows in registers as the B operands) and streams 64-query
+// tiles of one head through LDS: per half tile of 32 queries
 //   S  = Q K^T,  dP = dout V^T          (queries x keys)
 //   dV^T += dout^T P,  dK^T += Q^T dS   (dims x keys, dS and P rounded to bf16)
 // 64 products per wave and query tile.  Two launches:
@@ -21,7 +24,9 @@
 //             every query chunk after their window: the visible rows of a
 //             tile are a prefix (rows of chunks <= c - NWT - 1); adds to dk
 //             and dv.
-// The linear terms of dk / dv come from the fp32 kernels.
+// The query kernel streams the forward's key tiles for dq, then adds the
+// linear terms of the queries' features (dphi_q, dgate).  The keys' linear
+// terms, the NP-Map backward and the projection gradients follow below.
 #include "launch.h"
 #include "mfma_common.h"
 #include "mfma_tiles.h"
