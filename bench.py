@@ -481,6 +481,48 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()}, "roofline": roof}
 
 
+def bench_n_scaling(still, torch, steps=5, warmup=2):
+    """Prefill time against sequence length at a fixed selected-token budget
+    (full text Sec. 3.3, complexity; App. A.4): m - W = 8192 selected rows per
+    KV head, the per-chunk quota re-derived from each length,
+    lambda(N) = floor((m - W) / ceil(N / C)) (capped at C), the 16K prefill's
+    shape otherwise (32 / 8 heads, d 128, W = C = 64).  Once the budget is
+    full (N >= 16K) every query sees at most W + m keys, so the time per
+    token should stay flat and the step time grow linearly in N."""
+    cfg = dict(workloads.CONFIGS["prefill_16k"])
+    W, C = cfg["window"], cfg["chunk"]
+    m = 8192 + W
+    rows = []
+    for N in (4096, 8192, 16384, 32768, 65536):
+        lam = min(C, still.topk_for_budget(m, W, C, N))
+        c = dict(cfg, seqlen=N, topk=lam)
+        raw = workloads.make_prefill(c, workloads.seed_of("prefill_16k"))
+        dev = {k: torch.from_numpy(raw[k]).to(torch.bfloat16).cuda() for k in ("q", "k", "v")}
+        for k in ("wphi_q", "wphi_k"):
+            dev[k] = torch.from_numpy(raw[k]).cuda()
+        del raw
+        kw = dict(window=W, chunk=C, topk=lam)
+        sh = still.make_shape(batch=1, seqlen=N, n_q_heads=c["n_q_heads"], n_kv_heads=c["n_kv_heads"],
+                              head_dim=c["head_dim"], **kw)
+        ws = torch.empty(still.fwd_workspace_size(sh), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(dev["q"])
+        args = (dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"])
+        for _ in range(warmup):
+            still.fwd(*args, **kw, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            still.fwd(*args, **kw, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        rows.append({"seq_len": N, "topk": lam, "ms": round(ms, 4), "ns_per_token": round(ms * 1e6 / N, 2)})
+        log(f"[bench] n-scaling N={N} topk={lam}: {ms:.3f} ms ({ms * 1e6 / N:.1f} ns/token)")
+        del dev, ws, out
+    return {"budget_m": m, "window": W, "chunk": C, "rows": rows}
+
+
 def bench_utility(still, torch, name="prefill_4k"):
     """Future-KV-utility diagnostic (full text App. A.7.4, Table 12) on the
     4K prefill: the library's utilities of every remote key, then for each
@@ -571,6 +613,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-utility", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-scaling", action="store_true",
+                    help="skip the prefill-time-against-length sweep at a fixed budget")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step and print its JSON object")
     ap.add_argument("--ragged-only", action="store_true",
@@ -618,6 +662,7 @@ def main():
     bwd = None if args.no_backward else bench_backward(still, torch, max(3, args.steps // 4),
                                                          args.warmup)
     util = None if args.no_utility else bench_utility(still, torch)
+    nsc = None if args.no_scaling else bench_n_scaling(still, torch)
     cpu = None if args.no_cpu else cpu_baseline(pre["raw"], cfg)
     tok_s = pre["tokens"] / (pre["ms"] * 1e-3)
     line = {
@@ -637,6 +682,7 @@ def main():
         "decode_ragged": dec_r,
         "backward": bwd,
         "future_kv_utility": util,
+        "n_scaling": nsc,
     }
     print(json.dumps(line), flush=True)
 

@@ -85,6 +85,34 @@ def compare_cache(gc, oc, cfg, n_tok, tol):
 def test_prefill_handoff_then_decode(gpu_lib, name, general):
     cfg, N0, seed = DEC_CASES[name]
     say(f"[decode] case={name} general={general} shape={workloads.shape_of(cfg)} N0={N0} seed={seed}")
+    run_handoff_decode(gpu_lib, cfg, N0, seed, general)
+
+
+# Budget certification past N_max (full text App. A.4): the quota re-derived
+# from the deployment length, lambda(N) = floor((m - W) / ceil(N / C)), keeps
+# the selected cache within m - W rows for N > N_max.  The cache is given
+# exactly m - W rows; the prefill and every decode step to N must fit.
+BUDGET_CASES = {
+    # name: (m, N_max, cfg without topk, N0, seed)
+    "bf16_d128": (64 + 80, 320, make_case("j", 1, 640, 4, 2, 128, 64, 64, 0), 560, 45),
+    "f32_d64": (16 + 64, 128, make_case("k", 1, 256, 2, 1, 64, 16, 16, 0, dtype="f32"), 200, 46),
+}
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
+@pytest.mark.parametrize("name", list(BUDGET_CASES))
+def test_budget_past_n_max(gpu_lib, name, general):
+    m, n_max, base, N0, seed = BUDGET_CASES[name]
+    W, C, N = base["window"], base["chunk"], base["seqlen"]
+    lam_static = gpu_lib.topk_for_budget(m, W, C, n_max)
+    lam = gpu_lib.topk_for_budget(m, W, C, N)
+    assert lam == O.topk_for_budget(m, W, C, N) and 0 < lam < lam_static
+    cfg = dict(base, topk=lam)
+    say(f"[budget] case={name} general={general} m={m} N_max={n_max} N={N} topk {lam_static} -> {lam}")
+    run_handoff_decode(gpu_lib, cfg, N0, seed, general, cap=m - W)
+
+
+def run_handoff_decode(gpu_lib, cfg, N0, seed, general, cap=None):
     raw = workloads.make_prefill(cfg, seed)
     dt = torch_dtype(cfg["dtype"])
     dev, ref = prepare(raw, dt)
@@ -92,7 +120,8 @@ def test_prefill_handoff_then_decode(gpu_lib, name, general):
     Hq, Hkv, d = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
     p = O.Params(window=W, chunk=C, topk=lam)
-    cap = p.topk_eff() * (-(-N // C)) + 1
+    if cap is None:
+        cap = p.topk_eff() * (-(-N // C)) + 1
     tol = F32_TOL if cfg["dtype"] == "f32" else BF16_TOL
     state_tol = 1e-5
 
@@ -150,6 +179,8 @@ def test_prefill_handoff_then_decode(gpu_lib, name, general):
                 oc["win_route"][:, :, slots] = gf[:, :, slots]
     say(f"  {N - N0} steps, worst step rel-L2 {worst:.3e}")
     compare_cache(gc, oc, cfg, N, state_tol)
+    if lam > 0:
+        assert int(gc.sel_count.max()) <= cap
 
 
 def test_cache_checkpoint_restore_is_bit_exact(gpu_lib):
