@@ -39,7 +39,10 @@ using namespace mt;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kKW = 4;  // waves per block: 128 keys
+// key kernels: the window kernel's block takes kWinKPB key chunks (two
+// waves per chunk), the selected kernel's kSelW waves of 32 compact rows
+constexpr int kWinKPB = 2;
+constexpr int kSelW = 4;
 
 // staged query tile of one head: rows t0 .. t0 + 63 (zero past N)
 struct QTile {
@@ -51,17 +54,16 @@ struct QTile {
     float dd[kC];         // D = dout . out
 };
 
+template <int NTHR>
 __device__ __forceinline__ void stage_qtile(QTile& T, const bf16* __restrict__ q,
                                             const bf16* __restrict__ dout,
                                             const float* __restrict__ stat, const Dims& D, int b,
-                                            int t0, int h, int tid, int nthr) {
+                                            int t0, int h, int tid) {
     const int nv = min(kC, D.N - t0);
     const size_t ld = (size_t)D.Hq * kD;
     const size_t o = (((size_t)b * D.N + t0) * D.Hq + h) * kD;
-    load_k_tile(q + o, ld, nv, T.qs, tid, nthr);
-    load_k_tile(dout + o, ld, nv, T.ds, tid, nthr);
-    load_vt_tile(q + o, ld, nv, T.qt, tid, nthr);
-    load_vt_tile(dout + o, ld, nv, T.dt, tid, nthr);
+    load_tile_both<NTHR>(q + o, ld, nv, T.qs, T.qt, tid);
+    load_tile_both<NTHR>(dout + o, ld, nv, T.ds, T.dt, tid);
     if (tid < kC) {
         float a = 0.f, dd = 0.f;
         if (tid < nv) {
@@ -124,18 +126,18 @@ __device__ __forceinline__ void load_key_operand(const bf16* __restrict__ row, b
 }
 
 // window keys: block = 128 keys of chunks 2 cb, 2 cb + 1 of (b, g)
-template <int NWT>
-__global__ __launch_bounds__(kKW * 64) void bwd_kv_window_kernel(
+template <int NWT, int KPB>
+__global__ __launch_bounds__(KPB * 128) void bwd_kv_window_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const uint8_t* __restrict__ route, const float* __restrict__ stat,
     float* __restrict__ dk, float* __restrict__ dv, Dims D) {
-    const int npair = (D.T + 1) / 2;
+    const int npair = (D.T + KPB - 1) / KPB;
     const int cb = (int)(blockIdx.x % npair);
     const int bgi = (int)(blockIdx.x / npair);
     const int g = bgi % D.Hkv, b = bgi / D.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ck = 2 * cb + (wave >> 1);           // this wave's key chunk
+    const int ck = KPB * cb + (wave >> 1);         // this wave's key chunk
     const int ok = 32 * (wave & 1) + col;          // the lane's key offset in it
     const int j = ck * kC + ok;
     const bool kvalid = j < D.N;
@@ -151,13 +153,13 @@ __global__ __launch_bounds__(kKW * 64) void bwd_kv_window_kernel(
     for (int dt = 0; dt < 4; ++dt) dva[dt] = dka[dt] = zero16();
 
     __shared__ QTile T;
-    const int c_first = 2 * cb, c_last = min(D.T - 1, 2 * cb + 1 + NWT);
+    const int c_first = KPB * cb, c_last = min(D.T - 1, KPB * cb + KPB - 1 + NWT);
     for (int qc = c_first; qc <= c_last; ++qc) {
         const int i = qc - ck;  // query chunk relative to this wave's key chunk
         const int t0 = qc * kC;
         for (int hh = 0; hh < D.G; ++hh) {
             __syncthreads();
-            stage_qtile(T, q, dout, stat, D, b, t0, g * D.G + hh, tid, kKW * 64);
+            stage_qtile<KPB * 128>(T, q, dout, stat, D, b, t0, g * D.G + hh, tid);
             __syncthreads();
             if (i < 0 || i > NWT || ck >= D.T) continue;
             const int nq = min(kC, D.N - t0);
@@ -191,19 +193,19 @@ __global__ __launch_bounds__(kKW * 64) void bwd_kv_window_kernel(
 }
 
 // selected keys: block = 128 consecutive compact rows of (b, g)
-template <int NWT>
-__global__ __launch_bounds__(kKW * 64) void bwd_kv_selected_kernel(
+template <int NWT, int KW>
+__global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ ksel, const bf16* __restrict__ vsel,
     const bf16* __restrict__ dout, const int32_t* __restrict__ selw, const int* __restrict__ list_off,
     const float* __restrict__ stat, float* __restrict__ dk, float* __restrict__ dv, Dims D) {
-    const int ntile = (D.n_full * D.lam + kKW * 32 - 1) / (kKW * 32);
+    const int ntile = (D.n_full * D.lam + KW * 32 - 1) / (KW * 32);
     const int tb = (int)(blockIdx.x % ntile);
     const int bgi = (int)(blockIdx.x / ntile);
     const int g = bgi % D.Hkv, b = bgi / D.Hkv;
     const size_t bg = (size_t)b * D.Hkv + g;
     const int* loff = list_off + bg * (D.n_full + 1);
     const int total = loff[D.n_full];
-    const int r_blk = tb * kKW * 32;
+    const int r_blk = tb * KW * 32;
     if (r_blk >= total) return;  // every wave of the block leaves together
     const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(kKW * 64) void bwd_kv_selected_kernel(
         const int nq = min(kC, D.N - t0);
         for (int hh = 0; hh < D.G; ++hh) {
             __syncthreads();
-            stage_qtile(T, q, dout, stat, D, b, t0, g * D.G + hh, tid, kKW * 64);
+            stage_qtile<KW * 64>(T, q, dout, stat, D, b, t0, g * D.G + hh, tid);
             __syncthreads();
             if (32 * wave >= nvis) continue;
             const bool rv = rvalid && 32 * wave + col < nvis;
@@ -373,9 +375,8 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
             hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
         }
         __syncthreads();  // the previous tile's reads are done
-        load_k_tile(srck, ldkv, nv, ks, tid, NW * 64);
-        load_k_tile(srcv, ldkv, nv, vs, tid, NW * 64);
-        load_vt_tile(srck, ldkv, nv, kt, tid, NW * 64);
+        load_tile_both<NW * 64>(srck, ldkv, nv, ks, kt, tid);
+        load_rows<NW * 64>(srcv, ldkv, nv, vs, tid);
         __syncthreads();
         f32x16 sc[2], dp[2];
 #pragma unroll
@@ -1118,9 +1119,9 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
     const bf16* dd = reinterpret_cast<const bf16*>(dout);
     const int nwt = D.W / kC;
     if (phase == 0) {
-        const unsigned nblk = (unsigned)((D.T + 1) / 2) * D.B * D.Hkv;
+        const unsigned nblk = (unsigned)((D.T + kWinKPB - 1) / kWinKPB) * D.B * D.Hkv;
 #define STILL_KVW(NWT)                                                                           \
-    hipLaunchKernelGGL((bwd_kv_window_kernel<NWT>), dim3(nblk), dim3(kKW * 64), 0, s, qq,       \
+    hipLaunchKernelGGL((bwd_kv_window_kernel<NWT, kWinKPB>), dim3(nblk), dim3(kWinKPB * 128), 0, s, qq, \
                        reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(v), dd,  \
                        route, stat, dk, dv, D)
         if (nwt == 1) STILL_KVW(1);
@@ -1130,10 +1131,10 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
         return hipGetLastError();
     }
     if (D.lam == 0 || D.n_full == 0) return hipSuccess;
-    const int ntile = (D.n_full * D.lam + kKW * 32 - 1) / (kKW * 32);
+    const int ntile = (D.n_full * D.lam + kSelW * 32 - 1) / (kSelW * 32);
     const unsigned nblk = (unsigned)ntile * D.B * D.Hkv;
 #define STILL_KVS(NWT)                                                                           \
-    hipLaunchKernelGGL((bwd_kv_selected_kernel<NWT>), dim3(nblk), dim3(kKW * 64), 0, s, qq,     \
+    hipLaunchKernelGGL((bwd_kv_selected_kernel<NWT, kSelW>), dim3(nblk), dim3(kSelW * 64), 0, s, qq, \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
                        dd, selw, list_off, stat, dk, dv, D)
     if (nwt == 1) STILL_KVS(1);

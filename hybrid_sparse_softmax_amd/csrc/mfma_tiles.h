@@ -77,5 +77,60 @@ __device__ __forceinline__ void load_vt_tile64(const bf16* __restrict__ src, siz
     }
 }
 
+// 64 rows x 128 columns of a row-major bf16 matrix into LDS twice, in one
+// round trip per thread: row-major (dst[row * kKS + col]) and transposed
+// (dst_t[col * kVS + kperm(row)]); rows >= nvalid are zero.  Each task loads
+// rows 4 kq .. 4 kq + 3, columns 8 oct .. 8 oct + 7 and stores them both
+// ways; the loads of all a thread's tasks are issued before any store.
+template <int NTHR>
+__device__ __forceinline__ void load_tile_both(const bf16* __restrict__ src, size_t ld, int nvalid,
+                                               bf16* __restrict__ dst, bf16* __restrict__ dst_t, int tid) {
+    constexpr int NT = 256 / NTHR;  // tasks per thread
+    bf16x8 r[NT][4];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int x = tid + NTHR * u, kq = x & 15, oct = x >> 4;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int row = 4 * kq + rr;
+            r[u][rr] = row < nvalid ? ld_bf8(src + (size_t)row * ld + 8 * oct) : zero_bf8();
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int x = tid + NTHR * u, kq = x & 15, oct = x >> 4;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) st_bf8(dst + (4 * kq + rr) * kKS + 8 * oct, r[u][rr]);
+        const int pos = kperm(4 * kq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bf16x4 t4;
+            t4[0] = r[u][0][e];
+            t4[1] = r[u][1][e];
+            t4[2] = r[u][2][e];
+            t4[3] = r[u][3][e];
+            *reinterpret_cast<bf16x4*>(dst_t + (8 * oct + e) * kVS + pos) = t4;
+        }
+    }
+}
+
+// 64 rows x 128 columns row-major into LDS (stride kKS), loads first
+template <int NTHR>
+__device__ __forceinline__ void load_rows(const bf16* __restrict__ src, size_t ld, int nvalid,
+                                          bf16* __restrict__ dst, int tid) {
+    constexpr int NT = kC * 16 / NTHR;
+    bf16x8 r[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int x = tid + NTHR * u, row = x >> 4, piece = x & 15;
+        r[u] = row < nvalid ? ld_bf8(src + (size_t)row * ld + 8 * piece) : zero_bf8();
+    }
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int x = tid + NTHR * u, row = x >> 4, piece = x & 15;
+        st_bf8(dst + row * kKS + 8 * piece, r[u]);
+    }
+}
+
 }  // namespace mt
 }  // namespace still
