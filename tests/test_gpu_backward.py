@@ -14,10 +14,13 @@ index shows up at 1e-2 or more.
 
 The matrix-core path (bf16 storage, d = 128, chunk 64, window 64 / 128 /
 256, 1 / 2 / 4 / 8 query heads per KV head) takes the statistics from the
-forward's bf16 pass (probabilities rounded to bf16) and rounds dS to bf16
-before its product with K, so its gradients carry bf16 operand rounding
-(2^-9 relative per term): its bar is MFMA_GRAD_TOL per tensor, and every
-case also runs on the fp32 general kernels at 1e-4."""
+forward's bf16 pass (probabilities rounded to bf16), rounds dS and P to bf16
+before their products, and runs the linear terms (bf16 prefix states,
+features and chunk sums), the NP-Map backward (bf16 P^T and du) and the
+projection gradients (bf16 du) on the matrix cores too, so its gradients
+carry bf16 operand rounding (2^-9 relative per term): its bar is
+MFMA_GRAD_TOL per tensor, and every case also runs on the fp32 general
+kernels at 1e-4."""
 import numpy as np
 import pytest
 import torch
