@@ -1028,11 +1028,11 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_kv_win")) != hipSuccess) return e;
         if ((e = launch_bwd_kv(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw, w.list_off,
-                               w.stat, a.dk, a.dv, 0, s)) != hipSuccess)
+                               w.stat, a.dk, a.dv, w.kvpart, 0, s)) != hipSuccess)
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_kv_sel")) != hipSuccess) return e;
         if ((e = launch_bwd_kv(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw, w.list_off,
-                               w.stat, a.dk, a.dv, 1, s)) != hipSuccess)
+                               w.stat, a.dk, a.dv, w.kvpart, 1, s)) != hipSuccess)
             return e;
     } else {
     STILL_STEP("bwd_key_win",

@@ -192,15 +192,26 @@ __global__ __launch_bounds__(KPB * 128) void bwd_kv_window_kernel(
         }
 }
 
-// selected keys: block = 128 consecutive compact rows of (b, g)
+// selected keys: block = 128 consecutive compact rows of (b, g) and one of
+// kSelSeg segments of the query chunks after their window (rows of early
+// chunks meet many more query chunks than late ones; the segments spread
+// that work over blocks).  Segment 0 adds its sums to dk and dv; the others
+// write theirs to part [kSelSeg - 1][B, Hkv, n_full lam][2 d] (zeros for an
+// empty segment), which bwd_kv_merge_kernel adds afterwards: no atomics, a
+// fixed order of summation.
+constexpr int kSelSeg = 2;
 template <int NWT, int KW>
 __global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ ksel, const bf16* __restrict__ vsel,
     const bf16* __restrict__ dout, const int32_t* __restrict__ selw, const int* __restrict__ list_off,
-    const float* __restrict__ stat, float* __restrict__ dk, float* __restrict__ dv, Dims D) {
-    const int ntile = (D.n_full * D.lam + KW * 32 - 1) / (KW * 32);
-    const int tb = (int)(blockIdx.x % ntile);
-    const int bgi = (int)(blockIdx.x / ntile);
+    const float* __restrict__ stat, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ part, Dims D) {
+    // blocks in order of (row tile, segment), every (b, g) side by side:
+    // earlier row tiles meet more query chunks, so the longest go first
+    const int nbg = D.B * D.Hkv;
+    const int bgi = (int)(blockIdx.x % nbg);
+    const int sg = (int)((blockIdx.x / nbg) % kSelSeg);
+    const int tb = (int)(blockIdx.x / nbg / kSelSeg);
     const int g = bgi % D.Hkv, b = bgi / D.Hkv;
     const size_t bg = (size_t)b * D.Hkv + g;
     const int* loff = list_off + bg * (D.n_full + 1);
@@ -231,11 +242,15 @@ __global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
     for (int dt = 0; dt < 4; ++dt) dva[dt] = dka[dt] = zero16();
 
     // the block's first row belongs to chunk c0; query chunk qc sees the
-    // rows of chunks <= qc - NWT - 1
+    // rows of chunks <= qc - NWT - 1; this block takes segment sg of the
+    // query chunks c0 + NWT + 1 .. T - 1
     int c0 = 0;
     while (c0 + 1 < D.n_full && loff[c0 + 1] <= r_blk) ++c0;
+    const int qa = c0 + NWT + 1, nq_all = max(0, D.T - qa);
+    const int seg_len = (nq_all + kSelSeg - 1) / kSelSeg;
+    const int q_lo = qa + sg * seg_len, q_hi = min(D.T, q_lo + seg_len);
     __shared__ QTile T;
-    for (int qc = c0 + NWT + 1; qc < D.T; ++qc) {
+    for (int qc = q_lo; qc < q_hi; ++qc) {
         const int nvis = loff[min(qc - NWT, D.n_full)] - r_blk;  // visible rows: a prefix
         const int t0 = qc * kC;
         const int nq = min(kC, D.N - t0);
@@ -249,6 +264,24 @@ __global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
         }
     }
     if (!rvalid) return;
+    if (sg > 0) {
+        float* pr = part + (((size_t)(sg - 1) * D.B * D.Hkv + bg) * ((size_t)D.n_full * D.lam) + r) * (2 * kD);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int e = 32 * dt + acc_row(4 * v4, hf);
+                f32x4 a4, b4;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    a4[jj] = D.tau * dka[dt][4 * v4 + jj];
+                    b4[jj] = dva[dt][4 * v4 + jj];
+                }
+                *reinterpret_cast<f32x4*>(pr + e) = a4;
+                *reinterpret_cast<f32x4*>(pr + kD + e) = b4;
+            }
+        return;
+    }
     const size_t o = (((size_t)b * D.N + pos) * D.Hkv + g) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -265,6 +298,34 @@ __global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
             *reinterpret_cast<f32x4*>(dk + o + e) = a4;
             *reinterpret_cast<f32x4*>(dv + o + e) = b4;
         }
+}
+
+// Adds the later segments' sums of every compact row to dk and dv of its
+// position: one wave per row, four floats per lane (dk then dv).
+__global__ __launch_bounds__(256) void bwd_kv_merge_kernel(const float* __restrict__ part,
+                                                           const int32_t* __restrict__ selw,
+                                                           const int* __restrict__ list_off,
+                                                           float* __restrict__ dk, float* __restrict__ dv,
+                                                           Dims D) {
+    const int g = blockIdx.y, b = blockIdx.z;
+    const size_t bg = (size_t)b * D.Hkv + g;
+    const int* loff = list_off + bg * (D.n_full + 1);
+    const int total = loff[D.n_full];
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (r >= total) return;
+    int lo = 0, hi = D.n_full;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (loff[mid] <= r) lo = mid;
+        else hi = mid;
+    }
+    const int pos = selw[(bg * D.n_full + lo) * D.lam + (r - loff[lo])];
+    const size_t rows = (size_t)D.n_full * D.lam;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sg = 1; sg < kSelSeg; ++sg)
+        acc += *reinterpret_cast<const f32x4*>(part + (((size_t)(sg - 1) * D.B * D.Hkv + bg) * rows + r) * (2 * kD) + 4 * lane);
+    float* dst = (lane < kD / 4 ? dk : dv) + (((size_t)b * D.N + pos) * D.Hkv + g) * kD + 4 * (lane % (kD / 4));
+    *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(dst) + acc;
 }
 
 
@@ -1111,10 +1172,14 @@ hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, co
     return hipGetLastError();
 }
 
+size_t bwd_kv_part_floats(const Dims& D) {
+    return (size_t)(kSelSeg - 1) * D.B * D.Hkv * D.n_full * D.lam * (2 * kD);
+}
+
 hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,
                          const int32_t* selw, const int* list_off, const float* stat, float* dk,
-                         float* dv, int phase, hipStream_t s) {
+                         float* dv, float* part, int phase, hipStream_t s) {
     const bf16* qq = reinterpret_cast<const bf16*>(q);
     const bf16* dd = reinterpret_cast<const bf16*>(dout);
     const int nwt = D.W / kC;
@@ -1132,15 +1197,19 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
     }
     if (D.lam == 0 || D.n_full == 0) return hipSuccess;
     const int ntile = (D.n_full * D.lam + kSelW * 32 - 1) / (kSelW * 32);
-    const unsigned nblk = (unsigned)ntile * D.B * D.Hkv;
+    const unsigned nblk = (unsigned)ntile * kSelSeg * D.B * D.Hkv;
 #define STILL_KVS(NWT)                                                                           \
     hipLaunchKernelGGL((bwd_kv_selected_kernel<NWT, kSelW>), dim3(nblk), dim3(kSelW * 64), 0, s, qq, \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       dd, selw, list_off, stat, dk, dv, D)
+                       dd, selw, list_off, stat, dk, dv, part, D)
     if (nwt == 1) STILL_KVS(1);
     else if (nwt == 2) STILL_KVS(2);
     else STILL_KVS(4);
 #undef STILL_KVS
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || kSelSeg == 1) return e;
+    hipLaunchKernelGGL(bwd_kv_merge_kernel, dim3((D.n_full * D.lam + 3) / 4, D.Hkv, D.B), dim3(256), 0, s,
+                       part, selw, list_off, dk, dv, D);
     return hipGetLastError();
 }
 

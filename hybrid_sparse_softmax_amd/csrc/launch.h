@@ -114,11 +114,13 @@ hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, cons
                                const float* gate, const int* list_off, const void* dout,
                                float* stat, float* phiq, hipStream_t s);
 // softmax part of dk and dv: phase 0 the window keys (dk written, dv added
-// to), phase 1 the selected keys over the compact rows (both added to)
+// to), phase 1 the selected keys over the compact rows (both added to; part:
+// bwd_kv_part_floats(D) floats of segment sums, then merged)
+size_t bwd_kv_part_floats(const Dims& D);
 hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,
                          const int32_t* selw, const int* list_off, const float* stat, float* dk,
-                         float* dv, int phase, hipStream_t s);
+                         float* dv, float* part, int phase, hipStream_t s);
 // linear terms of the keys on the matrix cores: phase 0 the chunk sums
 // ust [B, Hkv, T, d' (d + 1)] (fp32, [i][e] then u; the suffix kernel turns
 // them into suffix sums), phase 1 dv (written: the linear part) and dphik
@@ -198,6 +200,7 @@ struct BwdWork {
     void* phik16;         // [B, Hkv, N, d'] bf16 (kperm features)
     void* wsplit;         // NP-Map projections as bf16 high / low parts
     LinBufs lin16;        // linear prefixes of the matrix-core path
+    float* kvpart;        // segment sums of the selected keys' dk, dv
 };
 // called before each launch with the kernel's name (per-launch events)
 struct BwdMark {

@@ -434,6 +434,7 @@ static BwdWork carve_bwd(const Dims& D, Carver& cv, bool mfma) {
     w.selw = cv.take<int32_t>(BG * D.n_full * D.lam);
     w.mfma = mfma;
     w.ksel = w.vsel = w.phik16 = w.wsplit = nullptr;
+    w.kvpart = nullptr;
     w.list_off = nullptr;
     w.lin16 = LinBufs{};
     if (mfma) {
@@ -450,6 +451,7 @@ static BwdWork carve_bwd(const Dims& D, Carver& cv, bool mfma) {
         w.lin16.gh = cv.take<uint16_t>(BG * ngroups * (size_t)D.d * D.fd);
         w.lin16.gz = cv.take<float>(BG * ngroups * (size_t)D.fd);
         w.wsplit = cv.take<uint16_t>((size_t)4 * D.Hkv * (D.fd / 2) * D.d);
+        w.kvpart = cv.take<float>(bwd_kv_part_floats(D));
     }
     return w;
 }
