@@ -46,6 +46,10 @@ KERNEL_SOURCES = {
     "bwd_query": ["hybrid_sparse_softmax_amd/csrc/backward.hip",
                   "hybrid_sparse_softmax_amd/csrc/device_common.h",
                   "hybrid_sparse_softmax_amd/csrc/row_ops.h"],
+    "bwd_dq": ["hybrid_sparse_softmax_amd/csrc/backward_mfma.hip",
+               "hybrid_sparse_softmax_amd/csrc/mfma_tiles.h",
+               "hybrid_sparse_softmax_amd/csrc/mfma_common.h",
+               "hybrid_sparse_softmax_amd/csrc/device_common.h"],
     "bwd_kv_sel": ["hybrid_sparse_softmax_amd/csrc/backward_mfma.hip",
                    "hybrid_sparse_softmax_amd/csrc/mfma_tiles.h",
                    "hybrid_sparse_softmax_amd/csrc/mfma_common.h",
