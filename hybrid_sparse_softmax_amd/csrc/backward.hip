@@ -38,10 +38,11 @@
 //   np_vjp_kernel      NP-Map backward per (token, KV group): dx += ..., du
 //   dw_partial_kernel  dP = sum du x^T over a slice of tokens
 //   dw_reduce_kernel   sum of the slices
-// On the matrix-core path (bf16, d = 128, chunk 64) the statistics, the
-// softmax parts of dq, dk and dv, the NP-Map backward and the projection
-// gradients run as MFMA kernels (prefill_mfma.hip, backward_mfma.hip); the
-// linear terms stay here.
+// On the matrix-core path (bf16, d = 128, W and C multiples of 64 up to 256,
+// C <= W) every gradient term, the statistics, the NP-Map backward and the
+// projection gradients run as MFMA kernels (prefill_mfma.hip,
+// backward_mfma.hip) over 64-token tiles; bwd_route and bwd_suffix are
+// shared with the general path.
 #include "device_common.h"
 #include "launch.h"
 #include "row_ops.h"
@@ -958,23 +959,31 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     STILL_STEP("bwd_route", hipLaunchKernelGGL(bwd_route_kernel, dim3(D.T, D.Hkv, D.B), dim3(256),
                                                (size_t)D.C * sizeof(int), s, a.sel_idx, w.route,
                                                w.selw, D));
+    // the matrix-core kernels after the lists work in 64-token tiles (DT: the
+    // tile dimensions, D itself when C = 64)
+    const Dims& DT = w.tile;
     if (w.mfma) {
         // first pass and the softmax part of dq on the matrix cores
         if ((e = mark.fn(mark.ctx, "bwd_lists")) != hipSuccess) return e;
-        if ((e = launch_bwd_lists(D, w.selw, a.k, a.v, w.ksel, w.vsel, w.list_off, a.wq, a.wk, w.wsplit,
-                                  s)) != hipSuccess)
+        if (D.C > 64) {
+            if ((e = launch_bwd_lists_tiles(D, DT, w.selw, a.k, a.v, w.selw_t, w.ksel, w.vsel, w.list_off,
+                                            a.wq, a.wk, w.wsplit, s)) != hipSuccess)
+                return e;
+        } else if ((e = launch_bwd_lists(D, w.selw, a.k, a.v, w.ksel, w.vsel, w.list_off, a.wq, a.wk,
+                                         w.wsplit, s)) != hipSuccess) {
             return e;
+        }
         if ((e = mark.fn(mark.ctx, "la_state")) != hipSuccess) return e;
-        if ((e = launch_la_state(D, a.k, a.v, w.wsplit, w.route, w.phik16, w.lin16, -1, s)) != hipSuccess)
+        if ((e = launch_la_state(DT, a.k, a.v, w.wsplit, w.route, w.phik16, w.lin16, -1, s)) != hipSuccess)
             return e;
         if ((e = mark.fn(mark.ctx, "la_scan16")) != hipSuccess) return e;
-        if ((e = launch_la_group_scan(D, w.lin16, -1, nullptr, nullptr, s)) != hipSuccess) return e;
+        if ((e = launch_la_group_scan(DT, w.lin16, -1, nullptr, nullptr, s)) != hipSuccess) return e;
         if ((e = mark.fn(mark.ctx, "bwd_stats")) != hipSuccess) return e;
-        if ((e = launch_hybrid_stats(D, a.q, a.k, a.v, w.wsplit, w.phik16, w.route, w.ksel, w.vsel,
+        if ((e = launch_hybrid_stats(DT, a.q, a.k, a.v, w.wsplit, w.phik16, w.route, w.ksel, w.vsel,
                                      w.lin16, a.gate, w.list_off, a.dout, w.stat, w.phiq, s)) != hipSuccess)
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_dq")) != hipSuccess) return e;
-        if ((e = launch_bwd_dq(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.list_off, w.stat,
+        if ((e = launch_bwd_dq(DT, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.list_off, w.stat,
                                w.phik16, w.lin16, a.gate, w.phiq, a.dq, w.dphiq,
                                a.gate ? a.dgate : nullptr, s)) != hipSuccess)
             return e;
@@ -1008,7 +1017,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 #undef STILL_BWD_QUERY
     if (w.mfma) {
         if ((e = mark.fn(mark.ctx, "bwd_uchunk")) != hipSuccess) return e;
-        if ((e = launch_bwd_key_lin(D, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, w.dphik,
+        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, w.dphik,
                                     0, s)) != hipSuccess)
             return e;
     } else {
@@ -1018,20 +1027,20 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     }
     STILL_STEP("bwd_suffix",
                hipLaunchKernelGGL(bwd_suffix_kernel, dim3((D.fd * (D.d + 1) + 255) / 256, D.Hkv, D.B),
-                                  dim3(256), 0, s, w.ust, D));
+                                  dim3(256), 0, s, w.ust, w.mfma ? DT : D));
     if (w.mfma) {
         // linear terms first (dv, dphi_k), then the softmax terms on the matrix
         // cores: window keys (write dk, add to dv), then selected keys (add)
         if ((e = mark.fn(mark.ctx, "bwd_key_la")) != hipSuccess) return e;
-        if ((e = launch_bwd_key_lin(D, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, w.dphik,
+        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, w.dphik,
                                     1, s)) != hipSuccess)
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_kv_win")) != hipSuccess) return e;
-        if ((e = launch_bwd_kv(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw, w.list_off,
+        if ((e = launch_bwd_kv(DT, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw_t, w.list_off,
                                w.stat, a.dk, a.dv, w.kvpart, 0, s)) != hipSuccess)
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_kv_sel")) != hipSuccess) return e;
-        if ((e = launch_bwd_kv(D, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw, w.list_off,
+        if ((e = launch_bwd_kv(DT, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw_t, w.list_off,
                                w.stat, a.dk, a.dv, w.kvpart, 1, s)) != hipSuccess)
             return e;
     } else {

@@ -64,15 +64,26 @@ hipError_t launch_handoff(const Dims& D, const void* k, const void* v, const flo
                           const float* scores, const int32_t* sel_idx, const uint8_t* route,
                           int cap_chunk, const CacheView& c, hipStream_t s);
 
-// ---- gfx950 MFMA forward (bf16, d = d' = 128, window = chunk = 64, any topk) ----
+// ---- gfx950 MFMA forward (bf16, d = d' = 128, W in {64, 128, 256}, C in
+// {64, 128, 256} with C <= W, any topk) ----
+// The kernels below the selection work in 64-token tiles: for C > 64 they take
+// the tile dimensions (C = 64, T and n_full counted in tiles, lam per chunk of
+// the true C) and a per-tile list offset table.
 bool mfma_fwd_supported(const Dims& D);
 // scores, top-k, route flags, compact selected K/V lists [B, sel_list_rows,
 // Hkv, d], and the NP-Map projections as bf16 high/low parts:
-// wsplit = [wq hi, wq lo, wk hi, wk lo], each Hkv * (d'/2) * d elements
+// wsplit = [wq hi, wq lo, wk hi, wk lo], each Hkv * (d'/2) * d elements.
+// chunk: the true chunk length; above 64 only the scores and wsplit (D in tiles)
 hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const void* v,
                              float* scores, int32_t* sel_idx, uint8_t* route, void* ksel,
                              void* vsel, const float* wphi_q, const float* wphi_k, void* wsplit,
-                             hipStream_t s);
+                             int chunk, hipStream_t s);
+// chunks of C = 128 or 256 (D in chunks): top-lam per chunk from the scores,
+// sel_idx, route flags, compact lists (list_rows rows per sequence) and the
+// per-tile offsets loff [B, Hkv, N / 64 + 1] (rows at positions below 64 tau)
+hipError_t launch_chunk_select(const Dims& D, const float* scores, const void* k, const void* v,
+                               int32_t* sel_idx, uint8_t* route, void* ksel, void* vsel, int* loff,
+                               int list_rows, hipStream_t s);
 // Linear-attention prefixes of the MFMA path.  A state is S^T [d][d'] plus
 // z [d'] (features in kperm order), E1 = (d + 1) d' entries in fp32 form.
 // ngroups = ceil(n_full / ng) runs of ng chunks.
@@ -95,9 +106,9 @@ hipError_t launch_la_group_scan(const Dims& D, const LinBufs& L, int cap_chunk, 
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const void* wsplit, const void* phik, const uint8_t* route,
                               const void* ksel, const void* vsel, const LinBufs& L,
-                              const float* gate, void* out, hipStream_t s);
+                              const float* gate, const int* list_off, void* out, hipStream_t s);
 
-// ---- backward on the matrix cores (bf16, d = 128, C = 64, W = 64 / 128 / 256) ----
+// ---- backward on the matrix cores (bf16, d = 128, W = 64 / 128 / 256, C = 64 / 128 / 256, C <= W) ----
 bool mfma_bwd_supported(const Dims& D);
 // compact K / V lists of the selection selw (ascending, -1 padded per chunk):
 // chunk c's rows start at list_off[(b Hkv + g) (n_full + 1) + c]; also the
@@ -105,6 +116,12 @@ bool mfma_bwd_supported(const Dims& D);
 hipError_t launch_bwd_lists(const Dims& D, const int32_t* selw, const void* k, const void* v,
                             void* ksel, void* vsel, int* list_off, const float* wq, const float* wk,
                             void* wsplit, hipStream_t s);
+// the same for chunks of C > 64 (D in chunks, DT in tiles): lists, per-tile
+// offsets list_off [B, Hkv, N / 64 + 1] and the selection by tile selw_t
+// [B, Hkv, N / 64, DT.lam] (-1 padded), so the later kernels run on DT
+hipError_t launch_bwd_lists_tiles(const Dims& D, const Dims& DT, const int32_t* selw, const void* k,
+                                  const void* v, int32_t* selw_t, void* ksel, void* vsel, int* list_off,
+                                  const float* wq, const float* wk, void* wsplit, hipStream_t s);
 // the forward's main kernel writing (m, l, D = dout . out, c) per query head
 // to stat [B, N, Hq, 4] instead of the output, and the gated NP-Map features
 // of the queries to phiq [B, N, Hq, d'] (fp32)
@@ -201,6 +218,13 @@ struct BwdWork {
     void* wsplit;         // NP-Map projections as bf16 high / low parts
     LinBufs lin16;        // linear prefixes of the matrix-core path
     float* kvpart;        // segment sums of the selected keys' dk, dv
+    // the matrix-core kernels after the lists work in 64-token tiles: tile
+    // holds those dimensions (C = 64, lam = min(lam, 64), T and n_full in
+    // tiles; the chunk dimensions themselves when C = 64) and selw_t the
+    // selection by tile (selw itself when C = 64); list_off, ust and the
+    // buffers above count tiles
+    Dims tile;
+    int32_t* selw_t;
 };
 // called before each launch with the kernel's name (per-launch events)
 struct BwdMark {

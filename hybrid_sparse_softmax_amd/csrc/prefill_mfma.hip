@@ -282,12 +282,16 @@ __device__ __forceinline__ void split_projections(const float* __restrict__ wq, 
 }
 
 // NWT = W / 64: the window of a query spans NWT chunks back from its own.
+// chunk: the true chunk length.  When it exceeds 64 (D then counts 64-token
+// tiles) the block writes its tile's scores and the projection split and
+// stops there; chunk_select_kernel selects per chunk.
 template <int NW, int NWT>
 __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     float* __restrict__ scores, int32_t* __restrict__ sel_idx, uint8_t* __restrict__ route,
     bf16* __restrict__ ksel, bf16* __restrict__ vsel, const float* __restrict__ wq,
-    const float* __restrict__ wk, bf16* __restrict__ wsplit, Dims D) {
+    const float* __restrict__ wk, bf16* __restrict__ wsplit, int chunk, Dims D) {
+    const bool score_only = chunk > kC;
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hf = lane >> 5, col = lane & 31;
     const int t0 = c * kC;
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
     // piece x = tid + 64 NW i is row x / 16, dims 8 (x % 16) .. +7
     constexpr int kVP = kC * 16 / (NW * 64);
     bf16x8 vrow[kVP];
-    if (c < D.n_full) {
+    if (c < D.n_full && !score_only) {
 #pragma unroll
         for (int i = 0; i < kVP; ++i) {
             const int x = tid + NW * 64 * i;
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
                 for (int e = 0; e < kD; ++e) kn = fmaf((float)kr[e], (float)kr[e], kn);
                 kn = sqrtf(kn);
             }
-            sig = query_free_score(D.route, kn, t0 + tid, b, g, D.Hkv, kC, D.lam);
+            sig = query_free_score(D.route, kn, t0 + tid, b, g, D.Hkv, chunk, D.lam);
         } else {
             float acc = 0.f;
             for (int hh = 0; hh < D.G; ++hh) acc += hsc[hh][tid];
@@ -451,6 +455,10 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
         }
         scores[bg * D.N + t0 + tid] = sig;
         key_s[tid] = route_key(sig);
+    }
+    if (score_only) {
+        if (c == 0 && b == 0) split_projections(wq, wk, wsplit, D.Hkv, g, NW * 64);
+        return;
     }
     __syncthreads();
     uint8_t* rt = route + bg * D.N + t0;
@@ -495,6 +503,98 @@ __global__ __launch_bounds__(NW * 64) void win_select_kernel(
             const size_t dst = list0 + ((size_t)c * D.lam + at) * ldkv + 8 * piece;
             st_bf8(ksel + dst, ld_bf8(kown + p * kKS + 8 * piece));
             st_bf8(vsel + dst, vrow[i]);
+        }
+    }
+}
+
+// Selection for chunks of C = 64 CT tokens (CT = 2 or 4; the window W >= C):
+// one block per (chunk, KV head, sequence) takes the top-lam of the chunk's
+// C window scores (written by win_select_kernel in score mode; ties to the
+// lower position), writes sel_idx, the chunk's route flags, its selected K/V
+// rows at rows c lam + rank of the compact lists (list_rows rows per
+// sequence), and the per-tile list offsets loff[tau] = number of compact rows
+// at positions below 64 tau, tau = 0 .. N / 64, for the tiles of this chunk;
+// the lists are in position order, so the selected tokens a query sees
+// beyond its window are a prefix of them.  The open chunk gets pending
+// flags and no rows; the last chunk's block writes the copy of an incomplete
+// last tile behind the selected rows (rows past N repeat token N-1; zeros
+// when N is a multiple of 64).  D holds the chunk dimensions.
+template <int CT>
+__global__ __launch_bounds__(256) void chunk_select_kernel(
+    const float* __restrict__ scores, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    int32_t* __restrict__ sel_idx, uint8_t* __restrict__ route, bf16* __restrict__ ksel,
+    bf16* __restrict__ vsel, int* __restrict__ loff, int list_rows, Dims D) {
+    constexpr int CC = kC * CT;
+    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63;
+    const size_t bg = (size_t)b * D.Hkv + g;
+    const int t0 = c * CC, n64 = D.N / kC;
+    const bool complete = c < D.n_full;
+    __shared__ int pos_s[CC];
+    __shared__ int cnt_s[CT];
+    uint8_t* rt = route + bg * D.N + t0;
+    if (tid < 64) {
+        if (complete) {
+            uint32_t kb[CT];
+            bool f[CT];
+            int at[CT];
+#pragma unroll
+            for (int r = 0; r < CT; ++r) {
+                kb[r] = key_bits(route_key(scores[bg * D.N + t0 + 64 * r + lane]));
+                f[r] = false;
+                at[r] = 0;
+            }
+            if (D.lam > 0) wave_topk<CT>(kb, CC, D.lam, f, at);
+            const size_t base = (bg * D.n_full + c) * D.lam;
+#pragma unroll
+            for (int r = 0; r < CT; ++r) {
+                rt[64 * r + lane] = f[r] ? kRouteSA : kRouteLA;
+                if (f[r]) sel_idx[base + at[r]] = t0 + 64 * r + lane;
+                pos_s[64 * r + lane] = f[r] ? at[r] : -1;
+                const int n = __popcll(__ballot(f[r]));
+                if (lane == 0) cnt_s[r] = n;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < CT; ++r) {
+                if (t0 + 64 * r + lane < D.N) rt[64 * r + lane] = kPending;
+                pos_s[64 * r + lane] = -1;
+                if (lane == 0) cnt_s[r] = 0;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid <= CT) {
+        // tiles of this chunk, and the tile right after the last chunk when
+        // that chunk is complete
+        const int tau = c * CT + tid;
+        if (tau <= n64 && (tid < CT || c == D.T - 1)) {
+            int val = D.lam * c;
+            for (int r = 0; r < tid; ++r) val += cnt_s[r];
+            loff[bg * (n64 + 1) + tau] = val;
+        }
+    }
+    const size_t ldkv = (size_t)D.Hkv * kD;
+    const size_t list0 = ((size_t)b * list_rows * D.Hkv + g) * kD;  // row 0 of (b, g)
+    if (complete) {
+        for (int x = tid; x < CC * 16; x += 256) {
+            const int p = x >> 4, piece = x & 15, at = pos_s[p];
+            if (at >= 0) {
+                const size_t src = (((size_t)b * D.N + t0 + p) * D.Hkv + g) * kD + 8 * piece;
+                const size_t dst = list0 + ((size_t)c * D.lam + at) * ldkv + 8 * piece;
+                st_bf8(ksel + dst, ld_bf8(k + src));
+                st_bf8(vsel + dst, ld_bf8(v + src));
+            }
+        }
+    }
+    if (c == D.T - 1) {
+        const size_t pad = list0 + (size_t)D.n_full * D.lam * ldkv;
+        const bool open = D.N % kC != 0;
+        const int tt0 = n64 * kC;
+        for (int x = tid; x < kC * 16; x += 256) {
+            const int p = x >> 4, piece = x & 15;
+            const size_t src = (((size_t)b * D.N + min(tt0 + p, D.N - 1)) * D.Hkv + g) * kD + 8 * piece;
+            st_bf8(ksel + pad + p * ldkv + 8 * piece, open ? ld_bf8(k + src) : zero_bf8());
+            st_bf8(vsel + pad + p * ldkv + 8 * piece, open ? ld_bf8(v + src) : zero_bf8());
         }
     }
 }
@@ -1623,18 +1723,94 @@ __global__ __launch_bounds__(256) void bwd_lists_kernel(const int32_t* __restric
     if (c == 0 && b == 0) split_projections(wq, wk, wsplit, D.Hkv, g, 256);
 }
 
+// The same lists when chunks span CT = C / 64 > 1 tiles, indexed by tile so
+// that the kernels after it work in 64-token tiles (D: chunk dimensions, DT:
+// tile dimensions, DT.lam = min(lam, 64)).  Block tau takes tile tau: its
+// selected tokens are a run of its chunk's entries of selw (ascending, valid
+// entries first), which it writes to selw_t [B, Hkv, N / 64, DT.lam] (-1
+// padded) and gathers to list rows off .. off + n - 1, off = loff[tau] = the
+// valid entries at positions below 64 tau.  Block tau = N / 64 writes the
+// total and the copy of an incomplete last tile (zeros when N is a multiple
+// of 64).  Tile 0's blocks of sequence 0 also split the NP-Map projections.
+__global__ __launch_bounds__(256) void bwd_lists_tiles_kernel(const int32_t* __restrict__ selw,
+                                                              const bf16* __restrict__ k,
+                                                              const bf16* __restrict__ v,
+                                                              int32_t* __restrict__ selw_t,
+                                                              bf16* __restrict__ ksel, bf16* __restrict__ vsel,
+                                                              int* __restrict__ list_off,
+                                                              const float* __restrict__ wq,
+                                                              const float* __restrict__ wk,
+                                                              bf16* __restrict__ wsplit, Dims D, Dims DT) {
+    const int tau = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const size_t bg = (size_t)b * D.Hkv + g;
+    const int ct = D.C / kC, cc = tau / ct, p0 = tau * kC;
+    const int32_t* sw = selw + bg * D.n_full * D.lam;
+    // valid entries of the earlier chunks, of chunk cc below p0, and of chunk
+    // cc inside the tile
+    __shared__ int red[3][256];
+    int prev = 0, below = 0, in = 0;
+    for (int i = tid; i < min(cc, D.n_full) * D.lam; i += 256) prev += sw[i] >= 0;
+    if (cc < D.n_full)
+        for (int i = tid; i < D.lam; i += 256) {
+            const int p = sw[cc * D.lam + i];
+            below += p >= 0 && p < p0;
+            in += p >= p0 && p < p0 + kC;
+        }
+    red[0][tid] = prev;
+    red[1][tid] = below;
+    red[2][tid] = in;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) {
+            red[0][tid] += red[0][tid + w];
+            red[1][tid] += red[1][tid + w];
+            red[2][tid] += red[2][tid + w];
+        }
+        __syncthreads();
+    }
+    below = red[1][0];
+    in = red[2][0];
+    const int off = red[0][0] + below;
+    if (tid == 0) list_off[bg * (DT.n_full + 1) + tau] = off;
+    const size_t ldkv = (size_t)D.Hkv * kD;
+    const size_t list0 = ((size_t)b * sel_list_rows(DT) * D.Hkv + g) * kD;
+    if (tau < DT.n_full) {
+        int32_t* st = selw_t + (bg * DT.n_full + tau) * DT.lam;
+        for (int i = tid; i < DT.lam; i += 256) st[i] = i < in ? sw[cc * D.lam + below + i] : -1;
+        for (int x = tid; x < in * 16; x += 256) {
+            const int i = x >> 4, piece = x & 15;
+            const int pos = sw[cc * D.lam + below + i];
+            const size_t src = (((size_t)b * D.N + pos) * D.Hkv + g) * kD + 8 * piece;
+            const size_t dst = list0 + (size_t)(off + i) * ldkv + 8 * piece;
+            st_bf8(ksel + dst, ld_bf8(k + src));
+            st_bf8(vsel + dst, ld_bf8(v + src));
+        }
+    } else {
+        const bool open = DT.T > DT.n_full;
+        const int t0 = DT.n_full * kC;
+        for (int x = tid; x < kC * 16; x += 256) {
+            const int p = x >> 4, piece = x & 15;
+            const size_t src = (((size_t)b * D.N + min(t0 + p, D.N - 1)) * D.Hkv + g) * kD + 8 * piece;
+            const size_t dst = list0 + (size_t)(off + p) * ldkv + 8 * piece;
+            st_bf8(ksel + dst, open ? ld_bf8(k + src) : zero_bf8());
+            st_bf8(vsel + dst, open ? ld_bf8(v + src) : zero_bf8());
+        }
+    }
+    if (tau == 0 && b == 0) split_projections(wq, wk, wsplit, D.Hkv, g, 256);
+}
+
 }  // namespace
 
 bool mfma_fwd_supported(const Dims& D) {
     return D.bf16 && D.d == kD && D.fd == kD && (D.W == kC || D.W == 2 * kC || D.W == 4 * kC) &&
-           D.C == kC &&
+           (D.C == kC || D.C == 2 * kC || D.C == 4 * kC) && D.W >= D.C &&
            (D.G == 1 || D.G == 2 || D.G == 4 || D.G == 8);
 }
 
 hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const void* v,
                              float* scores, int32_t* sel_idx, uint8_t* route, void* ksel,
                              void* vsel, const float* wphi_q, const float* wphi_k, void* wsplit,
-                             hipStream_t s) {
+                             int chunk, hipStream_t s) {
     dim3 grid(D.T, D.Hkv, D.B);
     const bf16* qq = reinterpret_cast<const bf16*>(q);
     const bf16* kk = reinterpret_cast<const bf16*>(k);
@@ -1643,7 +1819,8 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
     bf16* vs = reinterpret_cast<bf16*>(vsel);
 #define STILL_WS(NW, NWT)                                                                          \
     hipLaunchKernelGGL((win_select_kernel<NW, NWT>), grid, dim3(64 * NW), 0, s, qq, kk, vv, scores, \
-                       sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit), D)
+                       sel_idx, route, ks, vs, wphi_q, wphi_k, reinterpret_cast<bf16*>(wsplit),     \
+                       chunk, D)
     const int nwt = D.W / kC;
 #define STILL_WS_NWT(NW)          \
     do {                          \
@@ -1659,6 +1836,25 @@ hipError_t launch_win_select(const Dims& D, const void* q, const void* k, const 
     else STILL_WS_NWT(1);
 #undef STILL_WS_NWT
 #undef STILL_WS
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_select(const Dims& D, const float* scores, const void* k, const void* v,
+                               int32_t* sel_idx, uint8_t* route, void* ksel, void* vsel, int* loff,
+                               int list_rows, hipStream_t s) {
+    dim3 grid(D.T, D.Hkv, D.B);
+    const bf16* kk = reinterpret_cast<const bf16*>(k);
+    const bf16* vv = reinterpret_cast<const bf16*>(v);
+    bf16* ks = reinterpret_cast<bf16*>(ksel);
+    bf16* vs = reinterpret_cast<bf16*>(vsel);
+    if (D.C == 2 * kC)
+        hipLaunchKernelGGL(chunk_select_kernel<2>, grid, dim3(256), 0, s, scores, kk, vv, sel_idx, route, ks, vs,
+                           loff, list_rows, D);
+    else if (D.C == 4 * kC)
+        hipLaunchKernelGGL(chunk_select_kernel<4>, grid, dim3(256), 0, s, scores, kk, vv, sel_idx, route, ks, vs,
+                           loff, list_rows, D);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -1689,7 +1885,7 @@ hipError_t launch_la_group_scan(const Dims& D, const LinBufs& L, int cap_chunk, 
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const void* wsplit, const void* phik, const uint8_t* route,
                               const void* ksel, const void* vsel, const LinBufs& L,
-                              const float* gate, void* out, hipStream_t s) {
+                              const float* gate, const int* list_off, void* out, hipStream_t s) {
     const int n = D.Hkv * (kD / 2) * kD;
     const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
     const bf16* wql = wqh + n;
@@ -1702,7 +1898,7 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       L, gate, reinterpret_cast<bf16*>(out), nullptr, nullptr, nullptr, nullptr, D)
+                       L, gate, reinterpret_cast<bf16*>(out), list_off, nullptr, nullptr, nullptr, D)
 #define STILL_MAIN(H)              \
     do {                           \
         if (nwt == 1)              \
@@ -1729,6 +1925,16 @@ hipError_t launch_bwd_lists(const Dims& D, const int32_t* selw, const void* k, c
     hipLaunchKernelGGL(bwd_lists_kernel, grid, dim3(256), 0, s, selw, reinterpret_cast<const bf16*>(k),
                        reinterpret_cast<const bf16*>(v), reinterpret_cast<bf16*>(ksel),
                        reinterpret_cast<bf16*>(vsel), list_off, wq, wk, reinterpret_cast<bf16*>(wsplit), D);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_lists_tiles(const Dims& D, const Dims& DT, const int32_t* selw, const void* k,
+                                  const void* v, int32_t* selw_t, void* ksel, void* vsel, int* list_off,
+                                  const float* wq, const float* wk, void* wsplit, hipStream_t s) {
+    dim3 grid(DT.n_full + 1, D.Hkv, D.B);
+    hipLaunchKernelGGL(bwd_lists_tiles_kernel, grid, dim3(256), 0, s, selw, reinterpret_cast<const bf16*>(k),
+                       reinterpret_cast<const bf16*>(v), selw_t, reinterpret_cast<bf16*>(ksel),
+                       reinterpret_cast<bf16*>(vsel), list_off, wq, wk, reinterpret_cast<bf16*>(wsplit), D, DT);
     return hipGetLastError();
 }
 

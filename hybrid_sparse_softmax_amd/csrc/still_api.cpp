@@ -41,6 +41,25 @@ static int check_shape(const still_shape* sh, bool decode) {
     return STILL_OK;
 }
 
+// runs of consecutive chunks for the MFMA path's linear-state kernel: about
+// one block per compute unit, at most 16 chunks per run
+static int runs_of(const Dims& D) {
+    const int64_t chunks = (int64_t)D.B * D.Hkv * D.n_full;
+    const int64_t ng = chunks / 256;
+    return ng < 1 ? 1 : (ng > 16 ? 16 : (int)ng);
+}
+
+// The MFMA kernels after the selection work in 64-token tiles: the same
+// dimensions counted in tiles (lam stays per chunk of the true C).
+static Dims tile_dims(const Dims& D) {
+    Dims T = D;
+    T.C = 64;
+    T.T = (D.N + 63) / 64;
+    T.n_full = D.N / 64;
+    T.ng = runs_of(T);
+    return T;
+}
+
 static Dims make_dims(const still_shape* sh, int seqlen) {
     Dims D;
     D.B = sh->batch;
@@ -55,13 +74,7 @@ static Dims make_dims(const still_shape* sh, int seqlen) {
     D.lam = sh->topk < sh->chunk ? sh->topk : sh->chunk;
     D.T = (seqlen + D.C - 1) / D.C;
     D.n_full = seqlen / D.C;
-    {
-        // runs of consecutive chunks for the MFMA path's linear-state kernel:
-        // about one block per compute unit, at most 16 chunks per run
-        const int64_t chunks = (int64_t)D.B * D.Hkv * D.n_full;
-        const int64_t ng = chunks / 256;
-        D.ng = ng < 1 ? 1 : (ng > 16 ? 16 : (int)ng);
-    }
+    D.ng = runs_of(D);
     D.route = (int)((sh->flags & STILL_ROUTE_MASK) >> STILL_ROUTE_SHIFT);
     D.eps = sh->eps;
     D.tau = sh->softmax_scale > 0.f ? sh->softmax_scale : 1.0f / std::sqrt((float)D.d);
@@ -111,16 +124,20 @@ struct MfmaBuffers {
     int32_t* sel;
     uint8_t* route;
     void *ksel, *vsel, *phik, *wsplit;
+    int* loff;  // per-tile list offsets (chunks of more than 64 tokens)
     LinBufs lin;
 };
 
-static MfmaBuffers carve_mfma(const Dims& D, Carver& cv) {
+// D: the true dimensions; the lists and linear states are sized in tiles
+static MfmaBuffers carve_mfma(const Dims& Dc, Carver& cv) {
     MfmaBuffers f;
+    const Dims D = tile_dims(Dc);
     const size_t BG = (size_t)D.B * D.Hkv;
-    const size_t nsel = BG * D.n_full * D.lam;
+    const size_t nsel = BG * Dc.n_full * Dc.lam;
     f.scores = cv.take<float>(BG * D.N);
     f.sel = cv.take<int32_t>(nsel);
     f.route = cv.take<uint8_t>(BG * D.N);
+    f.loff = cv.take<int>(BG * (size_t)(D.n_full + 1));
     const size_t nlist = BG * (size_t)sel_list_rows(D);
     f.ksel = cv.take<uint16_t>(nlist * D.d);
     f.vsel = cv.take<uint16_t>(nlist * D.d);
@@ -215,7 +232,7 @@ struct Timeline {
     } while (0)
 
 static int fwd_launches(const Dims& D, const still_shape* sh, bool with_cache) {
-    if (use_mfma(D, sh)) return 4 + (with_cache ? 1 : 0);
+    if (use_mfma(D, sh)) return 4 + (D.C > 64 ? 1 : 0) + (with_cache ? 1 : 0);
     return 6 + (D.W > 0 ? 1 : 0) + (with_cache ? 1 : 0);
 }
 
@@ -249,15 +266,27 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
         MfmaBuffers f = carve_mfma(D, cv);
         float* scores = scores_opt ? scores_opt : f.scores;
         int32_t* sel = sel_idx_opt ? sel_idx_opt : f.sel;
+        // chunks of C > 64: scores per 64-token tile, selection per chunk,
+        // everything after it in tiles (cap_tile: the last tile of chunk cap_chunk)
+        const bool wide = D.C > 64;
+        const Dims DT = tile_dims(D);
+        const int ct = D.C / 64;
+        const int cap_tile = cap_chunk < 0 ? -1 : (cap_chunk + 1) * ct - 1;
         STILL_LAUNCH(tl, s, "win_select",
-                     launch_win_select(D, q, k, v, scores, sel, f.route, f.ksel, f.vsel, wq, wk, f.wsplit, s));
+                     launch_win_select(DT, q, k, v, scores, sel, f.route, f.ksel, f.vsel, wq, wk, f.wsplit,
+                                       D.C, s));
+        if (wide)
+            STILL_LAUNCH(tl, s, "chunk_select",
+                         launch_chunk_select(D, scores, k, v, sel, f.route, f.ksel, f.vsel, f.loff,
+                                             sel_list_rows(DT), s));
         STILL_LAUNCH(tl, s, "la_state",
-                     launch_la_state(D, k, v, f.wsplit, f.route, f.phik, f.lin, cap_chunk, s));
+                     launch_la_state(DT, k, v, f.wsplit, f.route, f.phik, f.lin, cap_tile, s));
         STILL_LAUNCH(tl, s, "la_scan",
-                     launch_la_group_scan(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
+                     launch_la_group_scan(DT, f.lin, cap_tile, cache ? cache->lin_S : nullptr,
                                           cache ? cache->lin_z : nullptr, s));
         STILL_LAUNCH(tl, s, "hybrid_main",
-                     launch_hybrid_main(D, q, k, v, f.wsplit, f.phik, f.route, f.ksel, f.vsel, f.lin, gate, out, s));
+                     launch_hybrid_main(DT, q, k, v, f.wsplit, f.phik, f.route, f.ksel, f.vsel, f.lin, gate,
+                                        wide ? f.loff : nullptr, out, s));
         if (cache)
             STILL_LAUNCH(tl, s, "handoff",
                          launch_handoff(D, k, v, wk, scores, sel, f.route, cap_chunk, view_of(cache), s));
@@ -419,6 +448,13 @@ static BwdWork carve_bwd(const Dims& D, Carver& cv, bool mfma) {
     BwdWork w;
     const size_t BN = (size_t)D.B * D.N, BG = (size_t)D.B * D.Hkv;
     const size_t E1 = (size_t)D.fd * (D.d + 1);
+    // the matrix-core kernels after the lists count 64-token tiles
+    Dims DT = D;
+    if (mfma) {
+        DT = tile_dims(D);
+        DT.lam = D.lam < 64 ? D.lam : 64;
+    }
+    w.tile = DT;
     w.nslice = bwd_slices(D, mfma);
     w.phiq = cv.take<float>(BN * D.Hq * D.fd);
     w.phik = cv.take<float>(BN * D.Hkv * D.fd);
@@ -426,32 +462,33 @@ static BwdWork carve_bwd(const Dims& D, Carver& cv, bool mfma) {
     w.stat = cv.take<float>(BN * D.Hq * 4);
     w.dphiq = cv.take<float>(BN * D.Hq * D.fd);
     w.dphik = cv.take<float>(BN * D.Hkv * D.fd);
-    w.ust = cv.take<float>(BG * D.T * E1);
+    w.ust = cv.take<float>(BG * DT.T * E1);
     w.duq = cv.take<float>(BN * D.Hq * (D.fd / 2));
     w.duk = cv.take<float>(BN * D.Hkv * (D.fd / 2));
     w.dwpart = cv.take<float>((size_t)w.nslice * D.Hkv * (D.fd / 2) * D.d);
     w.route = cv.take<uint8_t>(BG * D.N);
     w.selw = cv.take<int32_t>(BG * D.n_full * D.lam);
+    w.selw_t = D.C > 64 && mfma ? cv.take<int32_t>(BG * DT.n_full * DT.lam) : w.selw;
     w.mfma = mfma;
     w.ksel = w.vsel = w.phik16 = w.wsplit = nullptr;
     w.kvpart = nullptr;
     w.list_off = nullptr;
     w.lin16 = LinBufs{};
     if (mfma) {
-        const size_t nlist = BG * (size_t)sel_list_rows(D);
+        const size_t nlist = BG * (size_t)sel_list_rows(DT);
         w.ksel = cv.take<uint16_t>(nlist * D.d);
         w.vsel = cv.take<uint16_t>(nlist * D.d);
-        w.list_off = cv.take<int>(BG * (D.n_full + 1));
+        w.list_off = cv.take<int>(BG * (DT.n_full + 1));
         w.phik16 = cv.take<uint16_t>(BG * D.N * D.fd);
-        const size_t ngroups = D.n_full == 0 ? 0 : (size_t)(D.n_full + D.ng - 1) / D.ng;
-        w.lin16.sh = cv.take<uint16_t>(BG * D.n_full * (size_t)D.d * D.fd);
-        w.lin16.lz = cv.take<float>(BG * D.n_full * (size_t)D.fd);
+        const size_t ngroups = DT.n_full == 0 ? 0 : (size_t)(DT.n_full + DT.ng - 1) / DT.ng;
+        w.lin16.sh = cv.take<uint16_t>(BG * DT.n_full * (size_t)D.d * D.fd);
+        w.lin16.lz = cv.take<float>(BG * DT.n_full * (size_t)D.fd);
         w.lin16.ltot = cv.take<float>(BG * ngroups * E1);
         w.lin16.lcap = cv.take<float>(BG * E1);
         w.lin16.gh = cv.take<uint16_t>(BG * ngroups * (size_t)D.d * D.fd);
         w.lin16.gz = cv.take<float>(BG * ngroups * (size_t)D.fd);
         w.wsplit = cv.take<uint16_t>((size_t)4 * D.Hkv * (D.fd / 2) * D.d);
-        w.kvpart = cv.take<float>(bwd_kv_part_floats(D));
+        w.kvpart = cv.take<float>(bwd_kv_part_floats(DT));
     }
     return w;
 }

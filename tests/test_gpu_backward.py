@@ -12,8 +12,8 @@ sums have a few thousand terms, whose rounding stays near 1e-6 relative, so
 1e-4 leaves two orders of magnitude of room while a wrong term, sign or
 index shows up at 1e-2 or more.
 
-The matrix-core path (bf16 storage, d = 128, chunk 64, window 64 / 128 /
-256, 1 / 2 / 4 / 8 query heads per KV head) takes the statistics from the
+The matrix-core path (bf16 storage, d = 128, chunk 64 / 128 / 256 up to the
+window 64 / 128 / 256, 1 / 2 / 4 / 8 query heads per KV head) takes the statistics from the
 forward's bf16 pass (probabilities rounded to bf16), rounds dS and P to bf16
 before their products, and runs the linear terms (bf16 prefix states,
 features and chunk sums), the NP-Map backward (bf16 P^T and du) and the
@@ -38,8 +38,8 @@ MFMA_GRAD_TOL = 2e-2
 def mfma_path(cfg) -> bool:
     """Whether the library takes the matrix-core backward for this shape."""
     G = cfg["n_q_heads"] // cfg["n_kv_heads"]
-    return (cfg["dtype"] == "bf16" and cfg["head_dim"] == 128 and cfg["chunk"] == 64
-            and cfg["window"] in (64, 128, 256) and G in (1, 2, 4, 8))
+    return (cfg["dtype"] == "bf16" and cfg["head_dim"] == 128 and cfg["chunk"] in (64, 128, 256)
+            and cfg["window"] in (64, 128, 256) and cfg["window"] >= cfg["chunk"] and G in (1, 2, 4, 8))
 
 
 # Anti-aligned inputs (every key -a u plus noise, a = 56 against a spread of
@@ -75,6 +75,16 @@ CASES = {
     # queries with no linear term must keep finite softmax statistics
     "bf16_underflow_all_selected": (make_case("u", 1, 200, 4, 2, 128, 64, 64, 64, anti_align=56.0), 43),
     "bf16_underflow_G2": (make_case("v", 1, 300, 4, 2, 128, 64, 64, 16, anti_align=56.0), 44),
+    # windows of two and four chunks (W = 128 / 256, C = 64)
+    "bf16_W128_C64_G4": (make_case("w", 1, 450, 8, 2, 128, 128, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 46),
+    "bf16_W256_C64_G2": (make_case("x", 1, 600, 4, 2, 128, 256, 64, 8), 47),
+    # chunks of 128 / 256 tokens (the chunk-size ablation, W >= C): selection
+    # per chunk, the matrix-core kernels in 64-token tiles; lam > 64 puts up
+    # to 64 selected rows in one tile
+    "bf16_W128_C128_G4": (make_case("y", 1, 400, 8, 2, 128, 128, 128, 16, outlier_frac=0.02, heavy_scale=6.0), 48),
+    "bf16_W256_C128_G2": (make_case("z", 1, 600, 4, 2, 128, 256, 128, 40), 49),
+    "bf16_W256_C256_G1_lam100": (make_case("z", 1, 700, 2, 2, 128, 256, 256, 100), 50),
+    "bf16_W128_C128_swa_la": (make_case("z", 1, 350, 4, 1, 128, 128, 128, 0), 51),
 }
 
 
@@ -131,8 +141,9 @@ def test_bwd_matches_oracle(gpu_lib, name, general):
 
 
 @pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
-def test_bwd_ignores_repeated_and_foreign_selection_entries(gpu_lib, general):
-    cfg, seed = CASES["bf16_ragged_G2"]
+@pytest.mark.parametrize("name", ["bf16_ragged_G2", "bf16_W128_C128_G4"])
+def test_bwd_ignores_repeated_and_foreign_selection_entries(gpu_lib, name, general):
+    cfg, seed = CASES[name]
     say(f"[bwd] corrupted selection general={general} shape={workloads.shape_of(cfg)} seed={seed}")
     g, o = run(gpu_lib, cfg, seed, corrupt=True, general=general)
     compare(g, o, grad_tol(cfg, general))
@@ -261,11 +272,12 @@ def test_bwd_train_8x2k_sampled_rows_and_value_sums(gpu_lib, general):
     assert worst <= 1.0
 
 
-def test_bwd_projection_gradients_mid_size(gpu_lib):
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_bwd_projection_gradients_mid_size(gpu_lib, chunk):
     """The NP-Map projection gradients, which sum over every token of every
-    head of a KV group, at a mid size (1 x 1024, 8 / 2 heads, d 128, top-16):
-    whole tensors against the oracle, with dq, dk and dv."""
-    cfg = make_case("m", 1, 1024, 8, 2, 128, 64, 64, 16, outlier_frac=0.01, heavy_scale=6.0)
+    head of a KV group, at a mid size (1 x 1024, 8 / 2 heads, d 128, top-16,
+    W = C = 64 or 128): whole tensors against the oracle, with dq, dk and dv."""
+    cfg = make_case("m", 1, 1024, 8, 2, 128, chunk, chunk, 16, outlier_frac=0.01, heavy_scale=6.0)
     seed = 45
     for general in (False, True):
         say(f"[bwd] mid-size projections general={general} shape={workloads.shape_of(cfg)} seed={seed}")

@@ -40,6 +40,10 @@ DEC_CASES = {
     # two-chunk window (W = 128, C = 64): matrix-core prefill, then the steps
     "bf16_W128_C64_G4": (make_case("x", 1, 330 + 70, 8, 2, 128, 128, 64, 16), 330, 43),
     "bf16_W256_C64_G2": (make_case("y", 1, 450 + 70, 4, 2, 128, 256, 64, 8), 450, 44),
+    # chunks of 128 / 256 tokens: the matrix-core prefill (per-chunk selection,
+    # 64-token tiles after it) hands off mid-chunk; decode crosses chunk ends
+    "bf16_W128_C128_G4": (make_case("z", 1, 390 + 140, 8, 2, 128, 128, 128, 16), 390, 47),
+    "bf16_W256_C256_G2": (make_case("z", 1, 600 + 180, 4, 2, 128, 256, 256, 40), 600, 48),
     "f32_underflow_d64": (make_case("w", 1, 60 + 40, 4, 1, 64, 32, 16, 16, dtype="f32", anti_align=48.0),
                           60, 42),
 }

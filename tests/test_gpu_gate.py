@@ -23,6 +23,7 @@ FWD_CASES = {
     "f32_d64_W48_C16": (make_case("c", 1, 150, 4, 1, 64, 48, 16, 4, dtype="f32"), 83),
     "bf16_swa_la": (make_case("d", 1, 200, 4, 2, 128, 64, 64, 0), 84),
     "bf16_W128_G4": (make_case("j", 1, 400, 8, 2, 128, 128, 64, 16), 90),
+    "bf16_W128_C128_G4": (make_case("k", 1, 450, 8, 2, 128, 128, 128, 16), 91),
 }
 
 
@@ -154,6 +155,7 @@ BWD_CASES = {
     "bf16_G4": (make_case("g", 1, 300, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 87),
     "f32_d64_W48_C16": (make_case("h", 1, 150, 4, 1, 64, 48, 16, 4, dtype="f32"), 88),
     "bf16_swa_la": (make_case("i", 1, 200, 4, 2, 128, 64, 64, 0), 89),
+    "bf16_W128_C128_G4": (make_case("l", 1, 450, 8, 2, 128, 128, 128, 16), 92),
 }
 
 

@@ -44,6 +44,16 @@ CASES = {
     # four-chunk window (W = 256, C = 64: the widest S-NIAH window)
     "bf16_W256_C64_G4": (make_case("r", 2, 700, 8, 2, 128, 256, 64, 16, outlier_frac=0.01, heavy_scale=6.0), 37),
     "bf16_W256_C64_G2_swa_la": (make_case("s", 1, 500, 4, 2, 128, 256, 64, 0), 38),
+    # chunks of 128 and 256 tokens (the pages' chunk-size ablation runs W = C;
+    # W = 256 over C = 128 as well): the matrix-core path selects per chunk and
+    # runs everything after the selection in 64-token tiles.  Ragged tails end
+    # inside the open chunk; "lam_gt_64" ends on a complete chunk.
+    "bf16_W128_C128_G4": (make_case("z", 2, 700, 8, 2, 128, 128, 128, 16, outlier_frac=0.01, heavy_scale=6.0), 40),
+    "bf16_W256_C128_G2": (make_case("z", 1, 900, 4, 2, 128, 256, 128, 32), 41),
+    "bf16_W256_C256_G8": (make_case("z", 1, 1100, 8, 1, 128, 256, 256, 48, outlier_frac=0.01, heavy_scale=6.0), 42),
+    "bf16_W128_C128_lam_gt_64": (make_case("z", 1, 640, 4, 2, 128, 128, 128, 100), 43),
+    "bf16_W128_C128_swa_la": (make_case("z", 1, 500, 4, 1, 128, 128, 128, 0), 44),
+    "bf16_W128_C128_underflow": (make_case("z", 1, 400, 8, 2, 128, 128, 128, 16, anti_align=56.0), 45),
     # matrix-core path with two query heads per KV head, three sequences, a ragged tail
     "bf16_G2_B3_ragged": (make_case("k", 3, 777, 4, 2, 128, 64, 64, 20, outlier_frac=0.02, heavy_scale=6.0), 23),
     # keys scaled x80 at 2% of positions: logits beyond 2^128 in exp2 units, so
@@ -132,6 +142,21 @@ def test_fwd_matches_oracle(gpu_lib, name, general):
     assert serr <= 1e-4
 
 
+@pytest.mark.parametrize("W,C", [(64, 64), (128, 64), (128, 128), (256, 128), (256, 256)])
+def test_matrix_core_path_taken(gpu_lib, W, C):
+    """The pages' (W, C) settings with d = 128 in bf16 run on the matrix-core
+    kernels: the timed entry point names the launches it made."""
+    cfg = make_case("p", 1, 300, 4, 2, 128, W, C, 16)
+    dev, _ = prepare(workloads.make_prefill(cfg, 50), torch.bfloat16)
+    timer = gpu_lib.LaunchTimer()
+    gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W, chunk=C, topk=16,
+                timer=timer)
+    names = [n for n, _ in timer.durations_ms()]
+    want = ["win_select"] + (["chunk_select"] if C > 64 else []) + ["la_state", "la_scan", "hybrid_main"]
+    say(f"[path] W={W} C={C}: {names}")
+    assert names == want
+
+
 def test_fwd_is_deterministic(gpu_lib):
     cfg, seed = CASES["bf16_ragged_G4"]
     raw = workloads.make_prefill(cfg, seed)
@@ -151,17 +176,22 @@ def test_empty_sequence_is_noop(gpu_lib):
     assert res["out"].shape == (1, 0, 4, 128)
 
 
-ROUTE_CASE = (make_case("q", 1, 400, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 25)
+ROUTE_CASES = {
+    "C64": (make_case("q", 1, 400, 8, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 25),
+    # the uniform criterion's offsets depend on C; selection over 128 keys
+    "C128": (make_case("q", 1, 700, 8, 2, 128, 128, 128, 24, outlier_frac=0.02, heavy_scale=6.0), 39),
+}
 ROUTE_NAMES = ["diagonal", "qk", "keynorm", "uniform", "random"]
 
 
 @pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
 @pytest.mark.parametrize("route", ROUTE_NAMES)
-def test_routing_criteria_match_oracle(gpu_lib, route, general):
+@pytest.mark.parametrize("shape", list(ROUTE_CASES))
+def test_routing_criteria_match_oracle(gpu_lib, shape, route, general):
     """The routing criteria the pages compare with Self-Saliency: same scores,
     same selections (or near-ties the oracle adopts), same outputs."""
-    cfg, seed = ROUTE_CASE
-    say(f"[route] {route} general={general} shape={workloads.shape_of(cfg)} seed={seed}")
+    cfg, seed = ROUTE_CASES[shape]
+    say(f"[route] {route} {shape} general={general} shape={workloads.shape_of(cfg)} seed={seed}")
     raw = workloads.make_prefill(cfg, seed)
     dev, ref = prepare(raw, torch.bfloat16)
     W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
@@ -189,30 +219,33 @@ def test_routing_criteria_match_oracle(gpu_lib, route, general):
 
 @pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
 @pytest.mark.parametrize("route", ["saliency", "keynorm"])
-def test_selection_with_exact_ties(gpu_lib, route, general):
+@pytest.mark.parametrize("chunk,lam", [(64, 20), (128, 80)], ids=["C64", "C128"])
+def test_selection_with_exact_ties(gpu_lib, chunk, lam, route, general):
     """Every token of a KV head carries the same key (and every query head the
     same query), so every full-window score in a chunk is the same number:
     the top-lambda threshold falls inside one run of equal keys and the lower
-    positions must win, as the oracle's stable order says."""
-    cfg = make_case("t", 1, 300, 8, 2, 128, 64, 64, 20)
+    positions must win, as the oracle's stable order says (with C = 128 and
+    lambda = 80 the kept run spans both 64-key halves of a chunk)."""
+    C = chunk
+    cfg = make_case("t", 1, 300, 8, 2, 128, C, C, lam)
     raw = workloads.make_prefill(cfg, 32)
     raw["q"][:] = raw["q"][:, :1]
     raw["k"][:] = raw["k"][:, :1]
     dev, ref = prepare(raw, torch.bfloat16)
-    res = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=64, chunk=64,
-                      topk=20, return_scores=True, return_sel=True, general=general, route=route)
+    res = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=C, chunk=C,
+                      topk=lam, return_scores=True, return_sel=True, general=general, route=route)
     torch.cuda.synchronize()
-    p = O.Params(window=64, chunk=64, topk=20, route=route)
+    p = O.Params(window=C, chunk=C, topk=lam, route=route)
     sigma = O.window_scores(ref["q"], ref["k"], p, 2)
     osel, _ = O.select_chunks(sigma, p)
     gsel = res["sel_idx"].cpu().numpy().astype(np.int64)
     if route == "keynorm":
-        # one key norm per KV head: exact ties everywhere, the first 20 positions win
-        first = np.arange(20)[None, None, None, :] + 64 * np.arange(4)[None, None, :, None]
+        # one key norm per KV head: exact ties everywhere, the first lam positions win
+        first = np.arange(lam)[None, None, None, :] + C * np.arange(300 // C)[None, None, :, None]
         np.testing.assert_array_equal(gsel, np.broadcast_to(first, gsel.shape))
         np.testing.assert_array_equal(gsel, osel)
     else:
         # the Self-Saliency of equal full-window rows agrees to the last bits
         # only: the near-tie protocol decides, and must find nothing else
-        n_bad, worst = check_selection(gsel, sigma, osel, 64)
+        n_bad, worst = check_selection(gsel, sigma, osel, C)
         say(f"  {n_bad} chunks differ by near-ties (worst margin {worst:.2g})")
