@@ -528,6 +528,61 @@ def bench_n_scaling(still, torch, steps=5, warmup=2):
     return {"budget_m": m, "window": W, "chunk": C, "rows": rows}
 
 
+def bench_chunk_sweep(still, torch, steps=5, warmup=2, name="train_8x2k"):
+    """Cost of one training step (forward + backward) against the chunk size
+    (full text App. A.7.5, Table 14: C varied with the window spanning one
+    chunk, W = C, and 16 selected tokens per chunk), on the 8 x 2048 training
+    batch for the chunk sizes the matrix-core path takes (64, 128, 256)."""
+    cfg = workloads.CONFIGS[name]
+    seed = workloads.seed_of(name)
+    raw = workloads.make_prefill(cfg, seed)
+    dev = {k: torch.from_numpy(raw[k]).to(torch.bfloat16).cuda() for k in ("q", "k", "v")}
+    for k in ("wphi_q", "wphi_k"):
+        dev[k] = torch.from_numpy(raw[k]).cuda()
+    dout = torch.from_numpy(workloads.make_grad_out(cfg, seed)).to(torch.bfloat16).cuda()
+    args = (dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"])
+    lam = cfg["topk"]
+    rows = []
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for C in (64, 128, 256):
+        kw = dict(window=C, chunk=C, topk=lam)
+        sh = still.make_shape(batch=cfg["batch"], seqlen=cfg["seqlen"], n_q_heads=cfg["n_q_heads"],
+                              n_kv_heads=cfg["n_kv_heads"], head_dim=cfg["head_dim"], **kw)
+        fws = torch.empty(still.fwd_workspace_size(sh), dtype=torch.uint8, device="cuda")
+        bws = torch.empty(still.bwd_workspace_size(sh), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(dev["q"])
+        B, N = cfg["batch"], cfg["seqlen"]
+
+        def step():
+            sel = still.fwd(*args, **kw, out=out, workspace=fws, return_sel=True)["sel_idx"]
+            e_mid = torch.cuda.Event(enable_timing=True)
+            e_mid.record()
+            still.bwd(*args, sel, dout, **kw, workspace=bws)
+            return e_mid
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        fwd_ms = bwd_ms = 0.0
+        for _ in range(steps):
+            e0.record()
+            mid = step()
+            e1.record()
+            torch.cuda.synchronize()
+            fwd_ms += e0.elapsed_time(mid)
+            bwd_ms += mid.elapsed_time(e1)
+        fwd_ms /= steps
+        bwd_ms /= steps
+        ms = fwd_ms + bwd_ms
+        rows.append({"chunk": C, "window": C, "topk": lam, "forward_ms": round(fwd_ms, 4),
+                     "backward_ms": round(bwd_ms, 4), "step_ms": round(ms, 4),
+                     "tokens_per_s": round(B * N / (ms * 1e-3), 1)})
+        log(f"[bench] chunk sweep C=W={C} top-{lam}: forward {fwd_ms:.3f} + backward {bwd_ms:.3f} "
+            f"= {ms:.3f} ms/step")
+        del fws, bws, out
+    return {"workload": f"{name} forward + backward, W = C, top-{lam} per chunk", "rows": rows}
+
+
 def bench_utility(still, torch, name="prefill_4k"):
     """Future-KV-utility diagnostic (full text App. A.7.4, Table 12) on the
     4K prefill: the library's utilities of every remote key, then for each
@@ -620,6 +675,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-scaling", action="store_true",
                     help="skip the prefill-time-against-length sweep at a fixed budget")
+    ap.add_argument("--no-chunk-sweep", action="store_true",
+                    help="skip the training-step cost against the chunk size")
+    ap.add_argument("--chunk-sweep-only", action="store_true",
+                    help="time only the chunk-size sweep and print its JSON object")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode step and print its JSON object")
     ap.add_argument("--ragged-only", action="store_true",
@@ -656,6 +715,9 @@ def main():
     if args.backward_only:
         print(json.dumps(bench_backward(still, torch, args.steps, args.warmup)), flush=True)
         return
+    if args.chunk_sweep_only:
+        print(json.dumps(bench_chunk_sweep(still, torch)), flush=True)
+        return
     if args.ragged_only:
         print(json.dumps(bench_decode_ragged(still, torch, args.decode_steps, args.warmup)), flush=True)
         return
@@ -668,6 +730,7 @@ def main():
                                                          args.warmup)
     util = None if args.no_utility else bench_utility(still, torch)
     nsc = None if args.no_scaling else bench_n_scaling(still, torch)
+    csw = None if args.no_chunk_sweep else bench_chunk_sweep(still, torch)
     cpu = None if args.no_cpu else cpu_baseline(pre["raw"], cfg)
     tok_s = pre["tokens"] / (pre["ms"] * 1e-3)
     line = {
@@ -688,6 +751,7 @@ def main():
         "backward": bwd,
         "future_kv_utility": util,
         "n_scaling": nsc,
+        "chunk_sweep": csw,
     }
     print(json.dumps(line), flush=True)
 

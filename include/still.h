@@ -288,14 +288,16 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
  *             when gate_opt is given and this is not NULL; ignored without
  *             a gate
  *   workspace >= still_bwd_workspace_size bytes of device memory
- * For bf16 storage with d = d' = 128, chunk 64, window 64 / 128 / 256 and
- * 1, 2, 4 or 8 query heads per KV head, the softmax terms run on the
- * matrix cores: a first pass (the forward's main kernel over compact lists
- * of the given selection) gives each query's reference, normaliser and
- * dout . out, and the softmax part of dq is formed from bf16 logit and
- * dout . v products with dS rounded to bf16, as the forward rounds its
- * probabilities (gradients to about 1e-2 relative); the other terms and
- * every other shape use fp32 kernels (about 1e-6).  STILL_FLAG_GENERAL_KERNELS
+ * For bf16 storage with d = d' = 128, window 64 / 128 / 256, chunk 64 / 128 /
+ * 256 no longer than the window, and 1, 2, 4 or 8 query heads per KV head,
+ * every term runs on the matrix cores: a first pass (the forward's main
+ * kernel over compact lists of the given selection) gives each query's
+ * reference, normaliser and dout . out; the softmax terms are formed from
+ * bf16 logit and dout . v products with dS rounded to bf16, as the forward
+ * rounds its probabilities, and the linear terms, the NP-Map backward and
+ * the projection gradients take bf16 operands too (gradients to about 1e-2
+ * relative); every other shape uses fp32 kernels (about 1e-6).
+ * STILL_FLAG_GENERAL_KERNELS
  * forces the fp32 kernels everywhere; the routing-criterion flags do not
  * matter.  N == 0
  * or B == 0 writes zeros to dwphi_q and dwphi_k (when not NULL) and nothing
