@@ -349,7 +349,11 @@ def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=
     (saves recomputing them when only a few rows are evaluated).
     gate: optional gate logits [B,N,Hq] (R-GATE); None is no gate.
 
-    Returns dict(out [B,N,Hq,d] (NaN where not evaluated), scores, sel_idx, route).
+    Returns dict(out [B,N,Hq,d] (NaN where not evaluated), scores, sel_idx, route,
+    lse [B,N,Hq], has_linear [B,N,Hq]): lse is the log of the shared
+    normaliser, ln(sum over SA_t of exp(tau q.k) + sum over LA_t of the
+    gated linear weights), and has_linear whether LA_t carries any weight
+    (list view Fig. 2, hybrid aggregation: one denominator for both kinds).
 
     For query t of head h (KV head g):
       J_t  = [max(0, t-W+1), t]                       window (softmax)
@@ -384,6 +388,8 @@ def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=
     gam = np.ones((B, N, Hq)) if gate is None else gate_weight(gate)
 
     out = np.full(q.shape, np.nan)
+    lse = np.full((B, N, Hq), np.nan)
+    has_linear = np.zeros((B, N, Hq), bool)
     if rows is None:
         rows = [(b, t) for b in range(B) for t in range(N)]
     for b, t in rows:
@@ -412,7 +418,9 @@ def fwd_direct(q, k, v, wq, wk, p: Params, rows=None, sel_override=None, scores=
                 num = w_sa @ v[b, sa, g, :] + (w_la @ v[b, la_routed, g, :] if la_routed.size else 0.0)
                 den = w_sa.sum() + w_la.sum()
                 out[b, t, h] = num / den
-    return dict(out=out, scores=sigma, sel_idx=sel_idx, route=route)
+                lse[b, t, h] = M + math.log(den)
+                has_linear[b, t, h] = bool(w_la.sum() > 0.0)
+    return dict(out=out, scores=sigma, sel_idx=sel_idx, route=route, lse=lse, has_linear=has_linear)
 
 
 # --------------------------------------------------------------------------

@@ -45,9 +45,18 @@ def causal_softmax_attention(q, k, v):
 def test_window_covering_sequence_is_causal_softmax(topk):
     q, k, v, wq, wk = rand_inputs(1, 2, 37, 4, 2, 16)
     p = O.Params(window=64, chunk=8, topk=topk)
-    out = O.fwd_direct(q, k, v, wq, wk, p)["out"]
+    res = O.fwd_direct(q, k, v, wq, wk, p)
     ref = causal_softmax_attention(q, k, v)
-    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-12, atol=1e-12)
+    # the shared normaliser is the causal softmax's: its log is the
+    # logsumexp of tau q.k over j <= t (torch's, on the same float64 logits)
+    B, N, Hq, d = q.shape
+    for b in range(B):
+        for h in range(Hq):
+            s = torch.from_numpy(q[b, :, h] @ k[b, :, h // 2].T / math.sqrt(d))
+            s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), -math.inf)
+            np.testing.assert_allclose(res["lse"][b, :, h], torch.logsumexp(s, 1).numpy(), rtol=1e-12)
+    assert not res["has_linear"].any()
 
 
 @pytest.mark.parametrize("W,C,lam", [(8, 8, 8), (8, 8, 20), (12, 4, 4)])
@@ -113,6 +122,9 @@ def test_uniform_feature_map_gives_shared_normaliser():
         num = e @ v[0, sa, 0] + wla * v[0, la, 0].sum(0)
         den = e.sum() + wla * len(la)
         np.testing.assert_allclose(res["out"][0, t, 0], num / den, rtol=1e-12)
+        # the log of that shared denominator, and whether it has a linear part
+        np.testing.assert_allclose(res["lse"][0, t, 0], math.log(den), rtol=1e-12)
+        assert res["has_linear"][0, t, 0] == (len(la) > 0)
 
 
 # ---------------------------------------------------------------- P4
