@@ -409,7 +409,9 @@ MFMA_KERNELS = {"bwd_stats", "bwd_dq", "bwd_kv_win", "bwd_kv_sel", "bwd_uchunk",
 def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
     """The backward pass on the training-shaped batch (8 sequences of 2048
     tokens): gradients w.r.t. q, k, v and both NP-Map projections under the
-    forward's own routing, dout ~ N(0, 1)."""
+    forward's own routing, dout ~ N(0, 1), started from the forward's output
+    and statistics (the time from the routing alone, with the first pass
+    that recomputes them, is reported beside it)."""
     cfg = workloads.CONFIGS[name]
     seed = workloads.seed_of(name)
     raw = workloads.make_prefill(cfg, seed)
@@ -420,21 +422,32 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
     W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
     kw = dict(window=W, chunk=C, topk=lam)
     args = (dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"])
-    sel = still.fwd(*args, **kw, return_sel=True)["sel_idx"]
+    # the training pairing: the forward hands the backward its routing, its
+    # output and its per-query statistics
+    fw = still.fwd(*args, **kw, return_sel=True, return_stats=True)
+    sel, saved = fw["sel_idx"], dict(out=fw["out"], stats=fw["stats"])
     sh = still.make_shape(batch=cfg["batch"], seqlen=cfg["seqlen"], n_q_heads=cfg["n_q_heads"],
                           n_kv_heads=cfg["n_kv_heads"], head_dim=cfg["head_dim"], **kw)
     ws = torch.empty(still.bwd_workspace_size(sh), dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
-        still.bwd(*args, sel, dout, **kw, workspace=ws)
-    timers = [still.LaunchTimer() for _ in range(steps)]
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        still.bwd(*args, sel, dout, **kw, workspace=ws, timer=timers[i])
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    def time_bwd(extra, timers=None):
+        for _ in range(warmup):
+            still.bwd(*args, sel, dout, **kw, workspace=ws, **extra)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            still.bwd(*args, sel, dout, **kw, workspace=ws, **extra,
+                      timer=timers[i] if timers else None)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # from the routing alone (a first pass recomputes the statistics)
+    recompute_ms = time_bwd({})
+    log(f"[bench] {name} backward from the routing alone: {recompute_ms:.3f} ms/step")
+    timers = [still.LaunchTimer() for _ in range(steps)]
+    ms = time_bwd(saved, timers)
     per = {}
     for tm in timers:
         for kname, dur in tm.durations_ms():
@@ -442,15 +455,17 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
     kern = {k: float(np.mean(v)) for k, v in per.items()}
     log(f"[bench] {name} backward: {ms:.3f} ms/step; kernels (ms): " +
         ", ".join(f"{k}={v:.3f}" for k, v in kern.items()))
-    # the forward of the same batch, for the backward / forward ratio
+    # the forward of the same batch (writing the statistics), for the
+    # backward / forward ratio
     fws = torch.empty(still.fwd_workspace_size(sh), dtype=torch.uint8, device="cuda")
     fout = torch.empty_like(dev["q"])
+    fst = torch.empty_like(fw["stats"])
     for _ in range(warmup):
-        still.fwd(*args, **kw, out=fout, workspace=fws)
+        still.fwd(*args, **kw, out=fout, workspace=fws, stats=fst)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(steps):
-        still.fwd(*args, **kw, out=fout, workspace=fws)
+        still.fwd(*args, **kw, out=fout, workspace=fws, stats=fst)
     e1.record()
     torch.cuda.synchronize()
     fwd_ms = e0.elapsed_time(e1) / steps
@@ -480,6 +495,7 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
                        "projections (fp32) under the forward's routing", "batch": cfg["batch"],
                        "seq_len": cfg["seqlen"]},
             "forward_ms": round(fwd_ms, 4), "backward_over_forward": round(ms / fwd_ms, 2),
+            "from_forward_statistics": True, "recompute_statistics_ms": round(recompute_ms, 4),
             "whole_step_TFLOPs": round(total / (ms * 1e-3) / 1e12, 2),
             "whole_step_count": "method flops: 10d per softmax pair plus the linear and NP-Map terms",
             "matrix_core_kernels": mfma_kernels,
@@ -532,7 +548,8 @@ def bench_chunk_sweep(still, torch, steps=5, warmup=2, name="train_8x2k"):
     """Cost of one training step (forward + backward) against the chunk size
     (full text App. A.7.5, Table 14: C varied with the window spanning one
     chunk, W = C, and 16 selected tokens per chunk), on the 8 x 2048 training
-    batch for the chunk sizes the matrix-core path takes (64, 128, 256)."""
+    batch for the chunk sizes the matrix-core path takes (64, 128, 256); the
+    backward starts from the forward's output and statistics."""
     cfg = workloads.CONFIGS[name]
     seed = workloads.seed_of(name)
     raw = workloads.make_prefill(cfg, seed)
@@ -554,10 +571,10 @@ def bench_chunk_sweep(still, torch, steps=5, warmup=2, name="train_8x2k"):
         B, N = cfg["batch"], cfg["seqlen"]
 
         def step():
-            sel = still.fwd(*args, **kw, out=out, workspace=fws, return_sel=True)["sel_idx"]
+            fw = still.fwd(*args, **kw, out=out, workspace=fws, return_sel=True, return_stats=True)
             e_mid = torch.cuda.Event(enable_timing=True)
             e_mid.record()
-            still.bwd(*args, sel, dout, **kw, workspace=bws)
+            still.bwd(*args, fw["sel_idx"], dout, **kw, workspace=bws, out=out, stats=fw["stats"])
             return e_mid
 
         for _ in range(warmup):

@@ -978,14 +978,19 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
             return e;
         if ((e = mark.fn(mark.ctx, "la_scan16")) != hipSuccess) return e;
         if ((e = launch_la_group_scan(DT, w.lin16, -1, nullptr, nullptr, s)) != hipSuccess) return e;
-        if ((e = mark.fn(mark.ctx, "bwd_stats")) != hipSuccess) return e;
-        if ((e = launch_hybrid_stats(DT, a.q, a.k, a.v, w.wsplit, w.phik16, w.route, w.ksel, w.vsel,
-                                     w.lin16, a.gate, w.list_off, a.dout, w.stat, w.phiq, s)) != hipSuccess)
-            return e;
+        // the statistics and gated query features: a first pass, or (given
+        // the forward's out and statistics) the dq kernel's own prologue
+        if (!a.stats) {
+            if ((e = mark.fn(mark.ctx, "bwd_stats")) != hipSuccess) return e;
+            if ((e = launch_hybrid_stats(DT, a.q, a.k, a.v, w.wsplit, w.phik16, w.route, w.ksel, w.vsel,
+                                         w.lin16, a.gate, w.list_off, a.dout, w.stat, w.phiq, s)) !=
+                hipSuccess)
+                return e;
+        }
         if ((e = mark.fn(mark.ctx, "bwd_dq")) != hipSuccess) return e;
         if ((e = launch_bwd_dq(DT, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.list_off, w.stat,
                                w.phik16, w.lin16, a.gate, w.phiq, a.dq, w.dphiq,
-                               a.gate ? a.dgate : nullptr, s)) != hipSuccess)
+                               a.gate ? a.dgate : nullptr, a.stats, a.out, w.wsplit, s)) != hipSuccess)
             return e;
     }
     // the queries' features carry their gate weights (phi~_q = gamma phi_q), so

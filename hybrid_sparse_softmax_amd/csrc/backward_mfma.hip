@@ -37,7 +37,6 @@ namespace still {
 namespace {
 using namespace mt;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // key kernels: the window kernel's block takes kWinKPB key chunks (two
 // waves per chunk), the selected kernel's kSelW waves of 32 compact rows
@@ -356,9 +355,10 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const int* __restrict__ list_off,
-    const float* __restrict__ stat, const bf16* __restrict__ phik, LinBufs L,
-    const float* __restrict__ gate, const float* __restrict__ phiq, float* __restrict__ dq,
-    float* __restrict__ dphiq, float* __restrict__ dgate, Dims D) {
+    float* __restrict__ stat, const bf16* __restrict__ phik, LinBufs L,
+    const float* __restrict__ gate, bf16* __restrict__ phiq, float* __restrict__ dq,
+    float* __restrict__ dphiq, float* __restrict__ dgate, const float* __restrict__ stat_in,
+    const bf16* __restrict__ out, const bf16* __restrict__ wqh, const bf16* __restrict__ wql, Dims D) {
     constexpr int NW = HB * 2;
     const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
@@ -397,7 +397,51 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
         qf[st] = ld_bf8(q + qo * kD + 16 * st + 8 * hf);
         df[st] = ld_bf8(dout + qo * kD + 16 * st + 8 * hf);
     }
-    const f32x4 stq = *reinterpret_cast<const f32x4*>(stat + qo * 4);
+    f32x4 stq;
+    if (stat_in) {
+        // from the forward: (m, l, -, c) of the query, and its output for
+        // D = dout . out (the lane's 64 dims plus the other half's); the
+        // statistics and the gated features gamma phi_q (bf16, feature order)
+        // go to stat and phiq for the kernels after this one
+        stq = *reinterpret_cast<const f32x4*>(stat_in + qo * 4);
+        float dd = 0.f;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const bf16x8 o8 = ld_bf8(out + qo * kD + 16 * st + 8 * hf);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2 a2 = {o8[2 * j], o8[2 * j + 1]};
+                const bf16x2 b2 = {df[st][2 * j], df[st][2 * j + 1]};
+                dd = __builtin_amdgcn_fdot2_f32_bf16(a2, b2, dd, false);
+            }
+        }
+        stq[2] = dd + xor32(dd);
+        // the KV head's projection parts, staged once for the block's waves
+        // (the first tile's staging below waits for every wave's reads)
+        load_k_tile(wqh + (size_t)g * (kD / 2) * kD, kD, kD / 2, ks, tid, NW * 64);
+        load_k_tile(wql + (size_t)g * (kD / 2) * kD, kD, kD / 2, vs, tid, NW * 64);
+        __syncthreads();
+        f32x16 phi[1][2][2];
+        np_map_mfma<1>(*reinterpret_cast<const bf16x8(*)[1][8]>(&qf), ks, vs, kKS, phi);
+        const float gq = gate_weight(gate, qo);
+        if (t0 + oq < D.N) {
+            if (hf == 0) *reinterpret_cast<f32x4*>(stat + qo * 4) = stq;
+            bf16* pr = phiq + qo * kD;
+#pragma unroll
+            for (int sgn = 0; sgn < 2; ++sgn)
+#pragma unroll
+                for (int f2 = 0; f2 < 2; ++f2)
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4) {
+                        bf16x4 x4;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) x4[j] = (bf16)(gq * phi[0][sgn][f2][4 * v4 + j]);
+                        *reinterpret_cast<bf16x4*>(pr + 64 * sgn + 32 * f2 + acc_row(4 * v4, hf)) = x4;
+                    }
+        }
+    } else {
+        stq = *reinterpret_cast<const f32x4*>(stat + qo * 4);
+    }
     const float lse2 = stq[0] * kLog2e + __log2f(stq[1]);  // P = 2^(s cl2 - lse2)
     const float dq_d = stq[2];
     uint64_t selmask = 0;
@@ -578,7 +622,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const float cf = stq[3];
     const float gw = gate_weight(gate, qo);
     float* dpr = dphiq + qo * kD;
-    const float* fqr = phiq + qo * kD;
+    const bf16* fqr = phiq + qo * kD;
     float fdot = 0.f;
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft)
@@ -590,9 +634,9 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int j = 0; j < 4; ++j) o4[j] = gw * cf * dfq[ft][4 * v4 + j];
             *reinterpret_cast<f32x4*>(dpr + f0) = o4;
             if (dgate) {
-                const f32x4 fq4 = *reinterpret_cast<const f32x4*>(fqr + f0);
+                const bf16x4 fq4 = *reinterpret_cast<const bf16x4*>(fqr + f0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) fdot = fmaf(fq4[j], dfq[ft][4 * v4 + j], fdot);
+                for (int j = 0; j < 4; ++j) fdot = fmaf((float)fq4[j], dfq[ft][4 * v4 + j], fdot);
             }
         }
     if (dgate) {
@@ -612,20 +656,14 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
 // chunks) plus the queries of chunk cj + NWT at or after the key's offset.
 // ---------------------------------------------------------------------------
 
-// fq row (fp32, feature order) -> 8 bf16 features of storage positions
-// 8 oct .. 8 oct + 7 (position p holds feature kperm(p)), times sc
-__device__ __forceinline__ bf16x8 fq_oct_perm(const float* __restrict__ row, int oct, float sc) {
+// fq row (bf16, feature order) -> the 8 features of storage positions
+// 8 oct .. 8 oct + 7 (position p holds feature kperm(p))
+__device__ __forceinline__ bf16x8 fq_oct_perm(const bf16* __restrict__ row, int oct) {
     // positions 16 b + 8 h + 4 m + l hold features 16 b + 8 m + 4 h + l
     const int b16 = 16 * (oct >> 1), h4 = 4 * (oct & 1);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(row + b16 + h4);
-    const f32x4 c = *reinterpret_cast<const f32x4*>(row + b16 + 8 + h4);
-    bf16x8 r;
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-        r[l] = (bf16)(sc * a[l]);
-        r[4 + l] = (bf16)(sc * c[l]);
-    }
-    return r;
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + b16 + h4);
+    const bf16x4 c = *reinterpret_cast<const bf16x4*>(row + b16 + 8 + h4);
+    return __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Chunk sums per query chunk c of (b, g): U[i][e] = sum over its queries t
@@ -633,7 +671,7 @@ __device__ __forceinline__ bf16x8 fq_oct_perm(const float* __restrict__ row, int
 // (the fp32 layout [i][e] then u, (d + 1) d' floats).  Per head, (c fq)^T and
 // dout^T are staged with the queries as contraction index; wave w owns
 // features 32 w .. 32 w + 31.
-__global__ __launch_bounds__(256) void bwd_uchunk_mfma_kernel(const float* __restrict__ phiq,
+__global__ __launch_bounds__(256) void bwd_uchunk_mfma_kernel(const bf16* __restrict__ phiq,
                                                               const bf16* __restrict__ dout,
                                                               const float* __restrict__ stat,
                                                               float* __restrict__ ust, Dims D) {
@@ -662,13 +700,9 @@ __global__ __launch_bounds__(256) void bwd_uchunk_mfma_kernel(const float* __res
                     const size_t o = o0 + (size_t)row * D.Hq;
                     // the features in natural order here: position = feature
                     const float cf = stat[o * 4 + 3];
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(phiq + o * kD + 8 * oct);
-                    const f32x4 bb = *reinterpret_cast<const f32x4*>(phiq + o * kD + 8 * oct + 4);
+                    const bf16x8 a = ld_bf8(phiq + o * kD + 8 * oct);
 #pragma unroll
-                    for (int l = 0; l < 4; ++l) {
-                        rr[q4][l] = (bf16)(cf * a[l]);
-                        rr[q4][4 + l] = (bf16)(cf * bb[l]);
-                    }
+                    for (int l = 0; l < 8; ++l) rr[q4][l] = (bf16)(cf * (float)a[l]);
                 } else {
                     rr[q4] = zero_bf8();
                 }
@@ -718,7 +752,7 @@ __global__ __launch_bounds__(256) void bwd_uchunk_mfma_kernel(const float* __res
 // order) of every key of the chunk, zeros for keys with no linear term.
 template <int NWT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_lin_kernel(
-    const bf16* __restrict__ v, const bf16* __restrict__ dout, const float* __restrict__ phiq,
+    const bf16* __restrict__ v, const bf16* __restrict__ dout, const bf16* __restrict__ phiq,
     const bf16* __restrict__ phik16, const uint8_t* __restrict__ route, const float* __restrict__ stat,
     const float* __restrict__ ust, float* __restrict__ dv, float* __restrict__ dphik, Dims D) {
     const Item it = xcd_item(D.T, D.Hkv);
@@ -789,7 +823,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
             for (int x = tid; x < kC * 16; x += 256) {
                 const int row = x >> 4, oct = x & 15;
                 st_bf8(fq + row * kKS + 8 * oct,
-                       row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct, 1.f) : zero_bf8());
+                       row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct) : zero_bf8());
             }
             for (int x = tid; x < 16 * 16; x += 256) {
                 const int kq = x & 15, oct = x >> 4;
@@ -797,7 +831,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int row = 4 * kq + q4;
-                    rr[q4] = row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct, 1.f) : zero_bf8();
+                    rr[q4] = row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct) : zero_bf8();
                 }
                 const int pos = kperm(4 * kq);
 #pragma unroll
@@ -1122,10 +1156,13 @@ __global__ __launch_bounds__(256) void dw_mfma_kernel(const bf16* __restrict__ x
 
 hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,
-                         const int* list_off, const float* stat, const void* phik16, const LinBufs& L,
-                         const float* gate, const float* phiq, float* dq, float* dphiq, float* dgate,
-                         hipStream_t s) {
+                         const int* list_off, float* stat, const void* phik16, const LinBufs& L,
+                         const float* gate, void* phiq, float* dq, float* dphiq, float* dgate,
+                         const float* stat_in, const void* out, const void* wsplit, hipStream_t s) {
     const int HB = D.G >= 2 ? 2 : 1;
+    const int n = D.Hkv * (kD / 2) * kD;
+    const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
+    const bf16* wql = wqh + n;
     const unsigned nblk = (unsigned)D.T * D.B * D.Hkv * (D.G / HB);
     const int nwt = D.W / kC;
 #define STILL_DQ1(H, NWT)                                                                        \
@@ -1134,7 +1171,8 @@ hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void
                        reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout),   \
                        route, reinterpret_cast<const bf16*>(ksel),                                \
                        reinterpret_cast<const bf16*>(vsel), list_off, stat,                       \
-                       reinterpret_cast<const bf16*>(phik16), L, gate, phiq, dq, dphiq, dgate, D)
+                       reinterpret_cast<const bf16*>(phik16), L, gate, reinterpret_cast<bf16*>(phiq), dq, dphiq, dgate, \
+                       stat_in, reinterpret_cast<const bf16*>(out), wqh, wql, D)
 #define STILL_DQ(H)                \
     do {                           \
         if (nwt == 1)              \
@@ -1151,20 +1189,22 @@ hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const float* phiq,
+hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const void* phiq,
                               const void* phik16, const uint8_t* route, const float* stat, float* ust,
                               float* dv, float* dphik, int phase, hipStream_t s) {
     if (phase == 0) {
-        hipLaunchKernelGGL(bwd_uchunk_mfma_kernel, dim3(D.T, D.Hkv, D.B), dim3(256), 0, s, phiq,
-                           reinterpret_cast<const bf16*>(dout), stat, ust, D);
+        hipLaunchKernelGGL(bwd_uchunk_mfma_kernel, dim3(D.T, D.Hkv, D.B), dim3(256), 0, s,
+                           reinterpret_cast<const bf16*>(phiq), reinterpret_cast<const bf16*>(dout), stat, ust,
+                           D);
         return hipGetLastError();
     }
     const unsigned nblk = (unsigned)D.T * D.Hkv * D.B;
     const int nwt = D.W / kC;
 #define STILL_KL(NWT)                                                                            \
     hipLaunchKernelGGL((bwd_key_lin_kernel<NWT>), dim3(nblk), dim3(256), 0, s,                  \
-                       reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout), phiq, \
-                       reinterpret_cast<const bf16*>(phik16), route, stat, ust, dv, dphik, D)
+                       reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout),   \
+                       reinterpret_cast<const bf16*>(phiq), reinterpret_cast<const bf16*>(phik16), route, \
+                       stat, ust, dv, dphik, D)
     if (nwt == 1) STILL_KL(1);
     else if (nwt == 2) STILL_KL(2);
     else STILL_KL(4);

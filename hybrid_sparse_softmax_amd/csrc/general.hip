@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64) void main_general_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ phiq, const float* __restrict__ phik,
     const uint8_t* __restrict__ route, const int32_t* __restrict__ sel_idx,
-    const float* __restrict__ lin, T* __restrict__ out, Dims D) {
+    const float* __restrict__ lin, T* __restrict__ out, float* __restrict__ stat, Dims D) {
     constexpr int PL = DD / kWave;
     const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int g = h / D.G;
@@ -294,7 +294,8 @@ __global__ __launch_bounds__(64) void main_general_kernel(
     // token selected) the reference is the plain running maximum, which may
     // be negative: all logits far below 0 would otherwise underflow every
     // weight and leave 0 / 0.
-    if (!(l > 0.f)) m = kNegInf;
+    const bool lamass = l > 0.f;
+    if (!lamass) m = kNegInf;
     auto sa_batch = [&](int jpos) {
         float s = kNegInf;
         if (jpos >= 0) {
@@ -343,6 +344,13 @@ __global__ __launch_bounds__(64) void main_general_kernel(
     const float inv = 1.0f / l;
 #pragma unroll
     for (int p = 0; p < PL; ++p) out[qoff * DD + lane + kWave * p] = from_f32<T>(acc[p] * inv);
+    // optional statistics for a backward: (m, l, 0, exp(-m) / l with linear terms, else 0)
+    if (stat && lane == 0) {
+        stat[qoff * 4] = m;
+        stat[qoff * 4 + 1] = l;
+        stat[qoff * 4 + 2] = 0.f;
+        stat[qoff * 4 + 3] = lamass ? expf(-m) * inv : 0.f;
+    }
 }
 
 // Prefill -> decode hand-off for one (b, g): ring, route flags, pending
@@ -452,12 +460,12 @@ hipError_t scores_t(const Dims& D, const void* q, const void* k, float* hs, hipS
 template <typename T, int DD>
 hipError_t main_t(const Dims& D, const void* q, const void* k, const void* v, const float* phiq,
                   const float* phik, const uint8_t* route, const int32_t* sel_idx, const float* lin,
-                  void* out, hipStream_t s) {
+                  void* out, float* stat, hipStream_t s) {
     dim3 grid(D.N, D.Hq, D.B);
     hipLaunchKernelGGL((main_general_kernel<T, DD>), grid, dim3(64), 0, s,
                        reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k),
                        reinterpret_cast<const T*>(v), phiq, phik, route, sel_idx, lin,
-                       reinterpret_cast<T*>(out), D);
+                       reinterpret_cast<T*>(out), stat, D);
     return hipGetLastError();
 }
 }  // namespace
@@ -508,12 +516,13 @@ hipError_t launch_la_scan(const Dims& D, float* lin, int cap_chunk, float* cap_S
 
 hipError_t launch_main_general(const Dims& D, const void* q, const void* k, const void* v,
                                const float* phiq, const float* phik, const uint8_t* route,
-                               const int32_t* sel_idx, const float* lin, void* out, hipStream_t s) {
+                               const int32_t* sel_idx, const float* lin, void* out, float* stats,
+                               hipStream_t s) {
     if (D.d == 128)
-        return D.bf16 ? main_t<__bf16, 128>(D, q, k, v, phiq, phik, route, sel_idx, lin, out, s)
-                      : main_t<float, 128>(D, q, k, v, phiq, phik, route, sel_idx, lin, out, s);
-    return D.bf16 ? main_t<__bf16, 64>(D, q, k, v, phiq, phik, route, sel_idx, lin, out, s)
-                  : main_t<float, 64>(D, q, k, v, phiq, phik, route, sel_idx, lin, out, s);
+        return D.bf16 ? main_t<__bf16, 128>(D, q, k, v, phiq, phik, route, sel_idx, lin, out, stats, s)
+                      : main_t<float, 128>(D, q, k, v, phiq, phik, route, sel_idx, lin, out, stats, s);
+    return D.bf16 ? main_t<__bf16, 64>(D, q, k, v, phiq, phik, route, sel_idx, lin, out, stats, s)
+                  : main_t<float, 64>(D, q, k, v, phiq, phik, route, sel_idx, lin, out, stats, s);
 }
 
 hipError_t launch_handoff(const Dims& D, const void* k, const void* v, const float* wphi_k,

@@ -55,10 +55,12 @@ hipError_t launch_la_chunks(const Dims& D, const float* phik, const void* v, con
                             float* lin, hipStream_t s);
 hipError_t launch_la_scan(const Dims& D, float* lin, int cap_chunk, float* cap_S, float* cap_z,
                           hipStream_t s);
-// hybrid output, one wave per (b, t, h)
+// hybrid output, one wave per (b, t, h); stats (optional) [B, N, Hq, 4] gets
+// each query's (m, l, 0, c) for a backward
 hipError_t launch_main_general(const Dims& D, const void* q, const void* k, const void* v,
                                const float* phiq, const float* phik, const uint8_t* route,
-                               const int32_t* sel_idx, const float* lin, void* out, hipStream_t s);
+                               const int32_t* sel_idx, const float* lin, void* out, float* stats,
+                               hipStream_t s);
 // prefill -> decode cache hand-off (after the scan wrote chunk cap_chunk into lin_S / lin_z)
 hipError_t launch_handoff(const Dims& D, const void* k, const void* v, const float* wphi_k,
                           const float* scores, const int32_t* sel_idx, const uint8_t* route,
@@ -106,7 +108,8 @@ hipError_t launch_la_group_scan(const Dims& D, const LinBufs& L, int cap_chunk, 
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const void* wsplit, const void* phik, const uint8_t* route,
                               const void* ksel, const void* vsel, const LinBufs& L,
-                              const float* gate, const int* list_off, void* out, hipStream_t s);
+                              const float* gate, const int* list_off, void* out, float* stats,
+                              hipStream_t s);
 
 // ---- backward on the matrix cores (bf16, d = 128, W = 64 / 128 / 256, C = 64 / 128 / 256, C <= W) ----
 bool mfma_bwd_supported(const Dims& D);
@@ -124,12 +127,12 @@ hipError_t launch_bwd_lists_tiles(const Dims& D, const Dims& DT, const int32_t* 
                                   const float* wq, const float* wk, void* wsplit, hipStream_t s);
 // the forward's main kernel writing (m, l, D = dout . out, c) per query head
 // to stat [B, N, Hq, 4] instead of the output, and the gated NP-Map features
-// of the queries to phiq [B, N, Hq, d'] (fp32)
+// of the queries to phiq [B, N, Hq, d'] (bf16, feature order)
 hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, const void* v,
                                const void* wsplit, const void* phik, const uint8_t* route,
                                const void* ksel, const void* vsel, const LinBufs& L,
                                const float* gate, const int* list_off, const void* dout,
-                               float* stat, float* phiq, hipStream_t s);
+                               float* stat, void* phiq, hipStream_t s);
 // softmax part of dk and dv: phase 0 the window keys (dk written, dv added
 // to), phase 1 the selected keys over the compact rows (both added to; part:
 // bwd_kv_part_floats(D) floats of segment sums, then merged)
@@ -142,7 +145,7 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
 // ust [B, Hkv, T, d' (d + 1)] (fp32, [i][e] then u; the suffix kernel turns
 // them into suffix sums), phase 1 dv (written: the linear part) and dphik
 // [B, N, Hkv, d'] (fp32, feature order, written) from the suffix sums
-hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const float* phiq,
+hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const void* phiq,
                               const void* phik16, const uint8_t* route, const float* stat, float* ust,
                               float* dv, float* dphik, int phase, hipStream_t s);
 // NP-Map backward of one side (0: queries, 1: keys) on the matrix cores:
@@ -156,12 +159,15 @@ hipError_t launch_dw_mfma(const Dims& D, const void* x, int side, const void* du
                           int nslice, hipStream_t s);
 // softmax part of dq (fp32, overwritten), then the gradient w.r.t. the
 // queries' NP-Map features dphiq [B, N, Hq, d'] (fp32, feature order,
-// overwritten) and, with a gate, dgate
+// overwritten) and, with a gate, dgate.  stat_in (with the forward's out):
+// the forward's (m, l, -, c); the kernel then writes stat (with D = dout .
+// out) and phiq (gated features, from the projection split wsplit) itself
+// instead of reading what the first pass wrote there
 hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,
-                         const int* list_off, const float* stat, const void* phik16, const LinBufs& L,
-                         const float* gate, const float* phiq, float* dq, float* dphiq, float* dgate,
-                         hipStream_t s);
+                         const int* list_off, float* stat, const void* phik16, const LinBufs& L,
+                         const float* gate, void* phiq, float* dq, float* dphiq, float* dgate,
+                         const float* stat_in, const void* out, const void* wsplit, hipStream_t s);
 
 // ---- decode step ------------------------------------------------------------
 struct DecodeWork {
@@ -197,9 +203,13 @@ struct BwdArgs {
     float *dq, *dk, *dv, *dwq, *dwk;    // fp32 gradients, overwritten
     const float* gate;                  // [B, N, Hq] gate logits, or nullptr
     float* dgate;                       // [B, N, Hq] fp32, written when gate and dgate are set
+    // the forward's output and statistics (m, l, 0, c) per query head, or
+    // both nullptr: with them the matrix-core path skips its first pass
+    const void* out;
+    const float* stats;
 };
 struct BwdWork {
-    float *phiq, *phik;   // [B, N, Hq | Hkv, fd]
+    float *phiq, *phik;   // [B, N, Hq | Hkv, fd] (fp32; the matrix-core path keeps phiq in bf16)
     float* lin;           // [B, Hkv, T, fd (d + 1)] LA prefix states
     float* stat;          // [B, N, Hq, 4] m, l, D_t, exp(-m) / l
     float *dphiq, *dphik; // [B, N, Hq | Hkv, fd]
@@ -231,7 +241,7 @@ struct BwdMark {
     hipError_t (*fn)(void* ctx, const char* name);
     void* ctx;
 };
-int bwd_launch_count(bool mfma);
+int bwd_launch_count(bool mfma);  // at most this many launches
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s, BwdMark mark);
 hipError_t launch_zero(float* p, int n, hipStream_t s);
 

@@ -8,6 +8,7 @@ namespace mt {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kC = 64;          // chunk (and key / query tile) rows
 constexpr int kD = 128;         // head_dim = NP-Map feature dim
@@ -129,6 +130,89 @@ __device__ __forceinline__ void load_rows(const bf16* __restrict__ src, size_t l
     for (int u = 0; u < NT; ++u) {
         const int x = tid + NTHR * u, row = x >> 4, piece = x & 15;
         st_bf8(dst + row * kKS + 8 * piece, r[u]);
+    }
+}
+
+// NP-Map (Sec. 3.2, Hedgehog form of Sec. 2) of NT*32 tokens by one wave.
+//   u = P x (P: [64][128] fp32, given as bf16 high and low parts Ph, Pl with
+//   P = Ph + Pl up to the rounding of Pl; both go through the MFMA),
+//   z = ||x|| u / ||u|| (0 if u = 0),  phi = [softmax(z); softmax(-z)].
+// The softmax exps are exp2 of (z - max) log2(e), one fma each.
+// xb[tt][s]: token 32tt + l%32, dims 16s + 8(l/32) .. +7.
+// phi[tt][sgn][ft]: accumulator layout, rows = feature 64 sgn + 32 ft +
+// acc_row(v, l/32), column = token.
+template <int NT>
+__device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const bf16* __restrict__ Ph,
+                                            const bf16* __restrict__ Pl, int ldp, f32x16 (&phi)[NT][2][2]) {
+    const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
+    f32x16 u[NT][2];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+        u[tt][0] = zero16();
+        u[tt][1] = zero16();
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+            const bf16x8 hi = ld_bf8(Ph + (32 * ft + col) * ldp + 16 * s + 8 * hf);
+            const bf16x8 lo = ld_bf8(Pl + (32 * ft + col) * ldp + 16 * s + 8 * hf);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                u[tt][ft] = mfma32(hi, xb[tt][s], u[tt][ft]);
+                u[tt][ft] = mfma32(lo, xb[tt][s], u[tt][ft]);
+            }
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+        float nx = 0.f, nu = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2 x2 = {xb[tt][s][2 * j], xb[tt][s][2 * j + 1]};
+                nx = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, nx, false);
+            }
+        float umax = -__builtin_inff(), umin = __builtin_inff();
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                nu = fmaf(u[tt][ft][v], u[tt][ft][v], nu);
+                umax = vmax(umax, u[tt][ft][v]);
+                umin = vmin(umin, u[tt][ft][v]);
+            }
+        nx += xor32(nx);
+        nu += xor32(nu);
+        umax = vmax(umax, xor32(umax));
+        umin = vmin(umin, xor32(umin));
+        // z = sc u with sc >= 0, so max z = sc umax and max(-z) = -sc umin
+        const float scl = (nu > 0.f ? sqrtf(nx) / sqrtf(nu) : 0.f) * kLog2e;
+        const float mp = scl * umax, mn = -scl * umin;
+        float sp = 0.f, sn = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float uu = u[tt][ft][v];
+                const float ep = __builtin_amdgcn_exp2f(fmaf(uu, scl, -mp));
+                const float en = __builtin_amdgcn_exp2f(fmaf(uu, -scl, -mn));
+                phi[tt][0][ft][v] = ep;
+                phi[tt][1][ft][v] = en;
+                sp += ep;
+                sn += en;
+            }
+        sp += xor32(sp);
+        sn += xor32(sn);
+        const float ip = 1.f / sp, in = 1.f / sn;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                phi[tt][0][ft][v] *= ip;
+                phi[tt][1][ft][v] *= in;
+            }
     }
 }
 

@@ -36,7 +36,6 @@ namespace {
 using namespace mt;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kFS = kC + 4;     // LDS row stride (floats) of transposed phi_k
@@ -57,89 +56,6 @@ __device__ __forceinline__ void load_q(const bf16* __restrict__ q, const Dims& D
         const bf16* row = q + (((size_t)b * D.N + t) * D.Hq + h) * kD + 8 * hf;
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[qt][s] = ld_bf8(row + 16 * s);
-    }
-}
-
-// NP-Map (Sec. 3.2, Hedgehog form of Sec. 2) of NT*32 tokens by one wave.
-//   u = P x (P: [64][128] fp32, given as bf16 high and low parts Ph, Pl with
-//   P = Ph + Pl up to the rounding of Pl; both go through the MFMA),
-//   z = ||x|| u / ||u|| (0 if u = 0),  phi = [softmax(z); softmax(-z)].
-// The softmax exps are exp2 of (z - max) log2(e), one fma each.
-// xb[tt][s]: token 32tt + l%32, dims 16s + 8(l/32) .. +7.
-// phi[tt][sgn][ft]: accumulator layout, rows = feature 64 sgn + 32 ft +
-// acc_row(v, l/32), column = token.
-template <int NT>
-__device__ __forceinline__ void np_map_mfma(const bf16x8 (&xb)[NT][8], const bf16* __restrict__ Ph,
-                                            const bf16* __restrict__ Pl, int ldp, f32x16 (&phi)[NT][2][2]) {
-    const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
-    f32x16 u[NT][2];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-        u[tt][0] = zero16();
-        u[tt][1] = zero16();
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
-            const bf16x8 hi = ld_bf8(Ph + (32 * ft + col) * ldp + 16 * s + 8 * hf);
-            const bf16x8 lo = ld_bf8(Pl + (32 * ft + col) * ldp + 16 * s + 8 * hf);
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                u[tt][ft] = mfma32(hi, xb[tt][s], u[tt][ft]);
-                u[tt][ft] = mfma32(lo, xb[tt][s], u[tt][ft]);
-            }
-        }
-    }
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-        float nx = 0.f, nu = 0.f;
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x2 x2 = {xb[tt][s][2 * j], xb[tt][s][2 * j + 1]};
-                nx = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, nx, false);
-            }
-        float umax = kNegInf, umin = __builtin_inff();
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                nu = fmaf(u[tt][ft][v], u[tt][ft][v], nu);
-                umax = vmax(umax, u[tt][ft][v]);
-                umin = vmin(umin, u[tt][ft][v]);
-            }
-        nx += xor32(nx);
-        nu += xor32(nu);
-        umax = vmax(umax, xor32(umax));
-        umin = vmin(umin, xor32(umin));
-        // z = sc u with sc >= 0, so max z = sc umax and max(-z) = -sc umin
-        const float scl = (nu > 0.f ? sqrtf(nx) / sqrtf(nu) : 0.f) * kLog2e;
-        const float mp = scl * umax, mn = -scl * umin;
-        float sp = 0.f, sn = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float uu = u[tt][ft][v];
-                const float ep = __builtin_amdgcn_exp2f(fmaf(uu, scl, -mp));
-                const float en = __builtin_amdgcn_exp2f(fmaf(uu, -scl, -mn));
-                phi[tt][0][ft][v] = ep;
-                phi[tt][1][ft][v] = en;
-                sp += ep;
-                sn += en;
-            }
-        sp += xor32(sp);
-        sn += xor32(sn);
-        const float ip = 1.f / sp, in = 1.f / sn;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                phi[tt][0][ft][v] *= ip;
-                phi[tt][1][ft][v] *= in;
-            }
     }
 }
 
@@ -920,6 +836,8 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&o)[4], f32x16 (&sc)[2], co
 // Blocks are issued longest first (largest c); consecutive blocks take
 // different KV heads, so each XCD's L2 keeps few compact lists.
 //
+// stat (not STATS, when not null): with the output, each query head's (m, l,
+// 0, c) as below, for a backward that starts from them.
 // STATS (the backward's first pass): instead of the output, each query head
 // writes (m, l, D, c) to stat: the reference m in natural units, the
 // normaliser l at that reference (linear terms included), D = dout . out
@@ -928,7 +846,7 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&o)[4], f32x16 (&sc)[2], co
 // rows list_off[c] .. list_off[c + 1] - 1 of (b, g) (n_full + 1 entries, the
 // last the open chunk's copy), for lists built from a given selection whose
 // chunks may hold fewer than lam rows.  STATS also writes each query head's
-// gated NP-Map features gamma phi_q (fp32, feature order) to phiq_out (zeros
+// gated NP-Map features gamma phi_q (bf16, feature order) to phiq_out (zeros
 // for queries with no routed token).
 template <int HB, int NWT, bool STATS = false>
 __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
@@ -937,7 +855,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const uint8_t* __restrict__ route,
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, LinBufs L,
     const float* __restrict__ gate, bf16* __restrict__ out, const int* __restrict__ list_off,
-    const bf16* __restrict__ dout, float* __restrict__ stat, float* __restrict__ phiq_out, Dims D) {
+    const bf16* __restrict__ dout, float* __restrict__ stat, bf16* __restrict__ phiq_out, Dims D) {
     constexpr int NW = HB * 2;  // waves
     const int HG = D.G / HB;
     const int per_c = D.B * D.Hkv * HG;
@@ -1115,17 +1033,17 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         if constexpr (STATS) {
             // this lane's 64 features of its query: 64 sgn + 32 f2 + acc_row(..)
             if (t0 + oq < D.N) {
-                float* pr = phiq_out + (((size_t)b * D.N + t0 + oq) * D.Hq + h) * kD;
+                bf16* pr = phiq_out + (((size_t)b * D.N + t0 + oq) * D.Hq + h) * kD;
 #pragma unroll
                 for (int sgn = 0; sgn < 2; ++sgn)
 #pragma unroll
                     for (int f2 = 0; f2 < 2; ++f2)
 #pragma unroll
                         for (int v4 = 0; v4 < 4; ++v4) {
-                            f32x4 x4;
+                            bf16x4 x4;
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) x4[j] = phi[0][sgn][f2][4 * v4 + j];
-                            *reinterpret_cast<f32x4*>(pr + 64 * sgn + 32 * f2 + acc_row(4 * v4, hf)) = x4;
+                            for (int j = 0; j < 4; ++j) x4[j] = (bf16)phi[0][sgn][f2][4 * v4 + j];
+                            *reinterpret_cast<bf16x4*>(pr + 64 * sgn + 32 * f2 + acc_row(4 * v4, hf)) = x4;
                         }
             }
         }
@@ -1232,10 +1150,10 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
 
     if constexpr (STATS) {
         if (c < NWT && t0 + oq < D.N) {  // no routed token yet: no linear term
-            float* pr = phiq_out + (((size_t)b * D.N + t0 + oq) * D.Hq + h) * kD;
-            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+            bf16* pr = phiq_out + (((size_t)b * D.N + t0 + oq) * D.Hq + h) * kD;
+            const bf16x4 z4 = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
 #pragma unroll
-            for (int x = 0; x < 16; ++x) *reinterpret_cast<f32x4*>(pr + 32 * (x >> 2) + acc_row(4 * (x & 3), hf)) = z4;
+            for (int x = 0; x < 16; ++x) *reinterpret_cast<bf16x4*>(pr + 32 * (x >> 2) + acc_row(4 * (x & 3), hf)) = z4;
         }
     }
     // A query with no linear mass (t < W, or every routed token of its
@@ -1642,7 +1560,20 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
         return;
     }
     // epilogue: normalise, stage each wave's 32 x 128 tile in LDS, write rows
-    const float il = 1.f / (ls + xor32(ls));
+    const float lsum = ls + xor32(ls);
+    const float il = 1.f / lsum;
+    if (stat && hf == 0 && t0 + oq < D.N) {
+        // the statistics a backward can start from: reference m (natural
+        // units), normaliser l, 0 in place of dout . out, c = exp(-m) / l
+        // for a query with linear terms (else 0)
+        constexpr float kLn2 = 0.6931471805599453f;
+        f32x4 st;
+        st[0] = m2 * kLn2;
+        st[1] = lsum;
+        st[2] = 0.f;
+        st[3] = lamass ? __builtin_amdgcn_exp2f(-m2) / lsum : 0.f;
+        *reinterpret_cast<f32x4*>(stat + (((size_t)b * D.N + t0 + oq) * D.Hq + h) * 4) = st;
+    }
     bf16* ot = reinterpret_cast<bf16*>(sts) + wave * (32 * kKS);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -1885,7 +1816,8 @@ hipError_t launch_la_group_scan(const Dims& D, const LinBufs& L, int cap_chunk, 
 hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const void* v,
                               const void* wsplit, const void* phik, const uint8_t* route,
                               const void* ksel, const void* vsel, const LinBufs& L,
-                              const float* gate, const int* list_off, void* out, hipStream_t s) {
+                              const float* gate, const int* list_off, void* out, float* stats,
+                              hipStream_t s) {
     const int n = D.Hkv * (kD / 2) * kD;
     const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
     const bf16* wql = wqh + n;
@@ -1898,7 +1830,7 @@ hipError_t launch_hybrid_main(const Dims& D, const void* q, const void* k, const
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       L, gate, reinterpret_cast<bf16*>(out), list_off, nullptr, nullptr, nullptr, D)
+                       L, gate, reinterpret_cast<bf16*>(out), list_off, nullptr, stats, nullptr, D)
 #define STILL_MAIN(H)              \
     do {                           \
         if (nwt == 1)              \
@@ -1942,7 +1874,7 @@ hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, cons
                                const void* wsplit, const void* phik, const uint8_t* route,
                                const void* ksel, const void* vsel, const LinBufs& L,
                                const float* gate, const int* list_off, const void* dout,
-                               float* stat, float* phiq, hipStream_t s) {
+                               float* stat, void* phiq, hipStream_t s) {
     const int n = D.Hkv * (kD / 2) * kD;
     const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
     const bf16* wql = wqh + n;
@@ -1955,7 +1887,8 @@ hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, cons
                        reinterpret_cast<const bf16*>(v), wqh, wql,                                \
                        reinterpret_cast<const bf16*>(phik), route,                              \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
-                       L, gate, nullptr, list_off, reinterpret_cast<const bf16*>(dout), stat, phiq, D)
+                       L, gate, nullptr, list_off, reinterpret_cast<const bf16*>(dout), stat,       \
+                       reinterpret_cast<bf16*>(phiq), D)
 #define STILL_STATS(H)             \
     do {                           \
         if (nwt == 1)              \

@@ -238,7 +238,7 @@ static int fwd_launches(const Dims& D, const still_shape* sh, bool with_cache) {
 
 static int fwd(const still_shape* sh, const void* q, const void* k, const void* v,
                const float* wq, const float* wk, const float* gate, void* out, float* scores_opt,
-               int32_t* sel_idx_opt, still_cache* cache, void* ws, size_t ws_bytes,
+               int32_t* sel_idx_opt, float* stats_opt, still_cache* cache, void* ws, size_t ws_bytes,
                hipStream_t s, Timeline& tl) {
     int st = check_shape(sh, false);
     if (st) return st;
@@ -246,7 +246,7 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
     if (D.B == 0 || D.N == 0) return STILL_OK;  // nothing to compute; pointers unused
     if (!q || !k || !v || !wq || !wk || !out) return STILL_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(wq) ||
-        !aligned16(wk) || !aligned4(gate))
+        !aligned16(wk) || !aligned4(gate) || !aligned16(stats_opt))
         return STILL_ERR_INVALID_ARG;
     if (cache) {
         const int64_t need = D.lam * ceil_div((int64_t)D.N - D.W, D.C);
@@ -286,7 +286,7 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
                                           cache ? cache->lin_z : nullptr, s));
         STILL_LAUNCH(tl, s, "hybrid_main",
                      launch_hybrid_main(DT, q, k, v, f.wsplit, f.phik, f.route, f.ksel, f.vsel, f.lin, gate,
-                                        wide ? f.loff : nullptr, out, s));
+                                        wide ? f.loff : nullptr, out, stats_opt, s));
         if (cache)
             STILL_LAUNCH(tl, s, "handoff",
                          launch_handoff(D, k, v, wk, scores, sel, f.route, cap_chunk, view_of(cache), s));
@@ -305,7 +305,7 @@ static int fwd(const still_shape* sh, const void* q, const void* k, const void* 
     STILL_LAUNCH(tl, s, "la_scan", launch_la_scan(D, f.lin, cap_chunk, cache ? cache->lin_S : nullptr,
                                                   cache ? cache->lin_z : nullptr, s));
     STILL_LAUNCH(tl, s, "main_general",
-                 launch_main_general(D, q, k, v, f.phiq, f.phik, f.route, sel, f.lin, out, s));
+                 launch_main_general(D, q, k, v, f.phiq, f.phik, f.route, sel, f.lin, out, stats_opt, s));
     if (cache)
         STILL_LAUNCH(tl, s, "handoff",
                      launch_handoff(D, k, v, wk, scores, sel, f.route, cap_chunk, view_of(cache), s));
@@ -510,8 +510,9 @@ static hipError_t mark_launch(void* ctx, const char* name) {
 
 static int bwd(const still_shape* sh, const void* q, const void* k, const void* v,
                const float* wq, const float* wk, const float* gate, const int32_t* sel_idx,
-               const void* dout, float* dq, float* dk, float* dv, float* dwq, float* dwk,
-               float* dgate, void* ws, size_t ws_bytes, hipStream_t s, Timeline& tl) {
+               const void* dout, const void* out_opt, const float* stats_opt, float* dq, float* dk,
+               float* dv, float* dwq, float* dwk, float* dgate, void* ws, size_t ws_bytes,
+               hipStream_t s, Timeline& tl) {
     int st = check_shape(sh, false);
     if (st) return st;
     const Dims D = make_dims(sh, sh->seqlen);
@@ -527,6 +528,9 @@ static int bwd(const still_shape* sh, const void* q, const void* k, const void* 
     for (const void* p : ptrs)
         if (!aligned16(p)) return STILL_ERR_INVALID_ARG;
     if (!aligned4(gate) || !aligned4(dgate)) return STILL_ERR_INVALID_ARG;
+    // the forward's output and statistics come together or not at all
+    if ((out_opt == nullptr) != (stats_opt == nullptr) || !aligned16(out_opt) || !aligned16(stats_opt))
+        return STILL_ERR_INVALID_ARG;
     if (D.lam > 0 && D.n_full > 0 && (!sel_idx || (reinterpret_cast<uintptr_t>(sel_idx) & 3u)))
         return STILL_ERR_INVALID_ARG;
     if (!ws || ws_bytes < bwd_bytes(D, sh)) return STILL_ERR_WORKSPACE;
@@ -550,6 +554,8 @@ static int bwd(const still_shape* sh, const void* q, const void* k, const void* 
     a.dwk = dwk;
     a.gate = gate;
     a.dgate = gate ? dgate : nullptr;
+    a.out = out_opt;
+    a.stats = stats_opt;
     MarkCtx mc{&tl, s};
     STILL_TRY(launch_bwd(D, a, w, s, BwdMark{mark_launch, &mc}));
     STILL_TRY(tl.end(s));
@@ -612,18 +618,18 @@ int still_fwd_workspace_size(const still_shape* shape, size_t* bytes) {
 
 int still_hybrid_attn_fwd(const still_shape* shape, const void* q, const void* k, const void* v,
                           const float* wphi_q, const float* wphi_k, const float* gate_opt,
-                          void* out, float* scores_opt, int32_t* sel_idx_opt,
+                          void* out, float* scores_opt, int32_t* sel_idx_opt, float* stats_opt,
                           still_cache* cache_opt, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
     still::Timeline tl;
     return still::fwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, out, scores_opt, sel_idx_opt,
-                      cache_opt, workspace, workspace_bytes, stream, tl);
+                      stats_opt, cache_opt, workspace, workspace_bytes, stream, tl);
 }
 
 int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
                                 const float* gate_opt, void* out, float* scores_opt,
-                                int32_t* sel_idx_opt,
+                                int32_t* sel_idx_opt, float* stats_opt,
                                 still_cache* cache_opt, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream, hipEvent_t* events, int32_t max_events,
                                 int32_t* n_launches, const char** kernel_names_opt) {
@@ -633,7 +639,7 @@ int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const v
     tl.max_ev = max_events;
     tl.names = kernel_names_opt;
     const int st = still::fwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, out, scores_opt,
-                              sel_idx_opt, cache_opt, workspace, workspace_bytes, stream, tl);
+                              sel_idx_opt, stats_opt, cache_opt, workspace, workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
 }
@@ -705,17 +711,19 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes) {
 
 int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k, const void* v,
                           const float* wphi_q, const float* wphi_k, const float* gate_opt,
-                          const int32_t* sel_idx, const void* dout, float* dq, float* dk,
+                          const int32_t* sel_idx, const void* dout, const void* out_opt,
+                          const float* stats_opt, float* dq, float* dk,
                           float* dv, float* dwphi_q, float* dwphi_k, float* dgate_opt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
     still::Timeline tl;
-    return still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, dq, dk, dv, dwphi_q,
-                      dwphi_k, dgate_opt, workspace, workspace_bytes, stream, tl);
+    return still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, out_opt, stats_opt, dq,
+                      dk, dv, dwphi_q, dwphi_k, dgate_opt, workspace, workspace_bytes, stream, tl);
 }
 
 int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
                                 const float* gate_opt, const int32_t* sel_idx, const void* dout,
+                                const void* out_opt, const float* stats_opt,
                                 float* dq, float* dk, float* dv, float* dwphi_q, float* dwphi_k,
                                 float* dgate_opt, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
@@ -726,8 +734,9 @@ int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const v
     tl.ev = events;
     tl.max_ev = max_events;
     tl.names = kernel_names_opt;
-    const int st = still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, dq, dk, dv,
-                              dwphi_q, dwphi_k, dgate_opt, workspace, workspace_bytes, stream, tl);
+    const int st = still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, out_opt,
+                              stats_opt, dq, dk, dv, dwphi_q, dwphi_k, dgate_opt, workspace,
+                              workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
 }

@@ -78,7 +78,7 @@ def lib() -> ct.CDLL:
         L.still_fwd_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
         L.still_hybrid_attn_fwd.restype = ct.c_int
         L.still_hybrid_attn_fwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                            ct.POINTER(CacheStruct), vp, sz, vp]
+                                            vp, ct.POINTER(CacheStruct), vp, sz, vp]
         L.still_decode_workspace_size.restype = ct.c_int
         L.still_decode_workspace_size.argtypes = [ct.POINTER(Shape), ct.c_int32, ct.POINTER(sz)]
         L.still_hybrid_attn_decode_step.restype = ct.c_int
@@ -95,7 +95,7 @@ def lib() -> ct.CDLL:
         L.still_bwd_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
         L.still_hybrid_attn_bwd.restype = ct.c_int
         L.still_hybrid_attn_bwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                            vp, vp, vp, vp, vp, vp, sz, vp]
+                                            vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.still_future_kv_utility_workspace_size.restype = ct.c_int
         L.still_future_kv_utility_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
         L.still_future_kv_utility.restype = ct.c_int
@@ -237,12 +237,13 @@ class DecodeCache:
 
 
 def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale=0.0,
-        return_scores=False, return_sel=False, cache: DecodeCache | None = None,
+        return_scores=False, return_sel=False, return_stats=False, cache: DecodeCache | None = None,
         out=None, workspace=None, general=False, timer: LaunchTimer | None = None,
-        route="saliency", gate=None) -> dict:
+        route="saliency", gate=None, stats=None) -> dict:
     """still_hybrid_attn_fwd.  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or f32),
     wphi_* [Hkv, d'/2, d] f32, gate: optional gate logits [B,N,Hq] f32.
-    Returns dict(out, scores?, sel_idx?)."""
+    return_stats (or a given stats tensor [B,N,Hq,4] f32): the per-query
+    statistics bwd can start from.  Returns dict(out, scores?, sel_idx?, stats?)."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
@@ -261,12 +262,17 @@ def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale
     lam = min(topk, chunk)
     scores = torch.empty((B, Hkv, N), dtype=torch.float32, device=dev) if return_scores else None
     sel = torch.empty((B, Hkv, N // chunk, lam), dtype=torch.int32, device=dev) if return_sel else None
+    if stats is not None:
+        _expect(stats, "stats", torch.float32, (B, N, Hq, 4))
+    elif return_stats:
+        stats = torch.empty((B, N, Hq, 4), dtype=torch.float32, device=dev)
     nbytes = fwd_workspace_size(sh)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     cs = ct.byref(cache.struct()) if cache is not None else None
     args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(gate),
-            _ptr(out), _ptr(scores), _ptr(sel), cs, _ptr(workspace), workspace.numel(), _stream()]
+            _ptr(out), _ptr(scores), _ptr(sel), _ptr(stats), cs, _ptr(workspace), workspace.numel(),
+            _stream()]
     if timer is None:
         _check(lib().still_hybrid_attn_fwd(*args), "still_hybrid_attn_fwd")
     else:
@@ -276,6 +282,8 @@ def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale
         res["scores"] = scores
     if sel is not None:
         res["sel_idx"] = sel
+    if stats is not None:
+        res["stats"] = stats
     return res
 
 
@@ -380,12 +388,13 @@ def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.T
 
 def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6,
         softmax_scale=0.0, workspace=None, timer: LaunchTimer | None = None, gate=None,
-        general=False) -> dict:
+        general=False, out=None, stats=None) -> dict:
     """still_hybrid_attn_bwd: gradients of sum(dout * out) for the forward
     with the same arguments, under the routing sel_idx [B, Hkv, N/C, lambda]
     (the forward's sel_idx output; None when there is nothing selected).
-    Returns dict(dq, dk, dv, dwphi_q, dwphi_k), all fp32, plus dgate
-    [B, N, Hq] when gate logits [B, N, Hq] are given."""
+    out, stats: the forward's output and return_stats tensor, both or
+    neither.  Returns dict(dq, dk, dv, dwphi_q, dwphi_k), all fp32, plus
+    dgate [B, N, Hq] when gate logits [B, N, Hq] are given."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
@@ -399,6 +408,10 @@ def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6
     _expect(wphi_k, "wphi_k", torch.float32, (Hkv, wphi_q.shape[1], d))
     if sel_idx is not None:
         _expect(sel_idx, "sel_idx", torch.int32, (B, Hkv, N // chunk, min(topk, chunk)))
+    if out is not None:
+        _expect(out, "out", q.dtype, (B, N, Hq, d))
+    if stats is not None:
+        _expect(stats, "stats", torch.float32, (B, N, Hq, 4))
     dev = q.device
     f32 = dict(dtype=torch.float32, device=dev)
     res = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32),
@@ -411,7 +424,8 @@ def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(gate),
-            _ptr(sel_idx), _ptr(dout), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]),
+            _ptr(sel_idx), _ptr(dout), _ptr(out), _ptr(stats), _ptr(res["dq"]), _ptr(res["dk"]),
+            _ptr(res["dv"]),
             _ptr(res["dwphi_q"]), _ptr(res["dwphi_k"]), _ptr(res.get("dgate")), _ptr(workspace),
             workspace.numel(), _stream()]
     if timer is None:

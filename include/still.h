@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define STILL_ABI_VERSION 4
+#define STILL_ABI_VERSION 5
 
 typedef enum {
     STILL_OK = 0,
@@ -177,6 +177,14 @@ int still_fwd_workspace_size(const still_shape* shape, size_t* bytes);
  *   scores_opt      [B, Hkv, N] fp32 group-mean Self-Saliency, or NULL
  *   sel_idx_opt     [B, Hkv, N / C, min(topk, C)] int32 selected positions of
  *                   every complete chunk, ascending, or NULL
+ *   stats_opt       [B, N, Hq, 4] fp32, 16-byte aligned, or NULL: per query
+ *                   head (m, l, 0, c), the reference point of the shared
+ *                   normaliser (natural-log units), the normaliser at that
+ *                   reference (softmax and linear weights together, Fig. 2
+ *                   hybrid aggregation), 0, and c = exp(-m) / l for a query
+ *                   with linear terms (0 otherwise); with the output, what
+ *                   still_hybrid_attn_bwd can start from instead of
+ *                   recomputing them
  *   cache_opt       if not NULL, filled as the recurrent form would leave it
  *                   after these N tokens (prefill -> decode hand-off):
  *                   cache_opt->pos must equal N on entry; needs
@@ -188,7 +196,7 @@ int still_fwd_workspace_size(const still_shape* shape, size_t* bytes);
 int still_hybrid_attn_fwd(const still_shape* shape, const void* q, const void* k, const void* v,
                           const float* wphi_q, const float* wphi_k, const float* gate_opt,
                           void* out, float* scores_opt,
-                          int32_t* sel_idx_opt, still_cache* cache_opt, void* workspace,
+                          int32_t* sel_idx_opt, float* stats_opt, still_cache* cache_opt, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace one decode step needs for `shape` (seqlen is
@@ -281,6 +289,12 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
  *             their chunk, and repeats, are ignored.  May be NULL when
  *             min(topk, C) == 0 or N < C.
  *   dout      [B, N, Hq, d] dtype, the gradient of L w.r.t. out
+ *   out_opt, stats_opt  the forward's out and stats_opt for the same inputs,
+ *             gate and routing, both or neither (else STILL_ERR_INVALID_ARG),
+ *             16-byte aligned: the matrix-core path then takes each query's
+ *             reference, normaliser and linear weight from stats_opt and
+ *             dout . out from out instead of a first pass that recomputes
+ *             them; the fp32 kernels ignore them
  *   dq        [B, N, Hq, d] fp32, written
  *   dk, dv    [B, N, Hkv, d] fp32, written
  *   dwphi_q, dwphi_k  [Hkv, d'/2, d] fp32, written
@@ -291,8 +305,9 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
  * For bf16 storage with d = d' = 128, window 64 / 128 / 256, chunk 64 / 128 /
  * 256 no longer than the window, and 1, 2, 4 or 8 query heads per KV head,
  * every term runs on the matrix cores: a first pass (the forward's main
- * kernel over compact lists of the given selection) gives each query's
- * reference, normaliser and dout . out; the softmax terms are formed from
+ * kernel over compact lists of the given selection; skipped when out_opt and
+ * stats_opt are given) gives each query's reference, normaliser and
+ * dout . out; the softmax terms are formed from
  * bf16 logit and dout . v products with dS rounded to bf16, as the forward
  * rounds its probabilities, and the linear terms, the NP-Map backward and
  * the projection gradients take bf16 operands too (gradients to about 1e-2
@@ -305,7 +320,8 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
  * STILL_ERR_INVALID_ARG. */
 int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k, const void* v,
                           const float* wphi_q, const float* wphi_k, const float* gate_opt,
-                          const int32_t* sel_idx, const void* dout, float* dq, float* dk,
+                          const int32_t* sel_idx, const void* dout, const void* out_opt,
+                          const float* stats_opt, float* dq, float* dk,
                           float* dv, float* dwphi_q, float* dwphi_k, float* dgate_opt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -341,9 +357,9 @@ int still_future_kv_utility(const still_shape* shape, const void* q, const void*
 int still_hybrid_attn_fwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
                                 const float* gate_opt, void* out, float* scores_opt, int32_t* sel_idx_opt,
-                                still_cache* cache_opt, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream, hipEvent_t* events, int32_t max_events,
-                                int32_t* n_launches, const char** kernel_names_opt);
+                                float* stats_opt, still_cache* cache_opt, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                                int32_t max_events, int32_t* n_launches, const char** kernel_names_opt);
 int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q, const void* k,
                                         const void* v, const float* wphi_q,
                                         const float* wphi_k, const float* gate_opt,
@@ -355,6 +371,7 @@ int still_hybrid_attn_decode_step_timed(const still_shape* shape, const void* q,
 int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
                                 const float* gate_opt, const int32_t* sel_idx, const void* dout,
+                                const void* out_opt, const float* stats_opt,
                                 float* dq, float* dk, float* dv, float* dwphi_q, float* dwphi_k,
                                 float* dgate_opt, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,

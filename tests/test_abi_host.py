@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert S.abi_version() == 4
+    assert S.abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5):
         assert S.status_str(code) and S.status_str(code) != "unknown status"
     assert S.status_str(7) == "unknown status"
@@ -52,9 +52,9 @@ def shape(**kw):
     return S.make_shape(**base)
 
 
-def fwd_status(sh, ws_bytes=1 << 40, cache=None, ptr=FAKE, ws=FAKE, gate=None):
+def fwd_status(sh, ws_bytes=1 << 40, cache=None, ptr=FAKE, ws=FAKE, gate=None, stats=None):
     return S.lib().still_hybrid_attn_fwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, gate, ptr, None,
-                                         None, ct.byref(cache) if cache is not None else None, ws,
+                                         None, stats, ct.byref(cache) if cache is not None else None, ws,
                                          ws_bytes, None)
 
 
@@ -101,6 +101,8 @@ def test_null_and_misaligned_pointers():
     sh = shape()
     assert fwd_status(sh, ptr=None) == S.STILL_ERR_INVALID_ARG
     assert fwd_status(sh, ptr=MISALIGNED) == S.STILL_ERR_INVALID_ARG
+    assert fwd_status(sh, stats=MISALIGNED) == S.STILL_ERR_INVALID_ARG
+    assert fwd_status(sh, stats=FAKE, ws_bytes=16) == S.STILL_ERR_WORKSPACE  # accepted, then too small
 
 
 def test_workspace_size_and_too_small_workspace():
@@ -183,9 +185,10 @@ def test_ragged_decode_checks():
     assert c.pos == 7
 
 
-def bwd_status(sh, sel=FAKE, ws_bytes=1 << 40, ptr=FAKE, ws=FAKE, dw=FAKE, gate=None, dgate=None):
-    return S.lib().still_hybrid_attn_bwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, gate, sel, ptr, ptr,
-                                         ptr, ptr, dw, dw, dgate, ws, ws_bytes, None)
+def bwd_status(sh, sel=FAKE, ws_bytes=1 << 40, ptr=FAKE, ws=FAKE, dw=FAKE, gate=None, dgate=None,
+               out=None, stats=None):
+    return S.lib().still_hybrid_attn_bwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, gate, sel, ptr, out,
+                                         stats, ptr, ptr, ptr, dw, dw, dgate, ws, ws_bytes, None)
 
 
 def test_bwd_checks():
@@ -202,6 +205,10 @@ def test_bwd_checks():
     assert bwd_status(sh, ptr=None) == S.STILL_ERR_INVALID_ARG
     assert bwd_status(sh, ptr=MISALIGNED) == S.STILL_ERR_INVALID_ARG
     assert bwd_status(sh, dw=None) == S.STILL_ERR_INVALID_ARG
+    # the forward's out and statistics come together, 16-byte aligned
+    assert bwd_status(sh, out=FAKE) == S.STILL_ERR_INVALID_ARG
+    assert bwd_status(sh, stats=FAKE) == S.STILL_ERR_INVALID_ARG
+    assert bwd_status(sh, out=FAKE, stats=MISALIGNED) == S.STILL_ERR_INVALID_ARG
     for kw, st in ((dict(n_q_heads=6, n_kv_heads=4), S.STILL_ERR_INVALID_ARG),
                    (dict(head_dim=96), S.STILL_ERR_UNSUPPORTED)):
         assert bwd_status(shape(**kw)) == st
@@ -210,8 +217,9 @@ def test_bwd_checks():
     evs = (ct.c_void_p * 4)()
     # 16 (general) or 21 (matrix-core) launches need one event more; too few is
     # rejected before anything runs
-    assert timed(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                 FAKE, None, FAKE, 1 << 40, None, evs, 4, ct.byref(n), None) == S.STILL_ERR_INVALID_ARG
+    assert timed(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None, evs, 4, ct.byref(n),
+                 None) == S.STILL_ERR_INVALID_ARG
 
 
 def test_bwd_empty_problem_without_projection_gradients_is_noop():

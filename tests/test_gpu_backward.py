@@ -88,7 +88,9 @@ CASES = {
 }
 
 
-def run(gpu_lib, cfg, seed, corrupt=False, general=False):
+def run(gpu_lib, cfg, seed, corrupt=False, general=False, saved=False, fwd_general=False):
+    """saved: the backward starts from the forward's out and statistics (the
+    forward on the general kernels when fwd_general)."""
     raw = workloads.make_prefill(cfg, seed)
     dt = torch_dtype(cfg["dtype"])
     dev, ref = prepare(raw, dt)
@@ -97,9 +99,12 @@ def run(gpu_lib, cfg, seed, corrupt=False, general=False):
     dout = dout.cuda().contiguous()
     W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
     sel = None
-    if min(lam, C) > 0:
-        sel = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W,
-                          chunk=C, topk=lam, return_sel=True)["sel_idx"]
+    fw = None
+    if min(lam, C) > 0 or saved:
+        fw = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W,
+                         chunk=C, topk=lam, return_sel=min(lam, C) > 0, return_stats=saved,
+                         general=fwd_general)
+        sel = fw.get("sel_idx")
     osel = None if sel is None else sel.cpu().numpy().astype(np.int64)
     if corrupt and sel is not None and sel.shape[2] > 1:
         # a repeated entry and an out-of-chunk entry are ignored by the library;
@@ -110,8 +115,9 @@ def run(gpu_lib, cfg, seed, corrupt=False, general=False):
         osel = bad.cpu().numpy().astype(np.int64)
         osel[:, :, 1, 0] = osel[:, :, 1, 1]
         sel = bad
+    extra = dict(out=fw["out"], stats=fw["stats"]) if saved else {}
     g = gpu_lib.bwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], sel, dout,
-                    window=W, chunk=C, topk=lam, general=general)
+                    window=W, chunk=C, topk=lam, general=general, **extra)
     torch.cuda.synchronize()
     p = O.Params(window=W, chunk=C, topk=lam)
     o = O.bwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"], ref_dout, p,
@@ -138,6 +144,26 @@ def test_bwd_matches_oracle(gpu_lib, name, general):
         f"shape={workloads.shape_of(cfg)} seed={seed}")
     g, o = run(gpu_lib, cfg, seed, general=general)
     compare(g, o, grad_tol(cfg, general))
+
+
+SAVED_CASES = ["bf16_ragged_G2", "bf16_G1", "bf16_G4_linear", "bf16_swa_la", "bf16_all_selected",
+               "bf16_short_no_chunk", "bf16_single_token", "bf16_underflow_G2", "bf16_underflow_all_selected",
+               "bf16_W128_C64_G4", "bf16_W256_C64_G2", "bf16_W128_C128_G4", "bf16_W256_C256_G1_lam100",
+               "f32_d128_G2"]
+
+
+@pytest.mark.parametrize("fwd_general", [False, True], ids=["fwd_picked", "fwd_general"])
+@pytest.mark.parametrize("name", SAVED_CASES)
+def test_bwd_from_forward_statistics_matches_oracle(gpu_lib, name, fwd_general):
+    """The backward started from the forward's out and statistics (no first
+    pass on the matrix cores) against the oracle, with the statistics from
+    either forward path: both define (m, l) at their own reference point, so
+    either must do.  The fp32 kernels ignore them."""
+    cfg, seed = CASES[name]
+    say(f"[bwd] from forward stats case={name} fwd_general={fwd_general} "
+        f"matrix-core={mfma_path(cfg)} shape={workloads.shape_of(cfg)} seed={seed}")
+    g, o = run(gpu_lib, cfg, seed, saved=True, fwd_general=fwd_general)
+    compare(g, o, grad_tol(cfg, False))
 
 
 @pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])

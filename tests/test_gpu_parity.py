@@ -142,6 +142,46 @@ def test_fwd_matches_oracle(gpu_lib, name, general):
     assert serr <= 1e-4
 
 
+STATS_CASES = ["bf16_ragged_G4", "bf16_G1", "bf16_G8", "bf16_swa_la_W_eq_C", "bf16_all_selected",
+               "bf16_window_covers", "bf16_pure_linear", "bf16_overflow_G4", "bf16_underflow_G4",
+               "bf16_W128_C64_G4", "bf16_W128_C128_G4", "toy_fp32", "f32_G8_d64"]
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
+@pytest.mark.parametrize("name", STATS_CASES)
+def test_fwd_statistics_match_oracle(gpu_lib, name, general):
+    """The statistics the forward hands a backward, (m, l, 0, c) per query
+    head: m + ln l is the log of the shared normaliser whatever the reference
+    m (list view Fig. 2), c = exp(-m) / l exactly for the queries with linear
+    weight and 0 for the others."""
+    cfg, seed = CASES[name]
+    say(f"[fwd stats] case={name} general={general} shape={workloads.shape_of(cfg)} seed={seed}")
+    raw = workloads.make_prefill(cfg, seed)
+    dev, ref = prepare(raw, torch_dtype(cfg["dtype"]))
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    res = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W, chunk=C,
+                      topk=lam, return_sel=True, return_stats=True, general=general)
+    torch.cuda.synchronize()
+    p = O.Params(window=W, chunk=C, topk=lam)
+    gsel = res["sel_idx"].cpu().numpy().astype(np.int64) if p.topk_eff() > 0 else None
+    o = O.fwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"], p, sel_override=gsel)
+    st = res["stats"].double().cpu().numpy()
+    m, l, zero, c = st[..., 0], st[..., 1], st[..., 2], st[..., 3]
+    assert np.isfinite(st).all() and (l > 0).all() and (zero == 0).all()
+    err = float(np.max(np.abs(m + np.log(l) - o["lse"])))
+    tol = 1e-5 if cfg["dtype"] == "f32" else 1e-2
+    say(f"  max |m + ln l - lse| {err:.2e} (tol {tol:g})")
+    assert err <= tol
+    lin = o["has_linear"]
+    assert (c[~lin] == 0).all()
+    # where exp(-lse) is a normal fp32 number (not under the keys x80 outliers)
+    ok = lin & (o["lse"] < 80.0)
+    if ok.any():
+        cerr = float(np.max(np.abs(c[ok] * np.exp(o["lse"][ok]) - 1.0)))
+        say(f"  max |c exp(lse) - 1| over {int(ok.sum())} rows with linear weight {cerr:.2e}")
+        assert cerr <= tol
+
+
 @pytest.mark.parametrize("W,C", [(64, 64), (128, 64), (128, 128), (256, 128), (256, 256)])
 def test_matrix_core_path_taken(gpu_lib, W, C):
     """The pages' (W, C) settings with d = 128 in bf16 run on the matrix-core
