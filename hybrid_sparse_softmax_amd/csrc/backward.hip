@@ -989,7 +989,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
         }
         if ((e = mark.fn(mark.ctx, "bwd_dq")) != hipSuccess) return e;
         if ((e = launch_bwd_dq(DT, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.list_off, w.stat,
-                               w.phik16, w.lin16, a.gate, w.phiq, a.dq, w.dphiq,
+                               w.phik16, w.lin16, a.gate, w.phiq, a.dq, w.duq,
                                a.gate ? a.dgate : nullptr, a.stats, a.out, w.wsplit, s)) != hipSuccess)
             return e;
     }
@@ -1063,10 +1063,9 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     const int ntok = D.B * D.N, half = D.fd / 2;
     const int nw = D.Hkv * half * DD;
     if (w.mfma) {
-        // NP-Map backward and projection gradients on the matrix cores (du in
-        // bf16 in the du buffers)
-        if ((e = mark.fn(mark.ctx, "np_vjp_q")) != hipSuccess) return e;
-        if ((e = launch_np_bwd(D, a.q, w.wsplit, 0, w.dphiq, a.dq, w.duq, s)) != hipSuccess) return e;
+        // NP-Map backward of the keys (the queries' ran in the dq kernel) and
+        // the projection gradients on the matrix cores (du in bf16 in the du
+        // buffers)
         if ((e = mark.fn(mark.ctx, "np_vjp_k")) != hipSuccess) return e;
         if ((e = launch_np_bwd(D, a.k, w.wsplit, 1, w.dphik, a.dk, w.duk, s)) != hipSuccess) return e;
         if ((e = mark.fn(mark.ctx, "dw_q")) != hipSuccess) return e;
@@ -1104,7 +1103,7 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 
 }  // namespace
 
-int bwd_launch_count(bool mfma) { return mfma ? 17 : 16; }
+int bwd_launch_count(bool) { return 16; }
 
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t s,
                       BwdMark mark) {

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const bf16* __restrict__ ksel, const bf16* __restrict__ vsel, const int* __restrict__ list_off,
     float* __restrict__ stat, const bf16* __restrict__ phik, LinBufs L,
     const float* __restrict__ gate, bf16* __restrict__ phiq, float* __restrict__ dq,
-    float* __restrict__ dphiq, float* __restrict__ dgate, const float* __restrict__ stat_in,
+    bf16* __restrict__ du_out, float* __restrict__ dgate, const float* __restrict__ stat_in,
     const bf16* __restrict__ out, const bf16* __restrict__ wqh, const bf16* __restrict__ wql, Dims D) {
     constexpr int NW = HB * 2;
     const int HG = D.G / HB;
@@ -617,31 +617,182 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
         }
     }
-    if (!qvalid) return;
-    // dphi_q = gamma c_t dfq (feature order), dgate = (1 - gamma) c_t fq . dfq
+    // dphi_q = gamma c_t dfq (the ungated features' gradient), dgate =
+    // (1 - gamma) c_t fq . dfq
     const float cf = stq[3];
     const float gw = gate_weight(gate, qo);
-    float* dpr = dphiq + qo * kD;
-    const bf16* fqr = phiq + qo * kD;
-    float fdot = 0.f;
+    if (dgate) {
+        const bf16* fqr = phiq + qo * kD;
+        float fdot = 0.f;
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
+        for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-            const int f0 = kperm(32 * ft + acc_row(4 * v4, hf));  // four consecutive features
-            f32x4 o4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o4[j] = gw * cf * dfq[ft][4 * v4 + j];
-            *reinterpret_cast<f32x4*>(dpr + f0) = o4;
-            if (dgate) {
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int f0 = kperm(32 * ft + acc_row(4 * v4, hf));  // four consecutive features
                 const bf16x4 fq4 = *reinterpret_cast<const bf16x4*>(fqr + f0);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) fdot = fmaf((float)fq4[j], dfq[ft][4 * v4 + j], fdot);
             }
-        }
-    if (dgate) {
         fdot += xor32(fdot);
-        if (hf == 0) dgate[qo] = (1.f - gw) * cf * fdot;
+        if (hf == 0 && qvalid) dgate[qo] = (1.f - gw) * cf * fdot;
+    }
+#pragma unroll
+    for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) dfq[ft][vv] *= gw * cf;
+
+    // ---- NP-Map backward of the query (full text Sec. 3.2; the map
+    // u = P q, z = ||q|| u / ||u||, phi = [softmax(z); softmax(-z)]):
+    //   dz = phi+ (dphi+ - <phi+, dphi+>) - phi- (dphi- - <phi-, dphi->)
+    //   du = ||q|| (dz - uh <uh, dz>) / ||u||,  dq += P^T du + (<uh, dz> / ||q||) q
+    // and du (bf16) for the projection gradient.  dfq's row 32 ft + r (ft <
+    // 2) is the gradient of phi+ at feature kperm(32 ft + r) (ft >= 2: phi-
+    // of feature kperm(32 (ft - 2) + r)), so the projection's rows are
+    // staged in that order (LDS row r = P row kperm(r)): u then comes out of
+    // the matrix cores with the same rows, and P^T is staged in natural
+    // order for dQ^T = P^T dU^T, whose contraction positions are the features.
+    __syncthreads();  // the linear phase's reads of sm are done
+    {
+        const bf16* ph = wqh + (size_t)g * (kD / 2) * kD;
+        const bf16* pl = wql + (size_t)g * (kD / 2) * kD;
+        for (int x = tid; x < kC * 16; x += NW * 64) {
+            const int row = x >> 4, piece = x & 15;
+            const size_t src = (size_t)kperm(row) * kD + 8 * piece;
+            st_bf8(ks + row * kKS + 8 * piece, ld_bf8(ph + src));
+            st_bf8(vs + row * kKS + 8 * piece, ld_bf8(pl + src));
+        }
+        // P^T: kt[dim * kVS + f] = P[f][dim] (high part)
+        for (int x = tid; x < 16 * 16; x += NW * 64) {
+            const int kq = x & 15, oct = x >> 4;  // features 4 kq .. +3, dims 8 oct .. +7
+            bf16x8 r4[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) r4[rr] = ld_bf8(ph + (size_t)(4 * kq + rr) * kD + 8 * oct);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16x4 t4;
+                t4[0] = r4[0][e];
+                t4[1] = r4[1][e];
+                t4[2] = r4[2][e];
+                t4[3] = r4[3][e];
+                *reinterpret_cast<bf16x4*>(kt + (8 * oct + e) * kVS + 4 * kq) = t4;
+            }
+        }
+    }
+    // the query row again (read back rather than kept live through the
+    // linear phase)
+    bf16x8 xq[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) xq[st] = ld_bf8(q + qo * kD + 16 * st + 8 * hf);
+    __syncthreads();
+    f32x16 u[2];
+    u[0] = zero16();
+    u[1] = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+            u[ft] = mfma32(ld_bf8(ks + (32 * ft + col) * kKS + 16 * st + 8 * hf), xq[st], u[ft]);
+            u[ft] = mfma32(ld_bf8(vs + (32 * ft + col) * kKS + 16 * st + 8 * hf), xq[st], u[ft]);
+        }
+    float nx = 0.f, nu = 0.f, umax = -__builtin_inff(), umin = __builtin_inff();
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x2 x2 = {xq[st][2 * j], xq[st][2 * j + 1]};
+            nx = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, nx, false);
+        }
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            nu = fmaf(u[ft][vv], u[ft][vv], nu);
+            umax = vmax(umax, u[ft][vv]);
+            umin = vmin(umin, u[ft][vv]);
+        }
+    nx = sqrtf(nx + xor32(nx));
+    nu = sqrtf(nu + xor32(nu));
+    umax = vmax(umax, xor32(umax));
+    umin = vmin(umin, xor32(umin));
+    const float iu = nu > 0.f ? 1.f / nu : 0.f;  // uh = u iu (0 when u = 0)
+    const float scl = nx * iu * kLog2e;           // z log2(e) = scl u
+    float ep[2][16], en[2][16], sp = 0.f, sn = 0.f, sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            ep[ft][vv] = __builtin_amdgcn_exp2f(fmaf(u[ft][vv], scl, -scl * umax));
+            en[ft][vv] = __builtin_amdgcn_exp2f(fmaf(u[ft][vv], -scl, scl * umin));
+            sp += ep[ft][vv];
+            sn += en[ft][vv];
+            sa = fmaf(ep[ft][vv], dfq[ft][vv], sa);
+            sb = fmaf(en[ft][vv], dfq[ft + 2][vv], sb);
+        }
+    sp = 1.f / (sp + xor32(sp));
+    sn = 1.f / (sn + xor32(sn));
+    sa = (sa + xor32(sa)) * sp;
+    sb = (sb + xor32(sb)) * sn;
+    float dnx = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const float z = ep[ft][vv] * sp * (dfq[ft][vv] - sa) - en[ft][vv] * sn * (dfq[ft + 2][vv] - sb);
+            ep[ft][vv] = z;
+            dnx = fmaf(z, u[ft][vv] * iu, dnx);
+        }
+    dnx += xor32(dnx);
+    const float cu = nx * iu;
+    f32x16 dua[2];
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) dua[ft][vv] = cu * (ep[ft][vv] - dnx * u[ft][vv] * iu);
+    // dQ^T += P^T dU^T: the packed du rows are contraction positions = features
+    f32x16 dxt[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dxt[dt] = zero16();
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 pd = pack_acc(dua[ft], s2);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                dxt[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 32 * ft + 16 * s2 + 8 * hf), pd, dxt[dt]);
+        }
+    if (!qvalid) return;
+    const float rn = nx > 0.f ? dnx / nx : 0.f;
+    {
+        float* dr = dq + qo * kD;
+        const bf16* qrow = q + qo * kD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int e = 32 * dt + acc_row(4 * v4, hf);
+                f32x4 a4 = *reinterpret_cast<const f32x4*>(dr + e);
+                const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(qrow + e);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a4[j] += dxt[dt][4 * v4 + j] + rn * (float)x4[j];
+                *reinterpret_cast<f32x4*>(dr + e) = a4;
+            }
+    }
+    // du of row rho = token G + (h - g G) of group g, natural feature order:
+    // four consecutive rows of dua hold four consecutive features
+    {
+        const size_t nrho = (size_t)D.B * D.N * D.G;
+        const size_t rho = ((size_t)b * D.N + tq) * D.G + (h - g * D.G);
+        bf16* dur = du_out + ((size_t)g * nrho + rho) * (kD / 2);
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                bf16x4 d4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d4[j] = (bf16)dua[ft][4 * v4 + j];
+                *reinterpret_cast<bf16x4*>(dur + kperm(32 * ft + acc_row(4 * v4, hf))) = d4;
+            }
     }
 }
 
@@ -1157,7 +1308,7 @@ __global__ __launch_bounds__(256) void dw_mfma_kernel(const bf16* __restrict__ x
 hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,
                          const int* list_off, float* stat, const void* phik16, const LinBufs& L,
-                         const float* gate, void* phiq, float* dq, float* dphiq, float* dgate,
+                         const float* gate, void* phiq, float* dq, void* du, float* dgate,
                          const float* stat_in, const void* out, const void* wsplit, hipStream_t s) {
     const int HB = D.G >= 2 ? 2 : 1;
     const int n = D.Hkv * (kD / 2) * kD;
@@ -1171,7 +1322,8 @@ hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void
                        reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout),   \
                        route, reinterpret_cast<const bf16*>(ksel),                                \
                        reinterpret_cast<const bf16*>(vsel), list_off, stat,                       \
-                       reinterpret_cast<const bf16*>(phik16), L, gate, reinterpret_cast<bf16*>(phiq), dq, dphiq, dgate, \
+                       reinterpret_cast<const bf16*>(phik16), L, gate, reinterpret_cast<bf16*>(phiq), dq,           \
+                       reinterpret_cast<bf16*>(du), dgate,                                            \
                        stat_in, reinterpret_cast<const bf16*>(out), wqh, wql, D)
 #define STILL_DQ(H)                \
     do {                           \

@@ -157,16 +157,18 @@ hipError_t launch_np_bwd(const Dims& D, const void* x, const void* wsplit, int s
 // part [nslice, Hkv, d/2, d] (summed by the reduce kernel)
 hipError_t launch_dw_mfma(const Dims& D, const void* x, int side, const void* du16, float* part,
                           int nslice, hipStream_t s);
-// softmax part of dq (fp32, overwritten), then the gradient w.r.t. the
-// queries' NP-Map features dphiq [B, N, Hq, d'] (fp32, feature order,
-// overwritten) and, with a gate, dgate.  stat_in (with the forward's out):
+// dq (fp32, overwritten): the softmax part, then the linear terms' gradient
+// w.r.t. the queries' NP-Map features carried through the NP-Map backward
+// (P^T du and the norm term), with du (bf16 [Hkv, B N G, d'/2], rows token G
+// + head offset) for the projection gradient, and with a gate dgate.
+// stat_in (with the forward's out):
 // the forward's (m, l, -, c); the kernel then writes stat (with D = dout .
 // out) and phiq (gated features, from the projection split wsplit) itself
 // instead of reading what the first pass wrote there
 hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void* v, const void* dout,
                          const uint8_t* route, const void* ksel, const void* vsel,
                          const int* list_off, float* stat, const void* phik16, const LinBufs& L,
-                         const float* gate, void* phiq, float* dq, float* dphiq, float* dgate,
+                         const float* gate, void* phiq, float* dq, void* du, float* dgate,
                          const float* stat_in, const void* out, const void* wsplit, hipStream_t s);
 
 // ---- decode step ------------------------------------------------------------

@@ -215,7 +215,7 @@ def test_bwd_checks():
     timed = S.lib().still_hybrid_attn_bwd_timed
     n = ct.c_int32(0)
     evs = (ct.c_void_p * 4)()
-    # 16 (general) or 21 (matrix-core) launches need one event more; too few is
+    # up to 16 launches need one event more; too few is
     # rejected before anything runs
     assert timed(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE,
                  FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None, evs, 4, ct.byref(n),
