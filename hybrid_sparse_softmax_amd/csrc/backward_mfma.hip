@@ -518,18 +518,6 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     }
     const bool qvalid = t0 + oq < D.N;
-    if (qvalid) {
-        float* dr = dq + qo * kD;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                f32x4 o4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) o4[j] = D.tau * acc[dt][4 * v4 + j];
-                *reinterpret_cast<f32x4*>(dr + 32 * dt + acc_row(4 * v4, hf)) = o4;
-            }
-    }
 
     // ---- linear terms: dfq^T (rows = feature positions p of the prefix's
     // order, feature kperm(p); column = the lane's query) ----
@@ -748,19 +736,23 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
         for (int vv = 0; vv < 16; ++vv) dua[ft][vv] = cu * (ep[ft][vv] - dnx * u[ft][vv] * iu);
-    // dQ^T += P^T dU^T: the packed du rows are contraction positions = features
-    f32x16 dxt[4];
+    // dQ^T += P^T dU^T / tau into the softmax part's accumulators (dq =
+    // tau acc): the packed du rows are contraction positions = features
+    {
+        const float itau = 1.f / D.tau;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dxt[dt] = zero16();
+        for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-    for (int ft = 0; ft < 2; ++ft)
+            for (int s2 = 0; s2 < 2; ++s2) {
+                f32x16 dsc = dua[ft];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8 pd = pack_acc(dua[ft], s2);
+                for (int vv = 0; vv < 16; ++vv) dsc[vv] *= itau;
+                const bf16x8 pd = pack_acc(dsc, s2);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                dxt[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 32 * ft + 16 * s2 + 8 * hf), pd, dxt[dt]);
-        }
+                for (int dt = 0; dt < 4; ++dt)
+                    acc[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 32 * ft + 16 * s2 + 8 * hf), pd, acc[dt]);
+            }
+    }
     if (!qvalid) return;
     const float rn = nx > 0.f ? dnx / nx : 0.f;
     {
@@ -771,10 +763,10 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int e = 32 * dt + acc_row(4 * v4, hf);
-                f32x4 a4 = *reinterpret_cast<const f32x4*>(dr + e);
                 const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(qrow + e);
+                f32x4 a4;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) a4[j] += dxt[dt][4 * v4 + j] + rn * (float)x4[j];
+                for (int j = 0; j < 4; ++j) a4[j] = D.tau * acc[dt][4 * v4 + j] + rn * (float)x4[j];
                 *reinterpret_cast<f32x4*>(dr + e) = a4;
             }
     }
