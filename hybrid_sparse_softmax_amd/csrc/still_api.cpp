@@ -433,9 +433,10 @@ static int decode(const still_shape* sh, const void* q, const void* k, const voi
 // ---------------------------------------------------------------------------
 static int bwd_slices(const Dims& D, bool mfma) {
     // token slices of the projection-gradient sums: about 2048 blocks in all
-    // (256 on the matrix cores, whose blocks take 64-row tiles)
+    // (512 on the matrix cores, whose blocks take 64-row tiles: 256 leaves the
+    // query side latency-bound, 1024 makes the slice sum cost more than it saves)
     const int64_t ntok = (int64_t)D.B * D.N;
-    int64_t n = ((mfma ? 256 : 2048) + D.Hkv - 1) / D.Hkv;
+    int64_t n = ((mfma ? 512 : 2048) + D.Hkv - 1) / D.Hkv;
     if (n > ntok) n = ntok;
     return n < 1 ? 1 : (int)n;
 }
