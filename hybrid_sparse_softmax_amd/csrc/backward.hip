@@ -1022,8 +1022,8 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 #undef STILL_BWD_QUERY
     if (w.mfma) {
         if ((e = mark.fn(mark.ctx, "bwd_uchunk")) != hipSuccess) return e;
-        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, w.dphik,
-                                    0, s)) != hipSuccess)
+        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, a.k,
+                                    w.wsplit, a.dk, w.duk, 0, s)) != hipSuccess)
             return e;
     } else {
         STILL_STEP("bwd_uchunk",
@@ -1037,8 +1037,8 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
         // linear terms first (dv, dphi_k), then the softmax terms on the matrix
         // cores: window keys (write dk, add to dv), then selected keys (add)
         if ((e = mark.fn(mark.ctx, "bwd_key_la")) != hipSuccess) return e;
-        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, w.dphik,
-                                    1, s)) != hipSuccess)
+        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, a.k,
+                                    w.wsplit, a.dk, w.duk, 1, s)) != hipSuccess)
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_kv_win")) != hipSuccess) return e;
         if ((e = launch_bwd_kv(DT, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw_t, w.list_off,
@@ -1063,11 +1063,9 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     const int ntok = D.B * D.N, half = D.fd / 2;
     const int nw = D.Hkv * half * DD;
     if (w.mfma) {
-        // NP-Map backward of the keys (the queries' ran in the dq kernel) and
         // the projection gradients on the matrix cores (du in bf16 in the du
-        // buffers)
-        if ((e = mark.fn(mark.ctx, "np_vjp_k")) != hipSuccess) return e;
-        if ((e = launch_np_bwd(D, a.k, w.wsplit, 1, w.dphik, a.dk, w.duk, s)) != hipSuccess) return e;
+        // buffers, written by the NP-Map backwards inside the dq and key
+        // linear kernels)
         if ((e = mark.fn(mark.ctx, "dw_q")) != hipSuccess) return e;
         if ((e = launch_dw_mfma(D, a.q, 0, w.duq, w.dwpart, w.nslice, s)) != hipSuccess) return e;
         STILL_STEP("dw_q_reduce", hipLaunchKernelGGL(dw_reduce_kernel, dim3((nw + 255) / 256), dim3(256),

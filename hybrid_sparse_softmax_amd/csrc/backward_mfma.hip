@@ -1,7 +1,8 @@
 // The STILL backward pass on the gfx950 matrix cores (bf16 storage,
-// head_dim 128, chunk 64, window 64 NWT), routing held fixed: every kernel
-// of the matrix-core path but the first pass (the forward's main kernel
-// with statistics, prefill_mfma.hip).
+// head_dim 128, 64-token tiles, window 64 NWT), routing held fixed: every
+// kernel of the matrix-core path but the lists and the first pass (the
+// forward's main kernel with statistics, prefill_mfma.hip; skipped when the
+// forward's statistics are given).
 //
 // Softmax terms.  For a key j and every query t that attends to it by
 // softmax (its window t in [j, j + W - 1], and every later query t >= j + W
@@ -18,15 +19,16 @@
 // 64 products per wave and query tile.  Two launches:
 //   window    keys of chunk c' in position order, query chunks c' .. c'+NWT
 //             (causal in c'; in c'+NWT the window part plus, for a selected
-//             key, the routed part); writes dk and adds to dv (which holds
-//             the linear terms written before)
+//             key, the routed part); adds to dk and dv (which hold the
+//             NP-Map and linear terms written before)
 //   selected  the compact selected rows (positions from the selection),
 //             every query chunk after their window: the visible rows of a
 //             tile are a prefix (rows of chunks <= c - NWT - 1); adds to dk
 //             and dv.
-// The query kernel streams the forward's key tiles for dq, then adds the
-// linear terms of the queries' features (dphi_q, dgate).  The keys' linear
-// terms, the NP-Map backward and the projection gradients follow below.
+// The query kernel streams the forward's key tiles for dq, then forms the
+// gradient of the queries' features (dphi_q, dgate) and carries it through
+// their NP-Map backward into dq.  The keys' linear terms with their NP-Map
+// backward, and the projection gradients, follow below.
 #include "launch.h"
 #include "mfma_common.h"
 #include "mfma_tiles.h"
@@ -180,10 +182,11 @@ __global__ __launch_bounds__(KPB * 128) void bwd_kv_window_kernel(
         for (int v4 = 0; v4 < 4; ++v4) {
             const int e = 32 * dt + acc_row(4 * v4, hf);
             f32x4 a4, b4;
+            const f32x4 k_old = *reinterpret_cast<const f32x4*>(dk + o + e);
             const f32x4 v_old = *reinterpret_cast<const f32x4*>(dv + o + e);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                a4[jj] = D.tau * dka[dt][4 * v4 + jj];
+                a4[jj] = k_old[jj] + D.tau * dka[dt][4 * v4 + jj];
                 b4[jj] = v_old[jj] + dva[dt][4 * v4 + jj];
             }
             *reinterpret_cast<f32x4*>(dk + o + e) = a4;
@@ -897,7 +900,9 @@ template <int NWT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_lin_kernel(
     const bf16* __restrict__ v, const bf16* __restrict__ dout, const bf16* __restrict__ phiq,
     const bf16* __restrict__ phik16, const uint8_t* __restrict__ route, const float* __restrict__ stat,
-    const float* __restrict__ ust, float* __restrict__ dv, float* __restrict__ dphik, Dims D) {
+    const float* __restrict__ ust, float* __restrict__ dv, const bf16* __restrict__ k,
+    const bf16* __restrict__ wkh, const bf16* __restrict__ wkl, float* __restrict__ dk,
+    bf16* __restrict__ du_out, Dims D) {
     const Item it = xcd_item(D.T, D.Hkv);
     const int cj = it.x, g = it.y, b = it.z;
     const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
@@ -1033,201 +1038,167 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
             }
         }
     }
-    if (j >= D.N) return;
-    const size_t o = (((size_t)b * D.N + j) * D.Hkv + g) * kD;
+    // The keys' NP-Map backward follows in the role-0 waves (0, 1), with
+    // dphi_k = their acc (zero for keys with no linear term), as the
+    // queries' in bwd_dq_kernel: the projection's rows staged in the order
+    // of acc's rows (LDS row r = P row kperm(r)), P^T in natural order, by
+    // the whole block before the roles part; it writes dk = P^T du +
+    // (<uh, dz> / ||k||) k (the softmax kernels add their terms afterwards)
+    // and du (bf16, rows = tokens) for the projection gradient.
+    bf16* ks = sm;
+    bf16* vs = sm + kC * kKS;
+    bf16* kt = sm + 2 * kC * kKS;
+    __syncthreads();  // every wave's reads of sm are done
+    {
+        const bf16* ph = wkh + (size_t)g * (kD / 2) * kD;
+        const bf16* pl = wkl + (size_t)g * (kD / 2) * kD;
+        for (int x = tid; x < kC * 16; x += 256) {
+            const int row = x >> 4, piece = x & 15;
+            const size_t src = (size_t)kperm(row) * kD + 8 * piece;
+            st_bf8(ks + row * kKS + 8 * piece, ld_bf8(ph + src));
+            st_bf8(vs + row * kKS + 8 * piece, ld_bf8(pl + src));
+        }
+        for (int x = tid; x < 16 * 16; x += 256) {
+            const int kq = x & 15, oct = x >> 4;
+            bf16x8 r4[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) r4[rr] = ld_bf8(ph + (size_t)(4 * kq + rr) * kD + 8 * oct);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16x4 t4;
+                t4[0] = r4[0][e];
+                t4[1] = r4[1][e];
+                t4[2] = r4[2][e];
+                t4[3] = r4[3][e];
+                *reinterpret_cast<bf16x4*>(kt + (8 * oct + e) * kVS + 4 * kq) = t4;
+            }
+        }
+    }
+    __syncthreads();
+    const size_t o = (((size_t)b * D.N + jr) * D.Hkv + g) * kD;
+    if (role == 1) {
+        if (j >= D.N) return;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int r0 = 32 * t4 + acc_row(4 * v4, hf);
+                f32x4 w4;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) w4[jj] = la ? acc[t4][4 * v4 + jj] : 0.f;
+                *reinterpret_cast<f32x4*>(dv + o + r0) = w4;
+            }
+        return;
+    }
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-            const int r0 = 32 * t4 + acc_row(4 * v4, hf);
-            f32x4 w4;
+        for (int vv = 0; vv < 16; ++vv) acc[t4][vv] = la ? acc[t4][vv] : 0.f;
+    bf16x8 xk[8];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) w4[jj] = la ? acc[t4][4 * v4 + jj] : 0.f;
-            if (role == 0) *reinterpret_cast<f32x4*>(dphik + o + kperm(r0)) = w4;
-            else *reinterpret_cast<f32x4*>(dv + o + r0) = w4;
+    for (int st = 0; st < 8; ++st) xk[st] = ld_bf8(k + o + 16 * st + 8 * hf);
+    f32x16 u[2];
+    u[0] = zero16();
+    u[1] = zero16();
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+            u[ft] = mfma32(ld_bf8(ks + (32 * ft + col) * kKS + 16 * st + 8 * hf), xk[st], u[ft]);
+            u[ft] = mfma32(ld_bf8(vs + (32 * ft + col) * kKS + 16 * st + 8 * hf), xk[st], u[ft]);
+        }
+    float nx = 0.f, nu = 0.f, umax = -__builtin_inff(), umin = __builtin_inff();
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const bf16x2 x2 = {xk[st][2 * jj], xk[st][2 * jj + 1]};
+            nx = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, nx, false);
+        }
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            nu = fmaf(u[ft][vv], u[ft][vv], nu);
+            umax = vmax(umax, u[ft][vv]);
+            umin = vmin(umin, u[ft][vv]);
+        }
+    nx = sqrtf(nx + xor32(nx));
+    nu = sqrtf(nu + xor32(nu));
+    umax = vmax(umax, xor32(umax));
+    umin = vmin(umin, xor32(umin));
+    const float iu = nu > 0.f ? 1.f / nu : 0.f;
+    const float scl = nx * iu * kLog2e;
+    float ep[2][16], en[2][16], sp = 0.f, sn = 0.f, sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            ep[ft][vv] = __builtin_amdgcn_exp2f(fmaf(u[ft][vv], scl, -scl * umax));
+            en[ft][vv] = __builtin_amdgcn_exp2f(fmaf(u[ft][vv], -scl, scl * umin));
+            sp += ep[ft][vv];
+            sn += en[ft][vv];
+            sa = fmaf(ep[ft][vv], acc[ft][vv], sa);
+            sb = fmaf(en[ft][vv], acc[ft + 2][vv], sb);
+        }
+    sp = 1.f / (sp + xor32(sp));
+    sn = 1.f / (sn + xor32(sn));
+    sa = (sa + xor32(sa)) * sp;
+    sb = (sb + xor32(sb)) * sn;
+    float dnx = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            const float z = ep[ft][vv] * sp * (acc[ft][vv] - sa) - en[ft][vv] * sn * (acc[ft + 2][vv] - sb);
+            ep[ft][vv] = z;
+            dnx = fmaf(z, u[ft][vv] * iu, dnx);
+        }
+    dnx += xor32(dnx);
+    const float cu = nx * iu;
+    f32x16 dua[2];
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) dua[ft][vv] = cu * (ep[ft][vv] - dnx * u[ft][vv] * iu);
+    f32x16 dxt[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dxt[dt] = zero16();
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 pd = pack_acc(dua[ft], s2);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                dxt[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 32 * ft + 16 * s2 + 8 * hf), pd, dxt[dt]);
+        }
+    if (j >= D.N) return;
+    const float rn = nx > 0.f ? dnx / nx : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int e = 32 * dt + acc_row(4 * v4, hf);
+            const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(k + o + e);
+            f32x4 a4;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) a4[jj] = dxt[dt][4 * v4 + jj] + rn * (float)x4[jj];
+            *reinterpret_cast<f32x4*>(dk + o + e) = a4;
+        }
+    bf16* dur = du_out + ((size_t)g * D.B * D.N + (size_t)b * D.N + j) * (kD / 2);
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            bf16x4 d4;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) d4[jj] = (bf16)dua[ft][4 * v4 + jj];
+            *reinterpret_cast<bf16x4*>(dur + kperm(32 * ft + acc_row(4 * v4, hf))) = d4;
         }
 }
 
 // ---------------------------------------------------------------------------
-// NP-Map backward on the matrix cores.  The feature map of a row x (a query
-// or key head; full text Sec. 3.2) with its head group's projection P
-// (d/2 x d):  u = P x,  z = ||x|| u / ||u||,  phi = [softmax(z); softmax(-z)].
-// Given dphi (the gradient w.r.t. the ungated phi):
-//   dz = phi+ (dphi+ - <phi+, dphi+>) - phi- (dphi- - <phi-, dphi->)
-//   du = ||x|| (dz - uh <uh, dz>) / ||u||   (uh = u / ||u||)
-//   dx += P^T du + (<uh, dz> / ||x||) x,    dP += du x^T.
-// Rows of KV group g are rho = tok * hpp + hh (x row tok * H + g * hpp +
-// hh).  One wave takes 32 rows at a time: U^T = P X^T on the matrix cores
-// with P as bf16 high + low parts (fp32-grade u, as the forward's map), the
-// feature softmaxes and sums along the accumulator columns, dX^T = P^T dU^T
-// (bf16 P and du), dx updated in place; du goes out as bf16 for the
-// projection gradient.
-// ---------------------------------------------------------------------------
-constexpr int kNPW = 4;  // waves per block
-constexpr int kNPT = 4;  // 32-row tiles per wave
-
-__global__ __launch_bounds__(kNPW * 64) __attribute__((amdgpu_waves_per_eu(2))) void np_bwd_kernel(
-    const bf16* __restrict__ x, const bf16* __restrict__ phi_hi, const bf16* __restrict__ phi_lo,
-    const float* __restrict__ dphi, float* __restrict__ dx, bf16* __restrict__ du_out, int ntok,
-    int H, int hpp) {
-    constexpr int kF = kD / 2;  // 64 features per sign
-    const int g = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __shared__ __align__(16) bf16 ph[kF * kKS];
-    __shared__ __align__(16) bf16 pl[kF * kKS];
-    __shared__ __align__(16) bf16 pt[kD * kVS];  // P^T, features in kperm order
-    const size_t po = (size_t)g * kF * kD;
-    load_k_tile(phi_hi + po, kD, kF, ph, tid, kNPW * 64);
-    load_k_tile(phi_lo + po, kD, kF, pl, tid, kNPW * 64);
-    load_vt_tile(phi_hi + po, kD, kF, pt, tid, kNPW * 64);
-    __syncthreads();
-    const int nrho = ntok * hpp;
-#pragma unroll 1
-    for (int tt = 0; tt < kNPT; ++tt) {
-        // the projection fragments are read from LDS in every tile rather
-        // than held in registers across tiles
-        __asm__ volatile("" ::: "memory");
-        const int rho0 = ((blockIdx.x * kNPW + wave) * kNPT + tt) * 32;
-        if (rho0 >= nrho) break;  // wave-uniform
-        const bool act = rho0 + col < nrho;
-        const int rho = min(rho0 + col, nrho - 1);
-        const size_t xr = (size_t)(rho / hpp) * H + (size_t)g * hpp + rho % hpp;
-        bf16x8 xb[8];
-#pragma unroll
-        for (int st = 0; st < 8; ++st) xb[st] = ld_bf8(x + xr * kD + 16 * st + 8 * hf);
-        f32x16 u[2];
-        u[0] = zero16();
-        u[1] = zero16();
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-#pragma unroll
-            for (int ft = 0; ft < 2; ++ft) {
-                u[ft] = mfma32(ld_bf8(ph + (32 * ft + col) * kKS + 16 * st + 8 * hf), xb[st], u[ft]);
-                u[ft] = mfma32(ld_bf8(pl + (32 * ft + col) * kKS + 16 * st + 8 * hf), xb[st], u[ft]);
-            }
-        // column sums over the row's 64 features: this lane's 32 plus the other half's
-        float nx = 0.f, nu = 0.f, umax = -__builtin_inff(), umin = __builtin_inff();
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x2 x2 = {xb[st][2 * j], xb[st][2 * j + 1]};
-                nx = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, nx, false);
-            }
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) {
-                nu = fmaf(u[ft][vv], u[ft][vv], nu);
-                umax = vmax(umax, u[ft][vv]);
-                umin = vmin(umin, u[ft][vv]);
-            }
-        nx = sqrtf(nx + xor32(nx));
-        nu = sqrtf(nu + xor32(nu));
-        umax = vmax(umax, xor32(umax));
-        umin = vmin(umin, xor32(umin));
-        const float iu = nu > 0.f ? 1.f / nu : 0.f;  // uh = u iu (0 when u = 0)
-        const float scl = nx * iu * kLog2e;           // z log2(e) = scl u
-        float ep[2][16], en[2][16], sp = 0.f, sn = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) {
-                ep[ft][vv] = __builtin_amdgcn_exp2f(fmaf(u[ft][vv], scl, -scl * umax));
-                en[ft][vv] = __builtin_amdgcn_exp2f(fmaf(u[ft][vv], -scl, scl * umin));
-                sp += ep[ft][vv];
-                sn += en[ft][vv];
-            }
-        // dphi of the row (feature order: 64 of softmax(z), then 64 of
-        // softmax(-z)); <phi+-, dphi+-> from the unnormalised weights, then
-        // dz with dphi read again (cache hits) to keep registers low
-        const float* dr = dphi + xr * kD;
-        float sa = 0.f, sb = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                const int f = 32 * ft + acc_row(4 * v4, hf);
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(dr + f);
-                const f32x4 b4 = *reinterpret_cast<const f32x4*>(dr + kF + f);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sa = fmaf(ep[ft][4 * v4 + j], a4[j], sa);
-                    sb = fmaf(en[ft][4 * v4 + j], b4[j], sb);
-                }
-            }
-        sp = 1.f / (sp + xor32(sp));
-        sn = 1.f / (sn + xor32(sn));
-        sa = (sa + xor32(sa)) * sp;
-        sb = (sb + xor32(sb)) * sn;
-        // dz (in ep), then <uh, dz>
-        float dnx = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                const int f = 32 * ft + acc_row(4 * v4, hf);
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(dr + f);
-                const f32x4 b4 = *reinterpret_cast<const f32x4*>(dr + kF + f);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int vv = 4 * v4 + j;
-                    const float z = ep[ft][vv] * sp * (a4[j] - sa) - en[ft][vv] * sn * (b4[j] - sb);
-                    ep[ft][vv] = z;
-                    dnx = fmaf(z, u[ft][vv] * iu, dnx);
-                }
-            }
-        dnx += xor32(dnx);
-        float (&dz)[2][16] = ep;
-        // du = ||x|| (dz - uh <uh, dz>) / ||u||
-        f32x16 dua[2];
-        const float cu = nx * iu;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) dua[ft][vv] = cu * (dz[ft][vv] - dnx * u[ft][vv] * iu);
-        // dX^T = P^T dU^T (rows: dims 32 dt + acc_row, column: the row rho)
-        f32x16 dxt[4];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) dxt[dt] = zero16();
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const bf16x8 pd = pack_acc(dua[ft], s2);
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-                    dxt[dt] = mfma32(ld_bf8(pt + (32 * dt + col) * kVS + 32 * ft + 16 * s2 + 8 * hf), pd, dxt[dt]);
-            }
-        if (!act) continue;
-        const float rn = nx > 0.f ? dnx / nx : 0.f;
-        float* dxr = dx + xr * kD;
-        const bf16* xrow = x + xr * kD;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                const int e = 32 * dt + acc_row(4 * v4, hf);
-                f32x4 a4 = *reinterpret_cast<const f32x4*>(dxr + e);
-                const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(xrow + e);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) a4[j] += dxt[dt][4 * v4 + j] + rn * (float)x4[j];
-                *reinterpret_cast<f32x4*>(dxr + e) = a4;
-            }
-        bf16* dur = du_out + ((size_t)g * nrho + rho) * kF;
-#pragma unroll
-        for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                bf16x4 d4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) d4[j] = (bf16)dua[ft][4 * v4 + j];
-                *reinterpret_cast<bf16x4*>(dur + 32 * ft + acc_row(4 * v4, hf)) = d4;
-            }
-    }
-}
-
 // Projection gradient dP[g] = sum over the rows rho of group g of du x^T,
 // partial over one slice of rows per block: 64-row tiles of dU and X staged
 // transposed (rows as the contraction index), each wave one 32-feature by
@@ -1335,7 +1306,8 @@ hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void
 
 hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const void* phiq,
                               const void* phik16, const uint8_t* route, const float* stat, float* ust,
-                              float* dv, float* dphik, int phase, hipStream_t s) {
+                              float* dv, const void* k, const void* wsplit, float* dk, void* du16,
+                              int phase, hipStream_t s) {
     if (phase == 0) {
         hipLaunchKernelGGL(bwd_uchunk_mfma_kernel, dim3(D.T, D.Hkv, D.B), dim3(256), 0, s,
                            reinterpret_cast<const bf16*>(phiq), reinterpret_cast<const bf16*>(dout), stat, ust,
@@ -1344,11 +1316,14 @@ hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, co
     }
     const unsigned nblk = (unsigned)D.T * D.Hkv * D.B;
     const int nwt = D.W / kC;
+    const size_t part = (size_t)D.Hkv * (kD / 2) * kD;
+    const bf16* wkh = reinterpret_cast<const bf16*>(wsplit) + 2 * part;  // [wq hi, wq lo, wk hi, wk lo]
 #define STILL_KL(NWT)                                                                            \
     hipLaunchKernelGGL((bwd_key_lin_kernel<NWT>), dim3(nblk), dim3(256), 0, s,                  \
                        reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout),   \
                        reinterpret_cast<const bf16*>(phiq), reinterpret_cast<const bf16*>(phik16), route, \
-                       stat, ust, dv, dphik, D)
+                       stat, ust, dv, reinterpret_cast<const bf16*>(k), wkh, wkh + part, dk,          \
+                       reinterpret_cast<bf16*>(du16), D)
     if (nwt == 1) STILL_KL(1);
     else if (nwt == 2) STILL_KL(2);
     else STILL_KL(4);
@@ -1399,20 +1374,6 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
 
 // NP-Map backward of one side (q: H = Hq, hpp = G, projection parts 0 / 1;
 // k: H = Hkv, hpp = 1, parts 2 / 3 of wsplit) and its projection gradient
-hipError_t launch_np_bwd(const Dims& D, const void* x, const void* wsplit, int side, const float* dphi,
-                         float* dx, void* du16, hipStream_t s) {
-    const int H = side == 0 ? D.Hq : D.Hkv, hpp = side == 0 ? D.G : 1;
-    const size_t part = (size_t)D.Hkv * (kD / 2) * kD;
-    const bf16* ws = reinterpret_cast<const bf16*>(wsplit) + (size_t)(2 * side) * part;
-    const int ntok = D.B * D.N;
-    const int rows_per_blk = kNPW * kNPT * 32;
-    const unsigned nblk = (unsigned)((ntok * hpp + rows_per_blk - 1) / rows_per_blk);
-    hipLaunchKernelGGL(np_bwd_kernel, dim3(nblk, D.Hkv), dim3(kNPW * 64), 0, s,
-                       reinterpret_cast<const bf16*>(x), ws, ws + part, dphi, dx,
-                       reinterpret_cast<bf16*>(du16), ntok, H, hpp);
-    return hipGetLastError();
-}
-
 hipError_t launch_dw_mfma(const Dims& D, const void* x, int side, const void* du16, float* part,
                           int nslice, hipStream_t s) {
     const int H = side == 0 ? D.Hq : D.Hkv, hpp = side == 0 ? D.G : 1;

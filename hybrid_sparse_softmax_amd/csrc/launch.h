@@ -133,7 +133,7 @@ hipError_t launch_hybrid_stats(const Dims& D, const void* q, const void* k, cons
                                const void* ksel, const void* vsel, const LinBufs& L,
                                const float* gate, const int* list_off, const void* dout,
                                float* stat, void* phiq, hipStream_t s);
-// softmax part of dk and dv: phase 0 the window keys (dk written, dv added
+// softmax part of dk and dv: phase 0 the window keys (dk and dv added
 // to), phase 1 the selected keys over the compact rows (both added to; part:
 // bwd_kv_part_floats(D) floats of segment sums, then merged)
 size_t bwd_kv_part_floats(const Dims& D);
@@ -143,16 +143,14 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
                          float* dv, float* part, int phase, hipStream_t s);
 // linear terms of the keys on the matrix cores: phase 0 the chunk sums
 // ust [B, Hkv, T, d' (d + 1)] (fp32, [i][e] then u; the suffix kernel turns
-// them into suffix sums), phase 1 dv (written: the linear part) and dphik
-// [B, N, Hkv, d'] (fp32, feature order, written) from the suffix sums
+// them into suffix sums), phase 1 dv (written: the linear part) and, through
+// the keys' NP-Map backward (projections from wsplit), dk (written: the
+// NP-Map part; the softmax kernels add theirs) and du16 (bf16 [Hkv, B N,
+// d'/2]) for the projection gradient
 hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const void* phiq,
                               const void* phik16, const uint8_t* route, const float* stat, float* ust,
-                              float* dv, float* dphik, int phase, hipStream_t s);
-// NP-Map backward of one side (0: queries, 1: keys) on the matrix cores:
-// dx += the map's vector-Jacobian product of dphi; du16 receives du (bf16,
-// [Hkv][rows of the group][d/2]) for the projection gradient
-hipError_t launch_np_bwd(const Dims& D, const void* x, const void* wsplit, int side, const float* dphi,
-                         float* dx, void* du16, hipStream_t s);
+                              float* dv, const void* k, const void* wsplit, float* dk, void* du16,
+                              int phase, hipStream_t s);
 // partial projection gradients of one side over nslice row slices:
 // part [nslice, Hkv, d/2, d] (summed by the reduce kernel)
 hipError_t launch_dw_mfma(const Dims& D, const void* x, int side, const void* du16, float* part,
