@@ -347,9 +347,10 @@ def backward_flops(cfg: dict, sel_idx: np.ndarray) -> dict:
     on the matrix cores, whose first pass has the normaliser; 4d + 4d' in the
     fp32 kernel; key side 4d + 4d'); NP-Map backward 2 d' d and its
     projection gradient d' d per token-head.  On the matrix cores the dq
-    kernel also runs the queries' NP-Map backward (no np_vjp_q launch); its
-    recomputation of u = P q is not counted, nor, when it starts from the
-    forward's statistics (no first pass), its NP-Map of the queries."""
+    kernel also runs the queries' NP-Map backward and the key linear kernel
+    the keys' (no np_vjp launches); their recomputation of u = P x is not
+    counted, nor, when the dq kernel starts from the forward's statistics
+    (no first pass), its NP-Map of the queries."""
     B, N, Hq, Hkv = cfg["batch"], cfg["seqlen"], cfg["n_q_heads"], cfg["n_kv_heads"]
     d = fd = cfg["head_dim"]
     W, C = cfg["window"], cfg["chunk"]
@@ -387,7 +388,7 @@ def backward_flops(cfg: dict, sel_idx: np.ndarray) -> dict:
         bwd_dq=6.0 * d * sa + 2.0 * fd * d * tok_q + (2.0 * d + 2.0 * fd) * q_part + 2.0 * fd * d * tok_q,
         bwd_kv_win=8.0 * d * win_pairs,
         bwd_kv_sel=8.0 * d * sel_pairs,
-        bwd_key_la=lin_k,
+        bwd_key_la=lin_k + 2.0 * fd * d * tok_k,
         # general path
         bwd_query=6.0 * d * sa + lin_q,
         bwd_key_win=8.0 * d * win_pairs + lin_k,
@@ -406,7 +407,7 @@ def backward_flops(cfg: dict, sel_idx: np.ndarray) -> dict:
 
 
 MFMA_KERNELS = {"bwd_stats", "bwd_dq", "bwd_kv_win", "bwd_kv_sel", "bwd_uchunk", "bwd_key_la",
-                "np_vjp_k", "dw_q", "dw_k"}
+                "dw_q", "dw_k"}
 
 
 def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
