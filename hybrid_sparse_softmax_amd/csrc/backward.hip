@@ -445,15 +445,33 @@ __global__ __launch_bounds__(256) void bwd_uchunk_kernel(const float* __restrict
     if (tid < DD) out[E + tid] = uacc;
 }
 
-__global__ __launch_bounds__(256) void bwd_suffix_kernel(float* __restrict__ ust, Dims D) {
-    const int E1 = D.fd * (D.d + 1);
+// ust16 (matrix-core path, else nullptr): the U part (e < fd d) of each
+// suffix goes there in bf16, [B, Hkv, T, fd d], the operand precision of the
+// key kernel that reads it; u stays in place in fp32.
+__global__ __launch_bounds__(256) void bwd_suffix_kernel(float* __restrict__ ust, __bf16* __restrict__ ust16,
+                                                         Dims D) {
+    const int E1 = D.fd * (D.d + 1), EU = D.fd * D.d;
     const int e = blockIdx.x * 256 + threadIdx.x, g = blockIdx.y, b = blockIdx.z;
     if (e >= E1) return;
-    float* base = ust + ((size_t)b * D.Hkv + g) * D.T * (size_t)E1 + e;
+    const size_t bgT = ((size_t)b * D.Hkv + g) * D.T;
+    float* base = ust + bgT * (size_t)E1 + e;
+    __bf16* b16 = ust16 && e < EU ? ust16 + bgT * (size_t)EU + e : nullptr;
     float run = 0.f;
-    for (int c = D.T - 1; c >= 0; --c) {
-        run += base[(size_t)c * E1];
-        base[(size_t)c * E1] = run;
+    // chunks from the last down, eight loads in flight at a time
+    constexpr int kB = 8;
+    for (int c1 = D.T; c1 > 0; c1 -= kB) {
+        const int n = min(kB, c1);
+        float x[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) x[i] = i < n ? base[(size_t)(c1 - 1 - i) * E1] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            if (i >= n) break;
+            run += x[i];
+            const size_t c = (size_t)(c1 - 1 - i);
+            if (b16) b16[c * EU] = (__bf16)run;
+            else base[c * E1] = run;
+        }
     }
 }
 
@@ -933,8 +951,16 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict_
                                                         float* __restrict__ dw, int n, int nslice) {
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= n) return;
+    // slices in order, eight loads in flight at a time
+    constexpr int kB = 8;
     float s = 0.f;
-    for (int sl = 0; sl < nslice; ++sl) s += part[(size_t)sl * n + e];
+    for (int s0 = 0; s0 < nslice; s0 += kB) {
+        float x[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) x[i] = s0 + i < nslice ? part[(size_t)(s0 + i) * n + e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kB; ++i) s += x[i];
+    }
     dw[e] = s;
 }
 
@@ -1022,8 +1048,8 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
 #undef STILL_BWD_QUERY
     if (w.mfma) {
         if ((e = mark.fn(mark.ctx, "bwd_uchunk")) != hipSuccess) return e;
-        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, a.k,
-                                    w.wsplit, a.dk, w.duk, 0, s)) != hipSuccess)
+        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, w.ust16, a.dv,
+                                    a.k, w.wsplit, a.dk, w.duk, 0, s)) != hipSuccess)
             return e;
     } else {
         STILL_STEP("bwd_uchunk",
@@ -1032,13 +1058,14 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
     }
     STILL_STEP("bwd_suffix",
                hipLaunchKernelGGL(bwd_suffix_kernel, dim3((D.fd * (D.d + 1) + 255) / 256, D.Hkv, D.B),
-                                  dim3(256), 0, s, w.ust, w.mfma ? DT : D));
+                                  dim3(256), 0, s, w.ust, reinterpret_cast<__bf16*>(w.ust16),
+                                  w.mfma ? DT : D));
     if (w.mfma) {
         // linear terms first (dv, dphi_k), then the softmax terms on the matrix
         // cores: window keys (write dk, add to dv), then selected keys (add)
         if ((e = mark.fn(mark.ctx, "bwd_key_la")) != hipSuccess) return e;
-        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, a.dv, a.k,
-                                    w.wsplit, a.dk, w.duk, 1, s)) != hipSuccess)
+        if ((e = launch_bwd_key_lin(DT, a.v, a.dout, w.phiq, w.phik16, w.route, w.stat, w.ust, w.ust16, a.dv,
+                                    a.k, w.wsplit, a.dk, w.duk, 1, s)) != hipSuccess)
             return e;
         if ((e = mark.fn(mark.ctx, "bwd_kv_win")) != hipSuccess) return e;
         if ((e = launch_bwd_kv(DT, a.q, a.k, a.v, a.dout, w.route, w.ksel, w.vsel, w.selw_t, w.list_off,

@@ -900,7 +900,8 @@ template <int NWT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_lin_kernel(
     const bf16* __restrict__ v, const bf16* __restrict__ dout, const bf16* __restrict__ phiq,
     const bf16* __restrict__ phik16, const uint8_t* __restrict__ route, const float* __restrict__ stat,
-    const float* __restrict__ ust, float* __restrict__ dv, const bf16* __restrict__ k,
+    const float* __restrict__ ust, const bf16* __restrict__ ust16, float* __restrict__ dv,
+    const bf16* __restrict__ k,
     const bf16* __restrict__ wkh, const bf16* __restrict__ wkl, float* __restrict__ dk,
     bf16* __restrict__ du_out, Dims D) {
     const Item it = xcd_item(D.T, D.Hkv);
@@ -925,20 +926,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) acc[t4] = zero16();
     if (has_q && c0 + 1 < D.T) {
-        const float* U = ust + (bg * D.T + c0 + 1) * (size_t)(kD * (kD + 1));
+        const float* U = ust + (bg * D.T + c0 + 1) * (size_t)(kD * (kD + 1));  // its u
+        const bf16* U16 = ust16 + (bg * D.T + c0 + 1) * (size_t)(kD * kD);     // its U, bf16
         bf16* ub = sm;              // [p][e], kKS
         bf16* ut = sm + kD * kKS;   // [e][p], kKS
         for (int x = tid; x < kD * 16; x += 256) {
             const int pp = x >> 4, oct = x & 15;
             const int f = kperm(pp);
-            const f32x4 a = *reinterpret_cast<const f32x4*>(U + (size_t)f * kD + 8 * oct);
-            const f32x4 c = *reinterpret_cast<const f32x4*>(U + (size_t)f * kD + 8 * oct + 4);
-            bf16x8 r;
-#pragma unroll
-            for (int l = 0; l < 4; ++l) {
-                r[l] = (bf16)a[l];
-                r[4 + l] = (bf16)c[l];
-            }
+            const bf16x8 r = ld_bf8(U16 + (size_t)f * kD + 8 * oct);
             st_bf8(ub + pp * kKS + 8 * oct, r);
 #pragma unroll
             for (int e = 0; e < 8; ++e) ut[(8 * oct + e) * kKS + pp] = r[e];
@@ -1306,8 +1301,8 @@ hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void
 
 hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const void* phiq,
                               const void* phik16, const uint8_t* route, const float* stat, float* ust,
-                              float* dv, const void* k, const void* wsplit, float* dk, void* du16,
-                              int phase, hipStream_t s) {
+                              const void* ust16, float* dv, const void* k, const void* wsplit, float* dk,
+                              void* du16, int phase, hipStream_t s) {
     if (phase == 0) {
         hipLaunchKernelGGL(bwd_uchunk_mfma_kernel, dim3(D.T, D.Hkv, D.B), dim3(256), 0, s,
                            reinterpret_cast<const bf16*>(phiq), reinterpret_cast<const bf16*>(dout), stat, ust,
@@ -1322,7 +1317,8 @@ hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, co
     hipLaunchKernelGGL((bwd_key_lin_kernel<NWT>), dim3(nblk), dim3(256), 0, s,                  \
                        reinterpret_cast<const bf16*>(v), reinterpret_cast<const bf16*>(dout),   \
                        reinterpret_cast<const bf16*>(phiq), reinterpret_cast<const bf16*>(phik16), route, \
-                       stat, ust, dv, reinterpret_cast<const bf16*>(k), wkh, wkh + part, dk,          \
+                       stat, ust, reinterpret_cast<const bf16*>(ust16), dv,                         \
+                       reinterpret_cast<const bf16*>(k), wkh, wkh + part, dk,                         \
                        reinterpret_cast<bf16*>(du16), D)
     if (nwt == 1) STILL_KL(1);
     else if (nwt == 2) STILL_KL(2);

@@ -143,14 +143,14 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
                          float* dv, float* part, int phase, hipStream_t s);
 // linear terms of the keys on the matrix cores: phase 0 the chunk sums
 // ust [B, Hkv, T, d' (d + 1)] (fp32, [i][e] then u; the suffix kernel turns
-// them into suffix sums), phase 1 dv (written: the linear part) and, through
+// them into suffix sums, U in bf16 in ust16), phase 1 dv (written: the linear part) and, through
 // the keys' NP-Map backward (projections from wsplit), dk (written: the
 // NP-Map part; the softmax kernels add theirs) and du16 (bf16 [Hkv, B N,
 // d'/2]) for the projection gradient
 hipError_t launch_bwd_key_lin(const Dims& D, const void* v, const void* dout, const void* phiq,
                               const void* phik16, const uint8_t* route, const float* stat, float* ust,
-                              float* dv, const void* k, const void* wsplit, float* dk, void* du16,
-                              int phase, hipStream_t s);
+                              const void* ust16, float* dv, const void* k, const void* wsplit, float* dk,
+                              void* du16, int phase, hipStream_t s);
 // partial projection gradients of one side over nslice row slices:
 // part [nslice, Hkv, d/2, d] (summed by the reduce kernel)
 hipError_t launch_dw_mfma(const Dims& D, const void* x, int side, const void* du16, float* part,
@@ -214,6 +214,7 @@ struct BwdWork {
     float* stat;          // [B, N, Hq, 4] m, l, D_t, exp(-m) / l
     float *dphiq, *dphik; // [B, N, Hq | Hkv, fd]
     float* ust;           // [B, Hkv, T, fd (d + 1)] suffix sums of c phi_q dout^T, c D phi_q
+    void* ust16;          // matrix-core path: the U part of the suffix sums in bf16 [B, Hkv, T, fd d]
     float *duq, *duk;     // [B, N, Hq | Hkv, fd / 2]
     float* dwpart;        // [nslice, Hkv, fd / 2, d]
     uint8_t* route;       // [B, Hkv, N]

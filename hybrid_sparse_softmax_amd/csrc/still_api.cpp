@@ -473,6 +473,7 @@ static BwdWork carve_bwd(const Dims& D, Carver& cv, bool mfma) {
     w.mfma = mfma;
     w.ksel = w.vsel = w.phik16 = w.wsplit = nullptr;
     w.kvpart = nullptr;
+    w.ust16 = nullptr;
     w.list_off = nullptr;
     w.lin16 = LinBufs{};
     if (mfma) {
@@ -490,6 +491,7 @@ static BwdWork carve_bwd(const Dims& D, Carver& cv, bool mfma) {
         w.lin16.gz = cv.take<float>(BG * ngroups * (size_t)D.fd);
         w.wsplit = cv.take<uint16_t>((size_t)4 * D.Hkv * (D.fd / 2) * D.d);
         w.kvpart = cv.take<float>(bwd_kv_part_floats(DT));
+        w.ust16 = cv.take<uint16_t>(BG * DT.T * (size_t)D.fd * D.d);
     }
     return w;
 }
