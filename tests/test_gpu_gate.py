@@ -161,10 +161,14 @@ BWD_CASES = {
 
 @pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
 @pytest.mark.parametrize("name", list(BWD_CASES))
-def test_gated_bwd_matches_oracle(gpu_lib, name, general):
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "from_fwd_stats"])
+def test_gated_bwd_matches_oracle(gpu_lib, name, general, saved):
+    """saved: the backward starts from the gated forward's output and
+    statistics (the gate weight enters the features the dq kernel forms and
+    the linear weight c the forward wrote)."""
     from test_gpu_backward import grad_tol
     cfg, seed = BWD_CASES[name]
-    say(f"[gate bwd] case={name} general={general} shape={workloads.shape_of(cfg)} seed={seed}")
+    say(f"[gate bwd] case={name} general={general} saved={saved} shape={workloads.shape_of(cfg)} seed={seed}")
     raw = workloads.make_prefill(cfg, seed)
     dt = torch_dtype(cfg["dtype"])
     dev, ref = prepare(raw, dt)
@@ -173,11 +177,13 @@ def test_gated_bwd_matches_oracle(gpu_lib, name, general):
     dout = torch.from_numpy(workloads.make_grad_out(cfg, seed)).to(dt)
     W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
     sel = None
+    fw = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W, chunk=C,
+                     topk=lam, return_sel=min(lam, C) > 0, return_stats=saved, gate=gd)
     if min(lam, C) > 0:
-        sel = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W, chunk=C,
-                          topk=lam, return_sel=True, gate=gd)["sel_idx"]
+        sel = fw["sel_idx"]
+    extra = dict(out=fw["out"], stats=fw["stats"]) if saved else {}
     g = gpu_lib.bwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], sel, dout.cuda(),
-                    window=W, chunk=C, topk=lam, gate=gd, general=general)
+                    window=W, chunk=C, topk=lam, gate=gd, general=general, **extra)
     torch.cuda.synchronize()
     p = O.Params(window=W, chunk=C, topk=lam)
     o = O.bwd_direct(ref["q"], ref["k"], ref["v"], ref["wphi_q"], ref["wphi_k"], dout.double().numpy(),
