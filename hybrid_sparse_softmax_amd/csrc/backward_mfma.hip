@@ -385,11 +385,50 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const int tla = t0 - NWT * kC;
     const size_t ldkv = (size_t)D.Hkv * kD;
 
-    // K, V (row-major) and K^T tiles; the linear phase reuses the same bytes
-    __shared__ __align__(16) bf16 sm[2 * kC * kKS + kD * kVS];
-    bf16* ks = sm;
-    bf16* vs = sm + kC * kKS;
-    bf16* kt = sm + 2 * kC * kKS;
+    // Key tiles go straight into LDS (global_load_lds), double buffered:
+    // tile i+1 lands while tile i is computed.  Buffer j holds the K rows and
+    // the V rows in the padded K-tile layout (row reads for the logits and
+    // dout . v) and the K rows again in the swizzled V-tile layout (the
+    // transposed reads of dQ^T += K^T dS^T).  The phases after the loop reuse
+    // the front bytes as ks, vs and kt.
+    __shared__ __align__(16) bf16 smem[4 * kKTile + 2 * kVTile];
+    const unsigned lds0 = (unsigned)(size_t)(lds_void*)smem;
+    bf16* ks = smem;
+    bf16* vs = smem + kC * kKS;
+    bf16* kt = smem + 2 * kC * kKS;
+    auto kpb = [&](int j) { return smem + j * kKTile; };
+    auto vpb = [&](int j) { return smem + (2 + j) * kKTile; };
+    auto ktb = [&](int j) { return smem + 4 * kKTile + j * kVTile; };
+    // rows of tile i: a window chunk from k / v, or compact rows; every tile
+    // has nv >= 1 valid rows, and rows past nv repeat row nv - 1 (masked)
+    auto stage = [&](int i) {
+        const bf16 *srck, *srcv;
+        int nv;
+        if (i <= NWT) {
+            const int tc = c - NWT + i;
+            nv = min(kC, D.N - tc * kC);
+            const size_t off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
+            srck = k + off;
+            srcv = v + off;
+        } else {
+            const int r0 = (i - NWT - 1) * kC;
+            nv = min(kC, nrows - r0);
+            const size_t off = ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD + (size_t)r0 * ldkv;
+            srck = ksel + off;
+            srcv = vsel + off;
+        }
+        const unsigned j = (unsigned)((i - first) & 1);
+        const unsigned kd = lds0 + 2u * j * kKTile, vd = lds0 + 2u * (2 + j) * kKTile;
+        const unsigned td = lds0 + 2u * (4 * kKTile + j * kVTile);
+        for (int x = wave; x < kKPieces; x += NW) {
+            stage_k_piece_u(x, srck, (int)ldkv, nv, kd);
+            stage_k_piece_u(x, srcv, (int)ldkv, nv, vd);
+        }
+        for (int x = wave; x < kVPieces; x += NW) stage_v_piece_u(x, srck, (int)ldkv, nv, td);
+    };
+    stage(first);  // lands during the prologue (buffer 0)
+    int voff[4];
+    vt_lane_offsets(voff);
 
     // the lane's query: Q and dout operands, statistics
     const int tq = min(t0 + oq, D.N - 1);
@@ -404,8 +443,8 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     if (stat_in) {
         // from the forward: (m, l, -, c) of the query, and its output for
         // D = dout . out (the lane's 64 dims plus the other half's); the
-        // statistics and the gated features gamma phi_q (bf16, feature order)
-        // go to stat and phiq for the kernels after this one
+        // statistics go to stat for the kernels after this one (the gated
+        // features gamma phi_q follow from the NP-Map backward below)
         stq = *reinterpret_cast<const f32x4*>(stat_in + qo * 4);
         float dd = 0.f;
 #pragma unroll
@@ -419,29 +458,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
         stq[2] = dd + xor32(dd);
-        // the KV head's projection parts, staged once for the block's waves
-        // (the first tile's staging below waits for every wave's reads)
-        load_k_tile(wqh + (size_t)g * (kD / 2) * kD, kD, kD / 2, ks, tid, NW * 64);
-        load_k_tile(wql + (size_t)g * (kD / 2) * kD, kD, kD / 2, vs, tid, NW * 64);
-        __syncthreads();
-        f32x16 phi[1][2][2];
-        np_map_mfma<1>(*reinterpret_cast<const bf16x8(*)[1][8]>(&qf), ks, vs, kKS, phi);
-        const float gq = gate_weight(gate, qo);
-        if (t0 + oq < D.N) {
-            if (hf == 0) *reinterpret_cast<f32x4*>(stat + qo * 4) = stq;
-            bf16* pr = phiq + qo * kD;
-#pragma unroll
-            for (int sgn = 0; sgn < 2; ++sgn)
-#pragma unroll
-                for (int f2 = 0; f2 < 2; ++f2)
-#pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4) {
-                        bf16x4 x4;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) x4[j] = (bf16)(gq * phi[0][sgn][f2][4 * v4 + j]);
-                        *reinterpret_cast<bf16x4*>(pr + 64 * sgn + 32 * f2 + acc_row(4 * v4, hf)) = x4;
-                    }
-        }
+        if (hf == 0 && t0 + oq < D.N) *reinterpret_cast<f32x4*>(stat + qo * 4) = stq;
     } else {
         stq = *reinterpret_cast<const f32x4*>(stat + qo * 4);
     }
@@ -454,50 +471,41 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
 
+    // tile `first` has landed (each wave waits for its own staging) and the
+    // prologue's reads of buffer 1 are done
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
     for (int i = first; i < ntile; ++i) {
-        // rows of tile i: a window chunk from k / v, or compact rows
-        const bf16 *srck, *srcv;
-        int nv;
+        if (i + 1 < ntile) stage(i + 1);  // into the buffer tile i-1 used
+        const int j = (i - first) & 1;
+        const bf16* kr = kpb(j);
+        const bf16* vr = vpb(j);
+        const bf16* ktr = ktb(j);
         uint64_t hi_m, lo_m;
-        if (i <= NWT) {
-            const int tc = c - NWT + i;
-            nv = min(kC, D.N - tc * kC);
-            const size_t off = (((size_t)b * D.N + (size_t)tc * kC) * D.Hkv + g) * kD;
-            srck = k + off;
-            srcv = v + off;
-            if (i == 0) {
-                hi_m = ~0ull;
-                lo_m = selmask;
-            } else if (i == NWT) {
-                hi_m = 0ull;
-                lo_m = ~0ull;
-            } else {
-                hi_m = lo_m = ~0ull;
-            }
+        if (i == 0) {
+            hi_m = ~0ull;
+            lo_m = selmask;
+        } else if (i < NWT) {
+            hi_m = lo_m = ~0ull;
+        } else if (i == NWT) {
+            hi_m = 0ull;
+            lo_m = ~0ull;
         } else {
-            const int r0 = (i - NWT - 1) * kC;
-            nv = min(kC, nrows - r0);
-            const size_t off = ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD + (size_t)r0 * ldkv;
-            srck = ksel + off;
-            srcv = vsel + off;
+            const int nv = min(kC, nrows - (i - NWT - 1) * kC);
             hi_m = lo_m = nv == kC ? ~0ull : (1ull << nv) - 1ull;
         }
-        __syncthreads();  // the previous tile's reads are done
-        load_tile_both<NW * 64>(srck, ldkv, nv, ks, kt, tid);
-        load_rows<NW * 64>(srcv, ldkv, nv, vs, tid);
-        __syncthreads();
         f32x16 sc[2], dp[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            sc[j] = zero16();
-            dp[j] = zero16();
+        for (int jj = 0; jj < 2; ++jj) {
+            sc[jj] = zero16();
+            dp[jj] = zero16();
         }
 #pragma unroll
         for (int st = 0; st < 8; ++st)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                sc[j] = mfma32(ld_bf8(ks + (32 * j + col) * kKS + 16 * st + 8 * hf), qf[st], sc[j]);
-                dp[j] = mfma32(ld_bf8(vs + (32 * j + col) * kKS + 16 * st + 8 * hf), df[st], dp[j]);
+            for (int jj = 0; jj < 2; ++jj) {
+                sc[jj] = mfma32(ld_bf8(kr + (32 * jj + col) * kKS + 16 * st + 8 * hf), qf[st], sc[jj]);
+                dp[jj] = mfma32(ld_bf8(vr + (32 * jj + col) * kKS + 16 * st + 8 * hf), df[st], dp[jj]);
             }
         // key row rk counts for the lane's query when bit rk of
         // (rk > oq ? hi_m : lo_m) is set
@@ -505,20 +513,21 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
         const uint64_t mm = ((hi_m & gt) | (lo_m & ~gt)) >> (4 * hf);
         const uint32_t mw[2] = {(uint32_t)mm, (uint32_t)(mm >> 32)};
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
-                const bool ok = (mw[j] >> (8 * (vv >> 2) + (vv & 3))) & 1u;
-                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[j][vv], cl2, -lse2)) : 0.f;
-                sc[j][vv] = p * (dp[j][vv] - dq_d);
+                const bool ok = (mw[jj] >> (8 * (vv >> 2) + (vv & 3))) & 1u;
+                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sc[jj][vv], cl2, -lse2)) : 0.f;
+                sc[jj][vv] = p * (dp[jj][vv] - dq_d);
             }
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
             const bf16x8 pa = pack_acc(sc[s4 >> 1], s4 & 1);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                acc[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 16 * s4 + 8 * hf), pa, acc[dt]);
+            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma32(vt_frag(ktr, voff, dt, s4), pa, acc[dt]);
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i+1 landed
+        __syncthreads();
     }
     const bool qvalid = t0 + oq < D.N;
 
@@ -566,7 +575,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
             const int ngroups = (D.n_full + D.ng - 1) / D.ng;
             const bf16* shg = reinterpret_cast<const bf16*>(L.sh) + (bg * D.n_full + cq) * (size_t)(kD * kD);
             const bf16* ghg = reinterpret_cast<const bf16*>(L.gh) + (bg * ngroups + run) * (size_t)(kD * kD);
-            bf16* sT = sm;  // kD rows of kKS
+            bf16* sT = smem;  // kD rows of kKS
             __syncthreads();
             for (int x = tid; x < 32 * 16; x += NW * 64) {
                 const int eq = x & 31, oct = x >> 5;  // dims 4 eq .. +3, positions 8 oct .. +7
@@ -608,29 +617,11 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
         }
     }
-    // dphi_q = gamma c_t dfq (the ungated features' gradient), dgate =
-    // (1 - gamma) c_t fq . dfq
+    // dphi_q = gamma c_t dfq (the ungated features' gradient) and, for the
+    // gate logit, dgate = gamma (1 - gamma) c_t phi_q . dfq: dfq stays
+    // unscaled, the scale enters dz
     const float cf = stq[3];
     const float gw = gate_weight(gate, qo);
-    if (dgate) {
-        const bf16* fqr = phiq + qo * kD;
-        float fdot = 0.f;
-#pragma unroll
-        for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                const int f0 = kperm(32 * ft + acc_row(4 * v4, hf));  // four consecutive features
-                const bf16x4 fq4 = *reinterpret_cast<const bf16x4*>(fqr + f0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) fdot = fmaf((float)fq4[j], dfq[ft][4 * v4 + j], fdot);
-            }
-        fdot += xor32(fdot);
-        if (hf == 0 && qvalid) dgate[qo] = (1.f - gw) * cf * fdot;
-    }
-#pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-        for (int vv = 0; vv < 16; ++vv) dfq[ft][vv] *= gw * cf;
 
     // ---- NP-Map backward of the query (full text Sec. 3.2; the map
     // u = P q, z = ||q|| u / ||u||, phi = [softmax(z); softmax(-z)]):
@@ -721,14 +712,36 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     sp = 1.f / (sp + xor32(sp));
     sn = 1.f / (sn + xor32(sn));
-    sa = (sa + xor32(sa)) * sp;
-    sb = (sb + xor32(sb)) * sn;
+    sa = (sa + xor32(sa)) * sp;  // phi+ . dfq+
+    sb = (sb + xor32(sb)) * sn;  // phi- . dfq-
+    if (dgate && hf == 0 && qvalid) dgate[qo] = gw * (1.f - gw) * cf * (sa + sb);
+    if (stat_in && qvalid) {
+        // gamma phi_q (bf16, feature order) for the kernels after this one:
+        // rows 32 ft + acc_row(4 v4, hf) .. +3 hold four consecutive features
+        bf16* pr = phiq + qo * kD;
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                bf16x4 a4, b4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    a4[j] = (bf16)(gw * sp * ep[ft][4 * v4 + j]);
+                    b4[j] = (bf16)(gw * sn * en[ft][4 * v4 + j]);
+                }
+                const int f0 = kperm(32 * ft + acc_row(4 * v4, hf));
+                *reinterpret_cast<bf16x4*>(pr + f0) = a4;
+                *reinterpret_cast<bf16x4*>(pr + 64 + f0) = b4;
+            }
+    }
+    const float dsc = gw * cf;  // dphi_q = dsc dfq
     float dnx = 0.f;
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
         for (int vv = 0; vv < 16; ++vv) {
-            const float z = ep[ft][vv] * sp * (dfq[ft][vv] - sa) - en[ft][vv] * sn * (dfq[ft + 2][vv] - sb);
+            const float z =
+                dsc * (ep[ft][vv] * sp * (dfq[ft][vv] - sa) - en[ft][vv] * sn * (dfq[ft + 2][vv] - sb));
             ep[ft][vv] = z;
             dnx = fmaf(z, u[ft][vv] * iu, dnx);
         }
@@ -1268,7 +1281,7 @@ hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void
                          const int* list_off, float* stat, const void* phik16, const LinBufs& L,
                          const float* gate, void* phiq, float* dq, void* du, float* dgate,
                          const float* stat_in, const void* out, const void* wsplit, hipStream_t s) {
-    const int HB = D.G >= 2 ? 2 : 1;
+    const int HB = D.G >= 4 ? 4 : D.G;  // query heads per block, two waves each
     const int n = D.Hkv * (kD / 2) * kD;
     const bf16* wqh = reinterpret_cast<const bf16*>(wsplit);
     const bf16* wql = wqh + n;
@@ -1292,7 +1305,8 @@ hipError_t launch_bwd_dq(const Dims& D, const void* q, const void* k, const void
         else                       \
             STILL_DQ1(H, 4);       \
     } while (0)
-    if (HB == 2) STILL_DQ(2);
+    if (HB == 4) STILL_DQ(4);
+    else if (HB == 2) STILL_DQ(2);
     else STILL_DQ(1);
 #undef STILL_DQ
 #undef STILL_DQ1

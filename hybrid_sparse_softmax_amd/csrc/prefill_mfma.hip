@@ -59,110 +59,6 @@ __device__ __forceinline__ void load_q(const bf16* __restrict__ q, const Dims& D
     }
 }
 
-// Tile staging (window scores and output kernels): global memory straight into LDS
-// (global_load_lds, 16 bytes per lane; lane l of one instruction lands at
-// byte 16 l of that instruction's 1 KB).  Rows at or beyond a tile's valid
-// count nv (>= 1) repeat row nv-1, so every address stays in bounds; those
-// keys are masked out of every sum.
-//   K tile: 64 rows of kKS elements (17 slots of 16 bytes, the last one
-//     padding); 17 instructions cover its 1088 slots, padding slots load a
-//     slot of the same row.  The logits read a K row per lane at a fixed slot:
-//     the 17-slot stride spreads 16 rows over all banks.
-//   V tile: 64 unpadded rows of 128 elements; slot x of row r is stored at
-//     x ^ vswz(r); 16 instructions.  The value product reads it transposed.
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kKTile = kC * kKS;  // elements of a staged K tile
-constexpr int kVTile = kC * kD;   // elements of a staged V tile
-constexpr int kKPieces = kKTile / 512;  // 17 staging instructions
-constexpr int kVPieces = kVTile / 512;  // 16
-
-__device__ __forceinline__ int vswz(int r) { return 4 * (r & 3) + 2 * ((r >> 2) & 1); }
-
-__device__ __forceinline__ void dma16(const bf16* g, bf16* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
-}
-
-// The same load written out, for the lock-step loop: the compiler does not
-// track it, so it places no wait for it before later LDS reads of other
-// buffers; its users wait for it (vmcnt) explicitly.  M0 holds the LDS
-// destination (wave-uniform); one wait state separates the M0 write from the
-// load that reads it.
-__device__ __forceinline__ void dma16_untracked(const bf16* g, unsigned lds_byte) {
-    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
-    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(g), "s"(m0)
-                     : "memory", "m0");
-}
-
-// staging instruction j (0..16) of a K tile
-__device__ __forceinline__ void stage_k_piece(int j, const bf16* __restrict__ src, size_t ld, int nv,
-                                              bf16* __restrict__ dst) {
-    const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
-    dma16(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 512 * j);
-}
-
-// The same, issued only when en != 0 (wave-uniform); the test and skip sit
-// inside the asm statement, so the surrounding code stays one basic block.
-__device__ __forceinline__ void dma16_untracked_if(const bf16* g, unsigned lds_byte, int en) {
-    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
-    const int e = __builtin_amdgcn_readfirstlane(en);
-    __asm__ volatile("s_cmp_eq_u32 %2, 0\n\ts_cbranch_scc1 1f\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                     "global_load_lds_dwordx4 %0, off\n1:"
-                     :
-                     : "v"(g), "s"(m0), "s"(e)
-                     : "memory", "m0", "scc");
-}
-
-// staging instruction j (0..16) of a K tile, untracked load; dst = LDS
-// byte address of the tile; ld (elements) and row offsets fit 24 bits
-__device__ __forceinline__ void stage_k_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
-                                                unsigned dst) {
-    const int p = 64 * j + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
-    dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
-}
-
-// staging instruction j of a K tile when j < 17 (no branch around it)
-__device__ __forceinline__ void stage_k_piece_if(int j, const bf16* __restrict__ src, int ld, int nv,
-                                                 unsigned dst) {
-    const int jj = min(j, kKPieces - 1);
-    const int p = 64 * jj + (threadIdx.x & 63), row = p / 17, slot = min(p - 17 * row, 15);
-    dma16_untracked_if(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * jj, j < kKPieces);
-}
-
-// Untracked load in the scalar-base form: the address is base (wave-uniform,
-// 64-bit) plus the lane's unsigned 32-bit byte offset, so no per-lane 64-bit
-// arithmetic is needed.  Issued only when en != 0 (wave-uniform), the test
-// and skip inside the asm statement as above.
-__device__ __forceinline__ void dma16_sbase_if(const bf16* base, unsigned off, unsigned lds_byte, int en) {
-    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte);
-    const int e = __builtin_amdgcn_readfirstlane(en);
-    __asm__ volatile("s_cmp_eq_u32 %3, 0\n\ts_cbranch_scc1 1f\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                     "global_load_lds_dwordx4 %0, %1\n1:"
-                     :
-                     : "v"(off), "s"(base), "s"(m0), "s"(e)
-                     : "memory", "m0", "scc");
-}
-
-// Byte offset, from a tile's first row, of the lane's 16 bytes in staging
-// instruction j of a K or V tile whose 64 rows are all readable and ld2
-// bytes apart (the same for every tile of the output kernel's loop).
-__device__ __forceinline__ unsigned k_piece_off(int j, unsigned ld2) {
-    const int p = 64 * j + (threadIdx.x & 63), row = p / 17;
-    return (unsigned)row * ld2 + 16u * (unsigned)min(p - 17 * row, 15);
-}
-__device__ __forceinline__ unsigned v_piece_off(int j, unsigned ld2) {
-    const int l = threadIdx.x & 63, row = 4 * j + (l >> 4);
-    return (unsigned)row * ld2 + 16u * (unsigned)((l & 15) ^ vswz(row));
-}
-
-// staging instruction j (0..15) of a V tile, untracked load
-__device__ __forceinline__ void stage_v_piece_u(int j, const bf16* __restrict__ src, int ld, int nv,
-                                                unsigned dst) {
-    const int l = threadIdx.x & 63, row = 4 * j + (l >> 4), slot = (l & 15) ^ vswz(row);
-    dma16_untracked(src + (__umul24(min(row, nv - 1), ld) + 8 * slot), dst + 1024u * j);
-}
-
 // ---------------------------------------------------------------------------
 // window scores, selection, gather
 // ---------------------------------------------------------------------------
@@ -742,40 +638,6 @@ __device__ __forceinline__ void stage_v_share_u(const bf16* __restrict__ src, in
         if (w + NS * t < kVPieces) stage_v_piece_u(w + NS * t, src, ld, nv, dst);
 }
 
-// staging instruction j (0..15) of a V tile
-__device__ __forceinline__ void stage_v_piece(int j, const bf16* __restrict__ src, size_t ld, int nv,
-                                              bf16* __restrict__ dst) {
-    const int l = threadIdx.x & 63, row = 4 * j + (l >> 4), slot = (l & 15) ^ vswz(row);
-    dma16(src + (size_t)min(row, nv - 1) * ld + 8 * slot, dst + 512 * j);
-}
-
-// Transposed reads of a staged V tile: the value product's A operand for dims
-// 32 dt + l%32 and key storage positions 16 ks + 8 hf .. +7 (key kperm(pos)).
-// ds_read_b64_tr_b16 hands lane d of each 16-lane group element j of the
-// 8-byte read of lane 4j + d/4 of the group (element d%4); lane s of group
-// G = l/16 therefore reads row K0 + s/4, dims 32 dt + 16 (G&1) + 4 (s&3) ..+3,
-// and receives keys K0 .. K0+3 of dim 32 dt + l%32.  K0 = 16 ks + 4 hf for
-// operand elements 0-3 and K0 + 8 for elements 4-7, which are exactly the
-// keys kperm assigns to those elements.  voff[dt] holds the lane's part of
-// the element offset.
-__device__ __forceinline__ void vt_lane_offsets(int (&voff)[4]) {
-    const int l = threadIdx.x & 63, s = l & 15, grp = l >> 4, hf = grp >> 1, gc = grp & 1, m = s >> 2;
-    const int c = (4 * hf + m) * kD + 8 * ((2 * gc + ((s & 3) >> 1)) ^ (2 * hf)) + 4 * (s & 1);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) voff[dt] = c + 32 * (dt ^ m);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ bf16x8 vt_frag(const bf16* vtile, const int (&voff)[4], int dt, int ks) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const bf16* p = vtile + voff[dt] + 16 * ks * kD;
-    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-    const i16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * kD));
-    const i16x8 r = __builtin_shufflevector(a, b2, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, r);
-}
 
 // Scheduling pattern for one pair of products (value, logits) of the
 // software-pipelined loop: product, R1 LDS reads, NV vector instructions,
