@@ -386,12 +386,15 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const size_t ldkv = (size_t)D.Hkv * kD;
 
     // Key tiles go straight into LDS (global_load_lds), double buffered:
-    // tile i+1 lands while tile i is computed.  Buffer j holds the K rows and
-    // the V rows in the padded K-tile layout (row reads for the logits and
-    // dout . v) and the K rows again in the swizzled V-tile layout (the
-    // transposed reads of dQ^T += K^T dS^T).  The phases after the loop reuse
-    // the front bytes as ks, vs and kt.
-    __shared__ __align__(16) bf16 smem[4 * kKTile + 2 * kVTile];
+    // the next tile lands while the current one is computed.  Buffer j holds
+    // the K rows and the V rows in the padded K-tile layout (row reads for
+    // the logits and dout . v) and the K rows again in the swizzled V-tile
+    // layout (the transposed reads of dQ^T += K^T dS^T).  Behind them, the
+    // phi_k rows of chunk c-NWT (swizzled V-tile layout) for the linear
+    // terms.  The phases after the loop reuse the front bytes as ks, vs, kt.
+    // Tile order: with c >= NWT the partly covered chunk c-NWT (tile 0) comes
+    // last, and its dout . v products also give the linear terms' weights.
+    __shared__ __align__(16) bf16 smem[4 * kKTile + 3 * kVTile];
     const unsigned lds0 = (unsigned)(size_t)(lds_void*)smem;
     bf16* ks = smem;
     bf16* vs = smem + kC * kKS;
@@ -399,9 +402,13 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     auto kpb = [&](int j) { return smem + j * kKTile; };
     auto vpb = [&](int j) { return smem + (2 + j) * kKTile; };
     auto ktb = [&](int j) { return smem + 4 * kKTile + j * kVTile; };
+    const bf16* phkt = smem + 4 * kKTile + 2 * kVTile;
+    const int nt = ntile - first;  // tiles in the loop (>= 2 when c >= NWT)
+    auto tile_at = [&](int pos) { return first > 0 ? first + pos : (pos + 1 < nt ? pos + 1 : 0); };
     // rows of tile i: a window chunk from k / v, or compact rows; every tile
     // has nv >= 1 valid rows, and rows past nv repeat row nv - 1 (masked)
-    auto stage = [&](int i) {
+    auto stage = [&](int pos) {
+        const int i = tile_at(pos);
         const bf16 *srck, *srcv;
         int nv;
         if (i <= NWT) {
@@ -417,7 +424,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
             srck = ksel + off;
             srcv = vsel + off;
         }
-        const unsigned j = (unsigned)((i - first) & 1);
+        const unsigned j = (unsigned)(pos & 1);
         const unsigned kd = lds0 + 2u * j * kKTile, vd = lds0 + 2u * (2 + j) * kKTile;
         const unsigned td = lds0 + 2u * (4 * kKTile + j * kVTile);
         for (int x = wave; x < kKPieces; x += NW) {
@@ -426,7 +433,12 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         for (int x = wave; x < kVPieces; x += NW) stage_v_piece_u(x, srck, (int)ldkv, nv, td);
     };
-    stage(first);  // lands during the prologue (buffer 0)
+    stage(0);  // lands during the prologue (buffer 0)
+    if (c >= NWT) {
+        const bf16* pk = phik + (bg * D.N + tla) * kD;
+        const unsigned pd = lds0 + 2u * (4 * kKTile + 2 * kVTile);
+        for (int x = wave; x < kVPieces; x += NW) stage_v_piece_u(x, pk, kD, kC, pd);
+    }
     int voff[4];
     vt_lane_offsets(voff);
 
@@ -471,13 +483,16 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
 
-    // tile `first` has landed (each wave waits for its own staging) and the
-    // prologue's reads of buffer 1 are done
+    // the first tile and phi_k have landed (each wave waits for its own
+    // staging, then the barrier)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    for (int i = first; i < ntile; ++i) {
-        if (i + 1 < ntile) stage(i + 1);  // into the buffer tile i-1 used
-        const int j = (i - first) & 1;
+    // one tile: position pos in the order above; lin (tile 0 only) also
+    // packs the linear terms' weights dout . v_j - D of the routed
+    // unselected keys at or below the query's offset into wl
+    auto tile = [&](int pos, bool lin, bf16x8 (&wl)[4]) __attribute__((always_inline)) {
+        if (pos + 1 < nt) stage(pos + 1);  // into the buffer of position pos-1
+        const int i = tile_at(pos), j = pos & 1;
         const bf16* kr = kpb(j);
         const bf16* vr = vpb(j);
         const bf16* ktr = ktb(j);
@@ -507,6 +522,19 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
                 sc[jj] = mfma32(ld_bf8(kr + (32 * jj + col) * kKS + 16 * st + 8 * hf), qf[st], sc[jj]);
                 dp[jj] = mfma32(ld_bf8(vr + (32 * jj + col) * kKS + 16 * st + 8 * hf), df[st], dp[jj]);
             }
+        if (lin) {
+            f32x16 w[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    const int rk = 32 * jj + acc_row(vv, hf);
+                    const bool la = rk <= oq && !((selmask >> rk) & 1ull);
+                    w[jj][vv] = la ? dp[jj][vv] - dq_d : 0.f;
+                }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) wl[s4] = pack_acc(w[s4 >> 1], s4 & 1);
+        }
         // key row rk counts for the lane's query when bit rk of
         // (rk > oq ? hi_m : lo_m) is set
         const uint64_t gt = oq >= 63 ? 0ull : ~0ull << (oq + 1);
@@ -526,9 +554,16 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma32(vt_frag(ktr, voff, dt, s4), pa, acc[dt]);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile i+1 landed
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile landed
         __syncthreads();
+    };
+    const int nloop = c >= NWT ? nt - 1 : nt;
+    for (int pos = 0; pos < nloop; ++pos) {
+        bf16x8 unused[4];
+        tile(pos, false, unused);
     }
+    bf16x8 wl[4];
+    if (c >= NWT) tile(nt - 1, true, wl);
     const bool qvalid = t0 + oq < D.N;
 
     // ---- linear terms: dfq^T (rows = feature positions p of the prefix's
@@ -537,36 +572,12 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft) dfq[ft] = zero16();
     if (c >= NWT) {
-        // chunk c-NWT: V rows and phi_k^T of its keys
-        const int cp = c - NWT;
-        __syncthreads();
-        load_k_tile(v + (((size_t)b * D.N + (size_t)cp * kC) * D.Hkv + g) * kD, ldkv, kC, vs, tid, NW * 64);
-        load_vt_tile(phik + (bg * D.N + (size_t)cp * kC) * kD, kD, kC, kt, tid, NW * 64);
-        __syncthreads();
-        f32x16 w[2];
-        w[0] = zero16();
-        w[1] = zero16();
+        // chunk c-NWT: the weights from its tile, times phi_k^T (transposed
+        // reads of its staged rows)
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
+        for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                w[j] = mfma32(ld_bf8(vs + (32 * j + col) * kKS + 16 * st + 8 * hf), df[st], w[j]);
-        // dout . v_j - D on the routed linear keys at or below the query's offset
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int vv = 0; vv < 16; ++vv) {
-                const int rk = 32 * j + acc_row(vv, hf);
-                const bool la = rk <= oq && !((selmask >> rk) & 1ull);
-                w[j][vv] = la ? w[j][vv] - dq_d : 0.f;
-            }
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const bf16x8 pa = pack_acc(w[s4 >> 1], s4 & 1);
-#pragma unroll
-            for (int ft = 0; ft < 4; ++ft)
-                dfq[ft] = mfma32(ld_bf8(kt + (32 * ft + col) * kVS + 16 * s4 + 8 * hf), pa, dfq[ft]);
-        }
+            for (int ft = 0; ft < 4; ++ft) dfq[ft] = mfma32(vt_frag(phkt, voff, ft, s4), wl[s4], dfq[ft]);
         if (c > NWT) {
             // prefix of chunks <= c-NWT-1, staged as sT[p][e] (stored S^T rows
             // are [e][p]): the within-run part of chunk c-NWT-1 plus its run's
