@@ -385,24 +385,35 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const int tla = t0 - NWT * kC;
     const size_t ldkv = (size_t)D.Hkv * kD;
 
-    // Key tiles go straight into LDS (global_load_lds), double buffered:
-    // the next tile lands while the current one is computed.  Buffer j holds
-    // the K rows and the V rows in the padded K-tile layout (row reads for
-    // the logits and dout . v) and the K rows again in the swizzled V-tile
-    // layout (the transposed reads of dQ^T += K^T dS^T).  Behind them, the
-    // phi_k rows of chunk c-NWT (swizzled V-tile layout) for the linear
-    // terms.  The phases after the loop reuse the front bytes as ks, vs, kt.
+    // Everything the block reads from memory beyond its own query rows comes
+    // straight into LDS (global_load_lds), requested one step ahead:
+    //   buffers 0, 1: the key tiles, double buffered (the next tile lands
+    //     while the current one is computed): K and V rows in the padded
+    //     K-tile layout (row reads for the logits and dout . v), K rows again
+    //     in the swizzled V-tile layout (transposed reads of dQ^T += K^T dS^T);
+    //   phkt: the phi_k rows of chunk c-NWT (swizzled V-tile layout), from
+    //     the start;
+    //   during the last tile, the linear prefix's two bf16 matrices (64 KB)
+    //     into the other buffer (50 KB) and the overflow area, with the two
+    //     z vectors; they are summed into the last tile's buffer after it;
+    //   then the NP-Map projection (rows permuted for the NP-Map backward)
+    //     into the other buffer, in the key tiles' three layouts.
     // Tile order: with c >= NWT the partly covered chunk c-NWT (tile 0) comes
     // last, and its dout . v products also give the linear terms' weights.
-    __shared__ __align__(16) bf16 smem[4 * kKTile + 3 * kVTile];
+    constexpr int kBuf = 2 * kKTile + kVTile;  // elements of one buffer
+    constexpr int kBufPieces = kBuf / 512;     // its 1 KB pieces (50)
+    constexpr int kRawPieces = 2 * kD * kD / 512;  // the prefix's two matrices (64)
+    constexpr int kOver = (kRawPieces - kBufPieces) * 512;  // overflow elements
+    __shared__ __align__(16) bf16 smem[2 * kBuf + kVTile + kOver + 2 * kD * 2];
     const unsigned lds0 = (unsigned)(size_t)(lds_void*)smem;
-    bf16* ks = smem;
-    bf16* vs = smem + kC * kKS;
-    bf16* kt = smem + 2 * kC * kKS;
-    auto kpb = [&](int j) { return smem + j * kKTile; };
-    auto vpb = [&](int j) { return smem + (2 + j) * kKTile; };
-    auto ktb = [&](int j) { return smem + 4 * kKTile + j * kVTile; };
-    const bf16* phkt = smem + 4 * kKTile + 2 * kVTile;
+    auto kpb = [&](int j) { return smem + j * kBuf; };
+    auto vpb = [&](int j) { return smem + j * kBuf + kKTile; };
+    auto ktb = [&](int j) { return smem + j * kBuf + 2 * kKTile; };
+    const bf16* phkt = smem + 2 * kBuf;
+    constexpr int kOverOff = 2 * kBuf + kVTile;  // overflow area, then lz | gz
+    // LDS element offset of 1 KB piece x of the staged prefix (x < 32: the
+    // within-run part, x >= 32: the earlier runs'), buffer jr first
+    auto raw_piece = [&](int jr, int x) { return x < kBufPieces ? jr * kBuf + 512 * x : kOverOff + 512 * (x - kBufPieces); };
     const int nt = ntile - first;  // tiles in the loop (>= 2 when c >= NWT)
     auto tile_at = [&](int pos) { return first > 0 ? first + pos : (pos + 1 < nt ? pos + 1 : 0); };
     // rows of tile i: a window chunk from k / v, or compact rows; every tile
@@ -425,8 +436,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
             srcv = vsel + off;
         }
         const unsigned j = (unsigned)(pos & 1);
-        const unsigned kd = lds0 + 2u * j * kKTile, vd = lds0 + 2u * (2 + j) * kKTile;
-        const unsigned td = lds0 + 2u * (4 * kKTile + j * kVTile);
+        const unsigned kd = lds0 + 2u * j * kBuf, vd = kd + 2u * kKTile, td = kd + 4u * kKTile;
         for (int x = wave; x < kKPieces; x += NW) {
             stage_k_piece_u(x, srck, (int)ldkv, nv, kd);
             stage_k_piece_u(x, srcv, (int)ldkv, nv, vd);
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     stage(0);  // lands during the prologue (buffer 0)
     if (c >= NWT) {
         const bf16* pk = phik + (bg * D.N + tla) * kD;
-        const unsigned pd = lds0 + 2u * (4 * kKTile + 2 * kVTile);
+        const unsigned pd = lds0 + 2u * (2 * kBuf);
         for (int x = wave; x < kVPieces; x += NW) stage_v_piece_u(x, pk, kD, kC, pd);
     }
     int voff[4];
@@ -487,11 +497,26 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     // staging, then the barrier)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    const int ngroups = (D.n_full + D.ng - 1) / D.ng;
+    const int cq = c - NWT - 1, run = c > NWT ? cq / D.ng : 0;  // the prefix's last chunk, its run
+    auto stage_prefix = [&](int jr) {
+        const bf16* shg = reinterpret_cast<const bf16*>(L.sh) + (bg * D.n_full + cq) * (size_t)(kD * kD);
+        const bf16* ghg = reinterpret_cast<const bf16*>(L.gh) + (bg * ngroups + run) * (size_t)(kD * kD);
+        for (int x = wave; x < kRawPieces; x += NW)
+            dma16_untracked((x < 32 ? shg + 512 * x : ghg + 512 * (x - 32)) + 8 * lane,
+                            lds0 + 2u * (unsigned)raw_piece(jr, x));
+        if (wave == NW - 1) {
+            const float* zs = lane < 32 ? L.lz + (bg * D.n_full + cq) * kD + 4 * lane
+                                        : L.gz + (bg * ngroups + run) * kD + 4 * (lane - 32);
+            dma16_untracked(reinterpret_cast<const bf16*>(zs), lds0 + 2u * (kOverOff + kOver));
+        }
+    };
     // one tile: position pos in the order above; lin (tile 0 only) also
     // packs the linear terms' weights dout . v_j - D of the routed
     // unselected keys at or below the query's offset into wl
     auto tile = [&](int pos, bool lin, bf16x8 (&wl)[4]) __attribute__((always_inline)) {
         if (pos + 1 < nt) stage(pos + 1);  // into the buffer of position pos-1
+        if (lin && c > NWT) stage_prefix((pos & 1) ^ 1);
         const int i = tile_at(pos), j = pos & 1;
         const bf16* kr = kpb(j);
         const bf16* vr = vpb(j);
@@ -565,12 +590,61 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     bf16x8 wl[4];
     if (c >= NWT) tile(nt - 1, true, wl);
     const bool qvalid = t0 + oq < D.N;
+    const int jl = (nt - 1) & 1, jp = jl ^ 1;  // the last tile's buffer, the other one
+    // the NP-Map projection of KV head g (high and low parts, 64 rows each)
+    // into buffer jp, rows permuted (LDS row r = projection row kperm(r)):
+    // both parts in the padded layout, the high part again swizzled
+    const bf16* ph = wqh + (size_t)g * (kD / 2) * kD;
+    const bf16* pl = wql + (size_t)g * (kD / 2) * kD;
+    auto stage_proj = [&]() {
+        const unsigned kd = lds0 + 2u * jp * kBuf;
+        for (int x = wave; x < kKPieces; x += NW) {
+            const int pp = 64 * x + lane, row = pp / 17, slot = min(pp - 17 * row, 15);
+            const int so = kperm(row) * kD + 8 * slot;
+            dma16_untracked(ph + so, kd + 1024u * x);
+            dma16_untracked(pl + so, kd + 2u * kKTile + 1024u * x);
+        }
+        for (int x = wave; x < kVPieces; x += NW) {
+            const int row = 4 * x + (lane >> 4), slot = (lane & 15) ^ vswz(row);
+            dma16_untracked(ph + kperm(row) * kD + 8 * slot, kd + 4u * kKTile + 1024u * x);
+        }
+    };
 
     // ---- linear terms: dfq^T (rows = feature positions p of the prefix's
     // order, feature kperm(p); column = the lane's query) ----
     f32x16 dfq[4];
 #pragma unroll
     for (int ft = 0; ft < 4; ++ft) dfq[ft] = zero16();
+    if (c > NWT) {
+        // prefix of chunks <= c-NWT-1 into sT[p][e] (the stored S^T rows are
+        // [e][p]; kD rows of kKS over the last tile's K and V rows): the
+        // within-run part of chunk c-NWT-1 plus its run's exclusive prefix,
+        // summed in fp32
+        bf16* sT = kpb(jl);
+        for (int x = tid; x < 32 * 16; x += NW * 64) {
+            const int eq = x & 31, oct = x >> 5;  // dims 4 eq .. +3, positions 8 oct .. +7
+            bf16x8 rr[4];
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int o = (4 * eq + e4) * kD + 8 * oct;  // element of a stored matrix
+                const bf16x8 a8 = ld_bf8(smem + raw_piece(jp, o >> 9) + (o & 511));
+                const bf16x8 b8 = ld_bf8(smem + raw_piece(jp, 32 + (o >> 9)) + (o & 511));
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) rr[e4][jj] = (bf16)((float)a8[jj] + (float)b8[jj]);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                bf16x4 t4;
+                t4[0] = rr[0][jj];
+                t4[1] = rr[1][jj];
+                t4[2] = rr[2][jj];
+                t4[3] = rr[3][jj];
+                *reinterpret_cast<bf16x4*>(sT + (8 * oct + jj) * kKS + 4 * eq) = t4;
+            }
+        }
+        __syncthreads();  // sT complete, the stored matrices consumed
+    }
+    stage_proj();
     if (c >= NWT) {
         // chunk c-NWT: the weights from its tile, times phi_k^T (transposed
         // reads of its staged rows)
@@ -578,56 +652,32 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
             for (int ft = 0; ft < 4; ++ft) dfq[ft] = mfma32(vt_frag(phkt, voff, ft, s4), wl[s4], dfq[ft]);
-        if (c > NWT) {
-            // prefix of chunks <= c-NWT-1, staged as sT[p][e] (stored S^T rows
-            // are [e][p]): the within-run part of chunk c-NWT-1 plus its run's
-            // exclusive prefix
-            const int cq = c - NWT - 1, run = cq / D.ng;
-            const int ngroups = (D.n_full + D.ng - 1) / D.ng;
-            const bf16* shg = reinterpret_cast<const bf16*>(L.sh) + (bg * D.n_full + cq) * (size_t)(kD * kD);
-            const bf16* ghg = reinterpret_cast<const bf16*>(L.gh) + (bg * ngroups + run) * (size_t)(kD * kD);
-            bf16* sT = smem;  // kD rows of kKS
-            __syncthreads();
-            for (int x = tid; x < 32 * 16; x += NW * 64) {
-                const int eq = x & 31, oct = x >> 5;  // dims 4 eq .. +3, positions 8 oct .. +7
-                bf16x8 rr[4];
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const bf16x8 a8 = ld_bf8(shg + (size_t)(4 * eq + e4) * kD + 8 * oct);
-                    const bf16x8 b8 = ld_bf8(ghg + (size_t)(4 * eq + e4) * kD + 8 * oct);
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) rr[e4][jj] = (bf16)((float)a8[jj] + (float)b8[jj]);
-                }
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    bf16x4 t4;
-                    t4[0] = rr[0][jj];
-                    t4[1] = rr[1][jj];
-                    t4[2] = rr[2][jj];
-                    t4[3] = rr[3][jj];
-                    *reinterpret_cast<bf16x4*>(sT + (8 * oct + jj) * kKS + 4 * eq) = t4;
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-                for (int st = 0; st < 8; ++st)
-                    dfq[ft] = mfma32(ld_bf8(sT + (32 * ft + col) * kKS + 16 * st + 8 * hf), df[st], dfq[ft]);
-            const float* lz = L.lz + (bg * D.n_full + cq) * (size_t)kD;
-            const float* gz = L.gz + (bg * ngroups + run) * (size_t)kD;
-#pragma unroll
-            for (int ft = 0; ft < 4; ++ft)
-#pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4) {
-                    const int p0 = 32 * ft + acc_row(4 * v4, hf);
-                    const f32x4 z1 = *reinterpret_cast<const f32x4*>(lz + p0);
-                    const f32x4 z2 = *reinterpret_cast<const f32x4*>(gz + p0);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) dfq[ft][4 * v4 + j] -= dq_d * (z1[j] + z2[j]);
-                }
-        }
     }
+    if (c > NWT) {
+        const bf16* sT = kpb(jl);
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+            for (int st = 0; st < 8; ++st)
+                dfq[ft] = mfma32(ld_bf8(sT + (32 * ft + col) * kKS + 16 * st + 8 * hf), df[st], dfq[ft]);
+        const float* lz = reinterpret_cast<const float*>(smem + kOverOff + kOver);
+        const float* gz = lz + kD;
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int p0 = 32 * ft + acc_row(4 * v4, hf);
+                const f32x4 z1 = *reinterpret_cast<const f32x4*>(lz + p0);
+                const f32x4 z2 = *reinterpret_cast<const f32x4*>(gz + p0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dfq[ft][4 * v4 + j] -= dq_d * (z1[j] + z2[j]);
+            }
+    }
+    // the query row again (read back rather than kept live through the
+    // linear phase)
+    bf16x8 xq[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) xq[st] = ld_bf8(q + qo * kD + 16 * st + 8 * hf);
     // dphi_q = gamma c_t dfq (the ungated features' gradient) and, for the
     // gate logit, dgate = gamma (1 - gamma) c_t phi_q . dfq: dfq stays
     // unscaled, the scale enters dz
@@ -644,39 +694,11 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     // staged in that order (LDS row r = P row kperm(r)): u then comes out of
     // the matrix cores with the same rows, and P^T is staged in natural
     // order for dQ^T = P^T dU^T, whose contraction positions are the features.
-    __syncthreads();  // the linear phase's reads of sm are done
-    {
-        const bf16* ph = wqh + (size_t)g * (kD / 2) * kD;
-        const bf16* pl = wql + (size_t)g * (kD / 2) * kD;
-        for (int x = tid; x < kC * 16; x += NW * 64) {
-            const int row = x >> 4, piece = x & 15;
-            const size_t src = (size_t)kperm(row) * kD + 8 * piece;
-            st_bf8(ks + row * kKS + 8 * piece, ld_bf8(ph + src));
-            st_bf8(vs + row * kKS + 8 * piece, ld_bf8(pl + src));
-        }
-        // P^T: kt[dim * kVS + f] = P[f][dim] (high part)
-        for (int x = tid; x < 16 * 16; x += NW * 64) {
-            const int kq = x & 15, oct = x >> 4;  // features 4 kq .. +3, dims 8 oct .. +7
-            bf16x8 r4[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) r4[rr] = ld_bf8(ph + (size_t)(4 * kq + rr) * kD + 8 * oct);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 t4;
-                t4[0] = r4[0][e];
-                t4[1] = r4[1][e];
-                t4[2] = r4[2][e];
-                t4[3] = r4[3][e];
-                *reinterpret_cast<bf16x4*>(kt + (8 * oct + e) * kVS + 4 * kq) = t4;
-            }
-        }
-    }
-    // the query row again (read back rather than kept live through the
-    // linear phase)
-    bf16x8 xq[8];
-#pragma unroll
-    for (int st = 0; st < 8; ++st) xq[st] = ld_bf8(q + qo * kD + 16 * st + 8 * hf);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the projection has landed
     __syncthreads();
+    const bf16* ks = kpb(jp);  // high part, rows permuted
+    const bf16* vs = vpb(jp);  // low part, rows permuted
+    const bf16* pt = ktb(jp);  // high part swizzled: transposed reads give P^T in feature order
     f32x16 u[2];
     u[0] = zero16();
     u[1] = zero16();
@@ -777,7 +799,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
                 const bf16x8 pd = pack_acc(dsc, s2);
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
-                    acc[dt] = mfma32(ld_bf8(kt + (32 * dt + col) * kVS + 32 * ft + 16 * s2 + 8 * hf), pd, acc[dt]);
+                    acc[dt] = mfma32(vt_frag(pt, voff, dt, 2 * ft + s2), pd, acc[dt]);
             }
     }
     if (!qvalid) return;
