@@ -427,9 +427,11 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
     kw = dict(window=W, chunk=C, topk=lam)
     args = (dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"])
     # the training pairing: the forward hands the backward its routing, its
-    # output and its per-query statistics
-    fw = still.fwd(*args, **kw, return_sel=True, return_stats=True)
-    sel, saved = fw["sel_idx"], dict(out=fw["out"], stats=fw["stats"])
+    # output, its per-query statistics and its workspace (the keys' NP-Map
+    # features and the linear prefixes)
+    fw = still.fwd(*args, **kw, return_sel=True, return_stats=True, return_workspace=True)
+    sel = fw["sel_idx"]
+    saved = dict(out=fw["out"], stats=fw["stats"], fwd_workspace=fw["workspace"])
     sh = still.make_shape(batch=cfg["batch"], seqlen=cfg["seqlen"], n_q_heads=cfg["n_q_heads"],
                           n_kv_heads=cfg["n_kv_heads"], head_dim=cfg["head_dim"], **kw)
     ws = torch.empty(still.bwd_workspace_size(sh), dtype=torch.uint8, device="cuda")

@@ -999,11 +999,16 @@ hipError_t bwd_t(const Dims& D, const BwdArgs& a, const BwdWork& w, hipStream_t 
                                          w.wsplit, s)) != hipSuccess) {
             return e;
         }
-        if ((e = mark.fn(mark.ctx, "la_state")) != hipSuccess) return e;
-        if ((e = launch_la_state(DT, a.k, a.v, w.wsplit, w.route, w.phik16, w.lin16, -1, s)) != hipSuccess)
-            return e;
-        if ((e = mark.fn(mark.ctx, "la_scan16")) != hipSuccess) return e;
-        if ((e = launch_la_group_scan(DT, w.lin16, -1, nullptr, nullptr, s)) != hipSuccess) return e;
+        // the keys' NP-Map features and the linear prefixes, unless the
+        // forward's are given
+        if (!w.lin_given) {
+            if ((e = mark.fn(mark.ctx, "la_state")) != hipSuccess) return e;
+            if ((e = launch_la_state(DT, a.k, a.v, w.wsplit, w.route, w.phik16, w.lin16, -1, s)) !=
+                hipSuccess)
+                return e;
+            if ((e = mark.fn(mark.ctx, "la_scan16")) != hipSuccess) return e;
+            if ((e = launch_la_group_scan(DT, w.lin16, -1, nullptr, nullptr, s)) != hipSuccess) return e;
+        }
         // the statistics and gated query features: a first pass, or (given
         // the forward's out and statistics) the dq kernel's own prologue
         if (!a.stats) {

@@ -452,6 +452,8 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     int voff[4];
     vt_lane_offsets(voff);
 
+    // route flags of chunk c-NWT (requested with the query rows)
+    const uint8_t rtf = c >= NWT ? route[bg * D.N + tla + lane] : (uint8_t)0;
     // the lane's query: Q and dout operands, statistics
     const int tq = min(t0 + oq, D.N - 1);
     const size_t qo = ((size_t)b * D.N + tq) * D.Hq + h;
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const float lse2 = stq[0] * kLog2e + __log2f(stq[1]);  // P = 2^(s cl2 - lse2)
     const float dq_d = stq[2];
     uint64_t selmask = 0;
-    if (c >= NWT) selmask = __ballot(route[bg * D.N + tla + lane] == kRouteSA);
+    if (c >= NWT) selmask = __ballot(rtf == kRouteSA);
 
     f32x16 acc[4];
 #pragma unroll

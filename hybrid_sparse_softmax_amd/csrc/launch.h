@@ -228,6 +228,7 @@ struct BwdWork {
     void* phik16;         // [B, Hkv, N, d'] bf16 (kperm features)
     void* wsplit;         // NP-Map projections as bf16 high / low parts
     LinBufs lin16;        // linear prefixes of the matrix-core path
+    bool lin_given;       // phik16 and lin16 are the forward's (not recomputed)
     float* kvpart;        // segment sums of the selected keys' dk, dv
     // the matrix-core kernels after the lists work in 64-token tiles: tile
     // holds those dimensions (C = 64, lam = min(lam, 64), T and n_full in

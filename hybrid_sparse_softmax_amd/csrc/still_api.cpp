@@ -513,9 +513,9 @@ static hipError_t mark_launch(void* ctx, const char* name) {
 
 static int bwd(const still_shape* sh, const void* q, const void* k, const void* v,
                const float* wq, const float* wk, const float* gate, const int32_t* sel_idx,
-               const void* dout, const void* out_opt, const float* stats_opt, float* dq, float* dk,
-               float* dv, float* dwq, float* dwk, float* dgate, void* ws, size_t ws_bytes,
-               hipStream_t s, Timeline& tl) {
+               const void* dout, const void* out_opt, const float* stats_opt, const void* fws,
+               size_t fws_bytes, float* dq, float* dk, float* dv, float* dwq, float* dwk, float* dgate,
+               void* ws, size_t ws_bytes, hipStream_t s, Timeline& tl) {
     int st = check_shape(sh, false);
     if (st) return st;
     const Dims D = make_dims(sh, sh->seqlen);
@@ -539,9 +539,20 @@ static int bwd(const still_shape* sh, const void* q, const void* k, const void* 
     if (!ws || ws_bytes < bwd_bytes(D, sh)) return STILL_ERR_WORKSPACE;
     const bool mfma = use_mfma_bwd(D, sh);
     if (tl.ev && tl.max_ev < bwd_launch_count(mfma) + 1) return STILL_ERR_INVALID_ARG;
+    // the forward's workspace: its keys' NP-Map features and linear prefixes
+    // (the matrix-core forward leaves them there; same carving as the forward)
+    if (fws && mfma && fws_bytes < fwd_bytes(D, sh)) return STILL_ERR_WORKSPACE;
     void* wsa = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     Carver cv(wsa);
-    const BwdWork w = carve_bwd(D, cv, mfma);
+    BwdWork w = carve_bwd(D, cv, mfma);
+    w.lin_given = false;
+    if (fws && mfma) {
+        Carver cf(reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(fws) + 255) & ~uintptr_t(255)));
+        const MfmaBuffers f = carve_mfma(D, cf);
+        w.phik16 = f.phik;
+        w.lin16 = f.lin;
+        w.lin_given = true;
+    }
     BwdArgs a;
     a.q = q;
     a.k = k;
@@ -715,18 +726,21 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes) {
 int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k, const void* v,
                           const float* wphi_q, const float* wphi_k, const float* gate_opt,
                           const int32_t* sel_idx, const void* dout, const void* out_opt,
-                          const float* stats_opt, float* dq, float* dk,
+                          const float* stats_opt, const void* fwd_workspace_opt,
+                          size_t fwd_workspace_bytes, float* dq, float* dk,
                           float* dv, float* dwphi_q, float* dwphi_k, float* dgate_opt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
     still::Timeline tl;
-    return still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, out_opt, stats_opt, dq,
-                      dk, dv, dwphi_q, dwphi_k, dgate_opt, workspace, workspace_bytes, stream, tl);
+    return still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, out_opt, stats_opt,
+                      fwd_workspace_opt, fwd_workspace_bytes, dq, dk, dv, dwphi_q, dwphi_k, dgate_opt,
+                      workspace, workspace_bytes, stream, tl);
 }
 
 int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const void* k,
                                 const void* v, const float* wphi_q, const float* wphi_k,
                                 const float* gate_opt, const int32_t* sel_idx, const void* dout,
                                 const void* out_opt, const float* stats_opt,
+                                const void* fwd_workspace_opt, size_t fwd_workspace_bytes,
                                 float* dq, float* dk, float* dv, float* dwphi_q, float* dwphi_k,
                                 float* dgate_opt, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
@@ -738,8 +752,8 @@ int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const v
     tl.max_ev = max_events;
     tl.names = kernel_names_opt;
     const int st = still::bwd(shape, q, k, v, wphi_q, wphi_k, gate_opt, sel_idx, dout, out_opt,
-                              stats_opt, dq, dk, dv, dwphi_q, dwphi_k, dgate_opt, workspace,
-                              workspace_bytes, stream, tl);
+                              stats_opt, fwd_workspace_opt, fwd_workspace_bytes, dq, dk, dv, dwphi_q,
+                              dwphi_k, dgate_opt, workspace, workspace_bytes, stream, tl);
     *n_launches = tl.n;
     return st;
 }

@@ -95,7 +95,7 @@ def lib() -> ct.CDLL:
         L.still_bwd_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
         L.still_hybrid_attn_bwd.restype = ct.c_int
         L.still_hybrid_attn_bwd.argtypes = [ct.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                            vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+                                            vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.still_future_kv_utility_workspace_size.restype = ct.c_int
         L.still_future_kv_utility_workspace_size.argtypes = [ct.POINTER(Shape), ct.POINTER(sz)]
         L.still_future_kv_utility.restype = ct.c_int
@@ -239,11 +239,13 @@ class DecodeCache:
 def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale=0.0,
         return_scores=False, return_sel=False, return_stats=False, cache: DecodeCache | None = None,
         out=None, workspace=None, general=False, timer: LaunchTimer | None = None,
-        route="saliency", gate=None, stats=None) -> dict:
+        route="saliency", gate=None, stats=None, return_workspace=False) -> dict:
     """still_hybrid_attn_fwd.  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or f32),
     wphi_* [Hkv, d'/2, d] f32, gate: optional gate logits [B,N,Hq] f32.
     return_stats (or a given stats tensor [B,N,Hq,4] f32): the per-query
-    statistics bwd can start from.  Returns dict(out, scores?, sel_idx?, stats?)."""
+    statistics bwd can start from; return_workspace: the workspace tensor
+    used, whose linear state bwd can reuse (fwd_workspace).  Returns
+    dict(out, scores?, sel_idx?, stats?, workspace?)."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     sh = make_shape(batch=B, seqlen=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=window,
@@ -284,6 +286,8 @@ def fwd(q, k, v, wphi_q, wphi_k, *, window, chunk, topk, eps=1e-6, softmax_scale
         res["sel_idx"] = sel
     if stats is not None:
         res["stats"] = stats
+    if return_workspace:
+        res["workspace"] = workspace
     return res
 
 
@@ -388,12 +392,13 @@ def decode_step_ragged(q, k, v, wphi_q, wphi_k, cache: DecodeCache, pos: torch.T
 
 def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6,
         softmax_scale=0.0, workspace=None, timer: LaunchTimer | None = None, gate=None,
-        general=False, out=None, stats=None) -> dict:
+        general=False, out=None, stats=None, fwd_workspace=None) -> dict:
     """still_hybrid_attn_bwd: gradients of sum(dout * out) for the forward
     with the same arguments, under the routing sel_idx [B, Hkv, N/C, lambda]
     (the forward's sel_idx output; None when there is nothing selected).
     out, stats: the forward's output and return_stats tensor, both or
-    neither.  Returns dict(dq, dk, dv, dwphi_q, dwphi_k), all fp32, plus
+    neither.  fwd_workspace: the workspace tensor of that forward call
+    (untouched since), whose linear state the backward then reuses.  Returns dict(dq, dk, dv, dwphi_q, dwphi_k), all fp32, plus
     dgate [B, N, Hq] when gate logits [B, N, Hq] are given."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -424,7 +429,8 @@ def bwd(q, k, v, wphi_q, wphi_k, sel_idx, dout, *, window, chunk, topk, eps=1e-6
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     args = [ct.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(wphi_q), _ptr(wphi_k), _ptr(gate),
-            _ptr(sel_idx), _ptr(dout), _ptr(out), _ptr(stats), _ptr(res["dq"]), _ptr(res["dk"]),
+            _ptr(sel_idx), _ptr(dout), _ptr(out), _ptr(stats), _ptr(fwd_workspace),
+            0 if fwd_workspace is None else fwd_workspace.numel(), _ptr(res["dq"]), _ptr(res["dk"]),
             _ptr(res["dv"]),
             _ptr(res["dwphi_q"]), _ptr(res["dwphi_k"]), _ptr(res.get("dgate")), _ptr(workspace),
             workspace.numel(), _stream()]

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define STILL_ABI_VERSION 5
+#define STILL_ABI_VERSION 6
 
 typedef enum {
     STILL_OK = 0,
@@ -295,6 +295,12 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
  *             reference, normaliser and linear weight from stats_opt and
  *             dout . out from out instead of a first pass that recomputes
  *             them; the fp32 kernels ignore them
+ *   fwd_workspace_opt, fwd_workspace_bytes  if not NULL, the workspace of the
+ *             forward call that produced sel_idx (same shape and inputs,
+ *             untouched since): the matrix-core path then reads the keys'
+ *             NP-Map features and the linear prefixes the forward left there
+ *             instead of recomputing them (STILL_ERR_WORKSPACE when smaller
+ *             than still_fwd_workspace_size); the fp32 kernels ignore it
  *   dq        [B, N, Hq, d] fp32, written
  *   dk, dv    [B, N, Hkv, d] fp32, written
  *   dwphi_q, dwphi_k  [Hkv, d'/2, d] fp32, written
@@ -321,7 +327,8 @@ int still_bwd_workspace_size(const still_shape* shape, size_t* bytes);
 int still_hybrid_attn_bwd(const still_shape* shape, const void* q, const void* k, const void* v,
                           const float* wphi_q, const float* wphi_k, const float* gate_opt,
                           const int32_t* sel_idx, const void* dout, const void* out_opt,
-                          const float* stats_opt, float* dq, float* dk,
+                          const float* stats_opt, const void* fwd_workspace_opt,
+                          size_t fwd_workspace_bytes, float* dq, float* dk,
                           float* dv, float* dwphi_q, float* dwphi_k, float* dgate_opt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -372,6 +379,7 @@ int still_hybrid_attn_bwd_timed(const still_shape* shape, const void* q, const v
                                 const void* v, const float* wphi_q, const float* wphi_k,
                                 const float* gate_opt, const int32_t* sel_idx, const void* dout,
                                 const void* out_opt, const float* stats_opt,
+                                const void* fwd_workspace_opt, size_t fwd_workspace_bytes,
                                 float* dq, float* dk, float* dv, float* dwphi_q, float* dwphi_k,
                                 float* dgate_opt, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert S.abi_version() == 5
+    assert S.abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5):
         assert S.status_str(code) and S.status_str(code) != "unknown status"
     assert S.status_str(7) == "unknown status"
@@ -186,9 +186,10 @@ def test_ragged_decode_checks():
 
 
 def bwd_status(sh, sel=FAKE, ws_bytes=1 << 40, ptr=FAKE, ws=FAKE, dw=FAKE, gate=None, dgate=None,
-               out=None, stats=None):
+               out=None, stats=None, fws=None, fws_bytes=0):
     return S.lib().still_hybrid_attn_bwd(ct.byref(sh), ptr, ptr, ptr, ptr, ptr, gate, sel, ptr, out,
-                                         stats, ptr, ptr, ptr, dw, dw, dgate, ws, ws_bytes, None)
+                                         stats, fws, fws_bytes, ptr, ptr, ptr, dw, dw, dgate, ws,
+                                         ws_bytes, None)
 
 
 def test_bwd_checks():
@@ -209,6 +210,10 @@ def test_bwd_checks():
     assert bwd_status(sh, out=FAKE) == S.STILL_ERR_INVALID_ARG
     assert bwd_status(sh, stats=FAKE) == S.STILL_ERR_INVALID_ARG
     assert bwd_status(sh, out=FAKE, stats=MISALIGNED) == S.STILL_ERR_INVALID_ARG
+    # the forward's workspace must be as large as the forward needs (matrix-core
+    # path; the fp32 kernels ignore it)
+    fneed = S.fwd_workspace_size(sh)
+    assert bwd_status(sh, fws=FAKE, fws_bytes=fneed - 1) == S.STILL_ERR_WORKSPACE
     for kw, st in ((dict(n_q_heads=6, n_kv_heads=4), S.STILL_ERR_INVALID_ARG),
                    (dict(head_dim=96), S.STILL_ERR_UNSUPPORTED)):
         assert bwd_status(shape(**kw)) == st
@@ -217,8 +222,8 @@ def test_bwd_checks():
     evs = (ct.c_void_p * 4)()
     # up to 16 launches need one event more; too few is
     # rejected before anything runs
-    assert timed(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, FAKE,
-                 FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None, evs, 4, ct.byref(n),
+    assert timed(ct.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, None, 0,
+                 FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None, evs, 4, ct.byref(n),
                  None) == S.STILL_ERR_INVALID_ARG
 
 

@@ -88,9 +88,10 @@ CASES = {
 }
 
 
-def run(gpu_lib, cfg, seed, corrupt=False, general=False, saved=False, fwd_general=False):
+def run(gpu_lib, cfg, seed, corrupt=False, general=False, saved=False, fwd_general=False, fwd_ws=False):
     """saved: the backward starts from the forward's out and statistics (the
-    forward on the general kernels when fwd_general)."""
+    forward on the general kernels when fwd_general); fwd_ws: and from the
+    forward's workspace (its keys' features and linear prefixes)."""
     raw = workloads.make_prefill(cfg, seed)
     dt = torch_dtype(cfg["dtype"])
     dev, ref = prepare(raw, dt)
@@ -103,7 +104,7 @@ def run(gpu_lib, cfg, seed, corrupt=False, general=False, saved=False, fwd_gener
     if min(lam, C) > 0 or saved:
         fw = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W,
                          chunk=C, topk=lam, return_sel=min(lam, C) > 0, return_stats=saved,
-                         general=fwd_general)
+                         general=fwd_general, return_workspace=fwd_ws)
         sel = fw.get("sel_idx")
     osel = None if sel is None else sel.cpu().numpy().astype(np.int64)
     if corrupt and sel is not None and sel.shape[2] > 1:
@@ -116,6 +117,8 @@ def run(gpu_lib, cfg, seed, corrupt=False, general=False, saved=False, fwd_gener
         osel[:, :, 1, 0] = osel[:, :, 1, 1]
         sel = bad
     extra = dict(out=fw["out"], stats=fw["stats"]) if saved else {}
+    if fwd_ws:
+        extra["fwd_workspace"] = fw["workspace"]
     g = gpu_lib.bwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], sel, dout,
                     window=W, chunk=C, topk=lam, general=general, **extra)
     torch.cuda.synchronize()
@@ -152,17 +155,20 @@ SAVED_CASES = ["bf16_ragged_G2", "bf16_G1", "bf16_G4_linear", "bf16_swa_la", "bf
                "f32_d128_G2"]
 
 
-@pytest.mark.parametrize("fwd_general", [False, True], ids=["fwd_picked", "fwd_general"])
+@pytest.mark.parametrize("fwd", ["picked", "picked_ws", "general"], ids=lambda x: "fwd_" + x)
 @pytest.mark.parametrize("name", SAVED_CASES)
-def test_bwd_from_forward_statistics_matches_oracle(gpu_lib, name, fwd_general):
+def test_bwd_from_forward_statistics_matches_oracle(gpu_lib, name, fwd):
     """The backward started from the forward's out and statistics (no first
     pass on the matrix cores) against the oracle, with the statistics from
     either forward path: both define (m, l) at their own reference point, so
-    either must do.  The fp32 kernels ignore them."""
+    either must do.  picked_ws: the backward also takes the keys' features
+    and linear prefixes from the matrix-core forward's workspace.  The fp32
+    kernels ignore both."""
     cfg, seed = CASES[name]
-    say(f"[bwd] from forward stats case={name} fwd_general={fwd_general} "
+    fwd_general = fwd == "general"
+    say(f"[bwd] from forward stats case={name} fwd={fwd} "
         f"matrix-core={mfma_path(cfg)} shape={workloads.shape_of(cfg)} seed={seed}")
-    g, o = run(gpu_lib, cfg, seed, saved=True, fwd_general=fwd_general)
+    g, o = run(gpu_lib, cfg, seed, saved=True, fwd_general=fwd_general, fwd_ws=fwd == "picked_ws")
     compare(g, o, grad_tol(cfg, False))
 
 

@@ -161,11 +161,12 @@ BWD_CASES = {
 
 @pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
 @pytest.mark.parametrize("name", list(BWD_CASES))
-@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "from_fwd_stats"])
+@pytest.mark.parametrize("saved", [0, 1, 2], ids=["recompute", "from_fwd_stats", "from_fwd_stats_ws"])
 def test_gated_bwd_matches_oracle(gpu_lib, name, general, saved):
     """saved: the backward starts from the gated forward's output and
     statistics (the gate weight enters the features the dq kernel forms and
-    the linear weight c the forward wrote)."""
+    the linear weight c the forward wrote); 2: and from the forward's
+    workspace (its keys' features and linear prefixes)."""
     from test_gpu_backward import grad_tol
     cfg, seed = BWD_CASES[name]
     say(f"[gate bwd] case={name} general={general} saved={saved} shape={workloads.shape_of(cfg)} seed={seed}")
@@ -178,10 +179,13 @@ def test_gated_bwd_matches_oracle(gpu_lib, name, general, saved):
     W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
     sel = None
     fw = gpu_lib.fwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], window=W, chunk=C,
-                     topk=lam, return_sel=min(lam, C) > 0, return_stats=saved, gate=gd)
+                     topk=lam, return_sel=min(lam, C) > 0, return_stats=saved > 0, gate=gd,
+                     return_workspace=saved == 2)
     if min(lam, C) > 0:
         sel = fw["sel_idx"]
     extra = dict(out=fw["out"], stats=fw["stats"]) if saved else {}
+    if saved == 2:
+        extra["fwd_workspace"] = fw["workspace"]
     g = gpu_lib.bwd(dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"], sel, dout.cuda(),
                     window=W, chunk=C, topk=lam, gate=gd, general=general, **extra)
     torch.cuda.synchronize()
