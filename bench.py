@@ -555,7 +555,7 @@ def bench_chunk_sweep(still, torch, steps=5, warmup=2, name="train_8x2k"):
     (full text App. A.7.5, Table 14: C varied with the window spanning one
     chunk, W = C, and 16 selected tokens per chunk), on the 8 x 2048 training
     batch for the chunk sizes the matrix-core path takes (64, 128, 256); the
-    backward starts from the forward's output and statistics."""
+    backward starts from the forward's output, statistics and workspace."""
     cfg = workloads.CONFIGS[name]
     seed = workloads.seed_of(name)
     raw = workloads.make_prefill(cfg, seed)
@@ -580,7 +580,8 @@ def bench_chunk_sweep(still, torch, steps=5, warmup=2, name="train_8x2k"):
             fw = still.fwd(*args, **kw, out=out, workspace=fws, return_sel=True, return_stats=True)
             e_mid = torch.cuda.Event(enable_timing=True)
             e_mid.record()
-            still.bwd(*args, fw["sel_idx"], dout, **kw, workspace=bws, out=out, stats=fw["stats"])
+            still.bwd(*args, fw["sel_idx"], dout, **kw, workspace=bws, out=out, stats=fw["stats"],
+                      fwd_workspace=fws)
             return e_mid
 
         for _ in range(warmup):
