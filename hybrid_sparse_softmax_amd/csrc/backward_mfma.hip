@@ -332,27 +332,27 @@ __global__ __launch_bounds__(256) void bwd_kv_merge_kernel(const float* __restri
 
 
 // ---------------------------------------------------------------------------
-// Query side: dq's softmax part, then the linear terms of the queries' gated
-// features.  Block = HB query heads of KV head g x the 64 queries of chunk c
-// (two waves per head, 32 queries each), the key tiles of the forward in its
-// order (window chunks c-NWT .. c with their masks, then the compact selected
-// rows).  Per tile, with the statistics (m, l, D) of the first pass and
-// P = exp(tau q.k - m) / l:
+// Query side: dq's softmax part, the linear terms of the queries' gated
+// features, and their NP-Map backward.  Block = HB query heads of KV head g x
+// the 64 queries of chunk c (two waves per head, 32 queries each), the key
+// tiles of the forward (window chunks c-NWT+1 .. c, the compact selected
+// rows, and the partly covered chunk c-NWT last, each with its mask).  Per
+// tile, with the statistics (m, l, D) and P = exp(tau q.k - m) / l:
 //   S^T  = K Q^T           (logits, keys x queries)
 //   dP^T = V dout^T        (dout . v_j)
 //   dS^T = P^T (dP^T - D)  rounded to bf16 as the forward rounds P
 //   dQ^T += K^T dS^T       (K read transposed from LDS)
-// dq = tau (dQ^T)^T is written in fp32.  Then, for a query with linear
-// mass (c_t = exp(-m) / l > 0; full text Sec. 3.3, the chunk-wise linear
-// branch with the shared normaliser), the gradient w.r.t. its gated
-// features fq = gamma phi_q:
+// Then, for a query with linear mass (c_t = exp(-m) / l > 0; full text
+// Sec. 3.3, the chunk-wise linear branch with the shared normaliser), the
+// gradient w.r.t. its gated features fq = gamma phi_q:
 //   dfq = c_t (S dout - D z + sum over the routed unselected keys j of
 //         chunk c-NWT at or below the query's offset of (dout . v_j - D) phi_k(j))
 // with S, z the linear prefix of chunks <= c-NWT-1 (within-run part plus the
 // earlier runs', summed in fp32 and rounded to bf16 once), on the matrix
-// cores in the prefix's feature order; dphi_q = gamma dfq goes to the NP-Map
-// backward and dgate = (1 - gamma) fq . dfq.  Rows with no linear term get
-// zeros.
+// cores in the prefix's feature order.  dphi_q = gamma dfq goes through the
+// NP-Map backward into dQ^T; the same pass gives gamma phi_q (bf16) for the
+// kernels after this one and the gate logit's gradient gamma (1 - gamma)
+// phi_q . dfq.  dq = tau (dQ^T)^T plus the norm term is written once, fp32.
 template <int HB, int NWT>
 __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
