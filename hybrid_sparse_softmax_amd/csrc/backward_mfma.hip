@@ -1003,10 +1003,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
     if (has_q) {
         const int tq0 = c0 * kC, nq = min(kC, D.N - tq0);
-        bf16* fq = sm;                       // [q][p], kKS
-        bf16* dr = sm + kC * kKS;            // [q][e], kKS
-        bf16* fqt = sm + 2 * kC * kKS;       // [p][kperm(q)], kVS
-        bf16* drt = fqt + kD * kVS;          // [e][kperm(q)], kVS
+        // fq [q][p] and dout [q][e] rows (kKS); their transposes are read
+        // from the same rows (ds_read_b64_tr_b16)
+        bf16* fq = sm;
+        bf16* dr = sm + kC * kKS;
+        int poff[4];
+        kt_pad_lane_offsets(poff);
         for (int hh = 0; hh < D.G; ++hh) {
             const int h = g * D.G + hh;
             const size_t o0 = ((size_t)b * D.N + tq0) * D.Hq + h;
@@ -1016,27 +1018,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                 st_bf8(fq + row * kKS + 8 * oct,
                        row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct) : zero_bf8());
             }
-            for (int x = tid; x < 16 * 16; x += 256) {
-                const int kq = x & 15, oct = x >> 4;
-                bf16x8 rr[4];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int row = 4 * kq + q4;
-                    rr[q4] = row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct) : zero_bf8();
-                }
-                const int pos = kperm(4 * kq);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bf16x4 t4;
-                    t4[0] = rr[0][e];
-                    t4[1] = rr[1][e];
-                    t4[2] = rr[2][e];
-                    t4[3] = rr[3][e];
-                    *reinterpret_cast<bf16x4*>(fqt + (8 * oct + e) * kVS + pos) = t4;
-                }
-            }
             load_k_tile(dout + o0 * kD, (size_t)D.Hq * kD, nq, dr, tid, 256);
-            load_vt_tile(dout + o0 * kD, (size_t)D.Hq * kD, nq, drt, tid, 256);
             if (tid < kC) {
                 float cf = 0.f, dd = 0.f;
                 if (tid < nq) {
@@ -1069,14 +1051,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                         x[vv] = ok ? c4[jj] * (role == 0 ? x[vv] - d4[jj] : x[vv]) : 0.f;
                     }
                 }
-                const bf16* At = role == 0 ? fqt : drt;
+                const bf16* At = role == 0 ? fq : dr;
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const bf16x8 pw = pack_acc(x, s2);
                     const int ks = 2 * qb + s2;
 #pragma unroll
-                    for (int t4 = 0; t4 < 4; ++t4)
-                        acc[t4] = mfma32(ld_bf8(At + (32 * t4 + col) * kVS + 16 * ks + 8 * hf), pw, acc[t4]);
+                    for (int t4 = 0; t4 < 4; ++t4) acc[t4] = mfma32(kt_pad_frag(At, poff, t4, ks), pw, acc[t4]);
                 }
             }
         }

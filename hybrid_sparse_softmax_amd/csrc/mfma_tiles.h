@@ -356,5 +356,25 @@ __device__ __forceinline__ bf16x8 vt_frag(const bf16* vtile, const int (&voff)[4
     return __builtin_bit_cast(bf16x8, r);
 }
 
+// Transposed reads of a staged K tile (64 rows of kKS elements, the padded
+// layout): the same operand as vt_frag, dims 32 dt + l%32 and row storage
+// positions 16 ks + 8 hf .. +7 (row kperm(pos)), from the padded rows (the
+// four rows of one read sit 272 bytes apart, so some reads share banks).
+__device__ __forceinline__ void kt_pad_lane_offsets(int (&poff)[4]) {
+    const int l = threadIdx.x & 63, s16 = l & 15, grp = l >> 4;
+    const int c0 = (4 * (grp >> 1) + (s16 >> 2)) * kKS + 16 * (grp & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) poff[dt] = c0 + 32 * dt;
+}
+
+__device__ __forceinline__ bf16x8 kt_pad_frag(const bf16* ktile, const int (&poff)[4], int dt, int ks) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const bf16* p = ktile + poff[dt] + 16 * ks * kKS;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * kKS));
+    const i16x8 r = __builtin_shufflevector(a, b2, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 }  // namespace mt
 }  // namespace still
