@@ -85,6 +85,10 @@ CASES = {
     "bf16_W256_C128_G2": (make_case("z", 1, 600, 4, 2, 128, 256, 128, 40), 49),
     "bf16_W256_C256_G1_lam100": (make_case("z", 1, 700, 2, 2, 128, 256, 256, 100), 50),
     "bf16_W128_C128_swa_la": (make_case("z", 1, 350, 4, 1, 128, 128, 128, 0), 51),
+    # eight query heads per KV head: the query-side kernel's blocks take four
+    # heads each, so two blocks share every (KV head, chunk)
+    "bf16_G8": (make_case("l", 1, 300, 16, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 52),
+    "bf16_W128_C128_G8": (make_case("m", 1, 330, 8, 1, 128, 128, 128, 24), 53),
 }
 
 
@@ -152,7 +156,7 @@ def test_bwd_matches_oracle(gpu_lib, name, general):
 SAVED_CASES = ["bf16_ragged_G2", "bf16_G1", "bf16_G4_linear", "bf16_swa_la", "bf16_all_selected",
                "bf16_short_no_chunk", "bf16_single_token", "bf16_underflow_G2", "bf16_underflow_all_selected",
                "bf16_W128_C64_G4", "bf16_W256_C64_G2", "bf16_W128_C128_G4", "bf16_W256_C256_G1_lam100",
-               "f32_d128_G2"]
+               "bf16_G8", "f32_d128_G2"]
 
 
 @pytest.mark.parametrize("fwd", ["picked", "picked_ws", "general"], ids=lambda x: "fwd_" + x)
