@@ -501,7 +501,7 @@ def bench_backward(still, torch, steps, warmup, name="train_8x2k"):
                        "projections (fp32) under the forward's routing", "batch": cfg["batch"],
                        "seq_len": cfg["seqlen"]},
             "forward_ms": round(fwd_ms, 4), "backward_over_forward": round(ms / fwd_ms, 2),
-            "from_forward_statistics": True, "recompute_statistics_ms": round(recompute_ms, 4),
+            "from_forward_statistics": True, "from_forward_workspace": True, "recompute_statistics_ms": round(recompute_ms, 4),
             "whole_step_TFLOPs": round(total / (ms * 1e-3) / 1e12, 2),
             "whole_step_count": "method flops: 10d per softmax pair plus the linear and NP-Map terms",
             "matrix_core_kernels": mfma_kernels,
