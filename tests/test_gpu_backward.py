@@ -176,6 +176,34 @@ def test_bwd_from_forward_statistics_matches_oracle(gpu_lib, name, fwd):
     compare(g, o, grad_tol(cfg, False))
 
 
+@pytest.mark.parametrize("name", ["bf16_G4_linear", "bf16_W256_C64_G2", "bf16_W128_C128_G8"])
+def test_bwd_forward_workspace_gives_the_recomputed_linear_state(gpu_lib, name):
+    """The linear state the backward reads from the forward's workspace is
+    the one it would recompute (same kernels, same routing): the gradients
+    with and without the workspace agree to fp32 rounding, so the handed-over
+    buffers line up with the backward's own."""
+    cfg, seed = CASES[name]
+    say(f"[bwd] forward workspace vs recomputed linear state case={name} shape={workloads.shape_of(cfg)} seed={seed}")
+    raw = workloads.make_prefill(cfg, seed)
+    dt = torch_dtype(cfg["dtype"])
+    dev, _ = prepare(raw, dt)
+    dout = torch.from_numpy(workloads.make_grad_out(cfg, seed)).to(dt).cuda().contiguous()
+    W, C, lam = cfg["window"], cfg["chunk"], cfg["topk"]
+    args = (dev["q"], dev["k"], dev["v"], dev["wphi_q"], dev["wphi_k"])
+    fw = gpu_lib.fwd(*args, window=W, chunk=C, topk=lam, return_sel=True, return_stats=True,
+                     return_workspace=True)
+    saved = dict(out=fw["out"], stats=fw["stats"])
+    a = gpu_lib.bwd(*args, fw["sel_idx"], dout, window=W, chunk=C, topk=lam, **saved)
+    b = gpu_lib.bwd(*args, fw["sel_idx"], dout, window=W, chunk=C, topk=lam, **saved,
+                    fwd_workspace=fw["workspace"])
+    torch.cuda.synchronize()
+    for gname, _ in NAMES:
+        x, y = a[gname].double().cpu().numpy(), b[gname].double().cpu().numpy()
+        err = np.abs(x - y).max() / max(np.abs(x).max(), 1e-30)
+        say(f"  {gname} max difference / max {err:.2e}")
+        assert np.isfinite(y).all() and err <= 1e-6, (gname, err)
+
+
 @pytest.mark.parametrize("general", [False, True], ids=["picked", "general"])
 @pytest.mark.parametrize("name", ["bf16_ragged_G2", "bf16_W128_C128_G4"])
 def test_bwd_ignores_repeated_and_foreign_selection_entries(gpu_lib, name, general):
