@@ -89,6 +89,10 @@ CASES = {
     # heads each, so two blocks share every (KV head, chunk)
     "bf16_G8": (make_case("l", 1, 300, 16, 2, 128, 64, 64, 16, outlier_frac=0.02, heavy_scale=6.0), 52),
     "bf16_W128_C128_G8": (make_case("m", 1, 330, 8, 1, 128, 128, 128, 24), 53),
+    # wide chunks at the ends of the routing: every token selected (each
+    # 64-token tile of the lists full), and no selection (window + linear)
+    "bf16_W128_C128_all_selected": (make_case("n", 1, 400, 4, 2, 128, 128, 128, 128), 54),
+    "bf16_W256_C256_swa_la": (make_case("p", 1, 700, 4, 2, 128, 256, 256, 0), 55),
 }
 
 
