@@ -55,16 +55,16 @@ struct QTile {
     float dd[kC];         // D = dout . out
 };
 
-template <int NTHR>
-__device__ __forceinline__ void stage_qtile(QTile& T, const bf16* __restrict__ q,
-                                            const bf16* __restrict__ dout,
-                                            const float* __restrict__ stat, const Dims& D, int b,
-                                            int t0, int h, int tid) {
+// Stages the tile with 512 threads: Q (rows and transposed) by threads
+// 0-255, dout by 256-511, the statistics by the first 64.
+__device__ __forceinline__ void stage_qtile(QTile& T, const bf16* __restrict__ q, const bf16* __restrict__ dout,
+                                            const float* __restrict__ stat, const Dims& D, int b, int t0,
+                                            int h, int tid) {
     const int nv = min(kC, D.N - t0);
     const size_t ld = (size_t)D.Hq * kD;
     const size_t o = (((size_t)b * D.N + t0) * D.Hq + h) * kD;
-    load_tile_both<NTHR>(q + o, ld, nv, T.qs, T.qt, tid);
-    load_tile_both<NTHR>(dout + o, ld, nv, T.ds, T.dt, tid);
+    if (tid < 256) load_tile_both<256>(q + o, ld, nv, T.qs, T.qt, tid);
+    else load_tile_both<256>(dout + o, ld, nv, T.ds, T.dt, tid - 256);
     if (tid < kC) {
         float a = 0.f, dd = 0.f;
         if (tid < nv) {
@@ -77,46 +77,67 @@ __device__ __forceinline__ void stage_qtile(QTile& T, const bf16* __restrict__ q
     }
 }
 
-// One wave's contribution of a staged query tile to its 32 keys.  vis(r)
-// says whether query row r (0..63 of the tile) attends to this lane's key
-// by softmax.
-template <typename Vis>
-__device__ __forceinline__ void key_tile(const QTile& T, const bf16x8 (&kf)[8], const bf16x8 (&vf)[8],
-                                         float cl2, Vis vis, f32x16 (&dva)[4], f32x16 (&dka)[4]) {
+// One staged query tile's contribution to a block's key groups of 32 keys,
+// each group shared by two waves (on one SIMD): role 0 holds the group's K
+// rows and forms S = Q K^T, P and dV^T += dout^T P; role 1 holds the V rows
+// and forms dP = dout V^T, then dS = P (dP - D) with the P its partner
+// hands over through LDS (bf16, packed as the value product's operand, lane
+// for lane), and dK^T += Q^T dS.  vis(r) says whether query row r (0..63 of
+// the tile) attends to the lane's key by softmax; act (wave-uniform) whether
+// the group has a key the tile's queries see.  Every wave of the block calls
+// it (one barrier inside).
+template <int NG, typename Vis>
+__device__ __forceinline__ void key_tile_split(const QTile& T, const bf16x8 (&kv)[8], int role, int grp,
+                                               float cl2, bool act, Vis vis,
+                                               bf16x8 (&pbuf)[NG][2][2][64], f32x16 (&acc)[4]) {
     const int lane = threadIdx.x & 63, hf = lane >> 5, col = lane & 31;
+    f32x16 x[2];  // role 0: P, role 1: dP (rows: queries 32 qb + acc_row, column: the lane's key)
+    if (act) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s = zero16(), dp = zero16();
+        for (int qb = 0; qb < 2; ++qb) {
+            x[qb] = zero16();
+            const bf16* A = role == 0 ? T.qs : T.ds;
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            s = mfma32(ld_bf8(T.qs + (32 * qb + col) * kKS + 16 * st + 8 * hf), kf[st], s);
-            dp = mfma32(ld_bf8(T.ds + (32 * qb + col) * kKS + 16 * st + 8 * hf), vf[st], dp);
-        }
-        // rows are queries 32 qb + acc_row(vv, hf), the column is the lane's key
+            for (int st = 0; st < 8; ++st)
+                x[qb] = mfma32(ld_bf8(A + (32 * qb + col) * kKS + 16 * st + 8 * hf), kv[st], x[qb]);
+            if (role == 0) {
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-            const int r0 = 32 * qb + acc_row(4 * v4, hf);
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(T.lse2 + r0);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(T.dd + r0);
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int r0 = 32 * qb + acc_row(4 * v4, hf);
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(T.lse2 + r0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int vv = 4 * v4 + j;
-                const float p = vis(r0 + j) ? __builtin_amdgcn_exp2f(fmaf(s[vv], cl2, -l4[j])) : 0.f;
-                s[vv] = p;
-                dp[vv] = p * (dp[vv] - d4[j]);
-            }
-        }
+                    for (int j = 0; j < 4; ++j) {
+                        const int vv = 4 * v4 + j;
+                        x[qb][vv] = vis(r0 + j) ? __builtin_amdgcn_exp2f(fmaf(x[qb][vv], cl2, -l4[j])) : 0.f;
+                    }
+                }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8 pp = pack_acc(s, s2), pd = pack_acc(dp, s2);
-            const int ks = 2 * qb + s2;  // queries 16 ks .. 16 ks + 15 of the tile
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                dva[dt] = mfma32(ld_bf8(T.dt + (32 * dt + col) * kVS + 16 * ks + 8 * hf), pp, dva[dt]);
-                dka[dt] = mfma32(ld_bf8(T.qt + (32 * dt + col) * kVS + 16 * ks + 8 * hf), pd, dka[dt]);
+                for (int s2 = 0; s2 < 2; ++s2) pbuf[grp][qb][s2][lane] = pack_acc(x[qb], s2);
             }
         }
     }
+    __syncthreads();  // every group's P is in pbuf
+    if (!act) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            bf16x8 pk = pbuf[grp][qb][s2][lane];
+            if (role == 1) {
+                // dS on the same accumulator elements (element j of k-step s2
+                // is element 8 s2 + j)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int vv = 8 * s2 + j;
+                    pk[j] = (bf16)((float)pk[j] * (x[qb][vv] - T.dd[32 * qb + acc_row(vv, hf)]));
+                }
+            }
+            const int ks = 2 * qb + s2;  // queries 16 ks .. 16 ks + 15 of the tile
+            const bf16* A = role == 0 ? T.dt : T.qt;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                acc[dt] = mfma32(ld_bf8(A + (32 * dt + col) * kVS + 16 * ks + 8 * hf), pk, acc[dt]);
+        }
 }
 
 // B operand rows of key row `row` (bf16, 128 dims): dims 16 s + 8 hf .. +7
@@ -126,9 +147,10 @@ __device__ __forceinline__ void load_key_operand(const bf16* __restrict__ row, b
     for (int s = 0; s < 8; ++s) x[s] = ld_bf8(row + 16 * s + 8 * hf);
 }
 
-// window keys: block = 128 keys of chunks 2 cb, 2 cb + 1 of (b, g)
+// window keys: block = 128 keys of chunks 2 cb, 2 cb + 1 of (b, g), four
+// groups of 32 keys, two waves each (key_tile_split)
 template <int NWT, int KPB>
-__global__ __launch_bounds__(KPB * 128) void bwd_kv_window_kernel(
+__global__ __launch_bounds__(KPB * 256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_window_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const uint8_t* __restrict__ route, const float* __restrict__ stat,
     float* __restrict__ dk, float* __restrict__ dv, Dims D) {
@@ -137,60 +159,57 @@ __global__ __launch_bounds__(KPB * 128) void bwd_kv_window_kernel(
     const int bgi = (int)(blockIdx.x / npair);
     const int g = bgi % D.Hkv, b = bgi / D.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ck = KPB * cb + (wave >> 1);         // this wave's key chunk
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wv % (2 * KPB), role = wv / (2 * KPB);  // key group; 0: P and dv, 1: dS and dk
+    const int ck = KPB * cb + (wave >> 1);         // this group's key chunk
     const int ok = 32 * (wave & 1) + col;          // the lane's key offset in it
     const int j = ck * kC + ok;
     const bool kvalid = j < D.N;
     const size_t bg = (size_t)b * D.Hkv + g;
     const int jr = min(j, D.N - 1);
-    bf16x8 kf[8], vf[8];
-    load_key_operand(k + (((size_t)b * D.N + jr) * D.Hkv + g) * kD, kf);
-    load_key_operand(v + (((size_t)b * D.N + jr) * D.Hkv + g) * kD, vf);
+    bf16x8 kv[8];  // role 0: K rows, role 1: V rows
+    load_key_operand((role == 0 ? k : v) + (((size_t)b * D.N + jr) * D.Hkv + g) * kD, kv);
     const bool ksel = kvalid && route[bg * D.N + jr] == kRouteSA;
     const float cl2 = D.tau * kLog2e;
-    f32x16 dva[4], dka[4];
+    f32x16 acc[4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dva[dt] = dka[dt] = zero16();
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
 
     __shared__ QTile T;
+    __shared__ __align__(16) bf16x8 pbuf[2 * KPB][2][2][64];
     const int c_first = KPB * cb, c_last = min(D.T - 1, KPB * cb + KPB - 1 + NWT);
     for (int qc = c_first; qc <= c_last; ++qc) {
         const int i = qc - ck;  // query chunk relative to this wave's key chunk
         const int t0 = qc * kC;
         for (int hh = 0; hh < D.G; ++hh) {
             __syncthreads();
-            stage_qtile<KPB * 128>(T, q, dout, stat, D, b, t0, g * D.G + hh, tid);
+            stage_qtile(T, q, dout, stat, D, b, t0, g * D.G + hh, tid);
             __syncthreads();
-            if (i < 0 || i > NWT || ck >= D.T) continue;
             const int nq = min(kC, D.N - t0);
-            key_tile(T, kf, vf, cl2,
-                     [&](int r) {
-                         if (!kvalid || r >= nq) return false;
-                         if (i == 0) return r >= ok;                   // causal
-                         if (i < NWT) return true;                      // inside the window
-                         return r < ok || ksel;                         // window part, routed selected
-                     },
-                     dva, dka);
+            key_tile_split(T, kv, role, wave, cl2, !(i < 0 || i > NWT || ck >= D.T),
+                           [&](int r) {
+                               if (!kvalid || r >= nq) return false;
+                               if (i == 0) return r >= ok;                   // causal
+                               if (i < NWT) return true;                      // inside the window
+                               return r < ok || ksel;                         // window part, routed selected
+                           },
+                           pbuf, acc);
         }
     }
     if (!kvalid) return;
+    // role 0 adds to dv, role 1 tau times its sums to dk
     const size_t o = (((size_t)b * D.N + j) * D.Hkv + g) * kD;
+    float* dst = role == 1 ? dk : dv;
+    const float sc = role == 1 ? D.tau : 1.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
             const int e = 32 * dt + acc_row(4 * v4, hf);
-            f32x4 a4, b4;
-            const f32x4 k_old = *reinterpret_cast<const f32x4*>(dk + o + e);
-            const f32x4 v_old = *reinterpret_cast<const f32x4*>(dv + o + e);
+            f32x4 a4 = *reinterpret_cast<const f32x4*>(dst + o + e);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                a4[jj] = k_old[jj] + D.tau * dka[dt][4 * v4 + jj];
-                b4[jj] = v_old[jj] + dva[dt][4 * v4 + jj];
-            }
-            *reinterpret_cast<f32x4*>(dk + o + e) = a4;
-            *reinterpret_cast<f32x4*>(dv + o + e) = b4;
+            for (int jj = 0; jj < 4; ++jj) a4[jj] += sc * acc[dt][4 * v4 + jj];
+            *reinterpret_cast<f32x4*>(dst + o + e) = a4;
         }
 }
 
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(KPB * 128) void bwd_kv_window_kernel(
 // fixed order of summation.
 constexpr int kSelSeg = 2;
 template <int NWT, int KW>
-__global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
+__global__ __launch_bounds__(KW * 128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_selected_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ ksel, const bf16* __restrict__ vsel,
     const bf16* __restrict__ dout, const int32_t* __restrict__ selw, const int* __restrict__ list_off,
     const float* __restrict__ stat, float* __restrict__ dk, float* __restrict__ dv,
@@ -221,7 +240,8 @@ __global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
     const int r_blk = tb * KW * 32;
     if (r_blk >= total) return;  // every wave of the block leaves together
     const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hf = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wv % KW, role = wv / KW;  // key group; 0: P and dv, 1: dS and dk
     const int r = r_blk + 32 * wave + col;  // the lane's compact row
     const bool rvalid = r < total;
     // the row's chunk (loff[c] <= r < loff[c + 1]) and position
@@ -235,13 +255,13 @@ __global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
     const int pos = rvalid ? selw[(bg * D.n_full + crow) * D.lam + (r - loff[crow])] : 0;
     const size_t ldl = (size_t)D.Hkv * kD;
     const size_t rowo = ((size_t)b * sel_list_rows(D) * D.Hkv + g) * kD + (size_t)min(r, total - 1) * ldl;
-    bf16x8 kf[8], vf[8];
-    load_key_operand(ksel + rowo, kf);
-    load_key_operand(vsel + rowo, vf);
+    bf16x8 kv[8];  // role 0: K rows, role 1: V rows
+    load_key_operand((role == 0 ? ksel : vsel) + rowo, kv);
     const float cl2 = D.tau * kLog2e;
-    f32x16 dva[4], dka[4];
+    f32x16 acc[4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dva[dt] = dka[dt] = zero16();
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
+    __shared__ __align__(16) bf16x8 pbuf[KW][2][2][64];
 
     // the block's first row belongs to chunk c0; query chunk qc sees the
     // rows of chunks <= qc - NWT - 1; this block takes segment sg of the
@@ -258,47 +278,42 @@ __global__ __launch_bounds__(KW * 64) void bwd_kv_selected_kernel(
         const int nq = min(kC, D.N - t0);
         for (int hh = 0; hh < D.G; ++hh) {
             __syncthreads();
-            stage_qtile<KW * 64>(T, q, dout, stat, D, b, t0, g * D.G + hh, tid);
+            stage_qtile(T, q, dout, stat, D, b, t0, g * D.G + hh, tid);
             __syncthreads();
-            if (32 * wave >= nvis) continue;
             const bool rv = rvalid && 32 * wave + col < nvis;
-            key_tile(T, kf, vf, cl2, [&](int rr) { return rv && rr < nq; }, dva, dka);
+            key_tile_split(T, kv, role, wave, cl2, 32 * wave < nvis, [&](int rr) { return rv && rr < nq; },
+                           pbuf, acc);
         }
     }
     if (!rvalid) return;
+    // role 0's sums are dv's, role 1's (times tau) dk's
+    const float sc = role == 1 ? D.tau : 1.f;
     if (sg > 0) {
-        float* pr = part + (((size_t)(sg - 1) * D.B * D.Hkv + bg) * ((size_t)D.n_full * D.lam) + r) * (2 * kD);
+        float* pr = part + (((size_t)(sg - 1) * D.B * D.Hkv + bg) * ((size_t)D.n_full * D.lam) + r) * (2 * kD) +
+                    (role == 1 ? 0 : kD);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int e = 32 * dt + acc_row(4 * v4, hf);
-                f32x4 a4, b4;
+                f32x4 a4;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    a4[jj] = D.tau * dka[dt][4 * v4 + jj];
-                    b4[jj] = dva[dt][4 * v4 + jj];
-                }
+                for (int jj = 0; jj < 4; ++jj) a4[jj] = sc * acc[dt][4 * v4 + jj];
                 *reinterpret_cast<f32x4*>(pr + e) = a4;
-                *reinterpret_cast<f32x4*>(pr + kD + e) = b4;
             }
         return;
     }
     const size_t o = (((size_t)b * D.N + pos) * D.Hkv + g) * kD;
+    float* dst = role == 1 ? dk : dv;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
             const int e = 32 * dt + acc_row(4 * v4, hf);
-            f32x4 a4 = *reinterpret_cast<const f32x4*>(dk + o + e);
-            f32x4 b4 = *reinterpret_cast<const f32x4*>(dv + o + e);
+            f32x4 a4 = *reinterpret_cast<const f32x4*>(dst + o + e);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                a4[jj] += D.tau * dka[dt][4 * v4 + jj];
-                b4[jj] += dva[dt][4 * v4 + jj];
-            }
-            *reinterpret_cast<f32x4*>(dk + o + e) = a4;
-            *reinterpret_cast<f32x4*>(dv + o + e) = b4;
+            for (int jj = 0; jj < 4; ++jj) a4[jj] += sc * acc[dt][4 * v4 + jj];
+            *reinterpret_cast<f32x4*>(dst + o + e) = a4;
         }
 }
 
@@ -1371,7 +1386,7 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
     if (phase == 0) {
         const unsigned nblk = (unsigned)((D.T + kWinKPB - 1) / kWinKPB) * D.B * D.Hkv;
 #define STILL_KVW(NWT)                                                                           \
-    hipLaunchKernelGGL((bwd_kv_window_kernel<NWT, kWinKPB>), dim3(nblk), dim3(kWinKPB * 128), 0, s, qq, \
+    hipLaunchKernelGGL((bwd_kv_window_kernel<NWT, kWinKPB>), dim3(nblk), dim3(kWinKPB * 256), 0, s, qq, \
                        reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(v), dd,  \
                        route, stat, dk, dv, D)
         if (nwt == 1) STILL_KVW(1);
@@ -1384,7 +1399,7 @@ hipError_t launch_bwd_kv(const Dims& D, const void* q, const void* k, const void
     const int ntile = (D.n_full * D.lam + kSelW * 32 - 1) / (kSelW * 32);
     const unsigned nblk = (unsigned)ntile * kSelSeg * D.B * D.Hkv;
 #define STILL_KVS(NWT)                                                                           \
-    hipLaunchKernelGGL((bwd_kv_selected_kernel<NWT, kSelW>), dim3(nblk), dim3(kSelW * 64), 0, s, qq, \
+    hipLaunchKernelGGL((bwd_kv_selected_kernel<NWT, kSelW>), dim3(nblk), dim3(kSelW * 128), 0, s, qq, \
                        reinterpret_cast<const bf16*>(ksel), reinterpret_cast<const bf16*>(vsel), \
                        dd, selw, list_off, stat, dk, dv, part, D)
     if (nwt == 1) STILL_KVS(1);
