@@ -55,25 +55,71 @@ struct QTile {
     float dd[kC];         // D = dout . out
 };
 
-// Stages the tile with 512 threads: Q (rows and transposed) by threads
-// 0-255, dout by 256-511, the statistics by the first 64.
-__device__ __forceinline__ void stage_qtile(QTile& T, const bf16* __restrict__ q, const bf16* __restrict__ dout,
-                                            const float* __restrict__ stat, const Dims& D, int b, int t0,
-                                            int h, int tid) {
-    const int nv = min(kC, D.N - t0);
-    const size_t ld = (size_t)D.Hq * kD;
-    const size_t o = (((size_t)b * D.N + t0) * D.Hq + h) * kD;
-    if (tid < 256) load_tile_both<256>(q + o, ld, nv, T.qs, T.qt, tid);
-    else load_tile_both<256>(dout + o, ld, nv, T.ds, T.dt, tid - 256);
-    if (tid < kC) {
-        float a = 0.f, dd = 0.f;
-        if (tid < nv) {
-            const f32x4 st = *reinterpret_cast<const f32x4*>(stat + ((((size_t)b * D.N + t0 + tid) * D.Hq + h) * 4));
-            a = st[0] * kLog2e + __log2f(st[1]);
-            dd = st[2];
+// Streams the query tiles of steps 0 .. nstep-1 (step n: the 64 queries
+// from t0 of head h, step_of(n, t0, h)) through two LDS buffers for a block
+// of 512 threads, calling body(n, tile) for each step with every wave.  The
+// Q and dout rows (padded layout; rows past N repeat the last one) and the
+// raw statistics of step n+1 come by DMA (global_load_lds) while step n is
+// computed; once they have landed, the block builds the transposed copies
+// (Q by threads 0-255, dout by 256-511) and the statistics in LDS.
+template <typename StepOf, typename Body>
+__device__ __forceinline__ void stream_qtiles(QTile (&T2)[2], float (&rawst)[2][kC * 4], int nstep,
+                                              StepOf step_of, Body body, const bf16* __restrict__ q,
+                                              const bf16* __restrict__ dout, const float* __restrict__ stat,
+                                              const Dims& D, int b) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto issue = [&](int n) {
+        int t0, h;
+        step_of(n, t0, h);
+        const int nv = min(kC, D.N - t0);
+        const size_t o = (((size_t)b * D.N + t0) * D.Hq + h) * kD;
+        QTile& B = T2[n & 1];
+        const unsigned qd = (unsigned)(size_t)(lds_void*)B.qs, dd = (unsigned)(size_t)(lds_void*)B.ds;
+        for (int x = wv; x < kKPieces; x += 8) {
+            stage_k_piece_u(x, q + o, D.Hq * kD, nv, qd);
+            stage_k_piece_u(x, dout + o, D.Hq * kD, nv, dd);
         }
-        T.lse2[tid] = a;
-        T.dd[tid] = dd;
+        if (wv == 7) {
+            const float* ss = stat + (((size_t)b * D.N + t0 + min(lane, nv - 1)) * D.Hq + h) * 4;
+            dma16_untracked(reinterpret_cast<const bf16*>(ss), (unsigned)(size_t)(lds_void*)rawst[n & 1]);
+        }
+    };
+    auto finish = [&](int n) {
+        int t0, h;
+        step_of(n, t0, h);
+        const int nv = min(kC, D.N - t0);
+        QTile& B = T2[n & 1];
+        const bf16* src = tid < 256 ? B.qs : B.ds;
+        bf16* dst = tid < 256 ? B.qt : B.dt;
+        const int x = tid & 255, kq = x & 15, oct = x >> 4;  // rows 4 kq .. +3, columns 8 oct .. +7
+        bf16x8 r4[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) r4[rr] = ld_bf8(src + (4 * kq + rr) * kKS + 8 * oct);
+        const int pos = kperm(4 * kq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bf16x4 t4;
+            t4[0] = r4[0][e];
+            t4[1] = r4[1][e];
+            t4[2] = r4[2][e];
+            t4[3] = r4[3][e];
+            *reinterpret_cast<bf16x4*>(dst + (8 * oct + e) * kVS + pos) = t4;
+        }
+        if (tid < kC) {
+            const f32x4 st = *reinterpret_cast<const f32x4*>(rawst[n & 1] + 4 * tid);
+            B.lse2[tid] = tid < nv ? st[0] * kLog2e + __log2f(st[1]) : 0.f;  // P = 2^(s tau log2 e - lse2)
+            B.dd[tid] = tid < nv ? st[2] : 0.f;
+        }
+    };
+    if (nstep > 0) issue(0);
+    for (int n = 0; n < nstep; ++n) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of step n
+        __syncthreads();                      // every share landed; step n-1 is done
+        finish(n);
+        __syncthreads();
+        if (n + 1 < nstep) issue(n + 1);  // into the buffer of step n-1
+        body(n, T2[n & 1]);
     }
 }
 
@@ -154,6 +200,7 @@ __global__ __launch_bounds__(KPB * 256) __attribute__((amdgpu_waves_per_eu(2))) 
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const uint8_t* __restrict__ route, const float* __restrict__ stat,
     float* __restrict__ dk, float* __restrict__ dv, Dims D) {
+    static_assert(KPB * 256 == 512, "stream_qtiles takes blocks of 512 threads");
     const int npair = (D.T + KPB - 1) / KPB;
     const int cb = (int)(blockIdx.x % npair);
     const int bgi = (int)(blockIdx.x / npair);
@@ -175,17 +222,21 @@ __global__ __launch_bounds__(KPB * 256) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
 
-    __shared__ QTile T;
+    __shared__ QTile T2[2];
+    __shared__ __align__(16) float rawst[2][kC * 4];
     __shared__ __align__(16) bf16x8 pbuf[2 * KPB][2][2][64];
+    // steps: query chunks c_first .. c_last, every head of the group
     const int c_first = KPB * cb, c_last = min(D.T - 1, KPB * cb + KPB - 1 + NWT);
-    for (int qc = c_first; qc <= c_last; ++qc) {
-        const int i = qc - ck;  // query chunk relative to this wave's key chunk
-        const int t0 = qc * kC;
-        for (int hh = 0; hh < D.G; ++hh) {
-            __syncthreads();
-            stage_qtile(T, q, dout, stat, D, b, t0, g * D.G + hh, tid);
-            __syncthreads();
-            const int nq = min(kC, D.N - t0);
+    stream_qtiles(
+        T2, rawst, (c_last - c_first + 1) * D.G,
+        [&](int n, int& t0, int& h) {
+            t0 = (c_first + n / D.G) * kC;
+            h = g * D.G + n % D.G;
+        },
+        [&](int n, const QTile& T) {
+            const int qc = c_first + n / D.G;
+            const int i = qc - ck;  // query chunk relative to this group's key chunk
+            const int nq = min(kC, D.N - qc * kC);
             key_tile_split(T, kv, role, wave, cl2, !(i < 0 || i > NWT || ck >= D.T),
                            [&](int r) {
                                if (!kvalid || r >= nq) return false;
@@ -194,8 +245,8 @@ __global__ __launch_bounds__(KPB * 256) __attribute__((amdgpu_waves_per_eu(2))) 
                                return r < ok || ksel;                         // window part, routed selected
                            },
                            pbuf, acc);
-        }
-    }
+        },
+        q, dout, stat, D, b);
     if (!kvalid) return;
     // role 0 adds to dv, role 1 tau times its sums to dk
     const size_t o = (((size_t)b * D.N + j) * D.Hkv + g) * kD;
@@ -227,6 +278,7 @@ __global__ __launch_bounds__(KW * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const bf16* __restrict__ dout, const int32_t* __restrict__ selw, const int* __restrict__ list_off,
     const float* __restrict__ stat, float* __restrict__ dk, float* __restrict__ dv,
     float* __restrict__ part, Dims D) {
+    static_assert(KW * 128 == 512, "stream_qtiles takes blocks of 512 threads");
     // blocks in order of (row tile, segment), every (b, g) side by side:
     // earlier row tiles meet more query chunks, so the longest go first
     const int nbg = D.B * D.Hkv;
@@ -271,20 +323,24 @@ __global__ __launch_bounds__(KW * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     const int qa = c0 + NWT + 1, nq_all = max(0, D.T - qa);
     const int seg_len = (nq_all + kSelSeg - 1) / kSelSeg;
     const int q_lo = qa + sg * seg_len, q_hi = min(D.T, q_lo + seg_len);
-    __shared__ QTile T;
-    for (int qc = q_lo; qc < q_hi; ++qc) {
-        const int nvis = loff[min(qc - NWT, D.n_full)] - r_blk;  // visible rows: a prefix
-        const int t0 = qc * kC;
-        const int nq = min(kC, D.N - t0);
-        for (int hh = 0; hh < D.G; ++hh) {
-            __syncthreads();
-            stage_qtile(T, q, dout, stat, D, b, t0, g * D.G + hh, tid);
-            __syncthreads();
+    __shared__ QTile T2[2];
+    __shared__ __align__(16) float rawst[2][kC * 4];
+    // steps: query chunks q_lo .. q_hi - 1, every head of the group
+    stream_qtiles(
+        T2, rawst, (q_hi - q_lo) * D.G,
+        [&](int n, int& t0, int& h) {
+            t0 = (q_lo + n / D.G) * kC;
+            h = g * D.G + n % D.G;
+        },
+        [&](int n, const QTile& T) {
+            const int qc = q_lo + n / D.G;
+            const int nvis = loff[min(qc - NWT, D.n_full)] - r_blk;  // visible rows: a prefix
+            const int nq = min(kC, D.N - qc * kC);
             const bool rv = rvalid && 32 * wave + col < nvis;
             key_tile_split(T, kv, role, wave, cl2, 32 * wave < nvis, [&](int rr) { return rv && rr < nq; },
                            pbuf, acc);
-        }
-    }
+        },
+        q, dout, stat, D, b);
     if (!rvalid) return;
     // role 0's sums are dv's, role 1's (times tau) dk's
     const float sc = role == 1 ? D.tau : 1.f;
