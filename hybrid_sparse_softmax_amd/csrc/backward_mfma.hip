@@ -822,8 +822,9 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
     sb = (sb + xor32(sb)) * sn;  // phi- . dfq-
     if (dgate && hf == 0 && qvalid) dgate[qo] = gw * (1.f - gw) * cf * (sa + sb);
     if (stat_in && qvalid) {
-        // gamma phi_q (bf16, feature order) for the kernels after this one:
-        // rows 32 ft + acc_row(4 v4, hf) .. +3 hold four consecutive features
+        // gamma phi_q (bf16) for the kernels after this one, in the features'
+        // storage order (position p holds feature kperm(p), as phi_k): rows
+        // 32 ft + acc_row(4 v4, hf) .. +3 are four consecutive positions
         bf16* pr = phiq + qo * kD;
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft)
@@ -835,9 +836,9 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
                     a4[j] = (bf16)(gw * sp * ep[ft][4 * v4 + j]);
                     b4[j] = (bf16)(gw * sn * en[ft][4 * v4 + j]);
                 }
-                const int f0 = kperm(32 * ft + acc_row(4 * v4, hf));
-                *reinterpret_cast<bf16x4*>(pr + f0) = a4;
-                *reinterpret_cast<bf16x4*>(pr + 64 + f0) = b4;
+                const int p0 = 32 * ft + acc_row(4 * v4, hf);
+                *reinterpret_cast<bf16x4*>(pr + p0) = a4;
+                *reinterpret_cast<bf16x4*>(pr + 64 + p0) = b4;
             }
     }
     const float dsc = gw * cf;  // dphi_q = dsc dfq
@@ -921,18 +922,9 @@ __global__ __launch_bounds__(HB * 128) __attribute__((amdgpu_waves_per_eu(2))) v
 // chunks) plus the queries of chunk cj + NWT at or after the key's offset.
 // ---------------------------------------------------------------------------
 
-// fq row (bf16, feature order) -> the 8 features of storage positions
-// 8 oct .. 8 oct + 7 (position p holds feature kperm(p))
-__device__ __forceinline__ bf16x8 fq_oct_perm(const bf16* __restrict__ row, int oct) {
-    // positions 16 b + 8 h + 4 m + l hold features 16 b + 8 m + 4 h + l
-    const int b16 = 16 * (oct >> 1), h4 = 4 * (oct & 1);
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + b16 + h4);
-    const bf16x4 c = *reinterpret_cast<const bf16x4*>(row + b16 + 8 + h4);
-    return __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Chunk sums per query chunk c of (b, g): U[i][e] = sum over its queries t
 // and the group's heads of c_t fq_t[i] dout_t[e], u[i] = sum c_t D_t fq_t[i]
+// (i: the features' storage position, the order fq is stored in)
 // (the fp32 layout [i][e] then u, (d + 1) d' floats).  Per head, (c fq)^T and
 // dout^T are staged with the queries as contraction index; wave w owns
 // features 32 w .. 32 w + 31.
@@ -963,7 +955,7 @@ __global__ __launch_bounds__(256) void bwd_uchunk_mfma_kernel(const bf16* __rest
                 const int row = 4 * kq + q4;
                 if (row < nv) {
                     const size_t o = o0 + (size_t)row * D.Hq;
-                    // the features in natural order here: position = feature
+                    // fq in the features' storage order: U's rows are positions
                     const float cf = stat[o * 4 + 3];
                     const bf16x8 a = ld_bf8(phiq + o * kD + 8 * oct);
 #pragma unroll
@@ -1050,9 +1042,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         bf16* ub = sm;              // [p][e], kKS
         bf16* ut = sm + kD * kKS;   // [e][p], kKS
         for (int x = tid; x < kD * 16; x += 256) {
-            const int pp = x >> 4, oct = x & 15;
-            const int f = kperm(pp);
-            const bf16x8 r = ld_bf8(U16 + (size_t)f * kD + 8 * oct);
+            const int pp = x >> 4, oct = x & 15;  // U's rows are the features' storage positions
+            const bf16x8 r = ld_bf8(U16 + (size_t)pp * kD + 8 * oct);
             st_bf8(ub + pp * kKS + 8 * oct, r);
 #pragma unroll
             for (int e = 0; e < 8; ++e) ut[(8 * oct + e) * kKS + pp] = r[e];
@@ -1069,7 +1060,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-                for (int vv = 0; vv < 16; ++vv) acc[t4][vv] -= U[kD * kD + kperm(32 * t4 + acc_row(vv, hf))];
+                for (int vv = 0; vv < 16; ++vv) acc[t4][vv] -= U[kD * kD + 32 * t4 + acc_row(vv, hf)];
         }
     }
     if (has_q) {
@@ -1087,7 +1078,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
             for (int x = tid; x < kC * 16; x += 256) {
                 const int row = x >> 4, oct = x & 15;
                 st_bf8(fq + row * kKS + 8 * oct,
-                       row < nq ? fq_oct_perm(phiq + (o0 + (size_t)row * D.Hq) * kD, oct) : zero_bf8());
+                       row < nq ? ld_bf8(phiq + (o0 + (size_t)row * D.Hq) * kD + 8 * oct) : zero_bf8());
             }
             load_k_tile(dout + o0 * kD, (size_t)D.Hq * kD, nq, dr, tid, 256);
             if (tid < kC) {

@@ -708,8 +708,9 @@ __device__ __forceinline__ void matrix_phase(f32x16 (&o)[4], f32x16 (&sc)[2], co
 // rows list_off[c] .. list_off[c + 1] - 1 of (b, g) (n_full + 1 entries, the
 // last the open chunk's copy), for lists built from a given selection whose
 // chunks may hold fewer than lam rows.  STATS also writes each query head's
-// gated NP-Map features gamma phi_q (bf16, feature order) to phiq_out (zeros
-// for queries with no routed token).
+// gated NP-Map features gamma phi_q (bf16, in the features' storage order:
+// position p holds feature kperm(p), as for phi_k) to phiq_out (zeros for
+// queries with no routed token).
 template <int HB, int NWT, bool STATS = false>
 __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -893,7 +894,8 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                     for (int vv = 0; vv < 16; ++vv) phi[0][sgn][f2][vv] *= gw;
         }
         if constexpr (STATS) {
-            // this lane's 64 features of its query: 64 sgn + 32 f2 + acc_row(..)
+            // this lane's 64 features of its query, 64 sgn + 32 f2 + acc_row(..),
+            // at their storage positions (position p holds feature kperm(p))
             if (t0 + oq < D.N) {
                 bf16* pr = phiq_out + (((size_t)b * D.N + t0 + oq) * D.Hq + h) * kD;
 #pragma unroll
@@ -905,7 +907,7 @@ __global__ __launch_bounds__(HB * 128) void hybrid_main_kernel(
                             bf16x4 x4;
 #pragma unroll
                             for (int j = 0; j < 4; ++j) x4[j] = (bf16)phi[0][sgn][f2][4 * v4 + j];
-                            *reinterpret_cast<bf16x4*>(pr + 64 * sgn + 32 * f2 + acc_row(4 * v4, hf)) = x4;
+                            *reinterpret_cast<bf16x4*>(pr + kperm(64 * sgn + 32 * f2 + acc_row(4 * v4, hf))) = x4;
                         }
             }
         }
