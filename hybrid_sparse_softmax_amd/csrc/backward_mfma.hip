@@ -1033,6 +1033,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     // one area: U and U^T (bf16), then per head fq, fq^T, dout, dout^T
     __shared__ __align__(16) bf16 sm[2 * kC * kKS + 2 * kD * kVS];
     __shared__ float cq[kC], dq_[kC];
+    __shared__ __align__(16) float rawst[2][kC * 4];  // raw statistics of the staged heads
     f32x16 acc[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) acc[t4] = zero16();
@@ -1065,33 +1066,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
     if (has_q) {
         const int tq0 = c0 * kC, nq = min(kC, D.N - tq0);
-        // fq [q][p] and dout [q][e] rows (kKS); their transposes are read
-        // from the same rows (ds_read_b64_tr_b16)
-        bf16* fq = sm;
-        bf16* dr = sm + kC * kKS;
+        // Per head: fq [q][p] and dout [q][e] rows (kKS; rows past N repeat
+        // the last one, with weight c = 0) in one of two buffers, requested by
+        // DMA while the previous head is computed (head 0 after the suffix
+        // products, whose operands fill both); their transposes are read from
+        // the same rows (ds_read_b64_tr_b16).
         int poff[4];
         kt_pad_lane_offsets(poff);
+        const unsigned lds_sm = (unsigned)(size_t)(lds_void*)sm;
+        auto issue = [&](int hh) {
+            const size_t o0 = ((size_t)b * D.N + tq0) * D.Hq + g * D.G + hh;
+            const unsigned fb = lds_sm + 4u * kKTile * (unsigned)(hh & 1), db = fb + 2u * kKTile;
+            for (int x = wave; x < kKPieces; x += 4) {
+                stage_k_piece_u(x, phiq + o0 * kD, D.Hq * kD, nq, fb);
+                stage_k_piece_u(x, dout + o0 * kD, D.Hq * kD, nq, db);
+            }
+            if (wave == 3)
+                dma16_untracked(reinterpret_cast<const bf16*>(stat + (o0 + (size_t)min(lane, nq - 1) * D.Hq) * 4),
+                                (unsigned)(size_t)(lds_void*)rawst[hh & 1]);
+        };
+        __syncthreads();  // the suffix products' reads of sm are done
+        issue(0);
         for (int hh = 0; hh < D.G; ++hh) {
-            const int h = g * D.G + hh;
-            const size_t o0 = ((size_t)b * D.N + tq0) * D.Hq + h;
-            __syncthreads();
-            for (int x = tid; x < kC * 16; x += 256) {
-                const int row = x >> 4, oct = x & 15;
-                st_bf8(fq + row * kKS + 8 * oct,
-                       row < nq ? ld_bf8(phiq + (o0 + (size_t)row * D.Hq) * kD + 8 * oct) : zero_bf8());
-            }
-            load_k_tile(dout + o0 * kD, (size_t)D.Hq * kD, nq, dr, tid, 256);
+            const bf16* fq = sm + 2 * kKTile * (hh & 1);
+            const bf16* dr = fq + kKTile;
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of head hh
+            __syncthreads();                      // every share landed; head hh-1 is done
             if (tid < kC) {
-                float cf = 0.f, dd = 0.f;
-                if (tid < nq) {
-                    const f32x4 s4 = *reinterpret_cast<const f32x4*>(stat + (o0 + (size_t)tid * D.Hq) * 4);
-                    cf = s4[3];
-                    dd = s4[2];
-                }
-                cq[tid] = cf;
-                dq_[tid] = dd;
+                const f32x4 s4 = *reinterpret_cast<const f32x4*>(rawst[hh & 1] + 4 * tid);
+                cq[tid] = tid < nq ? s4[3] : 0.f;
+                dq_[tid] = tid < nq ? s4[2] : 0.f;
             }
             __syncthreads();
+            if (hh + 1 < D.G) issue(hh + 1);  // into the buffer of head hh-1
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 // rows: queries 32 qb + acc_row, column: the lane's key
