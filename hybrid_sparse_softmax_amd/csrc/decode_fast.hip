@@ -315,15 +315,23 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
         float* Sg = c.lin_S + bg * D.fd * kD;
         const bool la = ev == kRouteLA;
         const float vd = la ? vs[dim] : 0.f;
-        for (int f = half * 64; f < half * 64 + 64; ++f) {
-            float sv = Sg[(size_t)f * kD + dim];
-            if (la) {
-                sv = fmaf(ph[f], vd, sv);
-                Sg[(size_t)f * kD + dim] = sv;
-            }
+        // rows in batches of 32, each batch's loads issued before any is used
+        // (the step's latency chain otherwise)
+        for (int f0 = half * 64; f0 < half * 64 + 64; f0 += 32) {
+            float sv[32];
 #pragma unroll
-            for (int h = 0; h < 8; ++h)
-                if (h < G) num[h] = fmaf(phq[h][f], sv, num[h]);
+            for (int u = 0; u < 32; ++u) sv[u] = Sg[(size_t)(f0 + u) * kD + dim];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const int f = f0 + u;
+                if (la) {
+                    sv[u] = fmaf(ph[f], vd, sv[u]);
+                    Sg[(size_t)f * kD + dim] = sv[u];
+                }
+#pragma unroll
+                for (int h = 0; h < 8; ++h)
+                    if (h < G) num[h] = fmaf(phq[h][f], sv[u], num[h]);
+            }
         }
 #pragma unroll
         for (int h = 0; h < 8; ++h)
@@ -356,7 +364,7 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
                 const int64_t pos = t - n_win + 1 + i;
                 const bf16* kr = i == n_win - 1 ? kt : ring_k + (size_t)(pos % W) * kD;
                 float d = 0.f;
-#pragma unroll 4
+#pragma unroll 8
                 for (int x = 0; x < kD / 8; ++x) {
                     const bf16x8 kk = ld8(kr + 8 * x);
 #pragma unroll
@@ -422,14 +430,25 @@ __device__ __forceinline__ void state_role(const bf16* __restrict__ q, const bf1
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int nb = min(64, n_win - 64 * r);
-            for (int jj = 0; jj < nb; ++jj) {
-                const int j = 64 * r + jj;
-                const float pj = __shfl(p[r], jj, kWave);
-                const int64_t pos = t - n_win + 1 + j;
-                const bf16* vr = j == n_win - 1 ? vt : ring_v + (size_t)(pos % W) * kD;
-                const bf16x2 v2 = *reinterpret_cast<const bf16x2*>(vr + 2 * lane);
-                a0 = fmaf(pj, (float)v2[0], a0);
-                a1 = fmaf(pj, (float)v2[1], a1);
+            // rows in batches of 16, loaded before use; a batch's rows past
+            // the window repeat its last row and take no weight
+            for (int j0 = 0; j0 < nb; j0 += 16) {
+                bf16x2 v2[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int j = 64 * r + min(j0 + u, nb - 1);
+                    const int64_t pos = t - n_win + 1 + j;
+                    const bf16* vr = j == n_win - 1 ? vt : ring_v + (size_t)(pos % W) * kD;
+                    v2[u] = *reinterpret_cast<const bf16x2*>(vr + 2 * lane);
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const float pj = __shfl(p[r], min(j0 + u, 63), kWave);
+                    if (j0 + u < nb) {
+                        a0 = fmaf(pj, (float)v2[u][0], a0);
+                        a1 = fmaf(pj, (float)v2[u][1], a1);
+                    }
+                }
             }
         }
         float* wp = w.win + ((size_t)b * D.Hq + g * G + hh) * (kD + 2);
